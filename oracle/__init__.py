@@ -1,0 +1,145 @@
+"""ctypes front end of the CPU fp64 oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg; never by the library.  Every function takes and
+returns numpy float64 arrays holding the exact values of the inputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+             "-shared", "-fPIC"]
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (plain C, no GPU code)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        i64, dbl, p = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+        lib.oracle_bn_forward_train.argtypes = [i64, i64, i64, p, p, p, dbl, dbl, p, p, p, p]
+        lib.oracle_bn_backward.argtypes = [i64, i64, i64, p, p, p, dbl, p, p]
+        lib.oracle_layernorm_stats.argtypes = [i64, i64, p, dbl, p, p]
+        lib.oracle_layernorm_backward.argtypes = [i64, i64, p, p, p, p, p, p, p, p]
+        lib.oracle_rmsnorm_rms.argtypes = [i64, i64, p, dbl, p]
+        lib.oracle_rmsnorm_backward.argtypes = [i64, i64, p, p, p, p, dbl, p, p]
+        for f in ("oracle_bn_forward_train", "oracle_bn_backward", "oracle_layernorm_stats",
+                  "oracle_layernorm_backward", "oracle_rmsnorm_rms", "oracle_rmsnorm_backward"):
+            getattr(lib, f).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _d(a):
+    """Contiguous float64 copy-or-view of a."""
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError(f"{name}: bad arguments (rc={rc})")
+
+
+def bn_forward_train(x, gamma, beta, *, eps=1e-5, momentum=0.1,
+                     running_mean=None, running_var=None):
+    """x: [N,C,H,W] (or [N,C,HW]).  Returns (y, stats[4,C], rm', rv').
+    rm'/rv' are None when the running statistics are not given."""
+    x = _d(x)
+    N, C = x.shape[0], x.shape[1]
+    HW = int(np.prod(x.shape[2:])) if x.ndim > 2 else 1
+    g, b = _d(gamma), _d(beta)
+    rm = None if running_mean is None else _d(running_mean).copy()
+    rv = None if running_var is None else _d(running_var).copy()
+    y = np.empty_like(x)
+    stats = np.empty((4, C), np.float64)
+    rc = _load().oracle_bn_forward_train(N, C, HW, _ptr(x), _ptr(g), _ptr(b),
+                                         momentum, eps, _ptr(rm), _ptr(rv),
+                                         _ptr(y), _ptr(stats))
+    _check(rc, "oracle_bn_forward_train")
+    return y, stats, rm, rv
+
+
+def bn_backward(x, dy, gamma, *, eps=1e-5):
+    """Returns (dx, grads[4,C] = (dgamma, dbeta, k1, k2))."""
+    x, dy = _d(x), _d(dy)
+    N, C = x.shape[0], x.shape[1]
+    HW = int(np.prod(x.shape[2:])) if x.ndim > 2 else 1
+    g = _d(gamma)
+    dx = np.empty_like(x)
+    grads = np.empty((4, C), np.float64)
+    rc = _load().oracle_bn_backward(N, C, HW, _ptr(x), _ptr(dy), _ptr(g), eps,
+                                    _ptr(dx), _ptr(grads))
+    _check(rc, "oracle_bn_backward")
+    return dx, grads
+
+
+def layernorm_stats(x, *, eps=1e-5):
+    """x: [rows, cols].  Returns (mean[rows], rstd[rows])."""
+    x = _d(x)
+    rows, cols = x.shape
+    mean = np.empty(rows, np.float64)
+    rstd = np.empty(rows, np.float64)
+    _check(_load().oracle_layernorm_stats(rows, cols, _ptr(x), eps, _ptr(mean), _ptr(rstd)),
+           "oracle_layernorm_stats")
+    return mean, rstd
+
+
+def layernorm_backward(x, dy, mean, rstd, w=None):
+    """Returns (dx, dweight, dbias)."""
+    x, dy, mean, rstd = _d(x), _d(dy), _d(mean), _d(rstd)
+    w = None if w is None else _d(w)
+    rows, cols = x.shape
+    dx = np.empty_like(x)
+    dw = np.empty(cols, np.float64)
+    db = np.empty(cols, np.float64)
+    _check(_load().oracle_layernorm_backward(rows, cols, _ptr(x), _ptr(dy), _ptr(mean),
+                                             _ptr(rstd), _ptr(w), _ptr(dx), _ptr(dw), _ptr(db)),
+           "oracle_layernorm_backward")
+    return dx, dw, db
+
+
+def rmsnorm_rms(x, *, eps=1e-5):
+    x = _d(x)
+    rows, cols = x.shape
+    rms = np.empty(rows, np.float64)
+    _check(_load().oracle_rmsnorm_rms(rows, cols, _ptr(x), eps, _ptr(rms)), "oracle_rmsnorm_rms")
+    return rms
+
+
+def rmsnorm_backward(x, dy, w, rms=None, *, eps=1e-5):
+    """Returns (dx, dweight).  rms=None recomputes rms from x with eps."""
+    x, dy, w = _d(x), _d(dy), _d(w)
+    rms = None if rms is None else _d(rms)
+    rows, cols = x.shape
+    dx = np.empty_like(x)
+    dw = np.empty(cols, np.float64)
+    _check(_load().oracle_rmsnorm_backward(rows, cols, _ptr(x), _ptr(dy), _ptr(w), _ptr(rms),
+                                           eps, _ptr(dx), _ptr(dw)),
+           "oracle_rmsnorm_backward")
+    return dx, dw

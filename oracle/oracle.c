@@ -1,0 +1,364 @@
+/*
+ * CPU fp64 oracle for training-mode normalization forward/backward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, plain definition that the
+ * HIP library is checked against.  Only the test suite, the smoke check and
+ * the benchmark's CPU-baseline leg load it; the library never does, and the
+ * two share no source, header, table or helper.
+ *
+ * Every quantity is computed in double precision, straight from its
+ * definition: means and variances by two passes over the data, sums with
+ * Neumaier-compensated accumulation, no one-pass shifted sums, no partials,
+ * no coefficient-form shortcuts.  Loops are sequential and single-threaded.
+ *
+ * Layouts: BatchNorm tensors are NCHW, contiguous, element (n,c,j) at
+ * (n*C + c)*HW + j with HW = H*W.  LayerNorm/RMSNorm tensors are
+ * [rows, cols] row-major, reduced over cols.
+ *
+ * Sources (the pages these definitions are read from):
+ *  [AE]  Aether-ML PR #18, "perf(batchnorm): device-sized grid, one-pass
+ *        statistics, finalize kernels": commit messages and the PR body's
+ *        "One-pass statistics", "Backward finalize", "Behavior changes" and
+ *        "Testing" sections.
+ *  [TH]  lightning-thunder PR #182, "Improve batch_norm backward performance
+ *        for automatically generated backward" (batch_norm decomposition,
+ *        running_var accuracy fix).
+ *  [LN]  NVIDIA/Fuser issue #1473, "Why is LayerNorm Backward Segmenting?",
+ *        the 3-kernel layer_norm backward repro (nvfuser_fusion_id14).
+ *  [RM]  NVIDIA/Fuser issue #3629, "Performance gap between manual nvfuser
+ *        definition and thunder.jit for rmsnorm": rmsnorm_prims and the
+ *        pre-generated rmsnorm_bwd_fusion definition.
+ *
+ * Parity pins (tests/test_oracle_*.py): PyTorch CPU fp64 autograd of
+ * F.batch_norm / F.layer_norm / F.rms_norm, central finite differences of
+ * each forward, exact rational arithmetic on tiny inputs, the shift and
+ * scale invariants with their eps closed forms, and the large-offset
+ * variance case.  No function here is "parity unpinned".
+ *
+ * Return value of every entry point: 0 on success, -1 on a bad argument.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+/* ---- compensated summation (Neumaier's improvement of Kahan's method) ---- */
+typedef struct {
+    double s; /* running sum */
+    double c; /* running compensation: the low-order bits lost from s */
+} ksum_t;
+
+static void ks_init(ksum_t *k) { k->s = 0.0; k->c = 0.0; }
+
+static void ks_add(ksum_t *k, double v)
+{
+    double t = k->s + v;
+    if (fabs(k->s) >= fabs(v))
+        k->c += (k->s - t) + v;
+    else
+        k->c += (v - t) + k->s;
+    k->s = t;
+}
+
+static double ks_value(const ksum_t *k) { return k->s + k->c; }
+
+static size_t bn_index(int64_t n, int64_t c, int64_t j, int64_t C, int64_t HW)
+{
+    return (size_t)((n * C + c) * HW + j);
+}
+
+/* Per-channel batch statistics of an NCHW tensor: the mean over (N,H,W) and
+ * the biased variance (divide by M = N*H*W), two passes.  [AE] checks
+ * batch_var against "the float64 variance of the same data" ("Testing"); its
+ * k1 coefficient uses inv_std^2 with that same variance, which only holds for
+ * the biased estimator. */
+static void bn_channel_moments(const double *x, int64_t N, int64_t C, int64_t HW,
+                               int64_t c, double *mean, double *var)
+{
+    const double M = (double)(N * HW);
+    ksum_t s;
+    ks_init(&s);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t j = 0; j < HW; ++j)
+            ks_add(&s, x[bn_index(n, c, j, C, HW)]);
+    double mu = ks_value(&s) / M;
+    ksum_t q;
+    ks_init(&q);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t j = 0; j < HW; ++j) {
+            double d = x[bn_index(n, c, j, C, HW)] - mu;
+            ks_add(&q, d * d);
+        }
+    *mean = mu;
+    *var = ks_value(&q) / M;
+}
+
+/*
+ * BatchNorm2d training forward.  [AE] commit "one-pass statistics": the
+ * forward produces stats[4,C] = (mean, var, inv_std, gamma*inv_std), the
+ * output y = (x - mean)*scale + beta in its centred form, and updates the
+ * running statistics in place.
+ *
+ * Running-statistics update (the pages name it but give no formula; [TH]
+ * decomposes PyTorch's batch_norm, whose rule is taken):
+ *   running_mean <- (1 - momentum)*running_mean + momentum*mean
+ *   running_var  <- (1 - momentum)*running_var  + momentum*var*M/(M-1)
+ * i.e. the running variance uses the unbiased estimator.  running_mean and
+ * running_var may be NULL (no update); with them given, M must exceed 1.
+ *
+ * Inputs: x[N*C*HW], gamma[C], beta[C].  Outputs: y[N*C*HW], stats[4*C]
+ * (row-major: stats[0*C + c] = mean, [1*C + c] = var, [2*C + c] = inv_std,
+ * [3*C + c] = scale).
+ */
+int oracle_bn_forward_train(int64_t N, int64_t C, int64_t HW,
+                            const double *x, const double *gamma, const double *beta,
+                            double momentum, double eps,
+                            double *running_mean, double *running_var,
+                            double *y, double *stats)
+{
+    if (N < 0 || C < 0 || HW < 0) return -1;
+    const int64_t M = N * HW;
+    if (M == 0) return -1;
+    if ((running_mean || running_var) && M < 2) return -1;
+    for (int64_t c = 0; c < C; ++c) {
+        double mean, var;
+        bn_channel_moments(x, N, C, HW, c, &mean, &var);
+        double inv_std = 1.0 / sqrt(var + eps);
+        double scale = gamma[c] * inv_std;
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t j = 0; j < HW; ++j) {
+                size_t i = bn_index(n, c, j, C, HW);
+                double xhat = (x[i] - mean) * inv_std;
+                y[i] = gamma[c] * xhat + beta[c];
+            }
+        stats[0 * C + c] = mean;
+        stats[1 * C + c] = var;
+        stats[2 * C + c] = inv_std;
+        stats[3 * C + c] = scale;
+        if (running_mean)
+            running_mean[c] = (1.0 - momentum) * running_mean[c] + momentum * mean;
+        if (running_var)
+            running_var[c] = (1.0 - momentum) * running_var[c]
+                           + momentum * var * (double)M / (double)(M - 1);
+    }
+    return 0;
+}
+
+/*
+ * BatchNorm2d training backward: the gradient of the training forward above
+ * with respect to x, gamma and beta, for an incoming gradient dy.  The batch
+ * statistics are recomputed from x (two passes), so nothing saved by a
+ * forward run enters.
+ *
+ * Textbook form, per channel with xhat = (x - mean)*inv_std:
+ *   dbeta  = sum dy
+ *   dgamma = sum dy*xhat
+ *   dx     = gamma*inv_std/M * (M*dy - dbeta - xhat*dgamma)
+ * (deliberately not the coefficient form the pages' kernel uses).
+ *
+ * grads[4*C] = (dgamma, dbeta, k1, k2) as [AE]'s backward-finalize commit
+ * defines them:
+ *   k1 = -scale*inv_std^2 * sum(dy*(x - mean)) / M
+ *   k2 = -scale*dbeta / M
+ * with scale = gamma*inv_std.
+ */
+int oracle_bn_backward(int64_t N, int64_t C, int64_t HW,
+                       const double *x, const double *dy, const double *gamma,
+                       double eps, double *dx, double *grads)
+{
+    if (N < 0 || C < 0 || HW < 0) return -1;
+    const int64_t Mi = N * HW;
+    if (Mi == 0) return -1;
+    const double M = (double)Mi;
+    for (int64_t c = 0; c < C; ++c) {
+        double mean, var;
+        bn_channel_moments(x, N, C, HW, c, &mean, &var);
+        double inv_std = 1.0 / sqrt(var + eps);
+        double scale = gamma[c] * inv_std;
+        ksum_t sdy, sdyxhat, sdyxc;
+        ks_init(&sdy);
+        ks_init(&sdyxhat);
+        ks_init(&sdyxc);
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t j = 0; j < HW; ++j) {
+                size_t i = bn_index(n, c, j, C, HW);
+                double xc = x[i] - mean;
+                ks_add(&sdy, dy[i]);
+                ks_add(&sdyxhat, dy[i] * xc * inv_std);
+                ks_add(&sdyxc, dy[i] * xc);
+            }
+        double dbeta = ks_value(&sdy);
+        double dgamma = ks_value(&sdyxhat);
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t j = 0; j < HW; ++j) {
+                size_t i = bn_index(n, c, j, C, HW);
+                double xhat = (x[i] - mean) * inv_std;
+                dx[i] = gamma[c] * inv_std / M * (M * dy[i] - dbeta - xhat * dgamma);
+            }
+        grads[0 * C + c] = dgamma;
+        grads[1 * C + c] = dbeta;
+        grads[2 * C + c] = -scale * inv_std * inv_std * ks_value(&sdyxc) / M;
+        grads[3 * C + c] = -scale * dbeta / M;
+    }
+    return 0;
+}
+
+/*
+ * LayerNorm forward statistics over the last dimension, used to make the
+ * saved mean/rstd that the backward consumes: mean = sum x / H,
+ * var = sum (x - mean)^2 / H (biased), rstd = 1/sqrt(var + eps).
+ */
+int oracle_layernorm_stats(int64_t rows, int64_t cols, const double *x, double eps,
+                           double *mean, double *rstd)
+{
+    if (rows < 0 || cols <= 0) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *xr = x + (size_t)r * (size_t)cols;
+        ksum_t s;
+        ks_init(&s);
+        for (int64_t j = 0; j < cols; ++j) ks_add(&s, xr[j]);
+        double mu = ks_value(&s) / (double)cols;
+        ksum_t q;
+        ks_init(&q);
+        for (int64_t j = 0; j < cols; ++j) {
+            double d = xr[j] - mu;
+            ks_add(&q, d * d);
+        }
+        mean[r] = mu;
+        rstd[r] = 1.0 / sqrt(ks_value(&q) / (double)cols + eps);
+    }
+    return 0;
+}
+
+/*
+ * LayerNorm backward over the last dimension with saved per-row mean and rstd,
+ * as [LN]'s layer_norm backward definition computes it (tensor names of that
+ * definition in brackets):
+ *   g      = dy * w                                   [T18]
+ *   dvar_r = -1/2 * rstd^3 * sum_j g*(x - mean)       [T24, T38, T40, T41]
+ *   dmean_r = -sum_j g*rstd                           [T22, T30, T31]
+ *   dx     = g*rstd + 2*dvar*(x - mean)/H + dmean/H   [T55..T74]
+ *   dweight_j = sum_rows dy*(x - mean)*rstd           [T13, T19, T20]
+ *   dbias_j   = sum_rows dy                           [T16]
+ * The definition's incoming-gradient add (its T2) is not part of this
+ * backward.  weight may be NULL (weight = 1).  dweight/dbias may be NULL.
+ */
+int oracle_layernorm_backward(int64_t rows, int64_t cols,
+                              const double *x, const double *dy,
+                              const double *mean, const double *rstd,
+                              const double *w,
+                              double *dx, double *dweight, double *dbias)
+{
+    if (rows < 0 || cols <= 0) return -1;
+    const double H = (double)cols;
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *xr = x + (size_t)r * (size_t)cols;
+        const double *dyr = dy + (size_t)r * (size_t)cols;
+        double *dxr = dx + (size_t)r * (size_t)cols;
+        const double mu = mean[r], rs = rstd[r];
+        ksum_t sgx, sg;
+        ks_init(&sgx);
+        ks_init(&sg);
+        for (int64_t j = 0; j < cols; ++j) {
+            double g = dyr[j] * (w ? w[j] : 1.0);
+            ks_add(&sgx, g * (xr[j] - mu));
+            ks_add(&sg, g * rs);
+        }
+        double dvar = -0.5 * rs * rs * rs * ks_value(&sgx);
+        double dmean = -ks_value(&sg);
+        for (int64_t j = 0; j < cols; ++j) {
+            double g = dyr[j] * (w ? w[j] : 1.0);
+            dxr[j] = g * rs + 2.0 * dvar * (xr[j] - mu) / H + dmean / H;
+        }
+    }
+    /* Column sums over rows, each column accumulated in row order. */
+    ksum_t *sw = (ksum_t *)malloc((size_t)cols * sizeof(ksum_t));
+    ksum_t *sb = (ksum_t *)malloc((size_t)cols * sizeof(ksum_t));
+    if (!sw || !sb) { free(sw); free(sb); return -1; }
+    for (int64_t j = 0; j < cols; ++j) { ks_init(&sw[j]); ks_init(&sb[j]); }
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < cols; ++j) {
+            size_t i = (size_t)r * (size_t)cols + (size_t)j;
+            ks_add(&sw[j], dy[i] * (x[i] - mean[r]) * rstd[r]);
+            ks_add(&sb[j], dy[i]);
+        }
+    for (int64_t j = 0; j < cols; ++j) {
+        if (dweight) dweight[j] = ks_value(&sw[j]);
+        if (dbias) dbias[j] = ks_value(&sb[j]);
+    }
+    free(sw);
+    free(sb);
+    return 0;
+}
+
+/*
+ * RMSNorm forward statistic, [RM] rmsnorm_prims:
+ *   rms_r = sqrt(sum_j x^2 / H + eps)
+ */
+int oracle_rmsnorm_rms(int64_t rows, int64_t cols, const double *x, double eps,
+                       double *rms)
+{
+    if (rows < 0 || cols <= 0) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *xr = x + (size_t)r * (size_t)cols;
+        ksum_t s;
+        ks_init(&s);
+        for (int64_t j = 0; j < cols; ++j) ks_add(&s, xr[j] * xr[j]);
+        rms[r] = sqrt(ks_value(&s) / (double)cols + eps);
+    }
+    return 0;
+}
+
+/*
+ * RMSNorm backward, following [RM]'s pre-generated rmsnorm_bwd_fusion step by
+ * step (tensor names of that definition in brackets), with the saved rms:
+ *   rinv = 1/rms                                  [T15]
+ *   g    = dy * w                                 [T24]
+ *   s_r  = sum_j (-g * x / rms^2)                 [T29, T30, T32..T35]
+ *   t_r  = s_r / (2*rms) / H                      [T43..T49]
+ *   dx   = g*rinv + 2*t_r*x                       [T28, T59, T62, T63]
+ *   dweight_j = sum_rows dy * x * rinv            [T16, T23, T25]
+ * which is dx = g/rms - x*sum(g*x)/(H*rms^3).
+ * rms may be NULL: it is then recomputed from x with eps (oracle_rmsnorm_rms).
+ * dweight may be NULL.
+ */
+int oracle_rmsnorm_backward(int64_t rows, int64_t cols,
+                            const double *x, const double *dy, const double *w,
+                            const double *rms_saved, double eps,
+                            double *dx, double *dweight)
+{
+    if (rows < 0 || cols <= 0) return -1;
+    const double H = (double)cols;
+    double *rms = (double *)malloc((size_t)(rows > 0 ? rows : 1) * sizeof(double));
+    ksum_t *sw = (ksum_t *)malloc((size_t)cols * sizeof(ksum_t));
+    if (!rms || !sw) { free(rms); free(sw); return -1; }
+    if (rms_saved) {
+        for (int64_t r = 0; r < rows; ++r) rms[r] = rms_saved[r];
+    } else {
+        oracle_rmsnorm_rms(rows, cols, x, eps, rms);
+    }
+    for (int64_t j = 0; j < cols; ++j) ks_init(&sw[j]);
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *xr = x + (size_t)r * (size_t)cols;
+        const double *dyr = dy + (size_t)r * (size_t)cols;
+        double *dxr = dx + (size_t)r * (size_t)cols;
+        const double rinv = 1.0 / rms[r];
+        ksum_t s;
+        ks_init(&s);
+        for (int64_t j = 0; j < cols; ++j) {
+            double g = dyr[j] * w[j];
+            ks_add(&s, -g * xr[j] / (rms[r] * rms[r]));
+        }
+        double t = ks_value(&s) / (2.0 * rms[r]) / H;
+        for (int64_t j = 0; j < cols; ++j) {
+            double g = dyr[j] * w[j];
+            dxr[j] = g * rinv + 2.0 * t * xr[j];
+            ks_add(&sw[j], dyr[j] * xr[j] * rinv);
+        }
+    }
+    if (dweight)
+        for (int64_t j = 0; j < cols; ++j) dweight[j] = ks_value(&sw[j]);
+    free(rms);
+    free(sw);
+    return 0;
+}

@@ -1,0 +1,248 @@
+"""Pins for the oracle's LayerNorm and RMSNorm backward (CPU only).
+
+Pins: PyTorch's fp64 CPU F.layer_norm / F.rms_norm with autograd, central
+finite differences of the forwards written out here, the shift/scale
+invariants with their eps closed forms, exact rational arithmetic on tiny
+rows, and special cases.
+"""
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from bwd_bn_stats_amd import workloads as wl
+
+
+def _rel(a, b, floor=1e-300):
+    """Normwise relative difference; floor bounds the denominator below (for
+    outputs that are exactly zero by construction, e.g. a one-column row)."""
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), floor))
+
+
+def _dsqrt(q: Fraction) -> Fraction:
+    getcontext().prec = 60
+    return Fraction((Decimal(q.numerator) / Decimal(q.denominator)).sqrt())
+
+
+# ---------------------------------------------------------------- LayerNorm
+
+@pytest.mark.parametrize("rows,cols,seed", [(3, 7, 1), (16, 1600, 1003), (5, 1, 2), (9, 33, 4)])
+def test_ln_matches_torch_fp64(oracle_mod, rows, cols, seed):
+    c = wl.rows_case(rows, cols, x_t=wl.F32, dy_t=wl.BF16, w_t=wl.BF16, seed=seed, with_bias=True)
+    x, dy, w, b = c.x.value, c.dy.value, c.w.value, c.b.value
+    mean, rstd = oracle_mod.layernorm_stats(x, eps=c.eps)
+    tv, tm = torch.var_mean(torch.tensor(x), dim=1, unbiased=False)
+    assert _rel(mean, tm.numpy()) < 1e-13
+    assert _rel(rstd, 1.0 / np.sqrt(tv.numpy() + c.eps)) < 1e-12
+    dx, dw, db = oracle_mod.layernorm_backward(x, dy, mean, rstd, w)
+    xt = torch.tensor(x, requires_grad=True)
+    wt = torch.tensor(w, requires_grad=True)
+    bt = torch.tensor(b, requires_grad=True)
+    y = F.layer_norm(xt, (cols,), wt, bt, eps=c.eps)
+    y.backward(torch.tensor(dy))
+    assert _rel(dx, xt.grad.numpy(), 1.0) < 1e-11
+    assert _rel(dw, wt.grad.numpy(), 1.0) < 1e-12
+    assert _rel(db, bt.grad.numpy()) < 1e-13
+
+
+def test_ln_weight_none_means_one(oracle_mod):
+    c = wl.rows_case(4, 19, x_t=wl.F32, dy_t=wl.F32, w_t=wl.F32, seed=8)
+    x, dy = c.x.value, c.dy.value
+    mean, rstd = oracle_mod.layernorm_stats(x)
+    a = oracle_mod.layernorm_backward(x, dy, mean, rstd, None)
+    b = oracle_mod.layernorm_backward(x, dy, mean, rstd, np.ones(19))
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_ln_finite_differences(oracle_mod):
+    rng = np.random.default_rng(21)
+    R, H, eps = 3, 7, 1e-5
+    x = rng.normal(0.5, 1.5, size=(R, H))
+    dy = rng.normal(size=(R, H))
+    w = rng.uniform(0.5, 1.5, H)
+    b = rng.normal(size=H)
+
+    def fwd(xx, ww, bb):  # y = (x - mean) / sqrt(var + eps) * w + b
+        mu = xx.mean(axis=1, keepdims=True)
+        var = ((xx - mu) ** 2).mean(axis=1, keepdims=True)
+        return (xx - mu) / np.sqrt(var + eps) * ww + bb
+
+    def loss(xx, ww, bb):
+        return float(np.sum(dy * fwd(xx, ww, bb)))
+
+    mean, rstd = oracle_mod.layernorm_stats(x, eps=eps)
+    dx, dw, db = oracle_mod.layernorm_backward(x, dy, mean, rstd, w)
+    fd = np.zeros_like(x)
+    for idx in np.ndindex(x.shape):
+        h = 1e-6 * (1 + abs(x[idx]))
+        xp, xm = x.copy(), x.copy()
+        xp[idx] += h
+        xm[idx] -= h
+        fd[idx] = (loss(xp, w, b) - loss(xm, w, b)) / (2 * h)
+    assert _rel(dx, fd) < 1e-7
+    fdw, fdb = np.zeros(H), np.zeros(H)
+    for j in range(H):
+        e = np.zeros(H)
+        e[j] = 1e-6
+        fdw[j] = (loss(x, w + e, b) - loss(x, w - e, b)) / 2e-6
+        fdb[j] = (loss(x, w, b + e) - loss(x, w, b - e)) / 2e-6
+    assert _rel(dw, fdw) < 1e-7
+    assert _rel(db, fdb) < 1e-7
+
+
+def test_ln_invariants(oracle_mod):
+    c = wl.ln_bwd(rows=64)
+    x, dy, w = c.x.value, c.dy.value, c.w.value
+    mean, rstd = oracle_mod.layernorm_stats(x, eps=c.eps)
+    dx, dw, db = oracle_mod.layernorm_backward(x, dy, mean, rstd, w)
+    xhat = (x - mean[:, None]) * rstd[:, None]
+    g = dy * w
+    mag = np.abs(dx).max(axis=1) * x.shape[1]
+    assert np.all(np.abs(dx.sum(axis=1)) < 1e-13 * mag)
+    lhs = (dx * xhat).sum(axis=1)
+    rhs = c.eps * rstd ** 3 * (g * xhat).sum(axis=1)
+    assert np.all(np.abs(lhs - rhs) < 1e-12 * mag)
+    # closed forms of the parameter gradients
+    assert _rel(db, dy.sum(axis=0)) < 1e-13
+    assert _rel(dw, (dy * xhat).sum(axis=0)) < 1e-12
+
+
+def test_ln_exact_rational_given_stats(oracle_mod):
+    """Saved mean/rstd that are not the row's own statistics (the backward
+    takes them as inputs): the oracle equals the definition's formula
+    evaluated exactly."""
+    rng = np.random.default_rng(9)
+    R, H = 2, 5
+    x = np.round(rng.normal(size=(R, H)), 3)
+    dy = np.round(rng.normal(size=(R, H)), 3)
+    w = np.round(rng.uniform(0.5, 1.5, H), 3)
+    mean = np.array([0.125, -0.25])
+    rstd = np.array([1.5, 0.75])
+    dx, dw, db = oracle_mod.layernorm_backward(x, dy, mean, rstd, w)
+    for r in range(R):
+        X = [Fraction(float(v)) for v in x[r]]
+        D = [Fraction(float(v)) for v in dy[r]]
+        Wf = [Fraction(float(v)) for v in w]
+        mu, rs = Fraction(float(mean[r])), Fraction(float(rstd[r]))
+        g = [d * ww for d, ww in zip(D, Wf)]
+        xhat = [(v - mu) * rs for v in X]
+        A = sum(g) / H
+        B = sum(gg * xh for gg, xh in zip(g, xhat)) / H
+        want = [rs * (gg - A - xh * B) for gg, xh in zip(g, xhat)]
+        assert max(abs(float(a) - b) for a, b in zip(want, dx[r])) < 1e-14
+    for j in range(H):
+        want_w = sum(Fraction(float(dy[r, j])) * (Fraction(float(x[r, j])) - Fraction(float(mean[r])))
+                     * Fraction(float(rstd[r])) for r in range(R))
+        assert abs(float(want_w) - dw[j]) < 1e-15
+        assert abs(float(sum(Fraction(float(dy[r, j])) for r in range(R))) - db[j]) < 1e-15
+
+
+# ------------------------------------------------------------------ RMSNorm
+
+@pytest.mark.parametrize("rows,cols,seed,dt", [(3, 7, 1, wl.F32), (8, 8192, 1004, wl.BF16),
+                                              (6, 1, 5, wl.F32), (7, 100, 6, wl.BF16)])
+def test_rms_matches_torch_fp64(oracle_mod, rows, cols, seed, dt):
+    c = wl.rows_case(rows, cols, x_t=dt, dy_t=dt, w_t=dt, seed=seed)
+    x, dy, w = c.x.value, c.dy.value, c.w.value
+    rms = oracle_mod.rmsnorm_rms(x, eps=c.eps)
+    assert _rel(rms, np.sqrt((x * x).mean(axis=1) + c.eps)) < 1e-14
+    xt = torch.tensor(x, requires_grad=True)
+    wt = torch.tensor(w, requires_grad=True)
+    y = F.rms_norm(xt, (cols,), wt, eps=c.eps)
+    y.backward(torch.tensor(dy))
+    for saved in (rms, None):
+        dx, dw = oracle_mod.rmsnorm_backward(x, dy, w, saved, eps=c.eps)
+        assert _rel(dx, xt.grad.numpy(), 1.0) < 1e-11
+        assert _rel(dw, wt.grad.numpy(), 1.0) < 1e-12
+
+
+def test_rms_matches_prims_definition(oracle_mod):
+    """rmsnorm_prims of the nvFuser RMSNorm issue: w * (x / sqrt(mean(x^2) + 1e-5)),
+    differentiated by torch autograd."""
+    rng = np.random.default_rng(33)
+    x = rng.normal(size=(4, 64))
+    dy = rng.normal(size=(4, 64))
+    w = rng.uniform(0.5, 1.5, 64)
+    xt = torch.tensor(x, requires_grad=True)
+    wt = torch.tensor(w, requires_grad=True)
+    out = wt * (xt / torch.sqrt((xt ** 2).mean(1, keepdim=True) + 1e-5))
+    out.backward(torch.tensor(dy))
+    dx, dw = oracle_mod.rmsnorm_backward(x, dy, w, None, eps=1e-5)
+    assert _rel(dx, xt.grad.numpy()) < 1e-12
+    assert _rel(dw, wt.grad.numpy()) < 1e-12
+
+
+def test_rms_finite_differences(oracle_mod):
+    rng = np.random.default_rng(23)
+    R, H, eps = 3, 7, 1e-5
+    x = rng.normal(size=(R, H))
+    dy = rng.normal(size=(R, H))
+    w = rng.uniform(0.5, 1.5, H)
+
+    def loss(xx, ww):
+        rms = np.sqrt((xx * xx).mean(axis=1, keepdims=True) + eps)
+        return float(np.sum(dy * ww * xx / rms))
+
+    dx, dw = oracle_mod.rmsnorm_backward(x, dy, w, None, eps=eps)
+    fd = np.zeros_like(x)
+    for idx in np.ndindex(x.shape):
+        h = 1e-6 * (1 + abs(x[idx]))
+        xp, xm = x.copy(), x.copy()
+        xp[idx] += h
+        xm[idx] -= h
+        fd[idx] = (loss(xp, w) - loss(xm, w)) / (2 * h)
+    assert _rel(dx, fd) < 1e-7
+    fdw = np.zeros(H)
+    for j in range(H):
+        e = np.zeros(H)
+        e[j] = 1e-6
+        fdw[j] = (loss(x, w + e) - loss(x, w - e)) / 2e-6
+    assert _rel(dw, fdw) < 1e-7
+
+
+def test_rms_invariant_and_special_cases(oracle_mod):
+    c = wl.rms_bwd(wl.F32, rows=32, cols=512)
+    x, dy, w = c.x.value, c.dy.value, c.w.value
+    rms = oracle_mod.rmsnorm_rms(x, eps=c.eps)
+    dx, _ = oracle_mod.rmsnorm_backward(x, dy, w, rms, eps=c.eps)
+    rinv = 1.0 / rms
+    lhs = (dx * x).sum(axis=1)
+    rhs = c.eps * rinv ** 3 * (dy * w * x).sum(axis=1)
+    mag = np.abs(dx * x).sum(axis=1)
+    assert np.all(np.abs(lhs - rhs) < 1e-12 * mag)
+    assert np.all(np.abs(rhs) > 1e-9 * mag)  # the eps term is present
+    # constant row a: rms = sqrt(a^2 + eps)
+    r = oracle_mod.rmsnorm_rms(np.full((1, 10), -3.0), eps=0.5)
+    assert abs(r[0] - np.sqrt(9.5)) < 1e-15
+    # eps = 0: dx is orthogonal to x, and scaling x leaves dx*x unchanged in shape
+    dx0, _ = oracle_mod.rmsnorm_backward(x, dy, w, None, eps=0.0)
+    assert np.all(np.abs((dx0 * x).sum(axis=1)) < 1e-12 * np.abs(dx0 * x).sum(axis=1))
+    dx2, _ = oracle_mod.rmsnorm_backward(2.0 * x, dy, w, None, eps=0.0)
+    assert _rel(2.0 * dx2, dx0) < 1e-13
+
+
+def test_rms_exact_rational(oracle_mod):
+    rng = np.random.default_rng(19)
+    R, H, eps = 2, 6, 1e-5
+    x = np.round(rng.normal(size=(R, H)), 3)
+    dy = np.round(rng.normal(size=(R, H)), 3)
+    w = np.round(rng.uniform(0.5, 1.5, H), 3)
+    dx, dw = oracle_mod.rmsnorm_backward(x, dy, w, None, eps=eps)
+    want_w = [Fraction(0)] * H
+    for r in range(R):
+        X = [Fraction(float(v)) for v in x[r]]
+        D = [Fraction(float(v)) for v in dy[r]]
+        Wf = [Fraction(float(v)) for v in w]
+        rms = _dsqrt(sum(v * v for v in X) / H + Fraction(eps))
+        g = [d * ww for d, ww in zip(D, Wf)]
+        S = sum(gg * v for gg, v in zip(g, X))
+        want = [gg / rms - v * S / (H * rms ** 3) for gg, v in zip(g, X)]
+        assert max(abs(float(a) - b) for a, b in zip(want, dx[r])) < 1e-14
+        for j in range(H):
+            want_w[j] += D[j] * X[j] / rms
+    assert max(abs(float(a) - b) for a, b in zip(want_w, dw)) < 1e-14
