@@ -1,0 +1,604 @@
+// C ABI of normhip: argument validation, launch planning, per-kernel timing.
+// Every entry point validates all arguments before the first HIP call that
+// could launch work, so a failing call writes nothing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "nh_internal.hpp"
+#include "normhip.h"
+
+using namespace nh;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+nh_status fail(nh_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+nh_status fail(nh_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+nh_status ok()
+{
+    g_last_error.clear();
+    return NH_OK;
+}
+
+nh_status hip_fail(hipError_t e, const char *what)
+{
+    return fail(NH_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;  // exclusive bound: 32-bit device indexing
+
+bool valid_dtype(int t) { return t == NH_F32 || t == NH_BF16; }
+size_t dtype_bytes(int t) { return t == NH_F32 ? 4 : 2; }
+bool aligned(const void *p, size_t a) { return p == nullptr || ((uintptr_t)p % a) == 0; }
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---- device properties, cached per device -----------------------------------
+struct DeviceInfo {
+    bool valid = false;
+    int cus = 0;
+    int threads_per_cu = 0;
+    size_t lds_per_block = 0;
+};
+
+std::mutex g_dev_mu;
+DeviceInfo g_dev[64];
+
+nh_status device_info(DeviceInfo *out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(NH_ERR_HIP, "device id %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (!g_dev[dev].valid) {
+        hipDeviceProp_t p;
+        e = hipGetDeviceProperties(&p, dev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+        g_dev[dev].cus = p.multiProcessorCount;
+        g_dev[dev].threads_per_cu = p.maxThreadsPerMultiProcessor;
+        g_dev[dev].lds_per_block = p.sharedMemPerBlock;
+        g_dev[dev].valid = true;
+    }
+    *out = g_dev[dev];
+    return NH_OK;
+}
+
+// ---- plan overrides ------------------------------------------------------------
+std::atomic<int64_t> g_override_bn_grid_y{0};
+std::atomic<int64_t> g_override_rows_blocks{0};
+
+// ---- BatchNorm planning ----------------------------------------------------------
+// Resident 256-thread block slots of the device: CUs * (threads per CU / 256),
+// the rule of Aether-ML PR #18's "Reduction grid" section.
+int64_t bn_slots(const DeviceInfo &d)
+{
+    int64_t per_cu = d.threads_per_cu / kBnThreads;
+    if (per_cu < 1) per_cu = 1;
+    return (int64_t)d.cus * per_cu;
+}
+
+int64_t bn_grid_y_for(int64_t units, int64_t C, const DeviceInfo &d)
+{
+    const int64_t ov = g_override_bn_grid_y.load();
+    if (ov > 0) return ov < units ? ov : units;
+    return bn_auto_grid_y(units, C, bn_slots(d));
+}
+
+// Largest grid_y any dtype/alignment can take for this shape (scalar units).
+int64_t bn_grid_y_max(int64_t M, int64_t C, const DeviceInfo &d) { return bn_grid_y_for(M, C, d); }
+
+size_t bn_ws_bytes(int64_t M, int64_t C, const DeviceInfo &d)
+{
+    return round_up((size_t)(2 * bn_grid_y_max(M, C, d) * C) * sizeof(float), 256);
+}
+
+nh_status bn_check_shape(int64_t N, int64_t C, int64_t HW)
+{
+    if (N < 0 || C < 0 || HW < 0) return fail(NH_ERR_SHAPE, "negative size (N=%lld C=%lld HW=%lld)",
+                                              (long long)N, (long long)C, (long long)HW);
+    if (N > 0 && C > 0 && HW > 0 && (N >= kMaxElems || C >= kMaxElems || HW >= kMaxElems ||
+                                     N * C >= kMaxElems || N * C * HW >= kMaxElems))
+        return fail(NH_ERR_SHAPE, "N*C*HW must be below 2^31");
+    return NH_OK;
+}
+
+int bn_vec(int io, int64_t HW, const void *a, const void *b, const void *c)
+{
+    const int v = io == NH_F32 ? 4 : 8;
+    if (HW % v != 0) return 1;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16)) return 1;
+    return v;
+}
+
+// ---- rows planning ---------------------------------------------------------------
+struct RowsPlan {
+    int maxg = 0;   // 0 = generic path
+    int vec = 1;
+    int teams = 1;
+    int blocks = 0;
+};
+
+int64_t rows_blocks_max(int64_t rows, const DeviceInfo &d)
+{
+    const int64_t ov = g_override_rows_blocks.load();
+    int64_t g = ov > 0 ? ov : d.cus;
+    if (g > rows) g = rows;
+    return g;
+}
+
+size_t rows_ws_bytes(int Q, int64_t rows, int64_t cols, const DeviceInfo &d)
+{
+    return round_up((size_t)(Q * rows_blocks_max(rows, d) * cols) * sizeof(float), 256);
+}
+
+RowsPlan rows_plan(int Q, int64_t rows, int64_t cols, int vec, bool vec_ok, const DeviceInfo &d)
+{
+    RowsPlan p;
+    p.vec = vec;
+    const int64_t groups = vec_ok && cols % vec == 0 ? cols / vec : -1;
+    if (groups > 0) {
+        const int64_t per_thread = ceil_div(groups, 256);
+        int mg = 1;
+        while (mg < per_thread) mg <<= 1;
+        // LayerNorm (two column sums) caps a thread at 32 row elements.
+        if (mg <= 8 && (Q == 1 || mg * vec <= 32)) {
+            p.maxg = mg;
+            p.teams = rows_max_threads(mg, vec) / 256;
+            // LDS: row-sum buffer + one team-fold slot of Q*cols floats.
+            const size_t lds_cap = d.lds_per_block < 65536 ? d.lds_per_block : 65536;
+            if ((size_t)(64 + Q * cols) * sizeof(float) > lds_cap) p.teams = 1;
+        }
+    }
+    if (p.maxg == 0) {
+        p.vec = 1;
+        p.teams = 1;
+    }
+    int64_t g = ceil_div(rows, p.teams);
+    const int64_t gmax = rows_blocks_max(rows, d);
+    if (g > gmax) g = gmax;
+    if (g < 1) g = 1;
+    p.blocks = (int)g;
+    return p;
+}
+
+// ---- timing --------------------------------------------------------------------------
+std::atomic<bool> g_timing{false};
+std::mutex g_timing_mu;
+struct TimingRec { int kid; hipEvent_t start, stop; };
+std::vector<TimingRec> g_records;
+std::vector<hipEvent_t> g_event_pool;
+size_t g_pool_used = 0;
+
+hipEvent_t pool_event()
+{
+    if (g_pool_used == g_event_pool.size()) {
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        g_event_pool.push_back(e);
+    }
+    return g_event_pool[g_pool_used++];
+}
+
+} // namespace
+
+namespace nh {
+
+bool timing_on() { return g_timing.load(std::memory_order_relaxed); }
+
+void timing_events(int kid, hipEvent_t *start, hipEvent_t *stop)
+{
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    hipEvent_t a = pool_event(), b = pool_event();
+    if (!a || !b) { *start = *stop = nullptr; return; }
+    g_records.push_back({kid, a, b});
+    *start = a;
+    *stop = b;
+}
+
+} // namespace nh
+
+extern "C" {
+
+const char *nh_status_string(int status)
+{
+    switch (status) {
+    case NH_OK: return "NH_OK";
+    case NH_ERR_NULL: return "NH_ERR_NULL";
+    case NH_ERR_SHAPE: return "NH_ERR_SHAPE";
+    case NH_ERR_DTYPE: return "NH_ERR_DTYPE";
+    case NH_ERR_WORKSPACE: return "NH_ERR_WORKSPACE";
+    case NH_ERR_HIP: return "NH_ERR_HIP";
+    case NH_ERR_ARG: return "NH_ERR_ARG";
+    default: return "NH_ERR_UNKNOWN";
+    }
+}
+
+const char *nh_last_error(void) { return g_last_error.c_str(); }
+
+const char *nh_kernel_name(int k)
+{
+    static const char *names[NH_K_COUNT] = {
+        "bn_stats", "bn_fwd_finalize", "bn_apply", "bn_grad_sums", "bn_bwd_finalize", "bn_dx",
+        "ln_rows", "ln_colsum", "rms_rows", "rms_colsum", "calib"};
+    return (k >= 0 && k < NH_K_COUNT) ? names[k] : "";
+}
+
+// ---- BatchNorm ---------------------------------------------------------------------
+nh_status bn_forward_train_workspace(int64_t N, int64_t C, int64_t HW, size_t *ws_bytes)
+{
+    if (!ws_bytes) return fail(NH_ERR_NULL, "ws_bytes is NULL");
+    nh_status st = bn_check_shape(N, C, HW);
+    if (st != NH_OK) return st;
+    if (N * C * HW == 0) { *ws_bytes = 0; return ok(); }
+    DeviceInfo d;
+    if ((st = device_info(&d)) != NH_OK) return st;
+    *ws_bytes = bn_ws_bytes(N * HW, C, d);
+    return ok();
+}
+
+nh_status bn_backward_workspace(int64_t N, int64_t C, int64_t HW, size_t *ws_bytes)
+{
+    return bn_forward_train_workspace(N, C, HW, ws_bytes);
+}
+
+nh_status bn_forward_train(const void *x, void *y, nh_dtype io, int64_t N, int64_t C, int64_t HW,
+                           const float *gamma, const float *beta, float *running_mean,
+                           float *running_var, float momentum, float eps, float *stats, void *ws,
+                           size_t ws_bytes, void *stream)
+{
+    if (!valid_dtype(io)) return fail(NH_ERR_DTYPE, "io dtype %d", (int)io);
+    nh_status st = bn_check_shape(N, C, HW);
+    if (st != NH_OK) return st;
+    if (N * C * HW == 0) return ok();
+    if (!x || !y || !stats) return fail(NH_ERR_NULL, "x, y and stats are required");
+    const int64_t M = N * HW;
+    if ((running_mean || running_var) && M < 2)
+        return fail(NH_ERR_SHAPE, "running statistics need more than one element per channel");
+    if (!(eps >= 0.f) || !isfinite(eps)) return fail(NH_ERR_ARG, "eps must be finite and >= 0");
+    if (!isfinite(momentum)) return fail(NH_ERR_ARG, "momentum must be finite");
+    DeviceInfo d;
+    if ((st = device_info(&d)) != NH_OK) return st;
+    const size_t need = bn_ws_bytes(M, C, d);
+    if (!ws || ws_bytes < need || !aligned(ws, 16))
+        return fail(NH_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu)", need, ws_bytes);
+
+    BnCall a{};
+    a.io = io;
+    a.N = (int)N;
+    a.C = (int)C;
+    a.HW = (int)HW;
+    a.vec = bn_vec(io, HW, x, y, nullptr);
+    a.grid_y = (int)bn_grid_y_for(N * (HW / a.vec), C, d);
+    a.x = x;
+    a.out = y;
+    a.gamma = gamma;
+    a.beta = beta;
+    a.running_mean = running_mean;
+    a.running_var = running_var;
+    a.momentum = momentum;
+    a.eps = eps;
+    a.stats = stats;
+    a.partials = static_cast<float *>(ws);
+    hipError_t e = bn_forward_launch(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "bn_forward_train launch");
+    return ok();
+}
+
+nh_status bn_backward(const void *dy, const void *x, nh_dtype io, int64_t N, int64_t C, int64_t HW,
+                      const float *stats, void *dx, float *grads, void *ws, size_t ws_bytes,
+                      void *stream)
+{
+    if (!valid_dtype(io)) return fail(NH_ERR_DTYPE, "io dtype %d", (int)io);
+    nh_status st = bn_check_shape(N, C, HW);
+    if (st != NH_OK) return st;
+    if (N * C * HW == 0) return ok();
+    if (!dy || !x || !stats || !grads) return fail(NH_ERR_NULL, "dy, x, stats and grads are required");
+    DeviceInfo d;
+    if ((st = device_info(&d)) != NH_OK) return st;
+    const int64_t M = N * HW;
+    const size_t need = bn_ws_bytes(M, C, d);
+    if (!ws || ws_bytes < need || !aligned(ws, 16))
+        return fail(NH_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu)", need, ws_bytes);
+
+    BnCall a{};
+    a.io = io;
+    a.N = (int)N;
+    a.C = (int)C;
+    a.HW = (int)HW;
+    a.vec = bn_vec(io, HW, x, dy, dx);
+    a.grid_y = (int)bn_grid_y_for(N * (HW / a.vec), C, d);
+    a.x = x;
+    a.dy = dy;
+    a.out = dx;
+    a.stats = const_cast<float *>(stats);
+    a.grads = grads;
+    a.partials = static_cast<float *>(ws);
+    hipError_t e = bn_backward_launch(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "bn_backward launch");
+    return ok();
+}
+
+// ---- LayerNorm / RMSNorm ---------------------------------------------------------------
+static nh_status rows_check_shape(int64_t rows, int64_t cols)
+{
+    if (rows < 0 || cols < 0) return fail(NH_ERR_SHAPE, "negative size (rows=%lld cols=%lld)",
+                                          (long long)rows, (long long)cols);
+    if (rows >= kMaxElems || cols >= kMaxElems || (rows > 0 && cols > 0 && rows * cols >= kMaxElems))
+        return fail(NH_ERR_SHAPE, "rows*cols must be below 2^31");
+    return NH_OK;
+}
+
+nh_status layernorm_backward_workspace(int64_t rows, int64_t cols, size_t *ws_bytes)
+{
+    if (!ws_bytes) return fail(NH_ERR_NULL, "ws_bytes is NULL");
+    nh_status st = rows_check_shape(rows, cols);
+    if (st != NH_OK) return st;
+    if (rows * cols == 0) { *ws_bytes = 0; return ok(); }
+    DeviceInfo d;
+    if ((st = device_info(&d)) != NH_OK) return st;
+    *ws_bytes = rows_ws_bytes(2, rows, cols, d);
+    return ok();
+}
+
+nh_status rmsnorm_backward_workspace(int64_t rows, int64_t cols, size_t *ws_bytes)
+{
+    if (!ws_bytes) return fail(NH_ERR_NULL, "ws_bytes is NULL");
+    nh_status st = rows_check_shape(rows, cols);
+    if (st != NH_OK) return st;
+    if (rows * cols == 0) { *ws_bytes = 0; return ok(); }
+    DeviceInfo d;
+    if ((st = device_info(&d)) != NH_OK) return st;
+    *ws_bytes = rows_ws_bytes(1, rows, cols, d);
+    return ok();
+}
+
+static nh_status rows_run(RowsCall &a, int Q, void *ws, size_t ws_bytes, void *stream)
+{
+    DeviceInfo d;
+    nh_status st = device_info(&d);
+    if (st != NH_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (a.rows == 0) {
+        // No rows: the column sums are exact zeros; the finalize over zero
+        // partial rows writes them.
+        a.blocks = 0;
+        a.partials = nullptr;
+        a.dx = nullptr;
+        a.maxg = 0;
+        hipError_t e = rows_backward_launch(a, s);
+        if (e != hipSuccess) return hip_fail(e, "rows finalize launch");
+        return ok();
+    }
+    const size_t need = rows_ws_bytes(Q, a.rows, a.cols, d);
+    if (!ws || ws_bytes < need || !aligned(ws, 16))
+        return fail(NH_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu)", need, ws_bytes);
+    a.partials = static_cast<float *>(ws);
+    bool vec_ok = true;
+    auto need_align = [&](const void *p, int t) {
+        if (!p) return;
+        const size_t al = (size_t)a.vec * dtype_bytes(t);
+        if (!aligned(p, al < 16 ? al : 16)) vec_ok = false;
+    };
+    need_align(a.x, a.x_t);
+    need_align(a.dy, a.dy_t);
+    need_align(a.dx, a.dx_t);
+    need_align(a.w, a.w_t);
+    const RowsPlan p = rows_plan(Q, a.rows, a.cols, a.vec, vec_ok, d);
+    a.maxg = p.maxg;
+    a.vec = p.vec;
+    a.teams = p.teams;
+    a.blocks = p.blocks;
+    hipError_t e = rows_backward_launch(a, s);
+    if (e != hipSuccess) return hip_fail(e, "rows backward launch");
+    return ok();
+}
+
+nh_status layernorm_backward(const void *dy, nh_dtype dy_t, const void *x, nh_dtype x_t,
+                             const float *mean, const float *rstd, const void *weight,
+                             nh_dtype w_t, int64_t rows, int64_t cols, void *dx, nh_dtype dx_t,
+                             void *dweight, void *dbias, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!valid_dtype(dy_t) || !valid_dtype(x_t) || !valid_dtype(w_t) || !valid_dtype(dx_t))
+        return fail(NH_ERR_DTYPE, "dtypes must be NH_F32 or NH_BF16");
+    nh_status st = rows_check_shape(rows, cols);
+    if (st != NH_OK) return st;
+    if (cols == 0) return ok();
+    if (rows > 0 && (!dy || !x || !mean || !rstd))
+        return fail(NH_ERR_NULL, "dy, x, mean and rstd are required");
+    RowsCall a{};
+    a.kind = 0;
+    a.x_t = x_t;
+    a.dy_t = dy_t;
+    a.w_t = w_t;
+    a.dx_t = dx_t;
+    a.rows = (int)rows;
+    a.cols = (int)cols;
+    a.vec = (x_t == NH_F32 || dy_t == NH_F32 || (dx && dx_t == NH_F32)) ? 4 : 8;
+    a.x = x;
+    a.dy = dy;
+    a.w = weight;
+    a.mean = mean;
+    a.rstd = rstd;
+    a.dx = dx;
+    a.dweight = dweight;
+    a.dbias = dbias;
+    return rows_run(a, 2, ws, ws_bytes, stream);
+}
+
+nh_status rmsnorm_backward(const void *dy, const void *x, nh_dtype t, const float *rms, float eps,
+                           const void *weight, int64_t rows, int64_t cols, void *dx, void *dweight,
+                           void *ws, size_t ws_bytes, void *stream)
+{
+    if (!valid_dtype(t)) return fail(NH_ERR_DTYPE, "dtype must be NH_F32 or NH_BF16");
+    nh_status st = rows_check_shape(rows, cols);
+    if (st != NH_OK) return st;
+    if (cols == 0) return ok();
+    if (rows > 0 && (!dy || !x)) return fail(NH_ERR_NULL, "dy and x are required");
+    if (!rms && (!(eps >= 0.f) || !isfinite(eps)))
+        return fail(NH_ERR_ARG, "eps must be finite and >= 0 when rms is recomputed");
+    RowsCall a{};
+    a.kind = 1;
+    a.x_t = a.dy_t = a.dx_t = a.w_t = t;
+    a.rows = (int)rows;
+    a.cols = (int)cols;
+    a.vec = t == NH_F32 ? 4 : 8;
+    a.x = x;
+    a.dy = dy;
+    a.w = weight;
+    a.rms = rms;
+    a.eps = eps;
+    a.dx = dx;
+    a.dweight = dweight;
+    return rows_run(a, 1, ws, ws_bytes, stream);
+}
+
+// ---- measurement -------------------------------------------------------------------------
+nh_status nh_timing_enable(int on)
+{
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    if (on) {
+        g_records.clear();
+        g_pool_used = 0;
+    }
+    g_timing.store(on != 0);
+    return ok();
+}
+
+nh_status nh_timing_read(int kernel, double *total_ms, int64_t *launches)
+{
+    if (kernel < 0 || kernel >= NH_K_COUNT) return fail(NH_ERR_ARG, "kernel id %d", kernel);
+    if (!total_ms || !launches) return fail(NH_ERR_NULL, "total_ms and launches are required");
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    double tot = 0.0;
+    int64_t n = 0;
+    for (const TimingRec &r : g_records) {
+        if (r.kid != kernel) continue;
+        hipError_t e = hipEventSynchronize(r.stop);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+        float ms = 0.f;
+        e = hipEventElapsedTime(&ms, r.start, r.stop);
+        if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+        tot += ms;
+        ++n;
+    }
+    *total_ms = tot;
+    *launches = n;
+    return ok();
+}
+
+nh_status nh_calib_copy(const void *src, void *dst, size_t bytes, void *stream)
+{
+    if (bytes == 0) return ok();
+    if (!src || !dst) return fail(NH_ERR_NULL, "src and dst are required");
+    DeviceInfo d;
+    nh_status st = device_info(&d);
+    if (st != NH_OK) return st;
+    hipError_t e = calib_copy_launch(src, dst, bytes, (int)bn_slots(d), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "nh_calib_copy launch");
+    return ok();
+}
+
+nh_status nh_calib_add(const float *a, const float *b, float *out, int64_t n, void *stream)
+{
+    if (n < 0) return fail(NH_ERR_SHAPE, "negative n");
+    if (n == 0) return ok();
+    if (!a || !b || !out) return fail(NH_ERR_NULL, "a, b and out are required");
+    DeviceInfo d;
+    nh_status st = device_info(&d);
+    if (st != NH_OK) return st;
+    hipError_t e = calib_add_launch(a, b, out, n, (int)bn_slots(d), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "nh_calib_add launch");
+    return ok();
+}
+
+nh_status nh_bn_plan(int64_t N, int64_t C, int64_t HW, nh_dtype io, int *grid_y)
+{
+    if (!grid_y) return fail(NH_ERR_NULL, "grid_y is NULL");
+    if (!valid_dtype(io)) return fail(NH_ERR_DTYPE, "io dtype %d", (int)io);
+    nh_status st = bn_check_shape(N, C, HW);
+    if (st != NH_OK) return st;
+    if (N * C * HW == 0) { *grid_y = 0; return ok(); }
+    DeviceInfo d;
+    if ((st = device_info(&d)) != NH_OK) return st;
+    const int v = bn_vec(io, HW, nullptr, nullptr, nullptr);
+    *grid_y = (int)bn_grid_y_for(N * (HW / v), C, d);
+    return ok();
+}
+
+nh_status nh_rows_plan(int64_t rows, int64_t cols, int *blocks)
+{
+    if (!blocks) return fail(NH_ERR_NULL, "blocks is NULL");
+    nh_status st = rows_check_shape(rows, cols);
+    if (st != NH_OK) return st;
+    if (rows * cols == 0) { *blocks = 0; return ok(); }
+    DeviceInfo d;
+    if ((st = device_info(&d)) != NH_OK) return st;
+    *blocks = (int)rows_blocks_max(rows, d);
+    return ok();
+}
+
+nh_status nh_plan_override(const char *key, int64_t value)
+{
+    if (!key) return fail(NH_ERR_NULL, "key is NULL");
+    if (value < 0) return fail(NH_ERR_ARG, "value must be >= 0");
+    if (strcmp(key, "bn_grid_y") == 0) g_override_bn_grid_y.store(value);
+    else if (strcmp(key, "rows_blocks") == 0) g_override_rows_blocks.store(value);
+    else return fail(NH_ERR_ARG, "unknown override key '%s'", key);
+    return ok();
+}
+
+nh_status nh_selftest_host(void)
+{
+    // Fast division: exhaustive over small divisors and dividends, plus edges.
+    for (uint32_t d = 1; d <= 4096; ++d) {
+        const FastDiv f = make_fastdiv(d);
+        for (uint32_t n = 0; n < 20000; ++n)
+            if (f.div(n) != n / d) return fail(NH_ERR_ARG, "fastdiv %u/%u", n, d);
+        const uint32_t edges[] = {0x7fffffffu, 0x7ffffffeu, 0x40000000u, 0x3fffffffu,
+                                  d * 1000u - 1u, d * 1000u, d * 1000u + 1u};
+        for (uint32_t n : edges)
+            if (n < 0x80000000u && f.div(n) != n / d) return fail(NH_ERR_ARG, "fastdiv %u/%u", n, d);
+    }
+    uint64_t s = 0x9e3779b97f4a7c15ull;
+    for (int i = 0; i < 2000000; ++i) {
+        s ^= s << 13; s ^= s >> 7; s ^= s << 17;
+        const uint32_t d = (uint32_t)(s % 0x7fffffffull) + 1u;
+        const uint32_t n = (uint32_t)((s >> 32) & 0x7fffffffu);
+        if (make_fastdiv(d).div(n) != n / d) return fail(NH_ERR_ARG, "fastdiv %u/%u", n, d);
+    }
+    // BatchNorm grid: within [1, slots/C] (at least 1), and enough blocks to
+    // fill the slots whenever the channel has the work for them.
+    const int64_t slots = 2048;
+    const int64_t Cs[] = {1, 3, 32, 37, 256, 2048, 5000};
+    const int64_t Us[] = {1, 100, 1023, 1024, 65536, 1 << 20};
+    for (int64_t C : Cs)
+        for (int64_t u : Us) {
+            const int64_t g = bn_auto_grid_y(u, C, slots);
+            const int64_t cap = slots / C > 1 ? slots / C : 1;
+            if (g < 1 || g > cap || g > u) return fail(NH_ERR_ARG, "bn grid %lld for C=%lld u=%lld",
+                                                      (long long)g, (long long)C, (long long)u);
+            if (u >= cap * kBnThreads * kBnUnroll && g != cap)
+                return fail(NH_ERR_ARG, "bn grid underfills: %lld", (long long)g);
+        }
+    return ok();
+}
+
+} // extern "C"

@@ -1,0 +1,185 @@
+// Device-side helpers shared by the normhip kernels (gfx950, wave64).
+//
+// Storage types: `float` for fp32 and `uint16_t` bit patterns for bf16.  All
+// arithmetic happens in fp32 registers; bf16 is widened on load (exact) and
+// narrowed on store with round-to-nearest-even (gfx950 v_cvt_pk_bf16_f32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nh {
+
+constexpr int kWave = 64;
+
+// ---- scalar conversions ---------------------------------------------------
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v)
+{
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+}
+
+// ---- vector loads/stores of V consecutive elements --------------------------
+// p must be aligned to V*sizeof(T) bytes when V > 1.
+
+template <typename T, int V> struct Vec;
+
+template <> struct Vec<float, 1> {
+    static __device__ __forceinline__ void load(const float *p, float (&o)[1]) { o[0] = *p; }
+    static __device__ __forceinline__ void store(float *p, const float (&v)[1]) { *p = v[0]; }
+};
+template <> struct Vec<float, 4> {
+    static __device__ __forceinline__ void load(const float *p, float (&o)[4])
+    {
+        float4 v = *reinterpret_cast<const float4 *>(p);
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    }
+    static __device__ __forceinline__ void store(float *p, const float (&v)[4])
+    {
+        *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+};
+template <> struct Vec<float, 8> {
+    static __device__ __forceinline__ void load(const float *p, float (&o)[8])
+    {
+        float4 a = reinterpret_cast<const float4 *>(p)[0];
+        float4 b = reinterpret_cast<const float4 *>(p)[1];
+        o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+        o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    }
+    static __device__ __forceinline__ void store(float *p, const float (&v)[8])
+    {
+        reinterpret_cast<float4 *>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+        reinterpret_cast<float4 *>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+};
+
+__device__ __forceinline__ void unpack_bf16x2(uint32_t u, float &lo, float &hi)
+{
+    lo = __uint_as_float(u << 16);
+    hi = __uint_as_float(u & 0xffff0000u);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return (uint32_t)from_f32<uint16_t>(lo) | ((uint32_t)from_f32<uint16_t>(hi) << 16);
+}
+
+template <> struct Vec<uint16_t, 1> {
+    static __device__ __forceinline__ void load(const uint16_t *p, float (&o)[1]) { o[0] = to_f32(*p); }
+    static __device__ __forceinline__ void store(uint16_t *p, const float (&v)[1]) { *p = from_f32<uint16_t>(v[0]); }
+};
+template <> struct Vec<uint16_t, 4> {
+    static __device__ __forceinline__ void load(const uint16_t *p, float (&o)[4])
+    {
+        uint2 u = *reinterpret_cast<const uint2 *>(p);
+        unpack_bf16x2(u.x, o[0], o[1]);
+        unpack_bf16x2(u.y, o[2], o[3]);
+    }
+    static __device__ __forceinline__ void store(uint16_t *p, const float (&v)[4])
+    {
+        *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    }
+};
+template <> struct Vec<uint16_t, 8> {
+    static __device__ __forceinline__ void load(const uint16_t *p, float (&o)[8])
+    {
+        uint4 u = *reinterpret_cast<const uint4 *>(p);
+        unpack_bf16x2(u.x, o[0], o[1]);
+        unpack_bf16x2(u.y, o[2], o[3]);
+        unpack_bf16x2(u.z, o[4], o[5]);
+        unpack_bf16x2(u.w, o[6], o[7]);
+    }
+    static __device__ __forceinline__ void store(uint16_t *p, const float (&v)[8])
+    {
+        *reinterpret_cast<uint4 *>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                   pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    }
+};
+
+template <typename T, int V>
+__device__ __forceinline__ void load_vec(const T *p, float (&o)[V]) { Vec<T, V>::load(p, o); }
+template <typename T, int V>
+__device__ __forceinline__ void store_vec(T *p, const float (&v)[V]) { Vec<T, V>::store(p, v); }
+
+// ---- packed storage of V loaded elements -----------------------------------------
+// Keeps a loaded vector in its storage form (bf16 stays two-per-register) and
+// widens one element at a time, so a row held across a reduction costs
+// V*sizeof(T) bytes of registers, not V*4.
+template <typename T, int V> struct Raw;
+
+template <int V> struct Raw<float, V> {
+    float v[V];
+    __device__ __forceinline__ void load(const float *p) { Vec<float, V>::load(p, v); }
+    __device__ __forceinline__ float get(int e) const { return v[e]; }
+};
+
+template <int V> struct Raw<uint16_t, V> {
+    static_assert(V == 4 || V == 8, "bf16 groups hold 4 or 8 elements");
+    uint32_t u[V / 2];
+    __device__ __forceinline__ void load(const uint16_t *p)
+    {
+        if constexpr (V == 8) {
+            uint4 t = *reinterpret_cast<const uint4 *>(p);
+            u[0] = t.x; u[1] = t.y; u[2] = t.z; u[3] = t.w;
+        } else {
+            uint2 t = *reinterpret_cast<const uint2 *>(p);
+            u[0] = t.x; u[1] = t.y;
+        }
+    }
+    __device__ __forceinline__ float get(int e) const
+    {
+        const uint32_t w = u[e >> 1];
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+
+// ---- wave64 reductions ------------------------------------------------------
+// Butterfly over xor distances 32..1: every lane ends with the same bits
+// (IEEE addition is commutative, so the two partners of each exchange form
+// identical sums), and the order is fixed, so results repeat run to run.
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// ---- fast unsigned division by a run-time invariant --------------------------
+// Granlund & Montgomery, "Division by invariant integers using
+// multiplication" (PLDI 1994): with s = ceil(log2 d) and
+// m = floor(2^32 * (2^s - d) / d) + 1, n / d = (mulhi(n, m) + n) >> s.
+// The sum mulhi(n, m) + n stays below 2^32 for n < 2^31, the only range used.
+struct FastDiv {
+    uint32_t d;
+    uint32_t m;
+    uint32_t s;
+
+    __host__ __device__ __forceinline__ uint32_t div(uint32_t n) const
+    {
+#if defined(__HIP_DEVICE_COMPILE__)
+        uint32_t hi = __umulhi(n, m);
+#else
+        uint32_t hi = (uint32_t)(((uint64_t)n * (uint64_t)m) >> 32);
+#endif
+        return (hi + n) >> s;
+    }
+};
+
+inline FastDiv make_fastdiv(uint32_t d)
+{
+    FastDiv f;
+    f.d = d;
+    f.s = 0;
+    while ((1ull << f.s) < (uint64_t)d) ++f.s;
+    f.m = (uint32_t)((((1ull << 32) * ((1ull << f.s) - (uint64_t)d)) / (uint64_t)d) + 1ull);
+    return f;
+}
+
+} // namespace nh

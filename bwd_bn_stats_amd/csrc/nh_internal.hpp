@@ -1,0 +1,95 @@
+// Host-side interface between the C ABI (api.cpp) and the kernel sources.
+#pragma once
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nh_device.hpp"
+#include "normhip.h"
+
+namespace nh {
+
+// ---- per-kernel timing (api.cpp) -------------------------------------------
+bool timing_on();
+// Hands out a start/stop event pair recorded under kernel id `kid`.
+void timing_events(int kid, hipEvent_t *start, hipEvent_t *stop);
+
+// Launch through hipExtLaunchKernel so that, with timing on, the dispatch
+// packet itself carries the start/stop timestamps.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(int kid, void (*kernel)(KArgs...), dim3 grid, dim3 block,
+                         uint32_t shmem, hipStream_t stream, Args... args)
+{
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (timing_on()) timing_events(kid, &e0, &e1);
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, e0, e1, 0u,
+                          static_cast<KArgs>(args)...);
+    return hipGetLastError();
+}
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---- BatchNorm -------------------------------------------------------------
+constexpr int kBnThreads = 256;
+constexpr int kBnUnroll = 4;     // vector units in flight per thread
+
+// Blocks per channel for a channel of `units` vector units: enough blocks
+// that all C*grid_y blocks fill the device's resident slots once, but no
+// block gets less than one full unrolled sweep of its threads.
+inline int64_t bn_auto_grid_y(int64_t units, int64_t C, int64_t slots)
+{
+    int64_t per_channel = slots / (C > 0 ? C : 1);
+    if (per_channel < 1) per_channel = 1;
+    int64_t want = ceil_div(units, (int64_t)kBnThreads * kBnUnroll);
+    if (want < 1) want = 1;
+    return want < per_channel ? want : per_channel;
+}
+
+struct BnCall {
+    int io;              // 0 fp32, 1 bf16
+    int N, C, HW;
+    int vec;             // vector width in elements (1, 4 or 8)
+    int grid_y;          // blocks per channel of the reduction and elementwise passes
+    const void *x;
+    const void *dy;      // backward only
+    void *out;           // y (forward) or dx (backward; may be NULL)
+    const float *gamma, *beta;
+    float *running_mean, *running_var;
+    float momentum, eps;
+    float *stats;        // [4, C]
+    float *grads;        // [4, C] (backward)
+    float *partials;     // [2, grid_y, C]
+};
+
+hipError_t bn_forward_launch(const BnCall &a, hipStream_t s);
+hipError_t bn_backward_launch(const BnCall &a, hipStream_t s);
+
+// ---- LayerNorm / RMSNorm rows -------------------------------------------------
+struct RowsCall {
+    int kind;            // 0 LayerNorm, 1 RMSNorm
+    int x_t, dy_t, w_t, dx_t;
+    int rows, cols;
+    int blocks;          // G: column-partial rows
+    int teams;           // 256-thread teams per block (vector path)
+    int maxg;            // 16-byte groups per thread per row (vector path); 0 = generic path
+    int vec;             // elements per group
+    const void *x, *dy, *w;
+    const float *mean, *rstd;  // LayerNorm
+    const float *rms;          // RMSNorm (NULL: recompute)
+    float eps;
+    void *dx, *dweight, *dbias;
+    float *partials;     // [Q, G, cols]
+};
+
+hipError_t rows_backward_launch(const RowsCall &a, hipStream_t s);
+
+// Block-size bound of a vector row-kernel variant: up to 4 teams when a
+// thread holds at most 16 elements of a row, else 2 (register budget).
+constexpr int rows_max_threads(int maxg, int vec) { return maxg * vec <= 16 ? 1024 : 512; }
+
+// ---- calibration --------------------------------------------------------------
+hipError_t calib_copy_launch(const void *src, void *dst, size_t bytes, int slots, hipStream_t s);
+hipError_t calib_add_launch(const float *a, const float *b, float *o, int64_t n, int slots, hipStream_t s);
+
+} // namespace nh

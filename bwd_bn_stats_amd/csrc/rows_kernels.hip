@@ -1,0 +1,526 @@
+// LayerNorm and RMSNorm backward over the last dimension of [rows, H].
+//
+// Definitions: NVIDIA/Fuser issue #1473 ("Why is LayerNorm Backward
+// Segmenting?", the layer_norm backward definition) and NVIDIA/Fuser issue
+// #3629 ("Performance gap between manual nvfuser definition and thunder.jit
+// for rmsnorm", rmsnorm_bwd_fusion):
+//   LayerNorm: xhat = (x - mean)*rstd, g = dy*w,
+//              dx = rstd*(g - sum g/H - xhat*sum(g*xhat)/H),
+//              dweight_j = sum_rows dy*xhat, dbias_j = sum_rows dy
+//   RMSNorm:   rinv = 1/rms, g = dy*w,
+//              dx = rinv*g - x*rinv^3*sum(g*x)/H, dweight_j = sum_rows dy*x*rinv
+//
+// Design (one pass over x and dy; the row stays in registers):
+//   * A team of 256 threads (4 waves) owns one row at a time.  Thread t of a
+//     team owns the 16-byte column groups t, t+256, ... (at most MAXG of
+//     them), the same columns for every row it visits, so it keeps the
+//     weight and its share of the column sums (the dweight/dbias split over
+//     rows) in registers across rows.
+//   * A block holds `teams` teams; block b's teams take rows
+//     (it*G + b)*teams + team for it = 0, 1, ...  Row sums are wave
+//     butterflies followed by a fixed-order add of the 4 wave results
+//     through LDS, one block barrier per row step.
+//   * After its last row, the block folds its teams' column sums in team
+//     order through LDS and writes one row of partials[Q, G, H].
+//   * rows_colsum_kernel sums the G partial rows of each column in fp64, in
+//     index order, and rounds to the weight's dtype.
+// No atomics: every output has one writer and a fixed summation order.
+//
+// Rows whose width is not a multiple of the group, misaligned pointers, or
+// rows wider than 8 groups per thread take rows_generic_kernel: the same
+// arithmetic with scalar accesses, two reads of each row (the second mostly
+// from cache) and the column sums kept in the block's own partial row.
+#include "nh_internal.hpp"
+
+namespace nh {
+
+constexpr int kTeam = 256;
+constexpr int kTeamWaves = kTeam / kWave;
+constexpr int kMaxTeams = 4;
+constexpr int kRedFloats = 2 * kMaxTeams * kTeamWaves * 2;  // double-buffered row sums
+
+__device__ __forceinline__ float load_param(const void *w, int w_bf16, int col)
+{
+    return w_bf16 ? to_f32(static_cast<const uint16_t *>(w)[col]) : static_cast<const float *>(w)[col];
+}
+
+// The weight group of a thread, widened to fp32 once per kernel (NULL: 1.0).
+template <int VEC>
+struct WeightGroup {
+    float v[VEC];
+    __device__ __forceinline__ void load(const void *w, int w_bf16, int col)
+    {
+        if (w == nullptr) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) v[e] = 1.f;
+        } else if (w_bf16) {
+            load_vec<uint16_t, VEC>(static_cast<const uint16_t *>(w) + col, v);
+        } else {
+            load_vec<float, VEC>(static_cast<const float *>(w) + col, v);
+        }
+    }
+    __device__ __forceinline__ float get(int e) const { return v[e]; }
+};
+
+// Fixed-order sum of the 4 wave results of a team for two quantities.
+__device__ __forceinline__ void team_sum2(float *red, int team, int wave, int lane,
+                                          float &a, float &b)
+{
+    a = wave_sum(a);
+    b = wave_sum(b);
+    if (lane == 0) {
+        red[(team * kTeamWaves + wave) * 2 + 0] = a;
+        red[(team * kTeamWaves + wave) * 2 + 1] = b;
+    }
+    __syncthreads();
+    float sa = red[(team * kTeamWaves) * 2 + 0];
+    float sb = red[(team * kTeamWaves) * 2 + 1];
+#pragma unroll
+    for (int w = 1; w < kTeamWaves; ++w) {
+        sa += red[(team * kTeamWaves + w) * 2 + 0];
+        sb += red[(team * kTeamWaves + w) * 2 + 1];
+    }
+    a = sa;
+    b = sb;
+}
+
+// Folds the teams' column sums into team 0 in team order (slot: Q*H floats),
+// then team 0 writes the block's partial row.
+template <int VEC, int MAXG, int Q>
+__device__ __forceinline__ void fold_and_write(float (&p)[Q][MAXG][VEC], float *slot, int teams,
+                                               int team, int tt, int Gr, int H, int G,
+                                               float *__restrict__ partials)
+{
+    for (int t = 1; t < teams; ++t) {
+        __syncthreads();
+        if (team == t) {
+#pragma unroll
+            for (int k = 0; k < MAXG; ++k) {
+                const int grp = tt + k * kTeam;
+                if (grp < Gr)
+#pragma unroll
+                    for (int q = 0; q < Q; ++q)
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) slot[q * H + grp * VEC + e] = p[q][k][e];
+            }
+        }
+        __syncthreads();
+        if (team == 0) {
+#pragma unroll
+            for (int k = 0; k < MAXG; ++k) {
+                const int grp = tt + k * kTeam;
+                if (grp < Gr)
+#pragma unroll
+                    for (int q = 0; q < Q; ++q)
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) p[q][k][e] += slot[q * H + grp * VEC + e];
+            }
+        }
+    }
+    if (team == 0) {
+#pragma unroll
+        for (int k = 0; k < MAXG; ++k) {
+            const int grp = tt + k * kTeam;
+            if (grp < Gr)
+#pragma unroll
+                for (int q = 0; q < Q; ++q)
+                    store_vec<float, VEC>(partials + ((size_t)q * G + blockIdx.x) * H + grp * VEC, p[q][k]);
+        }
+    }
+}
+
+// ---- LayerNorm, vector path ----------------------------------------------------
+template <typename TX, typename TDY, typename TDX, int VEC, int MAXG, int MAXT>
+__global__ void __launch_bounds__(MAXT)
+ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
+               const float *__restrict__ mean, const float *__restrict__ rstd,
+               const void *__restrict__ w, int w_bf16, int rows, int H,
+               TDX *__restrict__ dx, float *__restrict__ partials, int want_cols)
+{
+    extern __shared__ float lds[];
+    float *red = lds;
+    float *slot = lds + kRedFloats;
+    const int teams = blockDim.x / kTeam;
+    const int team = threadIdx.x / kTeam;
+    const int tt = threadIdx.x - team * kTeam;
+    const int wave = tt / kWave;
+    const int lane = tt & (kWave - 1);
+    const int G = gridDim.x;
+    const int Gr = H / VEC;
+    const float invH = 1.0f / (float)H;
+
+    WeightGroup<VEC> wv[MAXG];
+    float p[2][MAXG][VEC];
+#pragma unroll
+    for (int k = 0; k < MAXG; ++k) {
+        const int grp = tt + k * kTeam;
+        if (grp < Gr) wv[k].load(w, w_bf16, grp * VEC);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) { p[0][k][e] = 0.f; p[1][k][e] = 0.f; }
+    }
+
+    const int iters = (int)ceil_div(rows, (int64_t)G * teams);
+    for (int it = 0; it < iters; ++it) {
+        const int r = (it * G + (int)blockIdx.x) * teams + team;
+        const bool active = r < rows;
+        Raw<TX, VEC> xv[MAXG];
+        Raw<TDY, VEC> dv[MAXG];
+        const size_t rowoff = (size_t)r * H;
+#pragma unroll
+        for (int k = 0; k < MAXG; ++k) {
+            const int grp = tt + k * kTeam;
+            if (active && grp < Gr) {
+                xv[k].load(x + rowoff + grp * VEC);
+                dv[k].load(dy + rowoff + grp * VEC);
+            }
+        }
+        const float mu = active ? mean[r] : 0.f;
+        const float rs = active ? rstd[r] : 0.f;
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int k = 0; k < MAXG; ++k) {
+            const int grp = tt + k * kTeam;
+            if (active && grp < Gr) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const float d = dv[k].get(e);
+                    const float xh = (xv[k].get(e) - mu) * rs;
+                    const float g = d * wv[k].get(e);
+                    a += g;
+                    b = fmaf(g, xh, b);
+                    p[0][k][e] = fmaf(d, xh, p[0][k][e]);
+                    p[1][k][e] += d;
+                }
+            }
+        }
+        team_sum2(red + (it & 1) * (kRedFloats / 2), team, wave, lane, a, b);
+        if (active && dx != nullptr) {
+            const float ca = a * invH, cb = b * invH;
+#pragma unroll
+            for (int k = 0; k < MAXG; ++k) {
+                const int grp = tt + k * kTeam;
+                if (grp < Gr) {
+                    float o[VEC];
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) {
+                        const float xh = (xv[k].get(e) - mu) * rs;
+                        const float g = dv[k].get(e) * wv[k].get(e);
+                        o[e] = rs * fmaf(-xh, cb, g - ca);
+                    }
+                    store_vec<TDX, VEC>(dx + rowoff + grp * VEC, o);
+                }
+            }
+        }
+    }
+    if (want_cols) fold_and_write<VEC, MAXG, 2>(p, slot, teams, team, tt, Gr, H, G, partials);
+}
+
+// ---- RMSNorm, vector path ----------------------------------------------------
+template <typename T, int VEC, int MAXG, int MAXT>
+__global__ void __launch_bounds__(MAXT)
+rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
+                const float *__restrict__ rms, float eps, const void *__restrict__ w,
+                int w_bf16, int rows, int H, T *__restrict__ dx,
+                float *__restrict__ partials, int want_cols)
+{
+    extern __shared__ float lds[];
+    float *red = lds;
+    float *slot = lds + kRedFloats;
+    const int teams = blockDim.x / kTeam;
+    const int team = threadIdx.x / kTeam;
+    const int tt = threadIdx.x - team * kTeam;
+    const int wave = tt / kWave;
+    const int lane = tt & (kWave - 1);
+    const int G = gridDim.x;
+    const int Gr = H / VEC;
+    const float invH = 1.0f / (float)H;
+
+    WeightGroup<VEC> wv[MAXG];
+    float p[1][MAXG][VEC];
+#pragma unroll
+    for (int k = 0; k < MAXG; ++k) {
+        const int grp = tt + k * kTeam;
+        if (grp < Gr) wv[k].load(w, w_bf16, grp * VEC);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) p[0][k][e] = 0.f;
+    }
+
+    const int iters = (int)ceil_div(rows, (int64_t)G * teams);
+    for (int it = 0; it < iters; ++it) {
+        const int r = (it * G + (int)blockIdx.x) * teams + team;
+        const bool active = r < rows;
+        Raw<T, VEC> xv[MAXG], dv[MAXG];
+        const size_t rowoff = (size_t)r * H;
+#pragma unroll
+        for (int k = 0; k < MAXG; ++k) {
+            const int grp = tt + k * kTeam;
+            if (active && grp < Gr) {
+                xv[k].load(x + rowoff + grp * VEC);
+                dv[k].load(dy + rowoff + grp * VEC);
+            }
+        }
+        float s = 0.f, q = 0.f;  // sum g*x, sum x^2
+#pragma unroll
+        for (int k = 0; k < MAXG; ++k) {
+            const int grp = tt + k * kTeam;
+            if (active && grp < Gr) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const float xe = xv[k].get(e);
+                    s = fmaf(dv[k].get(e) * wv[k].get(e), xe, s);
+                    q = fmaf(xe, xe, q);
+                }
+            }
+        }
+        team_sum2(red + (it & 1) * (kRedFloats / 2), team, wave, lane, s, q);
+        if (active) {
+            const float rinv = rms != nullptr ? 1.0f / rms[r] : 1.0f / sqrtf(fmaf(q, invH, eps));
+            const float c = rinv * rinv * rinv * s * invH;
+#pragma unroll
+            for (int k = 0; k < MAXG; ++k) {
+                const int grp = tt + k * kTeam;
+                if (grp < Gr) {
+                    float o[VEC];
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) {
+                        const float xe = xv[k].get(e);
+                        const float d = dv[k].get(e);
+                        o[e] = fmaf(-xe, c, rinv * (d * wv[k].get(e)));
+                        p[0][k][e] = fmaf(d * xe, rinv, p[0][k][e]);
+                    }
+                    if (dx != nullptr) store_vec<T, VEC>(dx + rowoff + grp * VEC, o);
+                }
+            }
+        }
+    }
+    if (want_cols) fold_and_write<VEC, MAXG, 1>(p, slot, teams, team, tt, Gr, H, G, partials);
+}
+
+// ---- generic path: scalar accesses, any width, any alignment -------------------
+// Block = one team of 256 threads; the block's column sums live in its own
+// partial row (written only by the thread owning the column).
+template <typename TX, typename TDY, typename TDX>
+__global__ void __launch_bounds__(kTeam)
+rows_generic_kernel(int kind, const TDY *__restrict__ dy, const TX *__restrict__ x,
+                    const float *__restrict__ mean, const float *__restrict__ rstd,
+                    const float *__restrict__ rms, float eps,
+                    const void *__restrict__ w, int w_bf16, int rows, int H,
+                    TDX *__restrict__ dx, float *__restrict__ partials, int want_cols)
+{
+    __shared__ float red[kRedFloats];
+    const int tt = threadIdx.x;
+    const int wave = tt / kWave;
+    const int lane = tt & (kWave - 1);
+    const int G = gridDim.x;
+    const int Q = kind == 0 ? 2 : 1;
+    const float invH = 1.0f / (float)H;
+    float *prow0 = partials + (size_t)blockIdx.x * H;
+    float *prow1 = partials + ((size_t)G + blockIdx.x) * H;
+    if (want_cols)
+        for (int j = tt; j < H; j += kTeam) {
+            prow0[j] = 0.f;
+            if (Q == 2) prow1[j] = 0.f;
+        }
+    int it = 0;
+    for (int r = blockIdx.x; r < rows; r += G, ++it) {
+        const size_t rowoff = (size_t)r * H;
+        float a = 0.f, b = 0.f;
+        float mu = 0.f, rs = 0.f;
+        if (kind == 0) { mu = mean[r]; rs = rstd[r]; }
+        for (int j = tt; j < H; j += kTeam) {
+            const float wj = w ? load_param(w, w_bf16, j) : 1.f;
+            const float xv = to_f32(x[rowoff + j]);
+            const float g = to_f32(dy[rowoff + j]) * wj;
+            if (kind == 0) {
+                a += g;
+                b = fmaf(g, (xv - mu) * rs, b);
+            } else {
+                a = fmaf(g, xv, a);
+                b = fmaf(xv, xv, b);
+            }
+        }
+        team_sum2(red + (it & 1) * (kRedFloats / 2), 0, wave, lane, a, b);
+        float rinv = 0.f, c = 0.f;
+        if (kind == 1) {
+            rinv = rms != nullptr ? 1.0f / rms[r] : 1.0f / sqrtf(fmaf(b, invH, eps));
+            c = rinv * rinv * rinv * a * invH;
+        }
+        for (int j = tt; j < H; j += kTeam) {
+            const float wj = w ? load_param(w, w_bf16, j) : 1.f;
+            const float xv = to_f32(x[rowoff + j]);
+            const float d = to_f32(dy[rowoff + j]);
+            const float g = d * wj;
+            float o;
+            if (kind == 0) {
+                const float xh = (xv - mu) * rs;
+                o = rs * fmaf(-xh, b * invH, g - a * invH);
+                if (want_cols) {
+                    prow0[j] = fmaf(d, xh, prow0[j]);
+                    prow1[j] += d;
+                }
+            } else {
+                o = fmaf(-xv, c, rinv * g);
+                if (want_cols) prow0[j] = fmaf(d * xv, rinv, prow0[j]);
+            }
+            if (dx != nullptr) dx[rowoff + j] = from_f32<TDX>(o);
+        }
+    }
+}
+
+// ---- column finalize: fp64 fixed-order sum of the G partial rows -------------
+constexpr int kColX = 64;   // columns per block
+constexpr int kColY = 16;   // slices of the G partial rows
+template <typename TOUT>
+__global__ void __launch_bounds__(kColX * kColY)
+rows_colsum_kernel(const float *__restrict__ partials, int G, int H, TOUT *__restrict__ out0,
+                   TOUT *__restrict__ out1)
+{
+    __shared__ double acc[kColY][kColX];
+    const int q = blockIdx.y;
+    TOUT *out = q == 0 ? out0 : out1;
+    if (out == nullptr) return;  // uniform across the block
+    const int tx = threadIdx.x % kColX;
+    const int ty = threadIdx.x / kColX;
+    const int j = blockIdx.x * kColX + tx;
+    double s = 0.0;
+    if (j < H)
+        for (int b = ty; b < G; b += kColY) s += (double)partials[((size_t)q * G + b) * H + j];
+    acc[ty][tx] = s;
+    __syncthreads();
+    if (ty == 0 && j < H) {
+        double t = acc[0][tx];
+#pragma unroll
+        for (int y = 1; y < kColY; ++y) t += acc[y][tx];
+        out[j] = from_f32<TOUT>((float)t);
+    }
+}
+
+// ---- host dispatch ---------------------------------------------------------------
+static inline int lds_bytes(const RowsCall &a)
+{
+    const int Q = a.kind == 0 ? 2 : 1;
+    return (kRedFloats + (a.teams > 1 ? Q * a.cols : 0)) * (int)sizeof(float);
+}
+
+
+template <typename TX, typename TDY, typename TDX, int VEC, int MAXG>
+static hipError_t ln_vec(const RowsCall &a, hipStream_t s)
+{
+    constexpr int MT = rows_max_threads(MAXG, VEC);
+    return launch(NH_K_LN_ROWS, ln_rows_kernel<TX, TDY, TDX, VEC, MAXG, MT>, dim3(a.blocks),
+                  dim3(a.teams * kTeam), (uint32_t)lds_bytes(a), s,
+                  static_cast<const TDY *>(a.dy), static_cast<const TX *>(a.x), a.mean, a.rstd,
+                  a.w, a.w_t, a.rows, a.cols, static_cast<TDX *>(a.dx), a.partials,
+                  (int)(a.dweight != nullptr || a.dbias != nullptr));
+}
+
+template <typename T, int VEC, int MAXG>
+static hipError_t rms_vec(const RowsCall &a, hipStream_t s)
+{
+    constexpr int MT = rows_max_threads(MAXG, VEC);
+    return launch(NH_K_RMS_ROWS, rms_rows_kernel<T, VEC, MAXG, MT>, dim3(a.blocks),
+                  dim3(a.teams * kTeam), (uint32_t)lds_bytes(a), s,
+                  static_cast<const T *>(a.dy), static_cast<const T *>(a.x), a.rms, a.eps, a.w,
+                  a.w_t, a.rows, a.cols, static_cast<T *>(a.dx), a.partials,
+                  (int)(a.dweight != nullptr));
+}
+
+// LayerNorm keeps two column sums per element, so its widest vector variant
+// holds 32 elements per thread (MAXG = 8 only with 4-element groups); the
+// planner sends wider rows to the generic path.
+template <typename TX, typename TDY, typename TDX, int VEC>
+static hipError_t ln_maxg(const RowsCall &a, hipStream_t s)
+{
+    switch (a.maxg) {
+    case 1: return ln_vec<TX, TDY, TDX, VEC, 1>(a, s);
+    case 2: return ln_vec<TX, TDY, TDX, VEC, 2>(a, s);
+    case 4: return ln_vec<TX, TDY, TDX, VEC, 4>(a, s);
+    default:
+        if constexpr (VEC == 4) return ln_vec<TX, TDY, TDX, VEC, 8>(a, s);
+        return hipErrorInvalidValue;
+    }
+}
+
+template <typename T, int VEC>
+static hipError_t rms_maxg(const RowsCall &a, hipStream_t s)
+{
+    switch (a.maxg) {
+    case 1: return rms_vec<T, VEC, 1>(a, s);
+    case 2: return rms_vec<T, VEC, 2>(a, s);
+    case 4: return rms_vec<T, VEC, 4>(a, s);
+    default: return rms_vec<T, VEC, 8>(a, s);
+    }
+}
+
+template <typename TX, typename TDY, typename TDX>
+static hipError_t ln_dispatch_vec(const RowsCall &a, hipStream_t s)
+{
+    return a.vec == 4 ? ln_maxg<TX, TDY, TDX, 4>(a, s) : ln_maxg<TX, TDY, TDX, 8>(a, s);
+}
+
+template <typename TX, typename TDY, typename TDX>
+static hipError_t generic_launch(const RowsCall &a, hipStream_t s)
+{
+    const int want = a.kind == 0 ? (a.dweight != nullptr || a.dbias != nullptr) : (a.dweight != nullptr);
+    return launch(a.kind == 0 ? NH_K_LN_ROWS : NH_K_RMS_ROWS, rows_generic_kernel<TX, TDY, TDX>,
+                  dim3(a.blocks), dim3(kTeam), 0u, s, a.kind, static_cast<const TDY *>(a.dy),
+                  static_cast<const TX *>(a.x), a.mean, a.rstd, a.rms, a.eps, a.w, a.w_t, a.rows,
+                  a.cols, static_cast<TDX *>(a.dx), a.partials, want);
+}
+
+// dtype code 0 = float, 1 = bf16 (uint16_t)
+template <template <typename, typename, typename> class F>
+static hipError_t by_types(int tx, int tdy, int tdx, const RowsCall &a, hipStream_t s)
+{
+    const int code = tx * 4 + tdy * 2 + tdx;
+    switch (code) {
+    case 0: return F<float, float, float>::run(a, s);
+    case 1: return F<float, float, uint16_t>::run(a, s);
+    case 2: return F<float, uint16_t, float>::run(a, s);
+    case 3: return F<float, uint16_t, uint16_t>::run(a, s);
+    case 4: return F<uint16_t, float, float>::run(a, s);
+    case 5: return F<uint16_t, float, uint16_t>::run(a, s);
+    case 6: return F<uint16_t, uint16_t, float>::run(a, s);
+    default: return F<uint16_t, uint16_t, uint16_t>::run(a, s);
+    }
+}
+
+template <typename TX, typename TDY, typename TDX> struct LnVecF {
+    static hipError_t run(const RowsCall &a, hipStream_t s) { return ln_dispatch_vec<TX, TDY, TDX>(a, s); }
+};
+template <typename TX, typename TDY, typename TDX> struct GenericF {
+    static hipError_t run(const RowsCall &a, hipStream_t s) { return generic_launch<TX, TDY, TDX>(a, s); }
+};
+
+template <typename TOUT>
+static hipError_t colsum(const RowsCall &a, int kid, hipStream_t s)
+{
+    const int Q = a.kind == 0 ? 2 : 1;
+    const dim3 grid((unsigned)ceil_div(a.cols, kColX), (unsigned)Q);
+    return launch(kid, rows_colsum_kernel<TOUT>, grid, dim3(kColX * kColY), 0u, s,
+                  (const float *)a.partials, a.blocks, a.cols, static_cast<TOUT *>(a.dweight),
+                  static_cast<TOUT *>(a.kind == 0 ? a.dbias : nullptr));
+}
+
+hipError_t rows_backward_launch(const RowsCall &a, hipStream_t s)
+{
+    // The dx dtype of a skipped dx is irrelevant: use the dy dtype.
+    const int dxt = a.dx != nullptr ? a.dx_t : a.dy_t;
+    hipError_t e = hipSuccess;
+    if (a.rows == 0) {
+        // nothing to launch for the rows; the finalize writes zero sums
+    } else if (a.maxg == 0) {
+        e = by_types<GenericF>(a.x_t, a.dy_t, dxt, a, s);
+    } else if (a.kind == 0) {
+        e = by_types<LnVecF>(a.x_t, a.dy_t, dxt, a, s);
+    } else {
+        e = a.x_t == 0 ? rms_maxg<float, 4>(a, s) : rms_maxg<uint16_t, 8>(a, s);
+    }
+    if (e != hipSuccess) return e;
+    const bool cols = a.kind == 0 ? (a.dweight != nullptr || a.dbias != nullptr) : a.dweight != nullptr;
+    if (!cols) return hipSuccess;
+    const int kid = a.kind == 0 ? NH_K_LN_COLSUM : NH_K_RMS_COLSUM;
+    return a.w_t == 0 ? colsum<float>(a, kid, s) : colsum<uint16_t>(a, kid, s);
+}
+
+} // namespace nh

@@ -1,0 +1,307 @@
+"""Python binding of libnormhip (include/normhip.h): argument marshalling only.
+
+Every computation runs in the library's HIP kernels.  PyTorch supplies device
+memory (torch tensors) and the stream (torch.cuda.current_stream()).  There is
+no fallback: importing the binding without the built library raises.
+
+Functions carry the C ABI's names:
+    bn_forward_train, bn_backward, layernorm_backward, rmsnorm_backward
+plus the workspace queries and measurement helpers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnormhip.so")
+
+F32, BF16 = 0, 1
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+
+KERNELS = ["bn_stats", "bn_fwd_finalize", "bn_apply", "bn_grad_sums", "bn_bwd_finalize", "bn_dx",
+           "ln_rows", "ln_colsum", "rms_rows", "rms_colsum", "calib"]
+
+EXPORTS = [
+    "nh_status_string", "nh_last_error", "nh_kernel_name",
+    "bn_forward_train_workspace", "bn_backward_workspace", "bn_forward_train", "bn_backward",
+    "layernorm_backward_workspace", "layernorm_backward",
+    "rmsnorm_backward_workspace", "rmsnorm_backward",
+    "nh_timing_enable", "nh_timing_read", "nh_calib_copy", "nh_calib_add",
+    "nh_bn_plan", "nh_rows_plan", "nh_plan_override", "nh_selftest_host",
+]
+
+
+class NormHipError(RuntimeError):
+    def __init__(self, status: int, fn: str, msg: str):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)}: {msg}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m bwd_bn_stats_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, sz, f32, p, i32 = ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p, ctypes.c_int
+    psz = ctypes.POINTER(ctypes.c_size_t)
+    sig = {
+        "nh_status_string": (ctypes.c_char_p, [i32]),
+        "nh_last_error": (ctypes.c_char_p, []),
+        "nh_kernel_name": (ctypes.c_char_p, [i32]),
+        "bn_forward_train_workspace": (i32, [i64, i64, i64, psz]),
+        "bn_backward_workspace": (i32, [i64, i64, i64, psz]),
+        "bn_forward_train": (i32, [p, p, i32, i64, i64, i64, p, p, p, p, f32, f32, p, p, sz, p]),
+        "bn_backward": (i32, [p, p, i32, i64, i64, i64, p, p, p, p, sz, p]),
+        "layernorm_backward_workspace": (i32, [i64, i64, psz]),
+        "layernorm_backward": (i32, [p, i32, p, i32, p, p, p, i32, i64, i64, p, i32, p, p, p, sz, p]),
+        "rmsnorm_backward_workspace": (i32, [i64, i64, psz]),
+        "rmsnorm_backward": (i32, [p, p, i32, p, f32, p, i64, i64, p, p, p, sz, p]),
+        "nh_timing_enable": (i32, [i32]),
+        "nh_timing_read": (i32, [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
+        "nh_calib_copy": (i32, [p, p, sz, p]),
+        "nh_calib_add": (i32, [p, p, p, i64, p]),
+        "nh_bn_plan": (i32, [i64, i64, i64, i32, ctypes.POINTER(ctypes.c_int)]),
+        "nh_rows_plan": (i32, [i64, i64, ctypes.POINTER(ctypes.c_int)]),
+        "nh_plan_override": (i32, [ctypes.c_char_p, i64]),
+        "nh_selftest_host": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.nh_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib.nh_last_error().decode()
+
+
+def _check(status: int, fn: str):
+    if status != 0:
+        raise NormHipError(status, fn, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}; float32 or bfloat16 only")
+    return _DT[t.dtype]
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev_tensor(t, name, dtype=None, numel=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    return t
+
+
+def _workspace(nbytes: int, device, workspace):
+    """The caller's workspace tensor as given (the library checks its size),
+    or a new one of the queried size."""
+    if workspace is None and nbytes > 0:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace
+
+
+def _nchw(x: torch.Tensor):
+    if x.dim() < 2:
+        raise ValueError("BatchNorm input must be [N, C, ...]")
+    N, C = x.shape[0], x.shape[1]
+    HW = 1
+    for s in x.shape[2:]:
+        HW *= s
+    return N, C, HW
+
+
+# ---- workspace queries ----------------------------------------------------------
+def bn_forward_train_workspace(N: int, C: int, HW: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib.bn_forward_train_workspace(N, C, HW, ctypes.byref(out)), "bn_forward_train_workspace")
+    return out.value
+
+
+def bn_backward_workspace(N: int, C: int, HW: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib.bn_backward_workspace(N, C, HW, ctypes.byref(out)), "bn_backward_workspace")
+    return out.value
+
+
+def layernorm_backward_workspace(rows: int, cols: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib.layernorm_backward_workspace(rows, cols, ctypes.byref(out)), "layernorm_backward_workspace")
+    return out.value
+
+
+def rmsnorm_backward_workspace(rows: int, cols: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib.rmsnorm_backward_workspace(rows, cols, ctypes.byref(out)), "rmsnorm_backward_workspace")
+    return out.value
+
+
+# ---- BatchNorm ---------------------------------------------------------------------
+def bn_forward_train(x, gamma=None, beta=None, running_mean=None, running_var=None,
+                     momentum: float = 0.1, eps: float = 1e-5, *, y=None, stats=None,
+                     workspace=None):
+    """BatchNorm2d training forward.  Returns (y, stats[4, C])."""
+    _dev_tensor(x, "x")
+    N, C, HW = _nchw(x)
+    f32 = torch.float32
+    for t, n in ((gamma, "gamma"), (beta, "beta"), (running_mean, "running_mean"),
+                 (running_var, "running_var")):
+        _dev_tensor(t, n, f32, C)
+    y = torch.empty_like(x) if y is None else _dev_tensor(y, "y", x.dtype, x.numel())
+    stats = torch.empty((4, C), dtype=f32, device=x.device) if stats is None else \
+        _dev_tensor(stats, "stats", f32, 4 * C)
+    ws = _workspace(bn_forward_train_workspace(N, C, HW), x.device, workspace)
+    nb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.bn_forward_train(_ptr(x), _ptr(y), _dt(x), N, C, HW, _ptr(gamma), _ptr(beta),
+                                _ptr(running_mean), _ptr(running_var), momentum, eps, _ptr(stats),
+                                _ptr(ws), nb, _stream(x.device)), "bn_forward_train")
+    return y, stats
+
+
+def bn_backward(dy, x, stats, *, dx=None, grads=None, need_dx=True, workspace=None):
+    """BatchNorm2d training backward.  Returns (dx or None, grads[4, C])."""
+    _dev_tensor(x, "x")
+    _dev_tensor(dy, "dy", x.dtype, x.numel())
+    N, C, HW = _nchw(x)
+    f32 = torch.float32
+    _dev_tensor(stats, "stats", f32, 4 * C)
+    if need_dx:
+        dx = torch.empty_like(x) if dx is None else _dev_tensor(dx, "dx", x.dtype, x.numel())
+    else:
+        dx = None
+    grads = torch.empty((4, C), dtype=f32, device=x.device) if grads is None else \
+        _dev_tensor(grads, "grads", f32, 4 * C)
+    ws = _workspace(bn_backward_workspace(N, C, HW), x.device, workspace)
+    nb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.bn_backward(_ptr(dy), _ptr(x), _dt(x), N, C, HW, _ptr(stats), _ptr(dx), _ptr(grads),
+                           _ptr(ws), nb, _stream(x.device)), "bn_backward")
+    return dx, grads
+
+
+# ---- LayerNorm / RMSNorm ---------------------------------------------------------------
+def _rows(x):
+    cols = x.shape[-1] if x.dim() > 0 else 1
+    rows = x.numel() // cols if cols else 0
+    return rows, cols
+
+
+def layernorm_backward(dy, x, mean, rstd, weight=None, *, dx_dtype=None, w_dtype=None,
+                       need_dx=True, need_dweight=True, need_dbias=True, dx=None,
+                       dweight=None, dbias=None, workspace=None):
+    """LayerNorm backward over the last dim.  Returns (dx, dweight, dbias)
+    (None for the outputs not requested).  dweight/dbias take the weight's
+    dtype (w_dtype when there is no weight, default float32)."""
+    _dev_tensor(x, "x")
+    _dev_tensor(dy, "dy", None, x.numel())
+    rows, cols = _rows(x)
+    f32 = torch.float32
+    _dev_tensor(mean, "mean", f32, rows)
+    _dev_tensor(rstd, "rstd", f32, rows)
+    _dev_tensor(weight, "weight", None, cols)
+    wdt = weight.dtype if weight is not None else (w_dtype or f32)
+    dxdt = dx_dtype or x.dtype
+    if need_dx:
+        dx = torch.empty(x.shape, dtype=dxdt, device=x.device) if dx is None else \
+            _dev_tensor(dx, "dx", dxdt, x.numel())
+    else:
+        dx = None
+    dweight = (torch.empty(cols, dtype=wdt, device=x.device) if dweight is None else
+               _dev_tensor(dweight, "dweight", wdt, cols)) if need_dweight else None
+    dbias = (torch.empty(cols, dtype=wdt, device=x.device) if dbias is None else
+             _dev_tensor(dbias, "dbias", wdt, cols)) if need_dbias else None
+    ws = _workspace(layernorm_backward_workspace(rows, cols), x.device, workspace)
+    nb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.layernorm_backward(_ptr(dy), _dt(dy), _ptr(x), _dt(x), _ptr(mean), _ptr(rstd),
+                                  _ptr(weight), _DT[wdt], rows, cols, _ptr(dx), _DT[dxdt],
+                                  _ptr(dweight), _ptr(dbias), _ptr(ws), nb, _stream(x.device)),
+           "layernorm_backward")
+    return dx, dweight, dbias
+
+
+def rmsnorm_backward(dy, x, rms=None, weight=None, eps: float = 1e-5, *, need_dx=True,
+                     need_dweight=True, dx=None, dweight=None, workspace=None):
+    """RMSNorm backward over the last dim.  rms=None recomputes rms from x
+    with eps.  Returns (dx, dweight) (None for outputs not requested)."""
+    _dev_tensor(x, "x")
+    _dev_tensor(dy, "dy", x.dtype, x.numel())
+    rows, cols = _rows(x)
+    _dev_tensor(rms, "rms", torch.float32, rows)
+    _dev_tensor(weight, "weight", x.dtype, cols)
+    if need_dx:
+        dx = torch.empty_like(x) if dx is None else _dev_tensor(dx, "dx", x.dtype, x.numel())
+    else:
+        dx = None
+    dweight = (torch.empty(cols, dtype=x.dtype, device=x.device) if dweight is None else
+               _dev_tensor(dweight, "dweight", x.dtype, cols)) if need_dweight else None
+    ws = _workspace(rmsnorm_backward_workspace(rows, cols), x.device, workspace)
+    nb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.rmsnorm_backward(_ptr(dy), _ptr(x), _dt(x), _ptr(rms), eps, _ptr(weight), rows, cols,
+                                _ptr(dx), _ptr(dweight), _ptr(ws), nb, _stream(x.device)),
+           "rmsnorm_backward")
+    return dx, dweight
+
+
+# ---- measurement --------------------------------------------------------------------------
+def timing_enable(on: bool):
+    _check(lib.nh_timing_enable(1 if on else 0), "nh_timing_enable")
+
+
+def timing_read(kernel) -> tuple[float, int]:
+    """(total ms, launches) recorded for a kernel id or name."""
+    kid = KERNELS.index(kernel) if isinstance(kernel, str) else int(kernel)
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(lib.nh_timing_read(kid, ctypes.byref(ms), ctypes.byref(n)), "nh_timing_read")
+    return ms.value, n.value
+
+
+def calib_copy(src, dst):
+    _check(lib.nh_calib_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(),
+                             _stream(src.device)), "nh_calib_copy")
+
+
+def calib_add(a, b, out):
+    _check(lib.nh_calib_add(_ptr(a), _ptr(b), _ptr(out), a.numel(), _stream(a.device)), "nh_calib_add")
+
+
+def bn_plan(N, C, HW, io=F32) -> int:
+    g = ctypes.c_int()
+    _check(lib.nh_bn_plan(N, C, HW, io, ctypes.byref(g)), "nh_bn_plan")
+    return g.value
+
+
+def rows_plan(rows, cols) -> int:
+    g = ctypes.c_int()
+    _check(lib.nh_rows_plan(rows, cols, ctypes.byref(g)), "nh_rows_plan")
+    return g.value
+
+
+def plan_override(key: str, value: int):
+    _check(lib.nh_plan_override(key.encode(), value), "nh_plan_override")

@@ -1,0 +1,261 @@
+/*
+ * normhip: training-mode normalization forward/backward for AMD Instinct
+ * MI355X (gfx950), as a C ABI over hand-written HIP kernels.
+ *
+ * Operations (and the pages that define them):
+ *   bn_forward_train    BatchNorm2d training forward.  Aether-ML PR #18,
+ *                       "perf(batchnorm): device-sized grid, one-pass
+ *                       statistics, finalize kernels": "One-pass statistics"
+ *                       section and the stats / bn_forward_finalize /
+ *                       _bn_apply_ew commit.
+ *   bn_backward         BatchNorm2d training backward.  Same PR, "Backward
+ *                       finalize" section and the bn_backward_finalize commit.
+ *   layernorm_backward  LayerNorm backward over the last dimension with saved
+ *                       mean/rstd.  NVIDIA/Fuser issue #1473, "Why is
+ *                       LayerNorm Backward Segmenting?", the layer_norm
+ *                       backward definition (nvfuser_fusion_id14).
+ *   rmsnorm_backward    RMSNorm backward over the last dimension.
+ *                       NVIDIA/Fuser issue #3629, "Performance gap between
+ *                       manual nvfuser definition and thunder.jit for
+ *                       rmsnorm": rmsnorm_prims and rmsnorm_bwd_fusion.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major buffers on
+ *     the current HIP device (hipGetDevice at call time).  `stream` is a
+ *     hipStream_t of that device passed as void* (NULL = the null stream).
+ *   - The caller owns every buffer, including the workspace: query its size
+ *     with the matching *_workspace function, allocate it, pass it in.  The
+ *     library never allocates, frees or synchronizes device memory in these
+ *     calls.  Workspace needs no initialisation: every slot is written before
+ *     it is read.
+ *   - Calls are asynchronous on `stream`.  Results are bit-identical across
+ *     runs for the same inputs, shape, device and build (no atomics; every
+ *     reduction has a fixed order).
+ *   - In-place is allowed for y == x (forward) and dx == dy (backward); any
+ *     other overlap between outputs and inputs is undefined.
+ *   - Validation happens before any launch.  On an error nothing is written
+ *     and the running statistics are untouched.  Order of checks: dtype,
+ *     shape, empty (a tensor with zero elements returns NH_OK and launches
+ *     nothing; its pointers may be NULL), pointers, argument values,
+ *     workspace.
+ *   - Element counts must be below 2^31 (32-bit index arithmetic on device).
+ *   - Misaligned pointers (not 16-byte aligned) and sizes that are not a
+ *     multiple of the vector width are accepted; they take a scalar path.
+ *   - Arithmetic: inputs are widened to fp32 at load, every reduction
+ *     accumulates in fp32 per thread and combines block partials in fp64,
+ *     outputs are rounded to their storage type at store (bf16: round to
+ *     nearest even).
+ */
+#ifndef NORMHIP_H
+#define NORMHIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NH_F32 = 0,  /* IEEE binary32 */
+    NH_BF16 = 1  /* bfloat16, stored as uint16 bit patterns */
+} nh_dtype;
+
+typedef enum {
+    NH_OK = 0,
+    NH_ERR_NULL = 1,      /* a required pointer is NULL */
+    NH_ERR_SHAPE = 2,     /* negative size, element count >= 2^31, or one element
+                             per channel with running statistics requested */
+    NH_ERR_DTYPE = 3,     /* dtype value not in nh_dtype, or an unsupported mix */
+    NH_ERR_WORKSPACE = 4, /* workspace NULL or smaller than the queried size */
+    NH_ERR_HIP = 5,       /* HIP runtime error (no device, launch failure) */
+    NH_ERR_ARG = 6        /* invalid scalar argument (eps < 0 or NaN, bad id) */
+} nh_status;
+
+/* Static string naming a status code ("NH_OK", ...); never NULL. */
+const char *nh_status_string(int status);
+
+/* Detail message of the last failing call on this host thread ("" if none). */
+const char *nh_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * BatchNorm2d, NCHW, statistics per channel over (N, H, W); HW = H*W,
+ * M = N*HW elements per channel.
+ * ---------------------------------------------------------------------- */
+
+/* Workspace bytes needed by bn_forward_train / bn_backward for this shape on
+ * the current device (the same size serves both calls and both dtypes). */
+nh_status bn_forward_train_workspace(int64_t N, int64_t C, int64_t HW, size_t *ws_bytes);
+nh_status bn_backward_workspace(int64_t N, int64_t C, int64_t HW, size_t *ws_bytes);
+
+/*
+ * Training forward.  Aether-ML PR #18, "One-pass statistics": per channel c
+ * the shifted sums of d = x - x[0,c,0,0] and d^2 give
+ *   mean = x[0,c,0,0] + sum d / M,  var = sum d^2 / M - (sum d / M)^2 (biased,
+ *   clamped at 0),  inv_std = 1/sqrt(var + eps),  scale = gamma*inv_std,
+ * and y = (x - mean)*scale + beta (the centred apply of that PR).
+ *
+ *   x, y          [N, C, HW] of dtype io (y may equal x)
+ *   gamma, beta   fp32 [C]; NULL means gamma = 1 / beta = 0 (affine off)
+ *   running_mean, running_var
+ *                 fp32 [C], updated in place when non-NULL:
+ *                 rm = (1-momentum)*rm + momentum*mean,
+ *                 rv = (1-momentum)*rv + momentum*var*M/(M-1)
+ *                 (PyTorch's rule; M must then be > 1, else NH_ERR_SHAPE)
+ *   stats         fp32 [4, C] out: rows (mean, var, inv_std, scale)
+ *   ws, ws_bytes  workspace from bn_forward_train_workspace
+ */
+nh_status bn_forward_train(const void *x, void *y, nh_dtype io,
+                           int64_t N, int64_t C, int64_t HW,
+                           const float *gamma, const float *beta,
+                           float *running_mean, float *running_var,
+                           float momentum, float eps,
+                           float *stats, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Training backward.  Aether-ML PR #18, "Backward finalize": per channel the
+ * sums sum dy and sum dy*(x - mean) give
+ *   dbeta = sum dy,  dgamma = inv_std * sum dy*(x - mean),
+ *   k1 = -scale*inv_std^2 * sum dy*(x - mean) / M,  k2 = -scale*dbeta / M,
+ * and dx = dy*scale + (x - mean)*k1 + k2.
+ *
+ *   dy, x         [N, C, HW] of dtype io
+ *   stats         fp32 [4, C] as written by bn_forward_train (mean, var,
+ *                 inv_std, scale); var is not read
+ *   dx            [N, C, HW] of dtype io, or NULL to skip the input gradient
+ *                 (dx may equal dy)
+ *   grads         fp32 [4, C] out: rows (dgamma, dbeta, k1, k2)
+ */
+nh_status bn_backward(const void *dy, const void *x, nh_dtype io,
+                      int64_t N, int64_t C, int64_t HW,
+                      const float *stats, void *dx, float *grads,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * LayerNorm / RMSNorm backward over the last dimension of [rows, cols].
+ * dweight/dbias are split over rows into per-block partials in the
+ * workspace and summed by a finalize kernel in a fixed order.
+ * ---------------------------------------------------------------------- */
+
+nh_status layernorm_backward_workspace(int64_t rows, int64_t cols, size_t *ws_bytes);
+
+/*
+ * NVIDIA/Fuser issue #1473, layer_norm backward definition: with
+ * xhat = (x - mean)*rstd and g = dy*weight,
+ *   dx = rstd*(g - sum_j g / H - xhat * sum_j g*xhat / H)
+ *   dweight_j = sum_rows dy*xhat,  dbias_j = sum_rows dy.
+ *
+ *   dy            [rows, cols] of dy_t;   x [rows, cols] of x_t
+ *   mean, rstd    fp32 [rows], the forward's saved statistics
+ *   weight        [cols] of w_t, or NULL (weight = 1)
+ *   dx            [rows, cols] of dx_t, or NULL (skip)
+ *   dweight, dbias [cols] of w_t, each may be NULL (skip)
+ * Every dtype is NH_F32 or NH_BF16, in any combination.
+ */
+nh_status layernorm_backward(const void *dy, nh_dtype dy_t,
+                             const void *x, nh_dtype x_t,
+                             const float *mean, const float *rstd,
+                             const void *weight, nh_dtype w_t,
+                             int64_t rows, int64_t cols,
+                             void *dx, nh_dtype dx_t,
+                             void *dweight, void *dbias,
+                             void *ws, size_t ws_bytes, void *stream);
+
+nh_status rmsnorm_backward_workspace(int64_t rows, int64_t cols, size_t *ws_bytes);
+
+/*
+ * NVIDIA/Fuser issue #3629, rmsnorm_bwd_fusion: with rinv = 1/rms_r and
+ * g = dy*weight,
+ *   dx = g*rinv - x * rinv^3 * sum_j g*x / H,   dweight_j = sum_rows dy*x*rinv.
+ *
+ *   dy, x, dx     [rows, cols] of dtype t (dx may equal dy; dx NULL = skip)
+ *   rms           fp32 [rows] saved rms = sqrt(mean(x^2) + eps), or NULL to
+ *                 recompute it from x with eps
+ *   weight        [cols] of dtype t, or NULL (weight = 1)
+ *   dweight       [cols] of dtype t, or NULL (skip)
+ */
+nh_status rmsnorm_backward(const void *dy, const void *x, nh_dtype t,
+                           const float *rms, float eps,
+                           const void *weight,
+                           int64_t rows, int64_t cols,
+                           void *dx, void *dweight,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement support.
+ * ---------------------------------------------------------------------- */
+
+/* Kernel ids for per-kernel timing. */
+typedef enum {
+    NH_K_BN_STATS = 0,        /* shifted sums -> partials[2, grid_y, C] */
+    NH_K_BN_FWD_FINALIZE = 1, /* partials -> stats[4, C], running stats */
+    NH_K_BN_APPLY = 2,        /* y = (x - mean)*scale + beta */
+    NH_K_BN_GRAD_SUMS = 3,    /* sum dy, sum dy*(x - mean) -> partials */
+    NH_K_BN_BWD_FINALIZE = 4, /* partials -> grads[4, C] */
+    NH_K_BN_DX = 5,           /* dx = dy*scale + (x - mean)*k1 + k2 */
+    NH_K_LN_ROWS = 6,         /* LayerNorm row pass: dx + column partials */
+    NH_K_LN_COLSUM = 7,       /* LayerNorm dweight/dbias finalize */
+    NH_K_RMS_ROWS = 8,        /* RMSNorm row pass: dx + column partials */
+    NH_K_RMS_COLSUM = 9,      /* RMSNorm dweight finalize */
+    NH_K_CALIB = 10,          /* calibration kernels below */
+    NH_K_COUNT = 11
+} nh_kernel;
+
+/* Static name of a kernel id; "" for an unknown id. */
+const char *nh_kernel_name(int kernel);
+
+/*
+ * Per-kernel timing.  nh_timing_enable(1) clears earlier records and from
+ * then on launches every kernel with hipExtLaunchKernel start/stop events,
+ * which time the dispatch itself (no extra packets between kernels).
+ * nh_timing_enable(0) stops recording and keeps the records.
+ * nh_timing_read waits for the recorded events of one kernel id and returns
+ * the sum of their durations in milliseconds and the number of launches.
+ * Records are process-wide; do not enable timing while another thread
+ * launches normhip kernels that should not be counted.
+ */
+nh_status nh_timing_enable(int on);
+nh_status nh_timing_read(int kernel, double *total_ms, int64_t *launches);
+
+/*
+ * Calibration streams for bandwidth floors (the PR #18 comparison of the
+ * backward elementwise pass against a plain add with the same traffic):
+ *   nh_calib_copy: dst[i] = src[i] for `bytes` bytes (16-byte multiples take
+ *                  the vector path);
+ *   nh_calib_add:  out[i] = a[i] + b[i] over n fp32 elements (two reads, one
+ *                  write).
+ * Both are timed under NH_K_CALIB.
+ */
+nh_status nh_calib_copy(const void *src, void *dst, size_t bytes, void *stream);
+nh_status nh_calib_add(const float *a, const float *b, float *out, int64_t n, void *stream);
+
+/*
+ * Launch plan of the BatchNorm reductions on the current device: the number
+ * of blocks per channel (grid_y) that bn_forward_train / bn_backward use for
+ * this shape and dtype.  Tests use it to cover single- and multi-block
+ * channels.
+ */
+nh_status nh_bn_plan(int64_t N, int64_t C, int64_t HW, nh_dtype io, int *grid_y);
+
+/* Row-kernel plan: the number of blocks G (column-partial rows) used for a
+ * [rows, cols] LayerNorm or RMSNorm backward on the current device. */
+nh_status nh_rows_plan(int64_t rows, int64_t cols, int *blocks);
+
+/*
+ * Plan overrides for tests and tuning sweeps: key "bn_grid_y" forces the
+ * BatchNorm blocks per channel (capped to what the workspace allows), key
+ * "rows_blocks" forces the row-kernel block count.  value 0 restores the
+ * automatic plan.  Process-wide; not for concurrent use with other calls.
+ */
+nh_status nh_plan_override(const char *key, int64_t value);
+
+/* Host-side self test of the library's integer helpers (fast division,
+ * planner invariants).  Needs no GPU.  Returns NH_OK or NH_ERR_ARG with a
+ * message in nh_last_error(). */
+nh_status nh_selftest_host(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NORMHIP_H */

@@ -1,0 +1,135 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/normhip.h declares, its host self test passes, and argument
+validation rejects bad calls before touching any device (the pointers passed
+here are never dereferenced: every call fails or returns before a launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bwd_bn_stats_amd import normhip as nh
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "normhip.h")
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced by the failing calls below
+NULL = None
+NH_OK, NH_ERR_NULL, NH_ERR_SHAPE, NH_ERR_DTYPE, NH_ERR_WORKSPACE, NH_ERR_HIP, NH_ERR_ARG = range(7)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_functions_are_exported():
+    names = declared_functions()
+    assert len(names) >= 19, names
+    for n in names:
+        assert hasattr(nh.lib, n), f"{n} declared in normhip.h but not exported"
+    assert set(names) == set(nh.EXPORTS)
+
+
+def test_host_selftest():
+    assert nh.lib.nh_selftest_host() == NH_OK, nh.last_error()
+
+
+def test_status_and_kernel_names():
+    assert [nh.status_string(i) for i in range(7)] == [
+        "NH_OK", "NH_ERR_NULL", "NH_ERR_SHAPE", "NH_ERR_DTYPE", "NH_ERR_WORKSPACE",
+        "NH_ERR_HIP", "NH_ERR_ARG"]
+    assert nh.status_string(99) == "NH_ERR_UNKNOWN"
+    assert [nh.lib.nh_kernel_name(i).decode() for i in range(11)] == nh.KERNELS
+    assert nh.lib.nh_kernel_name(11).decode() == ""
+
+
+def bn_fwd(x=FAKE, y=FAKE, io=0, N=2, C=3, HW=4, rm=NULL, rv=NULL, eps=1e-5, mom=0.1,
+           stats=FAKE):
+    return nh.lib.bn_forward_train(x, y, io, N, C, HW, NULL, NULL, rm, rv, mom, eps, stats, FAKE,
+                                   1 << 20, NULL)
+
+
+def test_bn_forward_validation():
+    assert bn_fwd(io=2) == NH_ERR_DTYPE
+    assert bn_fwd(io=-1) == NH_ERR_DTYPE
+    assert bn_fwd(N=-1) == NH_ERR_SHAPE
+    assert bn_fwd(HW=-5) == NH_ERR_SHAPE
+    assert bn_fwd(N=1 << 16, C=1 << 8, HW=1 << 8) == NH_ERR_SHAPE  # 2^32 elements
+    assert bn_fwd(N=1 << 31, C=1, HW=1) == NH_ERR_SHAPE
+    assert bn_fwd(x=NULL) == NH_ERR_NULL
+    assert bn_fwd(y=NULL) == NH_ERR_NULL
+    assert bn_fwd(stats=NULL) == NH_ERR_NULL
+    assert bn_fwd(N=1, HW=1, rm=FAKE, rv=FAKE) == NH_ERR_SHAPE  # unbiased var of one element
+    assert bn_fwd(N=1, HW=1, rm=FAKE) == NH_ERR_SHAPE
+    assert bn_fwd(eps=-1e-3) == NH_ERR_ARG
+    assert bn_fwd(eps=float("nan")) == NH_ERR_ARG
+    assert bn_fwd(mom=float("inf")) == NH_ERR_ARG
+    assert "momentum" in nh.last_error()
+    # empty tensors: nothing to do, no device needed, NULL pointers allowed
+    assert bn_fwd(x=NULL, y=NULL, stats=NULL, N=0) == NH_OK
+    assert bn_fwd(x=NULL, y=NULL, stats=NULL, C=0) == NH_OK
+    assert bn_fwd(x=NULL, y=NULL, stats=NULL, HW=0) == NH_OK
+
+
+def test_bn_backward_validation():
+    f = nh.lib.bn_backward
+    assert f(FAKE, FAKE, 7, 2, 3, 4, FAKE, FAKE, FAKE, FAKE, 1 << 20, NULL) == NH_ERR_DTYPE
+    assert f(FAKE, FAKE, 0, 2, -3, 4, FAKE, FAKE, FAKE, FAKE, 1 << 20, NULL) == NH_ERR_SHAPE
+    assert f(NULL, FAKE, 0, 2, 3, 4, FAKE, FAKE, FAKE, FAKE, 1 << 20, NULL) == NH_ERR_NULL
+    assert f(FAKE, FAKE, 0, 2, 3, 4, NULL, FAKE, FAKE, FAKE, 1 << 20, NULL) == NH_ERR_NULL
+    assert f(FAKE, FAKE, 0, 2, 3, 4, FAKE, FAKE, NULL, FAKE, 1 << 20, NULL) == NH_ERR_NULL
+    assert f(NULL, NULL, 0, 0, 3, 4, NULL, NULL, NULL, NULL, 0, NULL) == NH_OK
+
+
+def test_rows_validation():
+    ln = nh.lib.layernorm_backward
+    # dy, dy_t, x, x_t, mean, rstd, w, w_t, rows, cols, dx, dx_t, dw, db, ws, ws_bytes, stream
+    assert ln(FAKE, 3, FAKE, 0, FAKE, FAKE, NULL, 0, 4, 8, FAKE, 0, NULL, NULL, FAKE, 1, NULL) == NH_ERR_DTYPE
+    assert ln(FAKE, 0, FAKE, 0, FAKE, FAKE, NULL, 0, 4, 8, FAKE, 5, NULL, NULL, FAKE, 1, NULL) == NH_ERR_DTYPE
+    assert ln(FAKE, 0, FAKE, 0, FAKE, FAKE, NULL, 0, -4, 8, FAKE, 0, NULL, NULL, FAKE, 1, NULL) == NH_ERR_SHAPE
+    assert ln(FAKE, 0, FAKE, 0, FAKE, FAKE, NULL, 0, 1 << 20, 1 << 11, FAKE, 0, NULL, NULL, FAKE, 1,
+              NULL) == NH_ERR_SHAPE
+    assert ln(FAKE, 0, FAKE, 0, NULL, FAKE, NULL, 0, 4, 8, FAKE, 0, NULL, NULL, FAKE, 1, NULL) == NH_ERR_NULL
+    assert ln(FAKE, 0, NULL, 0, FAKE, FAKE, NULL, 0, 4, 8, FAKE, 0, NULL, NULL, FAKE, 1, NULL) == NH_ERR_NULL
+    assert ln(NULL, 0, NULL, 0, NULL, NULL, NULL, 0, 4, 0, NULL, 0, NULL, NULL, NULL, 0, NULL) == NH_OK
+    rms = nh.lib.rmsnorm_backward
+    # dy, x, t, rms, eps, w, rows, cols, dx, dw, ws, ws_bytes, stream
+    assert rms(FAKE, FAKE, 9, NULL, 1e-5, NULL, 4, 8, FAKE, NULL, FAKE, 1, NULL) == NH_ERR_DTYPE
+    assert rms(FAKE, FAKE, 0, NULL, 1e-5, NULL, 4, -8, FAKE, NULL, FAKE, 1, NULL) == NH_ERR_SHAPE
+    assert rms(NULL, FAKE, 0, NULL, 1e-5, NULL, 4, 8, FAKE, NULL, FAKE, 1, NULL) == NH_ERR_NULL
+    assert rms(FAKE, FAKE, 0, NULL, -1.0, NULL, 4, 8, FAKE, NULL, FAKE, 1, NULL) == NH_ERR_ARG
+    assert rms(FAKE, FAKE, 1, NULL, float("nan"), NULL, 4, 8, FAKE, NULL, FAKE, 1, NULL) == NH_ERR_ARG
+
+
+def test_measurement_validation():
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    assert nh.lib.nh_timing_read(99, ctypes.byref(ms), ctypes.byref(n)) == NH_ERR_ARG
+    assert nh.lib.nh_timing_read(0, None, ctypes.byref(n)) == NH_ERR_NULL
+    assert nh.lib.nh_plan_override(b"nope", 3) == NH_ERR_ARG
+    assert nh.lib.nh_plan_override(b"bn_grid_y", -1) == NH_ERR_ARG
+    assert nh.lib.nh_plan_override(b"bn_grid_y", 0) == NH_OK
+    assert nh.lib.nh_calib_add(FAKE, FAKE, FAKE, -1, NULL) == NH_ERR_SHAPE
+    assert nh.lib.nh_calib_add(NULL, NULL, NULL, 0, NULL) == NH_OK
+    assert nh.lib.nh_calib_copy(NULL, FAKE, 16, NULL) == NH_ERR_NULL
+    out = ctypes.c_size_t(123)
+    assert nh.lib.bn_forward_train_workspace(0, 3, 4, ctypes.byref(out)) == NH_OK and out.value == 0
+    assert nh.lib.bn_forward_train_workspace(-1, 3, 4, ctypes.byref(out)) == NH_ERR_SHAPE
+    assert nh.lib.layernorm_backward_workspace(3, 0, ctypes.byref(out)) == NH_OK and out.value == 0
+    assert nh.lib.rmsnorm_backward_workspace(3, 4, None) == NH_ERR_NULL
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    """The binding has no fallback: a missing library is an ImportError."""
+    import importlib.util
+    src = os.path.join(ROOT, "bwd_bn_stats_amd", "normhip.py")
+    pkg = tmp_path / "pkg"
+    pkg.mkdir()
+    (pkg / "normhip.py").write_text(open(src).read())
+    spec = importlib.util.spec_from_file_location("normhip_copy", str(pkg / "normhip.py"))
+    mod = importlib.util.module_from_spec(spec)
+    with pytest.raises(ImportError, match="no CPU fallback"):
+        spec.loader.exec_module(mod)
