@@ -1,0 +1,389 @@
+"""Benchmark of the normalization hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu-baseline]
+
+A step is one BatchNorm2d training forward + backward (bn_forward_train then
+bn_backward) over the CIFAR-shaped NCHW (256,32,32,32) fp32 batch, the
+workload of the Aether-ML BatchNorm PR's kernel measurements.  Inputs are
+resident in HBM before the timed region.  To time HBM rather than the 256 MB
+Infinity Cache, consecutive steps rotate through enough independent buffer
+sets that each step's tensors were last touched more than 1 GiB of traffic
+earlier ("cold"); back-to-back steps on one set ("warm") are reported too.
+
+Printed: ONE JSON line with the step throughput (algorithmic bytes of the
+forward + backward / step time), the roofline of the dominant kernel (its
+average duration from hipExtLaunchKernel start/stop events recorded during
+the timed region), the per-kernel breakdown, a calibration floor (a plain
+two-read/one-write stream of the same size) and the CPU oracle's throughput
+on this host.  The other workloads (bf16 BatchNorm shapes, LayerNorm and
+RMSNorm backward) are measured the same way and reported under "others".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "norm fwd+bwd µs/call and achieved HBM GB/s (% of MI355X peak) at 1 GPU"
+HBM_PEAK_GBS = 8000.0
+COLD_BYTES = 1 << 30  # traffic between two touches of the same buffer set
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------------
+def _dev(t, device):
+    import numpy as np
+    import torch
+    from bwd_bn_stats_amd import workloads as wl
+    if isinstance(t, wl.Tensor):
+        if t.dtype == wl.F32:
+            return torch.from_numpy(np.ascontiguousarray(t.store)).to(device)
+        return torch.from_numpy(np.ascontiguousarray(t.store).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(t, dtype=np.float32)).to(device)
+
+
+def _nsets(set_bytes, cold):
+    if not cold:
+        return 1
+    return max(2, int(-(-COLD_BYTES // max(set_bytes, 1))) + 1)
+
+
+class Timed:
+    """Runs `step(i)` K times after W warmups; returns host-clock ms/step and
+    per-kernel event durations recorded during the timed region."""
+
+    def __init__(self, nh, torch):
+        self.nh, self.torch = nh, torch
+
+    def run(self, step, K, W, kernels, launches_per_step=8):
+        """Returns (ms per step of the un-instrumented timed region, per-kernel
+        event durations of an identical instrumented region run right after).
+
+        The per-kernel start/stop events ride on the dispatch packets
+        (hipExtLaunchKernel) and time each kernel exactly, but they stop the
+        queue from overlapping one kernel's drain with the next one's launch,
+        so the step time is taken from a region without them."""
+        nh, torch = self.nh, self.torch
+        nh.timing_reserve(K * launches_per_step)
+        for i in range(W):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            step(W + i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        nh.timing_enable(True)
+        t2 = time.perf_counter()
+        for i in range(K):
+            step(W + K + i)
+        torch.cuda.synchronize()
+        self.events_ms = 1000.0 * (time.perf_counter() - t2) / K
+        nh.timing_enable(False)
+        per = {}
+        for k in kernels:
+            ms, n = nh.timing_read(k)
+            if n:
+                per[k] = {"launches": n, "avg_us": 1000.0 * ms / n}
+        return 1000.0 * (t1 - t0) / K, per
+
+
+# ---- BatchNorm --------------------------------------------------------------------
+BN_KERNELS = ["bn_stats", "bn_fwd_finalize", "bn_apply", "bn_grad_sums", "bn_bwd_finalize", "bn_dx"]
+
+
+def bn_bytes(case):
+    """Algorithmic bytes per launch: inputs read once, outputs written once."""
+    s = 4 if case.io == "f32" else 2
+    E = case.N * case.C * case.hw
+    return {"bn_stats": E * s, "bn_apply": 2 * E * s, "bn_grad_sums": 2 * E * s, "bn_dx": 3 * E * s,
+            "bn_fwd_finalize": None, "bn_bwd_finalize": None}
+
+
+def bench_bn(nh, torch, case, K, W, cold=True):
+    import ctypes
+    device = torch.device("cuda:0")
+    x0, dy0 = _dev(case.x, device), _dev(case.dy, device)
+    g, b = _dev(case.gamma, device), _dev(case.beta, device)
+    io = 0 if case.io == "f32" else 1
+    N, C, HW = case.N, case.C, case.hw
+    wsb = nh.bn_forward_train_workspace(N, C, HW)
+    set_bytes = 4 * x0.numel() * x0.element_size()
+    R = _nsets(set_bytes, cold)
+    sets = []
+    for _ in range(R):
+        s = dict(x=x0.clone(), dy=dy0.clone(), y=torch.empty_like(x0), dx=torch.empty_like(x0),
+                 rm=torch.zeros(C, device=device), rv=torch.ones(C, device=device),
+                 stats=torch.empty(4, C, device=device), grads=torch.empty(4, C, device=device),
+                 ws=torch.empty(max(wsb, 16), dtype=torch.uint8, device=device))
+        sets.append(s)
+    torch.cuda.synchronize()
+    P = ctypes.c_void_p
+    stream = P(torch.cuda.current_stream(device).cuda_stream)
+    calls = []
+    for s in sets:
+        p = {k: P(v.data_ptr()) for k, v in s.items()}
+        calls.append((p, s["ws"].numel()))
+    lib = nh.lib
+
+    def step(i):
+        p, nb = calls[i % R]
+        st = lib.bn_forward_train(p["x"], p["y"], io, N, C, HW, P(g.data_ptr()), P(b.data_ptr()),
+                                  p["rm"], p["rv"], case.momentum, case.eps, p["stats"], p["ws"], nb,
+                                  stream)
+        st |= lib.bn_backward(p["dy"], p["x"], io, N, C, HW, p["stats"], p["dx"], p["grads"],
+                              p["ws"], nb, stream)
+        if st:
+            raise RuntimeError(nh.last_error())
+
+    tm = Timed(nh, torch)
+    ms, per = tm.run(step, K, W, BN_KERNELS)
+    byt = bn_bytes(case)
+    for k, v in per.items():
+        if byt.get(k):
+            v["bytes"] = byt[k]
+            v["gbs"] = byt[k] / (v["avg_us"] * 1e3)
+            v["frac_of_peak"] = v["gbs"] / HBM_PEAK_GBS
+    step_bytes = sum(v for v in byt.values() if v)
+    del sets, calls
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms, "us_per_call": 1000.0 * ms,
+            "us_per_call_with_kernel_events": 1000.0 * tm.events_ms, "step_bytes": step_bytes,
+            "gbs": step_bytes / (ms * 1e6), "buffer_sets": R, "kernels": per,
+            "grid_y": nh.bn_plan(N, C, HW, io)}
+
+
+# ---- LayerNorm / RMSNorm -----------------------------------------------------------
+def bench_rows(nh, torch, case, kind, K, W, cold=True, saved=True):
+    import ctypes
+    device = torch.device("cuda:0")
+    x0, dy0, w = _dev(case.x, device), _dev(case.dy, device), _dev(case.w, device)
+    R_, H = case.rows, case.cols
+    xf = x0.float()
+    if kind == "ln":
+        var, mean = torch.var_mean(xf, dim=1, unbiased=False)
+        stat_a, stat_b = mean.contiguous(), torch.rsqrt(var + case.eps).contiguous()
+        wsb = nh.layernorm_backward_workspace(R_, H)
+    else:
+        stat_a = torch.sqrt((xf * xf).mean(dim=1) + case.eps).contiguous()
+        stat_b = None
+        wsb = nh.rmsnorm_backward_workspace(R_, H)
+    del xf
+    dx_dtype = x0.dtype
+    set_bytes = x0.numel() * (x0.element_size() * 2 + dy0.element_size())
+    R = _nsets(set_bytes, cold)
+    sets = [dict(x=x0.clone(), dy=dy0.clone(), dx=torch.empty(x0.shape, dtype=dx_dtype, device=device),
+                 dw=torch.empty(H, dtype=w.dtype, device=device),
+                 db=torch.empty(H, dtype=w.dtype, device=device),
+                 ws=torch.empty(max(wsb, 16), dtype=torch.uint8, device=device)) for _ in range(R)]
+    torch.cuda.synchronize()
+    P = ctypes.c_void_p
+    stream = P(torch.cuda.current_stream(device).cuda_stream)
+    dt = {torch.float32: 0, torch.bfloat16: 1}
+    calls = [({k: P(v.data_ptr()) for k, v in s.items()}, s["ws"].numel()) for s in sets]
+    lib = nh.lib
+    pa, pb, pw = P(stat_a.data_ptr()), (P(stat_b.data_ptr()) if stat_b is not None else None), P(w.data_ptr())
+
+    if kind == "ln":
+        def step(i):
+            p, nb = calls[i % R]
+            st = lib.layernorm_backward(p["dy"], dt[dy0.dtype], p["x"], dt[x0.dtype], pa, pb, pw,
+                                        dt[w.dtype], R_, H, p["dx"], dt[dx_dtype], p["dw"], p["db"],
+                                        p["ws"], nb, stream)
+            if st:
+                raise RuntimeError(nh.last_error())
+        kernels = ["ln_rows", "ln_colsum"]
+    else:
+        rms_p = pa if saved else None
+
+        def step(i):
+            p, nb = calls[i % R]
+            st = lib.rmsnorm_backward(p["dy"], p["x"], dt[x0.dtype], rms_p, case.eps, pw, R_, H,
+                                      p["dx"], p["dw"], p["ws"], nb, stream)
+            if st:
+                raise RuntimeError(nh.last_error())
+        kernels = ["rms_rows", "rms_colsum"]
+
+    ms, per = Timed(nh, torch).run(step, K, W, kernels)
+    E = R_ * H
+    row_bytes = E * (x0.element_size() + dy0.element_size() + torch.empty(0, dtype=dx_dtype).element_size())
+    row_bytes += R_ * 4 * (2 if kind == "ln" else (1 if saved else 0)) + H * w.element_size()
+    rk = kernels[0]
+    if rk in per:
+        per[rk]["bytes"] = row_bytes
+        per[rk]["gbs"] = row_bytes / (per[rk]["avg_us"] * 1e3)
+        per[rk]["frac_of_peak"] = per[rk]["gbs"] / HBM_PEAK_GBS
+    G = nh.rows_plan(R_, H)
+    del sets, calls
+    torch.cuda.empty_cache()
+    return {"ms_per_call": ms, "us_per_call": 1000.0 * ms, "bytes": row_bytes,
+            "gbs": row_bytes / (ms * 1e6), "buffer_sets": R, "kernels": per, "blocks": G,
+            "partials_bytes_written": G * H * 4 * (2 if kind == "ln" else 1)}
+
+
+# ---- calibration floor ---------------------------------------------------------------
+def bench_calib(nh, torch, n_floats, K, W):
+    device = torch.device("cuda:0")
+    set_bytes = 3 * n_floats * 4
+    R = _nsets(set_bytes, True)
+    sets = [(torch.randn(n_floats, device=device), torch.randn(n_floats, device=device),
+             torch.empty(n_floats, device=device)) for _ in range(R)]
+    torch.cuda.synchronize()
+
+    def step(i):
+        a, b, o = sets[i % R]
+        nh.calib_add(a, b, o)
+
+    ms, per = Timed(nh, torch).run(step, K, W, ["calib"])
+    byt = 3 * n_floats * 4
+    avg = per["calib"]["avg_us"]
+    del sets
+    torch.cuda.empty_cache()
+    return {"bytes": byt, "avg_us": avg, "gbs": byt / (avg * 1e3), "frac_of_peak": byt / (avg * 1e3) / HBM_PEAK_GBS}
+
+
+# ---- CPU baseline: the oracle on this host ----------------------------------------------
+def cpu_baseline(case, budget_s=12.0):
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    x, dy = case.x.value, case.dy.value
+    g, b = case.gamma.astype(np.float64), case.beta.astype(np.float64)
+    reps, t_total = 0, 0.0
+    while t_total < budget_s and reps < 50:
+        t0 = time.perf_counter()
+        oracle.bn_forward_train(x, g, b, eps=case.eps, momentum=case.momentum,
+                                running_mean=case.running_mean, running_var=case.running_var)
+        oracle.bn_backward(x, dy, g, eps=case.eps)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    step_bytes = sum(v for v in bn_bytes(case).values() if v)
+    return {"value": step_bytes * reps / t_total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "ms_per_step": 1000.0 * t_total / reps,
+            "sample": f"full {case.N}x{case.C}x{case.hw // 32}x32 {case.io} forward+backward step, "
+                      f"{reps} repetitions (fp64, single thread, same algorithmic bytes as the GPU step)"}
+
+
+def _traffic_for(kernel_name, workload_tag):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_name}_{workload_tag}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "bwd_bn_stats_amd", "csrc", fields.get("source", ""))
+    if not os.path.exists(src):
+        return None
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if digest != fields.get("source_sha256_16"):
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--quick", action="store_true", help="main workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "this library has no multi-GPU path to time.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bwd_bn_stats_amd import normhip as nh
+    from bwd_bn_stats_amd import workloads as wl
+
+    torch.cuda.set_device(0)
+    K, W = args.steps, args.warmup
+    log(f"[bench] device: {torch.cuda.get_device_name(0)}")
+
+    main_case = wl.bn_cifar(wl.F32)
+    log("[bench] main: BatchNorm2d (256,32,32,32) fp32 fwd+bwd, cold")
+    cold = bench_bn(nh, torch, main_case, K, W, cold=True)
+    log(f"[bench]   {cold['us_per_call']:.1f} us/step, {cold['gbs']:.0f} GB/s")
+    log("[bench] main: warm")
+    warm = bench_bn(nh, torch, main_case, K, W, cold=False)
+    log("[bench] calibration floor (two reads, one write, bn_dx-sized)")
+    calib = bench_calib(nh, torch, main_case.N * main_case.C * main_case.hw, K, W)
+
+    others = {}
+    if not args.quick:
+        kk = max(10, K // 2)
+        for name, fn in (("bn_cifar_256x32x32x32_bf16", lambda: wl.bn_cifar(wl.BF16)),
+                         ("bn_resnet_64x256x56x56_bf16", wl.bn_resnet),
+                         ("bn_ragged_3x37x41x40_f32", wl.bn_ragged)):
+            log(f"[bench] {name}")
+            others[name] = bench_bn(nh, torch, fn(), kk, W, cold=True)
+        log("[bench] ln_bwd_16x512x1600 (x f32, dy bf16, w bf16, dx f32)")
+        others["ln_bwd_16x512x1600"] = bench_rows(nh, torch, wl.ln_bwd(), "ln", kk, W)
+        for dt in (wl.BF16, wl.F32):
+            for saved in (True, False):
+                name = f"rms_bwd_2048x8192_{dt}_{'saved' if saved else 'recompute'}_rms"
+                log(f"[bench] {name}")
+                others[name] = bench_rows(nh, torch, wl.rms_bwd(dt), "rms", kk, W, saved=saved)
+
+    # dominant kernel of the step: the largest share of the step's kernel time
+    per = cold["kernels"]
+    dom = max((k for k in per if per[k].get("bytes")), key=lambda k: per[k]["avg_us"] * per[k]["launches"])
+    traffic = _traffic_for(dom, "bn_cifar_f32")
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(per[dom]["gbs"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(per[dom]["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "avg_us": round(per[dom]["avg_us"], 3), "algorithmic_bytes": per[dom]["bytes"]}
+
+    out = {
+        "metric": METRIC,
+        "value": round(cold["gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(cold["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "batchnorm2d_train_fwd_bwd", "shape_nchw": [256, 32, 32, 32],
+                   "io": "f32", "stats": "f32", "cache": "cold (rotating buffer sets)",
+                   "step": "bn_forward_train + bn_backward", "parallelism": "single GPU"},
+        "us_per_call": round(cold["us_per_call"], 2),
+        "us_per_call_with_kernel_events": round(cold["us_per_call_with_kernel_events"], 2),
+        "frac_of_peak": round(cold["gbs"] / HBM_PEAK_GBS, 4),
+        "frac_of_calib_floor": round(cold["gbs"] / calib["gbs"], 4),
+        "roofline": roofline,
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in per.items()},
+        "warm": {"us_per_call": round(warm["us_per_call"], 2), "gbs": round(warm["gbs"], 1)},
+        "calib_read2_write1": {k: round(v, 4) if isinstance(v, float) else v for k, v in calib.items()},
+        "others": others,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline: oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(main_case)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

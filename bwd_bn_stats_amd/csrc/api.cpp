@@ -84,6 +84,7 @@ nh_status device_info(DeviceInfo *out)
 // ---- plan overrides ------------------------------------------------------------
 std::atomic<int64_t> g_override_bn_grid_y{0};
 std::atomic<int64_t> g_override_rows_blocks{0};
+std::atomic<int64_t> g_override_bn_finalize_kernels{0};
 
 // ---- BatchNorm planning ----------------------------------------------------------
 // Resident 256-thread block slots of the device: CUs * (threads per CU / 256),
@@ -107,7 +108,8 @@ int64_t bn_grid_y_max(int64_t M, int64_t C, const DeviceInfo &d) { return bn_gri
 
 size_t bn_ws_bytes(int64_t M, int64_t C, const DeviceInfo &d)
 {
-    return round_up((size_t)(2 * bn_grid_y_max(M, C, d) * C) * sizeof(float), 256);
+    // partials[2, grid_y, C] + shifts K[C]
+    return round_up((size_t)((2 * bn_grid_y_max(M, C, d) + 1) * C) * sizeof(float), 256);
 }
 
 nh_status bn_check_shape(int64_t N, int64_t C, int64_t HW)
@@ -158,8 +160,8 @@ RowsPlan rows_plan(int Q, int64_t rows, int64_t cols, int vec, bool vec_ok, cons
         const int64_t per_thread = ceil_div(groups, 256);
         int mg = 1;
         while (mg < per_thread) mg <<= 1;
-        // LayerNorm (two column sums) caps a thread at 32 row elements.
-        if (mg <= 8 && (Q == 1 || mg * vec <= 32)) {
+        // A thread holds at most 32 row elements in registers.
+        if (mg <= 8 && mg * vec <= 32) {
             p.maxg = mg;
             p.teams = rows_max_threads(mg, vec) / 256;
             // LDS: row-sum buffer + one team-fold slot of Q*cols floats.
@@ -297,6 +299,7 @@ nh_status bn_forward_train(const void *x, void *y, nh_dtype io, int64_t N, int64
     a.eps = eps;
     a.stats = stats;
     a.partials = static_cast<float *>(ws);
+    a.separate_finalize = g_override_bn_finalize_kernels.load() != 0;
     hipError_t e = bn_forward_launch(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "bn_forward_train launch");
     return ok();
@@ -331,6 +334,7 @@ nh_status bn_backward(const void *dy, const void *x, nh_dtype io, int64_t N, int
     a.stats = const_cast<float *>(stats);
     a.grads = grads;
     a.partials = static_cast<float *>(ws);
+    a.separate_finalize = g_override_bn_finalize_kernels.load() != 0;
     hipError_t e = bn_backward_launch(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "bn_backward launch");
     return ok();
@@ -482,6 +486,19 @@ nh_status nh_timing_enable(int on)
     return ok();
 }
 
+nh_status nh_timing_reserve(int64_t launches)
+{
+    if (launches < 0) return fail(NH_ERR_ARG, "launches must be >= 0");
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    while ((int64_t)g_event_pool.size() < 2 * launches) {
+        hipEvent_t e = nullptr;
+        hipError_t err = hipEventCreate(&e);
+        if (err != hipSuccess) return hip_fail(err, "hipEventCreate");
+        g_event_pool.push_back(e);
+    }
+    return ok();
+}
+
 nh_status nh_timing_read(int kernel, double *total_ms, int64_t *launches)
 {
     if (kernel < 0 || kernel >= NH_K_COUNT) return fail(NH_ERR_ARG, "kernel id %d", kernel);
@@ -561,6 +578,7 @@ nh_status nh_plan_override(const char *key, int64_t value)
     if (value < 0) return fail(NH_ERR_ARG, "value must be >= 0");
     if (strcmp(key, "bn_grid_y") == 0) g_override_bn_grid_y.store(value);
     else if (strcmp(key, "rows_blocks") == 0) g_override_rows_blocks.store(value);
+    else if (strcmp(key, "bn_finalize_kernels") == 0) g_override_bn_finalize_kernels.store(value);
     else return fail(NH_ERR_ARG, "unknown override key '%s'", key);
     return ok();
 }

@@ -7,12 +7,21 @@
 //   forward : bn_stats_kernel      one read of x: shifted sums
 //                                  (sum d, sum d^2), d = x - x[0,c,0,0],
 //                                  one slot of partials[2, grid_y, C] per block
-//             bn_fwd_finalize      fixed-order fp64 combine of the partials ->
+//             finalize             fixed-order fp64 combine of the partials ->
 //                                  stats[4, C]; running statistics in place
 //             bn_apply_kernel      y = fmaf(x - mean, scale, beta)
 //   backward: bn_grad_sums_kernel  (sum dy, sum dy*(x - mean)) -> partials
-//             bn_bwd_finalize      -> grads[4, C] = (dgamma, dbeta, k1, k2)
+//             finalize             -> grads[4, C] = (dgamma, dbeta, k1, k2)
 //             bn_dx_kernel         dx = dy*scale + (x - mean)*k1 + k2
+//
+// The finalize step runs either as its own small kernel (bn_fwd_finalize /
+// bn_bwd_finalize, the pages' three-launch structure) or, by default, in the
+// prologue of the elementwise kernel that consumes it: on MI355X a dependent
+// launch of a few-KB kernel costs about 4 us, a sizeable share of a 50 us
+// forward+backward step, while re-reading a channel's partials per block
+// costs a few hundred bytes of L2 traffic.
+//
+// Workspace: partials[2, grid_y, C] followed by the shifts K[C].
 //
 // Work split: channel c owns N planes of HW contiguous elements (one per
 // image n, stride C*HW).  Its M = N*HW elements are cut into `units` of `V`
@@ -29,6 +38,18 @@
 #include "nh_internal.hpp"
 
 namespace nh {
+
+// Cache policy of the BatchNorm streams: which accesses carry the
+// nontemporal hint.  Measured on MI355X over cold 33-103 MB tensors, the best
+// of the eight combinations keeps the reduction passes' loads cacheable (the
+// elementwise pass re-reads the same x and dy right after, and finds them in
+// the 256 MB Infinity Cache), streams the elementwise passes' loads (last
+// use) and streams every store.
+enum : int { kNtReduceLoads = 1, kNtEwLoads = 2, kNtStores = 4 };
+#ifndef NH_BN_NT_POLICY
+#define NH_BN_NT_POLICY (kNtEwLoads | kNtStores)
+#endif
+constexpr int kBnNtPolicy = NH_BN_NT_POLICY;
 
 struct BnGeom {
     int C;
@@ -74,7 +95,7 @@ __device__ __forceinline__ void block_sum2(float &a, float &b)
 }
 
 // ---- forward reduction: shifted one-pass sums ------------------------------
-template <typename T, int V>
+template <typename T, int V, int NT>
 __global__ void __launch_bounds__(kBnThreads)
 bn_stats_kernel(const T *__restrict__ x, BnGeom g, float *__restrict__ partials)
 {
@@ -94,7 +115,7 @@ bn_stats_kernel(const T *__restrict__ x, BnGeom g, float *__restrict__ partials)
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
             const int u = base + k * kBnThreads;
-            if (u < u1) load_vec<T, V>(x + bn_unit_offset<V>(g, c, u), v[k]);
+            if (u < u1) ld<(NT & kNtReduceLoads) != 0, T, V>(x + bn_unit_offset<V>(g, c, u), v[k]);
         }
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
@@ -116,11 +137,14 @@ bn_stats_kernel(const T *__restrict__ x, BnGeom g, float *__restrict__ partials)
     if (threadIdx.x == 0) {
         partials[(0 * g.grid_y + yb) * g.C + c] = a;
         partials[(1 * g.grid_y + yb) * g.C + c] = b;
+        // The shift itself, kept beside the partials: with y == x the apply
+        // pass may overwrite x[0, c, 0, 0] before every block has read it.
+        if (yb == 0) partials[2 * g.grid_y * g.C + c] = K;
     }
 }
 
 // ---- backward reduction: sum dy, sum dy*(x - mean) ----------------------------
-template <typename T, int V>
+template <typename T, int V, int NT>
 __global__ void __launch_bounds__(kBnThreads)
 bn_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x,
                     const float *__restrict__ stats, BnGeom g, float *__restrict__ partials)
@@ -142,8 +166,8 @@ bn_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x,
             const int u = base + k * kBnThreads;
             if (u < u1) {
                 const int off = bn_unit_offset<V>(g, c, u);
-                load_vec<T, V>(x + off, vx[k]);
-                load_vec<T, V>(dy + off, vd[k]);
+                ld<(NT & kNtReduceLoads) != 0, T, V>(x + off, vx[k]);
+                ld<(NT & kNtReduceLoads) != 0, T, V>(dy + off, vd[k]);
             }
         }
 #pragma unroll
@@ -168,7 +192,7 @@ bn_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x,
     }
 }
 
-// ---- finalize kernels: one wave per channel, fp64 fixed-order combine -------
+// ---- finalize: one wave per channel, fp64 fixed-order combine -----------------
 // Lane l sums slots l, l+64, ... in order; the butterfly then combines lanes.
 __device__ __forceinline__ void sum_partials(const float *__restrict__ partials, int grid_y,
                                              int C, int c, double &s1, double &s2)
@@ -183,10 +207,63 @@ __device__ __forceinline__ void sum_partials(const float *__restrict__ partials,
     s2 = wave_sum(b);
 }
 
-template <typename T>
+// Forward finalize of channel c from its shifted sums (called by one lane):
+// stats[4, C] = (mean, var, inv_std, scale) and the running statistics.
+// Returns mean and scale for the caller's apply.
+__device__ __forceinline__ void fwd_finalize_channel(double S1, double S2, float K, int C, int c,
+                                                     int64_t M, const float *__restrict__ gamma,
+                                                     float *__restrict__ running_mean,
+                                                     float *__restrict__ running_var,
+                                                     float momentum, float eps, bool write,
+                                                     float *__restrict__ stats, float &mean_out,
+                                                     float &scale_out)
+{
+    const double Md = (double)M;
+    const double md = S1 / Md;                    // mean of the shifted values
+    double var = S2 / Md - md * md;               // biased variance
+    if (var < 0.0) var = 0.0;
+    const double mean = (double)K + md;
+    const double inv_std = 1.0 / sqrt(var + (double)eps);
+    const double gm = gamma ? (double)gamma[c] : 1.0;
+    const float meanf = (float)mean, scalef = (float)(gm * inv_std);
+    mean_out = meanf;
+    scale_out = scalef;
+    if (!write) return;
+    stats[0 * C + c] = meanf;
+    stats[1 * C + c] = (float)var;
+    stats[2 * C + c] = (float)inv_std;
+    stats[3 * C + c] = scalef;
+    const double m = (double)momentum;
+    if (running_mean)
+        running_mean[c] = (float)((1.0 - m) * (double)running_mean[c] + m * mean);
+    if (running_var)
+        running_var[c] = (float)((1.0 - m) * (double)running_var[c] + m * var * Md / (Md - 1.0));
+}
+
+// Backward finalize of channel c (called by one lane): grads[4, C] =
+// (dgamma, dbeta, k1, k2) with k1 = -scale*inv_std^2*S/M, k2 = -scale*dbeta/M.
+__device__ __forceinline__ void bwd_finalize_channel(double Sdy, double Sdyxc, int C, int c, int64_t M,
+                                                     const float *__restrict__ stats, bool write,
+                                                     float *__restrict__ grads, float &k1_out,
+                                                     float &k2_out)
+{
+    const double Md = (double)M;
+    const double inv_std = (double)stats[2 * C + c];
+    const double scale = (double)stats[3 * C + c];
+    const float k1 = (float)(-scale * inv_std * inv_std * Sdyxc / Md);
+    const float k2 = (float)(-scale * Sdy / Md);
+    k1_out = k1;
+    k2_out = k2;
+    if (!write) return;
+    grads[0 * C + c] = (float)(inv_std * Sdyxc);  // dgamma
+    grads[1 * C + c] = (float)Sdy;                // dbeta
+    grads[2 * C + c] = k1;
+    grads[3 * C + c] = k2;
+}
+
 __global__ void __launch_bounds__(kBnThreads)
-bn_fwd_finalize(const T *__restrict__ x, const float *__restrict__ partials, int grid_y,
-                int C, int HW, int64_t M, const float *__restrict__ gamma,
+bn_fwd_finalize(const float *__restrict__ partials, int grid_y, int C, int64_t M,
+                const float *__restrict__ gamma,
                 float *__restrict__ running_mean, float *__restrict__ running_var,
                 float momentum, float eps, float *__restrict__ stats)
 {
@@ -195,23 +272,9 @@ bn_fwd_finalize(const T *__restrict__ x, const float *__restrict__ partials, int
     double S1, S2;
     sum_partials(partials, grid_y, C, c, S1, S2);
     if ((threadIdx.x & (kWave - 1)) != 0) return;
-    const double Md = (double)M;
-    const double K = (double)to_f32(x[c * HW]);
-    const double md = S1 / Md;                    // mean of the shifted values
-    double var = S2 / Md - md * md;               // biased variance
-    if (var < 0.0) var = 0.0;
-    const double mean = K + md;
-    const double inv_std = 1.0 / sqrt(var + (double)eps);
-    const double gm = gamma ? (double)gamma[c] : 1.0;
-    stats[0 * C + c] = (float)mean;
-    stats[1 * C + c] = (float)var;
-    stats[2 * C + c] = (float)inv_std;
-    stats[3 * C + c] = (float)(gm * inv_std);
-    const double m = (double)momentum;
-    if (running_mean)
-        running_mean[c] = (float)((1.0 - m) * (double)running_mean[c] + m * mean);
-    if (running_var)
-        running_var[c] = (float)((1.0 - m) * (double)running_var[c] + m * var * Md / (Md - 1.0));
+    float mean, scale;
+    fwd_finalize_channel(S1, S2, partials[2 * grid_y * C + c], C, c, M, gamma, running_mean,
+                         running_var, momentum, eps, true, stats, mean, scale);
 }
 
 __global__ void __launch_bounds__(kBnThreads)
@@ -223,38 +286,66 @@ bn_bwd_finalize(const float *__restrict__ partials, int grid_y, int C, int64_t M
     double Sdy, Sdyxc;
     sum_partials(partials, grid_y, C, c, Sdy, Sdyxc);
     if ((threadIdx.x & (kWave - 1)) != 0) return;
-    const double Md = (double)M;
-    const double inv_std = (double)stats[2 * C + c];
-    const double scale = (double)stats[3 * C + c];
-    grads[0 * C + c] = (float)(inv_std * Sdyxc);                       // dgamma
-    grads[1 * C + c] = (float)Sdy;                                     // dbeta
-    grads[2 * C + c] = (float)(-scale * inv_std * inv_std * Sdyxc / Md); // k1
-    grads[3 * C + c] = (float)(-scale * Sdy / Md);                     // k2
+    float k1, k2;
+    bwd_finalize_channel(Sdy, Sdyxc, C, c, M, stats, true, grads, k1, k2);
 }
 
 // ---- elementwise passes ------------------------------------------------------
-template <typename T, int V>
+// FUSED: the block first finalizes its own channel from the partials (wave 0,
+// fixed order, the same arithmetic as the finalize kernels; block yb == 0
+// writes stats/grads and the running statistics), with its first loads of x
+// already in flight.  This removes the finalize launch from the dependency
+// chain at the cost of every block re-reading its channel's grid_y partials.
+struct FwdFinalizeArgs {
+    const float *partials;
+    const float *gamma;
+    float *running_mean, *running_var;
+    float momentum, eps;
+    int64_t M;
+};
+
+template <typename T, int V, bool FUSED, int NT>
 __global__ void __launch_bounds__(kBnThreads)
-bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, const float *__restrict__ stats,
-                const float *__restrict__ beta, BnGeom g)
+bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ stats,
+                const float *__restrict__ beta, BnGeom g, FwdFinalizeArgs f)
 {
     const int c = blockIdx.x / g.grid_y;
     const int yb = blockIdx.x - c * g.grid_y;
     const int u0 = yb * g.upb;
     const int u1 = min(u0 + g.upb, g.units);
-    const float mean = stats[c];
-    const float scale = stats[3 * g.C + c];
     const float b = beta ? beta[c] : 0.f;
 
-    for (int base = u0 + (int)threadIdx.x; base < u1; base += kBnThreads * kBnUnroll) {
-        float v[kBnUnroll][V];
-        int off[kBnUnroll];
+    int base = u0 + (int)threadIdx.x;
+    float v[kBnUnroll][V];
+    int off[kBnUnroll];
 #pragma unroll
-        for (int k = 0; k < kBnUnroll; ++k) {
-            const int u = base + k * kBnThreads;
-            off[k] = bn_unit_offset<V>(g, c, u);
-            if (u < u1) load_vec<T, V>(x + off[k], v[k]);
+    for (int k = 0; k < kBnUnroll; ++k) {
+        const int u = base + k * kBnThreads;
+        off[k] = bn_unit_offset<V>(g, c, u);
+        if (u < u1) ld<(NT & kNtEwLoads) != 0, T, V>(x + off[k], v[k]);
+    }
+
+    float mean, scale;
+    if constexpr (FUSED) {
+        __shared__ float sh[2];
+        if (threadIdx.x < kWave) {
+            double S1, S2;
+            sum_partials(f.partials, g.grid_y, g.C, c, S1, S2);
+            if (threadIdx.x == 0) {
+                fwd_finalize_channel(S1, S2, f.partials[2 * g.grid_y * g.C + c], g.C, c, f.M, f.gamma,
+                                     f.running_mean, f.running_var, f.momentum, f.eps, yb == 0,
+                                     stats, sh[0], sh[1]);
+            }
         }
+        __syncthreads();
+        mean = sh[0];
+        scale = sh[1];
+    } else {
+        mean = stats[c];
+        scale = stats[3 * g.C + c];
+    }
+
+    for (;;) {
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
             const int u = base + k * kBnThreads;
@@ -262,16 +353,25 @@ bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, const float *__restr
                 float o[V];
 #pragma unroll
                 for (int e = 0; e < V; ++e) o[e] = fmaf(v[k][e] - mean, scale, b);
-                store_vec<T, V>(y + off[k], o);
+                st<(NT & kNtStores) != 0, T, V>(y + off[k], o);
             }
+        }
+        base += kBnThreads * kBnUnroll;
+        if (base >= u1) break;
+#pragma unroll
+        for (int k = 0; k < kBnUnroll; ++k) {
+            const int u = base + k * kBnThreads;
+            off[k] = bn_unit_offset<V>(g, c, u);
+            if (u < u1) ld<(NT & kNtEwLoads) != 0, T, V>(x + off[k], v[k]);
         }
     }
 }
 
-template <typename T, int V>
+template <typename T, int V, bool FUSED, int NT>
 __global__ void __launch_bounds__(kBnThreads)
 bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ dx,
-             const float *__restrict__ stats, const float *__restrict__ grads, BnGeom g)
+             const float *__restrict__ stats, float *__restrict__ grads, BnGeom g,
+             const float *__restrict__ partials, int64_t M)
 {
     const int c = blockIdx.x / g.grid_y;
     const int yb = blockIdx.x - c * g.grid_y;
@@ -279,21 +379,38 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
     const int u1 = min(u0 + g.upb, g.units);
     const float mean = stats[c];
     const float scale = stats[3 * g.C + c];
-    const float k1 = grads[2 * g.C + c];
-    const float k2 = grads[3 * g.C + c];
 
-    for (int base = u0 + (int)threadIdx.x; base < u1; base += kBnThreads * kBnUnroll) {
-        float vx[kBnUnroll][V], vd[kBnUnroll][V];
-        int off[kBnUnroll];
+    int base = u0 + (int)threadIdx.x;
+    float vx[kBnUnroll][V], vd[kBnUnroll][V];
+    int off[kBnUnroll];
 #pragma unroll
-        for (int k = 0; k < kBnUnroll; ++k) {
-            const int u = base + k * kBnThreads;
-            off[k] = bn_unit_offset<V>(g, c, u);
-            if (u < u1) {
-                load_vec<T, V>(x + off[k], vx[k]);
-                load_vec<T, V>(dy + off[k], vd[k]);
-            }
+    for (int k = 0; k < kBnUnroll; ++k) {
+        const int u = base + k * kBnThreads;
+        off[k] = bn_unit_offset<V>(g, c, u);
+        if (u < u1) {
+            ld<(NT & kNtEwLoads) != 0, T, V>(x + off[k], vx[k]);
+            ld<(NT & kNtEwLoads) != 0, T, V>(dy + off[k], vd[k]);
         }
+    }
+
+    float k1, k2;
+    if constexpr (FUSED) {
+        __shared__ float sh[2];
+        if (threadIdx.x < kWave) {
+            double Sdy, Sdyxc;
+            sum_partials(partials, g.grid_y, g.C, c, Sdy, Sdyxc);
+            if (threadIdx.x == 0)
+                bwd_finalize_channel(Sdy, Sdyxc, g.C, c, M, stats, yb == 0, grads, sh[0], sh[1]);
+        }
+        __syncthreads();
+        k1 = sh[0];
+        k2 = sh[1];
+    } else {
+        k1 = grads[2 * g.C + c];
+        k2 = grads[3 * g.C + c];
+    }
+
+    for (;;) {
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
             const int u = base + k * kBnThreads;
@@ -302,7 +419,18 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
 #pragma unroll
                 for (int e = 0; e < V; ++e)
                     o[e] = fmaf(vd[k][e], scale, fmaf(vx[k][e] - mean, k1, k2));
-                store_vec<T, V>(dx + off[k], o);
+                st<(NT & kNtStores) != 0, T, V>(dx + off[k], o);
+            }
+        }
+        base += kBnThreads * kBnUnroll;
+        if (base >= u1) break;
+#pragma unroll
+        for (int k = 0; k < kBnUnroll; ++k) {
+            const int u = base + k * kBnThreads;
+            off[k] = bn_unit_offset<V>(g, c, u);
+            if (u < u1) {
+                ld<(NT & kNtEwLoads) != 0, T, V>(x + off[k], vx[k]);
+                ld<(NT & kNtEwLoads) != 0, T, V>(dy + off[k], vd[k]);
             }
         }
     }
@@ -328,15 +456,21 @@ static hipError_t bn_forward_t(const BnCall &a, hipStream_t s)
     const BnGeom g = make_geom(a);
     const T *x = static_cast<const T *>(a.x);
     const dim3 grid((unsigned)(a.C * a.grid_y)), block(kBnThreads);
-    hipError_t e = launch(NH_K_BN_STATS, bn_stats_kernel<T, V>, grid, block, 0, s, x, g, a.partials);
+    hipError_t e = launch(NH_K_BN_STATS, bn_stats_kernel<T, V, kBnNtPolicy>, grid, block, 0, s, x, g, a.partials);
     if (e != hipSuccess) return e;
-    const dim3 fgrid((unsigned)ceil_div(a.C, kBnThreads / kWave));
-    e = launch(NH_K_BN_FWD_FINALIZE, bn_fwd_finalize<T>, fgrid, block, 0, s, x, a.partials,
-               a.grid_y, a.C, a.HW, (int64_t)a.N * a.HW, a.gamma, a.running_mean,
-               a.running_var, a.momentum, a.eps, a.stats);
-    if (e != hipSuccess) return e;
-    return launch(NH_K_BN_APPLY, bn_apply_kernel<T, V>, grid, block, 0, s, x,
-                  static_cast<T *>(a.out), a.stats, a.beta, g);
+    const int64_t M = (int64_t)a.N * a.HW;
+    FwdFinalizeArgs f{a.partials, a.gamma, a.running_mean, a.running_var, a.momentum, a.eps, M};
+    if (a.separate_finalize) {
+        const dim3 fgrid((unsigned)ceil_div(a.C, kBnThreads / kWave));
+        e = launch(NH_K_BN_FWD_FINALIZE, bn_fwd_finalize, fgrid, block, 0, s, a.partials,
+                   a.grid_y, a.C, M, a.gamma, a.running_mean, a.running_var, a.momentum,
+                   a.eps, a.stats);
+        if (e != hipSuccess) return e;
+        return launch(NH_K_BN_APPLY, bn_apply_kernel<T, V, false, kBnNtPolicy>, grid, block, 0, s, x,
+                      static_cast<T *>(a.out), a.stats, a.beta, g, f);
+    }
+    return launch(NH_K_BN_APPLY, bn_apply_kernel<T, V, true, kBnNtPolicy>, grid, block, 0, s, x,
+                  static_cast<T *>(a.out), a.stats, a.beta, g, f);
 }
 
 template <typename T, int V>
@@ -346,15 +480,20 @@ static hipError_t bn_backward_t(const BnCall &a, hipStream_t s)
     const T *x = static_cast<const T *>(a.x);
     const T *dy = static_cast<const T *>(a.dy);
     const dim3 grid((unsigned)(a.C * a.grid_y)), block(kBnThreads);
-    hipError_t e = launch(NH_K_BN_GRAD_SUMS, bn_grad_sums_kernel<T, V>, grid, block, 0, s, dy, x,
+    hipError_t e = launch(NH_K_BN_GRAD_SUMS, bn_grad_sums_kernel<T, V, kBnNtPolicy>, grid, block, 0, s, dy, x,
                           a.stats, g, a.partials);
     if (e != hipSuccess) return e;
-    const dim3 fgrid((unsigned)ceil_div(a.C, kBnThreads / kWave));
-    e = launch(NH_K_BN_BWD_FINALIZE, bn_bwd_finalize, fgrid, block, 0, s, a.partials, a.grid_y,
-               a.C, (int64_t)a.N * a.HW, a.stats, a.grads);
-    if (e != hipSuccess || a.out == nullptr) return e;
-    return launch(NH_K_BN_DX, bn_dx_kernel<T, V>, grid, block, 0, s, dy, x,
-                  static_cast<T *>(a.out), a.stats, a.grads, g);
+    const int64_t M = (int64_t)a.N * a.HW;
+    if (a.separate_finalize || a.out == nullptr) {
+        const dim3 fgrid((unsigned)ceil_div(a.C, kBnThreads / kWave));
+        e = launch(NH_K_BN_BWD_FINALIZE, bn_bwd_finalize, fgrid, block, 0, s, a.partials, a.grid_y,
+                   a.C, M, a.stats, a.grads);
+        if (e != hipSuccess || a.out == nullptr) return e;
+        return launch(NH_K_BN_DX, bn_dx_kernel<T, V, false, kBnNtPolicy>, grid, block, 0, s, dy, x,
+                      static_cast<T *>(a.out), a.stats, a.grads, g, a.partials, M);
+    }
+    return launch(NH_K_BN_DX, bn_dx_kernel<T, V, true, kBnNtPolicy>, grid, block, 0, s, dy, x,
+                  static_cast<T *>(a.out), a.stats, a.grads, g, a.partials, M);
 }
 
 hipError_t bn_forward_launch(const BnCall &a, hipStream_t s)

@@ -10,22 +10,27 @@ namespace nh {
 constexpr int kCalibThreads = 256;
 constexpr int kCalibUnroll = 4;
 
+// Each block streams one contiguous chunk, kCalibUnroll 16-byte accesses in
+// flight per thread, every access nontemporal: the fastest plain stream
+// shape measured on MI355X.
 __global__ void __launch_bounds__(kCalibThreads)
-calib_copy16_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst, int64_t n16)
+calib_copy16_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst, int64_t n16, int64_t chunk)
 {
-    const int64_t stride = (int64_t)gridDim.x * kCalibThreads;
-    for (int64_t base = (int64_t)blockIdx.x * kCalibThreads + threadIdx.x; base < n16;
-         base += stride * kCalibUnroll) {
-        uint4 v[kCalibUnroll];
+    const int64_t b0 = (int64_t)blockIdx.x * chunk;
+    const int64_t b1 = b0 + chunk < n16 ? b0 + chunk : n16;
+    const u32x4_t *s4 = reinterpret_cast<const u32x4_t *>(src);
+    u32x4_t *d4 = reinterpret_cast<u32x4_t *>(dst);
+    for (int64_t base = b0 + threadIdx.x; base < b1; base += kCalibThreads * kCalibUnroll) {
+        u32x4_t v[kCalibUnroll];
 #pragma unroll
         for (int k = 0; k < kCalibUnroll; ++k) {
-            const int64_t i = base + k * stride;
-            if (i < n16) v[k] = src[i];
+            const int64_t i = base + k * kCalibThreads;
+            if (i < b1) v[k] = nt_load(s4 + i);
         }
 #pragma unroll
         for (int k = 0; k < kCalibUnroll; ++k) {
-            const int64_t i = base + k * stride;
-            if (i < n16) dst[i] = v[k];
+            const int64_t i = base + k * kCalibThreads;
+            if (i < b1) __builtin_nontemporal_store(v[k], d4 + i);
         }
     }
 }
@@ -39,23 +44,24 @@ calib_copy1_kernel(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, i
 
 __global__ void __launch_bounds__(kCalibThreads)
 calib_add4_kernel(const float4 *__restrict__ a, const float4 *__restrict__ b,
-                  float4 *__restrict__ o, int64_t n4)
+                  float4 *__restrict__ o, int64_t n4, int64_t chunk)
 {
-    const int64_t stride = (int64_t)gridDim.x * kCalibThreads;
-    for (int64_t base = (int64_t)blockIdx.x * kCalibThreads + threadIdx.x; base < n4;
-         base += stride * kCalibUnroll) {
-        float4 va[kCalibUnroll], vb[kCalibUnroll];
+    const int64_t b0 = (int64_t)blockIdx.x * chunk;
+    const int64_t b1 = b0 + chunk < n4 ? b0 + chunk : n4;
+    const f32x4_t *a4 = reinterpret_cast<const f32x4_t *>(a);
+    const f32x4_t *c4 = reinterpret_cast<const f32x4_t *>(b);
+    f32x4_t *o4 = reinterpret_cast<f32x4_t *>(o);
+    for (int64_t base = b0 + threadIdx.x; base < b1; base += kCalibThreads * kCalibUnroll) {
+        f32x4_t va[kCalibUnroll], vb[kCalibUnroll];
 #pragma unroll
         for (int k = 0; k < kCalibUnroll; ++k) {
-            const int64_t i = base + k * stride;
-            if (i < n4) { va[k] = a[i]; vb[k] = b[i]; }
+            const int64_t i = base + k * kCalibThreads;
+            if (i < b1) { va[k] = nt_load(a4 + i); vb[k] = nt_load(c4 + i); }
         }
 #pragma unroll
         for (int k = 0; k < kCalibUnroll; ++k) {
-            const int64_t i = base + k * stride;
-            if (i < n4)
-                o[i] = make_float4(va[k].x + vb[k].x, va[k].y + vb[k].y, va[k].z + vb[k].z,
-                                   va[k].w + vb[k].w);
+            const int64_t i = base + k * kCalibThreads;
+            if (i < b1) __builtin_nontemporal_store(va[k] + vb[k], o4 + i);
         }
     }
 }
@@ -82,8 +88,9 @@ hipError_t calib_copy_launch(const void *src, void *dst, size_t bytes, int slots
     const bool vec = bytes % 16 == 0 && ((uintptr_t)src % 16) == 0 && ((uintptr_t)dst % 16) == 0;
     if (vec) {
         const int64_t n16 = (int64_t)(bytes / 16);
-        return launch(NH_K_CALIB, calib_copy16_kernel, dim3(calib_grid(n16, slots)),
-                      dim3(kCalibThreads), 0u, s, (const uint4 *)src, (uint4 *)dst, n16);
+        const unsigned grid = calib_grid(n16, slots);
+        return launch(NH_K_CALIB, calib_copy16_kernel, dim3(grid), dim3(kCalibThreads), 0u, s,
+                      (const uint4 *)src, (uint4 *)dst, n16, ceil_div(n16, grid));
     }
     return launch(NH_K_CALIB, calib_copy1_kernel, dim3(calib_grid((int64_t)bytes, slots)),
                   dim3(kCalibThreads), 0u, s, (const uint8_t *)src, (uint8_t *)dst, (int64_t)bytes);
@@ -93,10 +100,12 @@ hipError_t calib_add_launch(const float *a, const float *b, float *o, int64_t n,
 {
     const bool vec = n % 4 == 0 && ((uintptr_t)a % 16) == 0 && ((uintptr_t)b % 16) == 0 &&
                      ((uintptr_t)o % 16) == 0;
-    if (vec)
-        return launch(NH_K_CALIB, calib_add4_kernel, dim3(calib_grid(n / 4, slots)),
-                      dim3(kCalibThreads), 0u, s, (const float4 *)a, (const float4 *)b, (float4 *)o,
-                      n / 4);
+    if (vec) {
+        const unsigned grid = calib_grid(n / 4, slots);
+        return launch(NH_K_CALIB, calib_add4_kernel, dim3(grid), dim3(kCalibThreads), 0u, s,
+                      (const float4 *)a, (const float4 *)b, (float4 *)o, n / 4,
+                      ceil_div(n / 4, grid));
+    }
     return launch(NH_K_CALIB, calib_add1_kernel, dim3(calib_grid(n, slots)), dim3(kCalibThreads),
                   0u, s, a, b, o, n);
 }

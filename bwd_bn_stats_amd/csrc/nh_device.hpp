@@ -106,6 +106,94 @@ __device__ __forceinline__ void load_vec(const T *p, float (&o)[V]) { Vec<T, V>:
 template <typename T, int V>
 __device__ __forceinline__ void store_vec(T *p, const float (&v)[V]) { Vec<T, V>::store(p, v); }
 
+// ---- nontemporal (streaming) variants ---------------------------------------------
+// Loads and stores that carry the nontemporal hint: on MI355X a stream that is
+// touched once moves through the caches markedly faster this way (plain
+// stores in particular), measured on 33-537 MB streams.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4_t nt_load(const f32x4_t *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ u32x4_t nt_load(const u32x4_t *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ u32x2_t nt_load(const u32x2_t *p) { return __builtin_nontemporal_load(p); }
+
+template <bool NT, typename T, int V> struct VecNT;
+
+template <typename T, int V> struct VecNT<false, T, V> {
+    static __device__ __forceinline__ void load(const T *p, float (&o)[V]) { Vec<T, V>::load(p, o); }
+    static __device__ __forceinline__ void store(T *p, const float (&v)[V]) { Vec<T, V>::store(p, v); }
+};
+template <> struct VecNT<true, float, 1> {
+    static __device__ __forceinline__ void load(const float *p, float (&o)[1]) { o[0] = __builtin_nontemporal_load(p); }
+    static __device__ __forceinline__ void store(float *p, const float (&v)[1]) { __builtin_nontemporal_store(v[0], p); }
+};
+template <> struct VecNT<true, uint16_t, 1> {
+    static __device__ __forceinline__ void load(const uint16_t *p, float (&o)[1]) { o[0] = to_f32((uint16_t)__builtin_nontemporal_load(p)); }
+    static __device__ __forceinline__ void store(uint16_t *p, const float (&v)[1]) { __builtin_nontemporal_store(from_f32<uint16_t>(v[0]), p); }
+};
+template <> struct VecNT<true, float, 4> {
+    static __device__ __forceinline__ void load(const float *p, float (&o)[4])
+    {
+        f32x4_t v = nt_load(reinterpret_cast<const f32x4_t *>(p));
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    }
+    static __device__ __forceinline__ void store(float *p, const float (&v)[4])
+    {
+        f32x4_t t = {v[0], v[1], v[2], v[3]};
+        __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t *>(p));
+    }
+};
+template <> struct VecNT<true, float, 8> {
+    static __device__ __forceinline__ void load(const float *p, float (&o)[8])
+    {
+        f32x4_t a = nt_load(reinterpret_cast<const f32x4_t *>(p));
+        f32x4_t b = nt_load(reinterpret_cast<const f32x4_t *>(p) + 1);
+        o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+        o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    }
+    static __device__ __forceinline__ void store(float *p, const float (&v)[8])
+    {
+        f32x4_t a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+        __builtin_nontemporal_store(a, reinterpret_cast<f32x4_t *>(p));
+        __builtin_nontemporal_store(b, reinterpret_cast<f32x4_t *>(p) + 1);
+    }
+};
+template <> struct VecNT<true, uint16_t, 4> {
+    static __device__ __forceinline__ void load(const uint16_t *p, float (&o)[4])
+    {
+        u32x2_t u = nt_load(reinterpret_cast<const u32x2_t *>(p));
+        unpack_bf16x2(u.x, o[0], o[1]);
+        unpack_bf16x2(u.y, o[2], o[3]);
+    }
+    static __device__ __forceinline__ void store(uint16_t *p, const float (&v)[4])
+    {
+        u32x2_t t = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        __builtin_nontemporal_store(t, reinterpret_cast<u32x2_t *>(p));
+    }
+};
+template <> struct VecNT<true, uint16_t, 8> {
+    static __device__ __forceinline__ void load(const uint16_t *p, float (&o)[8])
+    {
+        u32x4_t u = nt_load(reinterpret_cast<const u32x4_t *>(p));
+        unpack_bf16x2(u.x, o[0], o[1]);
+        unpack_bf16x2(u.y, o[2], o[3]);
+        unpack_bf16x2(u.z, o[4], o[5]);
+        unpack_bf16x2(u.w, o[6], o[7]);
+    }
+    static __device__ __forceinline__ void store(uint16_t *p, const float (&v)[8])
+    {
+        u32x4_t t = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                     pack_bf16x2(v[6], v[7])};
+        __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t *>(p));
+    }
+};
+
+template <bool NT, typename T, int V>
+__device__ __forceinline__ void ld(const T *p, float (&o)[V]) { VecNT<NT, T, V>::load(p, o); }
+template <bool NT, typename T, int V>
+__device__ __forceinline__ void st(T *p, const float (&v)[V]) { VecNT<NT, T, V>::store(p, v); }
+
 // ---- packed storage of V loaded elements -----------------------------------------
 // Keeps a loaded vector in its storage form (bf16 stays two-per-register) and
 // widens one element at a time, so a row held across a reduction costs
@@ -115,6 +203,7 @@ template <typename T, int V> struct Raw;
 template <int V> struct Raw<float, V> {
     float v[V];
     __device__ __forceinline__ void load(const float *p) { Vec<float, V>::load(p, v); }
+    __device__ __forceinline__ void load_nt(const float *p) { VecNT<true, float, V>::load(p, v); }
     __device__ __forceinline__ float get(int e) const { return v[e]; }
 };
 
@@ -131,6 +220,7 @@ template <int V> struct Raw<uint16_t, V> {
             u[0] = t.x; u[1] = t.y;
         }
     }
+    __device__ __forceinline__ void load_nt(const uint16_t *p);
     __device__ __forceinline__ float get(int e) const
     {
         const uint32_t w = u[e >> 1];
@@ -171,6 +261,18 @@ struct FastDiv {
         return (hi + n) >> s;
     }
 };
+
+template <int V>
+__device__ __forceinline__ void Raw<uint16_t, V>::load_nt(const uint16_t *p)
+{
+    if constexpr (V == 8) {
+        u32x4_t t = nt_load(reinterpret_cast<const u32x4_t *>(p));
+        u[0] = t.x; u[1] = t.y; u[2] = t.z; u[3] = t.w;
+    } else {
+        u32x2_t t = nt_load(reinterpret_cast<const u32x2_t *>(p));
+        u[0] = t.x; u[1] = t.y;
+    }
+}
 
 inline FastDiv make_fastdiv(uint32_t d)
 {

@@ -51,6 +51,7 @@ struct BnCall {
     int N, C, HW;
     int vec;             // vector width in elements (1, 4 or 8)
     int grid_y;          // blocks per channel of the reduction and elementwise passes
+    int separate_finalize;  // 1: finalize as its own kernel; 0: in the elementwise prologue
     const void *x;
     const void *dy;      // backward only
     void *out;           // y (forward) or dx (backward; may be NULL)
@@ -84,9 +85,11 @@ struct RowsCall {
 
 hipError_t rows_backward_launch(const RowsCall &a, hipStream_t s);
 
-// Block-size bound of a vector row-kernel variant: up to 4 teams when a
-// thread holds at most 16 elements of a row, else 2 (register budget).
-constexpr int rows_max_threads(int maxg, int vec) { return maxg * vec <= 16 ? 1024 : 512; }
+// Block-size bound of a vector row-kernel variant: 4 teams (128 VGPRs per
+// thread) when a thread holds at most 8 elements of a row, else 2 teams
+// (256 VGPRs): the row (two register sets when prefetching), the weights and
+// the column sums all live in registers.
+constexpr int rows_max_threads(int maxg, int vec) { return maxg * vec <= 8 ? 1024 : 512; }
 
 // ---- calibration --------------------------------------------------------------
 hipError_t calib_copy_launch(const void *src, void *dst, size_t bytes, int slots, hipStream_t s);

@@ -130,7 +130,11 @@ __device__ __forceinline__ void fold_and_write(float (&p)[Q][MAXG][VEC], float *
 }
 
 // ---- LayerNorm, vector path ----------------------------------------------------
-template <typename TX, typename TDY, typename TDX, int VEC, int MAXG, int MAXT>
+// PF: software-pipelined rows.  While a team reduces and writes row i, the
+// loads of its row i+1 are already in flight (two register sets, used
+// alternately), so each team keeps two rows of HBM traffic outstanding
+// across the block barrier of the row sum.
+template <typename TX, typename TDY, typename TDX, int VEC, int MAXG, int MAXT, bool PF>
 __global__ void __launch_bounds__(MAXT)
 ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
                const float *__restrict__ mean, const float *__restrict__ rstd,
@@ -160,20 +164,25 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
     }
 
     const int iters = (int)ceil_div(rows, (int64_t)G * teams);
-    for (int it = 0; it < iters; ++it) {
-        const int r = (it * G + (int)blockIdx.x) * teams + team;
-        const bool active = r < rows;
-        Raw<TX, VEC> xv[MAXG];
-        Raw<TDY, VEC> dv[MAXG];
+    auto row_of = [&](int it) { return (it * G + (int)blockIdx.x) * teams + team; };
+
+    auto load_row = [&](Raw<TX, VEC> (&xr)[MAXG], Raw<TDY, VEC> (&dr)[MAXG], int it) {
+        const int r = row_of(it);
+        if (r >= rows) return;
         const size_t rowoff = (size_t)r * H;
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
             const int grp = tt + k * kTeam;
-            if (active && grp < Gr) {
-                xv[k].load(x + rowoff + grp * VEC);
-                dv[k].load(dy + rowoff + grp * VEC);
+            if (grp < Gr) {
+                xr[k].load_nt(x + rowoff + grp * VEC);
+                dr[k].load_nt(dy + rowoff + grp * VEC);
             }
         }
+    };
+
+    auto do_row = [&](const Raw<TX, VEC> (&xr)[MAXG], const Raw<TDY, VEC> (&dr)[MAXG], int it) {
+        const int r = row_of(it);
+        const bool active = r < rows;
         const float mu = active ? mean[r] : 0.f;
         const float rs = active ? rstd[r] : 0.f;
         float a = 0.f, b = 0.f;
@@ -183,8 +192,8 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
             if (active && grp < Gr) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    const float d = dv[k].get(e);
-                    const float xh = (xv[k].get(e) - mu) * rs;
+                    const float d = dr[k].get(e);
+                    const float xh = (xr[k].get(e) - mu) * rs;
                     const float g = d * wv[k].get(e);
                     a += g;
                     b = fmaf(g, xh, b);
@@ -196,6 +205,7 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
         team_sum2(red + (it & 1) * (kRedFloats / 2), team, wave, lane, a, b);
         if (active && dx != nullptr) {
             const float ca = a * invH, cb = b * invH;
+            const size_t rowoff = (size_t)r * H;
 #pragma unroll
             for (int k = 0; k < MAXG; ++k) {
                 const int grp = tt + k * kTeam;
@@ -203,20 +213,40 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
                     float o[VEC];
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) {
-                        const float xh = (xv[k].get(e) - mu) * rs;
-                        const float g = dv[k].get(e) * wv[k].get(e);
+                        const float xh = (xr[k].get(e) - mu) * rs;
+                        const float g = dr[k].get(e) * wv[k].get(e);
                         o[e] = rs * fmaf(-xh, cb, g - ca);
                     }
-                    store_vec<TDX, VEC>(dx + rowoff + grp * VEC, o);
+                    st<true, TDX, VEC>(dx + rowoff + grp * VEC, o);
                 }
             }
+        }
+    };
+
+    Raw<TX, VEC> xa[MAXG];
+    Raw<TDY, VEC> da[MAXG];
+    if constexpr (PF) {
+        Raw<TX, VEC> xb[MAXG];
+        Raw<TDY, VEC> db[MAXG];
+        load_row(xa, da, 0);
+        for (int it = 0; it < iters; it += 2) {
+            if (it + 1 < iters) load_row(xb, db, it + 1);
+            do_row(xa, da, it);
+            if (it + 1 >= iters) break;
+            if (it + 2 < iters) load_row(xa, da, it + 2);
+            do_row(xb, db, it + 1);
+        }
+    } else {
+        for (int it = 0; it < iters; ++it) {
+            load_row(xa, da, it);
+            do_row(xa, da, it);
         }
     }
     if (want_cols) fold_and_write<VEC, MAXG, 2>(p, slot, teams, team, tt, Gr, H, G, partials);
 }
 
 // ---- RMSNorm, vector path ----------------------------------------------------
-template <typename T, int VEC, int MAXG, int MAXT>
+template <typename T, int VEC, int MAXG, int MAXT, bool PF>
 __global__ void __launch_bounds__(MAXT)
 rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
                 const float *__restrict__ rms, float eps, const void *__restrict__ w,
@@ -246,19 +276,25 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
     }
 
     const int iters = (int)ceil_div(rows, (int64_t)G * teams);
-    for (int it = 0; it < iters; ++it) {
-        const int r = (it * G + (int)blockIdx.x) * teams + team;
-        const bool active = r < rows;
-        Raw<T, VEC> xv[MAXG], dv[MAXG];
+    auto row_of = [&](int it) { return (it * G + (int)blockIdx.x) * teams + team; };
+
+    auto load_row = [&](Raw<T, VEC> (&xr)[MAXG], Raw<T, VEC> (&dr)[MAXG], int it) {
+        const int r = row_of(it);
+        if (r >= rows) return;
         const size_t rowoff = (size_t)r * H;
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
             const int grp = tt + k * kTeam;
-            if (active && grp < Gr) {
-                xv[k].load(x + rowoff + grp * VEC);
-                dv[k].load(dy + rowoff + grp * VEC);
+            if (grp < Gr) {
+                xr[k].load_nt(x + rowoff + grp * VEC);
+                dr[k].load_nt(dy + rowoff + grp * VEC);
             }
         }
+    };
+
+    auto do_row = [&](const Raw<T, VEC> (&xr)[MAXG], const Raw<T, VEC> (&dr)[MAXG], int it) {
+        const int r = row_of(it);
+        const bool active = r < rows;
         float s = 0.f, q = 0.f;  // sum g*x, sum x^2
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
@@ -266,8 +302,8 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
             if (active && grp < Gr) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    const float xe = xv[k].get(e);
-                    s = fmaf(dv[k].get(e) * wv[k].get(e), xe, s);
+                    const float xe = xr[k].get(e);
+                    s = fmaf(dr[k].get(e) * wv[k].get(e), xe, s);
                     q = fmaf(xe, xe, q);
                 }
             }
@@ -276,6 +312,7 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
         if (active) {
             const float rinv = rms != nullptr ? 1.0f / rms[r] : 1.0f / sqrtf(fmaf(q, invH, eps));
             const float c = rinv * rinv * rinv * s * invH;
+            const size_t rowoff = (size_t)r * H;
 #pragma unroll
             for (int k = 0; k < MAXG; ++k) {
                 const int grp = tt + k * kTeam;
@@ -283,14 +320,32 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
                     float o[VEC];
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) {
-                        const float xe = xv[k].get(e);
-                        const float d = dv[k].get(e);
+                        const float xe = xr[k].get(e);
+                        const float d = dr[k].get(e);
                         o[e] = fmaf(-xe, c, rinv * (d * wv[k].get(e)));
                         p[0][k][e] = fmaf(d * xe, rinv, p[0][k][e]);
                     }
-                    if (dx != nullptr) store_vec<T, VEC>(dx + rowoff + grp * VEC, o);
+                    if (dx != nullptr) st<true, T, VEC>(dx + rowoff + grp * VEC, o);
                 }
             }
+        }
+    };
+
+    Raw<T, VEC> xa[MAXG], da[MAXG];
+    if constexpr (PF) {
+        Raw<T, VEC> xb[MAXG], db[MAXG];
+        load_row(xa, da, 0);
+        for (int it = 0; it < iters; it += 2) {
+            if (it + 1 < iters) load_row(xb, db, it + 1);
+            do_row(xa, da, it);
+            if (it + 1 >= iters) break;
+            if (it + 2 < iters) load_row(xa, da, it + 2);
+            do_row(xb, db, it + 1);
+        }
+    } else {
+        for (int it = 0; it < iters; ++it) {
+            load_row(xa, da, it);
+            do_row(xa, da, it);
         }
     }
     if (want_cols) fold_and_write<VEC, MAXG, 1>(p, slot, teams, team, tt, Gr, H, G, partials);
@@ -368,8 +423,8 @@ rows_generic_kernel(int kind, const TDY *__restrict__ dy, const TX *__restrict__
 }
 
 // ---- column finalize: fp64 fixed-order sum of the G partial rows -------------
-constexpr int kColX = 64;   // columns per block
-constexpr int kColY = 16;   // slices of the G partial rows
+constexpr int kColX = 32;   // columns per block (one 128-byte line of a partial row)
+constexpr int kColY = 32;   // slices of the G partial rows
 template <typename TOUT>
 __global__ void __launch_bounds__(kColX * kColY)
 rows_colsum_kernel(const float *__restrict__ partials, int G, int H, TOUT *__restrict__ out0,
@@ -383,8 +438,10 @@ rows_colsum_kernel(const float *__restrict__ partials, int G, int H, TOUT *__res
     const int ty = threadIdx.x / kColX;
     const int j = blockIdx.x * kColX + tx;
     double s = 0.0;
-    if (j < H)
+    if (j < H) {
+#pragma unroll 4
         for (int b = ty; b < G; b += kColY) s += (double)partials[((size_t)q * G + b) * H + j];
+    }
     acc[ty][tx] = s;
     __syncthreads();
     if (ty == 0 && j < H) {
@@ -407,7 +464,8 @@ template <typename TX, typename TDY, typename TDX, int VEC, int MAXG>
 static hipError_t ln_vec(const RowsCall &a, hipStream_t s)
 {
     constexpr int MT = rows_max_threads(MAXG, VEC);
-    return launch(NH_K_LN_ROWS, ln_rows_kernel<TX, TDY, TDX, VEC, MAXG, MT>, dim3(a.blocks),
+    constexpr bool PF = MAXG * VEC <= 16;
+    return launch(NH_K_LN_ROWS, ln_rows_kernel<TX, TDY, TDX, VEC, MAXG, MT, PF>, dim3(a.blocks),
                   dim3(a.teams * kTeam), (uint32_t)lds_bytes(a), s,
                   static_cast<const TDY *>(a.dy), static_cast<const TX *>(a.x), a.mean, a.rstd,
                   a.w, a.w_t, a.rows, a.cols, static_cast<TDX *>(a.dx), a.partials,
@@ -418,16 +476,16 @@ template <typename T, int VEC, int MAXG>
 static hipError_t rms_vec(const RowsCall &a, hipStream_t s)
 {
     constexpr int MT = rows_max_threads(MAXG, VEC);
-    return launch(NH_K_RMS_ROWS, rms_rows_kernel<T, VEC, MAXG, MT>, dim3(a.blocks),
+    constexpr bool PF = MAXG * VEC * (int)sizeof(T) <= 64;
+    return launch(NH_K_RMS_ROWS, rms_rows_kernel<T, VEC, MAXG, MT, PF>, dim3(a.blocks),
                   dim3(a.teams * kTeam), (uint32_t)lds_bytes(a), s,
                   static_cast<const T *>(a.dy), static_cast<const T *>(a.x), a.rms, a.eps, a.w,
                   a.w_t, a.rows, a.cols, static_cast<T *>(a.dx), a.partials,
                   (int)(a.dweight != nullptr));
 }
 
-// LayerNorm keeps two column sums per element, so its widest vector variant
-// holds 32 elements per thread (MAXG = 8 only with 4-element groups); the
-// planner sends wider rows to the generic path.
+// The widest vector variant holds 32 row elements per thread (MAXG = 8 only
+// with 4-element groups); the planner sends wider rows to the generic path.
 template <typename TX, typename TDY, typename TDX, int VEC>
 static hipError_t ln_maxg(const RowsCall &a, hipStream_t s)
 {
@@ -441,6 +499,8 @@ static hipError_t ln_maxg(const RowsCall &a, hipStream_t s)
     }
 }
 
+// A thread holds at most 32 row elements in the vector path (64 would not
+// fit the registers); the planner sends wider rows to the generic path.
 template <typename T, int VEC>
 static hipError_t rms_maxg(const RowsCall &a, hipStream_t s)
 {
@@ -448,7 +508,9 @@ static hipError_t rms_maxg(const RowsCall &a, hipStream_t s)
     case 1: return rms_vec<T, VEC, 1>(a, s);
     case 2: return rms_vec<T, VEC, 2>(a, s);
     case 4: return rms_vec<T, VEC, 4>(a, s);
-    default: return rms_vec<T, VEC, 8>(a, s);
+    default:
+        if constexpr (VEC == 4) return rms_vec<T, VEC, 8>(a, s);
+        return hipErrorInvalidValue;
     }
 }
 

@@ -29,7 +29,7 @@ EXPORTS = [
     "bn_forward_train_workspace", "bn_backward_workspace", "bn_forward_train", "bn_backward",
     "layernorm_backward_workspace", "layernorm_backward",
     "rmsnorm_backward_workspace", "rmsnorm_backward",
-    "nh_timing_enable", "nh_timing_read", "nh_calib_copy", "nh_calib_add",
+    "nh_timing_enable", "nh_timing_reserve", "nh_timing_read", "nh_calib_copy", "nh_calib_add",
     "nh_bn_plan", "nh_rows_plan", "nh_plan_override", "nh_selftest_host",
 ]
 
@@ -61,6 +61,7 @@ def _load():
         "rmsnorm_backward_workspace": (i32, [i64, i64, psz]),
         "rmsnorm_backward": (i32, [p, p, i32, p, f32, p, i64, i64, p, p, p, sz, p]),
         "nh_timing_enable": (i32, [i32]),
+        "nh_timing_reserve": (i32, [i64]),
         "nh_timing_read": (i32, [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
         "nh_calib_copy": (i32, [p, p, sz, p]),
         "nh_calib_add": (i32, [p, p, p, i64, p]),
@@ -271,6 +272,10 @@ def rmsnorm_backward(dy, x, rms=None, weight=None, eps: float = 1e-5, *, need_dx
 # ---- measurement --------------------------------------------------------------------------
 def timing_enable(on: bool):
     _check(lib.nh_timing_enable(1 if on else 0), "nh_timing_enable")
+
+
+def timing_reserve(launches: int):
+    _check(lib.nh_timing_reserve(launches), "nh_timing_reserve")
 
 
 def timing_read(kernel) -> tuple[float, int]:

@@ -215,6 +215,9 @@ const char *nh_kernel_name(int kernel);
  * launches normhip kernels that should not be counted.
  */
 nh_status nh_timing_enable(int on);
+/* Pre-creates events for `launches` timed launches so that event creation
+ * does not fall inside a timed region. */
+nh_status nh_timing_reserve(int64_t launches);
 nh_status nh_timing_read(int kernel, double *total_ms, int64_t *launches);
 
 /*
@@ -243,9 +246,12 @@ nh_status nh_rows_plan(int64_t rows, int64_t cols, int *blocks);
 
 /*
  * Plan overrides for tests and tuning sweeps: key "bn_grid_y" forces the
- * BatchNorm blocks per channel (capped to what the workspace allows), key
- * "rows_blocks" forces the row-kernel block count.  value 0 restores the
- * automatic plan.  Process-wide; not for concurrent use with other calls.
+ * BatchNorm blocks per channel, key "rows_blocks" forces the row-kernel
+ * block count (both also size the workspace queried afterwards), key
+ * "bn_finalize_kernels" = 1 runs the BatchNorm finalize steps as separate
+ * kernels instead of inside the elementwise kernels (same results).  value 0
+ * restores the automatic plan.  Process-wide; not for concurrent use with
+ * other calls.
  */
 nh_status nh_plan_override(const char *key, int64_t value);
 

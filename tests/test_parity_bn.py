@@ -153,10 +153,14 @@ def test_bn_misaligned_pointers(nh, oracle_mod):
     _compare(c, got, want)
 
 
-def test_bn_in_place(nh, oracle_mod):
-    """y may overwrite x, dx may overwrite dy."""
-    c = wl.bn_case(2, 8, 16, 16, wl.BF16, seed=45)
-    print("[bn parity] in place", flush=True)
+@pytest.mark.parametrize("shape,io", [((2, 8, 16, 16), wl.BF16), ((16, 8, 32, 32), wl.F32),
+                                      ((64, 3, 30, 30), wl.BF16)])
+def test_bn_in_place(nh, oracle_mod, shape, io):
+    """y may overwrite x, dx may overwrite dy, also when a channel spans
+    several blocks (the shift x[0,c,0,0] is overwritten by the apply pass)."""
+    c = wl.bn_case(*shape, io, seed=45)
+    print(f"[bn parity] in place {shape} {io} grid_y={nh.bn_plan(c.N, c.C, c.hw, 0 if io == wl.F32 else 1)}",
+          flush=True)
     want = _oracle_bn(oracle_mod, c)
     x_fwd, x_bwd, dy = dev(c.x), dev(c.x), dev(c.dy)
     rm, rv = dev(c.running_mean), dev(c.running_var)
@@ -252,3 +256,21 @@ def test_bn_bit_identical_runs(nh, name):
         outs.append(_gpu_bn(nh, c))
     for k in outs[0]:
         assert np.array_equal(outs[0][k].view(np.uint64), outs[1][k].view(np.uint64)), k
+
+
+@pytest.mark.parametrize("name", ["ragged_3x37x41x40_f32", "cifar_256x32x32x32_bf16",
+                                  "one_channel_64x1x128x128_f32"])
+def test_bn_separate_finalize_kernels_match_fused(nh, oracle_mod, name):
+    """The finalize step as its own kernels (the three-launch structure) gives
+    the same bits as the finalize folded into the elementwise kernels."""
+    c = CASES[name]()
+    print(f"[bn parity] separate finalize kernels {name}", flush=True)
+    fused = _gpu_bn(nh, c)
+    nh.plan_override("bn_finalize_kernels", 1)
+    try:
+        separate = _gpu_bn(nh, c)
+    finally:
+        nh.plan_override("bn_finalize_kernels", 0)
+    _compare(c, separate, _oracle_bn(oracle_mod, c))
+    for k in fused:
+        assert np.array_equal(fused[k].view(np.uint64), separate[k].view(np.uint64)), k

@@ -163,7 +163,7 @@ def test_rms_full_config(nh, oracle_mod, dt, saved):
     (3, 8, wl.BF16),
     (257, 1024, wl.F32),
     (100, 2048, wl.BF16),
-    (40, 16384, wl.BF16),   # 8 groups per thread (bf16)
+    (40, 16384, wl.BF16),   # 64 elements per thread: generic path
     (20, 12288, wl.F32),    # wider than the fp32 vector path: generic
     (31, 999, wl.F32),      # ragged width: generic
     (17, 4100, wl.BF16),    # ragged groups per thread
