@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <map>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -60,6 +61,7 @@ struct DeviceInfo {
 
 std::mutex g_dev_mu;
 DeviceInfo g_dev[64];
+std::map<int64_t, int> g_rows_occupancy;  // (device, variant) -> blocks per CU
 
 nh_status device_info(DeviceInfo *out)
 {
@@ -138,10 +140,12 @@ struct RowsPlan {
     int blocks = 0;
 };
 
+// Upper bound of the row kernels' block count G (the workspace holds G
+// column-partial rows): kRowsMaxBlocksPerCu per CU, at most one per row.
 int64_t rows_blocks_max(int64_t rows, const DeviceInfo &d)
 {
     const int64_t ov = g_override_rows_blocks.load();
-    int64_t g = ov > 0 ? ov : d.cus;
+    int64_t g = ov > 0 ? ov : (int64_t)d.cus * kRowsMaxBlocksPerCu;
     if (g > rows) g = rows;
     return g;
 }
@@ -151,7 +155,9 @@ size_t rows_ws_bytes(int Q, int64_t rows, int64_t cols, const DeviceInfo &d)
     return round_up((size_t)(Q * rows_blocks_max(rows, d) * cols) * sizeof(float), 256);
 }
 
-RowsPlan rows_plan(int Q, int64_t rows, int64_t cols, int vec, bool vec_ok, const DeviceInfo &d)
+// Kernel variant for a row width: vector groups per thread (maxg, 0 = the
+// generic path) and the group width.  One 256-thread team per block.
+RowsPlan rows_variant(int64_t cols, int vec, bool vec_ok)
 {
     RowsPlan p;
     p.vec = vec;
@@ -161,24 +167,27 @@ RowsPlan rows_plan(int Q, int64_t rows, int64_t cols, int vec, bool vec_ok, cons
         int mg = 1;
         while (mg < per_thread) mg <<= 1;
         // A thread holds at most 32 row elements in registers.
-        if (mg <= 8 && mg * vec <= 32) {
-            p.maxg = mg;
-            p.teams = rows_max_threads(mg, vec) / 256;
-            // LDS: row-sum buffer + one team-fold slot of Q*cols floats.
-            const size_t lds_cap = d.lds_per_block < 65536 ? d.lds_per_block : 65536;
-            if ((size_t)(64 + Q * cols) * sizeof(float) > lds_cap) p.teams = 1;
-        }
+        if (mg <= 8 && mg * vec <= 32) p.maxg = mg;
     }
-    if (p.maxg == 0) {
-        p.vec = 1;
-        p.teams = 1;
-    }
-    int64_t g = ceil_div(rows, p.teams);
-    const int64_t gmax = rows_blocks_max(rows, d);
-    if (g > gmax) g = gmax;
+    if (p.maxg == 0) p.vec = 1;
+    p.teams = 1;
+    return p;
+}
+
+// Blocks: as many as fit on the device at once (occupancy of the chosen
+// variant, at most kRowsMaxBlocksPerCu per CU), at most one per row.
+// Measured on MI355X: single-team blocks filling the CU beat fewer, wider
+// blocks that synchronize more waves per row.
+void rows_grid(RowsPlan &p, int64_t rows, int occ, const DeviceInfo &d)
+{
+    if (occ < 1) occ = 1;
+    if (occ > kRowsMaxBlocksPerCu) occ = kRowsMaxBlocksPerCu;
+    int64_t g = (int64_t)d.cus * occ;
+    const int64_t ov = g_override_rows_blocks.load();
+    if (ov > 0) g = ov;
+    if (g > rows) g = rows;
     if (g < 1) g = 1;
     p.blocks = (int)g;
-    return p;
 }
 
 // ---- timing --------------------------------------------------------------------------
@@ -405,12 +414,34 @@ static nh_status rows_run(RowsCall &a, int Q, void *ws, size_t ws_bytes, void *s
     need_align(a.dy, a.dy_t);
     need_align(a.dx, a.dx_t);
     need_align(a.w, a.w_t);
-    const RowsPlan p = rows_plan(Q, a.rows, a.cols, a.vec, vec_ok, d);
+    RowsPlan p = rows_variant(a.cols, a.vec, vec_ok);
     a.maxg = p.maxg;
     a.vec = p.vec;
     a.teams = p.teams;
+    // Occupancy of the chosen variant, cached per device and variant.
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const int dxt = a.dx != nullptr ? a.dx_t : a.dy_t;
+    const int64_t key = ((((((int64_t)dev * 2 + a.kind) * 2 + a.x_t) * 2 + a.dy_t) * 2 + dxt) * 16 +
+                         a.maxg) * 16 + a.vec;
+    int occ = 0;
+    {
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        auto it = g_rows_occupancy.find(key);
+        if (it != g_rows_occupancy.end()) occ = it->second;
+    }
+    hipError_t e = hipSuccess;
+    if (occ == 0) {
+        a.occupancy_out = &occ;
+        e = rows_backward_launch(a, s);
+        a.occupancy_out = nullptr;
+        if (e != hipSuccess) return hip_fail(e, "row kernel occupancy query");
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        g_rows_occupancy[key] = occ;
+    }
+    rows_grid(p, a.rows, occ, d);
     a.blocks = p.blocks;
-    hipError_t e = rows_backward_launch(a, s);
+    e = rows_backward_launch(a, s);
     if (e != hipSuccess) return hip_fail(e, "rows backward launch");
     return ok();
 }

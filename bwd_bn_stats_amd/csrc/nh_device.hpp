@@ -200,10 +200,15 @@ __device__ __forceinline__ void st(T *p, const float (&v)[V]) { VecNT<NT, T, V>:
 // V*sizeof(T) bytes of registers, not V*4.
 template <typename T, int V> struct Raw;
 
+template <typename T, int V> struct BufLoad;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes);
+
 template <int V> struct Raw<float, V> {
     float v[V];
     __device__ __forceinline__ void load(const float *p) { Vec<float, V>::load(p, v); }
     __device__ __forceinline__ void load_nt(const float *p) { VecNT<true, float, V>::load(p, v); }
+    // Nontemporal, range-checked load at byte offset `off` of buffer `r`.
+    __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, int off) { BufLoad<float, V>::load(r, off, v); }
     __device__ __forceinline__ float get(int e) const { return v[e]; }
 };
 
@@ -221,6 +226,7 @@ template <int V> struct Raw<uint16_t, V> {
         }
     }
     __device__ __forceinline__ void load_nt(const uint16_t *p);
+    __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, int off);
     __device__ __forceinline__ float get(int e) const
     {
         const uint32_t w = u[e >> 1];
@@ -239,6 +245,18 @@ __device__ __forceinline__ T wave_sum(T v)
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
     return v;
+}
+
+// ---- workgroup barrier for LDS traffic only ---------------------------------------
+// __syncthreads() orders every address space, so it also waits for all of the
+// wave's outstanding global loads (s_waitcnt vmcnt(0)) -- including loads
+// issued ahead for the next row.  Where only LDS data is exchanged, fence LDS
+// alone: the barrier then leaves prefetched global loads in flight.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // ---- fast unsigned division by a run-time invariant --------------------------
@@ -262,6 +280,42 @@ struct FastDiv {
     }
 };
 
+// ---- buffer loads: range-checked without branches ----------------------------------
+// A raw buffer resource covers [base, base + bytes); a load at an offset past
+// that range returns zeros and touches no memory.  Loads guarded this way
+// stay in straight-line code, which lets the compiler wait for exactly the
+// older loads instead of draining all of them at every control-flow merge.
+// The descriptor's last word (0x00020000: 32-bit data format, raw access) is
+// the gfx9-family value; aux = 2 sets the nontemporal bit.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kBufferNT = 2;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
+template <typename T, int V> struct BufLoad;
+template <> struct BufLoad<float, 4> {
+    static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int off, float (&o)[4])
+    {
+        u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kBufferNT);
+        o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+        o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+    }
+};
+template <> struct BufLoad<float, 8> {
+    static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int off, float (&o)[8])
+    {
+        u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kBufferNT);
+        u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, kBufferNT);
+        o[0] = __uint_as_float(a.x); o[1] = __uint_as_float(a.y);
+        o[2] = __uint_as_float(a.z); o[3] = __uint_as_float(a.w);
+        o[4] = __uint_as_float(b.x); o[5] = __uint_as_float(b.y);
+        o[6] = __uint_as_float(b.z); o[7] = __uint_as_float(b.w);
+    }
+};
+
 template <int V>
 __device__ __forceinline__ void Raw<uint16_t, V>::load_nt(const uint16_t *p)
 {
@@ -270,6 +324,18 @@ __device__ __forceinline__ void Raw<uint16_t, V>::load_nt(const uint16_t *p)
         u[0] = t.x; u[1] = t.y; u[2] = t.z; u[3] = t.w;
     } else {
         u32x2_t t = nt_load(reinterpret_cast<const u32x2_t *>(p));
+        u[0] = t.x; u[1] = t.y;
+    }
+}
+
+template <int V>
+__device__ __forceinline__ void Raw<uint16_t, V>::load_buf(__amdgpu_buffer_rsrc_t r, int off)
+{
+    if constexpr (V == 8) {
+        u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kBufferNT);
+        u[0] = t.x; u[1] = t.y; u[2] = t.z; u[3] = t.w;
+    } else {
+        u32x2_t t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kBufferNT);
         u[0] = t.x; u[1] = t.y;
     }
 }

@@ -81,6 +81,8 @@ struct RowsCall {
     float eps;
     void *dx, *dweight, *dbias;
     float *partials;     // [Q, G, cols]
+    int *occupancy_out;  // non-NULL: report resident 256-thread blocks per CU
+                         // of the selected row kernel instead of launching
 };
 
 hipError_t rows_backward_launch(const RowsCall &a, hipStream_t s);
@@ -90,6 +92,7 @@ hipError_t rows_backward_launch(const RowsCall &a, hipStream_t s);
 // (256 VGPRs): the row (two register sets when prefetching), the weights and
 // the column sums all live in registers.
 constexpr int rows_max_threads(int maxg, int vec) { return maxg * vec <= 8 ? 1024 : 512; }
+constexpr int kRowsMaxBlocksPerCu = 4;  // bound on the column-partial rows per CU
 
 // ---- calibration --------------------------------------------------------------
 hipError_t calib_copy_launch(const void *src, void *dst, size_t bytes, int slots, hipStream_t s);

@@ -72,7 +72,7 @@ __device__ __forceinline__ void team_sum2(float *red, int team, int wave, int la
         red[(team * kTeamWaves + wave) * 2 + 0] = a;
         red[(team * kTeamWaves + wave) * 2 + 1] = b;
     }
-    __syncthreads();
+    lds_barrier();
     float sa = red[(team * kTeamWaves) * 2 + 0];
     float sb = red[(team * kTeamWaves) * 2 + 1];
 #pragma unroll
@@ -166,45 +166,57 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
     const int iters = (int)ceil_div(rows, (int64_t)G * teams);
     auto row_of = [&](int it) { return (it * G + (int)blockIdx.x) * teams + team; };
 
-    auto load_row = [&](Raw<TX, VEC> (&xr)[MAXG], Raw<TDY, VEC> (&dr)[MAXG], int it) {
-        const int r = row_of(it);
-        if (r >= rows) return;
-        const size_t rowoff = (size_t)r * H;
+    // One row in flight: its x/dy groups and its saved statistics.  The row
+    // is read through buffer resources sized to the row (empty past the last
+    // row), so the loads need no branches: out-of-range groups and rows read
+    // as zeros without memory traffic, and the compiler can wait for exactly
+    // the older row's loads while the next row's are in flight.
+    struct RowBuf {
+        Raw<TX, VEC> x[MAXG];
+        Raw<TDY, VEC> d[MAXG];
+        float mu, rs;
+    };
+    auto load_row = [&](RowBuf &b, int it) {
+        const int r = __builtin_amdgcn_readfirstlane(row_of(it));
+        const bool live = r < rows;
+        const int rc = live ? r : rows - 1;
+        const size_t rowoff = (size_t)rc * H;
+        const auto rx = make_rsrc(x + rowoff, live ? (uint32_t)(H * sizeof(TX)) : 0u);
+        const auto rd = make_rsrc(dy + rowoff, live ? (uint32_t)(H * sizeof(TDY)) : 0u);
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
             const int grp = tt + k * kTeam;
-            if (grp < Gr) {
-                xr[k].load_nt(x + rowoff + grp * VEC);
-                dr[k].load_nt(dy + rowoff + grp * VEC);
-            }
+            b.x[k].load_buf(rx, grp * VEC * (int)sizeof(TX));
+            b.d[k].load_buf(rd, grp * VEC * (int)sizeof(TDY));
         }
+        b.mu = mean[rc];
+        b.rs = rstd[rc];
     };
 
-    auto do_row = [&](const Raw<TX, VEC> (&xr)[MAXG], const Raw<TDY, VEC> (&dr)[MAXG], int it) {
+    auto do_row = [&](const RowBuf &b, int it) {
         const int r = row_of(it);
         const bool active = r < rows;
-        const float mu = active ? mean[r] : 0.f;
-        const float rs = active ? rstd[r] : 0.f;
-        float a = 0.f, b = 0.f;
+        const float mu = b.mu, rs = b.rs;
+        float a = 0.f, bb = 0.f;
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
             const int grp = tt + k * kTeam;
             if (active && grp < Gr) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    const float d = dr[k].get(e);
-                    const float xh = (xr[k].get(e) - mu) * rs;
+                    const float d = b.d[k].get(e);
+                    const float xh = (b.x[k].get(e) - mu) * rs;
                     const float g = d * wv[k].get(e);
                     a += g;
-                    b = fmaf(g, xh, b);
+                    bb = fmaf(g, xh, bb);
                     p[0][k][e] = fmaf(d, xh, p[0][k][e]);
                     p[1][k][e] += d;
                 }
             }
         }
-        team_sum2(red + (it & 1) * (kRedFloats / 2), team, wave, lane, a, b);
+        team_sum2(red + (it & 1) * (kRedFloats / 2), team, wave, lane, a, bb);
         if (active && dx != nullptr) {
-            const float ca = a * invH, cb = b * invH;
+            const float ca = a * invH, cb = bb * invH;
             const size_t rowoff = (size_t)r * H;
 #pragma unroll
             for (int k = 0; k < MAXG; ++k) {
@@ -213,8 +225,8 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
                     float o[VEC];
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) {
-                        const float xh = (xr[k].get(e) - mu) * rs;
-                        const float g = dr[k].get(e) * wv[k].get(e);
+                        const float xh = (b.x[k].get(e) - mu) * rs;
+                        const float g = b.d[k].get(e) * wv[k].get(e);
                         o[e] = rs * fmaf(-xh, cb, g - ca);
                     }
                     st<true, TDX, VEC>(dx + rowoff + grp * VEC, o);
@@ -223,23 +235,22 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
         }
     };
 
-    Raw<TX, VEC> xa[MAXG];
-    Raw<TDY, VEC> da[MAXG];
+    RowBuf ba;
     if constexpr (PF) {
-        Raw<TX, VEC> xb[MAXG];
-        Raw<TDY, VEC> db[MAXG];
-        load_row(xa, da, 0);
+        RowBuf bb;
+        // Prefetches past the last row are empty buffer loads: no branch.
+        load_row(ba, 0);
         for (int it = 0; it < iters; it += 2) {
-            if (it + 1 < iters) load_row(xb, db, it + 1);
-            do_row(xa, da, it);
+            load_row(bb, it + 1);
+            do_row(ba, it);
             if (it + 1 >= iters) break;
-            if (it + 2 < iters) load_row(xa, da, it + 2);
-            do_row(xb, db, it + 1);
+            load_row(ba, it + 2);
+            do_row(bb, it + 1);
         }
     } else {
         for (int it = 0; it < iters; ++it) {
-            load_row(xa, da, it);
-            do_row(xa, da, it);
+            load_row(ba, it);
+            do_row(ba, it);
         }
     }
     if (want_cols) fold_and_write<VEC, MAXG, 2>(p, slot, teams, team, tt, Gr, H, G, partials);
@@ -278,40 +289,49 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
     const int iters = (int)ceil_div(rows, (int64_t)G * teams);
     auto row_of = [&](int it) { return (it * G + (int)blockIdx.x) * teams + team; };
 
-    auto load_row = [&](Raw<T, VEC> (&xr)[MAXG], Raw<T, VEC> (&dr)[MAXG], int it) {
-        const int r = row_of(it);
-        if (r >= rows) return;
-        const size_t rowoff = (size_t)r * H;
+    // One row in flight (see the LayerNorm kernel: branch-free buffer loads).
+    struct RowBuf {
+        Raw<T, VEC> x[MAXG];
+        Raw<T, VEC> d[MAXG];
+        float rms;
+    };
+    auto load_row = [&](RowBuf &b, int it) {
+        const int r = __builtin_amdgcn_readfirstlane(row_of(it));
+        const bool live = r < rows;
+        const int rc = live ? r : rows - 1;
+        const size_t rowoff = (size_t)rc * H;
+        const uint32_t nbytes = live ? (uint32_t)(H * sizeof(T)) : 0u;
+        const auto rx = make_rsrc(x + rowoff, nbytes);
+        const auto rd = make_rsrc(dy + rowoff, nbytes);
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
             const int grp = tt + k * kTeam;
-            if (grp < Gr) {
-                xr[k].load_nt(x + rowoff + grp * VEC);
-                dr[k].load_nt(dy + rowoff + grp * VEC);
-            }
+            b.x[k].load_buf(rx, grp * VEC * (int)sizeof(T));
+            b.d[k].load_buf(rd, grp * VEC * (int)sizeof(T));
         }
+        b.rms = rms != nullptr ? rms[rc] : 0.f;
     };
 
-    auto do_row = [&](const Raw<T, VEC> (&xr)[MAXG], const Raw<T, VEC> (&dr)[MAXG], int it) {
+    auto do_row = [&](const RowBuf &b, int it) {
         const int r = row_of(it);
         const bool active = r < rows;
-        float s = 0.f, q = 0.f;  // sum g*x, sum x^2
+        float sgx = 0.f, q = 0.f;  // sum g*x, sum x^2
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
             const int grp = tt + k * kTeam;
             if (active && grp < Gr) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    const float xe = xr[k].get(e);
-                    s = fmaf(dr[k].get(e) * wv[k].get(e), xe, s);
+                    const float xe = b.x[k].get(e);
+                    sgx = fmaf(b.d[k].get(e) * wv[k].get(e), xe, sgx);
                     q = fmaf(xe, xe, q);
                 }
             }
         }
-        team_sum2(red + (it & 1) * (kRedFloats / 2), team, wave, lane, s, q);
+        team_sum2(red + (it & 1) * (kRedFloats / 2), team, wave, lane, sgx, q);
         if (active) {
-            const float rinv = rms != nullptr ? 1.0f / rms[r] : 1.0f / sqrtf(fmaf(q, invH, eps));
-            const float c = rinv * rinv * rinv * s * invH;
+            const float rinv = rms != nullptr ? 1.0f / b.rms : 1.0f / sqrtf(fmaf(q, invH, eps));
+            const float c = rinv * rinv * rinv * sgx * invH;
             const size_t rowoff = (size_t)r * H;
 #pragma unroll
             for (int k = 0; k < MAXG; ++k) {
@@ -320,8 +340,8 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
                     float o[VEC];
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) {
-                        const float xe = xr[k].get(e);
-                        const float d = dr[k].get(e);
+                        const float xe = b.x[k].get(e);
+                        const float d = b.d[k].get(e);
                         o[e] = fmaf(-xe, c, rinv * (d * wv[k].get(e)));
                         p[0][k][e] = fmaf(d * xe, rinv, p[0][k][e]);
                     }
@@ -331,21 +351,22 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
         }
     };
 
-    Raw<T, VEC> xa[MAXG], da[MAXG];
+    RowBuf ba;
     if constexpr (PF) {
-        Raw<T, VEC> xb[MAXG], db[MAXG];
-        load_row(xa, da, 0);
+        RowBuf bb;
+        // Prefetches past the last row are empty buffer loads: no branch.
+        load_row(ba, 0);
         for (int it = 0; it < iters; it += 2) {
-            if (it + 1 < iters) load_row(xb, db, it + 1);
-            do_row(xa, da, it);
+            load_row(bb, it + 1);
+            do_row(ba, it);
             if (it + 1 >= iters) break;
-            if (it + 2 < iters) load_row(xa, da, it + 2);
-            do_row(xb, db, it + 1);
+            load_row(ba, it + 2);
+            do_row(bb, it + 1);
         }
     } else {
         for (int it = 0; it < iters; ++it) {
-            load_row(xa, da, it);
-            do_row(xa, da, it);
+            load_row(ba, it);
+            do_row(ba, it);
         }
     }
     if (want_cols) fold_and_write<VEC, MAXG, 1>(p, slot, teams, team, tt, Gr, H, G, partials);
@@ -460,11 +481,21 @@ static inline int lds_bytes(const RowsCall &a)
 }
 
 
+// With a.occupancy_out set, report how many 256-thread blocks of `kernel`
+// fit on a CU (registers, LDS) instead of launching it.
+template <typename K>
+static hipError_t occupancy(const RowsCall &a, K kernel)
+{
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kernel, kTeam,
+                                                        (size_t)lds_bytes(a));
+}
+
 template <typename TX, typename TDY, typename TDX, int VEC, int MAXG>
 static hipError_t ln_vec(const RowsCall &a, hipStream_t s)
 {
     constexpr int MT = rows_max_threads(MAXG, VEC);
     constexpr bool PF = MAXG * VEC <= 16;
+    if (a.occupancy_out) return occupancy(a, ln_rows_kernel<TX, TDY, TDX, VEC, MAXG, MT, PF>);
     return launch(NH_K_LN_ROWS, ln_rows_kernel<TX, TDY, TDX, VEC, MAXG, MT, PF>, dim3(a.blocks),
                   dim3(a.teams * kTeam), (uint32_t)lds_bytes(a), s,
                   static_cast<const TDY *>(a.dy), static_cast<const TX *>(a.x), a.mean, a.rstd,
@@ -477,6 +508,7 @@ static hipError_t rms_vec(const RowsCall &a, hipStream_t s)
 {
     constexpr int MT = rows_max_threads(MAXG, VEC);
     constexpr bool PF = MAXG * VEC * (int)sizeof(T) <= 64;
+    if (a.occupancy_out) return occupancy(a, rms_rows_kernel<T, VEC, MAXG, MT, PF>);
     return launch(NH_K_RMS_ROWS, rms_rows_kernel<T, VEC, MAXG, MT, PF>, dim3(a.blocks),
                   dim3(a.teams * kTeam), (uint32_t)lds_bytes(a), s,
                   static_cast<const T *>(a.dy), static_cast<const T *>(a.x), a.rms, a.eps, a.w,
@@ -524,6 +556,7 @@ template <typename TX, typename TDY, typename TDX>
 static hipError_t generic_launch(const RowsCall &a, hipStream_t s)
 {
     const int want = a.kind == 0 ? (a.dweight != nullptr || a.dbias != nullptr) : (a.dweight != nullptr);
+    if (a.occupancy_out) return occupancy(a, rows_generic_kernel<TX, TDY, TDX>);
     return launch(a.kind == 0 ? NH_K_LN_ROWS : NH_K_RMS_ROWS, rows_generic_kernel<TX, TDY, TDX>,
                   dim3(a.blocks), dim3(kTeam), 0u, s, a.kind, static_cast<const TDY *>(a.dy),
                   static_cast<const TX *>(a.x), a.mean, a.rstd, a.rms, a.eps, a.w, a.w_t, a.rows,
@@ -578,7 +611,7 @@ hipError_t rows_backward_launch(const RowsCall &a, hipStream_t s)
     } else {
         e = a.x_t == 0 ? rms_maxg<float, 4>(a, s) : rms_maxg<uint16_t, 8>(a, s);
     }
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || a.occupancy_out) return e;
     const bool cols = a.kind == 0 ? (a.dweight != nullptr || a.dbias != nullptr) : a.dweight != nullptr;
     if (!cols) return hipSuccess;
     const int kid = a.kind == 0 ? NH_K_LN_COLSUM : NH_K_RMS_COLSUM;

@@ -240,8 +240,9 @@ nh_status nh_calib_add(const float *a, const float *b, float *out, int64_t n, vo
  */
 nh_status nh_bn_plan(int64_t N, int64_t C, int64_t HW, nh_dtype io, int *grid_y);
 
-/* Row-kernel plan: the number of blocks G (column-partial rows) used for a
- * [rows, cols] LayerNorm or RMSNorm backward on the current device. */
+/* Row-kernel plan: the largest number of blocks G (column-partial rows) a
+ * [rows, cols] LayerNorm or RMSNorm backward uses on the current device
+ * (the workspace is sized for it; the dtypes decide the actual G). */
 nh_status nh_rows_plan(int64_t rows, int64_t cols, int *blocks);
 
 /*
