@@ -274,6 +274,95 @@ def cpu_baseline(case, budget_s=12.0):
                       f"{reps} repetitions (fp64, single thread, same algorithmic bytes as the GPU step)"}
 
 
+# ---- rocprofv3 summaries (text files under profiles/) ------------------------------
+PROFILE_CMD_TRACE = ("rocprofv3 --kernel-trace --stats -f csv --kernel-include-regex \"nh::\" "
+                     "-d <dir> -o bench_quick -- python3 bench.py --quick --steps 20 --warmup 5 "
+                     "--no-cpu-baseline")
+PROFILE_CMD_PMC = ("rocprofv3 --pmc {counter} -f csv --kernel-include-regex \"nh::\" -d <dir> "
+                   "-o bench_quick -- python3 bench.py --quick --steps 5 --warmup 2 --no-cpu-baseline")
+BN_SOURCES = ["bn_kernels.hip", "nh_device.hpp", "nh_internal.hpp"]
+
+
+def _short_kernel(name):
+    import re
+    return re.sub(r"\(.*", "", name).replace("void ", "").strip()
+
+
+def sources_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "bwd_bn_stats_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def summarize_trace(stats_csv, out_path):
+    """Kernel-trace statistics (rocprofv3 --stats) -> short text table."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = ["# rocprofv3 kernel-trace statistics: BatchNorm2d (256,32,32,32) fp32 fwd+bwd",
+             "# (cold and warm steps of bench.py --quick plus the calibration add)",
+             f"command: {PROFILE_CMD_TRACE}",
+             "summarized by: python bench.py --summarize-trace <dir>/bench_quick_kernel_stats.csv",
+             "",
+             f"{'kernel':60s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    for r in rows:
+        lines.append(f"{_short_kernel(r['Name'])[:60]:60s} {int(r['Calls']):6d} "
+                     f"{float(r['AverageNs']) / 1e3:9.3f} {float(r['MinNs']) / 1e3:9.3f} "
+                     f"{float(r['MaxNs']) / 1e3:9.3f}")
+    open(out_path, "w").write("\n".join(lines) + "\n")
+
+
+def summarize_counters(fetch_csv, write_csv, out_dir):
+    """FETCH_SIZE / WRITE_SIZE per dispatch (first half of each kernel's
+    dispatches = the cold steps), scaled by the calibration add of known size
+    (two 32 MiB reads, one 32 MiB write).  Writes one file per BN kernel."""
+    import collections
+    import csv
+
+    def load(path):
+        d = collections.OrderedDict()
+        for r in csv.DictReader(open(path)):
+            d.setdefault(_short_kernel(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return d
+
+    f, w = load(fetch_csv), load(write_csv)
+    cold = {k: sum(v[:max(1, len(v) // 2)]) / max(1, len(v) // 2) for k, v in f.items()}
+    coldw = {k: sum(v[:max(1, len(v) // 2)]) / max(1, len(v) // 2) for k, v in w.items()}
+    calib = next(k for k in cold if "calib_add4" in k)
+    n = 256 * 32 * 32 * 32
+    fscale = (2 * n * 4) / (cold[calib] * 1024)
+    wscale = (n * 4) / (coldw[calib] * 1024)
+    digest = sources_digest(BN_SOURCES)
+    alg = {"bn_stats": n * 4, "bn_apply": 2 * n * 4, "bn_grad_sums": 2 * n * 4, "bn_dx": 3 * n * 4}
+    for k in cold:
+        tag = next((a for a in alg if f"{a}_kernel" in k), None)
+        if tag is None:
+            continue
+        fb = cold[k] * 1024 * fscale
+        wb = coldw.get(k, 0.0) * 1024 * wscale
+        text = "\n".join([
+            f"# HBM-side traffic of {k}: BatchNorm2d (256,32,32,32) fp32, cold steps",
+            f"command_fetch: {PROFILE_CMD_PMC.format(counter='FETCH_SIZE')}",
+            f"command_write: {PROFILE_CMD_PMC.format(counter='WRITE_SIZE')}",
+            "summarized by: python bench.py --summarize-counters <fetch_dir>/bench_quick_counter_collection.csv "
+            "<write_dir>/bench_quick_counter_collection.csv",
+            f"fetch_kib_per_dispatch: {cold[k]:.1f}",
+            f"write_kib_per_dispatch: {coldw.get(k, 0.0):.1f}",
+            f"calib_add fetch_kib / write_kib: {cold[calib]:.1f} / {coldw[calib]:.1f} "
+            f"(known: {2 * n * 4 // 1024} / {n * 4 // 1024})",
+            f"fetch_scale: {fscale:.5f}",
+            f"write_scale: {wscale:.5f}",
+            f"hbm_bytes_per_launch: {fb + wb:.0f}",
+            f"algorithmic_bytes_per_launch: {alg[tag]}",
+            f"traffic_over_algorithmic: {(fb + wb) / alg[tag]:.4f}",
+            f"sources: {','.join(BN_SOURCES)}",
+            f"source_sha256_16: {digest}",
+            "note: FETCH_SIZE counts L2 misses served by the data fabric, so reads that hit the "
+            "256 MB Infinity Cache are included",
+        ])
+        open(os.path.join(out_dir, f"{tag}_bn_cifar_f32_counters.txt"), "w").write(text + "\n")
+
+
 def _traffic_for(kernel_name, workload_tag):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel source (else None)."""
@@ -285,11 +374,10 @@ def _traffic_for(kernel_name, workload_tag):
         if ":" in line and not line.startswith(" "):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "bwd_bn_stats_amd", "csrc", fields.get("source", ""))
-    if not os.path.exists(src):
+    srcs = [x for x in fields.get("sources", "").split(",") if x]
+    if not srcs or not all(os.path.exists(os.path.join(ROOT, "bwd_bn_stats_amd", "csrc", x)) for x in srcs):
         return None
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if digest != fields.get("source_sha256_16"):
+    if sources_digest(srcs) != fields.get("source_sha256_16"):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -304,7 +392,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="main workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
+                    help="write profiles/ summary of a rocprofv3 --stats run and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/ traffic summaries of two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.summarize_trace or args.summarize_counters:
+        os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+        if args.summarize_trace:
+            summarize_trace(args.summarize_trace,
+                            os.path.join(ROOT, "profiles", "bn_cifar_f32_kernel_trace.txt"))
+        if args.summarize_counters:
+            summarize_counters(*args.summarize_counters, os.path.join(ROOT, "profiles"))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
