@@ -146,6 +146,7 @@ int64_t rows_blocks_max(int64_t rows, const DeviceInfo &d)
 {
     const int64_t ov = g_override_rows_blocks.load();
     int64_t g = ov > 0 ? ov : (int64_t)d.cus * kRowsMaxBlocksPerCu;
+    if (g > kRowsMaxBlocks) g = kRowsMaxBlocks;
     if (g > rows) g = rows;
     return g;
 }
@@ -176,8 +177,8 @@ RowsPlan rows_variant(int64_t cols, int vec, bool vec_ok)
 
 // Blocks: as many as fit on the device at once (occupancy of the chosen
 // variant, at most kRowsMaxBlocksPerCu per CU), at most one per row.
-// Measured on MI355X: single-team blocks filling the CU beat fewer, wider
-// blocks that synchronize more waves per row.
+// Measured on MI355X: single-team blocks beat fewer, wider blocks that
+// synchronize more waves per row.
 void rows_grid(RowsPlan &p, int64_t rows, int occ, const DeviceInfo &d)
 {
     if (occ < 1) occ = 1;
@@ -185,6 +186,7 @@ void rows_grid(RowsPlan &p, int64_t rows, int occ, const DeviceInfo &d)
     int64_t g = (int64_t)d.cus * occ;
     const int64_t ov = g_override_rows_blocks.load();
     if (ov > 0) g = ov;
+    if (g > kRowsMaxBlocks) g = kRowsMaxBlocks;
     if (g > rows) g = rows;
     if (g < 1) g = 1;
     p.blocks = (int)g;

@@ -92,7 +92,12 @@ hipError_t rows_backward_launch(const RowsCall &a, hipStream_t s);
 // (256 VGPRs): the row (two register sets when prefetching), the weights and
 // the column sums all live in registers.
 constexpr int rows_max_threads(int maxg, int vec) { return maxg * vec <= 8 ? 1024 : 512; }
-constexpr int kRowsMaxBlocksPerCu = 4;  // bound on the column-partial rows per CU
+// Row-kernel blocks per CU, at most: more blocks shorten the row kernel a
+// little but every block adds a partial row that the column finalize reads
+// back (measured on MI355X: 2 per CU is the best total for 1600..8192 wide
+// rows).
+constexpr int kRowsMaxBlocksPerCu = 2;
+constexpr int kRowsMaxBlocks = 2048;
 
 // ---- calibration --------------------------------------------------------------
 hipError_t calib_copy_launch(const void *src, void *dst, size_t bytes, int slots, hipStream_t s);

@@ -444,6 +444,11 @@ rows_generic_kernel(int kind, const TDY *__restrict__ dy, const TX *__restrict__
 }
 
 // ---- column finalize: fp64 fixed-order sum of the G partial rows -------------
+// Block = kColX columns x kColY slices; slice ty sums partial rows
+// ty, ty + kColY, ... in order (loads unrolled by 4 ahead of the adds), then
+// the slices are combined in slice order through LDS.  The partials were
+// just written and sit in L2 / the Infinity Cache: the kernel is
+// latency-bound, its cost grows with G.
 constexpr int kColX = 32;   // columns per block (one 128-byte line of a partial row)
 constexpr int kColY = 32;   // slices of the G partial rows
 template <typename TOUT>

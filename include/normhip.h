@@ -248,7 +248,8 @@ nh_status nh_rows_plan(int64_t rows, int64_t cols, int *blocks);
 /*
  * Plan overrides for tests and tuning sweeps: key "bn_grid_y" forces the
  * BatchNorm blocks per channel, key "rows_blocks" forces the row-kernel
- * block count (both also size the workspace queried afterwards), key
+ * block count (at most 2048 and at most one per row; both keys also size
+ * the workspace queried afterwards), key
  * "bn_finalize_kernels" = 1 runs the BatchNorm finalize steps as separate
  * kernels instead of inside the elementwise kernels (same results).  value 0
  * restores the automatic plan.  Process-wide; not for concurrent use with
