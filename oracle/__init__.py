@@ -42,11 +42,14 @@ def _load():
         lib.oracle_bn_forward_train.argtypes = [i64, i64, i64, p, p, p, dbl, dbl, p, p, p, p]
         lib.oracle_bn_backward.argtypes = [i64, i64, i64, p, p, p, dbl, p, p]
         lib.oracle_layernorm_stats.argtypes = [i64, i64, p, dbl, p, p]
+        lib.oracle_layernorm_forward.argtypes = [i64, i64, p, p, p, dbl, p, p, p]
+        lib.oracle_rmsnorm_forward.argtypes = [i64, i64, p, p, dbl, p, p]
         lib.oracle_layernorm_backward.argtypes = [i64, i64, p, p, p, p, p, p, p, p]
         lib.oracle_rmsnorm_rms.argtypes = [i64, i64, p, dbl, p]
         lib.oracle_rmsnorm_backward.argtypes = [i64, i64, p, p, p, p, dbl, p, p]
         for f in ("oracle_bn_forward_train", "oracle_bn_backward", "oracle_layernorm_stats",
-                  "oracle_layernorm_backward", "oracle_rmsnorm_rms", "oracle_rmsnorm_backward"):
+                  "oracle_layernorm_forward", "oracle_layernorm_backward", "oracle_rmsnorm_rms",
+                  "oracle_rmsnorm_forward", "oracle_rmsnorm_backward"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -110,6 +113,20 @@ def layernorm_stats(x, *, eps=1e-5):
     return mean, rstd
 
 
+def layernorm_forward(x, w=None, b=None, *, eps=1e-5):
+    """Returns (y, mean[rows], rstd[rows])."""
+    x = _d(x)
+    rows, cols = x.shape
+    w = None if w is None else _d(w)
+    b = None if b is None else _d(b)
+    y = np.empty_like(x)
+    mean = np.empty(rows, np.float64)
+    rstd = np.empty(rows, np.float64)
+    _check(_load().oracle_layernorm_forward(rows, cols, _ptr(x), _ptr(w), _ptr(b), eps, _ptr(y),
+                                            _ptr(mean), _ptr(rstd)), "oracle_layernorm_forward")
+    return y, mean, rstd
+
+
 def layernorm_backward(x, dy, mean, rstd, w=None):
     """Returns (dx, dweight, dbias)."""
     x, dy, mean, rstd = _d(x), _d(dy), _d(mean), _d(rstd)
@@ -130,6 +147,18 @@ def rmsnorm_rms(x, *, eps=1e-5):
     rms = np.empty(rows, np.float64)
     _check(_load().oracle_rmsnorm_rms(rows, cols, _ptr(x), eps, _ptr(rms)), "oracle_rmsnorm_rms")
     return rms
+
+
+def rmsnorm_forward(x, w=None, *, eps=1e-5):
+    """Returns (y, rms[rows])."""
+    x = _d(x)
+    rows, cols = x.shape
+    w = None if w is None else _d(w)
+    y = np.empty_like(x)
+    rms = np.empty(rows, np.float64)
+    _check(_load().oracle_rmsnorm_forward(rows, cols, _ptr(x), _ptr(w), eps, _ptr(y), _ptr(rms)),
+           "oracle_rmsnorm_forward")
+    return y, rms
 
 
 def rmsnorm_backward(x, dy, w, rms=None, *, eps=1e-5):

@@ -231,6 +231,31 @@ int oracle_layernorm_stats(int64_t rows, int64_t cols, const double *x, double e
 }
 
 /*
+ * LayerNorm training forward over the last dimension (the forward whose saved
+ * statistics [LN]'s backward consumes as its mean and rstd inputs):
+ *   mean_r = sum_j x / H,  var_r = sum_j (x - mean)^2 / H  (two passes),
+ *   rstd_r = 1/sqrt(var_r + eps),  y = (x - mean)*rstd*w + b.
+ * w may be NULL (1), b may be NULL (0); mean/rstd may be NULL (not returned).
+ */
+int oracle_layernorm_forward(int64_t rows, int64_t cols, const double *x,
+                             const double *w, const double *b, double eps,
+                             double *y, double *mean, double *rstd)
+{
+    if (rows < 0 || cols <= 0) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *xr = x + (size_t)r * (size_t)cols;
+        double *yr = y + (size_t)r * (size_t)cols;
+        double mu, rs;
+        oracle_layernorm_stats(1, cols, xr, eps, &mu, &rs);
+        for (int64_t j = 0; j < cols; ++j)
+            yr[j] = (xr[j] - mu) * rs * (w ? w[j] : 1.0) + (b ? b[j] : 0.0);
+        if (mean) mean[r] = mu;
+        if (rstd) rstd[r] = rs;
+    }
+    return 0;
+}
+
+/*
  * LayerNorm backward over the last dimension with saved per-row mean and rstd,
  * as [LN]'s layer_norm backward definition computes it (tensor names of that
  * definition in brackets):
@@ -305,6 +330,25 @@ int oracle_rmsnorm_rms(int64_t rows, int64_t cols, const double *x, double eps,
         ks_init(&s);
         for (int64_t j = 0; j < cols; ++j) ks_add(&s, xr[j] * xr[j]);
         rms[r] = sqrt(ks_value(&s) / (double)cols + eps);
+    }
+    return 0;
+}
+
+/*
+ * RMSNorm forward, [RM] rmsnorm_prims:  y = w * (x / rms),
+ * rms = sqrt(sum_j x^2 / H + eps).  w may be NULL (1); rms may be NULL.
+ */
+int oracle_rmsnorm_forward(int64_t rows, int64_t cols, const double *x, const double *w,
+                           double eps, double *y, double *rms_out)
+{
+    if (rows < 0 || cols <= 0) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *xr = x + (size_t)r * (size_t)cols;
+        double *yr = y + (size_t)r * (size_t)cols;
+        double rms;
+        oracle_rmsnorm_rms(1, cols, xr, eps, &rms);
+        for (int64_t j = 0; j < cols; ++j) yr[j] = (w ? w[j] : 1.0) * (xr[j] / rms);
+        if (rms_out) rms_out[r] = rms;
     }
     return 0;
 }

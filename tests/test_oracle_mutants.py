@@ -41,6 +41,9 @@ MUTANTS = [
     ("rms_no_eps", "rms[r] = sqrt(ks_value(&s) / (double)cols + eps);", "rms[r] = sqrt(ks_value(&s) / (double)cols);"),
     ("rms_dx_factor", "dxr[j] = g * rinv + 2.0 * t * xr[j];", "dxr[j] = g * rinv + t * xr[j];"),
     ("rms_dweight_no_rinv", "ks_add(&sw[j], dyr[j] * xr[j] * rinv);", "ks_add(&sw[j], dyr[j] * xr[j]);"),
+    ("ln_fwd_drops_bias", "yr[j] = (xr[j] - mu) * rs * (w ? w[j] : 1.0) + (b ? b[j] : 0.0);",
+     "yr[j] = (xr[j] - mu) * rs * (w ? w[j] : 1.0);"),
+    ("rms_fwd_inverted", "yr[j] = (w ? w[j] : 1.0) * (xr[j] / rms);", "yr[j] = (w ? w[j] : 1.0) * (xr[j] * rms);"),
 ]
 
 PINS = [
@@ -59,6 +62,9 @@ PINS = [
     ("rms_fd", pr.test_rms_finite_differences),
     ("rms_invariants", pr.test_rms_invariant_and_special_cases),
     ("rms_exact", pr.test_rms_exact_rational),
+    ("ln_fwd_torch", lambda m: pr.test_ln_forward_matches_torch(m, 3, 7, 1)),
+    ("rms_fwd_torch", lambda m: pr.test_rms_forward_matches_torch(m, 3, 7, 1)),
+    ("fwd_exact", pr.test_forwards_exact_rational),
 ]
 
 

@@ -246,3 +246,61 @@ def test_rms_exact_rational(oracle_mod):
         for j in range(H):
             want_w[j] += D[j] * X[j] / rms
     assert max(abs(float(a) - b) for a, b in zip(want_w, dw)) < 1e-14
+
+
+# ---------------------------------------------------------- forwards (next)
+
+@pytest.mark.parametrize("rows,cols,seed", [(3, 7, 1), (16, 1600, 1003), (5, 1, 2)])
+def test_ln_forward_matches_torch(oracle_mod, rows, cols, seed):
+    c = wl.rows_case(rows, cols, x_t=wl.F32, dy_t=wl.BF16, w_t=wl.BF16, seed=seed, with_bias=True)
+    x, w, b = c.x.value, c.w.value, c.b.value
+    y, mean, rstd = oracle_mod.layernorm_forward(x, w, b, eps=c.eps)
+    ty = F.layer_norm(torch.tensor(x), (cols,), torch.tensor(w), torch.tensor(b), eps=c.eps).numpy()
+    assert _rel(y, ty, 1.0) < 1e-13
+    m2, r2 = oracle_mod.layernorm_stats(x, eps=c.eps)
+    assert np.array_equal(mean, m2) and np.array_equal(rstd, r2)
+    # no affine parameters: every row of y has mean 0 and variance var/(var+eps)
+    y0, _, _ = oracle_mod.layernorm_forward(x, None, None, eps=c.eps)
+    if cols > 1:
+        assert np.all(np.abs(y0.mean(axis=1)) < 1e-14 * np.abs(y0).max())
+        var = 1.0 / rstd ** 2 - c.eps
+        assert _rel(y0.var(axis=1), var / (var + c.eps)) < 1e-12
+
+
+@pytest.mark.parametrize("rows,cols,seed", [(3, 7, 1), (8, 8192, 1004), (6, 1, 5)])
+def test_rms_forward_matches_torch(oracle_mod, rows, cols, seed):
+    c = wl.rows_case(rows, cols, x_t=wl.BF16, dy_t=wl.BF16, w_t=wl.BF16, seed=seed)
+    x, w = c.x.value, c.w.value
+    y, rms = oracle_mod.rmsnorm_forward(x, w, eps=c.eps)
+    ty = F.rms_norm(torch.tensor(x), (cols,), torch.tensor(w), eps=c.eps).numpy()
+    assert _rel(y, ty) < 1e-13
+    assert np.array_equal(rms, oracle_mod.rmsnorm_rms(x, eps=c.eps))
+    # rmsnorm_prims of the RMSNorm issue
+    xt = torch.tensor(x)
+    prims = (torch.tensor(w) * (xt / torch.sqrt((xt ** 2).mean(1, keepdim=True) + 1e-5))).numpy()
+    assert _rel(y, prims) < 1e-13
+    # w = 1: mean(y^2) = ms / (ms + eps)
+    y1, _ = oracle_mod.rmsnorm_forward(x, None, eps=c.eps)
+    ms = (x * x).mean(axis=1)
+    assert _rel((y1 * y1).mean(axis=1), ms / (ms + c.eps)) < 1e-13
+
+
+def test_forwards_exact_rational(oracle_mod):
+    rng = np.random.default_rng(77)
+    x = np.round(rng.normal(size=(2, 5)), 3)
+    w = np.round(rng.uniform(0.5, 1.5, 5), 3)
+    b = np.round(rng.normal(size=5), 3)
+    eps = 1e-5
+    y, mean, rstd = oracle_mod.layernorm_forward(x, w, b, eps=eps)
+    yr, rms = oracle_mod.rmsnorm_forward(x, w, eps=eps)
+    for r in range(2):
+        X = [Fraction(float(v)) for v in x[r]]
+        mu = sum(X) / 5
+        var = sum((v - mu) ** 2 for v in X) / 5
+        rs = 1 / _dsqrt(var + Fraction(eps))
+        want = [(v - mu) * rs * Fraction(float(ww)) + Fraction(float(bb)) for v, ww, bb in zip(X, w, b)]
+        assert max(abs(float(a) - c) for a, c in zip(want, y[r])) < 1e-14
+        ms = _dsqrt(sum(v * v for v in X) / 5 + Fraction(eps))
+        want_r = [Fraction(float(ww)) * (v / ms) for v, ww in zip(X, w)]
+        assert max(abs(float(a) - c) for a, c in zip(want_r, yr[r])) < 1e-14
+        assert abs(float(ms) - rms[r]) < 1e-15 * float(ms)
