@@ -231,6 +231,55 @@ def bench_rows(nh, torch, case, kind, K, W, cold=True, saved=True):
             "partials_bytes_written": G * H * 4 * (2 if kind == "ln" else 1)}
 
 
+def bench_rows_fwd(nh, torch, case, kind, K, W, cold=True):
+    """LayerNorm / RMSNorm training forward: read x (+ weight, bias once),
+    write y and the per-row statistics."""
+    import ctypes
+    device = torch.device("cuda:0")
+    x0, w = _dev(case.x, device), _dev(case.w, device)
+    b = _dev(case.b, device) if (kind == "ln" and case.b is not None) else None
+    R_, H = case.rows, case.cols
+    set_bytes = 2 * x0.numel() * x0.element_size()
+    R = _nsets(set_bytes, cold)
+    sets = [dict(x=x0.clone(), y=torch.empty_like(x0), s0=torch.empty(R_, device=device),
+                 s1=torch.empty(R_, device=device)) for _ in range(R)]
+    torch.cuda.synchronize()
+    P = ctypes.c_void_p
+    stream = P(torch.cuda.current_stream(device).cuda_stream)
+    dt = {torch.float32: 0, torch.bfloat16: 1}
+    calls = [{k: P(v.data_ptr()) for k, v in s.items()} for s in sets]
+    lib = nh.lib
+    pw, pb = P(w.data_ptr()), (P(b.data_ptr()) if b is not None else None)
+    xt = dt[x0.dtype]
+    if kind == "ln":
+        def step(i):
+            p = calls[i % R]
+            st = lib.layernorm_forward(p["x"], xt, pw, pb, dt[w.dtype], R_, H, case.eps, p["y"], xt,
+                                       p["s0"], p["s1"], stream)
+            if st:
+                raise RuntimeError(nh.last_error())
+        kernels = ["ln_fwd"]
+    else:
+        def step(i):
+            p = calls[i % R]
+            st = lib.rmsnorm_forward(p["x"], xt, pw, R_, H, case.eps, p["y"], p["s0"], stream)
+            if st:
+                raise RuntimeError(nh.last_error())
+        kernels = ["rms_fwd"]
+    ms, per = Timed(nh, torch).run(step, K, W, kernels)
+    E = R_ * H
+    byt = 2 * E * x0.element_size() + R_ * 4 * (2 if kind == "ln" else 1)
+    k = kernels[0]
+    if k in per:
+        per[k]["bytes"] = byt
+        per[k]["gbs"] = byt / (per[k]["avg_us"] * 1e3)
+        per[k]["frac_of_peak"] = per[k]["gbs"] / HBM_PEAK_GBS
+    del sets, calls
+    torch.cuda.empty_cache()
+    return {"us_per_call": 1000.0 * ms, "bytes": byt, "gbs": byt / (ms * 1e6), "buffer_sets": R,
+            "kernels": per}
+
+
 # ---- calibration floor ---------------------------------------------------------------
 def bench_calib(nh, torch, n_floats, K, W):
     device = torch.device("cuda:0")
@@ -443,6 +492,11 @@ def main():
                 name = f"rms_bwd_2048x8192_{dt}_{'saved' if saved else 'recompute'}_rms"
                 log(f"[bench] {name}")
                 others[name] = bench_rows(nh, torch, wl.rms_bwd(dt), "rms", kk, W, saved=saved)
+        log("[bench] ln_fwd_16x512x1600 (x f32, w/b bf16, y f32)")
+        others["ln_fwd_16x512x1600"] = bench_rows_fwd(nh, torch, wl.ln_bwd(), "ln", kk, W)
+        for dt in (wl.BF16, wl.F32):
+            log(f"[bench] rms_fwd_2048x8192_{dt}")
+            others[f"rms_fwd_2048x8192_{dt}"] = bench_rows_fwd(nh, torch, wl.rms_bwd(dt), "rms", kk, W)
 
     # dominant kernel of the step: the largest share of the step's kernel time
     per = cold["kernels"]

@@ -250,7 +250,7 @@ const char *nh_kernel_name(int k)
 {
     static const char *names[NH_K_COUNT] = {
         "bn_stats", "bn_fwd_finalize", "bn_apply", "bn_grad_sums", "bn_bwd_finalize", "bn_dx",
-        "ln_rows", "ln_colsum", "rms_rows", "rms_colsum", "calib"};
+        "ln_rows", "ln_colsum", "rms_rows", "rms_colsum", "calib", "ln_fwd", "rms_fwd"};
     return (k >= 0 && k < NH_K_COUNT) ? names[k] : "";
 }
 
@@ -505,6 +505,105 @@ nh_status rmsnorm_backward(const void *dy, const void *x, nh_dtype t, const floa
     a.dx = dx;
     a.dweight = dweight;
     return rows_run(a, 1, ws, ws_bytes, stream);
+}
+
+// ---- LayerNorm / RMSNorm forward ----------------------------------------------------------
+static nh_status rows_forward_run(FwdCall &a, void *stream)
+{
+    DeviceInfo d;
+    nh_status st = device_info(&d);
+    if (st != NH_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    bool vec_ok = true;
+    auto need_align = [&](const void *p, int t) {
+        if (!p) return;
+        const size_t al = (size_t)a.vec * dtype_bytes(t);
+        if (!aligned(p, al < 16 ? al : 16)) vec_ok = false;
+    };
+    need_align(a.x, a.x_t);
+    need_align(a.y, a.y_t);
+    need_align(a.w, a.w_t);
+    need_align(a.b, a.w_t);
+    RowsPlan p = rows_variant(a.cols, a.vec, vec_ok);
+    a.maxg = p.maxg;
+    a.vec = p.vec;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const int64_t key = -1 - (((((((int64_t)dev * 2 + a.kind) * 2 + a.x_t) * 2 + a.y_t) * 16 + a.maxg) * 16) + a.vec);
+    int occ = 0;
+    {
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        auto it = g_rows_occupancy.find(key);
+        if (it != g_rows_occupancy.end()) occ = it->second;
+    }
+    hipError_t e = hipSuccess;
+    if (occ == 0) {
+        a.occupancy_out = &occ;
+        e = rows_forward_launch(a, s);
+        a.occupancy_out = nullptr;
+        if (e != hipSuccess) return hip_fail(e, "forward row kernel occupancy query");
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        g_rows_occupancy[key] = occ;
+    }
+    // No column partials in the forward: fill the device (at most 8 blocks per CU).
+    int64_t g = (int64_t)d.cus * (occ < 1 ? 1 : (occ > 8 ? 8 : occ));
+    if (g > a.rows) g = a.rows;
+    a.blocks = (int)g;
+    e = rows_forward_launch(a, s);
+    if (e != hipSuccess) return hip_fail(e, "forward row kernel launch");
+    return ok();
+}
+
+nh_status layernorm_forward(const void *x, nh_dtype x_t, const void *weight, const void *bias,
+                            nh_dtype w_t, int64_t rows, int64_t cols, float eps, void *y,
+                            nh_dtype y_t, float *mean, float *rstd, void *stream)
+{
+    if (!valid_dtype(x_t) || !valid_dtype(w_t) || !valid_dtype(y_t))
+        return fail(NH_ERR_DTYPE, "dtypes must be NH_F32 or NH_BF16");
+    nh_status st = rows_check_shape(rows, cols);
+    if (st != NH_OK) return st;
+    if (rows * cols == 0) return ok();
+    if (!x || !y || !mean) return fail(NH_ERR_NULL, "x, y and mean are required");
+    if (!(eps >= 0.f) || !isfinite(eps)) return fail(NH_ERR_ARG, "eps must be finite and >= 0");
+    FwdCall a{};
+    a.kind = 0;
+    a.x_t = x_t;
+    a.y_t = y_t;
+    a.w_t = w_t;
+    a.rows = (int)rows;
+    a.cols = (int)cols;
+    a.vec = (x_t == NH_F32 || y_t == NH_F32) ? 4 : 8;
+    a.x = x;
+    a.w = weight;
+    a.b = bias;
+    a.eps = eps;
+    a.y = y;
+    a.stat0 = mean;
+    a.stat1 = rstd;
+    return rows_forward_run(a, stream);
+}
+
+nh_status rmsnorm_forward(const void *x, nh_dtype t, const void *weight, int64_t rows, int64_t cols,
+                          float eps, void *y, float *rms, void *stream)
+{
+    if (!valid_dtype(t)) return fail(NH_ERR_DTYPE, "dtype must be NH_F32 or NH_BF16");
+    nh_status st = rows_check_shape(rows, cols);
+    if (st != NH_OK) return st;
+    if (rows * cols == 0) return ok();
+    if (!x || !y) return fail(NH_ERR_NULL, "x and y are required");
+    if (!(eps >= 0.f) || !isfinite(eps)) return fail(NH_ERR_ARG, "eps must be finite and >= 0");
+    FwdCall a{};
+    a.kind = 1;
+    a.x_t = a.y_t = a.w_t = t;
+    a.rows = (int)rows;
+    a.cols = (int)cols;
+    a.vec = t == NH_F32 ? 4 : 8;
+    a.x = x;
+    a.w = weight;
+    a.y = y;
+    a.eps = eps;
+    a.stat0 = rms;
+    return rows_forward_run(a, stream);
 }
 
 // ---- measurement -------------------------------------------------------------------------

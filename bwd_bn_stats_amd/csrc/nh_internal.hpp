@@ -99,6 +99,23 @@ constexpr int rows_max_threads(int maxg, int vec) { return maxg * vec <= 8 ? 102
 constexpr int kRowsMaxBlocksPerCu = 2;
 constexpr int kRowsMaxBlocks = 2048;
 
+// ---- LayerNorm / RMSNorm forward ---------------------------------------------------
+struct FwdCall {
+    int kind;            // 0 LayerNorm, 1 RMSNorm
+    int x_t, y_t, w_t;
+    int rows, cols;
+    int blocks;
+    int maxg;            // 16-byte groups per thread per row (vector path); 0 = generic path
+    int vec;
+    const void *x, *w, *b;
+    float eps;
+    void *y;
+    float *stat0, *stat1;  // LayerNorm: mean, rstd; RMSNorm: rms
+    int *occupancy_out;    // non-NULL: report blocks per CU instead of launching
+};
+
+hipError_t rows_forward_launch(const FwdCall &a, hipStream_t s);
+
 // ---- calibration --------------------------------------------------------------
 hipError_t calib_copy_launch(const void *src, void *dst, size_t bytes, int slots, hipStream_t s);
 hipError_t calib_add_launch(const float *a, const float *b, float *o, int64_t n, int slots, hipStream_t s);

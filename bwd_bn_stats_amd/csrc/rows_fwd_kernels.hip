@@ -1,0 +1,271 @@
+// LayerNorm and RMSNorm training forward over the last dimension of [rows, H],
+// writing the statistics their backward passes consume.
+//
+//   LayerNorm: the statistics NVIDIA/Fuser issue #1473's layer_norm backward
+//     takes as inputs (mean and rstd per row), computed with the one-pass
+//     shifted sums of Aether-ML PR #18 ("One-pass statistics") applied per
+//     row: with K = the row's first element and d = x - K,
+//       mean = K + sum d / H,  var = sum d^2 / H - (sum d / H)^2 (clamped at 0),
+//       rstd = 1/sqrt(var + eps),  y = (x - mean)*rstd*w + b.
+//   RMSNorm: NVIDIA/Fuser issue #3629's rmsnorm_prims,
+//       rms = sqrt(sum x^2 / H + eps),  y = w*(x/rms)
+//     (rms is what that issue's rmsnorm_bwd_fusion takes as its saved input).
+//
+// Same structure as the backward row kernels: a 256-thread team per row, the
+// row in registers (read once, one row ahead, through range-checked buffer
+// loads), one fixed-order team sum per row, nontemporal y stores.
+#include "rows_common.hpp"
+
+namespace nh {
+
+// A parameter group widened to fp32 once; NULL reads as `dflt`.
+template <int VEC>
+struct ParamGroup {
+    float v[VEC];
+    __device__ __forceinline__ void load(const void *p, int bf16, int col, float dflt)
+    {
+        if (p == nullptr) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) v[e] = dflt;
+        } else if (bf16) {
+            load_vec<uint16_t, VEC>(static_cast<const uint16_t *>(p) + col, v);
+        } else {
+            load_vec<float, VEC>(static_cast<const float *>(p) + col, v);
+        }
+    }
+};
+
+// KIND 0: LayerNorm (stat0 = mean, stat1 = rstd); KIND 1: RMSNorm (stat0 = rms).
+template <int KIND, typename TX, typename TY, int VEC, int MAXG, int MT, bool PF>
+__global__ void __launch_bounds__(MT)
+norm_fwd_rows_kernel(const TX *__restrict__ x, const void *__restrict__ w,
+                     const void *__restrict__ b, int w_bf16, int rows, int H, float eps,
+                     TY *__restrict__ y, float *__restrict__ stat0, float *__restrict__ stat1)
+{
+    __shared__ float red[kRedFloats];
+    const int tt = threadIdx.x;
+    const int wave = tt / kWave;
+    const int lane = tt & (kWave - 1);
+    const int G = gridDim.x;
+    const int Gr = H / VEC;
+    const float invH = 1.0f / (float)H;
+
+    ParamGroup<VEC> wv[MAXG];
+    ParamGroup<VEC> bv[KIND == 0 ? MAXG : 1];
+#pragma unroll
+    for (int k = 0; k < MAXG; ++k) {
+        const int grp = tt + k * kTeam;
+        if (grp < Gr) {
+            wv[k].load(w, w_bf16, grp * VEC, 1.f);
+            if constexpr (KIND == 0) bv[k].load(b, w_bf16, grp * VEC, 0.f);
+        }
+    }
+
+    const int iters = (int)ceil_div(rows, (int64_t)G);
+    struct RowBuf {
+        Raw<TX, VEC> x[MAXG];
+        float K;
+    };
+    auto load_row = [&](RowBuf &rb, int it) {
+        const int r = __builtin_amdgcn_readfirstlane(it * G + (int)blockIdx.x);
+        const bool live = r < rows;
+        const int rc = live ? r : rows - 1;
+        const size_t rowoff = (size_t)rc * H;
+        const auto rx = make_rsrc(x + rowoff, live ? (uint32_t)(H * sizeof(TX)) : 0u);
+#pragma unroll
+        for (int k = 0; k < MAXG; ++k) rb.x[k].load_buf(rx, (tt + k * kTeam) * VEC * (int)sizeof(TX));
+        rb.K = KIND == 0 ? to_f32(x[rowoff]) : 0.f;
+    };
+    auto do_row = [&](const RowBuf &rb, int it) {
+        const int r = it * G + (int)blockIdx.x;
+        const bool active = r < rows;
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < MAXG; ++k) {
+            const int grp = tt + k * kTeam;
+            if (active && grp < Gr) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const float v = rb.x[k].get(e);
+                    if constexpr (KIND == 0) {
+                        const float d = v - rb.K;
+                        s1 += d;
+                        s2 = fmaf(d, d, s2);
+                    } else {
+                        s2 = fmaf(v, v, s2);
+                    }
+                }
+            }
+        }
+        team_sum2(red + (it & 1) * (kRedFloats / 2), 0, wave, lane, s1, s2);
+        if (!active) return;
+        float a, c;  // y = fmaf(x - c, a*w, b) (LN) or y = (x*a)*w (RMS)
+        if constexpr (KIND == 0) {
+            const float md = s1 * invH;
+            const float var = fmaxf(s2 * invH - md * md, 0.f);
+            c = rb.K + md;
+            a = 1.0f / sqrtf(var + eps);
+            if (tt == 0) {
+                stat0[r] = c;
+                if (stat1 != nullptr) stat1[r] = a;
+            }
+        } else {
+            const float rms = sqrtf(fmaf(s2, invH, eps));
+            a = 1.0f / rms;
+            c = 0.f;
+            if (tt == 0 && stat0 != nullptr) stat0[r] = rms;
+        }
+        const size_t rowoff = (size_t)r * H;
+#pragma unroll
+        for (int k = 0; k < MAXG; ++k) {
+            const int grp = tt + k * kTeam;
+            if (grp < Gr) {
+                float o[VEC];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    if constexpr (KIND == 0)
+                        o[e] = fmaf((rb.x[k].get(e) - c) * a, wv[k].v[e], bv[k].v[e]);
+                    else
+                        o[e] = wv[k].v[e] * (rb.x[k].get(e) * a);
+                }
+                st<true, TY, VEC>(y + rowoff + grp * VEC, o);
+            }
+        }
+    };
+
+    RowBuf ra;
+    if constexpr (PF) {
+        RowBuf rb;
+        load_row(ra, 0);
+        for (int it = 0; it < iters; it += 2) {
+            load_row(rb, it + 1);
+            do_row(ra, it);
+            if (it + 1 >= iters) break;
+            load_row(ra, it + 2);
+            do_row(rb, it + 1);
+        }
+    } else {
+        for (int it = 0; it < iters; ++it) {
+            load_row(ra, it);
+            do_row(ra, it);
+        }
+    }
+}
+
+// Any width, any alignment: scalar accesses, two reads of the row (the second
+// from cache).
+template <int KIND, typename TX, typename TY>
+__global__ void __launch_bounds__(kTeam)
+norm_fwd_generic_kernel(const TX *__restrict__ x, const void *__restrict__ w,
+                        const void *__restrict__ b, int w_bf16, int rows, int H, float eps,
+                        TY *__restrict__ y, float *__restrict__ stat0, float *__restrict__ stat1)
+{
+    __shared__ float red[kRedFloats];
+    const int tt = threadIdx.x;
+    const int wave = tt / kWave;
+    const int lane = tt & (kWave - 1);
+    const float invH = 1.0f / (float)H;
+    int it = 0;
+    for (int r = blockIdx.x; r < rows; r += gridDim.x, ++it) {
+        const size_t rowoff = (size_t)r * H;
+        const float K = KIND == 0 ? to_f32(x[rowoff]) : 0.f;
+        float s1 = 0.f, s2 = 0.f;
+        for (int j = tt; j < H; j += kTeam) {
+            const float v = to_f32(x[rowoff + j]);
+            if (KIND == 0) {
+                const float d = v - K;
+                s1 += d;
+                s2 = fmaf(d, d, s2);
+            } else {
+                s2 = fmaf(v, v, s2);
+            }
+        }
+        team_sum2(red + (it & 1) * (kRedFloats / 2), 0, wave, lane, s1, s2);
+        float a, c;
+        if (KIND == 0) {
+            const float md = s1 * invH;
+            const float var = fmaxf(s2 * invH - md * md, 0.f);
+            c = K + md;
+            a = 1.0f / sqrtf(var + eps);
+            if (tt == 0) {
+                stat0[r] = c;
+                if (stat1 != nullptr) stat1[r] = a;
+            }
+        } else {
+            const float rms = sqrtf(fmaf(s2, invH, eps));
+            a = 1.0f / rms;
+            c = 0.f;
+            if (tt == 0 && stat0 != nullptr) stat0[r] = rms;
+        }
+        for (int j = tt; j < H; j += kTeam) {
+            const float v = to_f32(x[rowoff + j]);
+            const float wj = w ? load_param(w, w_bf16, j) : 1.f;
+            float o;
+            if (KIND == 0) {
+                const float bj = b ? load_param(b, w_bf16, j) : 0.f;
+                o = fmaf((v - c) * a, wj, bj);
+            } else {
+                o = wj * (v * a);
+            }
+            y[rowoff + j] = from_f32<TY>(o);
+        }
+    }
+}
+
+// ---- host dispatch ------------------------------------------------------------------
+template <int KIND, typename TX, typename TY, int VEC, int MAXG>
+static hipError_t fwd_vec(const FwdCall &a, hipStream_t s)
+{
+    constexpr int MT = rows_max_threads(MAXG, VEC);
+    constexpr bool PF = MAXG * VEC * (int)sizeof(TX) <= 64;
+    auto kern = norm_fwd_rows_kernel<KIND, TX, TY, VEC, MAXG, MT, PF>;
+    if (a.occupancy_out)
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kern, kTeam, 0);
+    return launch(KIND == 0 ? NH_K_LN_FWD : NH_K_RMS_FWD, kern, dim3(a.blocks), dim3(kTeam), 0u, s,
+                  static_cast<const TX *>(a.x), a.w, a.b, a.w_t, a.rows, a.cols, a.eps,
+                  static_cast<TY *>(a.y), a.stat0, a.stat1);
+}
+
+template <int KIND, typename TX, typename TY>
+static hipError_t fwd_generic(const FwdCall &a, hipStream_t s)
+{
+    auto kern = norm_fwd_generic_kernel<KIND, TX, TY>;
+    if (a.occupancy_out)
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kern, kTeam, 0);
+    return launch(KIND == 0 ? NH_K_LN_FWD : NH_K_RMS_FWD, kern, dim3(a.blocks), dim3(kTeam), 0u, s,
+                  static_cast<const TX *>(a.x), a.w, a.b, a.w_t, a.rows, a.cols, a.eps,
+                  static_cast<TY *>(a.y), a.stat0, a.stat1);
+}
+
+template <int KIND, typename TX, typename TY, int VEC>
+static hipError_t fwd_maxg(const FwdCall &a, hipStream_t s)
+{
+    switch (a.maxg) {
+    case 1: return fwd_vec<KIND, TX, TY, VEC, 1>(a, s);
+    case 2: return fwd_vec<KIND, TX, TY, VEC, 2>(a, s);
+    case 4: return fwd_vec<KIND, TX, TY, VEC, 4>(a, s);
+    default:
+        if constexpr (VEC == 4) return fwd_vec<KIND, TX, TY, VEC, 8>(a, s);
+        return hipErrorInvalidValue;
+    }
+}
+
+template <int KIND, typename TX, typename TY>
+static hipError_t fwd_types(const FwdCall &a, hipStream_t s)
+{
+    if (a.maxg == 0) return fwd_generic<KIND, TX, TY>(a, s);
+    return a.vec == 4 ? fwd_maxg<KIND, TX, TY, 4>(a, s) : fwd_maxg<KIND, TX, TY, 8>(a, s);
+}
+
+hipError_t rows_forward_launch(const FwdCall &a, hipStream_t s)
+{
+    if (a.kind == 1) return a.x_t == 0 ? fwd_types<1, float, float>(a, s) : fwd_types<1, uint16_t, uint16_t>(a, s);
+    switch (a.x_t * 2 + a.y_t) {
+    case 0: return fwd_types<0, float, float>(a, s);
+    case 1: return fwd_types<0, float, uint16_t>(a, s);
+    case 2: return fwd_types<0, uint16_t, float>(a, s);
+    default: return fwd_types<0, uint16_t, uint16_t>(a, s);
+    }
+}
+
+} // namespace nh

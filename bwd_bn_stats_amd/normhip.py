@@ -22,13 +22,13 @@ F32, BF16 = 0, 1
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 
 KERNELS = ["bn_stats", "bn_fwd_finalize", "bn_apply", "bn_grad_sums", "bn_bwd_finalize", "bn_dx",
-           "ln_rows", "ln_colsum", "rms_rows", "rms_colsum", "calib"]
+           "ln_rows", "ln_colsum", "rms_rows", "rms_colsum", "calib", "ln_fwd", "rms_fwd"]
 
 EXPORTS = [
     "nh_status_string", "nh_last_error", "nh_kernel_name",
     "bn_forward_train_workspace", "bn_backward_workspace", "bn_forward_train", "bn_backward",
     "layernorm_backward_workspace", "layernorm_backward",
-    "rmsnorm_backward_workspace", "rmsnorm_backward",
+    "rmsnorm_backward_workspace", "rmsnorm_backward", "layernorm_forward", "rmsnorm_forward",
     "nh_timing_enable", "nh_timing_reserve", "nh_timing_read", "nh_calib_copy", "nh_calib_add",
     "nh_bn_plan", "nh_rows_plan", "nh_plan_override", "nh_selftest_host",
 ]
@@ -60,6 +60,8 @@ def _load():
         "layernorm_backward": (i32, [p, i32, p, i32, p, p, p, i32, i64, i64, p, i32, p, p, p, sz, p]),
         "rmsnorm_backward_workspace": (i32, [i64, i64, psz]),
         "rmsnorm_backward": (i32, [p, p, i32, p, f32, p, i64, i64, p, p, p, sz, p]),
+        "layernorm_forward": (i32, [p, i32, p, p, i32, i64, i64, f32, p, i32, p, p, p]),
+        "rmsnorm_forward": (i32, [p, i32, p, i64, i64, f32, p, p, p]),
         "nh_timing_enable": (i32, [i32]),
         "nh_timing_reserve": (i32, [i64]),
         "nh_timing_read": (i32, [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
@@ -267,6 +269,45 @@ def rmsnorm_backward(dy, x, rms=None, weight=None, eps: float = 1e-5, *, need_dx
                                 _ptr(dx), _ptr(dweight), _ptr(ws), nb, _stream(x.device)),
            "rmsnorm_backward")
     return dx, dweight
+
+
+def layernorm_forward(x, weight=None, bias=None, eps: float = 1e-5, *, y_dtype=None, w_dtype=None,
+                      y=None, mean=None, rstd=None, need_rstd=True):
+    """LayerNorm training forward over the last dim.  Returns (y, mean, rstd)
+    (rstd None when not requested)."""
+    _dev_tensor(x, "x")
+    rows, cols = _rows(x)
+    f32 = torch.float32
+    wdt = weight.dtype if weight is not None else (bias.dtype if bias is not None else (w_dtype or f32))
+    _dev_tensor(weight, "weight", wdt, cols)
+    _dev_tensor(bias, "bias", wdt, cols)
+    ydt = y_dtype or x.dtype
+    y = torch.empty(x.shape, dtype=ydt, device=x.device) if y is None else _dev_tensor(y, "y", ydt, x.numel())
+    mean = torch.empty(rows, dtype=f32, device=x.device) if mean is None else _dev_tensor(mean, "mean", f32, rows)
+    if need_rstd:
+        rstd = torch.empty(rows, dtype=f32, device=x.device) if rstd is None else _dev_tensor(rstd, "rstd", f32, rows)
+    else:
+        rstd = None
+    _check(lib.layernorm_forward(_ptr(x), _dt(x), _ptr(weight), _ptr(bias), _DT[wdt], rows, cols, eps,
+                                 _ptr(y), _DT[ydt], _ptr(mean), _ptr(rstd), _stream(x.device)),
+           "layernorm_forward")
+    return y, mean, rstd
+
+
+def rmsnorm_forward(x, weight=None, eps: float = 1e-5, *, y=None, rms=None, need_rms=True):
+    """RMSNorm forward over the last dim.  Returns (y, rms or None)."""
+    _dev_tensor(x, "x")
+    rows, cols = _rows(x)
+    _dev_tensor(weight, "weight", x.dtype, cols)
+    y = torch.empty_like(x) if y is None else _dev_tensor(y, "y", x.dtype, x.numel())
+    if need_rms:
+        rms = torch.empty(rows, dtype=torch.float32, device=x.device) if rms is None else \
+            _dev_tensor(rms, "rms", torch.float32, rows)
+    else:
+        rms = None
+    _check(lib.rmsnorm_forward(_ptr(x), _dt(x), _ptr(weight), rows, cols, eps, _ptr(y), _ptr(rms),
+                               _stream(x.device)), "rmsnorm_forward")
+    return y, rms
 
 
 # ---- measurement --------------------------------------------------------------------------

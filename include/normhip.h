@@ -182,6 +182,40 @@ nh_status rmsnorm_backward(const void *dy, const void *x, nh_dtype t,
                            void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * LayerNorm / RMSNorm training forward over the last dimension of
+ * [rows, cols]: the forwards whose saved statistics the backwards above take.
+ * No workspace.
+ * ---------------------------------------------------------------------- */
+
+/*
+ * LayerNorm forward.  NVIDIA/Fuser issue #1473's layer_norm backward takes
+ * the per-row mean and rstd of this forward as inputs; they are computed with
+ * the one-pass shifted sums of Aether-ML PR #18 ("One-pass statistics")
+ * applied per row (shift = the row's first element):
+ *   mean = K + sum d / H, var = sum d^2 / H - (sum d / H)^2 (clamped at 0),
+ *   rstd = 1/sqrt(var + eps), y = (x - mean)*rstd*weight + bias.
+ *
+ *   x             [rows, cols] of x_t;   y [rows, cols] of y_t (y may equal x)
+ *   weight, bias  [cols] of w_t, each may be NULL (weight = 1, bias = 0)
+ *   mean          fp32 [rows] out (required); rstd fp32 [rows] out, or NULL
+ */
+nh_status layernorm_forward(const void *x, nh_dtype x_t, const void *weight, const void *bias,
+                            nh_dtype w_t, int64_t rows, int64_t cols, float eps,
+                            void *y, nh_dtype y_t, float *mean, float *rstd, void *stream);
+
+/*
+ * RMSNorm forward, NVIDIA/Fuser issue #3629's rmsnorm_prims:
+ *   rms = sqrt(sum_j x^2 / H + eps),  y = weight * (x / rms).
+ *
+ *   x, y          [rows, cols] of dtype t (y may equal x)
+ *   weight        [cols] of dtype t, or NULL (weight = 1)
+ *   rms           fp32 [rows] out (the saved input of rmsnorm_backward), or NULL
+ */
+nh_status rmsnorm_forward(const void *x, nh_dtype t, const void *weight,
+                          int64_t rows, int64_t cols, float eps, void *y, float *rms,
+                          void *stream);
+
+/* ------------------------------------------------------------------------
  * Measurement support.
  * ---------------------------------------------------------------------- */
 
@@ -198,7 +232,9 @@ typedef enum {
     NH_K_RMS_ROWS = 8,        /* RMSNorm row pass: dx + column partials */
     NH_K_RMS_COLSUM = 9,      /* RMSNorm dweight finalize */
     NH_K_CALIB = 10,          /* calibration kernels below */
-    NH_K_COUNT = 11
+    NH_K_LN_FWD = 11,         /* LayerNorm forward row pass */
+    NH_K_RMS_FWD = 12,        /* RMSNorm forward row pass */
+    NH_K_COUNT = 13
 } nh_kernel;
 
 /* Static name of a kernel id; "" for an unknown id. */

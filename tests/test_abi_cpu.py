@@ -43,8 +43,8 @@ def test_status_and_kernel_names():
         "NH_OK", "NH_ERR_NULL", "NH_ERR_SHAPE", "NH_ERR_DTYPE", "NH_ERR_WORKSPACE",
         "NH_ERR_HIP", "NH_ERR_ARG"]
     assert nh.status_string(99) == "NH_ERR_UNKNOWN"
-    assert [nh.lib.nh_kernel_name(i).decode() for i in range(11)] == nh.KERNELS
-    assert nh.lib.nh_kernel_name(11).decode() == ""
+    assert [nh.lib.nh_kernel_name(i).decode() for i in range(13)] == nh.KERNELS
+    assert nh.lib.nh_kernel_name(13).decode() == ""
 
 
 def bn_fwd(x=FAKE, y=FAKE, io=0, N=2, C=3, HW=4, rm=NULL, rv=NULL, eps=1e-5, mom=0.1,
@@ -103,6 +103,25 @@ def test_rows_validation():
     assert rms(NULL, FAKE, 0, NULL, 1e-5, NULL, 4, 8, FAKE, NULL, FAKE, 1, NULL) == NH_ERR_NULL
     assert rms(FAKE, FAKE, 0, NULL, -1.0, NULL, 4, 8, FAKE, NULL, FAKE, 1, NULL) == NH_ERR_ARG
     assert rms(FAKE, FAKE, 1, NULL, float("nan"), NULL, 4, 8, FAKE, NULL, FAKE, 1, NULL) == NH_ERR_ARG
+
+
+def test_forward_validation():
+    lnf = nh.lib.layernorm_forward
+    # x, x_t, w, b, w_t, rows, cols, eps, y, y_t, mean, rstd, stream
+    assert lnf(FAKE, 2, NULL, NULL, 0, 4, 8, 1e-5, FAKE, 0, FAKE, NULL, NULL) == NH_ERR_DTYPE
+    assert lnf(FAKE, 0, NULL, NULL, 0, 4, 8, 1e-5, FAKE, 9, FAKE, NULL, NULL) == NH_ERR_DTYPE
+    assert lnf(FAKE, 0, NULL, NULL, 0, -4, 8, 1e-5, FAKE, 0, FAKE, NULL, NULL) == NH_ERR_SHAPE
+    assert lnf(FAKE, 0, NULL, NULL, 0, 4, 8, 1e-5, FAKE, 0, NULL, NULL, NULL) == NH_ERR_NULL
+    assert lnf(NULL, 0, NULL, NULL, 0, 4, 8, 1e-5, FAKE, 0, FAKE, NULL, NULL) == NH_ERR_NULL
+    assert lnf(FAKE, 0, NULL, NULL, 0, 4, 8, -1.0, FAKE, 0, FAKE, NULL, NULL) == NH_ERR_ARG
+    assert lnf(NULL, 0, NULL, NULL, 0, 0, 8, 1e-5, NULL, 0, NULL, NULL, NULL) == NH_OK
+    rmf = nh.lib.rmsnorm_forward
+    # x, t, w, rows, cols, eps, y, rms, stream
+    assert rmf(FAKE, 5, NULL, 4, 8, 1e-5, FAKE, NULL, NULL) == NH_ERR_DTYPE
+    assert rmf(FAKE, 0, NULL, 1 << 20, 1 << 12, 1e-5, FAKE, NULL, NULL) == NH_ERR_SHAPE
+    assert rmf(FAKE, 0, NULL, 4, 8, 1e-5, NULL, NULL, NULL) == NH_ERR_NULL
+    assert rmf(FAKE, 0, NULL, 4, 8, float("inf"), FAKE, NULL, NULL) == NH_ERR_ARG
+    assert rmf(NULL, 0, NULL, 3, 0, 1e-5, NULL, NULL, NULL) == NH_OK
 
 
 def test_measurement_validation():
