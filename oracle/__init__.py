@@ -41,13 +41,17 @@ def _load():
         i64, dbl, p = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
         lib.oracle_bn_forward_train.argtypes = [i64, i64, i64, p, p, p, dbl, dbl, p, p, p, p]
         lib.oracle_bn_backward.argtypes = [i64, i64, i64, p, p, p, dbl, p, p]
+        lib.oracle_bn_act_forward_train.argtypes = [i64, i64, i64, p, p, p, dbl, dbl, ctypes.c_int,
+                                                     dbl, p, p, p, p]
+        lib.oracle_bn_act_backward.argtypes = [i64, i64, i64, p, p, p, p, dbl, ctypes.c_int, dbl, p, p]
         lib.oracle_layernorm_stats.argtypes = [i64, i64, p, dbl, p, p]
         lib.oracle_layernorm_forward.argtypes = [i64, i64, p, p, p, dbl, p, p, p]
         lib.oracle_rmsnorm_forward.argtypes = [i64, i64, p, p, dbl, p, p]
         lib.oracle_layernorm_backward.argtypes = [i64, i64, p, p, p, p, p, p, p, p]
         lib.oracle_rmsnorm_rms.argtypes = [i64, i64, p, dbl, p]
         lib.oracle_rmsnorm_backward.argtypes = [i64, i64, p, p, p, p, dbl, p, p]
-        for f in ("oracle_bn_forward_train", "oracle_bn_backward", "oracle_layernorm_stats",
+        for f in ("oracle_bn_forward_train", "oracle_bn_backward", "oracle_bn_act_forward_train",
+                  "oracle_bn_act_backward", "oracle_layernorm_stats",
                   "oracle_layernorm_forward", "oracle_layernorm_backward", "oracle_rmsnorm_rms",
                   "oracle_rmsnorm_forward", "oracle_rmsnorm_backward"):
             getattr(lib, f).restype = ctypes.c_int
@@ -99,6 +103,41 @@ def bn_backward(x, dy, gamma, *, eps=1e-5):
     rc = _load().oracle_bn_backward(N, C, HW, _ptr(x), _ptr(dy), _ptr(g), eps,
                                     _ptr(dx), _ptr(grads))
     _check(rc, "oracle_bn_backward")
+    return dx, grads
+
+
+ACTS = {"none": 0, "relu": 1, "leaky_relu": 2}
+
+
+def bn_act_forward_train(x, gamma, beta, act, slope=0.01, *, eps=1e-5, momentum=0.1,
+                         running_mean=None, running_var=None):
+    """BatchNorm2d + activation forward.  Returns (y, stats[4,C], rm', rv')."""
+    x = _d(x)
+    N, C = x.shape[0], x.shape[1]
+    HW = int(np.prod(x.shape[2:])) if x.ndim > 2 else 1
+    g, b = _d(gamma), _d(beta)
+    rm = None if running_mean is None else _d(running_mean).copy()
+    rv = None if running_var is None else _d(running_var).copy()
+    y = np.empty_like(x)
+    stats = np.empty((4, C), np.float64)
+    rc = _load().oracle_bn_act_forward_train(N, C, HW, _ptr(x), _ptr(g), _ptr(b), momentum, eps,
+                                             ACTS[act], slope, _ptr(rm), _ptr(rv), _ptr(y),
+                                             _ptr(stats))
+    _check(rc, "oracle_bn_act_forward_train")
+    return y, stats, rm, rv
+
+
+def bn_act_backward(x, dy, gamma, beta, act, slope=0.01, *, eps=1e-5):
+    """Returns (dx, grads[4,C]) of y = act(BatchNorm(x))."""
+    x, dy = _d(x), _d(dy)
+    N, C = x.shape[0], x.shape[1]
+    HW = int(np.prod(x.shape[2:])) if x.ndim > 2 else 1
+    g, b = _d(gamma), _d(beta)
+    dx = np.empty_like(x)
+    grads = np.empty((4, C), np.float64)
+    rc = _load().oracle_bn_act_backward(N, C, HW, _ptr(x), _ptr(dy), _ptr(g), _ptr(b), eps,
+                                        ACTS[act], slope, _ptr(dx), _ptr(grads))
+    _check(rc, "oracle_bn_act_backward")
     return dx, grads
 
 

@@ -204,6 +204,64 @@ int oracle_bn_backward(int64_t N, int64_t C, int64_t HW,
 }
 
 /*
+ * BatchNorm2d followed by an activation, the fusion [AE] names as its next
+ * step ("Follow-ups": ReLU/LeakyReLU fused into BatchNorm).  z = the
+ * BatchNorm training forward output above, y = act(z) with
+ *   act = none (act 0), ReLU max(z, 0) (act 1), LeakyReLU z > 0 ? z : slope*z (act 2).
+ * Backward: dz = dy * act'(z) with act'(z) = 1 for z > 0, else 0 (ReLU) or
+ * slope (LeakyReLU) -- the derivative at z = 0 taken from the left, as
+ * PyTorch does -- then the BatchNorm backward of dz.
+ */
+static double act_value(int act, double slope, double z)
+{
+    if (act == 1) return z > 0.0 ? z : 0.0;
+    if (act == 2) return z > 0.0 ? z : slope * z;
+    return z;
+}
+
+static double act_slope(int act, double slope, double z)
+{
+    if (act == 0 || z > 0.0) return 1.0;
+    return act == 1 ? 0.0 : slope;
+}
+
+int oracle_bn_act_forward_train(int64_t N, int64_t C, int64_t HW, const double *x,
+                                const double *gamma, const double *beta, double momentum,
+                                double eps, int act, double slope, double *running_mean,
+                                double *running_var, double *y, double *stats)
+{
+    if (act < 0 || act > 2) return -1;
+    int rc = oracle_bn_forward_train(N, C, HW, x, gamma, beta, momentum, eps, running_mean,
+                                     running_var, y, stats);
+    if (rc != 0) return rc;
+    const size_t n = (size_t)(N * C * HW);
+    for (size_t i = 0; i < n; ++i) y[i] = act_value(act, slope, y[i]);
+    return 0;
+}
+
+int oracle_bn_act_backward(int64_t N, int64_t C, int64_t HW, const double *x, const double *dy,
+                           const double *gamma, const double *beta, double eps, int act,
+                           double slope, double *dx, double *grads)
+{
+    if (N < 0 || C < 0 || HW < 0 || act < 0 || act > 2) return -1;
+    const size_t n = (size_t)(N * C * HW);
+    if (n == 0) return -1;
+    double *z = (double *)malloc(n * sizeof(double));
+    double *dz = (double *)malloc(n * sizeof(double));
+    double *stats = (double *)malloc((size_t)(4 * C) * sizeof(double));
+    if (!z || !dz || !stats) { free(z); free(dz); free(stats); return -1; }
+    int rc = oracle_bn_forward_train(N, C, HW, x, gamma, beta, 0.0, eps, NULL, NULL, z, stats);
+    if (rc == 0) {
+        for (size_t i = 0; i < n; ++i) dz[i] = dy[i] * act_slope(act, slope, z[i]);
+        rc = oracle_bn_backward(N, C, HW, x, dz, gamma, eps, dx, grads);
+    }
+    free(z);
+    free(dz);
+    free(stats);
+    return rc;
+}
+
+/*
  * LayerNorm forward statistics over the last dimension, used to make the
  * saved mean/rstd that the backward consumes: mean = sum x / H,
  * var = sum (x - mean)^2 / H (biased), rstd = 1/sqrt(var + eps).

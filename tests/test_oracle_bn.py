@@ -237,3 +237,61 @@ def test_bn_special_cases(oracle_mod):
     with pytest.raises(ValueError):
         oracle_mod.bn_forward_train(np.ones((1, 2, 1, 1)), [1, 1], [0, 0],
                                     running_mean=np.zeros(2), running_var=np.ones(2))
+
+
+# ------------------------------------------- BatchNorm + activation (next step)
+
+@pytest.mark.parametrize("act,slope", [("relu", 0.0), ("leaky_relu", 0.01), ("leaky_relu", 0.2),
+                                       ("none", 0.0)])
+def test_bn_act_matches_torch(oracle_mod, act, slope):
+    c = wl.bn_case(3, 5, 6, 7, wl.F32, seed=91, x_mean=0.3, x_std=1.3, beta_std=0.5)
+    x, dy = c.x.value, c.dy.value
+    g, b = c.gamma.astype(np.float64), c.beta.astype(np.float64)
+    y, stats, rm, rv = oracle_mod.bn_act_forward_train(x, g, b, act, slope, eps=c.eps,
+                                                       running_mean=np.zeros(5), running_var=np.ones(5))
+    dx, grads = oracle_mod.bn_act_backward(x, dy, g, b, act, slope, eps=c.eps)
+    xt = torch.tensor(x, requires_grad=True)
+    gt = torch.tensor(g, requires_grad=True)
+    bt = torch.tensor(b, requires_grad=True)
+    rmt, rvt = torch.zeros(5, dtype=torch.float64), torch.ones(5, dtype=torch.float64)
+    z = F.batch_norm(xt, rmt, rvt, gt, bt, training=True, momentum=0.1, eps=c.eps)
+    yt = F.relu(z) if act == "relu" else (F.leaky_relu(z, slope) if act == "leaky_relu" else z)
+    yt.backward(torch.tensor(dy))
+    assert _rel(y, yt.detach().numpy()) < 1e-13
+    assert _rel(dx, xt.grad.numpy()) < 1e-12
+    assert _rel(grads[0], gt.grad.numpy()) < 1e-12
+    assert _rel(grads[1], bt.grad.numpy()) < 1e-12
+    assert _rel(rm, rmt.numpy()) < 1e-14 and _rel(rv, rvt.numpy()) < 1e-14
+    # act = none reduces to the plain BatchNorm functions
+    if act == "none":
+        y0, _, _, _ = oracle_mod.bn_forward_train(x, g, b, eps=c.eps)
+        dx0, gr0 = oracle_mod.bn_backward(x, dy, g, eps=c.eps)
+        assert np.array_equal(y, y0) and np.array_equal(dx, dx0) and np.array_equal(grads, gr0)
+
+
+def test_bn_act_finite_differences(oracle_mod):
+    """Away from the kink (every |z| > 0.05), the backward is the derivative of
+    the forward."""
+    rng = np.random.default_rng(92)
+    N, C, H, W = 2, 2, 3, 3
+    for _ in range(100):
+        x = rng.normal(0.0, 1.0, size=(N, C, H, W))
+        g = rng.uniform(0.5, 1.5, size=C)
+        b = rng.normal(0.0, 0.3, size=C)
+        z, _, _, _ = oracle_mod.bn_forward_train(x, g, b, eps=1e-5)
+        if np.min(np.abs(z)) > 0.05:
+            break
+    dy = rng.normal(size=x.shape)
+    for act, slope in (("relu", 0.0), ("leaky_relu", 0.1)):
+        def loss(xx):
+            y, _, _, _ = oracle_mod.bn_act_forward_train(xx, g, b, act, slope, eps=1e-5)
+            return float(np.sum(dy * y))
+        dx, _ = oracle_mod.bn_act_backward(x, dy, g, b, act, slope, eps=1e-5)
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            h = 1e-7
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            fd[idx] = (loss(xp) - loss(xm)) / (2 * h)
+        assert _rel(dx, fd) < 1e-6

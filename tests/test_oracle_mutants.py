@@ -43,6 +43,11 @@ MUTANTS = [
     ("rms_dweight_no_rinv", "ks_add(&sw[j], dyr[j] * xr[j] * rinv);", "ks_add(&sw[j], dyr[j] * xr[j]);"),
     ("ln_fwd_drops_bias", "yr[j] = (xr[j] - mu) * rs * (w ? w[j] : 1.0) + (b ? b[j] : 0.0);",
      "yr[j] = (xr[j] - mu) * rs * (w ? w[j] : 1.0);"),
+    ("act_leaky_fwd_no_slope", "if (act == 2) return z > 0.0 ? z : slope * z;",
+     "if (act == 2) return z > 0.0 ? z : z;"),
+    ("act_relu_bwd_passes", "return act == 1 ? 0.0 : slope;", "return act == 1 ? 1.0 : slope;"),
+    ("act_leaky_bwd_unit", "return act == 1 ? 0.0 : slope;", "return act == 1 ? 0.0 : 1.0;"),
+    ("act_mask_inverted", "if (act == 0 || z > 0.0) return 1.0;", "if (act == 0 || z < 0.0) return 1.0;"),
     ("rms_fwd_inverted", "yr[j] = (w ? w[j] : 1.0) * (xr[j] / rms);", "yr[j] = (w ? w[j] : 1.0) * (xr[j] * rms);"),
 ]
 
@@ -65,6 +70,9 @@ PINS = [
     ("ln_fwd_torch", lambda m: pr.test_ln_forward_matches_torch(m, 3, 7, 1)),
     ("rms_fwd_torch", lambda m: pr.test_rms_forward_matches_torch(m, 3, 7, 1)),
     ("fwd_exact", pr.test_forwards_exact_rational),
+    ("bn_act_relu", lambda m: pb.test_bn_act_matches_torch(m, "relu", 0.0)),
+    ("bn_act_leaky", lambda m: pb.test_bn_act_matches_torch(m, "leaky_relu", 0.2)),
+    ("bn_act_fd", pb.test_bn_act_finite_differences),
 ]
 
 
