@@ -44,6 +44,7 @@ def _load():
         lib.oracle_bn_act_forward_train.argtypes = [i64, i64, i64, p, p, p, dbl, dbl, ctypes.c_int,
                                                      dbl, p, p, p, p]
         lib.oracle_bn_act_backward.argtypes = [i64, i64, i64, p, p, p, p, dbl, ctypes.c_int, dbl, p, p]
+        lib.oracle_bn_infer.argtypes = [i64, i64, i64, p, p, p, p, p, dbl, ctypes.c_int, dbl, p]
         lib.oracle_layernorm_stats.argtypes = [i64, i64, p, dbl, p, p]
         lib.oracle_layernorm_forward.argtypes = [i64, i64, p, p, p, dbl, p, p, p]
         lib.oracle_rmsnorm_forward.argtypes = [i64, i64, p, p, dbl, p, p]
@@ -51,7 +52,7 @@ def _load():
         lib.oracle_rmsnorm_rms.argtypes = [i64, i64, p, dbl, p]
         lib.oracle_rmsnorm_backward.argtypes = [i64, i64, p, p, p, p, dbl, p, p]
         for f in ("oracle_bn_forward_train", "oracle_bn_backward", "oracle_bn_act_forward_train",
-                  "oracle_bn_act_backward", "oracle_layernorm_stats",
+                  "oracle_bn_act_backward", "oracle_bn_infer", "oracle_layernorm_stats",
                   "oracle_layernorm_forward", "oracle_layernorm_backward", "oracle_rmsnorm_rms",
                   "oracle_rmsnorm_forward", "oracle_rmsnorm_backward"):
             getattr(lib, f).restype = ctypes.c_int
@@ -139,6 +140,21 @@ def bn_act_backward(x, dy, gamma, beta, act, slope=0.01, *, eps=1e-5):
                                         ACTS[act], slope, _ptr(dx), _ptr(grads))
     _check(rc, "oracle_bn_act_backward")
     return dx, grads
+
+
+def bn_infer(x, gamma, beta, running_mean, running_var, act="none", slope=0.01, *, eps=1e-5):
+    """BatchNorm2d inference (+ activation) from the running statistics."""
+    x = _d(x)
+    N, C = x.shape[0], x.shape[1]
+    HW = int(np.prod(x.shape[2:])) if x.ndim > 2 else 1
+    g = None if gamma is None else _d(gamma)
+    b = None if beta is None else _d(beta)
+    rm, rv = _d(running_mean), _d(running_var)
+    y = np.empty_like(x)
+    rc = _load().oracle_bn_infer(N, C, HW, _ptr(x), _ptr(g), _ptr(b), _ptr(rm), _ptr(rv), eps,
+                                 ACTS[act], slope, _ptr(y))
+    _check(rc, "oracle_bn_infer")
+    return y
 
 
 def layernorm_stats(x, *, eps=1e-5):

@@ -262,6 +262,30 @@ int oracle_bn_act_backward(int64_t N, int64_t C, int64_t HW, const double *x, co
 }
 
 /*
+ * BatchNorm2d inference (evaluation mode) with the same optional activation:
+ * the running statistics stand in for the batch statistics,
+ *   y = act(gamma * (x - running_mean) / sqrt(running_var + eps) + beta).
+ * The Aether-ML BatchNorm PR applies inference with the same centred
+ * elementwise step as training (its _bn_apply_ew commit).
+ */
+int oracle_bn_infer(int64_t N, int64_t C, int64_t HW, const double *x, const double *gamma,
+                    const double *beta, const double *running_mean, const double *running_var,
+                    double eps, int act, double slope, double *y)
+{
+    if (N < 0 || C < 0 || HW < 0 || act < 0 || act > 2 || !running_mean || !running_var) return -1;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t c = 0; c < C; ++c) {
+            const double g = gamma ? gamma[c] : 1.0, b = beta ? beta[c] : 0.0;
+            const double sd = sqrt(running_var[c] + eps);
+            for (int64_t j = 0; j < HW; ++j) {
+                const size_t i = bn_index(n, c, j, C, HW);
+                y[i] = act_value(act, slope, g * (x[i] - running_mean[c]) / sd + b);
+            }
+        }
+    return 0;
+}
+
+/*
  * LayerNorm forward statistics over the last dimension, used to make the
  * saved mean/rstd that the backward consumes: mean = sum x / H,
  * var = sum (x - mean)^2 / H (biased), rstd = 1/sqrt(var + eps).

@@ -295,3 +295,35 @@ def test_bn_act_finite_differences(oracle_mod):
             xm[idx] -= h
             fd[idx] = (loss(xp) - loss(xm)) / (2 * h)
         assert _rel(dx, fd) < 1e-6
+
+
+@pytest.mark.parametrize("act,slope", [("none", 0.0), ("relu", 0.0), ("leaky_relu", 0.1)])
+def test_bn_infer_matches_torch(oracle_mod, act, slope):
+    c = wl.bn_case(4, 6, 5, 3, wl.F32, seed=93, x_mean=1.0, x_std=2.0, beta_std=0.5)
+    rng = np.random.default_rng(94)
+    rm = rng.normal(1.0, 0.5, size=6)
+    rv = rng.uniform(0.5, 4.0, size=6)
+    g, b = c.gamma.astype(np.float64), c.beta.astype(np.float64)
+    y = oracle_mod.bn_infer(c.x.value, g, b, rm, rv, act, slope, eps=c.eps)
+    z = F.batch_norm(torch.tensor(c.x.value), torch.tensor(rm), torch.tensor(rv), torch.tensor(g),
+                     torch.tensor(b), training=False, eps=c.eps)
+    yt = F.relu(z) if act == "relu" else (F.leaky_relu(z, slope) if act == "leaky_relu" else z)
+    assert _rel(y, yt.numpy()) < 1e-14
+    # affine off
+    y0 = oracle_mod.bn_infer(c.x.value, None, None, rm, rv, act, slope, eps=c.eps)
+    z0 = F.batch_norm(torch.tensor(c.x.value), torch.tensor(rm), torch.tensor(rv), training=False,
+                      eps=c.eps)
+    y0t = F.relu(z0) if act == "relu" else (F.leaky_relu(z0, slope) if act == "leaky_relu" else z0)
+    assert _rel(y0, y0t.numpy()) < 1e-14
+
+
+def test_bn_infer_with_batch_statistics_is_training_forward(oracle_mod):
+    """Evaluation with running statistics equal to the batch's own (mean,
+    biased var) reproduces the training forward output."""
+    c = wl.bn_case(3, 5, 4, 4, wl.F32, seed=95, x_mean=-2.0, x_std=0.7, beta_std=1.0)
+    for act, slope in (("none", 0.0), ("relu", 0.0), ("leaky_relu", 0.3)):
+        yt, stats, _, _ = oracle_mod.bn_act_forward_train(c.x.value, c.gamma, c.beta, act, slope,
+                                                          eps=c.eps)
+        yi = oracle_mod.bn_infer(c.x.value, c.gamma, c.beta, stats[0], stats[1], act, slope,
+                                 eps=c.eps)
+        assert _rel(yi, yt) < 1e-14

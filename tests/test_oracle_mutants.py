@@ -48,6 +48,9 @@ MUTANTS = [
     ("act_relu_bwd_passes", "return act == 1 ? 0.0 : slope;", "return act == 1 ? 1.0 : slope;"),
     ("act_leaky_bwd_unit", "return act == 1 ? 0.0 : slope;", "return act == 1 ? 0.0 : 1.0;"),
     ("act_mask_inverted", "if (act == 0 || z > 0.0) return 1.0;", "if (act == 0 || z < 0.0) return 1.0;"),
+    ("infer_drops_mean", "y[i] = act_value(act, slope, g * (x[i] - running_mean[c]) / sd + b);",
+     "y[i] = act_value(act, slope, g * x[i] / sd + b);"),
+    ("infer_no_eps", "const double sd = sqrt(running_var[c] + eps);", "const double sd = sqrt(running_var[c]);"),
     ("rms_fwd_inverted", "yr[j] = (w ? w[j] : 1.0) * (xr[j] / rms);", "yr[j] = (w ? w[j] : 1.0) * (xr[j] * rms);"),
 ]
 
@@ -73,6 +76,8 @@ PINS = [
     ("bn_act_relu", lambda m: pb.test_bn_act_matches_torch(m, "relu", 0.0)),
     ("bn_act_leaky", lambda m: pb.test_bn_act_matches_torch(m, "leaky_relu", 0.2)),
     ("bn_act_fd", pb.test_bn_act_finite_differences),
+    ("bn_infer_torch", lambda m: pb.test_bn_infer_matches_torch(m, "relu", 0.0)),
+    ("bn_infer_batch", pb.test_bn_infer_with_batch_statistics_is_training_forward),
 ]
 
 
