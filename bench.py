@@ -100,6 +100,7 @@ class Timed:
 
 # ---- BatchNorm --------------------------------------------------------------------
 BN_KERNELS = ["bn_stats", "bn_fwd_finalize", "bn_apply", "bn_grad_sums", "bn_bwd_finalize", "bn_dx"]
+ACT_IDS = {"none": 0, "relu": 1, "leaky_relu": 2}
 
 
 def bn_bytes(case):
@@ -110,7 +111,7 @@ def bn_bytes(case):
             "bn_fwd_finalize": None, "bn_bwd_finalize": None}
 
 
-def bench_bn(nh, torch, case, K, W, cold=True):
+def bench_bn(nh, torch, case, K, W, cold=True, act="none", slope=0.01):
     import ctypes
     device = torch.device("cuda:0")
     x0, dy0 = _dev(case.x, device), _dev(case.dy, device)
@@ -136,15 +137,28 @@ def bench_bn(nh, torch, case, K, W, cold=True):
         calls.append((p, s["ws"].numel()))
     lib = nh.lib
 
-    def step(i):
-        p, nb = calls[i % R]
-        st = lib.bn_forward_train(p["x"], p["y"], io, N, C, HW, P(g.data_ptr()), P(b.data_ptr()),
-                                  p["rm"], p["rv"], case.momentum, case.eps, p["stats"], p["ws"], nb,
-                                  stream)
-        st |= lib.bn_backward(p["dy"], p["x"], io, N, C, HW, p["stats"], p["dx"], p["grads"],
-                              p["ws"], nb, stream)
-        if st:
-            raise RuntimeError(nh.last_error())
+    if act == "none":
+        def step(i):
+            p, nb = calls[i % R]
+            st = lib.bn_forward_train(p["x"], p["y"], io, N, C, HW, P(g.data_ptr()), P(b.data_ptr()),
+                                      p["rm"], p["rv"], case.momentum, case.eps, p["stats"], p["ws"],
+                                      nb, stream)
+            st |= lib.bn_backward(p["dy"], p["x"], io, N, C, HW, p["stats"], p["dx"], p["grads"],
+                                  p["ws"], nb, stream)
+            if st:
+                raise RuntimeError(nh.last_error())
+    else:
+        a = ACT_IDS[act]
+
+        def step(i):
+            p, nb = calls[i % R]
+            st = lib.bn_act_forward_train(p["x"], p["y"], io, N, C, HW, P(g.data_ptr()),
+                                          P(b.data_ptr()), p["rm"], p["rv"], case.momentum, case.eps,
+                                          a, slope, p["stats"], p["ws"], nb, stream)
+            st |= lib.bn_act_backward(p["dy"], p["x"], io, N, C, HW, p["stats"], P(b.data_ptr()), a,
+                                      slope, p["dx"], p["grads"], p["ws"], nb, stream)
+            if st:
+                raise RuntimeError(nh.last_error())
 
     tm = Timed(nh, torch)
     ms, per = tm.run(step, K, W, BN_KERNELS)
@@ -161,6 +175,44 @@ def bench_bn(nh, torch, case, K, W, cold=True):
             "us_per_call_with_kernel_events": 1000.0 * tm.events_ms, "step_bytes": step_bytes,
             "gbs": step_bytes / (ms * 1e6), "buffer_sets": R, "kernels": per,
             "grid_y": nh.bn_plan(N, C, HW, io)}
+
+
+def bench_bn_infer(nh, torch, case, K, W, act="relu", slope=0.01):
+    """BatchNorm2d inference (+ activation): one elementwise pass, x read and
+    y written once."""
+    import ctypes
+    device = torch.device("cuda:0")
+    x0 = _dev(case.x, device)
+    g, b = _dev(case.gamma, device), _dev(case.beta, device)
+    io = 0 if case.io == "f32" else 1
+    N, C, HW = case.N, case.C, case.hw
+    rm = torch.linspace(-0.5, 0.5, C, device=device)
+    rv = torch.linspace(0.5, 2.0, C, device=device)
+    R = _nsets(2 * x0.numel() * x0.element_size(), True)
+    sets = [(x0.clone(), torch.empty_like(x0)) for _ in range(R)]
+    torch.cuda.synchronize()
+    P = ctypes.c_void_p
+    stream = P(torch.cuda.current_stream(device).cuda_stream)
+    ptrs = [(P(x.data_ptr()), P(y.data_ptr())) for x, y in sets]
+    a = ACT_IDS[act]
+
+    def step(i):
+        x, y = ptrs[i % R]
+        if nh.lib.bn_forward_infer(x, y, io, N, C, HW, P(g.data_ptr()), P(b.data_ptr()),
+                                   P(rm.data_ptr()), P(rv.data_ptr()), case.eps, a, slope, stream):
+            raise RuntimeError(nh.last_error())
+
+    tm = Timed(nh, torch)
+    ms, per = tm.run(step, K, W, ["bn_infer"], launches_per_step=1)
+    byt = 2 * x0.numel() * x0.element_size()
+    for v in per.values():
+        v["bytes"] = byt
+        v["gbs"] = byt / (v["avg_us"] * 1e3)
+        v["frac_of_peak"] = v["gbs"] / HBM_PEAK_GBS
+    del sets, ptrs
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms, "us_per_call": 1000.0 * ms, "step_bytes": byt,
+            "gbs": byt / (ms * 1e6), "buffer_sets": R, "kernels": per}
 
 
 # ---- LayerNorm / RMSNorm -----------------------------------------------------------
@@ -485,6 +537,16 @@ def main():
                          ("bn_ragged_3x37x41x40_f32", wl.bn_ragged)):
             log(f"[bench] {name}")
             others[name] = bench_bn(nh, torch, fn(), kk, W, cold=True)
+        for name, fn, act in (("bn_relu_cifar_256x32x32x32_f32", lambda: wl.bn_cifar(wl.F32), "relu"),
+                              ("bn_leaky_relu_cifar_256x32x32x32_f32", lambda: wl.bn_cifar(wl.F32),
+                               "leaky_relu"),
+                              ("bn_relu_resnet_64x256x56x56_bf16", wl.bn_resnet, "relu")):
+            log(f"[bench] {name}")
+            others[name] = bench_bn(nh, torch, fn(), kk, W, cold=True, act=act)
+        for name, fn in (("bn_infer_relu_cifar_256x32x32x32_f32", lambda: wl.bn_cifar(wl.F32)),
+                         ("bn_infer_relu_resnet_64x256x56x56_bf16", wl.bn_resnet)):
+            log(f"[bench] {name}")
+            others[name] = bench_bn_infer(nh, torch, fn(), kk, W)
         log("[bench] ln_bwd_16x512x1600 (x f32, dy bf16, w bf16, dx f32)")
         others["ln_bwd_16x512x1600"] = bench_rows(nh, torch, wl.ln_bwd(), "ln", kk, W)
         for dt in (wl.BF16, wl.F32):

@@ -250,7 +250,7 @@ const char *nh_kernel_name(int k)
 {
     static const char *names[NH_K_COUNT] = {
         "bn_stats", "bn_fwd_finalize", "bn_apply", "bn_grad_sums", "bn_bwd_finalize", "bn_dx",
-        "ln_rows", "ln_colsum", "rms_rows", "rms_colsum", "calib", "ln_fwd", "rms_fwd"};
+        "ln_rows", "ln_colsum", "rms_rows", "rms_colsum", "calib", "ln_fwd", "rms_fwd", "bn_infer"};
     return (k >= 0 && k < NH_K_COUNT) ? names[k] : "";
 }
 
@@ -272,10 +272,18 @@ nh_status bn_backward_workspace(int64_t N, int64_t C, int64_t HW, size_t *ws_byt
     return bn_forward_train_workspace(N, C, HW, ws_bytes);
 }
 
-nh_status bn_forward_train(const void *x, void *y, nh_dtype io, int64_t N, int64_t C, int64_t HW,
-                           const float *gamma, const float *beta, float *running_mean,
-                           float *running_var, float momentum, float eps, float *stats, void *ws,
-                           size_t ws_bytes, void *stream)
+static nh_status check_act(nh_act act, float slope)
+{
+    if (act != NH_ACT_NONE && act != NH_ACT_RELU && act != NH_ACT_LEAKY_RELU)
+        return fail(NH_ERR_ARG, "act %d is not an nh_act value", (int)act);
+    if (act == NH_ACT_LEAKY_RELU && !isfinite(slope)) return fail(NH_ERR_ARG, "slope must be finite");
+    return NH_OK;
+}
+
+nh_status bn_act_forward_train(const void *x, void *y, nh_dtype io, int64_t N, int64_t C, int64_t HW,
+                               const float *gamma, const float *beta, float *running_mean,
+                               float *running_var, float momentum, float eps, nh_act act, float slope,
+                               float *stats, void *ws, size_t ws_bytes, void *stream)
 {
     if (!valid_dtype(io)) return fail(NH_ERR_DTYPE, "io dtype %d", (int)io);
     nh_status st = bn_check_shape(N, C, HW);
@@ -287,6 +295,7 @@ nh_status bn_forward_train(const void *x, void *y, nh_dtype io, int64_t N, int64
         return fail(NH_ERR_SHAPE, "running statistics need more than one element per channel");
     if (!(eps >= 0.f) || !isfinite(eps)) return fail(NH_ERR_ARG, "eps must be finite and >= 0");
     if (!isfinite(momentum)) return fail(NH_ERR_ARG, "momentum must be finite");
+    if ((st = check_act(act, slope)) != NH_OK) return st;
     DeviceInfo d;
     if ((st = device_info(&d)) != NH_OK) return st;
     const size_t need = bn_ws_bytes(M, C, d);
@@ -308,6 +317,8 @@ nh_status bn_forward_train(const void *x, void *y, nh_dtype io, int64_t N, int64
     a.running_var = running_var;
     a.momentum = momentum;
     a.eps = eps;
+    a.act = act;
+    a.slope = slope;
     a.stats = stats;
     a.partials = static_cast<float *>(ws);
     a.separate_finalize = g_override_bn_finalize_kernels.load() != 0;
@@ -316,15 +327,25 @@ nh_status bn_forward_train(const void *x, void *y, nh_dtype io, int64_t N, int64
     return ok();
 }
 
-nh_status bn_backward(const void *dy, const void *x, nh_dtype io, int64_t N, int64_t C, int64_t HW,
-                      const float *stats, void *dx, float *grads, void *ws, size_t ws_bytes,
-                      void *stream)
+nh_status bn_forward_train(const void *x, void *y, nh_dtype io, int64_t N, int64_t C, int64_t HW,
+                           const float *gamma, const float *beta, float *running_mean,
+                           float *running_var, float momentum, float eps, float *stats, void *ws,
+                           size_t ws_bytes, void *stream)
+{
+    return bn_act_forward_train(x, y, io, N, C, HW, gamma, beta, running_mean, running_var, momentum,
+                                eps, NH_ACT_NONE, 0.f, stats, ws, ws_bytes, stream);
+}
+
+nh_status bn_act_backward(const void *dy, const void *x, nh_dtype io, int64_t N, int64_t C, int64_t HW,
+                          const float *stats, const float *beta, nh_act act, float slope, void *dx,
+                          float *grads, void *ws, size_t ws_bytes, void *stream)
 {
     if (!valid_dtype(io)) return fail(NH_ERR_DTYPE, "io dtype %d", (int)io);
     nh_status st = bn_check_shape(N, C, HW);
     if (st != NH_OK) return st;
     if (N * C * HW == 0) return ok();
     if (!dy || !x || !stats || !grads) return fail(NH_ERR_NULL, "dy, x, stats and grads are required");
+    if ((st = check_act(act, slope)) != NH_OK) return st;
     DeviceInfo d;
     if ((st = device_info(&d)) != NH_OK) return st;
     const int64_t M = N * HW;
@@ -342,12 +363,60 @@ nh_status bn_backward(const void *dy, const void *x, nh_dtype io, int64_t N, int
     a.x = x;
     a.dy = dy;
     a.out = dx;
+    a.beta = beta;
+    a.act = act;
+    a.slope = slope;
     a.stats = const_cast<float *>(stats);
     a.grads = grads;
     a.partials = static_cast<float *>(ws);
     a.separate_finalize = g_override_bn_finalize_kernels.load() != 0;
     hipError_t e = bn_backward_launch(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "bn_backward launch");
+    return ok();
+}
+
+nh_status bn_backward(const void *dy, const void *x, nh_dtype io, int64_t N, int64_t C, int64_t HW,
+                      const float *stats, void *dx, float *grads, void *ws, size_t ws_bytes,
+                      void *stream)
+{
+    return bn_act_backward(dy, x, io, N, C, HW, stats, nullptr, NH_ACT_NONE, 0.f, dx, grads, ws,
+                           ws_bytes, stream);
+}
+
+nh_status bn_forward_infer(const void *x, void *y, nh_dtype io, int64_t N, int64_t C, int64_t HW,
+                           const float *gamma, const float *beta, const float *running_mean,
+                           const float *running_var, float eps, nh_act act, float slope, void *stream)
+{
+    if (!valid_dtype(io)) return fail(NH_ERR_DTYPE, "io dtype %d", (int)io);
+    nh_status st = bn_check_shape(N, C, HW);
+    if (st != NH_OK) return st;
+    if (N * C * HW == 0) return ok();
+    if (!x || !y || !running_mean || !running_var)
+        return fail(NH_ERR_NULL, "x, y, running_mean and running_var are required");
+    if (!(eps >= 0.f) || !isfinite(eps)) return fail(NH_ERR_ARG, "eps must be finite and >= 0");
+    if ((st = check_act(act, slope)) != NH_OK) return st;
+    DeviceInfo d;
+    if ((st = device_info(&d)) != NH_OK) return st;
+
+    BnCall a{};
+    a.io = io;
+    a.N = (int)N;
+    a.C = (int)C;
+    a.HW = (int)HW;
+    a.vec = bn_vec(io, HW, x, y, nullptr);
+    a.grid_y = (int)bn_grid_y_for(N * (HW / a.vec), C, d);
+    a.inference = 1;
+    a.x = x;
+    a.out = y;
+    a.gamma = gamma;
+    a.beta = beta;
+    a.running_mean = const_cast<float *>(running_mean);
+    a.running_var = const_cast<float *>(running_var);
+    a.eps = eps;
+    a.act = act;
+    a.slope = slope;
+    hipError_t e = bn_forward_launch(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "bn_forward_infer launch");
     return ok();
 }
 

@@ -32,6 +32,18 @@
 // only and reads its per-channel constants once into scalar registers.  The
 // elementwise passes use the same split as the reductions.
 //
+// Activation (the BatchNorm + ReLU/LeakyReLU fusion the PR lists as its
+// follow-up): with z = fmaf(x - mean, scale, beta) the forward stores act(z),
+// and the backward multiplies dy by act'(z) before both of its passes use it.
+// The backward recomputes z from x, which it reads anyway, and from the same
+// fp32 mean/scale/beta the forward used, so its mask is bit-for-bit the
+// forward's and the fusion adds no memory traffic.  act'(0) is taken from the
+// left (ReLU 0, LeakyReLU slope).
+//
+// Inference applies the same centred step with the running statistics in
+// place of the batch statistics (mean = running_mean, scale =
+// gamma/sqrt(running_var + eps)): one elementwise pass, no workspace.
+//
 // No atomics anywhere: each reduction block writes its own partial slot, the
 // finalize kernels combine slots in index order, so results are
 // bit-identical run to run and the workspace needs no zeroing.
@@ -68,6 +80,24 @@ __device__ __forceinline__ int bn_unit_offset(const BnGeom &g, int c, int u)
     int n = (int)g.div_hwv.div((uint32_t)u);
     int j = u - n * g.HWv;
     return (n * g.C + c) * g.HW + j * V;
+}
+
+// Activations: 0 none, 1 ReLU, 2 LeakyReLU.
+template <int ACT>
+__device__ __forceinline__ float act_fwd(float z, float slope)
+{
+    if constexpr (ACT == 1) return z > 0.f ? z : 0.f;
+    else if constexpr (ACT == 2) return z > 0.f ? z : z * slope;
+    else return z;
+}
+
+// dy * act'(z).
+template <int ACT>
+__device__ __forceinline__ float act_bwd(float dy, float z, float slope)
+{
+    if constexpr (ACT == 1) return z > 0.f ? dy : 0.f;
+    else if constexpr (ACT == 2) return z > 0.f ? dy : dy * slope;
+    else return dy;
 }
 
 // Sums of (a, b) over a 256-thread block; the result is valid in thread 0.
@@ -144,16 +174,20 @@ bn_stats_kernel(const T *__restrict__ x, BnGeom g, float *__restrict__ partials)
 }
 
 // ---- backward reduction: sum dy, sum dy*(x - mean) ----------------------------
-template <typename T, int V, int NT>
+// With an activation, dy is first replaced by dz = dy * act'(z).
+template <typename T, int V, int NT, int ACT>
 __global__ void __launch_bounds__(kBnThreads)
 bn_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x,
-                    const float *__restrict__ stats, BnGeom g, float *__restrict__ partials)
+                    const float *__restrict__ stats, const float *__restrict__ beta, float slope,
+                    BnGeom g, float *__restrict__ partials)
 {
     const int c = blockIdx.x / g.grid_y;
     const int yb = blockIdx.x - c * g.grid_y;
     const int u0 = yb * g.upb;
     const int u1 = min(u0 + g.upb, g.units);
     const float mean = stats[c];
+    const float scale = ACT != 0 ? stats[3 * g.C + c] : 0.f;
+    const float bz = (ACT != 0 && beta) ? beta[c] : 0.f;
 
     float s1[kBnUnroll], s2[kBnUnroll];
 #pragma unroll
@@ -176,8 +210,10 @@ bn_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x,
             if (u < u1) {
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
-                    s1[k] += vd[k][e];
-                    s2[k] = fmaf(vd[k][e], vx[k][e] - mean, s2[k]);
+                    const float xc = vx[k][e] - mean;
+                    const float dz = act_bwd<ACT>(vd[k][e], fmaf(xc, scale, bz), slope);
+                    s1[k] += dz;
+                    s2[k] = fmaf(dz, xc, s2[k]);
                 }
             }
         }
@@ -304,10 +340,17 @@ struct FwdFinalizeArgs {
     int64_t M;
 };
 
-template <typename T, int V, bool FUSED, int NT>
+// Where the apply pass takes its per-channel (mean, scale) from.
+enum : int {
+    kApplyStats = 0,     // stats[4, C] written by a finalize kernel
+    kApplyFinalize = 1,  // finalize the channel in the prologue (FUSED above)
+    kApplyRunning = 2    // inference: running_mean, gamma/sqrt(running_var + eps)
+};
+
+template <typename T, int V, int SRC, int NT, int ACT>
 __global__ void __launch_bounds__(kBnThreads)
 bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ stats,
-                const float *__restrict__ beta, BnGeom g, FwdFinalizeArgs f)
+                const float *__restrict__ beta, BnGeom g, FwdFinalizeArgs f, float slope)
 {
     const int c = blockIdx.x / g.grid_y;
     const int yb = blockIdx.x - c * g.grid_y;
@@ -326,7 +369,7 @@ bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ 
     }
 
     float mean, scale;
-    if constexpr (FUSED) {
+    if constexpr (SRC == kApplyFinalize) {
         __shared__ float sh[2];
         if (threadIdx.x < kWave) {
             double S1, S2;
@@ -340,6 +383,12 @@ bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ 
         __syncthreads();
         mean = sh[0];
         scale = sh[1];
+    } else if constexpr (SRC == kApplyRunning) {
+        // Same rounding steps as the training finalize: inv_std in fp64,
+        // scale rounded once to fp32.
+        mean = f.running_mean[c];
+        const double inv_std = 1.0 / sqrt((double)f.running_var[c] + (double)f.eps);
+        scale = (float)((f.gamma ? (double)f.gamma[c] : 1.0) * inv_std);
     } else {
         mean = stats[c];
         scale = stats[3 * g.C + c];
@@ -352,7 +401,7 @@ bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ 
             if (u < u1) {
                 float o[V];
 #pragma unroll
-                for (int e = 0; e < V; ++e) o[e] = fmaf(v[k][e] - mean, scale, b);
+                for (int e = 0; e < V; ++e) o[e] = act_fwd<ACT>(fmaf(v[k][e] - mean, scale, b), slope);
                 st<(NT & kNtStores) != 0, T, V>(y + off[k], o);
             }
         }
@@ -367,11 +416,12 @@ bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ 
     }
 }
 
-template <typename T, int V, bool FUSED, int NT>
+template <typename T, int V, bool FUSED, int NT, int ACT>
 __global__ void __launch_bounds__(kBnThreads)
 bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ dx,
              const float *__restrict__ stats, float *__restrict__ grads, BnGeom g,
-             const float *__restrict__ partials, int64_t M)
+             const float *__restrict__ partials, int64_t M, const float *__restrict__ beta,
+             float slope)
 {
     const int c = blockIdx.x / g.grid_y;
     const int yb = blockIdx.x - c * g.grid_y;
@@ -379,6 +429,7 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
     const int u1 = min(u0 + g.upb, g.units);
     const float mean = stats[c];
     const float scale = stats[3 * g.C + c];
+    const float b = (ACT != 0 && beta) ? beta[c] : 0.f;
 
     int base = u0 + (int)threadIdx.x;
     float vx[kBnUnroll][V], vd[kBnUnroll][V];
@@ -417,8 +468,11 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
             if (u < u1) {
                 float o[V];
 #pragma unroll
-                for (int e = 0; e < V; ++e)
-                    o[e] = fmaf(vd[k][e], scale, fmaf(vx[k][e] - mean, k1, k2));
+                for (int e = 0; e < V; ++e) {
+                    const float xc = vx[k][e] - mean;
+                    const float dz = act_bwd<ACT>(vd[k][e], fmaf(xc, scale, b), slope);
+                    o[e] = fmaf(dz, scale, fmaf(xc, k1, k2));
+                }
                 st<(NT & kNtStores) != 0, T, V>(dx + off[k], o);
             }
         }
@@ -450,38 +504,41 @@ static BnGeom make_geom(const BnCall &a)
     return g;
 }
 
-template <typename T, int V>
+template <typename T, int V, int ACT>
 static hipError_t bn_forward_t(const BnCall &a, hipStream_t s)
 {
     const BnGeom g = make_geom(a);
     const T *x = static_cast<const T *>(a.x);
     const dim3 grid((unsigned)(a.C * a.grid_y)), block(kBnThreads);
-    hipError_t e = launch(NH_K_BN_STATS, bn_stats_kernel<T, V, kBnNtPolicy>, grid, block, 0, s, x, g, a.partials);
-    if (e != hipSuccess) return e;
     const int64_t M = (int64_t)a.N * a.HW;
     FwdFinalizeArgs f{a.partials, a.gamma, a.running_mean, a.running_var, a.momentum, a.eps, M};
+    if (a.inference)
+        return launch(NH_K_BN_INFER, bn_apply_kernel<T, V, kApplyRunning, kBnNtPolicy, ACT>, grid, block,
+                      0, s, x, static_cast<T *>(a.out), a.stats, a.beta, g, f, a.slope);
+    hipError_t e = launch(NH_K_BN_STATS, bn_stats_kernel<T, V, kBnNtPolicy>, grid, block, 0, s, x, g, a.partials);
+    if (e != hipSuccess) return e;
     if (a.separate_finalize) {
         const dim3 fgrid((unsigned)ceil_div(a.C, kBnThreads / kWave));
         e = launch(NH_K_BN_FWD_FINALIZE, bn_fwd_finalize, fgrid, block, 0, s, a.partials,
                    a.grid_y, a.C, M, a.gamma, a.running_mean, a.running_var, a.momentum,
                    a.eps, a.stats);
         if (e != hipSuccess) return e;
-        return launch(NH_K_BN_APPLY, bn_apply_kernel<T, V, false, kBnNtPolicy>, grid, block, 0, s, x,
-                      static_cast<T *>(a.out), a.stats, a.beta, g, f);
+        return launch(NH_K_BN_APPLY, bn_apply_kernel<T, V, kApplyStats, kBnNtPolicy, ACT>, grid, block, 0,
+                      s, x, static_cast<T *>(a.out), a.stats, a.beta, g, f, a.slope);
     }
-    return launch(NH_K_BN_APPLY, bn_apply_kernel<T, V, true, kBnNtPolicy>, grid, block, 0, s, x,
-                  static_cast<T *>(a.out), a.stats, a.beta, g, f);
+    return launch(NH_K_BN_APPLY, bn_apply_kernel<T, V, kApplyFinalize, kBnNtPolicy, ACT>, grid, block, 0,
+                  s, x, static_cast<T *>(a.out), a.stats, a.beta, g, f, a.slope);
 }
 
-template <typename T, int V>
+template <typename T, int V, int ACT>
 static hipError_t bn_backward_t(const BnCall &a, hipStream_t s)
 {
     const BnGeom g = make_geom(a);
     const T *x = static_cast<const T *>(a.x);
     const T *dy = static_cast<const T *>(a.dy);
     const dim3 grid((unsigned)(a.C * a.grid_y)), block(kBnThreads);
-    hipError_t e = launch(NH_K_BN_GRAD_SUMS, bn_grad_sums_kernel<T, V, kBnNtPolicy>, grid, block, 0, s, dy, x,
-                          a.stats, g, a.partials);
+    hipError_t e = launch(NH_K_BN_GRAD_SUMS, bn_grad_sums_kernel<T, V, kBnNtPolicy, ACT>, grid, block, 0,
+                          s, dy, x, a.stats, a.beta, a.slope, g, a.partials);
     if (e != hipSuccess) return e;
     const int64_t M = (int64_t)a.N * a.HW;
     if (a.separate_finalize || a.out == nullptr) {
@@ -489,23 +546,45 @@ static hipError_t bn_backward_t(const BnCall &a, hipStream_t s)
         e = launch(NH_K_BN_BWD_FINALIZE, bn_bwd_finalize, fgrid, block, 0, s, a.partials, a.grid_y,
                    a.C, M, a.stats, a.grads);
         if (e != hipSuccess || a.out == nullptr) return e;
-        return launch(NH_K_BN_DX, bn_dx_kernel<T, V, false, kBnNtPolicy>, grid, block, 0, s, dy, x,
-                      static_cast<T *>(a.out), a.stats, a.grads, g, a.partials, M);
+        return launch(NH_K_BN_DX, bn_dx_kernel<T, V, false, kBnNtPolicy, ACT>, grid, block, 0, s, dy, x,
+                      static_cast<T *>(a.out), a.stats, a.grads, g, a.partials, M, a.beta, a.slope);
     }
-    return launch(NH_K_BN_DX, bn_dx_kernel<T, V, true, kBnNtPolicy>, grid, block, 0, s, dy, x,
-                  static_cast<T *>(a.out), a.stats, a.grads, g, a.partials, M);
+    return launch(NH_K_BN_DX, bn_dx_kernel<T, V, true, kBnNtPolicy, ACT>, grid, block, 0, s, dy, x,
+                  static_cast<T *>(a.out), a.stats, a.grads, g, a.partials, M, a.beta, a.slope);
+}
+
+template <int ACT>
+static hipError_t bn_forward_act(const BnCall &a, hipStream_t s)
+{
+    if (a.io == 0) return a.vec == 4 ? bn_forward_t<float, 4, ACT>(a, s) : bn_forward_t<float, 1, ACT>(a, s);
+    return a.vec == 8 ? bn_forward_t<uint16_t, 8, ACT>(a, s) : bn_forward_t<uint16_t, 1, ACT>(a, s);
+}
+
+template <int ACT>
+static hipError_t bn_backward_act(const BnCall &a, hipStream_t s)
+{
+    if (a.io == 0) return a.vec == 4 ? bn_backward_t<float, 4, ACT>(a, s) : bn_backward_t<float, 1, ACT>(a, s);
+    return a.vec == 8 ? bn_backward_t<uint16_t, 8, ACT>(a, s) : bn_backward_t<uint16_t, 1, ACT>(a, s);
 }
 
 hipError_t bn_forward_launch(const BnCall &a, hipStream_t s)
 {
-    if (a.io == 0) return a.vec == 4 ? bn_forward_t<float, 4>(a, s) : bn_forward_t<float, 1>(a, s);
-    return a.vec == 8 ? bn_forward_t<uint16_t, 8>(a, s) : bn_forward_t<uint16_t, 1>(a, s);
+    switch (a.act) {
+    case 0: return bn_forward_act<0>(a, s);
+    case 1: return bn_forward_act<1>(a, s);
+    case 2: return bn_forward_act<2>(a, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t bn_backward_launch(const BnCall &a, hipStream_t s)
 {
-    if (a.io == 0) return a.vec == 4 ? bn_backward_t<float, 4>(a, s) : bn_backward_t<float, 1>(a, s);
-    return a.vec == 8 ? bn_backward_t<uint16_t, 8>(a, s) : bn_backward_t<uint16_t, 1>(a, s);
+    switch (a.act) {
+    case 0: return bn_backward_act<0>(a, s);
+    case 1: return bn_backward_act<1>(a, s);
+    case 2: return bn_backward_act<2>(a, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 } // namespace nh

@@ -52,10 +52,13 @@ struct BnCall {
     int vec;             // vector width in elements (1, 4 or 8)
     int grid_y;          // blocks per channel of the reduction and elementwise passes
     int separate_finalize;  // 1: finalize as its own kernel; 0: in the elementwise prologue
+    int inference;       // forward only: apply with the running statistics, no reduction
+    int act;             // 0 none, 1 ReLU, 2 LeakyReLU
+    float slope;         // LeakyReLU negative slope
     const void *x;
     const void *dy;      // backward only
     void *out;           // y (forward) or dx (backward; may be NULL)
-    const float *gamma, *beta;
+    const float *gamma, *beta;         // beta is also read by the backward with an activation
     float *running_mean, *running_var;
     float momentum, eps;
     float *stats;        // [4, C]

@@ -22,11 +22,14 @@ F32, BF16 = 0, 1
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 
 KERNELS = ["bn_stats", "bn_fwd_finalize", "bn_apply", "bn_grad_sums", "bn_bwd_finalize", "bn_dx",
-           "ln_rows", "ln_colsum", "rms_rows", "rms_colsum", "calib", "ln_fwd", "rms_fwd"]
+           "ln_rows", "ln_colsum", "rms_rows", "rms_colsum", "calib", "ln_fwd", "rms_fwd", "bn_infer"]
+
+ACTS = {"none": 0, "relu": 1, "leaky_relu": 2}
 
 EXPORTS = [
     "nh_status_string", "nh_last_error", "nh_kernel_name",
     "bn_forward_train_workspace", "bn_backward_workspace", "bn_forward_train", "bn_backward",
+    "bn_act_forward_train", "bn_act_backward", "bn_forward_infer",
     "layernorm_backward_workspace", "layernorm_backward",
     "rmsnorm_backward_workspace", "rmsnorm_backward", "layernorm_forward", "rmsnorm_forward",
     "nh_timing_enable", "nh_timing_reserve", "nh_timing_read", "nh_calib_copy", "nh_calib_add",
@@ -56,6 +59,10 @@ def _load():
         "bn_backward_workspace": (i32, [i64, i64, i64, psz]),
         "bn_forward_train": (i32, [p, p, i32, i64, i64, i64, p, p, p, p, f32, f32, p, p, sz, p]),
         "bn_backward": (i32, [p, p, i32, i64, i64, i64, p, p, p, p, sz, p]),
+        "bn_act_forward_train": (i32, [p, p, i32, i64, i64, i64, p, p, p, p, f32, f32, i32, f32, p, p,
+                                       sz, p]),
+        "bn_act_backward": (i32, [p, p, i32, i64, i64, i64, p, p, i32, f32, p, p, p, sz, p]),
+        "bn_forward_infer": (i32, [p, p, i32, i64, i64, i64, p, p, p, p, f32, i32, f32, p]),
         "layernorm_backward_workspace": (i32, [i64, i64, psz]),
         "layernorm_backward": (i32, [p, i32, p, i32, p, p, p, i32, i64, i64, p, i32, p, p, p, sz, p]),
         "rmsnorm_backward_workspace": (i32, [i64, i64, psz]),
@@ -167,10 +174,15 @@ def rmsnorm_backward_workspace(rows: int, cols: int) -> int:
 
 
 # ---- BatchNorm ---------------------------------------------------------------------
+def _act(act):
+    return ACTS[act] if isinstance(act, str) else int(act)
+
+
 def bn_forward_train(x, gamma=None, beta=None, running_mean=None, running_var=None,
-                     momentum: float = 0.1, eps: float = 1e-5, *, y=None, stats=None,
-                     workspace=None):
-    """BatchNorm2d training forward.  Returns (y, stats[4, C])."""
+                     momentum: float = 0.1, eps: float = 1e-5, *, act="none", slope: float = 0.01,
+                     y=None, stats=None, workspace=None):
+    """BatchNorm2d training forward (bn_forward_train, or bn_act_forward_train
+    when act is not "none").  Returns (y, stats[4, C])."""
     _dev_tensor(x, "x")
     N, C, HW = _nchw(x)
     f32 = torch.float32
@@ -182,19 +194,28 @@ def bn_forward_train(x, gamma=None, beta=None, running_mean=None, running_var=No
         _dev_tensor(stats, "stats", f32, 4 * C)
     ws = _workspace(bn_forward_train_workspace(N, C, HW), x.device, workspace)
     nb = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib.bn_forward_train(_ptr(x), _ptr(y), _dt(x), N, C, HW, _ptr(gamma), _ptr(beta),
-                                _ptr(running_mean), _ptr(running_var), momentum, eps, _ptr(stats),
-                                _ptr(ws), nb, _stream(x.device)), "bn_forward_train")
+    if act == "none":
+        _check(lib.bn_forward_train(_ptr(x), _ptr(y), _dt(x), N, C, HW, _ptr(gamma), _ptr(beta),
+                                    _ptr(running_mean), _ptr(running_var), momentum, eps,
+                                    _ptr(stats), _ptr(ws), nb, _stream(x.device)), "bn_forward_train")
+    else:
+        _check(lib.bn_act_forward_train(_ptr(x), _ptr(y), _dt(x), N, C, HW, _ptr(gamma), _ptr(beta),
+                                        _ptr(running_mean), _ptr(running_var), momentum, eps,
+                                        _act(act), slope, _ptr(stats), _ptr(ws), nb,
+                                        _stream(x.device)), "bn_act_forward_train")
     return y, stats
 
 
-def bn_backward(dy, x, stats, *, dx=None, grads=None, need_dx=True, workspace=None):
-    """BatchNorm2d training backward.  Returns (dx or None, grads[4, C])."""
+def bn_backward(dy, x, stats, *, beta=None, act="none", slope: float = 0.01, dx=None, grads=None,
+                need_dx=True, workspace=None):
+    """BatchNorm2d training backward (bn_backward, or bn_act_backward when act
+    is not "none").  Returns (dx or None, grads[4, C])."""
     _dev_tensor(x, "x")
     _dev_tensor(dy, "dy", x.dtype, x.numel())
     N, C, HW = _nchw(x)
     f32 = torch.float32
     _dev_tensor(stats, "stats", f32, 4 * C)
+    _dev_tensor(beta, "beta", f32, C)
     if need_dx:
         dx = torch.empty_like(x) if dx is None else _dev_tensor(dx, "dx", x.dtype, x.numel())
     else:
@@ -203,9 +224,30 @@ def bn_backward(dy, x, stats, *, dx=None, grads=None, need_dx=True, workspace=No
         _dev_tensor(grads, "grads", f32, 4 * C)
     ws = _workspace(bn_backward_workspace(N, C, HW), x.device, workspace)
     nb = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib.bn_backward(_ptr(dy), _ptr(x), _dt(x), N, C, HW, _ptr(stats), _ptr(dx), _ptr(grads),
-                           _ptr(ws), nb, _stream(x.device)), "bn_backward")
+    if act == "none":
+        _check(lib.bn_backward(_ptr(dy), _ptr(x), _dt(x), N, C, HW, _ptr(stats), _ptr(dx),
+                               _ptr(grads), _ptr(ws), nb, _stream(x.device)), "bn_backward")
+    else:
+        _check(lib.bn_act_backward(_ptr(dy), _ptr(x), _dt(x), N, C, HW, _ptr(stats), _ptr(beta),
+                                   _act(act), slope, _ptr(dx), _ptr(grads), _ptr(ws), nb,
+                                   _stream(x.device)), "bn_act_backward")
     return dx, grads
+
+
+def bn_forward_infer(x, running_mean, running_var, gamma=None, beta=None, eps: float = 1e-5, *,
+                     act="none", slope: float = 0.01, y=None):
+    """BatchNorm2d inference from the running statistics (+ activation).  Returns y."""
+    _dev_tensor(x, "x")
+    N, C, HW = _nchw(x)
+    f32 = torch.float32
+    for t, n in ((gamma, "gamma"), (beta, "beta"), (running_mean, "running_mean"),
+                 (running_var, "running_var")):
+        _dev_tensor(t, n, f32, C)
+    y = torch.empty_like(x) if y is None else _dev_tensor(y, "y", x.dtype, x.numel())
+    _check(lib.bn_forward_infer(_ptr(x), _ptr(y), _dt(x), N, C, HW, _ptr(gamma), _ptr(beta),
+                                _ptr(running_mean), _ptr(running_var), eps, _act(act), slope,
+                                _stream(x.device)), "bn_forward_infer")
+    return y
 
 
 # ---- LayerNorm / RMSNorm ---------------------------------------------------------------

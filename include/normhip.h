@@ -10,6 +10,10 @@
  *                       _bn_apply_ew commit.
  *   bn_backward         BatchNorm2d training backward.  Same PR, "Backward
  *                       finalize" section and the bn_backward_finalize commit.
+ *   bn_act_forward_train, bn_act_backward, bn_forward_infer
+ *                       BatchNorm2d fused with ReLU/LeakyReLU (the same PR's
+ *                       "Follow-ups") and inference through the shared apply
+ *                       (its _bn_apply_ew commit).
  *   layernorm_backward  LayerNorm backward over the last dimension with saved
  *                       mean/rstd.  NVIDIA/Fuser issue #1473, "Why is
  *                       LayerNorm Backward Segmenting?", the layer_norm
@@ -132,6 +136,75 @@ nh_status bn_backward(const void *dy, const void *x, nh_dtype io,
                       void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * BatchNorm2d + activation, and BatchNorm2d inference.
+ *
+ * The Aether-ML PR #18 description lists fusing ReLU/LeakyReLU into
+ * BatchNorm as its follow-up ("Follow-ups"), and its _bn_apply_ew commit
+ * shares the centred apply between training and inference.  With
+ * z = (x - mean)*scale + beta (the training forward above):
+ *   act NH_ACT_NONE        y = z
+ *   act NH_ACT_RELU        y = z > 0 ? z : 0
+ *   act NH_ACT_LEAKY_RELU  y = z > 0 ? z : slope*z
+ * and the backward is bn_backward applied to dz = dy * act'(z), with act'(z)
+ * = 1 for z > 0, else 0 (ReLU) or slope (LeakyReLU): the derivative at 0 is
+ * taken from the left.  The backward recomputes z from x, stats and beta
+ * (no read of y), in the same fp32 steps as the forward, so with the forward's
+ * stats it sees exactly the forward's signs of z.
+ * ---------------------------------------------------------------------- */
+
+typedef enum {
+    NH_ACT_NONE = 0,
+    NH_ACT_RELU = 1,
+    NH_ACT_LEAKY_RELU = 2
+} nh_act;
+
+/*
+ * Training forward with activation: bn_forward_train, then y = act(z) in the
+ * same elementwise pass.  Arguments as bn_forward_train, plus
+ *   act           an nh_act value (else NH_ERR_ARG)
+ *   slope         LeakyReLU negative slope, finite (read for
+ *                 NH_ACT_LEAKY_RELU only)
+ * The workspace is bn_forward_train_workspace's.  stats hold the statistics
+ * of x (z's, not y's).
+ */
+nh_status bn_act_forward_train(const void *x, void *y, nh_dtype io,
+                               int64_t N, int64_t C, int64_t HW,
+                               const float *gamma, const float *beta,
+                               float *running_mean, float *running_var,
+                               float momentum, float eps, nh_act act, float slope,
+                               float *stats, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Training backward through the activation: dz = dy*act'(z) inside both
+ * passes, then bn_backward's (dgamma, dbeta, k1, k2) and dx for dz.
+ *   dy, x, stats, dx, grads, ws   as bn_backward (x must be the forward's
+ *                 input, not its output: an in-place forward's x is gone)
+ *   beta          fp32 [C] as given to the forward, or NULL (beta = 0)
+ *   act, slope    as given to the forward
+ * grads row 1 (dbeta) is sum dz; row 0 (dgamma) is inv_std * sum dz*(x - mean).
+ */
+nh_status bn_act_backward(const void *dy, const void *x, nh_dtype io,
+                          int64_t N, int64_t C, int64_t HW,
+                          const float *stats, const float *beta, nh_act act, float slope,
+                          void *dx, float *grads, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Inference (evaluation mode): the training apply with the running statistics
+ * in place of the batch statistics,
+ *   y = act((x - running_mean) * gamma/sqrt(running_var + eps) + beta),
+ * one elementwise pass, no workspace, nothing but y written.
+ *   x, y          [N, C, HW] of dtype io (y may equal x)
+ *   gamma, beta   fp32 [C], or NULL (1 / 0)
+ *   running_mean, running_var   fp32 [C], required
+ *   eps           finite, >= 0; act, slope as bn_act_forward_train
+ */
+nh_status bn_forward_infer(const void *x, void *y, nh_dtype io,
+                           int64_t N, int64_t C, int64_t HW,
+                           const float *gamma, const float *beta,
+                           const float *running_mean, const float *running_var,
+                           float eps, nh_act act, float slope, void *stream);
+
+/* ------------------------------------------------------------------------
  * LayerNorm / RMSNorm backward over the last dimension of [rows, cols].
  * dweight/dbias are split over rows into per-block partials in the
  * workspace and summed by a finalize kernel in a fixed order.
@@ -234,7 +307,8 @@ typedef enum {
     NH_K_CALIB = 10,          /* calibration kernels below */
     NH_K_LN_FWD = 11,         /* LayerNorm forward row pass */
     NH_K_RMS_FWD = 12,        /* RMSNorm forward row pass */
-    NH_K_COUNT = 13
+    NH_K_BN_INFER = 13,       /* BatchNorm inference apply */
+    NH_K_COUNT = 14
 } nh_kernel;
 
 /* Static name of a kernel id; "" for an unknown id. */

@@ -67,3 +67,40 @@ def check(name, got, want, dtype, tol=None, report=True):
         sys.stdout.flush()
     assert e <= tol, f"{name}: normwise relative error {e:.3e} > {tol:.0e}"
     return e
+
+
+def _next_toward(v: np.ndarray, up: np.ndarray, dtype) -> np.ndarray:
+    """The neighbouring representable value of each v (fp32 values of dtype
+    storage), upwards where `up`, else downwards."""
+    v32 = np.asarray(v, np.float32)
+    if dtype == wl.F32:
+        return np.nextafter(v32, np.where(up, np.float32(np.inf), np.float32(-np.inf))).astype(np.float32)
+    bits = wl.f32_to_bf16_bits(v32).astype(np.int32)
+    mag_up = up == (v32 > 0)
+    nb = np.where(v32 == 0, np.where(up, 0x0001, 0x8001),
+                  np.where(mag_up, bits + 1, bits - 1))
+    return wl.bf16_bits_to_f32(nb.astype(np.uint16))
+
+
+def clear_of_kink(oracle_mod, t, gamma, beta, eps, delta, max_iter=8):
+    """Moves the few elements of x whose BatchNorm output z lies within
+    `delta` of 0 (the kink of ReLU/LeakyReLU) away from it, in x's storage
+    type, until every |z| >= delta as the fp64 oracle computes it.  There the
+    fp32 kernel and the fp64 oracle take the same activation branch for
+    every element, since the kernel's error in z is far below delta."""
+    x32 = (t.store.astype(np.float32) if t.dtype == wl.F32
+           else wl.bf16_bits_to_f32(t.store)).copy()
+    for _ in range(max_iter):
+        z, stats, _, _ = oracle_mod.bn_forward_train(x32.astype(np.float64), gamma, beta, eps=eps)
+        near = np.abs(z) < delta
+        if not near.any():
+            return wl.make_tensor(x32.astype(np.float64), t.dtype)
+        scale = np.broadcast_to(stats[3].reshape((1, -1) + (1,) * (x32.ndim - 2)), x32.shape)
+        up = (z >= 0) == (scale >= 0)             # the direction of x that moves z away from 0
+        step = np.where(up, 1.0, -1.0) * 3.0 * delta / np.maximum(np.abs(scale), 1e-30)
+        cand = wl.make_tensor(x32.astype(np.float64) + step, t.dtype)
+        c32 = cand.store.astype(np.float32) if t.dtype == wl.F32 else wl.bf16_bits_to_f32(cand.store)
+        stuck = c32 == x32
+        c32 = np.where(stuck, _next_toward(x32, up, t.dtype), c32)
+        x32 = np.where(near, c32, x32)
+    raise AssertionError("could not move x clear of the activation kink")

@@ -43,8 +43,8 @@ def test_status_and_kernel_names():
         "NH_OK", "NH_ERR_NULL", "NH_ERR_SHAPE", "NH_ERR_DTYPE", "NH_ERR_WORKSPACE",
         "NH_ERR_HIP", "NH_ERR_ARG"]
     assert nh.status_string(99) == "NH_ERR_UNKNOWN"
-    assert [nh.lib.nh_kernel_name(i).decode() for i in range(13)] == nh.KERNELS
-    assert nh.lib.nh_kernel_name(13).decode() == ""
+    assert [nh.lib.nh_kernel_name(i).decode() for i in range(14)] == nh.KERNELS
+    assert nh.lib.nh_kernel_name(14).decode() == ""
 
 
 def bn_fwd(x=FAKE, y=FAKE, io=0, N=2, C=3, HW=4, rm=NULL, rv=NULL, eps=1e-5, mom=0.1,
@@ -83,6 +83,45 @@ def test_bn_backward_validation():
     assert f(FAKE, FAKE, 0, 2, 3, 4, NULL, FAKE, FAKE, FAKE, 1 << 20, NULL) == NH_ERR_NULL
     assert f(FAKE, FAKE, 0, 2, 3, 4, FAKE, FAKE, NULL, FAKE, 1 << 20, NULL) == NH_ERR_NULL
     assert f(NULL, NULL, 0, 0, 3, 4, NULL, NULL, NULL, NULL, 0, NULL) == NH_OK
+
+
+def test_bn_act_and_infer_validation():
+    fa = nh.lib.bn_act_forward_train
+    # x, y, io, N, C, HW, gamma, beta, rm, rv, momentum, eps, act, slope, stats, ws, ws_bytes, stream
+    assert fa(FAKE, FAKE, 0, 2, 3, 4, NULL, NULL, NULL, NULL, 0.1, 1e-5, 3, 0.0, FAKE, FAKE, 1 << 20,
+              NULL) == NH_ERR_ARG
+    assert "act" in nh.last_error()
+    assert fa(FAKE, FAKE, 0, 2, 3, 4, NULL, NULL, NULL, NULL, 0.1, 1e-5, -1, 0.0, FAKE, FAKE, 1 << 20,
+              NULL) == NH_ERR_ARG
+    assert fa(FAKE, FAKE, 0, 2, 3, 4, NULL, NULL, NULL, NULL, 0.1, 1e-5, 2, float("nan"), FAKE, FAKE,
+              1 << 20, NULL) == NH_ERR_ARG
+    assert "slope" in nh.last_error()
+    assert fa(FAKE, FAKE, 5, 2, 3, 4, NULL, NULL, NULL, NULL, 0.1, 1e-5, 1, 0.0, FAKE, FAKE, 1 << 20,
+              NULL) == NH_ERR_DTYPE
+    assert fa(NULL, FAKE, 0, 2, 3, 4, NULL, NULL, NULL, NULL, 0.1, 1e-5, 1, 0.0, FAKE, FAKE, 1 << 20,
+              NULL) == NH_ERR_NULL
+    assert fa(NULL, NULL, 0, 0, 3, 4, NULL, NULL, NULL, NULL, 0.1, 1e-5, 1, 0.0, NULL, NULL, 0,
+              NULL) == NH_OK
+    fb = nh.lib.bn_act_backward
+    # dy, x, io, N, C, HW, stats, beta, act, slope, dx, grads, ws, ws_bytes, stream
+    assert fb(FAKE, FAKE, 0, 2, 3, 4, FAKE, NULL, 9, 0.0, FAKE, FAKE, FAKE, 1 << 20, NULL) == NH_ERR_ARG
+    assert fb(FAKE, FAKE, 0, 2, 3, 4, FAKE, NULL, 2, float("inf"), FAKE, FAKE, FAKE, 1 << 20,
+              NULL) == NH_ERR_ARG
+    assert fb(FAKE, FAKE, 0, 2, 3, 4, NULL, NULL, 1, 0.0, FAKE, FAKE, FAKE, 1 << 20, NULL) == NH_ERR_NULL
+    assert fb(FAKE, FAKE, 0, -2, 3, 4, FAKE, NULL, 1, 0.0, FAKE, FAKE, FAKE, 1 << 20,
+              NULL) == NH_ERR_SHAPE
+    # slope is not read for ReLU: a NaN there is accepted by validation (the
+    # call then fails on the missing device, never on the argument)
+    fi = nh.lib.bn_forward_infer
+    # x, y, io, N, C, HW, gamma, beta, rm, rv, eps, act, slope, stream
+    assert fi(FAKE, FAKE, 0, 2, 3, 4, NULL, NULL, NULL, FAKE, 1e-5, 0, 0.0, NULL) == NH_ERR_NULL
+    assert "running_mean" in nh.last_error()
+    assert fi(FAKE, FAKE, 0, 2, 3, 4, NULL, NULL, FAKE, NULL, 1e-5, 0, 0.0, NULL) == NH_ERR_NULL
+    assert fi(FAKE, FAKE, 0, 2, 3, 4, NULL, NULL, FAKE, FAKE, -1.0, 0, 0.0, NULL) == NH_ERR_ARG
+    assert fi(FAKE, FAKE, 0, 2, 3, 4, NULL, NULL, FAKE, FAKE, 1e-5, 4, 0.0, NULL) == NH_ERR_ARG
+    assert fi(FAKE, FAKE, 2, 2, 3, 4, NULL, NULL, FAKE, FAKE, 1e-5, 0, 0.0, NULL) == NH_ERR_DTYPE
+    assert fi(FAKE, FAKE, 0, 2, 3, 1 << 31, NULL, NULL, FAKE, FAKE, 1e-5, 0, 0.0, NULL) == NH_ERR_SHAPE
+    assert fi(NULL, NULL, 0, 2, 0, 4, NULL, NULL, NULL, NULL, 1e-5, 0, 0.0, NULL) == NH_OK
 
 
 def test_rows_validation():

@@ -1,0 +1,248 @@
+"""GPU parity of BatchNorm2d + ReLU/LeakyReLU (bn_act_forward_train,
+bn_act_backward) and of BatchNorm2d inference (bn_forward_infer) against the
+CPU fp64 oracle, at the tolerances of the plain BatchNorm tests (normwise
+<= 2e-5 fp32, <= 8e-3 bf16).
+
+The activation's branch (z > 0) is an integer decision taken from floating
+point: the kernel takes it in fp32, the oracle in fp64.  Parity cases for the
+backward therefore move the few elements with |z| < delta clear of the kink
+first (tests/helpers.clear_of_kink), so both sides take the same branch
+everywhere.  Without that margin, the backward is checked bit for bit against
+the plain BatchNorm backward of dz = dy * act'(z), with the mask read from
+the GPU forward's own output: the forward and backward see the same signs of
+z on every element, including those next to the kink.
+"""
+import numpy as np
+import pytest
+
+from bwd_bn_stats_amd import workloads as wl
+
+from helpers import check, clear_of_kink, dev, host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+ACTS = [("relu", 0.0), ("leaky_relu", 0.01), ("leaky_relu", 0.2)]
+
+
+@pytest.fixture(scope="module")
+def nh():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from bwd_bn_stats_amd import normhip
+    return normhip
+
+
+def _delta(io):
+    return 1e-3 if io == wl.F32 else 1e-2
+
+
+def _run_case(nh, oracle_mod, c, act, slope, *, affine=True, running=True, need_dx=True,
+              in_place=False):
+    x_t = clear_of_kink(oracle_mod, c.x, c.gamma if affine else np.ones(c.C),
+                        c.beta if affine else np.zeros(c.C), c.eps, _delta(c.io))
+    gamma = c.gamma.astype(np.float64) if affine else None
+    beta = c.beta.astype(np.float64) if affine else None
+    print(f"[bn act parity] N={c.N} C={c.C} HW={c.hw} io={c.io} act={act} slope={slope} "
+          f"affine={affine} running={running} need_dx={need_dx} in_place={in_place}", flush=True)
+    wy, wstats, wrm, wrv = oracle_mod.bn_act_forward_train(
+        x_t.value, gamma if affine else np.ones(c.C), beta if affine else np.zeros(c.C), act, slope,
+        eps=c.eps, momentum=c.momentum, running_mean=c.running_mean if running else None,
+        running_var=c.running_var if running else None)
+    wdx, wgrads = oracle_mod.bn_act_backward(x_t.value, c.dy.value,
+                                             gamma if affine else np.ones(c.C),
+                                             beta if affine else np.zeros(c.C), act, slope, eps=c.eps)
+    x, dy = dev(x_t), dev(c.dy)
+    g = dev(c.gamma) if affine else None
+    b = dev(c.beta) if affine else None
+    rm = dev(c.running_mean) if running else None
+    rv = dev(c.running_var) if running else None
+    x_keep = x.clone() if in_place else x
+    y, stats = nh.bn_forward_train(x, g, b, rm, rv, c.momentum, c.eps, act=act, slope=slope,
+                                   y=x if in_place else None)
+    dx, grads = nh.bn_backward(dy, x_keep, stats, beta=b, act=act, slope=slope, need_dx=need_dx)
+    torch.cuda.synchronize()
+    check("y", host(y), wy, c.io)
+    for i, n in enumerate(("mean", "var", "inv_std", "scale")):
+        check(f"stats.{n}", host(stats)[i], wstats[i], wl.F32)
+    if running:
+        check("running_mean", host(rm), wrm, wl.F32)
+        check("running_var", host(rv), wrv, wl.F32)
+    if need_dx:
+        check("dx", host(dx), wdx, c.io)
+    for i, n in enumerate(("dgamma", "dbeta", "k1", "k2")):
+        check(f"grads.{n}", host(grads)[i], wgrads[i], wl.F32)
+
+
+CASES = {
+    "ragged_3x37x41x40_f32": lambda: wl.bn_case(3, 37, 41, 40, wl.F32, seed=1001, x_mean=5.0,
+                                                 x_std=0.5, beta_std=1.0),
+    "cifar_256x32x32x32_f32": lambda: wl.bn_cifar(wl.F32),
+    "cifar_256x32x32x32_bf16": lambda: wl.bn_cifar(wl.BF16),
+    "odd_plane_2x5x7x3_f32": lambda: wl.bn_case(2, 5, 7, 3, wl.F32, seed=131, x_mean=1.0, x_std=2.0,
+                                                beta_std=1.0),
+    "odd_plane_3x6x5x5_bf16": lambda: wl.bn_case(3, 6, 5, 5, wl.BF16, seed=132, x_mean=-2.0,
+                                                 x_std=0.7, beta_std=1.0),
+    "many_channels_2x3000x2x2_f32": lambda: wl.bn_case(2, 3000, 2, 2, wl.F32, seed=133, beta_std=1.0),
+    "one_channel_64x1x128x128_f32": lambda: wl.bn_case(64, 1, 128, 128, wl.F32, seed=134, x_mean=3.0,
+                                                       beta_std=1.0),
+}
+
+
+@pytest.mark.parametrize("act,slope", ACTS)
+@pytest.mark.parametrize("name", list(CASES))
+def test_bn_act_parity(nh, oracle_mod, name, act, slope):
+    _run_case(nh, oracle_mod, CASES[name](), act, slope)
+
+
+def test_bn_act_resnet_bf16(nh, oracle_mod):
+    _run_case(nh, oracle_mod, wl.bn_resnet(), "relu", 0.0)
+
+
+def test_bn_act_options(nh, oracle_mod):
+    c = wl.bn_case(4, 9, 6, 8, wl.F32, seed=141, x_mean=0.5, beta_std=0.5)
+    _run_case(nh, oracle_mod, c, "relu", 0.0, affine=False, running=False)
+    _run_case(nh, oracle_mod, c, "leaky_relu", 0.1, need_dx=False)
+    _run_case(nh, oracle_mod, c, "leaky_relu", 0.1, in_place=True)
+    cb = wl.bn_case(4, 9, 6, 8, wl.BF16, seed=142, x_mean=0.5, beta_std=0.5)
+    _run_case(nh, oracle_mod, cb, "relu", 0.0, in_place=True)
+
+
+@pytest.mark.parametrize("grid_y", [1, 3, 1000])
+def test_bn_act_forced_grid(nh, oracle_mod, grid_y):
+    c = wl.bn_case(8, 5, 33, 31, wl.F32, seed=143, x_mean=-1.0, x_std=1.5, beta_std=1.0)
+    nh.plan_override("bn_grid_y", grid_y)
+    try:
+        _run_case(nh, oracle_mod, c, "leaky_relu", 0.2)
+    finally:
+        nh.plan_override("bn_grid_y", 0)
+
+
+def test_bn_act_negative_slope(nh, oracle_mod):
+    """A negative LeakyReLU slope (z < 0 maps to a positive y): the backward
+    still follows the sign of z, which it recomputes from x."""
+    c = wl.bn_case(4, 7, 9, 9, wl.F32, seed=144, beta_std=1.0)
+    _run_case(nh, oracle_mod, c, "leaky_relu", -0.5)
+
+
+@pytest.mark.parametrize("io,act,slope", [(wl.F32, "relu", 0.0), (wl.F32, "leaky_relu", 0.2),
+                                          (wl.BF16, "relu", 0.0)])
+def test_bn_act_mask_matches_forward(nh, io, act, slope):
+    """No margin: every element, the ones next to z = 0 included.  The fused
+    backward equals the plain backward of dz = where(y > 0, dy, slope*dy)
+    (the mask from the GPU forward's y, dz formed in fp32 -- exact for ReLU
+    in bf16) bit for bit."""
+    c = wl.bn_case(64, 16, 32, 32, io, seed=145, x_mean=0.0, x_std=1.0, beta_std=0.05)
+    x, dy, g, b = dev(c.x), dev(c.dy), dev(c.gamma), dev(c.beta)
+    print(f"[bn act mask] io={io} act={act} slope={slope}", flush=True)
+    y, stats = nh.bn_forward_train(x, g, b, None, None, c.momentum, c.eps, act=act, slope=slope)
+    dx, grads = nh.bn_backward(dy, x, stats, beta=b, act=act, slope=slope)
+    pos = y.float() > 0
+    if act == "relu":
+        dz = torch.where(pos, dy, torch.zeros_like(dy))
+    else:
+        dz = torch.where(pos, dy.float(), dy.float() * slope).to(dy.dtype)
+    dx0, grads0 = nh.bn_backward(dz, x, stats)
+    torch.cuda.synchronize()
+    near = int(((y.float().abs() < 1e-3) & ~pos).sum())
+    print(f"  elements next to the kink (|y| < 1e-3, not positive): {near}", flush=True)
+    iv = torch.int16 if io == wl.BF16 else torch.int32
+    assert torch.equal(dx.view(iv), dx0.view(iv))
+    assert torch.equal(grads, grads0)
+
+
+def test_bn_act_separate_finalize_bit_identical(nh):
+    c = wl.bn_case(16, 12, 20, 20, wl.F32, seed=146, beta_std=1.0)
+    x, dy, g, b = dev(c.x), dev(c.dy), dev(c.gamma), dev(c.beta)
+    outs = []
+    for sep in (0, 1):
+        nh.plan_override("bn_finalize_kernels", sep)
+        try:
+            y, stats = nh.bn_forward_train(x, g, b, None, None, c.momentum, c.eps, act="leaky_relu",
+                                           slope=0.1)
+            dx, grads = nh.bn_backward(dy, x, stats, beta=b, act="leaky_relu", slope=0.1)
+        finally:
+            nh.plan_override("bn_finalize_kernels", 0)
+        outs.append((y, stats, dx, grads))
+    torch.cuda.synchronize()
+    for u, v in zip(*outs):
+        assert torch.equal(u.view(torch.int32), v.view(torch.int32))
+
+
+def test_bn_act_none_is_plain(nh):
+    """act = "none" through the activation entry points is the plain path."""
+    c = wl.bn_case(8, 6, 10, 12, wl.F32, seed=147)
+    x, dy, g, b = dev(c.x), dev(c.dy), dev(c.gamma), dev(c.beta)
+    y0, s0 = nh.bn_forward_train(x, g, b)
+    dx0, g0 = nh.bn_backward(dy, x, s0)
+    ws = torch.empty(nh.bn_forward_train_workspace(c.N, c.C, c.hw), dtype=torch.uint8, device="cuda")
+    y1 = torch.empty_like(x)
+    s1 = torch.empty_like(s0)
+    rc = nh.lib.bn_act_forward_train(x.data_ptr(), y1.data_ptr(), 0, c.N, c.C, c.hw, g.data_ptr(),
+                                     b.data_ptr(), None, None, 0.1, c.eps, 0, 0.0, s1.data_ptr(),
+                                     ws.data_ptr(), ws.numel(), None)
+    assert rc == 0
+    dx1 = torch.empty_like(x)
+    g1 = torch.empty_like(g0)
+    rc = nh.lib.bn_act_backward(dy.data_ptr(), x.data_ptr(), 0, c.N, c.C, c.hw, s1.data_ptr(),
+                                b.data_ptr(), 0, 0.0, dx1.data_ptr(), g1.data_ptr(), ws.data_ptr(),
+                                ws.numel(), None)
+    assert rc == 0
+    torch.cuda.synchronize()
+    for u, v in ((y0, y1), (s0, s1), (dx0, dx1), (g0, g1)):
+        assert torch.equal(u.view(torch.int32), v.view(torch.int32))
+
+
+# ---- inference -------------------------------------------------------------------------
+INFER_CASES = [
+    (wl.F32, "none", 0.0, (3, 37, 41, 40)),
+    (wl.F32, "relu", 0.0, (256, 32, 32, 32)),
+    (wl.BF16, "relu", 0.0, (256, 32, 32, 32)),
+    (wl.BF16, "leaky_relu", 0.1, (64, 256, 56, 56)),
+    (wl.F32, "leaky_relu", 0.01, (2, 5, 7, 3)),
+    (wl.BF16, "none", 0.0, (3, 6, 5, 5)),
+    (wl.F32, "relu", 0.0, (2, 3000, 2, 2)),
+]
+
+
+@pytest.mark.parametrize("io,act,slope,shape", INFER_CASES)
+def test_bn_infer_parity(nh, oracle_mod, io, act, slope, shape):
+    c = wl.bn_case(*shape, io, seed=150 + shape[1], x_mean=1.0, x_std=2.0, beta_std=0.5)
+    rng = np.random.Generator(np.random.PCG64(151))
+    rm = wl.round_f32(rng.normal(1.0, 0.5, size=c.C))
+    rv = wl.round_f32(rng.uniform(0.5, 8.0, size=c.C))
+    print(f"[bn infer parity] shape={shape} io={io} act={act} slope={slope}", flush=True)
+    want = oracle_mod.bn_infer(c.x.value, c.gamma, c.beta, rm, rv, act, slope, eps=c.eps)
+    x = dev(c.x)
+    rmd, rvd = dev(rm), dev(rv)
+    y = nh.bn_forward_infer(x, rmd, rvd, dev(c.gamma), dev(c.beta), c.eps, act=act, slope=slope)
+    torch.cuda.synchronize()
+    check("y", host(y), want, io)
+    # nothing else written
+    assert torch.equal(rmd.cpu(), torch.from_numpy(rm)) and torch.equal(rvd.cpu(), torch.from_numpy(rv))
+
+
+def test_bn_infer_affine_off_and_in_place(nh, oracle_mod):
+    c = wl.bn_case(4, 8, 12, 12, wl.F32, seed=152, x_mean=-3.0, x_std=0.5)
+    rm = wl.round_f32(np.linspace(-3.5, -2.5, 8))
+    rv = wl.round_f32(np.linspace(0.1, 0.4, 8))
+    want = oracle_mod.bn_infer(c.x.value, None, None, rm, rv, "relu", 0.0, eps=c.eps)
+    x = dev(c.x)
+    y = nh.bn_forward_infer(x, dev(rm), dev(rv), None, None, c.eps, act="relu", y=x)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == x.data_ptr()
+    check("y", host(y), want, wl.F32)
+
+
+def test_bn_infer_with_batch_stats_matches_training(nh):
+    """Inference fed the batch's own (mean, biased var) reproduces the
+    training forward's output, within the fp32 tolerance (the two paths round
+    inv_std from different fp32 inputs)."""
+    c = wl.bn_case(16, 24, 14, 14, wl.F32, seed=153, x_mean=2.0, beta_std=1.0)
+    x, g, b = dev(c.x), dev(c.gamma), dev(c.beta)
+    yt, stats = nh.bn_forward_train(x, g, b, act="leaky_relu", slope=0.2)
+    yi = nh.bn_forward_infer(x, stats[0].contiguous(), stats[1].contiguous(), g, b, c.eps,
+                             act="leaky_relu", slope=0.2)
+    torch.cuda.synchronize()
+    check("y", host(yi), host(yt), wl.F32)
