@@ -16,6 +16,9 @@ Workloads (shapes and distributions follow the pages' benchmark settings):
 * ``rms_bwd``    -- RMSNorm backward (2048,8192), bf16 or fp32 (nvFuser
   issue 3629, the rmsnorm_bwd benchmark size).
 * ``bn_resnet``  -- BatchNorm2d NCHW (64,256,56,56) bf16 I/O, x ~ N(3, 1).
+* ``bda_bwd``    -- bias + dropout + add + LayerNorm backward (16,512,1600):
+  the LayerNorm inputs of ``ln_bwd`` plus an fp32 incoming gradient and a
+  dropout keep-mask (nvFuser issue 1473, its one-kernel fusion example).
 """
 from __future__ import annotations
 
@@ -136,7 +139,31 @@ def rows_case(rows, cols, *, x_t, dy_t, w_t, seed, with_bias=False,
     return RowsCase(name, rows, cols, x, dy, w, b)
 
 
-# ---- the five workloads ---------------------------------------------------
+@dataclass
+class BdaCase:
+    """Inputs of the bias + dropout + add + LayerNorm backward: a LayerNorm
+    case plus the gradient reaching h from elsewhere (fp32), the dropout
+    keep-mask (uint8 0/1, drawn here: it is random state of the forward) and
+    the dropout scale 1/(1 - p) rounded to fp32."""
+    ln: RowsCase
+    dresidual: np.ndarray   # fp32 [rows, cols]
+    mask: np.ndarray        # uint8 [rows, cols]
+    scale: float
+    p_drop: float
+
+
+def bda_case(rows, cols, *, x_t=F32, dy_t=BF16, w_t=BF16, seed, p_drop=0.1,
+             name="bda") -> BdaCase:
+    """rows_case inputs, then dresidual ~ N(0, 1) and mask ~ Bernoulli(1 - p_drop)."""
+    ln = rows_case(rows, cols, x_t=x_t, dy_t=dy_t, w_t=w_t, seed=seed, name=name)
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    dres = round_f32(rng.normal(0.0, 1.0, size=(rows, cols)))
+    mask = (rng.random(size=(rows, cols)) >= p_drop).astype(np.uint8)
+    scale = float(np.float32(1.0 / (1.0 - p_drop)))
+    return BdaCase(ln, dres, mask, scale, p_drop)
+
+
+# ---- the workloads ----------------------------------------------------------
 
 def bn_ragged(seed=1001) -> BNCase:
     return bn_case(3, 37, 41, 40, F32, seed=seed, x_mean=5.0, x_std=0.5,
@@ -161,3 +188,8 @@ def rms_bwd(dtype=BF16, seed=1004, rows=2048, cols=8192) -> RowsCase:
 def bn_resnet(seed=1005) -> BNCase:
     return bn_case(64, 256, 56, 56, BF16, seed=seed, x_mean=3.0, x_std=1.0,
                    beta_std=0.1, name="bn_resnet_64x256x56x56_bf16")
+
+
+def bda_bwd(seed=1006, rows=16 * 512, cols=1600) -> BdaCase:
+    return bda_case(rows, cols, x_t=F32, dy_t=BF16, w_t=BF16, seed=seed, p_drop=0.1,
+                    name=f"bda_bwd_{rows}x{cols}")

@@ -49,11 +49,14 @@ def _load():
         lib.oracle_layernorm_forward.argtypes = [i64, i64, p, p, p, dbl, p, p, p]
         lib.oracle_rmsnorm_forward.argtypes = [i64, i64, p, p, dbl, p, p]
         lib.oracle_layernorm_backward.argtypes = [i64, i64, p, p, p, p, p, p, p, p]
+        lib.oracle_bda_layernorm_backward.argtypes = [i64, i64, p, p, p, p, p, p, p, dbl, p, p, p,
+                                                       p, p]
         lib.oracle_rmsnorm_rms.argtypes = [i64, i64, p, dbl, p]
         lib.oracle_rmsnorm_backward.argtypes = [i64, i64, p, p, p, p, dbl, p, p]
         for f in ("oracle_bn_forward_train", "oracle_bn_backward", "oracle_bn_act_forward_train",
                   "oracle_bn_act_backward", "oracle_bn_infer", "oracle_layernorm_stats",
-                  "oracle_layernorm_forward", "oracle_layernorm_backward", "oracle_rmsnorm_rms",
+                  "oracle_layernorm_forward", "oracle_layernorm_backward",
+                  "oracle_bda_layernorm_backward", "oracle_rmsnorm_rms",
                   "oracle_rmsnorm_forward", "oracle_rmsnorm_backward"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
@@ -194,6 +197,26 @@ def layernorm_backward(x, dy, mean, rstd, w=None):
                                              _ptr(rstd), _ptr(w), _ptr(dx), _ptr(dw), _ptr(db)),
            "oracle_layernorm_backward")
     return dx, dw, db
+
+
+def bda_layernorm_backward(x, dy, mean, rstd, w=None, dresidual=None, mask=None, scale=1.0):
+    """Backward of bias + dropout + add + LayerNorm.  mask: 0/1 array (any
+    integer or bool dtype) or None.  Returns (dh, da, dweight, dbias, dbias_in)."""
+    x, dy, mean, rstd = _d(x), _d(dy), _d(mean), _d(rstd)
+    w = None if w is None else _d(w)
+    dres = None if dresidual is None else _d(dresidual)
+    m = None if mask is None else np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8)
+    rows, cols = x.shape
+    dh = np.empty_like(x)
+    da = np.empty_like(x)
+    dw = np.empty(cols, np.float64)
+    db = np.empty(cols, np.float64)
+    dbi = np.empty(cols, np.float64)
+    _check(_load().oracle_bda_layernorm_backward(rows, cols, _ptr(x), _ptr(dy), _ptr(mean),
+                                                 _ptr(rstd), _ptr(w), _ptr(dres), _ptr(m), scale,
+                                                 _ptr(dh), _ptr(da), _ptr(dw), _ptr(db), _ptr(dbi)),
+           "oracle_bda_layernorm_backward")
+    return dh, da, dw, db, dbi
 
 
 def rmsnorm_rms(x, *, eps=1e-5):

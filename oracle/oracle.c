@@ -399,6 +399,54 @@ int oracle_layernorm_backward(int64_t rows, int64_t cols,
 }
 
 /*
+ * Backward of bias + dropout + add + LayerNorm: NVIDIA/Fuser issue #1473,
+ * the one-kernel fusion of its first example (nvfuser_fusion_id9).  The
+ * forward it differentiates is h = residual + dropout(a + bias), y =
+ * LayerNorm(h) with the saved mean/rstd of h; dropout multiplies by a 0/1
+ * mask and by `scale` (the fusion's scalar input).  With dx_ln the LayerNorm
+ * backward above (the same steps: g = dy*w, dvar, dmean, the three-term
+ * input gradient):
+ *   dh        = dresidual + dx_ln        (gradient at h; dresidual is the
+ *                                         gradient reaching h from its other
+ *                                         consumers, NULL = 0)
+ *   da        = dh * scale * mask         (gradient of a, and of bias per row)
+ *   dbias_in  = sum over rows of da
+ *   dweight, dbias = the LayerNorm parameter gradients.
+ * mask holds 0/1 bytes (NULL = all ones).
+ */
+int oracle_bda_layernorm_backward(int64_t rows, int64_t cols, const double *x, const double *dy,
+                                  const double *mean, const double *rstd, const double *w,
+                                  const double *dresidual, const uint8_t *mask, double scale,
+                                  double *dh, double *da, double *dweight, double *dbias,
+                                  double *dbias_in)
+{
+    if (rows < 0 || cols <= 0) return -1;
+    const size_t n = (size_t)rows * (size_t)cols;
+    double *dx = (double *)malloc((n ? n : 1) * sizeof(double));
+    ksum_t *sa = (ksum_t *)malloc((size_t)cols * sizeof(ksum_t));
+    if (!dx || !sa) { free(dx); free(sa); return -1; }
+    int rc = oracle_layernorm_backward(rows, cols, x, dy, mean, rstd, w, dx, dweight, dbias);
+    if (rc == 0) {
+        for (int64_t j = 0; j < cols; ++j) ks_init(&sa[j]);
+        for (int64_t r = 0; r < rows; ++r)
+            for (int64_t j = 0; j < cols; ++j) {
+                const size_t i = (size_t)r * (size_t)cols + (size_t)j;
+                const double h = (dresidual ? dresidual[i] : 0.0) + dx[i];
+                const double m = mask ? (mask[i] ? 1.0 : 0.0) : 1.0;
+                const double a = h * scale * m;
+                if (dh) dh[i] = h;
+                if (da) da[i] = a;
+                ks_add(&sa[j], a);
+            }
+        if (dbias_in)
+            for (int64_t j = 0; j < cols; ++j) dbias_in[j] = ks_value(&sa[j]);
+    }
+    free(dx);
+    free(sa);
+    return rc;
+}
+
+/*
  * RMSNorm forward statistic, [RM] rmsnorm_prims:
  *   rms_r = sqrt(sum_j x^2 / H + eps)
  */

@@ -51,6 +51,11 @@ MUTANTS = [
     ("infer_drops_mean", "y[i] = act_value(act, slope, g * (x[i] - running_mean[c]) / sd + b);",
      "y[i] = act_value(act, slope, g * x[i] / sd + b);"),
     ("infer_no_eps", "const double sd = sqrt(running_var[c] + eps);", "const double sd = sqrt(running_var[c]);"),
+    ("bda_drops_dresidual", "const double h = (dresidual ? dresidual[i] : 0.0) + dx[i];",
+     "const double h = dx[i];"),
+    ("bda_no_scale", "const double a = h * scale * m;", "const double a = h * m;"),
+    ("bda_mask_ignored", "const double m = mask ? (mask[i] ? 1.0 : 0.0) : 1.0;", "const double m = 1.0;"),
+    ("bda_dbias_sums_dh", "ks_add(&sa[j], a);", "ks_add(&sa[j], h);"),
     ("rms_fwd_inverted", "yr[j] = (w ? w[j] : 1.0) * (xr[j] / rms);", "yr[j] = (w ? w[j] : 1.0) * (xr[j] * rms);"),
 ]
 
@@ -78,6 +83,9 @@ PINS = [
     ("bn_act_fd", pb.test_bn_act_finite_differences),
     ("bn_infer_torch", lambda m: pb.test_bn_infer_matches_torch(m, "relu", 0.0)),
     ("bn_infer_batch", pb.test_bn_infer_with_batch_statistics_is_training_forward),
+    ("bda_torch", lambda m: pr.test_bda_matches_torch(m, 6, 10, 0.3, 71)),
+    ("bda_special", pr.test_bda_special_cases),
+    ("bda_exact", pr.test_bda_exact_rational),
 ]
 
 

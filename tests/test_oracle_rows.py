@@ -304,3 +304,98 @@ def test_forwards_exact_rational(oracle_mod):
         want_r = [Fraction(float(ww)) * (v / ms) for v, ww in zip(X, w)]
         assert max(abs(float(a) - c) for a, c in zip(want_r, yr[r])) < 1e-14
         assert abs(float(ms) - rms[r]) < 1e-15 * float(ms)
+
+
+# ------------------------------------- bias + dropout + add + LayerNorm backward
+
+def _torch_bda(x0, a0, bias0, w0, b0, mask, scale, dy, dres, eps):
+    """The forward written out in torch fp64 with autograd: h = residual +
+    (a + bias)*mask*scale (residual = x0 - that term, so h equals x0), y =
+    layer_norm(h); the loss sum(y*dy) + sum(h*dres) makes dres the gradient
+    reaching h from elsewhere."""
+    t = lambda v, g=True: torch.tensor(v, dtype=torch.float64, requires_grad=g)
+    a, bias, w, b = t(a0), t(bias0), t(w0), t(b0)
+    mk = torch.tensor(mask, dtype=torch.float64)
+    drop = (a + bias) * mk * scale
+    resid = t(x0 - drop.detach().numpy())
+    h = resid + drop
+    y = F.layer_norm(h, (x0.shape[1],), w, b, eps=eps)
+    loss = (y * torch.tensor(dy)).sum() + (h * torch.tensor(dres)).sum()
+    loss.backward()
+    return h.detach().numpy(), resid.grad.numpy(), a.grad.numpy(), w.grad.numpy(), b.grad.numpy(), \
+        bias.grad.numpy()
+
+
+@pytest.mark.parametrize("rows,cols,p_drop,seed", [(6, 10, 0.3, 71), (4, 33, 0.0, 72), (3, 7, 0.9, 73)])
+def test_bda_matches_torch(oracle_mod, rows, cols, p_drop, seed):
+    c = wl.bda_case(rows, cols, x_t=wl.F32, dy_t=wl.F32, w_t=wl.F32, seed=seed, p_drop=p_drop)
+    rng = np.random.default_rng(seed)
+    a0 = rng.normal(size=(rows, cols))
+    bias0 = rng.normal(size=cols)
+    b0 = rng.normal(size=cols)
+    x0 = c.ln.x.value
+    h, dres_t, da_t, dw_t, db_t, dbias_t = _torch_bda(x0, a0, bias0, c.ln.w.value, b0, c.mask, c.scale,
+                                                      c.ln.dy.value, c.dresidual.astype(np.float64),
+                                                      c.ln.eps)
+    mean, rstd = oracle_mod.layernorm_stats(h, eps=c.ln.eps)
+    dh, da, dw, db, dbi = oracle_mod.bda_layernorm_backward(h, c.ln.dy.value, mean, rstd, c.ln.w.value,
+                                                            c.dresidual, c.mask, c.scale)
+    assert _rel(dh, dres_t) < 1e-12
+    assert _rel(da, da_t) < 1e-12
+    assert _rel(dw, dw_t) < 1e-12
+    assert _rel(db, db_t) < 1e-12
+    assert _rel(dbi, dbias_t) < 1e-12
+
+
+def test_bda_special_cases(oracle_mod):
+    """No dropout (mask all ones, scale 1) and no incoming gradient: dh = da =
+    the LayerNorm input gradient, dbias_in = its column sums; every row of dh
+    - dresidual sums to 0; a zero mask zeroes da and dbias_in exactly."""
+    c = wl.bda_case(9, 24, x_t=wl.F32, dy_t=wl.F32, w_t=wl.F32, seed=74)
+    x, dy, w = c.ln.x.value, c.ln.dy.value, c.ln.w.value
+    mean, rstd = oracle_mod.layernorm_stats(x, eps=c.ln.eps)
+    dx, dw0, db0 = oracle_mod.layernorm_backward(x, dy, mean, rstd, w)
+    dh, da, dw, db, dbi = oracle_mod.bda_layernorm_backward(x, dy, mean, rstd, w, None, None, 1.0)
+    assert np.array_equal(dh, dx) and np.array_equal(da, dx)
+    assert np.array_equal(dw, dw0) and np.array_equal(db, db0)
+    assert _rel(dbi, dx.sum(axis=0), floor=1.0) < 1e-13
+    dh, da, _, _, dbi = oracle_mod.bda_layernorm_backward(x, dy, mean, rstd, w, c.dresidual, c.mask,
+                                                          c.scale)
+    rows_sum = (dh - c.dresidual).sum(axis=1)
+    assert np.max(np.abs(rows_sum)) < 1e-12 * np.max(np.abs(dh)) * x.shape[1]
+    # dropped elements are exactly zero, kept ones are dh*scale
+    assert np.all(da[c.mask == 0] == 0.0)
+    assert _rel(da[c.mask == 1], dh[c.mask == 1] * c.scale) < 1e-15
+    _, da0, _, _, dbi0 = oracle_mod.bda_layernorm_backward(x, dy, mean, rstd, w, c.dresidual,
+                                                           np.zeros_like(c.mask), c.scale)
+    assert np.all(da0 == 0.0) and np.all(dbi0 == 0.0)
+
+
+def test_bda_exact_rational(oracle_mod):
+    """Tiny case in exact rational arithmetic given the saved statistics."""
+    rng = np.random.default_rng(75)
+    rows, cols = 3, 5
+    x = np.round(rng.normal(size=(rows, cols)), 3)
+    dy = np.round(rng.normal(size=(rows, cols)), 3)
+    w = np.round(rng.uniform(0.5, 1.5, size=cols), 3)
+    dres = np.round(rng.normal(size=(rows, cols)), 3)
+    mask = (rng.random(size=(rows, cols)) > 0.4).astype(np.uint8)
+    scale = 1.25
+    mean = np.round(x.mean(axis=1), 3)
+    rstd = np.array([0.875, 1.125, 1.5])
+    dh, da, _, _, dbi = oracle_mod.bda_layernorm_backward(x, dy, mean, rstd, w, dres, mask, scale)
+    F_ = lambda v: Fraction(float(v))
+    H = Fraction(cols)
+    for r in range(rows):
+        mu, rs = F_(mean[r]), F_(rstd[r])
+        g = [F_(dy[r, j]) * F_(w[j]) for j in range(cols)]
+        xc = [F_(x[r, j]) - mu for j in range(cols)]
+        dvar = Fraction(-1, 2) * rs ** 3 * sum(gj * xj for gj, xj in zip(g, xc))
+        dmean = -rs * sum(g)
+        for j in range(cols):
+            want_h = F_(dres[r, j]) + g[j] * rs + 2 * dvar * xc[j] / H + dmean / H
+            want_a = want_h * Fraction(scale) * int(mask[r, j])
+            assert abs(float(want_h) - dh[r, j]) < 1e-14
+            assert abs(float(want_a) - da[r, j]) < 1e-14
+    for j in range(cols):
+        assert abs(sum(da[:, j]) - dbi[j]) < 1e-14
