@@ -283,6 +283,60 @@ def bench_rows(nh, torch, case, kind, K, W, cold=True, saved=True):
             "partials_bytes_written": G * H * 4 * (2 if kind == "ln" else 1)}
 
 
+def bench_bda(nh, torch, case, K, W, cold=True):
+    """Backward of bias + dropout + add + LayerNorm: reads x, dy, the incoming
+    gradient and the mask, writes dh (fp32) and da, plus the column sums."""
+    import ctypes
+    device = torch.device("cuda:0")
+    ln = case.ln
+    x0, dy0, w = _dev(ln.x, device), _dev(ln.dy, device), _dev(ln.w, device)
+    dres0 = torch.from_numpy(case.dresidual).to(device)
+    mask0 = torch.from_numpy(case.mask).to(device)
+    R_, H = ln.rows, ln.cols
+    var, mean = torch.var_mean(x0.float(), dim=1, unbiased=False)
+    mean, rstd = mean.contiguous(), torch.rsqrt(var + ln.eps).contiguous()
+    wsb = nh.bda_layernorm_backward_workspace(R_, H)
+    E = R_ * H
+    per_elem = x0.element_size() + dy0.element_size() + 4 + 1 + 4 + dy0.element_size()
+    R = _nsets(E * per_elem, cold)
+    sets = [dict(x=x0.clone(), dy=dy0.clone(), dres=dres0.clone(), mask=mask0.clone(),
+                 dh=torch.empty(x0.shape, dtype=torch.float32, device=device),
+                 da=torch.empty(x0.shape, dtype=dy0.dtype, device=device),
+                 dw=torch.empty(H, dtype=w.dtype, device=device),
+                 db=torch.empty(H, dtype=w.dtype, device=device),
+                 dbi=torch.empty(H, dtype=w.dtype, device=device),
+                 ws=torch.empty(max(wsb, 16), dtype=torch.uint8, device=device)) for _ in range(R)]
+    torch.cuda.synchronize()
+    P = ctypes.c_void_p
+    stream = P(torch.cuda.current_stream(device).cuda_stream)
+    dt = {torch.float32: 0, torch.bfloat16: 1}
+    calls = [({k: P(v.data_ptr()) for k, v in s.items()}, s["ws"].numel()) for s in sets]
+    pm, pr, pw = P(mean.data_ptr()), P(rstd.data_ptr()), P(w.data_ptr())
+
+    def step(i):
+        p, nb = calls[i % R]
+        st = nh.lib.bda_layernorm_backward(p["dy"], dt[dy0.dtype], p["x"], dt[x0.dtype], pm, pr, pw,
+                                           dt[w.dtype], p["dres"], p["mask"], case.scale, R_, H,
+                                           p["dh"], p["da"], p["dw"], p["db"], p["dbi"], p["ws"], nb,
+                                           stream)
+        if st:
+            raise RuntimeError(nh.last_error())
+
+    kernels = ["bda_rows", "bda_colsum"]
+    ms, per = Timed(nh, torch).run(step, K, W, kernels)
+    row_bytes = E * per_elem + R_ * 8 + H * w.element_size()
+    if "bda_rows" in per:
+        per["bda_rows"]["bytes"] = row_bytes
+        per["bda_rows"]["gbs"] = row_bytes / (per["bda_rows"]["avg_us"] * 1e3)
+        per["bda_rows"]["frac_of_peak"] = per["bda_rows"]["gbs"] / HBM_PEAK_GBS
+    G = nh.rows_plan(R_, H)
+    del sets, calls
+    torch.cuda.empty_cache()
+    return {"ms_per_call": ms, "us_per_call": 1000.0 * ms, "bytes": row_bytes,
+            "gbs": row_bytes / (ms * 1e6), "buffer_sets": R, "kernels": per, "blocks": G,
+            "partials_bytes_written": G * H * 4 * 3}
+
+
 def bench_rows_fwd(nh, torch, case, kind, K, W, cold=True):
     """LayerNorm / RMSNorm training forward: read x (+ weight, bias once),
     write y and the per-row statistics."""
@@ -549,6 +603,8 @@ def main():
             others[name] = bench_bn_infer(nh, torch, fn(), kk, W)
         log("[bench] ln_bwd_16x512x1600 (x f32, dy bf16, w bf16, dx f32)")
         others["ln_bwd_16x512x1600"] = bench_rows(nh, torch, wl.ln_bwd(), "ln", kk, W)
+        log("[bench] bda_bwd_16x512x1600 (bias+dropout+add+LayerNorm backward)")
+        others["bda_bwd_16x512x1600"] = bench_bda(nh, torch, wl.bda_bwd(), kk, W)
         for dt in (wl.BF16, wl.F32):
             for saved in (True, False):
                 name = f"rms_bwd_2048x8192_{dt}_{'saved' if saved else 'recompute'}_rms"

@@ -158,7 +158,7 @@ size_t rows_ws_bytes(int Q, int64_t rows, int64_t cols, const DeviceInfo &d)
 
 // Kernel variant for a row width: vector groups per thread (maxg, 0 = the
 // generic path) and the group width.  One 256-thread team per block.
-RowsPlan rows_variant(int64_t cols, int vec, bool vec_ok)
+RowsPlan rows_variant(int64_t cols, int vec, bool vec_ok, int max_elems = kRowsMaxRowElems)
 {
     RowsPlan p;
     p.vec = vec;
@@ -167,8 +167,8 @@ RowsPlan rows_variant(int64_t cols, int vec, bool vec_ok)
         const int64_t per_thread = ceil_div(groups, 256);
         int mg = 1;
         while (mg < per_thread) mg <<= 1;
-        // A thread holds at most 32 row elements in registers.
-        if (mg <= 8 && mg * vec <= 32) p.maxg = mg;
+        // A thread holds at most max_elems row elements in registers.
+        if (mg <= 8 && mg * vec <= max_elems) p.maxg = mg;
     }
     if (p.maxg == 0) p.vec = 1;
     p.teams = 1;
@@ -250,7 +250,8 @@ const char *nh_kernel_name(int k)
 {
     static const char *names[NH_K_COUNT] = {
         "bn_stats", "bn_fwd_finalize", "bn_apply", "bn_grad_sums", "bn_bwd_finalize", "bn_dx",
-        "ln_rows", "ln_colsum", "rms_rows", "rms_colsum", "calib", "ln_fwd", "rms_fwd", "bn_infer"};
+        "ln_rows", "ln_colsum", "rms_rows", "rms_colsum", "calib", "ln_fwd", "rms_fwd", "bn_infer",
+        "bda_rows", "bda_colsum"};
     return (k >= 0 && k < NH_K_COUNT) ? names[k] : "";
 }
 
@@ -485,7 +486,12 @@ static nh_status rows_run(RowsCall &a, int Q, void *ws, size_t ws_bytes, void *s
     need_align(a.dy, a.dy_t);
     need_align(a.dx, a.dx_t);
     need_align(a.w, a.w_t);
-    RowsPlan p = rows_variant(a.cols, a.vec, vec_ok);
+    if (a.kind == 2) {
+        need_align(a.dresidual, NH_F32);
+        need_align(a.dh, NH_F32);
+        if (a.mask && !aligned(a.mask, (size_t)a.vec)) vec_ok = false;
+    }
+    RowsPlan p = rows_variant(a.cols, a.vec, vec_ok, a.kind == 2 ? kBdaMaxRowElems : kRowsMaxRowElems);
     a.maxg = p.maxg;
     a.vec = p.vec;
     a.teams = p.teams;
@@ -493,7 +499,7 @@ static nh_status rows_run(RowsCall &a, int Q, void *ws, size_t ws_bytes, void *s
     int dev = 0;
     (void)hipGetDevice(&dev);
     const int dxt = a.dx != nullptr ? a.dx_t : a.dy_t;
-    const int64_t key = ((((((int64_t)dev * 2 + a.kind) * 2 + a.x_t) * 2 + a.dy_t) * 2 + dxt) * 16 +
+    const int64_t key = ((((((int64_t)dev * 4 + a.kind) * 2 + a.x_t) * 2 + a.dy_t) * 2 + dxt) * 16 +
                          a.maxg) * 16 + a.vec;
     int occ = 0;
     {
@@ -547,6 +553,58 @@ nh_status layernorm_backward(const void *dy, nh_dtype dy_t, const void *x, nh_dt
     a.dweight = dweight;
     a.dbias = dbias;
     return rows_run(a, 2, ws, ws_bytes, stream);
+}
+
+nh_status bda_layernorm_backward_workspace(int64_t rows, int64_t cols, size_t *ws_bytes)
+{
+    if (!ws_bytes) return fail(NH_ERR_NULL, "ws_bytes is NULL");
+    nh_status st = rows_check_shape(rows, cols);
+    if (st != NH_OK) return st;
+    if (rows * cols == 0) { *ws_bytes = 0; return ok(); }
+    DeviceInfo d;
+    if ((st = device_info(&d)) != NH_OK) return st;
+    *ws_bytes = rows_ws_bytes(3, rows, cols, d);
+    return ok();
+}
+
+nh_status bda_layernorm_backward(const void *dy, nh_dtype dy_t, const void *x, nh_dtype x_t,
+                                 const float *mean, const float *rstd, const void *weight,
+                                 nh_dtype w_t, const float *dresidual, const uint8_t *mask,
+                                 float scale, int64_t rows, int64_t cols, float *dh, void *da,
+                                 void *dweight, void *dbias, void *dbias_in, void *ws,
+                                 size_t ws_bytes, void *stream)
+{
+    if (!valid_dtype(dy_t) || !valid_dtype(x_t) || !valid_dtype(w_t))
+        return fail(NH_ERR_DTYPE, "dtypes must be NH_F32 or NH_BF16");
+    nh_status st = rows_check_shape(rows, cols);
+    if (st != NH_OK) return st;
+    if (cols == 0) return ok();
+    if (rows > 0 && (!dy || !x || !mean || !rstd))
+        return fail(NH_ERR_NULL, "dy, x, mean and rstd are required");
+    if (!isfinite(scale)) return fail(NH_ERR_ARG, "scale must be finite");
+    RowsCall a{};
+    a.kind = 2;
+    a.x_t = x_t;
+    a.dy_t = dy_t;
+    a.w_t = w_t;
+    a.dx_t = dy_t;
+    a.rows = (int)rows;
+    a.cols = (int)cols;
+    a.vec = (x_t == NH_F32 || dy_t == NH_F32) ? 4 : 8;
+    a.x = x;
+    a.dy = dy;
+    a.w = weight;
+    a.mean = mean;
+    a.rstd = rstd;
+    a.dx = da;
+    a.dresidual = dresidual;
+    a.mask = mask;
+    a.scale = scale;
+    a.dh = dh;
+    a.dweight = dweight;
+    a.dbias = dbias;
+    a.dbias_in = dbias_in;
+    return rows_run(a, 3, ws, ws_bytes, stream);
 }
 
 nh_status rmsnorm_backward(const void *dy, const void *x, nh_dtype t, const float *rms, float eps,

@@ -71,7 +71,7 @@ hipError_t bn_backward_launch(const BnCall &a, hipStream_t s);
 
 // ---- LayerNorm / RMSNorm rows -------------------------------------------------
 struct RowsCall {
-    int kind;            // 0 LayerNorm, 1 RMSNorm
+    int kind;            // 0 LayerNorm, 1 RMSNorm, 2 bias + dropout + add + LayerNorm
     int x_t, dy_t, w_t, dx_t;
     int rows, cols;
     int blocks;          // G: column-partial rows
@@ -82,13 +82,26 @@ struct RowsCall {
     const float *mean, *rstd;  // LayerNorm
     const float *rms;          // RMSNorm (NULL: recompute)
     float eps;
-    void *dx, *dweight, *dbias;
+    void *dx, *dweight, *dbias;  // kind 2: dx is da (dtype dy_t)
+    const float *dresidual;      // kind 2: fp32 [rows, cols] or NULL
+    const uint8_t *mask;         // kind 2: 0/1 bytes [rows, cols] or NULL
+    float scale;                 // kind 2: dropout scale
+    float *dh;                   // kind 2: fp32 [rows, cols] out or NULL
+    void *dbias_in;              // kind 2: [cols] of w_t out or NULL
     float *partials;     // [Q, G, cols]
     int *occupancy_out;  // non-NULL: report resident 256-thread blocks per CU
                          // of the selected row kernel instead of launching
 };
 
 hipError_t rows_backward_launch(const RowsCall &a, hipStream_t s);
+hipError_t bda_backward_launch(const RowsCall &a, hipStream_t s);
+// Column finalize of the Q = rows_q(kind) partial rows into dweight, dbias, dbias_in.
+hipError_t rows_colsum_launch(const RowsCall &a, int kid, hipStream_t s);
+// Dynamic LDS of a row-kernel launch: row sums, plus the team-fold slot.
+int rows_lds_bytes(const RowsCall &a);
+// Column sums per kind: LayerNorm dweight, dbias; RMSNorm dweight;
+// bias + dropout + add + LayerNorm dweight, dbias, dbias_in.
+constexpr int rows_q(int kind) { return kind == 0 ? 2 : (kind == 1 ? 1 : 3); }
 
 // Block-size bound of a vector row-kernel variant: 4 teams (128 VGPRs per
 // thread) when a thread holds at most 8 elements of a row, else 2 teams
@@ -101,6 +114,11 @@ constexpr int rows_max_threads(int maxg, int vec) { return maxg * vec <= 8 ? 102
 // rows).
 constexpr int kRowsMaxBlocksPerCu = 2;
 constexpr int kRowsMaxBlocks = 2048;
+// Row elements a thread holds in the vector row kernels: 32 for LayerNorm and
+// RMSNorm; 16 for the bias + dropout + add + LayerNorm backward, whose row
+// also carries the incoming gradient and the mask (32 would spill).
+constexpr int kRowsMaxRowElems = 32;
+constexpr int kBdaMaxRowElems = 16;
 
 // ---- LayerNorm / RMSNorm forward ---------------------------------------------------
 struct FwdCall {

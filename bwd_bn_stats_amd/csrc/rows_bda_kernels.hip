@@ -1,0 +1,294 @@
+// Backward of bias + dropout + add + LayerNorm over the last dimension of
+// [rows, H]: NVIDIA/Fuser issue #1473, the one-kernel fusion of its first
+// example.  The forward is h = residual + dropout(a + bias), y =
+// LayerNorm(h); with xhat = (h - mean)*rstd and g = dy*w,
+//   dx_ln     = rstd*(g - sum g/H - xhat*sum(g*xhat)/H)    (LayerNorm backward)
+//   dh        = dresidual + dx_ln                         (fp32 out)
+//   da        = dh * scale * mask                         (dy's dtype out)
+//   dweight_j = sum_rows dy*xhat,  dbias_j = sum_rows dy,  dbias_in_j = sum_rows da.
+//
+// The LayerNorm backward row kernel extended by the fused epilogue: the
+// incoming gradient and the keep-mask of a row are read with its x and dy
+// (one row ahead, through range-checked buffer loads; a NULL input is an
+// empty buffer that reads as zeros), the epilogue writes dh and da, and a
+// third column accumulator carries dbias_in through the same split-over-rows
+// partials and fixed-order column finalize.  Every element of every input
+// is read once and every output written once.
+#include "rows_common.hpp"
+
+namespace nh {
+
+// A group of V keep-mask bytes (V = 4 or 8), packed four to a register.
+template <int V>
+struct MaskGroup {
+    static_assert(V == 4 || V == 8, "mask groups hold 4 or 8 bytes");
+    uint32_t u[V / 4];
+    __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, int off)
+    {
+        if constexpr (V == 8) {
+            u32x2_t t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kBufferNT);
+            u[0] = t.x;
+            u[1] = t.y;
+        } else {
+            u[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kBufferNT);
+        }
+    }
+    __device__ __forceinline__ float get(int e) const
+    {
+        return ((u[e >> 2] >> (8 * (e & 3))) & 0xffu) != 0u ? 1.f : 0.f;
+    }
+};
+
+template <typename TX, typename TDY, int VEC, int MAXG, int MAXT, bool PF>
+__global__ void __launch_bounds__(MAXT)
+bda_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
+                const float *__restrict__ mean, const float *__restrict__ rstd,
+                const void *__restrict__ w, int w_bf16, const float *__restrict__ dres,
+                const uint8_t *__restrict__ mask, float scale, int rows, int H,
+                float *__restrict__ dh, TDY *__restrict__ da, float *__restrict__ partials,
+                int want_cols)
+{
+    extern __shared__ float lds[];
+    float *red = lds;
+    float *slot = lds + kRedFloats;
+    const int teams = blockDim.x / kTeam;
+    const int team = threadIdx.x / kTeam;
+    const int tt = threadIdx.x - team * kTeam;
+    const int wave = tt / kWave;
+    const int lane = tt & (kWave - 1);
+    const int G = gridDim.x;
+    const int Gr = H / VEC;
+    const float invH = 1.0f / (float)H;
+    const bool has_mask = mask != nullptr;
+
+    WeightGroup<VEC> wv[MAXG];
+    float p[3][MAXG][VEC];
+#pragma unroll
+    for (int k = 0; k < MAXG; ++k) {
+        const int grp = tt + k * kTeam;
+        if (grp < Gr) wv[k].load(w, w_bf16, grp * VEC);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) { p[0][k][e] = 0.f; p[1][k][e] = 0.f; p[2][k][e] = 0.f; }
+    }
+
+    const int iters = (int)ceil_div(rows, (int64_t)G * teams);
+    auto row_of = [&](int it) { return (it * G + (int)blockIdx.x) * teams + team; };
+
+    struct RowBuf {
+        Raw<TX, VEC> x[MAXG];
+        Raw<TDY, VEC> d[MAXG];
+        Raw<float, VEC> r[MAXG];
+        MaskGroup<VEC> m[MAXG];
+        float mu, rs;
+    };
+    auto load_row = [&](RowBuf &b, int it) {
+        const int r = __builtin_amdgcn_readfirstlane(row_of(it));
+        const bool live = r < rows;
+        const int rc = live ? r : rows - 1;
+        const size_t rowoff = (size_t)rc * H;
+        const auto rx = make_rsrc(x + rowoff, live ? (uint32_t)(H * sizeof(TX)) : 0u);
+        const auto rd = make_rsrc(dy + rowoff, live ? (uint32_t)(H * sizeof(TDY)) : 0u);
+        const auto rr = make_rsrc(dres ? dres + rowoff : nullptr,
+                                  live && dres ? (uint32_t)(H * sizeof(float)) : 0u);
+        const auto rm = make_rsrc(mask ? mask + rowoff : nullptr, live && mask ? (uint32_t)H : 0u);
+#pragma unroll
+        for (int k = 0; k < MAXG; ++k) {
+            const int grp = tt + k * kTeam;
+            b.x[k].load_buf(rx, grp * VEC * (int)sizeof(TX));
+            b.d[k].load_buf(rd, grp * VEC * (int)sizeof(TDY));
+            b.r[k].load_buf(rr, grp * VEC * (int)sizeof(float));
+            b.m[k].load_buf(rm, grp * VEC);
+        }
+        b.mu = mean[rc];
+        b.rs = rstd[rc];
+    };
+
+    auto do_row = [&](const RowBuf &b, int it) {
+        const int r = row_of(it);
+        const bool active = r < rows;
+        const float mu = b.mu, rs = b.rs;
+        float sa = 0.f, sb = 0.f;
+#pragma unroll
+        for (int k = 0; k < MAXG; ++k) {
+            const int grp = tt + k * kTeam;
+            if (active && grp < Gr) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const float d = b.d[k].get(e);
+                    const float xh = (b.x[k].get(e) - mu) * rs;
+                    const float g = d * wv[k].get(e);
+                    sa += g;
+                    sb = fmaf(g, xh, sb);
+                    p[0][k][e] = fmaf(d, xh, p[0][k][e]);
+                    p[1][k][e] += d;
+                }
+            }
+        }
+        team_sum2(red + (it & 1) * (kRedFloats / 2), team, wave, lane, sa, sb);
+        if (!active) return;
+        const float ca = sa * invH, cb = sb * invH;
+        const size_t rowoff = (size_t)r * H;
+#pragma unroll
+        for (int k = 0; k < MAXG; ++k) {
+            const int grp = tt + k * kTeam;
+            if (grp < Gr) {
+                float hv[VEC], av[VEC];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const float xh = (b.x[k].get(e) - mu) * rs;
+                    const float g = b.d[k].get(e) * wv[k].get(e);
+                    hv[e] = rs * fmaf(-xh, cb, g - ca) + b.r[k].get(e);
+                    av[e] = hv[e] * scale * (has_mask ? b.m[k].get(e) : 1.f);
+                    p[2][k][e] += av[e];
+                }
+                if (dh != nullptr) st<true, float, VEC>(dh + rowoff + grp * VEC, hv);
+                if (da != nullptr) st<true, TDY, VEC>(da + rowoff + grp * VEC, av);
+            }
+        }
+    };
+
+    RowBuf ba;
+    if constexpr (PF) {
+        RowBuf bb;
+        load_row(ba, 0);
+        for (int it = 0; it < iters; it += 2) {
+            load_row(bb, it + 1);
+            do_row(ba, it);
+            if (it + 1 >= iters) break;
+            load_row(ba, it + 2);
+            do_row(bb, it + 1);
+        }
+    } else {
+        for (int it = 0; it < iters; ++it) {
+            load_row(ba, it);
+            do_row(ba, it);
+        }
+    }
+    if (want_cols) fold_and_write<VEC, MAXG, 3>(p, slot, teams, team, tt, Gr, H, G, partials);
+}
+
+// Any width, any alignment: scalar accesses, two reads of each row (the
+// second mostly from cache), the column sums in the block's own partial rows.
+template <typename TX, typename TDY>
+__global__ void __launch_bounds__(kTeam)
+bda_generic_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
+                   const float *__restrict__ mean, const float *__restrict__ rstd,
+                   const void *__restrict__ w, int w_bf16, const float *__restrict__ dres,
+                   const uint8_t *__restrict__ mask, float scale, int rows, int H,
+                   float *__restrict__ dh, TDY *__restrict__ da, float *__restrict__ partials,
+                   int want_cols)
+{
+    __shared__ float red[kRedFloats];
+    const int tt = threadIdx.x;
+    const int wave = tt / kWave;
+    const int lane = tt & (kWave - 1);
+    const int G = gridDim.x;
+    const float invH = 1.0f / (float)H;
+    float *prow0 = partials + (size_t)blockIdx.x * H;
+    float *prow1 = partials + ((size_t)G + blockIdx.x) * H;
+    float *prow2 = partials + ((size_t)2 * G + blockIdx.x) * H;
+    if (want_cols)
+        for (int j = tt; j < H; j += kTeam) {
+            prow0[j] = 0.f;
+            prow1[j] = 0.f;
+            prow2[j] = 0.f;
+        }
+    int it = 0;
+    for (int r = blockIdx.x; r < rows; r += G, ++it) {
+        const size_t rowoff = (size_t)r * H;
+        const float mu = mean[r], rs = rstd[r];
+        float sa = 0.f, sb = 0.f;
+        for (int j = tt; j < H; j += kTeam) {
+            const float wj = w ? load_param(w, w_bf16, j) : 1.f;
+            const float g = to_f32(dy[rowoff + j]) * wj;
+            sa += g;
+            sb = fmaf(g, (to_f32(x[rowoff + j]) - mu) * rs, sb);
+        }
+        team_sum2(red + (it & 1) * (kRedFloats / 2), 0, wave, lane, sa, sb);
+        const float ca = sa * invH, cb = sb * invH;
+        for (int j = tt; j < H; j += kTeam) {
+            const size_t i = rowoff + j;
+            const float wj = w ? load_param(w, w_bf16, j) : 1.f;
+            const float d = to_f32(dy[i]);
+            const float xh = (to_f32(x[i]) - mu) * rs;
+            const float h = rs * fmaf(-xh, cb, d * wj - ca) + (dres ? dres[i] : 0.f);
+            const float a = h * scale * (mask ? (mask[i] != 0 ? 1.f : 0.f) : 1.f);
+            if (want_cols) {
+                prow0[j] = fmaf(d, xh, prow0[j]);
+                prow1[j] += d;
+                prow2[j] += a;
+            }
+            if (dh != nullptr) dh[i] = h;
+            if (da != nullptr) da[i] = from_f32<TDY>(a);
+        }
+    }
+}
+
+// ---- host dispatch ---------------------------------------------------------------
+template <typename TX, typename TDY, int VEC, int MAXG>
+static hipError_t bda_vec(const RowsCall &a, hipStream_t s)
+{
+    constexpr int MT = rows_max_threads(MAXG, VEC);
+    constexpr bool PF = MAXG * VEC <= 16;
+    auto kern = bda_rows_kernel<TX, TDY, VEC, MAXG, MT, PF>;
+    if (a.occupancy_out)
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kern, kTeam,
+                                                            (size_t)rows_lds_bytes(a));
+    return launch(NH_K_BDA_ROWS, kern, dim3(a.blocks), dim3(a.teams * kTeam),
+                  (uint32_t)rows_lds_bytes(a), s, static_cast<const TDY *>(a.dy),
+                  static_cast<const TX *>(a.x), a.mean, a.rstd, a.w, a.w_t, a.dresidual, a.mask,
+                  a.scale, a.rows, a.cols, a.dh, static_cast<TDY *>(a.dx), a.partials,
+                  (int)(a.dweight != nullptr || a.dbias != nullptr || a.dbias_in != nullptr));
+}
+
+template <typename TX, typename TDY>
+static hipError_t bda_generic(const RowsCall &a, hipStream_t s)
+{
+    auto kern = bda_generic_kernel<TX, TDY>;
+    if (a.occupancy_out)
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kern, kTeam, 0);
+    return launch(NH_K_BDA_ROWS, kern, dim3(a.blocks), dim3(kTeam), 0u, s,
+                  static_cast<const TDY *>(a.dy), static_cast<const TX *>(a.x), a.mean, a.rstd, a.w,
+                  a.w_t, a.dresidual, a.mask, a.scale, a.rows, a.cols, a.dh,
+                  static_cast<TDY *>(a.dx), a.partials,
+                  (int)(a.dweight != nullptr || a.dbias != nullptr || a.dbias_in != nullptr));
+}
+
+template <typename TX, typename TDY>
+static hipError_t bda_types(const RowsCall &a, hipStream_t s)
+{
+    if (a.maxg == 0) return bda_generic<TX, TDY>(a, s);
+    // At most kBdaMaxRowElems row elements per thread (the planner sends
+    // wider rows to the generic path).
+    if (a.vec == 4) {
+        switch (a.maxg) {
+        case 1: return bda_vec<TX, TDY, 4, 1>(a, s);
+        case 2: return bda_vec<TX, TDY, 4, 2>(a, s);
+        case 4: return bda_vec<TX, TDY, 4, 4>(a, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (a.maxg) {
+    case 1: return bda_vec<TX, TDY, 8, 1>(a, s);
+    case 2: return bda_vec<TX, TDY, 8, 2>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t bda_backward_launch(const RowsCall &a, hipStream_t s)
+{
+    hipError_t e = hipSuccess;
+    if (a.rows > 0) {
+        switch (a.x_t * 2 + a.dy_t) {
+        case 0: e = bda_types<float, float>(a, s); break;
+        case 1: e = bda_types<float, uint16_t>(a, s); break;
+        case 2: e = bda_types<uint16_t, float>(a, s); break;
+        default: e = bda_types<uint16_t, uint16_t>(a, s); break;
+        }
+    }
+    if (e != hipSuccess || a.occupancy_out) return e;
+    if (a.dweight == nullptr && a.dbias == nullptr && a.dbias_in == nullptr) return hipSuccess;
+    return rows_colsum_launch(a, NH_K_BDA_COLSUM, s);
+}
+
+} // namespace nh

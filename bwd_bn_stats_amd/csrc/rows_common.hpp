@@ -57,4 +57,49 @@ __device__ __forceinline__ void team_sum2(float *red, int team, int wave, int la
     b = sb;
 }
 
+// Folds the teams' column sums into team 0 in team order (slot: Q*H floats),
+// then team 0 writes the block's partial row.
+template <int VEC, int MAXG, int Q>
+__device__ __forceinline__ void fold_and_write(float (&p)[Q][MAXG][VEC], float *slot, int teams,
+                                               int team, int tt, int Gr, int H, int G,
+                                               float *__restrict__ partials)
+{
+    for (int t = 1; t < teams; ++t) {
+        __syncthreads();
+        if (team == t) {
+#pragma unroll
+            for (int k = 0; k < MAXG; ++k) {
+                const int grp = tt + k * kTeam;
+                if (grp < Gr)
+#pragma unroll
+                    for (int q = 0; q < Q; ++q)
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) slot[q * H + grp * VEC + e] = p[q][k][e];
+            }
+        }
+        __syncthreads();
+        if (team == 0) {
+#pragma unroll
+            for (int k = 0; k < MAXG; ++k) {
+                const int grp = tt + k * kTeam;
+                if (grp < Gr)
+#pragma unroll
+                    for (int q = 0; q < Q; ++q)
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) p[q][k][e] += slot[q * H + grp * VEC + e];
+            }
+        }
+    }
+    if (team == 0) {
+#pragma unroll
+        for (int k = 0; k < MAXG; ++k) {
+            const int grp = tt + k * kTeam;
+            if (grp < Gr)
+#pragma unroll
+                for (int q = 0; q < Q; ++q)
+                    store_vec<float, VEC>(partials + ((size_t)q * G + blockIdx.x) * H + grp * VEC, p[q][k]);
+        }
+    }
+}
+
 } // namespace nh

@@ -34,51 +34,6 @@
 
 namespace nh {
 
-// Folds the teams' column sums into team 0 in team order (slot: Q*H floats),
-// then team 0 writes the block's partial row.
-template <int VEC, int MAXG, int Q>
-__device__ __forceinline__ void fold_and_write(float (&p)[Q][MAXG][VEC], float *slot, int teams,
-                                               int team, int tt, int Gr, int H, int G,
-                                               float *__restrict__ partials)
-{
-    for (int t = 1; t < teams; ++t) {
-        __syncthreads();
-        if (team == t) {
-#pragma unroll
-            for (int k = 0; k < MAXG; ++k) {
-                const int grp = tt + k * kTeam;
-                if (grp < Gr)
-#pragma unroll
-                    for (int q = 0; q < Q; ++q)
-#pragma unroll
-                        for (int e = 0; e < VEC; ++e) slot[q * H + grp * VEC + e] = p[q][k][e];
-            }
-        }
-        __syncthreads();
-        if (team == 0) {
-#pragma unroll
-            for (int k = 0; k < MAXG; ++k) {
-                const int grp = tt + k * kTeam;
-                if (grp < Gr)
-#pragma unroll
-                    for (int q = 0; q < Q; ++q)
-#pragma unroll
-                        for (int e = 0; e < VEC; ++e) p[q][k][e] += slot[q * H + grp * VEC + e];
-            }
-        }
-    }
-    if (team == 0) {
-#pragma unroll
-        for (int k = 0; k < MAXG; ++k) {
-            const int grp = tt + k * kTeam;
-            if (grp < Gr)
-#pragma unroll
-                for (int q = 0; q < Q; ++q)
-                    store_vec<float, VEC>(partials + ((size_t)q * G + blockIdx.x) * H + grp * VEC, p[q][k]);
-        }
-    }
-}
-
 // ---- LayerNorm, vector path ----------------------------------------------------
 // PF: software-pipelined rows.  While a team reduces and writes row i, the
 // loads of its row i+1 are already in flight (two register sets, used
@@ -404,11 +359,11 @@ constexpr int kColY = 32;   // slices of the G partial rows
 template <typename TOUT>
 __global__ void __launch_bounds__(kColX * kColY)
 rows_colsum_kernel(const float *__restrict__ partials, int G, int H, TOUT *__restrict__ out0,
-                   TOUT *__restrict__ out1)
+                   TOUT *__restrict__ out1, TOUT *__restrict__ out2)
 {
     __shared__ double acc[kColY][kColX];
     const int q = blockIdx.y;
-    TOUT *out = q == 0 ? out0 : out1;
+    TOUT *out = q == 0 ? out0 : (q == 1 ? out1 : out2);
     if (out == nullptr) return;  // uniform across the block
     const int tx = threadIdx.x % kColX;
     const int ty = threadIdx.x / kColX;
@@ -429,9 +384,9 @@ rows_colsum_kernel(const float *__restrict__ partials, int G, int H, TOUT *__res
 }
 
 // ---- host dispatch ---------------------------------------------------------------
-static inline int lds_bytes(const RowsCall &a)
+int rows_lds_bytes(const RowsCall &a)
 {
-    const int Q = a.kind == 0 ? 2 : 1;
+    const int Q = rows_q(a.kind);
     return (kRedFloats + (a.teams > 1 ? Q * a.cols : 0)) * (int)sizeof(float);
 }
 
@@ -442,7 +397,7 @@ template <typename K>
 static hipError_t occupancy(const RowsCall &a, K kernel)
 {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kernel, kTeam,
-                                                        (size_t)lds_bytes(a));
+                                                        (size_t)rows_lds_bytes(a));
 }
 
 template <typename TX, typename TDY, typename TDX, int VEC, int MAXG>
@@ -452,7 +407,7 @@ static hipError_t ln_vec(const RowsCall &a, hipStream_t s)
     constexpr bool PF = MAXG * VEC <= 16;
     if (a.occupancy_out) return occupancy(a, ln_rows_kernel<TX, TDY, TDX, VEC, MAXG, MT, PF>);
     return launch(NH_K_LN_ROWS, ln_rows_kernel<TX, TDY, TDX, VEC, MAXG, MT, PF>, dim3(a.blocks),
-                  dim3(a.teams * kTeam), (uint32_t)lds_bytes(a), s,
+                  dim3(a.teams * kTeam), (uint32_t)rows_lds_bytes(a), s,
                   static_cast<const TDY *>(a.dy), static_cast<const TX *>(a.x), a.mean, a.rstd,
                   a.w, a.w_t, a.rows, a.cols, static_cast<TDX *>(a.dx), a.partials,
                   (int)(a.dweight != nullptr || a.dbias != nullptr));
@@ -465,7 +420,7 @@ static hipError_t rms_vec(const RowsCall &a, hipStream_t s)
     constexpr bool PF = MAXG * VEC * (int)sizeof(T) <= 64;
     if (a.occupancy_out) return occupancy(a, rms_rows_kernel<T, VEC, MAXG, MT, PF>);
     return launch(NH_K_RMS_ROWS, rms_rows_kernel<T, VEC, MAXG, MT, PF>, dim3(a.blocks),
-                  dim3(a.teams * kTeam), (uint32_t)lds_bytes(a), s,
+                  dim3(a.teams * kTeam), (uint32_t)rows_lds_bytes(a), s,
                   static_cast<const T *>(a.dy), static_cast<const T *>(a.x), a.rms, a.eps, a.w,
                   a.w_t, a.rows, a.cols, static_cast<T *>(a.dx), a.partials,
                   (int)(a.dweight != nullptr));
@@ -545,15 +500,22 @@ template <typename TX, typename TDY, typename TDX> struct GenericF {
 template <typename TOUT>
 static hipError_t colsum(const RowsCall &a, int kid, hipStream_t s)
 {
-    const int Q = a.kind == 0 ? 2 : 1;
+    const int Q = rows_q(a.kind);
     const dim3 grid((unsigned)ceil_div(a.cols, kColX), (unsigned)Q);
     return launch(kid, rows_colsum_kernel<TOUT>, grid, dim3(kColX * kColY), 0u, s,
                   (const float *)a.partials, a.blocks, a.cols, static_cast<TOUT *>(a.dweight),
-                  static_cast<TOUT *>(a.kind == 0 ? a.dbias : nullptr));
+                  static_cast<TOUT *>(a.kind != 1 ? a.dbias : nullptr),
+                  static_cast<TOUT *>(a.kind == 2 ? a.dbias_in : nullptr));
+}
+
+hipError_t rows_colsum_launch(const RowsCall &a, int kid, hipStream_t s)
+{
+    return a.w_t == 0 ? colsum<float>(a, kid, s) : colsum<uint16_t>(a, kid, s);
 }
 
 hipError_t rows_backward_launch(const RowsCall &a, hipStream_t s)
 {
+    if (a.kind == 2) return bda_backward_launch(a, s);
     // The dx dtype of a skipped dx is irrelevant: use the dy dtype.
     const int dxt = a.dx != nullptr ? a.dx_t : a.dy_t;
     hipError_t e = hipSuccess;
@@ -570,7 +532,7 @@ hipError_t rows_backward_launch(const RowsCall &a, hipStream_t s)
     const bool cols = a.kind == 0 ? (a.dweight != nullptr || a.dbias != nullptr) : a.dweight != nullptr;
     if (!cols) return hipSuccess;
     const int kid = a.kind == 0 ? NH_K_LN_COLSUM : NH_K_RMS_COLSUM;
-    return a.w_t == 0 ? colsum<float>(a, kid, s) : colsum<uint16_t>(a, kid, s);
+    return rows_colsum_launch(a, kid, s);
 }
 
 } // namespace nh

@@ -22,7 +22,8 @@ F32, BF16 = 0, 1
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 
 KERNELS = ["bn_stats", "bn_fwd_finalize", "bn_apply", "bn_grad_sums", "bn_bwd_finalize", "bn_dx",
-           "ln_rows", "ln_colsum", "rms_rows", "rms_colsum", "calib", "ln_fwd", "rms_fwd", "bn_infer"]
+           "ln_rows", "ln_colsum", "rms_rows", "rms_colsum", "calib", "ln_fwd", "rms_fwd", "bn_infer",
+           "bda_rows", "bda_colsum"]
 
 ACTS = {"none": 0, "relu": 1, "leaky_relu": 2}
 
@@ -31,6 +32,7 @@ EXPORTS = [
     "bn_forward_train_workspace", "bn_backward_workspace", "bn_forward_train", "bn_backward",
     "bn_act_forward_train", "bn_act_backward", "bn_forward_infer",
     "layernorm_backward_workspace", "layernorm_backward",
+    "bda_layernorm_backward_workspace", "bda_layernorm_backward",
     "rmsnorm_backward_workspace", "rmsnorm_backward", "layernorm_forward", "rmsnorm_forward",
     "nh_timing_enable", "nh_timing_reserve", "nh_timing_read", "nh_calib_copy", "nh_calib_add",
     "nh_bn_plan", "nh_rows_plan", "nh_plan_override", "nh_selftest_host",
@@ -65,6 +67,9 @@ def _load():
         "bn_forward_infer": (i32, [p, p, i32, i64, i64, i64, p, p, p, p, f32, i32, f32, p]),
         "layernorm_backward_workspace": (i32, [i64, i64, psz]),
         "layernorm_backward": (i32, [p, i32, p, i32, p, p, p, i32, i64, i64, p, i32, p, p, p, sz, p]),
+        "bda_layernorm_backward_workspace": (i32, [i64, i64, psz]),
+        "bda_layernorm_backward": (i32, [p, i32, p, i32, p, p, p, i32, p, p, f32, i64, i64, p, p, p, p, p,
+                                         p, sz, p]),
         "rmsnorm_backward_workspace": (i32, [i64, i64, psz]),
         "rmsnorm_backward": (i32, [p, p, i32, p, f32, p, i64, i64, p, p, p, sz, p]),
         "layernorm_forward": (i32, [p, i32, p, p, i32, i64, i64, f32, p, i32, p, p, p]),
@@ -164,6 +169,13 @@ def bn_backward_workspace(N: int, C: int, HW: int) -> int:
 def layernorm_backward_workspace(rows: int, cols: int) -> int:
     out = ctypes.c_size_t()
     _check(lib.layernorm_backward_workspace(rows, cols, ctypes.byref(out)), "layernorm_backward_workspace")
+    return out.value
+
+
+def bda_layernorm_backward_workspace(rows: int, cols: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib.bda_layernorm_backward_workspace(rows, cols, ctypes.byref(out)),
+           "bda_layernorm_backward_workspace")
     return out.value
 
 
@@ -288,6 +300,39 @@ def layernorm_backward(dy, x, mean, rstd, weight=None, *, dx_dtype=None, w_dtype
                                   _ptr(dweight), _ptr(dbias), _ptr(ws), nb, _stream(x.device)),
            "layernorm_backward")
     return dx, dweight, dbias
+
+
+def bda_layernorm_backward(dy, x, mean, rstd, weight=None, dresidual=None, mask=None,
+                           scale: float = 1.0, *, w_dtype=None, need_dh=True, need_da=True,
+                           need_dweight=True, need_dbias=True, need_dbias_in=True, workspace=None):
+    """Backward of bias + dropout + add + LayerNorm over the last dim.
+    mask: bool or uint8 tensor (nonzero = kept) or None.  Returns
+    (dh fp32, da in dy's dtype, dweight, dbias, dbias_in), None where not
+    requested; the column gradients take the weight's dtype."""
+    _dev_tensor(x, "x")
+    _dev_tensor(dy, "dy", None, x.numel())
+    rows, cols = _rows(x)
+    f32 = torch.float32
+    _dev_tensor(mean, "mean", f32, rows)
+    _dev_tensor(rstd, "rstd", f32, rows)
+    _dev_tensor(weight, "weight", None, cols)
+    _dev_tensor(dresidual, "dresidual", f32, x.numel())
+    if mask is not None:
+        _dev_tensor(mask, "mask", None, x.numel())
+        if mask.dtype not in (torch.bool, torch.uint8):
+            raise TypeError("mask must be bool or uint8")
+    wdt = weight.dtype if weight is not None else (w_dtype or f32)
+    dh = torch.empty(x.shape, dtype=f32, device=x.device) if need_dh else None
+    da = torch.empty(x.shape, dtype=dy.dtype, device=x.device) if need_da else None
+    cols_out = [torch.empty(cols, dtype=wdt, device=x.device) if need else None
+                for need in (need_dweight, need_dbias, need_dbias_in)]
+    ws = _workspace(bda_layernorm_backward_workspace(rows, cols), x.device, workspace)
+    nb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.bda_layernorm_backward(_ptr(dy), _dt(dy), _ptr(x), _dt(x), _ptr(mean), _ptr(rstd),
+                                      _ptr(weight), _DT[wdt], _ptr(dresidual), _ptr(mask), scale,
+                                      rows, cols, _ptr(dh), _ptr(da), *[_ptr(t) for t in cols_out],
+                                      _ptr(ws), nb, _stream(x.device)), "bda_layernorm_backward")
+    return (dh, da, *cols_out)
 
 
 def rmsnorm_backward(dy, x, rms=None, weight=None, eps: float = 1e-5, *, need_dx=True,

@@ -18,6 +18,10 @@
  *                       mean/rstd.  NVIDIA/Fuser issue #1473, "Why is
  *                       LayerNorm Backward Segmenting?", the layer_norm
  *                       backward definition (nvfuser_fusion_id14).
+ *   bda_layernorm_backward
+ *                       Backward of bias + dropout + add + LayerNorm.  Same
+ *                       issue, its one-kernel fusion example
+ *                       (nvfuser_fusion_id9).
  *   rmsnorm_backward    RMSNorm backward over the last dimension.
  *                       NVIDIA/Fuser issue #3629, "Performance gap between
  *                       manual nvfuser definition and thunder.jit for
@@ -254,6 +258,42 @@ nh_status rmsnorm_backward(const void *dy, const void *x, nh_dtype t,
                            void *dx, void *dweight,
                            void *ws, size_t ws_bytes, void *stream);
 
+nh_status bda_layernorm_backward_workspace(int64_t rows, int64_t cols, size_t *ws_bytes);
+
+/*
+ * Backward of bias + dropout + add + LayerNorm.  NVIDIA/Fuser issue #1473,
+ * the one-kernel fusion of its first example (nvfuser_fusion_id9).  The
+ * forward is h = residual + dropout(a + bias), y = LayerNorm(h), dropout
+ * being a multiply by a 0/1 keep-mask and by `scale`.  With dx_ln the
+ * layernorm_backward input gradient for (dy, h, mean, rstd, weight):
+ *   dh        = dresidual + dx_ln    (the gradient of residual, and of h)
+ *   da        = dh * scale * mask    (the gradient of a)
+ *   dbias_in  = sum over rows of da  (the gradient of bias)
+ *   dweight, dbias                    as layernorm_backward.
+ *
+ *   dy            [rows, cols] of dy_t;   x [rows, cols] of x_t: h
+ *   mean, rstd    fp32 [rows], saved by the forward for h
+ *   weight        [cols] of w_t, or NULL (weight = 1)
+ *   dresidual     fp32 [rows, cols], the gradient reaching h from its other
+ *                 consumers, or NULL (zero)
+ *   mask          [rows, cols] bytes, nonzero = kept, or NULL (all kept)
+ *   scale         dropout scale, finite (typically 1/(1 - p))
+ *   dh            fp32 [rows, cols] out, or NULL (skip)
+ *   da            [rows, cols] of dy_t out, or NULL (skip)
+ *   dweight, dbias, dbias_in   [cols] of w_t out, each may be NULL (skip)
+ * dy_t, x_t, w_t are NH_F32 or NH_BF16 in any combination.  dh and da may
+ * not alias any input.
+ */
+nh_status bda_layernorm_backward(const void *dy, nh_dtype dy_t,
+                                 const void *x, nh_dtype x_t,
+                                 const float *mean, const float *rstd,
+                                 const void *weight, nh_dtype w_t,
+                                 const float *dresidual, const uint8_t *mask, float scale,
+                                 int64_t rows, int64_t cols,
+                                 float *dh, void *da,
+                                 void *dweight, void *dbias, void *dbias_in,
+                                 void *ws, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------------------
  * LayerNorm / RMSNorm training forward over the last dimension of
  * [rows, cols]: the forwards whose saved statistics the backwards above take.
@@ -308,7 +348,9 @@ typedef enum {
     NH_K_LN_FWD = 11,         /* LayerNorm forward row pass */
     NH_K_RMS_FWD = 12,        /* RMSNorm forward row pass */
     NH_K_BN_INFER = 13,       /* BatchNorm inference apply */
-    NH_K_COUNT = 14
+    NH_K_BDA_ROWS = 14,       /* bias+dropout+add+LayerNorm backward row pass */
+    NH_K_BDA_COLSUM = 15,     /* its dweight/dbias/dbias_in finalize */
+    NH_K_COUNT = 16
 } nh_kernel;
 
 /* Static name of a kernel id; "" for an unknown id. */

@@ -43,8 +43,8 @@ def test_status_and_kernel_names():
         "NH_OK", "NH_ERR_NULL", "NH_ERR_SHAPE", "NH_ERR_DTYPE", "NH_ERR_WORKSPACE",
         "NH_ERR_HIP", "NH_ERR_ARG"]
     assert nh.status_string(99) == "NH_ERR_UNKNOWN"
-    assert [nh.lib.nh_kernel_name(i).decode() for i in range(14)] == nh.KERNELS
-    assert nh.lib.nh_kernel_name(14).decode() == ""
+    assert [nh.lib.nh_kernel_name(i).decode() for i in range(16)] == nh.KERNELS
+    assert nh.lib.nh_kernel_name(16).decode() == ""
 
 
 def bn_fwd(x=FAKE, y=FAKE, io=0, N=2, C=3, HW=4, rm=NULL, rv=NULL, eps=1e-5, mom=0.1,
@@ -122,6 +122,29 @@ def test_bn_act_and_infer_validation():
     assert fi(FAKE, FAKE, 2, 2, 3, 4, NULL, NULL, FAKE, FAKE, 1e-5, 0, 0.0, NULL) == NH_ERR_DTYPE
     assert fi(FAKE, FAKE, 0, 2, 3, 1 << 31, NULL, NULL, FAKE, FAKE, 1e-5, 0, 0.0, NULL) == NH_ERR_SHAPE
     assert fi(NULL, NULL, 0, 2, 0, 4, NULL, NULL, NULL, NULL, 1e-5, 0, 0.0, NULL) == NH_OK
+
+
+def test_bda_validation():
+    f = nh.lib.bda_layernorm_backward
+    # dy, dy_t, x, x_t, mean, rstd, w, w_t, dres, mask, scale, rows, cols, dh, da, dw, db, dbi,
+    # ws, ws_bytes, stream
+    def call(dy=FAKE, dyt=1, x=FAKE, xt=0, mean=FAKE, rstd=FAKE, wt=1, scale=1.1, rows=4, cols=8):
+        return f(dy, dyt, x, xt, mean, rstd, FAKE, wt, FAKE, FAKE, scale, rows, cols, FAKE, FAKE, FAKE,
+                 FAKE, FAKE, FAKE, 1 << 20, NULL)
+    assert call(dyt=2) == NH_ERR_DTYPE
+    assert call(wt=-1) == NH_ERR_DTYPE
+    assert call(rows=-1) == NH_ERR_SHAPE
+    assert call(rows=1 << 16, cols=1 << 15) == NH_ERR_SHAPE
+    assert call(dy=NULL) == NH_ERR_NULL
+    assert call(rstd=NULL) == NH_ERR_NULL
+    assert call(scale=float("nan")) == NH_ERR_ARG
+    assert "scale" in nh.last_error()
+    assert call(scale=float("-inf")) == NH_ERR_ARG
+    assert call(dy=NULL, x=NULL, mean=NULL, rstd=NULL, cols=0) == NH_OK
+    ws = ctypes.c_size_t(7)
+    assert nh.lib.bda_layernorm_backward_workspace(0, 5, ctypes.byref(ws)) == NH_OK and ws.value == 0
+    assert nh.lib.bda_layernorm_backward_workspace(-1, 5, ctypes.byref(ws)) == NH_ERR_SHAPE
+    assert nh.lib.bda_layernorm_backward_workspace(3, 5, None) == NH_ERR_NULL
 
 
 def test_rows_validation():
