@@ -436,6 +436,10 @@ PROFILE_CMD_TRACE = ("rocprofv3 --kernel-trace --stats -f csv --kernel-include-r
 PROFILE_CMD_PMC = ("rocprofv3 --pmc {counter} -f csv --kernel-include-regex \"nh::\" -d <dir> "
                    "-o bench_quick -- python3 bench.py --quick --steps 5 --warmup 2 --no-cpu-baseline")
 BN_SOURCES = ["bn_kernels.hip", "nh_device.hpp", "nh_internal.hpp"]
+PROFILE_CMD_ALL_TRACE = ("rocprofv3 --kernel-trace --stats -f csv -d <dir> -o bench_all -- "
+                         "python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline")
+PROFILE_CMD_ALL_PMC = ("rocprofv3 --pmc {counter} -f csv --kernel-include-regex \"nh::\" -d <dir> "
+                       "-o bench_all -- python3 bench.py --steps 4 --warmup 1 --no-cpu-baseline")
 
 
 def _short_kernel(name):
@@ -518,6 +522,59 @@ def summarize_counters(fetch_csv, write_csv, out_dir):
         open(os.path.join(out_dir, f"{tag}_bn_cifar_f32_counters.txt"), "w").write(text + "\n")
 
 
+def summarize_all(trace_csv, fetch_csv, write_csv, out_path):
+    """Every normhip kernel of a full bench.py run, one line per (kernel,
+    grid): dispatches and mean duration from the kernel trace, and HBM-side
+    bytes per dispatch from FETCH_SIZE / WRITE_SIZE scaled by the calibration
+    add of known size.  Lines follow the order of the bench's workloads."""
+    import collections
+    import csv
+
+    def grid_blocks(r, x_key, wg_key):
+        return int(float(r[x_key])) // max(1, int(float(r[wg_key])))
+
+    trace = collections.OrderedDict()
+    for r in csv.DictReader(open(trace_csv)):
+        name = _short_kernel(r["Kernel_Name"])
+        if not name.startswith("nh::"):
+            continue
+        key = (name, grid_blocks(r, "Grid_Size_X", "Workgroup_Size_X") * int(r["Grid_Size_Y"]))
+        trace.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+
+    def counters(path):
+        d = collections.OrderedDict()
+        for r in csv.DictReader(open(path)):
+            key = (_short_kernel(r["Kernel_Name"]), int(float(r["Grid_Size"])) // max(1, int(r["Workgroup_Size"])))
+            d.setdefault(key, []).append(float(r["Counter_Value"]))
+        return d
+
+    f, w = counters(fetch_csv), counters(write_csv)
+    n = 256 * 32 * 32 * 32
+    calib = next(k for k in f if "calib_add4" in k[0])
+    fscale = (2 * n * 4) / (sum(f[calib]) / len(f[calib]) * 1024)
+    wscale = (n * 4) / (sum(w[calib]) / len(w[calib]) * 1024)
+    lines = ["# normhip kernels over every bench.py workload (MI355X): duration and HBM-side traffic",
+             f"command_trace: {PROFILE_CMD_ALL_TRACE}",
+             f"command_fetch: {PROFILE_CMD_ALL_PMC.format(counter='FETCH_SIZE')}",
+             f"command_write: {PROFILE_CMD_ALL_PMC.format(counter='WRITE_SIZE')}",
+             "summarized by: python bench.py --summarize-all <trace_dir>/bench_all_kernel_trace.csv "
+             "<fetch_dir>/bench_all_counter_collection.csv <write_dir>/bench_all_counter_collection.csv",
+             f"fetch_scale: {fscale:.5f} (FETCH_SIZE of the calibration add vs its known reads)",
+             f"write_scale: {wscale:.5f}",
+             "note: FETCH_SIZE counts L2 misses served by the data fabric, so reads served by the "
+             "256 MB Infinity Cache are included",
+             "note: the BatchNorm (256,32,32,32) fp32 lines average its cold and warm steps; every "
+             "other workload runs cold only",
+             "",
+             f"{'kernel':64s} {'blocks':>7s} {'calls':>6s} {'avg_us':>8s} {'read_MB':>9s} {'write_MB':>9s}"]
+    for key, durs in trace.items():
+        fk, wk = f.get(key), w.get(key)
+        rd = f"{sum(fk) / len(fk) * 1024 * fscale / 1e6:9.2f}" if fk else f"{'-':>9s}"
+        wr = f"{sum(wk) / len(wk) * 1024 * wscale / 1e6:9.2f}" if wk else f"{'-':>9s}"
+        lines.append(f"{key[0][:64]:64s} {key[1]:7d} {len(durs):6d} {sum(durs) / len(durs):8.2f} {rd} {wr}")
+    open(out_path, "w").write("\n".join(lines) + "\n")
+
+
 def _traffic_for(kernel_name, workload_tag):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel source (else None)."""
@@ -551,7 +608,12 @@ def main():
                     help="write profiles/ summary of a rocprofv3 --stats run and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/ traffic summaries of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-all", nargs=3, metavar=("TRACE_CSV", "FETCH_CSV", "WRITE_CSV"),
+                    help="write the profiles/ summary of every kernel of a full run and exit")
     args = ap.parse_args()
+    if args.summarize_all:
+        summarize_all(*args.summarize_all, os.path.join(ROOT, "profiles", "norm_kernels_all_workloads.txt"))
+        return
     if args.summarize_trace or args.summarize_counters:
         os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
         if args.summarize_trace:
