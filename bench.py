@@ -279,8 +279,7 @@ def bench_rows(nh, torch, case, kind, K, W, cold=True, saved=True):
     del sets, calls
     torch.cuda.empty_cache()
     return {"ms_per_call": ms, "us_per_call": 1000.0 * ms, "bytes": row_bytes,
-            "gbs": row_bytes / (ms * 1e6), "buffer_sets": R, "kernels": per, "blocks": G,
-            "partials_bytes_written": G * H * 4 * (2 if kind == "ln" else 1)}
+            "gbs": row_bytes / (ms * 1e6), "buffer_sets": R, "kernels": per, "blocks_max": G}
 
 
 def bench_bda(nh, torch, case, K, W, cold=True):
@@ -333,8 +332,7 @@ def bench_bda(nh, torch, case, K, W, cold=True):
     del sets, calls
     torch.cuda.empty_cache()
     return {"ms_per_call": ms, "us_per_call": 1000.0 * ms, "bytes": row_bytes,
-            "gbs": row_bytes / (ms * 1e6), "buffer_sets": R, "kernels": per, "blocks": G,
-            "partials_bytes_written": G * H * 4 * 3}
+            "gbs": row_bytes / (ms * 1e6), "buffer_sets": R, "kernels": per, "blocks_max": G}
 
 
 def bench_rows_fwd(nh, torch, case, kind, K, W, cold=True):

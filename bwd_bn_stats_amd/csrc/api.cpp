@@ -87,6 +87,7 @@ nh_status device_info(DeviceInfo *out)
 std::atomic<int64_t> g_override_bn_grid_y{0};
 std::atomic<int64_t> g_override_rows_blocks{0};
 std::atomic<int64_t> g_override_bn_finalize_kernels{0};
+std::atomic<int64_t> g_override_rows_depth{0};
 
 // ---- BatchNorm planning ----------------------------------------------------------
 // Resident 256-thread block slots of the device: CUs * (threads per CU / 256),
@@ -176,13 +177,13 @@ RowsPlan rows_variant(int64_t cols, int vec, bool vec_ok, int max_elems = kRowsM
 }
 
 // Blocks: as many as fit on the device at once (occupancy of the chosen
-// variant, at most kRowsMaxBlocksPerCu per CU), at most one per row.
+// variant, at most rows_blocks_per_cu(kind) per CU), at most one per row.
 // Measured on MI355X: single-team blocks beat fewer, wider blocks that
 // synchronize more waves per row.
-void rows_grid(RowsPlan &p, int64_t rows, int occ, const DeviceInfo &d)
+void rows_grid(RowsPlan &p, int kind, int64_t rows, int occ, const DeviceInfo &d)
 {
     if (occ < 1) occ = 1;
-    if (occ > kRowsMaxBlocksPerCu) occ = kRowsMaxBlocksPerCu;
+    if (occ > rows_blocks_per_cu(kind)) occ = rows_blocks_per_cu(kind);
     int64_t g = (int64_t)d.cus * occ;
     const int64_t ov = g_override_rows_blocks.load();
     if (ov > 0) g = ov;
@@ -495,12 +496,13 @@ static nh_status rows_run(RowsCall &a, int Q, void *ws, size_t ws_bytes, void *s
     a.maxg = p.maxg;
     a.vec = p.vec;
     a.teams = p.teams;
+    a.depth = (int)g_override_rows_depth.load();
     // Occupancy of the chosen variant, cached per device and variant.
     int dev = 0;
     (void)hipGetDevice(&dev);
     const int dxt = a.dx != nullptr ? a.dx_t : a.dy_t;
-    const int64_t key = ((((((int64_t)dev * 4 + a.kind) * 2 + a.x_t) * 2 + a.dy_t) * 2 + dxt) * 16 +
-                         a.maxg) * 16 + a.vec;
+    const int64_t key = (((((((int64_t)dev * 4 + a.kind) * 2 + a.x_t) * 2 + a.dy_t) * 2 + dxt) * 16 +
+                          a.maxg) * 16 + a.vec) * 8 + a.depth;
     int occ = 0;
     {
         std::lock_guard<std::mutex> lk(g_dev_mu);
@@ -516,7 +518,7 @@ static nh_status rows_run(RowsCall &a, int Q, void *ws, size_t ws_bytes, void *s
         std::lock_guard<std::mutex> lk(g_dev_mu);
         g_rows_occupancy[key] = occ;
     }
-    rows_grid(p, a.rows, occ, d);
+    rows_grid(p, a.kind, a.rows, occ, d);
     a.blocks = p.blocks;
     e = rows_backward_launch(a, s);
     if (e != hipSuccess) return hip_fail(e, "rows backward launch");
@@ -654,9 +656,11 @@ static nh_status rows_forward_run(FwdCall &a, void *stream)
     RowsPlan p = rows_variant(a.cols, a.vec, vec_ok);
     a.maxg = p.maxg;
     a.vec = p.vec;
+    a.depth = (int)g_override_rows_depth.load();
     int dev = 0;
     (void)hipGetDevice(&dev);
-    const int64_t key = -1 - (((((((int64_t)dev * 2 + a.kind) * 2 + a.x_t) * 2 + a.y_t) * 16 + a.maxg) * 16) + a.vec);
+    const int64_t key = -1 - ((((((((int64_t)dev * 2 + a.kind) * 2 + a.x_t) * 2 + a.y_t) * 16 + a.maxg) * 16) +
+                               a.vec) * 8 + a.depth);
     int occ = 0;
     {
         std::lock_guard<std::mutex> lk(g_dev_mu);
@@ -837,6 +841,10 @@ nh_status nh_plan_override(const char *key, int64_t value)
     if (value < 0) return fail(NH_ERR_ARG, "value must be >= 0");
     if (strcmp(key, "bn_grid_y") == 0) g_override_bn_grid_y.store(value);
     else if (strcmp(key, "rows_blocks") == 0) g_override_rows_blocks.store(value);
+    else if (strcmp(key, "rows_depth") == 0) {
+        if (value < 0 || value > 4) return fail(NH_ERR_ARG, "rows_depth must be 0..4");
+        g_override_rows_depth.store(value);
+    }
     else if (strcmp(key, "bn_finalize_kernels") == 0) g_override_bn_finalize_kernels.store(value);
     else return fail(NH_ERR_ARG, "unknown override key '%s'", key);
     return ok();

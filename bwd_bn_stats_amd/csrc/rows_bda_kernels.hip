@@ -39,8 +39,8 @@ struct MaskGroup {
     }
 };
 
-template <typename TX, typename TDY, int VEC, int MAXG, int MAXT, bool PF>
-__global__ void __launch_bounds__(MAXT)
+template <typename TX, typename TDY, int VEC, int MAXG, int MAXT, int D>
+__global__ void __launch_bounds__(MAXT, kRowsBwdWavesPerSimd)
 bda_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
                 const float *__restrict__ mean, const float *__restrict__ rstd,
                 const void *__restrict__ w, int w_bf16, const float *__restrict__ dres,
@@ -147,23 +147,7 @@ bda_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
         }
     };
 
-    RowBuf ba;
-    if constexpr (PF) {
-        RowBuf bb;
-        load_row(ba, 0);
-        for (int it = 0; it < iters; it += 2) {
-            load_row(bb, it + 1);
-            do_row(ba, it);
-            if (it + 1 >= iters) break;
-            load_row(ba, it + 2);
-            do_row(bb, it + 1);
-        }
-    } else {
-        for (int it = 0; it < iters; ++it) {
-            load_row(ba, it);
-            do_row(ba, it);
-        }
-    }
+    pipeline_rows<D, RowBuf>(iters, load_row, do_row);
     if (want_cols) fold_and_write<VEC, MAXG, 3>(p, slot, teams, team, tt, Gr, H, G, partials);
 }
 
@@ -225,12 +209,11 @@ bda_generic_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
 }
 
 // ---- host dispatch ---------------------------------------------------------------
-template <typename TX, typename TDY, int VEC, int MAXG>
-static hipError_t bda_vec(const RowsCall &a, hipStream_t s)
+template <typename TX, typename TDY, int VEC, int MAXG, int D>
+static hipError_t bda_vec_d(const RowsCall &a, hipStream_t s)
 {
-    constexpr int MT = rows_max_threads(MAXG, VEC);
-    constexpr bool PF = MAXG * VEC <= 16;
-    auto kern = bda_rows_kernel<TX, TDY, VEC, MAXG, MT, PF>;
+    constexpr int MT = kTeam;
+    auto kern = bda_rows_kernel<TX, TDY, VEC, MAXG, MT, D>;
     if (a.occupancy_out)
         return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kern, kTeam,
                                                             (size_t)rows_lds_bytes(a));
@@ -239,6 +222,19 @@ static hipError_t bda_vec(const RowsCall &a, hipStream_t s)
                   static_cast<const TX *>(a.x), a.mean, a.rstd, a.w, a.w_t, a.dresidual, a.mask,
                   a.scale, a.rows, a.cols, a.dh, static_cast<TDY *>(a.dx), a.partials,
                   (int)(a.dweight != nullptr || a.dbias != nullptr || a.dbias_in != nullptr));
+}
+
+template <typename TX, typename TDY, int VEC, int MAXG>
+static hipError_t bda_vec(const RowsCall &a, hipStream_t s)
+{
+    // Row buffer: x, dy, the fp32 incoming gradient and the mask byte.
+    constexpr int DEF = rows_depth(MAXG * VEC * (int)(sizeof(TX) + sizeof(TDY) + 5));
+    switch (a.depth > 0 ? a.depth : DEF) {
+    case 1: return bda_vec_d<TX, TDY, VEC, MAXG, 1>(a, s);
+    case 2: return bda_vec_d<TX, TDY, VEC, MAXG, 2>(a, s);
+    case 3: return bda_vec_d<TX, TDY, VEC, MAXG, 3>(a, s);
+    default: return bda_vec_d<TX, TDY, VEC, MAXG, 4>(a, s);
+    }
 }
 
 template <typename TX, typename TDY>

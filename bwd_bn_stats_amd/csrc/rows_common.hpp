@@ -57,6 +57,40 @@ __device__ __forceinline__ void team_sum2(float *red, int team, int wave, int la
     b = sb;
 }
 
+// Software-pipelined walk over a team's rows with D row buffers in
+// registers: while row i is reduced and written, the loads of rows i+1 ..
+// i+D-1 are in flight.  Buffers rotate by unrolling, so each stays in fixed
+// registers.  load_row(buf, it) must be branch-free and accept any it (rows
+// past the end load nothing); do_row(buf, it) handles row iteration it.
+template <int D, typename RowBuf, typename Load, typename Do>
+__device__ __forceinline__ void pipeline_rows(int iters, Load &&load_row, Do &&do_row)
+{
+    RowBuf buf[D];
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) load_row(buf[d], d);
+    for (int it = 0; it < iters; it += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (it + d >= iters) return;
+            load_row(buf[(d + D - 1) % D], it + d + D - 1);
+            do_row(buf[d], it + d);
+        }
+    }
+}
+
+// Default pipeline depth of a backward row kernel (2 waves per SIMD) from
+// the bytes of one row buffer per thread.  Measured on MI355X: LayerNorm at
+// 1600 columns (48 B) is best at 3, RMSNorm at 8192 columns (128 B bf16,
+// 256 B fp32) and the bias+dropout+add backward (88 B) at 2; deeper
+// pipelines gain nothing and cost registers.
+constexpr int rows_depth(int row_bytes_per_thread)
+{
+    return row_bytes_per_thread <= 32 ? 4 : (row_bytes_per_thread <= 64 ? 3 : (row_bytes_per_thread <= 256 ? 2 : 1));
+}
+// The forward kernels run up to 8 blocks per CU, so many rows are in flight
+// per CU already: depth 2 measured best (LayerNorm 1600, RMSNorm 8192).
+constexpr int kFwdDepth = 2;
+
 // Folds the teams' column sums into team 0 in team order (slot: Q*H floats),
 // then team 0 writes the block's partial row.
 template <int VEC, int MAXG, int Q>

@@ -36,7 +36,7 @@ struct ParamGroup {
 };
 
 // KIND 0: LayerNorm (stat0 = mean, stat1 = rstd); KIND 1: RMSNorm (stat0 = rms).
-template <int KIND, typename TX, typename TY, int VEC, int MAXG, int MT, bool PF>
+template <int KIND, typename TX, typename TY, int VEC, int MAXG, int MT, int D>
 __global__ void __launch_bounds__(MT)
 norm_fwd_rows_kernel(const TX *__restrict__ x, const void *__restrict__ w,
                      const void *__restrict__ b, int w_bf16, int rows, int H, float eps,
@@ -133,23 +133,7 @@ norm_fwd_rows_kernel(const TX *__restrict__ x, const void *__restrict__ w,
         }
     };
 
-    RowBuf ra;
-    if constexpr (PF) {
-        RowBuf rb;
-        load_row(ra, 0);
-        for (int it = 0; it < iters; it += 2) {
-            load_row(rb, it + 1);
-            do_row(ra, it);
-            if (it + 1 >= iters) break;
-            load_row(ra, it + 2);
-            do_row(rb, it + 1);
-        }
-    } else {
-        for (int it = 0; it < iters; ++it) {
-            load_row(ra, it);
-            do_row(ra, it);
-        }
-    }
+    pipeline_rows<D, RowBuf>(iters, load_row, do_row);
 }
 
 // Any width, any alignment: scalar accesses, two reads of the row (the second
@@ -213,17 +197,27 @@ norm_fwd_generic_kernel(const TX *__restrict__ x, const void *__restrict__ w,
 }
 
 // ---- host dispatch ------------------------------------------------------------------
-template <int KIND, typename TX, typename TY, int VEC, int MAXG>
-static hipError_t fwd_vec(const FwdCall &a, hipStream_t s)
+template <int KIND, typename TX, typename TY, int VEC, int MAXG, int D>
+static hipError_t fwd_vec_d(const FwdCall &a, hipStream_t s)
 {
     constexpr int MT = rows_max_threads(MAXG, VEC);
-    constexpr bool PF = MAXG * VEC * (int)sizeof(TX) <= 64;
-    auto kern = norm_fwd_rows_kernel<KIND, TX, TY, VEC, MAXG, MT, PF>;
+    auto kern = norm_fwd_rows_kernel<KIND, TX, TY, VEC, MAXG, MT, D>;
     if (a.occupancy_out)
         return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kern, kTeam, 0);
     return launch(KIND == 0 ? NH_K_LN_FWD : NH_K_RMS_FWD, kern, dim3(a.blocks), dim3(kTeam), 0u, s,
                   static_cast<const TX *>(a.x), a.w, a.b, a.w_t, a.rows, a.cols, a.eps,
                   static_cast<TY *>(a.y), a.stat0, a.stat1);
+}
+
+template <int KIND, typename TX, typename TY, int VEC, int MAXG>
+static hipError_t fwd_vec(const FwdCall &a, hipStream_t s)
+{
+    switch (a.depth > 0 ? a.depth : kFwdDepth) {
+    case 1: return fwd_vec_d<KIND, TX, TY, VEC, MAXG, 1>(a, s);
+    case 2: return fwd_vec_d<KIND, TX, TY, VEC, MAXG, 2>(a, s);
+    case 3: return fwd_vec_d<KIND, TX, TY, VEC, MAXG, 3>(a, s);
+    default: return fwd_vec_d<KIND, TX, TY, VEC, MAXG, 4>(a, s);
+    }
 }
 
 template <int KIND, typename TX, typename TY>

@@ -35,12 +35,12 @@
 namespace nh {
 
 // ---- LayerNorm, vector path ----------------------------------------------------
-// PF: software-pipelined rows.  While a team reduces and writes row i, the
-// loads of its row i+1 are already in flight (two register sets, used
-// alternately), so each team keeps two rows of HBM traffic outstanding
+// D: software-pipeline depth.  While a team reduces and writes row i, the
+// loads of its rows i+1 .. i+D-1 are already in flight (D register sets,
+// used in rotation), so each team keeps D rows of HBM traffic outstanding
 // across the block barrier of the row sum.
-template <typename TX, typename TDY, typename TDX, int VEC, int MAXG, int MAXT, bool PF>
-__global__ void __launch_bounds__(MAXT)
+template <typename TX, typename TDY, typename TDX, int VEC, int MAXG, int MAXT, int D>
+__global__ void __launch_bounds__(MAXT, kRowsBwdWavesPerSimd)
 ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
                const float *__restrict__ mean, const float *__restrict__ rstd,
                const void *__restrict__ w, int w_bf16, int rows, int H,
@@ -140,30 +140,13 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
         }
     };
 
-    RowBuf ba;
-    if constexpr (PF) {
-        RowBuf bb;
-        // Prefetches past the last row are empty buffer loads: no branch.
-        load_row(ba, 0);
-        for (int it = 0; it < iters; it += 2) {
-            load_row(bb, it + 1);
-            do_row(ba, it);
-            if (it + 1 >= iters) break;
-            load_row(ba, it + 2);
-            do_row(bb, it + 1);
-        }
-    } else {
-        for (int it = 0; it < iters; ++it) {
-            load_row(ba, it);
-            do_row(ba, it);
-        }
-    }
+    pipeline_rows<D, RowBuf>(iters, load_row, do_row);
     if (want_cols) fold_and_write<VEC, MAXG, 2>(p, slot, teams, team, tt, Gr, H, G, partials);
 }
 
 // ---- RMSNorm, vector path ----------------------------------------------------
-template <typename T, int VEC, int MAXG, int MAXT, bool PF>
-__global__ void __launch_bounds__(MAXT)
+template <typename T, int VEC, int MAXG, int MAXT, int D>
+__global__ void __launch_bounds__(MAXT, kRowsBwdWavesPerSimd)
 rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
                 const float *__restrict__ rms, float eps, const void *__restrict__ w,
                 int w_bf16, int rows, int H, T *__restrict__ dx,
@@ -256,24 +239,7 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
         }
     };
 
-    RowBuf ba;
-    if constexpr (PF) {
-        RowBuf bb;
-        // Prefetches past the last row are empty buffer loads: no branch.
-        load_row(ba, 0);
-        for (int it = 0; it < iters; it += 2) {
-            load_row(bb, it + 1);
-            do_row(ba, it);
-            if (it + 1 >= iters) break;
-            load_row(ba, it + 2);
-            do_row(bb, it + 1);
-        }
-    } else {
-        for (int it = 0; it < iters; ++it) {
-            load_row(ba, it);
-            do_row(ba, it);
-        }
-    }
+    pipeline_rows<D, RowBuf>(iters, load_row, do_row);
     if (want_cols) fold_and_write<VEC, MAXG, 1>(p, slot, teams, team, tt, Gr, H, G, partials);
 }
 
@@ -400,30 +366,52 @@ static hipError_t occupancy(const RowsCall &a, K kernel)
                                                         (size_t)rows_lds_bytes(a));
 }
 
-template <typename TX, typename TDY, typename TDX, int VEC, int MAXG>
-static hipError_t ln_vec(const RowsCall &a, hipStream_t s)
+template <typename TX, typename TDY, typename TDX, int VEC, int MAXG, int D>
+static hipError_t ln_vec_d(const RowsCall &a, hipStream_t s)
 {
-    constexpr int MT = rows_max_threads(MAXG, VEC);
-    constexpr bool PF = MAXG * VEC <= 16;
-    if (a.occupancy_out) return occupancy(a, ln_rows_kernel<TX, TDY, TDX, VEC, MAXG, MT, PF>);
-    return launch(NH_K_LN_ROWS, ln_rows_kernel<TX, TDY, TDX, VEC, MAXG, MT, PF>, dim3(a.blocks),
-                  dim3(a.teams * kTeam), (uint32_t)rows_lds_bytes(a), s,
+    constexpr int MT = kTeam;
+    auto kern = ln_rows_kernel<TX, TDY, TDX, VEC, MAXG, MT, D>;
+    if (a.occupancy_out) return occupancy(a, kern);
+    return launch(NH_K_LN_ROWS, kern, dim3(a.blocks), dim3(a.teams * kTeam), (uint32_t)rows_lds_bytes(a), s,
                   static_cast<const TDY *>(a.dy), static_cast<const TX *>(a.x), a.mean, a.rstd,
                   a.w, a.w_t, a.rows, a.cols, static_cast<TDX *>(a.dx), a.partials,
                   (int)(a.dweight != nullptr || a.dbias != nullptr));
 }
 
-template <typename T, int VEC, int MAXG>
-static hipError_t rms_vec(const RowsCall &a, hipStream_t s)
+template <typename TX, typename TDY, typename TDX, int VEC, int MAXG>
+static hipError_t ln_vec(const RowsCall &a, hipStream_t s)
 {
-    constexpr int MT = rows_max_threads(MAXG, VEC);
-    constexpr bool PF = MAXG * VEC * (int)sizeof(T) <= 64;
-    if (a.occupancy_out) return occupancy(a, rms_rows_kernel<T, VEC, MAXG, MT, PF>);
-    return launch(NH_K_RMS_ROWS, rms_rows_kernel<T, VEC, MAXG, MT, PF>, dim3(a.blocks),
-                  dim3(a.teams * kTeam), (uint32_t)rows_lds_bytes(a), s,
+    constexpr int DEF = rows_depth(MAXG * VEC * (int)(sizeof(TX) + sizeof(TDY)));
+    switch (a.depth > 0 ? a.depth : DEF) {
+    case 1: return ln_vec_d<TX, TDY, TDX, VEC, MAXG, 1>(a, s);
+    case 2: return ln_vec_d<TX, TDY, TDX, VEC, MAXG, 2>(a, s);
+    case 3: return ln_vec_d<TX, TDY, TDX, VEC, MAXG, 3>(a, s);
+    default: return ln_vec_d<TX, TDY, TDX, VEC, MAXG, 4>(a, s);
+    }
+}
+
+template <typename T, int VEC, int MAXG, int D>
+static hipError_t rms_vec_d(const RowsCall &a, hipStream_t s)
+{
+    constexpr int MT = kTeam;
+    auto kern = rms_rows_kernel<T, VEC, MAXG, MT, D>;
+    if (a.occupancy_out) return occupancy(a, kern);
+    return launch(NH_K_RMS_ROWS, kern, dim3(a.blocks), dim3(a.teams * kTeam), (uint32_t)rows_lds_bytes(a), s,
                   static_cast<const T *>(a.dy), static_cast<const T *>(a.x), a.rms, a.eps, a.w,
                   a.w_t, a.rows, a.cols, static_cast<T *>(a.dx), a.partials,
                   (int)(a.dweight != nullptr));
+}
+
+template <typename T, int VEC, int MAXG>
+static hipError_t rms_vec(const RowsCall &a, hipStream_t s)
+{
+    constexpr int DEF = rows_depth(MAXG * VEC * 2 * (int)sizeof(T));
+    switch (a.depth > 0 ? a.depth : DEF) {
+    case 1: return rms_vec_d<T, VEC, MAXG, 1>(a, s);
+    case 2: return rms_vec_d<T, VEC, MAXG, 2>(a, s);
+    case 3: return rms_vec_d<T, VEC, MAXG, 3>(a, s);
+    default: return rms_vec_d<T, VEC, MAXG, 4>(a, s);
+    }
 }
 
 // The widest vector variant holds 32 row elements per thread (MAXG = 8 only

@@ -403,8 +403,10 @@ nh_status nh_rows_plan(int64_t rows, int64_t cols, int *blocks);
  * block count (at most 2048 and at most one per row; both keys also size
  * the workspace queried afterwards), key
  * "bn_finalize_kernels" = 1 runs the BatchNorm finalize steps as separate
- * kernels instead of inside the elementwise kernels (same results).  value 0
- * restores the automatic plan.  Process-wide; not for concurrent use with
+ * kernels instead of inside the elementwise kernels (same results), key
+ * "rows_depth" = 1..4 forces the number of rows a row-kernel team keeps in
+ * flight (its software-pipeline depth; same results).  value 0 restores the
+ * automatic plan.  Process-wide; not for concurrent use with
  * other calls.
  */
 nh_status nh_plan_override(const char *key, int64_t value);

@@ -161,3 +161,12 @@ def test_bda_bit_identical_runs(nh, oracle_mod):
     for u, v in zip(a, b):
         iv = torch.int16 if u.dtype == torch.bfloat16 else torch.int32
         assert torch.equal(u.view(iv), v.view(iv))
+
+
+@pytest.mark.parametrize("depth", [1, 2, 3, 4])
+def test_bda_pipeline_depths(nh, oracle_mod, depth):
+    nh.plan_override("rows_depth", depth)
+    try:
+        _bda_case(nh, oracle_mod, wl.bda_case(1037, 1600, seed=87), override_blocks=100)
+    finally:
+        nh.plan_override("rows_depth", 0)

@@ -156,3 +156,15 @@ def test_forwards_bit_identical_runs(nh):
     for u, v in list(zip(a, bb)) + list(zip(ra, rb)):
         iv = torch.int16 if u.dtype == torch.bfloat16 else torch.int32
         assert torch.equal(u.view(iv), v.view(iv))
+
+
+@pytest.mark.parametrize("depth", [1, 2, 3, 4])
+def test_forward_pipeline_depths(nh, oracle_mod, depth):
+    nh.plan_override("rows_depth", depth)
+    try:
+        c = wl.rows_case(1037, 1600, x_t=wl.F32, dy_t=wl.BF16, w_t=wl.BF16, seed=75, with_bias=True)
+        _ln_fwd_case(nh, oracle_mod, c, wl.F32)
+        _rms_fwd_case(nh, oracle_mod, wl.rows_case(333, 4096, x_t=wl.BF16, dy_t=wl.BF16, w_t=wl.BF16,
+                                                    seed=76))
+    finally:
+        nh.plan_override("rows_depth", 0)

@@ -205,3 +205,18 @@ def test_rows_error_paths(nh):
     with pytest.raises(nh.NormHipError) as ei:
         nh.rmsnorm_backward(x, x, None, None, workspace=torch.empty(4, dtype=torch.uint8, device="cuda"))
     assert ei.value.status == 4
+
+
+@pytest.mark.parametrize("depth", [1, 2, 3, 4])
+def test_rows_pipeline_depths(nh, oracle_mod, depth):
+    """Every row-pipeline depth of the vector kernels (forced through the
+    plan override) gives the oracle's results, for rows that do not divide
+    evenly among the teams."""
+    nh.plan_override("rows_depth", depth)
+    try:
+        c = wl.rows_case(1037, 1600, x_t=wl.F32, dy_t=wl.BF16, w_t=wl.BF16, seed=91)
+        _ln_case(nh, oracle_mod, c, wl.F32, override_blocks=100)
+        r = wl.rows_case(333, 4096, x_t=wl.BF16, dy_t=wl.BF16, w_t=wl.BF16, seed=92)
+        _rms_case(nh, oracle_mod, r, saved=True, override_blocks=50)
+    finally:
+        nh.plan_override("rows_depth", 0)
