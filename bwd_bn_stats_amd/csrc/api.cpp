@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <map>
 #include <mutex>
@@ -883,6 +884,44 @@ nh_status nh_selftest_host(void)
             if (u >= cap * kBnThreads * kBnUnroll && g != cap)
                 return fail(NH_ERR_ARG, "bn grid underfills: %lld", (long long)g);
         }
+    // BatchNorm unit walk at the largest shapes the ABI accepts: for every
+    // block, the unsigned loop index (up to a stride past the block's last
+    // unit) must not wrap, and the first and last unit of every block (of the
+    // first and last channel) must map inside the tensor, at the offset the
+    // plain division gives.
+    struct MaxShape { int N, C, HW, vec; };
+    const MaxShape shapes[] = {
+        {1, 1, 0x7fffffff, 1},                 // one channel of 2^31 - 1 elements, scalar units
+        {1, 2, 0x3fffffff, 1},                 // 2 channels, odd planes
+        {2, 4, (1 << 28) - 8, 8},              // bf16 vector units
+        {2, 4, (1 << 28) - 8, 4},              // fp32 vector units
+        {16384, 3, 43690, 1},                  // many planes per channel
+    };
+    for (const MaxShape &m : shapes) {
+        const int64_t total = (int64_t)m.N * m.C * m.HW;
+        if (total >= kMaxElems) return fail(NH_ERR_ARG, "max shape exceeds the element limit");
+        const int64_t units = (int64_t)m.N * (m.HW / m.vec);
+        const int grid_y = (int)bn_auto_grid_y(units, m.C, slots);
+        const BnGeom g = make_bn_geom(m.N, m.C, m.HW, m.vec, grid_y);
+        const uint64_t stride = (uint64_t)kBnThreads * kBnUnroll;
+        for (int c = 0; c < m.C; c += (m.C > 1 ? m.C - 1 : 1)) {
+            for (int yb = 0; yb < g.grid_y; ++yb) {
+                const uint64_t u0 = (uint64_t)yb * (uint64_t)g.upb;
+                const uint64_t u1 = std::min<uint64_t>(u0 + (uint64_t)g.upb, (uint64_t)g.units);
+                if (u0 + (uint64_t)g.upb >= (1ull << 32) || u1 + stride >= (1ull << 32))
+                    return fail(NH_ERR_ARG, "bn unit index wraps (C=%d yb=%d)", c, yb);
+                if (u0 >= u1) continue;
+                const uint32_t probe[] = {(uint32_t)u0, (uint32_t)(u1 - 1)};
+                for (uint32_t u : probe) {
+                    const int64_t off = m.vec == 1 ? bn_unit_offset<1>(g, c, u)
+                                        : (m.vec == 4 ? bn_unit_offset<4>(g, c, u) : bn_unit_offset<8>(g, c, u));
+                    const int64_t n = u / (uint32_t)g.HWv, j = u % (uint32_t)g.HWv;
+                    if (off != (n * m.C + c) * m.HW + j * m.vec || off < 0 || off + m.vec > total)
+                        return fail(NH_ERR_ARG, "bn unit offset out of range (u=%u)", u);
+                }
+            }
+        }
+    }
     return ok();
 }
 

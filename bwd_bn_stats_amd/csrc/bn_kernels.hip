@@ -63,25 +63,6 @@ enum : int { kNtReduceLoads = 1, kNtEwLoads = 2, kNtStores = 4 };
 #endif
 constexpr int kBnNtPolicy = NH_BN_NT_POLICY;
 
-struct BnGeom {
-    int C;
-    int HW;
-    int HWv;        // units per plane
-    FastDiv div_hwv;
-    int units;      // units per channel (N * HWv)
-    int upb;        // units per block
-    int grid_y;
-};
-
-// Element offset of unit u of channel c.
-template <int V>
-__device__ __forceinline__ int bn_unit_offset(const BnGeom &g, int c, int u)
-{
-    int n = (int)g.div_hwv.div((uint32_t)u);
-    int j = u - n * g.HWv;
-    return (n * g.C + c) * g.HW + j * V;
-}
-
 // Activations: 0 none, 1 ReLU, 2 LeakyReLU.
 template <int ACT>
 __device__ __forceinline__ float act_fwd(float z, float slope)
@@ -131,8 +112,10 @@ bn_stats_kernel(const T *__restrict__ x, BnGeom g, float *__restrict__ partials)
 {
     const int c = blockIdx.x / g.grid_y;
     const int yb = blockIdx.x - c * g.grid_y;
-    const int u0 = yb * g.upb;
-    const int u1 = min(u0 + g.upb, g.units);
+    // Unit indices are unsigned: a channel may hold up to 2^31 - 1 units,
+    // and the loop index runs up to a stride past the last one.
+    const uint32_t u0 = (uint32_t)yb * (uint32_t)g.upb;
+    const uint32_t u1 = min(u0 + (uint32_t)g.upb, (uint32_t)g.units);
     // The shift: the channel's first element, x[0, c, 0, 0].
     const float K = to_f32(x[c * g.HW]);
 
@@ -140,16 +123,16 @@ bn_stats_kernel(const T *__restrict__ x, BnGeom g, float *__restrict__ partials)
 #pragma unroll
     for (int k = 0; k < kBnUnroll; ++k) { s1[k] = 0.f; s2[k] = 0.f; }
 
-    for (int base = u0 + (int)threadIdx.x; base < u1; base += kBnThreads * kBnUnroll) {
+    for (uint32_t base = u0 + threadIdx.x; base < u1; base += kBnThreads * kBnUnroll) {
         float v[kBnUnroll][V];
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
-            const int u = base + k * kBnThreads;
+            const uint32_t u = base + k * kBnThreads;
             if (u < u1) ld<(NT & kNtReduceLoads) != 0, T, V>(x + bn_unit_offset<V>(g, c, u), v[k]);
         }
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
-            const int u = base + k * kBnThreads;
+            const uint32_t u = base + k * kBnThreads;
             if (u < u1) {
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
@@ -183,8 +166,10 @@ bn_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x,
 {
     const int c = blockIdx.x / g.grid_y;
     const int yb = blockIdx.x - c * g.grid_y;
-    const int u0 = yb * g.upb;
-    const int u1 = min(u0 + g.upb, g.units);
+    // Unit indices are unsigned: a channel may hold up to 2^31 - 1 units,
+    // and the loop index runs up to a stride past the last one.
+    const uint32_t u0 = (uint32_t)yb * (uint32_t)g.upb;
+    const uint32_t u1 = min(u0 + (uint32_t)g.upb, (uint32_t)g.units);
     const float mean = stats[c];
     const float scale = ACT != 0 ? stats[3 * g.C + c] : 0.f;
     const float bz = (ACT != 0 && beta) ? beta[c] : 0.f;
@@ -193,11 +178,11 @@ bn_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x,
 #pragma unroll
     for (int k = 0; k < kBnUnroll; ++k) { s1[k] = 0.f; s2[k] = 0.f; }
 
-    for (int base = u0 + (int)threadIdx.x; base < u1; base += kBnThreads * kBnUnroll) {
+    for (uint32_t base = u0 + threadIdx.x; base < u1; base += kBnThreads * kBnUnroll) {
         float vx[kBnUnroll][V], vd[kBnUnroll][V];
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
-            const int u = base + k * kBnThreads;
+            const uint32_t u = base + k * kBnThreads;
             if (u < u1) {
                 const int off = bn_unit_offset<V>(g, c, u);
                 ld<(NT & kNtReduceLoads) != 0, T, V>(x + off, vx[k]);
@@ -206,7 +191,7 @@ bn_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x,
         }
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
-            const int u = base + k * kBnThreads;
+            const uint32_t u = base + k * kBnThreads;
             if (u < u1) {
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
@@ -354,16 +339,18 @@ bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ 
 {
     const int c = blockIdx.x / g.grid_y;
     const int yb = blockIdx.x - c * g.grid_y;
-    const int u0 = yb * g.upb;
-    const int u1 = min(u0 + g.upb, g.units);
+    // Unit indices are unsigned: a channel may hold up to 2^31 - 1 units,
+    // and the loop index runs up to a stride past the last one.
+    const uint32_t u0 = (uint32_t)yb * (uint32_t)g.upb;
+    const uint32_t u1 = min(u0 + (uint32_t)g.upb, (uint32_t)g.units);
     const float b = beta ? beta[c] : 0.f;
 
-    int base = u0 + (int)threadIdx.x;
+    uint32_t base = u0 + threadIdx.x;
     float v[kBnUnroll][V];
     int off[kBnUnroll];
 #pragma unroll
     for (int k = 0; k < kBnUnroll; ++k) {
-        const int u = base + k * kBnThreads;
+        const uint32_t u = base + k * kBnThreads;
         off[k] = bn_unit_offset<V>(g, c, u);
         if (u < u1) ld<(NT & kNtEwLoads) != 0, T, V>(x + off[k], v[k]);
     }
@@ -397,7 +384,7 @@ bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ 
     for (;;) {
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
-            const int u = base + k * kBnThreads;
+            const uint32_t u = base + k * kBnThreads;
             if (u < u1) {
                 float o[V];
 #pragma unroll
@@ -409,7 +396,7 @@ bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ 
         if (base >= u1) break;
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
-            const int u = base + k * kBnThreads;
+            const uint32_t u = base + k * kBnThreads;
             off[k] = bn_unit_offset<V>(g, c, u);
             if (u < u1) ld<(NT & kNtEwLoads) != 0, T, V>(x + off[k], v[k]);
         }
@@ -425,18 +412,20 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
 {
     const int c = blockIdx.x / g.grid_y;
     const int yb = blockIdx.x - c * g.grid_y;
-    const int u0 = yb * g.upb;
-    const int u1 = min(u0 + g.upb, g.units);
+    // Unit indices are unsigned: a channel may hold up to 2^31 - 1 units,
+    // and the loop index runs up to a stride past the last one.
+    const uint32_t u0 = (uint32_t)yb * (uint32_t)g.upb;
+    const uint32_t u1 = min(u0 + (uint32_t)g.upb, (uint32_t)g.units);
     const float mean = stats[c];
     const float scale = stats[3 * g.C + c];
     const float b = (ACT != 0 && beta) ? beta[c] : 0.f;
 
-    int base = u0 + (int)threadIdx.x;
+    uint32_t base = u0 + threadIdx.x;
     float vx[kBnUnroll][V], vd[kBnUnroll][V];
     int off[kBnUnroll];
 #pragma unroll
     for (int k = 0; k < kBnUnroll; ++k) {
-        const int u = base + k * kBnThreads;
+        const uint32_t u = base + k * kBnThreads;
         off[k] = bn_unit_offset<V>(g, c, u);
         if (u < u1) {
             ld<(NT & kNtEwLoads) != 0, T, V>(x + off[k], vx[k]);
@@ -464,7 +453,7 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
     for (;;) {
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
-            const int u = base + k * kBnThreads;
+            const uint32_t u = base + k * kBnThreads;
             if (u < u1) {
                 float o[V];
 #pragma unroll
@@ -480,7 +469,7 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
         if (base >= u1) break;
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
-            const int u = base + k * kBnThreads;
+            const uint32_t u = base + k * kBnThreads;
             off[k] = bn_unit_offset<V>(g, c, u);
             if (u < u1) {
                 ld<(NT & kNtEwLoads) != 0, T, V>(x + off[k], vx[k]);
@@ -491,18 +480,7 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
 }
 
 // ---- host launchers -----------------------------------------------------------
-static BnGeom make_geom(const BnCall &a)
-{
-    BnGeom g;
-    g.C = a.C;
-    g.HW = a.HW;
-    g.HWv = a.HW / a.vec;
-    g.div_hwv = make_fastdiv((uint32_t)g.HWv);
-    g.units = a.N * g.HWv;
-    g.grid_y = a.grid_y;
-    g.upb = (int)ceil_div(g.units, a.grid_y);
-    return g;
-}
+static BnGeom make_geom(const BnCall &a) { return make_bn_geom(a.N, a.C, a.HW, a.vec, a.grid_y); }
 
 template <typename T, int V, int ACT>
 static hipError_t bn_forward_t(const BnCall &a, hipStream_t s)

@@ -46,6 +46,43 @@ inline int64_t bn_auto_grid_y(int64_t units, int64_t C, int64_t slots)
     return want < per_channel ? want : per_channel;
 }
 
+// Geometry of a BatchNorm launch: channel c's M elements in units of V
+// consecutive elements inside one plane, block (c, yb) owning units
+// [yb*upb, min((yb+1)*upb, units)).
+struct BnGeom {
+    int C;
+    int HW;
+    int HWv;        // units per plane
+    FastDiv div_hwv;
+    int units;      // units per channel (N * HWv)
+    int upb;        // units per block
+    int grid_y;
+};
+
+// Element offset of unit u of channel c.  Unsigned arithmetic: callers may
+// form the offset of a unit past the end (never dereferenced), which must
+// not be signed overflow.
+template <int V>
+__host__ __device__ __forceinline__ int bn_unit_offset(const BnGeom &g, int c, uint32_t u)
+{
+    const uint32_t n = g.div_hwv.div(u);
+    const uint32_t j = u - n * (uint32_t)g.HWv;
+    return (int)((n * (uint32_t)g.C + (uint32_t)c) * (uint32_t)g.HW + j * (uint32_t)V);
+}
+
+inline BnGeom make_bn_geom(int N, int C, int HW, int vec, int grid_y)
+{
+    BnGeom g;
+    g.C = C;
+    g.HW = HW;
+    g.HWv = HW / vec;
+    g.div_hwv = make_fastdiv((uint32_t)g.HWv);
+    g.units = N * g.HWv;
+    g.grid_y = grid_y;
+    g.upb = (int)ceil_div(g.units, grid_y);
+    return g;
+}
+
 struct BnCall {
     int io;              // 0 fp32, 1 bf16
     int N, C, HW;

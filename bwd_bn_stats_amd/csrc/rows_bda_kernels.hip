@@ -178,7 +178,8 @@ bda_generic_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
             prow2[j] = 0.f;
         }
     int it = 0;
-    for (int r = blockIdx.x; r < rows; r += G, ++it) {
+    // 64-bit row index: rows may reach 2^31 - 1 (one column), r + G must not wrap.
+    for (int64_t r = blockIdx.x; r < rows; r += G, ++it) {
         const size_t rowoff = (size_t)r * H;
         const float mu = mean[r], rs = rstd[r];
         float sa = 0.f, sb = 0.f;

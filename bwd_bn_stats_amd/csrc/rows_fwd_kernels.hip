@@ -150,7 +150,8 @@ norm_fwd_generic_kernel(const TX *__restrict__ x, const void *__restrict__ w,
     const int lane = tt & (kWave - 1);
     const float invH = 1.0f / (float)H;
     int it = 0;
-    for (int r = blockIdx.x; r < rows; r += gridDim.x, ++it) {
+    // 64-bit row index: rows may reach 2^31 - 1 (one column), r + G must not wrap.
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x, ++it) {
         const size_t rowoff = (size_t)r * H;
         const float K = KIND == 0 ? to_f32(x[rowoff]) : 0.f;
         float s1 = 0.f, s2 = 0.f;

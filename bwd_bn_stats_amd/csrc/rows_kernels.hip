@@ -269,7 +269,8 @@ rows_generic_kernel(int kind, const TDY *__restrict__ dy, const TX *__restrict__
             if (Q == 2) prow1[j] = 0.f;
         }
     int it = 0;
-    for (int r = blockIdx.x; r < rows; r += G, ++it) {
+    // 64-bit row index: rows may reach 2^31 - 1 (one column), r + G must not wrap.
+    for (int64_t r = blockIdx.x; r < rows; r += G, ++it) {
         const size_t rowoff = (size_t)r * H;
         float a = 0.f, b = 0.f;
         float mu = 0.f, rs = 0.f;
