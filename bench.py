@@ -27,6 +27,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -97,6 +99,30 @@ class Timed:
                 per[k] = {"launches": n, "avg_us": 1000.0 * ms / n}
         return 1000.0 * (t1 - t0) / K, per
 
+    def per_call(self, parts, K, start):
+        """Times each call of `parts` ([(name, fn(i))], run in order as one
+        step) with stream events around it, over K cold steps; returns
+        p10/median/p90 in microseconds per part and for their sum."""
+        torch = self.torch
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(K)]
+        torch.cuda.synchronize()
+        for i in range(K):
+            ev[i][0].record()
+            for j, (_, fn) in enumerate(parts):
+                fn(start + i)
+                ev[i][j + 1].record()
+        torch.cuda.synchronize()
+        out = {}
+        cols = [[1000.0 * ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)] for j in range(len(parts))]
+        if len(parts) > 1:
+            cols.append([sum(c[i] for c in cols) for i in range(K)])
+        names = [n for n, _ in parts] + (["sum"] if len(parts) > 1 else [])
+        for n, c in zip(names, cols):
+            q = np.percentile(np.asarray(c), [10, 50, 90])
+            out[n] = {"p10_us": round(float(q[0]), 2), "median_us": round(float(q[1]), 2),
+                      "p90_us": round(float(q[2]), 2)}
+        return out
+
 
 # ---- BatchNorm --------------------------------------------------------------------
 BN_KERNELS = ["bn_stats", "bn_fwd_finalize", "bn_apply", "bn_grad_sums", "bn_bwd_finalize", "bn_dx"]
@@ -137,31 +163,39 @@ def bench_bn(nh, torch, case, K, W, cold=True, act="none", slope=0.01):
         calls.append((p, s["ws"].numel()))
     lib = nh.lib
 
-    if act == "none":
-        def step(i):
-            p, nb = calls[i % R]
+    a = ACT_IDS[act]
+
+    def fwd(i):
+        p, nb = calls[i % R]
+        if act == "none":
             st = lib.bn_forward_train(p["x"], p["y"], io, N, C, HW, P(g.data_ptr()), P(b.data_ptr()),
                                       p["rm"], p["rv"], case.momentum, case.eps, p["stats"], p["ws"],
                                       nb, stream)
-            st |= lib.bn_backward(p["dy"], p["x"], io, N, C, HW, p["stats"], p["dx"], p["grads"],
-                                  p["ws"], nb, stream)
-            if st:
-                raise RuntimeError(nh.last_error())
-    else:
-        a = ACT_IDS[act]
-
-        def step(i):
-            p, nb = calls[i % R]
+        else:
             st = lib.bn_act_forward_train(p["x"], p["y"], io, N, C, HW, P(g.data_ptr()),
                                           P(b.data_ptr()), p["rm"], p["rv"], case.momentum, case.eps,
                                           a, slope, p["stats"], p["ws"], nb, stream)
-            st |= lib.bn_act_backward(p["dy"], p["x"], io, N, C, HW, p["stats"], P(b.data_ptr()), a,
-                                      slope, p["dx"], p["grads"], p["ws"], nb, stream)
-            if st:
-                raise RuntimeError(nh.last_error())
+        if st:
+            raise RuntimeError(nh.last_error())
+
+    def bwd(i):
+        p, nb = calls[i % R]
+        if act == "none":
+            st = lib.bn_backward(p["dy"], p["x"], io, N, C, HW, p["stats"], p["dx"], p["grads"],
+                                 p["ws"], nb, stream)
+        else:
+            st = lib.bn_act_backward(p["dy"], p["x"], io, N, C, HW, p["stats"], P(b.data_ptr()), a,
+                                     slope, p["dx"], p["grads"], p["ws"], nb, stream)
+        if st:
+            raise RuntimeError(nh.last_error())
+
+    def step(i):
+        fwd(i)
+        bwd(i)
 
     tm = Timed(nh, torch)
     ms, per = tm.run(step, K, W, BN_KERNELS)
+    calls_pct = tm.per_call([("bn_forward_train", fwd), ("bn_backward", bwd)], K, W + 2 * K)
     byt = bn_bytes(case)
     for k, v in per.items():
         if byt.get(k):
@@ -171,10 +205,13 @@ def bench_bn(nh, torch, case, K, W, cold=True, act="none", slope=0.01):
     step_bytes = sum(v for v in byt.values() if v)
     del sets, calls
     torch.cuda.empty_cache()
+    # one-touch minimum: forward x + y, backward x + dy + dx
+    one_touch = 5 * N * C * HW * (4 if case.io == "f32" else 2)
     return {"ms_per_step": ms, "us_per_call": 1000.0 * ms,
             "us_per_call_with_kernel_events": 1000.0 * tm.events_ms, "step_bytes": step_bytes,
-            "gbs": step_bytes / (ms * 1e6), "buffer_sets": R, "kernels": per,
-            "grid_y": nh.bn_plan(N, C, HW, io)}
+            "gbs": step_bytes / (ms * 1e6), "one_touch_bytes": one_touch,
+            "one_touch_gbs": one_touch / (ms * 1e6), "buffer_sets": R, "kernels": per,
+            "per_call": calls_pct, "grid_y": nh.bn_plan(N, C, HW, io)}
 
 
 def bench_bn_infer(nh, torch, case, K, W, act="relu", slope=0.01):
@@ -266,7 +303,10 @@ def bench_rows(nh, torch, case, kind, K, W, cold=True, saved=True):
                 raise RuntimeError(nh.last_error())
         kernels = ["rms_rows", "rms_colsum"]
 
-    ms, per = Timed(nh, torch).run(step, K, W, kernels)
+    tm = Timed(nh, torch)
+    ms, per = tm.run(step, K, W, kernels)
+    calls_pct = tm.per_call([("layernorm_backward" if kind == "ln" else "rmsnorm_backward", step)], K,
+                            W + 2 * K)
     E = R_ * H
     row_bytes = E * (x0.element_size() + dy0.element_size() + torch.empty(0, dtype=dx_dtype).element_size())
     row_bytes += R_ * 4 * (2 if kind == "ln" else (1 if saved else 0)) + H * w.element_size()
@@ -279,7 +319,8 @@ def bench_rows(nh, torch, case, kind, K, W, cold=True, saved=True):
     del sets, calls
     torch.cuda.empty_cache()
     return {"ms_per_call": ms, "us_per_call": 1000.0 * ms, "bytes": row_bytes,
-            "gbs": row_bytes / (ms * 1e6), "buffer_sets": R, "kernels": per, "blocks_max": G}
+            "gbs": row_bytes / (ms * 1e6), "buffer_sets": R, "kernels": per, "blocks_max": G,
+            "per_call": calls_pct}
 
 
 def bench_bda(nh, torch, case, K, W, cold=True):
@@ -421,8 +462,17 @@ def cpu_baseline(case, budget_s=12.0):
         t_total += time.perf_counter() - t0
         reps += 1
     step_bytes = sum(v for v in bn_bytes(case).values() if v)
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": step_bytes * reps / t_total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "ms_per_step": 1000.0 * t_total / reps,
+            "ms_per_step": 1000.0 * t_total / reps, "cpu_model": model,
+            "host_cores_available": os.cpu_count(),
             "sample": f"full {case.N}x{case.C}x{case.hw // 32}x32 {case.io} forward+backward step, "
                       f"{reps} repetitions (fp64, single thread, same algorithmic bytes as the GPU step)"}
 
@@ -704,6 +754,9 @@ def main():
         "us_per_call_with_kernel_events": round(cold["us_per_call_with_kernel_events"], 2),
         "frac_of_peak": round(cold["gbs"] / HBM_PEAK_GBS, 4),
         "frac_of_calib_floor": round(cold["gbs"] / calib["gbs"], 4),
+        "one_touch": {"bytes": cold["one_touch_bytes"], "gbs": round(cold["one_touch_gbs"], 1),
+                      "frac_of_peak": round(cold["one_touch_gbs"] / HBM_PEAK_GBS, 4)},
+        "per_call": cold["per_call"],
         "roofline": roofline,
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in per.items()},
