@@ -89,6 +89,7 @@ std::atomic<int64_t> g_override_bn_grid_y{0};
 std::atomic<int64_t> g_override_rows_blocks{0};
 std::atomic<int64_t> g_override_bn_finalize_kernels{0};
 std::atomic<int64_t> g_override_rows_depth{0};
+std::atomic<int64_t> g_override_colsum_cols{0};
 
 // ---- BatchNorm planning ----------------------------------------------------------
 // Resident 256-thread block slots of the device: CUs * (threads per CU / 256),
@@ -498,6 +499,7 @@ static nh_status rows_run(RowsCall &a, int Q, void *ws, size_t ws_bytes, void *s
     a.vec = p.vec;
     a.teams = p.teams;
     a.depth = (int)g_override_rows_depth.load();
+    a.colsum_cols = (int)g_override_colsum_cols.load();
     // Occupancy of the chosen variant, cached per device and variant.
     int dev = 0;
     (void)hipGetDevice(&dev);
@@ -845,6 +847,11 @@ nh_status nh_plan_override(const char *key, int64_t value)
     else if (strcmp(key, "rows_depth") == 0) {
         if (value < 0 || value > 4) return fail(NH_ERR_ARG, "rows_depth must be 0..4");
         g_override_rows_depth.store(value);
+    }
+    else if (strcmp(key, "colsum_cols") == 0) {
+        if (value != 0 && value != 8 && value != 16 && value != 32 && value != 64)
+            return fail(NH_ERR_ARG, "colsum_cols must be 0, 8, 16, 32 or 64");
+        g_override_colsum_cols.store(value);
     }
     else if (strcmp(key, "bn_finalize_kernels") == 0) g_override_bn_finalize_kernels.store(value);
     else return fail(NH_ERR_ARG, "unknown override key '%s'", key);

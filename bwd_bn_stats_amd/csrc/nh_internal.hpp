@@ -127,6 +127,7 @@ struct RowsCall {
     void *dbias_in;              // kind 2: [cols] of w_t out or NULL
     float *partials;     // [Q, G, cols]
     int depth;           // row-pipeline depth of the vector path (0 = the kernel's default)
+    int colsum_cols;     // columns per column-finalize block (0 = default)
     int *occupancy_out;  // non-NULL: report resident 256-thread blocks per CU
                          // of the selected row kernel instead of launching
 };

@@ -316,36 +316,43 @@ rows_generic_kernel(int kind, const TDY *__restrict__ dy, const TX *__restrict__
 }
 
 // ---- column finalize: fp64 fixed-order sum of the G partial rows -------------
-// Block = kColX columns x kColY slices; slice ty sums partial rows
-// ty, ty + kColY, ... in order (loads unrolled by 4 ahead of the adds), then
-// the slices are combined in slice order through LDS.  The partials were
-// just written and sit in L2 / the Infinity Cache: the kernel is
-// latency-bound, its cost grows with G.
-constexpr int kColX = 32;   // columns per block (one 128-byte line of a partial row)
-constexpr int kColY = 32;   // slices of the G partial rows
-template <typename TOUT>
-__global__ void __launch_bounds__(kColX * kColY)
+// Block = CX columns x (1024/CX) slices; slice ty sums partial rows
+// ty, ty + CY, ... in order, then the slices are combined in slice order
+// through LDS.  The partials were just written and sit in L2 / the Infinity
+// Cache, so the kernel is latency-bound: a thread issues NL loads at once
+// (rows past G re-read row G-1 and are added as zero, so the loads need no
+// branch), one round trip per NL*CY partial rows.
+constexpr int kColThreads = 1024;
+template <typename TOUT, int CX, int NL>
+__global__ void __launch_bounds__(kColThreads)
 rows_colsum_kernel(const float *__restrict__ partials, int G, int H, TOUT *__restrict__ out0,
                    TOUT *__restrict__ out1, TOUT *__restrict__ out2)
 {
-    __shared__ double acc[kColY][kColX];
+    constexpr int CY = kColThreads / CX;
+    __shared__ double acc[CY][CX];
     const int q = blockIdx.y;
     TOUT *out = q == 0 ? out0 : (q == 1 ? out1 : out2);
     if (out == nullptr) return;  // uniform across the block
-    const int tx = threadIdx.x % kColX;
-    const int ty = threadIdx.x / kColX;
-    const int j = blockIdx.x * kColX + tx;
+    const int tx = threadIdx.x % CX;
+    const int ty = threadIdx.x / CX;
+    const int j = blockIdx.x * CX + tx;
     double s = 0.0;
     if (j < H) {
-#pragma unroll 4
-        for (int b = ty; b < G; b += kColY) s += (double)partials[((size_t)q * G + b) * H + j];
+        const float *col = partials + (size_t)q * G * H + j;
+        for (int b0 = ty; b0 < G; b0 += NL * CY) {
+            float v[NL];
+#pragma unroll
+            for (int i = 0; i < NL; ++i) v[i] = col[(size_t)min(b0 + i * CY, G - 1) * H];
+#pragma unroll
+            for (int i = 0; i < NL; ++i) s += b0 + i * CY < G ? (double)v[i] : 0.0;
+        }
     }
     acc[ty][tx] = s;
     __syncthreads();
     if (ty == 0 && j < H) {
         double t = acc[0][tx];
-#pragma unroll
-        for (int y = 1; y < kColY; ++y) t += acc[y][tx];
+#pragma unroll 8
+        for (int y = 1; y < CY; ++y) t += acc[y][tx];
         out[j] = from_f32<TOUT>((float)t);
     }
 }
@@ -486,15 +493,29 @@ template <typename TX, typename TDY, typename TDX> struct GenericF {
     static hipError_t run(const RowsCall &a, hipStream_t s) { return generic_launch<TX, TDY, TDX>(a, s); }
 };
 
-template <typename TOUT>
-static hipError_t colsum(const RowsCall &a, int kid, hipStream_t s)
+template <typename TOUT, int CX>
+static hipError_t colsum_cx(const RowsCall &a, int kid, hipStream_t s)
 {
     const int Q = rows_q(a.kind);
-    const dim3 grid((unsigned)ceil_div(a.cols, kColX), (unsigned)Q);
-    return launch(kid, rows_colsum_kernel<TOUT>, grid, dim3(kColX * kColY), 0u, s,
+    const dim3 grid((unsigned)ceil_div(a.cols, CX), (unsigned)Q);
+    constexpr int CY = kColThreads / CX;
+    // All of a thread's partial rows in one round when they fit 16 loads.
+    auto kern = a.blocks > 8 * CY ? rows_colsum_kernel<TOUT, CX, 16> : rows_colsum_kernel<TOUT, CX, 8>;
+    return launch(kid, kern, grid, dim3(kColThreads), 0u, s,
                   (const float *)a.partials, a.blocks, a.cols, static_cast<TOUT *>(a.dweight),
                   static_cast<TOUT *>(a.kind != 1 ? a.dbias : nullptr),
                   static_cast<TOUT *>(a.kind == 2 ? a.dbias_in : nullptr));
+}
+
+template <typename TOUT>
+static hipError_t colsum(const RowsCall &a, int kid, hipStream_t s)
+{
+    switch (a.colsum_cols > 0 ? a.colsum_cols : 32) {
+    case 8: return colsum_cx<TOUT, 8>(a, kid, s);
+    case 16: return colsum_cx<TOUT, 16>(a, kid, s);
+    case 64: return colsum_cx<TOUT, 64>(a, kid, s);
+    default: return colsum_cx<TOUT, 32>(a, kid, s);
+    }
 }
 
 hipError_t rows_colsum_launch(const RowsCall &a, int kid, hipStream_t s)

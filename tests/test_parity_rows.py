@@ -220,3 +220,14 @@ def test_rows_pipeline_depths(nh, oracle_mod, depth):
         _rms_case(nh, oracle_mod, r, saved=True, override_blocks=50)
     finally:
         nh.plan_override("rows_depth", 0)
+
+
+@pytest.mark.parametrize("cx", [8, 16, 64])
+def test_rows_colsum_widths(nh, oracle_mod, cx):
+    """Every column-finalize block width gives the oracle's column sums."""
+    nh.plan_override("colsum_cols", cx)
+    try:
+        c = wl.rows_case(777, 1000, x_t=wl.F32, dy_t=wl.F32, w_t=wl.F32, seed=93)
+        _ln_case(nh, oracle_mod, c, wl.F32, override_blocks=300)
+    finally:
+        nh.plan_override("colsum_cols", 0)
