@@ -214,6 +214,55 @@ def bench_bn(nh, torch, case, K, W, cold=True, act="none", slope=0.01):
             "per_call": calls_pct, "grid_y": nh.bn_plan(N, C, HW, io)}
 
 
+def bench_bn_graph(nh, torch, case, K, W):
+    """A launch-bound step (small shape): fwd+bwd issued eagerly, one call
+    at a time, against the same two calls captured once in a HIP graph and
+    replayed.  Buffers stay warm (the shape fits in cache)."""
+    device = torch.device("cuda:0")
+    x, dy = _dev(case.x, device), _dev(case.dy, device)
+    g, b = _dev(case.gamma, device), _dev(case.beta, device)
+    ws = torch.empty(max(16, nh.bn_forward_train_workspace(case.N, case.C, case.hw)), dtype=torch.uint8,
+                     device=device)
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    stats = torch.empty(4, case.C, device=device)
+    grads = torch.empty(4, case.C, device=device)
+
+    def step():
+        nh.bn_forward_train(x, g, b, None, None, case.momentum, case.eps, y=y, stats=stats,
+                            workspace=ws)
+        nh.bn_backward(dy, x, stats, dx=dx, grads=grads, workspace=ws)
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    eager_us = 1e6 * (time.perf_counter() - t0) / K
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    res = {"eager_us_per_step": round(eager_us, 2), "kernels_per_step": 4}
+    for inner in (1, 10):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(inner):
+                step()
+        for _ in range(W):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            graph.replay()
+        torch.cuda.synchronize()
+        res[f"graph_{inner}_steps_us_per_step"] = round(1e6 * (time.perf_counter() - t0) / (K * inner), 2)
+        del graph
+    return res
+
+
 def bench_bn_infer(nh, torch, case, K, W, act="relu", slope=0.01):
     """BatchNorm2d inference (+ activation): one elementwise pass, x read and
     y written once."""
@@ -701,6 +750,8 @@ def main():
                          ("bn_ragged_3x37x41x40_f32", wl.bn_ragged)):
             log(f"[bench] {name}")
             others[name] = bench_bn(nh, torch, fn(), kk, W, cold=True)
+        log("[bench] bn_ragged_3x37x41x40_f32 eager vs HIP graph replay (launch-bound)")
+        others["bn_ragged_3x37x41x40_f32_graph"] = bench_bn_graph(nh, torch, wl.bn_ragged(), max(50, K), W)
         for name, fn, act in (("bn_relu_cifar_256x32x32x32_f32", lambda: wl.bn_cifar(wl.F32), "relu"),
                               ("bn_leaky_relu_cifar_256x32x32x32_f32", lambda: wl.bn_cifar(wl.F32),
                                "leaky_relu"),

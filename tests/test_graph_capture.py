@@ -1,0 +1,74 @@
+"""The entry points under HIP graph capture (torch.cuda.graph): they
+allocate nothing, synchronize nothing and record no memset, so a captured
+forward+backward replays with the eager results.  Each replay is checked bit
+for bit against the eager run, with eager work and synchronizations between
+replays."""
+import pytest
+
+from bwd_bn_stats_amd import workloads as wl
+
+from helpers import dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def nh():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from bwd_bn_stats_amd import normhip
+    return normhip
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def test_graph_replays_match_eager(nh):
+    c = wl.bn_ragged()
+    x, dy, g, b = dev(c.x), dev(c.dy), dev(c.gamma), dev(c.beta)
+    r = wl.ln_bwd(rows=1024)
+    lx, ldy, lw, lb = dev(r.x), dev(r.dy), dev(r.w), dev(r.b)
+    m = wl.rms_bwd(wl.BF16, rows=256)
+    mx, mdy, mw = dev(m.x), dev(m.dy), dev(m.w)
+    ws_bn = torch.empty(nh.bn_forward_train_workspace(c.N, c.C, c.hw), dtype=torch.uint8, device="cuda")
+    ws_ln = torch.empty(nh.layernorm_backward_workspace(r.rows, r.cols), dtype=torch.uint8, device="cuda")
+    ws_rms = torch.empty(nh.rmsnorm_backward_workspace(m.rows, m.cols), dtype=torch.uint8, device="cuda")
+    outs = {}
+
+    def work():
+        y, stats = nh.bn_forward_train(x, g, b, act="relu", workspace=ws_bn)
+        dx, grads = nh.bn_backward(dy, x, stats, beta=b, act="relu", workspace=ws_bn)
+        ly, mean, rstd = nh.layernorm_forward(lx, lw, lb, 1e-5)
+        ldx, ldw, ldb = nh.layernorm_backward(ldy, lx, mean, rstd, lw, dx_dtype=torch.float32,
+                                              workspace=ws_ln)
+        my, rms = nh.rmsnorm_forward(mx, mw, 1e-5)
+        mdx, mdw = nh.rmsnorm_backward(mdy, mx, rms, mw, 1e-5, workspace=ws_rms)
+        return dict(y=y, stats=stats, dx=dx, grads=grads, ly=ly, mean=mean, rstd=rstd, ldx=ldx,
+                    ldw=ldw, ldb=ldb, my=my, rms=rms, mdx=mdx, mdw=mdw)
+
+    eager = work()
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in eager.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()   # warm the caching allocator outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = work()
+    print("[graph] captured BN+ReLU fwd/bwd, LN fwd/bwd, RMS fwd/bwd", flush=True)
+    for rep in range(3):
+        # unrelated eager work between replays overwrites the inputs' neighbours
+        scratch = torch.randn(1 << 20, device="cuda") * rep
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in eager.items():
+            assert torch.equal(_bits(outs[k]), _bits(v)), f"replay {rep}: {k} differs from eager"
+        del scratch
+    print("[graph] 3 replays bit-identical to eager", flush=True)
