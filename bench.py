@@ -495,6 +495,28 @@ def bench_calib(nh, torch, n_floats, K, W):
     return {"bytes": byt, "avg_us": avg, "gbs": byt / (avg * 1e3), "frac_of_peak": byt / (avg * 1e3) / HBM_PEAK_GBS}
 
 
+def bench_copy(nh, torch, nbytes, K, W):
+    """Calibration floor of a one-read/one-write stream: nh_calib_copy of
+    nbytes (cold rotating buffers); GB/s counts the bytes read plus written."""
+    device = torch.device("cuda:0")
+    R = _nsets(2 * nbytes, True)
+    sets = [(torch.empty(nbytes, dtype=torch.uint8, device=device),
+             torch.empty(nbytes, dtype=torch.uint8, device=device)) for _ in range(R)]
+    for a, _ in sets:
+        a.fill_(1)
+    torch.cuda.synchronize()
+
+    def step(i):
+        a, b = sets[i % R]
+        nh.calib_copy(a, b)
+
+    ms, per = Timed(nh, torch).run(step, K, W, ["calib"])
+    avg = per["calib"]["avg_us"]
+    del sets
+    torch.cuda.empty_cache()
+    return {"bytes": 2 * nbytes, "avg_us": avg, "gbs": 2 * nbytes / (avg * 1e3)}
+
+
 # ---- CPU baseline: the oracle on this host ----------------------------------------------
 def cpu_baseline(case, budget_s=12.0):
     import numpy as np
@@ -776,6 +798,20 @@ def main():
         for dt in (wl.BF16, wl.F32):
             log(f"[bench] rms_fwd_2048x8192_{dt}")
             others[f"rms_fwd_2048x8192_{dt}"] = bench_rows_fwd(nh, torch, wl.rms_bwd(dt), "rms", kk, W)
+
+    if not args.quick:
+        # one-read/one-write kernels against a plain copy of the same bytes
+        for name, kern in (("bn_infer_relu_cifar_256x32x32x32_f32", "bn_infer"),
+                           ("bn_infer_relu_resnet_64x256x56x56_bf16", "bn_infer"),
+                           ("ln_fwd_16x512x1600", "ln_fwd"), ("rms_fwd_2048x8192_bf16", "rms_fwd"),
+                           ("rms_fwd_2048x8192_f32", "rms_fwd")):
+            o = others.get(name)
+            if not o or kern not in o["kernels"] or not o["kernels"][kern].get("bytes"):
+                continue
+            log(f"[bench] copy floor for {name}")
+            cp = bench_copy(nh, torch, o["kernels"][kern]["bytes"] // 32 * 16, max(10, K // 2), W)
+            o["copy_floor"] = {"gbs": round(cp["gbs"], 1), "avg_us": round(cp["avg_us"], 3)}
+            o["kernels"][kern]["frac_of_copy_floor"] = round(o["kernels"][kern]["gbs"] / cp["gbs"], 4)
 
     # dominant kernel of the step: the largest share of the step's kernel time
     per = cold["kernels"]
