@@ -139,7 +139,6 @@ int bn_vec(int io, int64_t HW, const void *a, const void *b, const void *c)
 struct RowsPlan {
     int maxg = 0;   // 0 = generic path
     int vec = 1;
-    int teams = 1;
     int blocks = 0;
 };
 
@@ -174,7 +173,6 @@ RowsPlan rows_variant(int64_t cols, int vec, bool vec_ok, int max_elems = kRowsM
         if (mg <= 8 && mg * vec <= max_elems) p.maxg = mg;
     }
     if (p.maxg == 0) p.vec = 1;
-    p.teams = 1;
     return p;
 }
 
@@ -497,7 +495,6 @@ static nh_status rows_run(RowsCall &a, int Q, void *ws, size_t ws_bytes, void *s
     RowsPlan p = rows_variant(a.cols, a.vec, vec_ok, a.kind == 2 ? kBdaMaxRowElems : kRowsMaxRowElems);
     a.maxg = p.maxg;
     a.vec = p.vec;
-    a.teams = p.teams;
     a.depth = (int)g_override_rows_depth.load();
     a.colsum_cols = (int)g_override_colsum_cols.load();
     // Occupancy of the chosen variant, cached per device and variant.

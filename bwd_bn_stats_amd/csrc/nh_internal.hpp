@@ -112,7 +112,6 @@ struct RowsCall {
     int x_t, dy_t, w_t, dx_t;
     int rows, cols;
     int blocks;          // G: column-partial rows
-    int teams;           // 256-thread teams per block (vector path)
     int maxg;            // 16-byte groups per thread per row (vector path); 0 = generic path
     int vec;             // elements per group
     const void *x, *dy, *w;
@@ -136,8 +135,6 @@ hipError_t rows_backward_launch(const RowsCall &a, hipStream_t s);
 hipError_t bda_backward_launch(const RowsCall &a, hipStream_t s);
 // Column finalize of the Q = rows_q(kind) partial rows into dweight, dbias, dbias_in.
 hipError_t rows_colsum_launch(const RowsCall &a, int kid, hipStream_t s);
-// Dynamic LDS of a row-kernel launch: row sums, plus the team-fold slot.
-int rows_lds_bytes(const RowsCall &a);
 // Column sums per kind: LayerNorm dweight, dbias; RMSNorm dweight;
 // bias + dropout + add + LayerNorm dweight, dbias, dbias_in.
 constexpr int rows_q(int kind) { return kind == 0 ? 2 : (kind == 1 ? 1 : 3); }

@@ -48,12 +48,8 @@ bda_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
                 float *__restrict__ dh, TDY *__restrict__ da, float *__restrict__ partials,
                 int want_cols)
 {
-    extern __shared__ float lds[];
-    float *red = lds;
-    float *slot = lds + kRedFloats;
-    const int teams = blockDim.x / kTeam;
-    const int team = threadIdx.x / kTeam;
-    const int tt = threadIdx.x - team * kTeam;
+    __shared__ float red[kRedFloats];
+    const int tt = threadIdx.x;
     const int wave = tt / kWave;
     const int lane = tt & (kWave - 1);
     const int G = gridDim.x;
@@ -71,8 +67,8 @@ bda_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
         for (int e = 0; e < VEC; ++e) { p[0][k][e] = 0.f; p[1][k][e] = 0.f; p[2][k][e] = 0.f; }
     }
 
-    const int iters = (int)ceil_div(rows, (int64_t)G * teams);
-    auto row_of = [&](int it) { return (it * G + (int)blockIdx.x) * teams + team; };
+    const int iters = (int)ceil_div(rows, (int64_t)G);
+    auto row_of = [&](int it) { return it * G + (int)blockIdx.x; };
 
     struct RowBuf {
         Raw<TX, VEC> x[MAXG];
@@ -124,7 +120,7 @@ bda_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
                 }
             }
         }
-        team_sum2(red + (it & 1) * (kRedFloats / 2), team, wave, lane, sa, sb);
+        team_sum2(red + (it & 1) * (kRedFloats / 2), wave, lane, sa, sb);
         if (!active) return;
         const float ca = sa * invH, cb = sb * invH;
         const size_t rowoff = (size_t)r * H;
@@ -148,7 +144,7 @@ bda_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
     };
 
     pipeline_rows<D, RowBuf>(iters, load_row, do_row);
-    if (want_cols) fold_and_write<VEC, MAXG, 3>(p, slot, teams, team, tt, Gr, H, G, partials);
+    if (want_cols) write_partials<VEC, MAXG, 3>(p, tt, Gr, H, G, partials);
 }
 
 // Any width, any alignment: scalar accesses, two reads of each row (the
@@ -189,7 +185,7 @@ bda_generic_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
             sa += g;
             sb = fmaf(g, (to_f32(x[rowoff + j]) - mu) * rs, sb);
         }
-        team_sum2(red + (it & 1) * (kRedFloats / 2), 0, wave, lane, sa, sb);
+        team_sum2(red + (it & 1) * (kRedFloats / 2), wave, lane, sa, sb);
         const float ca = sa * invH, cb = sb * invH;
         for (int j = tt; j < H; j += kTeam) {
             const size_t i = rowoff + j;
@@ -216,10 +212,8 @@ static hipError_t bda_vec_d(const RowsCall &a, hipStream_t s)
     constexpr int MT = kTeam;
     auto kern = bda_rows_kernel<TX, TDY, VEC, MAXG, MT, D>;
     if (a.occupancy_out)
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kern, kTeam,
-                                                            (size_t)rows_lds_bytes(a));
-    return launch(NH_K_BDA_ROWS, kern, dim3(a.blocks), dim3(a.teams * kTeam),
-                  (uint32_t)rows_lds_bytes(a), s, static_cast<const TDY *>(a.dy),
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kern, kTeam, 0);
+    return launch(NH_K_BDA_ROWS, kern, dim3(a.blocks), dim3(kTeam), 0u, s, static_cast<const TDY *>(a.dy),
                   static_cast<const TX *>(a.x), a.mean, a.rstd, a.w, a.w_t, a.dresidual, a.mask,
                   a.scale, a.rows, a.cols, a.dh, static_cast<TDY *>(a.dx), a.partials,
                   (int)(a.dweight != nullptr || a.dbias != nullptr || a.dbias_in != nullptr));

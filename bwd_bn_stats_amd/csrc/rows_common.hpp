@@ -9,8 +9,7 @@ namespace nh {
 
 constexpr int kTeam = 256;
 constexpr int kTeamWaves = kTeam / kWave;
-constexpr int kMaxTeams = 4;
-constexpr int kRedFloats = 2 * kMaxTeams * kTeamWaves * 2;  // double-buffered row sums
+constexpr int kRedFloats = 2 * kTeamWaves * 2;  // double-buffered row sums of two quantities
 
 __device__ __forceinline__ float load_param(const void *w, int w_bf16, int col)
 {
@@ -36,22 +35,21 @@ struct WeightGroup {
 };
 
 // Fixed-order sum of the 4 wave results of a team for two quantities.
-__device__ __forceinline__ void team_sum2(float *red, int team, int wave, int lane,
-                                          float &a, float &b)
+__device__ __forceinline__ void team_sum2(float *red, int wave, int lane, float &a, float &b)
 {
     a = wave_sum(a);
     b = wave_sum(b);
     if (lane == 0) {
-        red[(team * kTeamWaves + wave) * 2 + 0] = a;
-        red[(team * kTeamWaves + wave) * 2 + 1] = b;
+        red[wave * 2 + 0] = a;
+        red[wave * 2 + 1] = b;
     }
     lds_barrier();
-    float sa = red[(team * kTeamWaves) * 2 + 0];
-    float sb = red[(team * kTeamWaves) * 2 + 1];
+    float sa = red[0];
+    float sb = red[1];
 #pragma unroll
     for (int w = 1; w < kTeamWaves; ++w) {
-        sa += red[(team * kTeamWaves + w) * 2 + 0];
-        sb += red[(team * kTeamWaves + w) * 2 + 1];
+        sa += red[w * 2 + 0];
+        sb += red[w * 2 + 1];
     }
     a = sa;
     b = sb;
@@ -91,48 +89,18 @@ constexpr int rows_depth(int row_bytes_per_thread)
 // per CU already: depth 2 measured best (LayerNorm 1600, RMSNorm 8192).
 constexpr int kFwdDepth = 2;
 
-// Folds the teams' column sums into team 0 in team order (slot: Q*H floats),
-// then team 0 writes the block's partial row.
+// Writes a block's column sums (Q quantities) as its row of partials[Q, G, H].
 template <int VEC, int MAXG, int Q>
-__device__ __forceinline__ void fold_and_write(float (&p)[Q][MAXG][VEC], float *slot, int teams,
-                                               int team, int tt, int Gr, int H, int G,
-                                               float *__restrict__ partials)
+__device__ __forceinline__ void write_partials(const float (&p)[Q][MAXG][VEC], int tt, int Gr, int H,
+                                               int G, float *__restrict__ partials)
 {
-    for (int t = 1; t < teams; ++t) {
-        __syncthreads();
-        if (team == t) {
 #pragma unroll
-            for (int k = 0; k < MAXG; ++k) {
-                const int grp = tt + k * kTeam;
-                if (grp < Gr)
+    for (int k = 0; k < MAXG; ++k) {
+        const int grp = tt + k * kTeam;
+        if (grp < Gr)
 #pragma unroll
-                    for (int q = 0; q < Q; ++q)
-#pragma unroll
-                        for (int e = 0; e < VEC; ++e) slot[q * H + grp * VEC + e] = p[q][k][e];
-            }
-        }
-        __syncthreads();
-        if (team == 0) {
-#pragma unroll
-            for (int k = 0; k < MAXG; ++k) {
-                const int grp = tt + k * kTeam;
-                if (grp < Gr)
-#pragma unroll
-                    for (int q = 0; q < Q; ++q)
-#pragma unroll
-                        for (int e = 0; e < VEC; ++e) p[q][k][e] += slot[q * H + grp * VEC + e];
-            }
-        }
-    }
-    if (team == 0) {
-#pragma unroll
-        for (int k = 0; k < MAXG; ++k) {
-            const int grp = tt + k * kTeam;
-            if (grp < Gr)
-#pragma unroll
-                for (int q = 0; q < Q; ++q)
-                    store_vec<float, VEC>(partials + ((size_t)q * G + blockIdx.x) * H + grp * VEC, p[q][k]);
-        }
+            for (int q = 0; q < Q; ++q)
+                store_vec<float, VEC>(partials + ((size_t)q * G + blockIdx.x) * H + grp * VEC, p[q][k]);
     }
 }
 

@@ -97,7 +97,7 @@ norm_fwd_rows_kernel(const TX *__restrict__ x, const void *__restrict__ w,
                 }
             }
         }
-        team_sum2(red + (it & 1) * (kRedFloats / 2), 0, wave, lane, s1, s2);
+        team_sum2(red + (it & 1) * (kRedFloats / 2), wave, lane, s1, s2);
         if (!active) return;
         float a, c;  // y = fmaf(x - c, a*w, b) (LN) or y = (x*a)*w (RMS)
         if constexpr (KIND == 0) {
@@ -165,7 +165,7 @@ norm_fwd_generic_kernel(const TX *__restrict__ x, const void *__restrict__ w,
                 s2 = fmaf(v, v, s2);
             }
         }
-        team_sum2(red + (it & 1) * (kRedFloats / 2), 0, wave, lane, s1, s2);
+        team_sum2(red + (it & 1) * (kRedFloats / 2), wave, lane, s1, s2);
         float a, c;
         if (KIND == 0) {
             const float md = s1 * invH;

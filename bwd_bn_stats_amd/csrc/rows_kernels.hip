@@ -16,18 +16,18 @@
 //     them), the same columns for every row it visits, so it keeps the
 //     weight and its share of the column sums (the dweight/dbias split over
 //     rows) in registers across rows.
-//   * A block holds `teams` teams; block b's teams take rows
-//     (it*G + b)*teams + team for it = 0, 1, ...  Row sums are wave
+//   * A block is one team; block b takes rows it*G + b for it = 0, 1, ...,
+//     keeping D of them in flight (software pipeline).  Row sums are wave
 //     butterflies followed by a fixed-order add of the 4 wave results
-//     through LDS, one block barrier per row step.
-//   * After its last row, the block folds its teams' column sums in team
-//     order through LDS and writes one row of partials[Q, G, H].
+//     through LDS, one block barrier per row.
+//   * After its last row, the block writes its column sums as one row of
+//     partials[Q, G, H].
 //   * rows_colsum_kernel sums the G partial rows of each column in fp64, in
 //     index order, and rounds to the weight's dtype.
 // No atomics: every output has one writer and a fixed summation order.
 //
 // Rows whose width is not a multiple of the group, misaligned pointers, or
-// rows wider than 8 groups per thread take rows_generic_kernel: the same
+// rows wider than the vector path's register budget take rows_generic_kernel: the same
 // arithmetic with scalar accesses, two reads of each row (the second mostly
 // from cache) and the column sums kept in the block's own partial row.
 #include "rows_common.hpp"
@@ -46,12 +46,8 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
                const void *__restrict__ w, int w_bf16, int rows, int H,
                TDX *__restrict__ dx, float *__restrict__ partials, int want_cols)
 {
-    extern __shared__ float lds[];
-    float *red = lds;
-    float *slot = lds + kRedFloats;
-    const int teams = blockDim.x / kTeam;
-    const int team = threadIdx.x / kTeam;
-    const int tt = threadIdx.x - team * kTeam;
+    __shared__ float red[kRedFloats];
+    const int tt = threadIdx.x;
     const int wave = tt / kWave;
     const int lane = tt & (kWave - 1);
     const int G = gridDim.x;
@@ -68,8 +64,8 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
         for (int e = 0; e < VEC; ++e) { p[0][k][e] = 0.f; p[1][k][e] = 0.f; }
     }
 
-    const int iters = (int)ceil_div(rows, (int64_t)G * teams);
-    auto row_of = [&](int it) { return (it * G + (int)blockIdx.x) * teams + team; };
+    const int iters = (int)ceil_div(rows, (int64_t)G);
+    auto row_of = [&](int it) { return it * G + (int)blockIdx.x; };
 
     // One row in flight: its x/dy groups and its saved statistics.  The row
     // is read through buffer resources sized to the row (empty past the last
@@ -119,7 +115,7 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
                 }
             }
         }
-        team_sum2(red + (it & 1) * (kRedFloats / 2), team, wave, lane, a, bb);
+        team_sum2(red + (it & 1) * (kRedFloats / 2), wave, lane, a, bb);
         if (active && dx != nullptr) {
             const float ca = a * invH, cb = bb * invH;
             const size_t rowoff = (size_t)r * H;
@@ -141,7 +137,7 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
     };
 
     pipeline_rows<D, RowBuf>(iters, load_row, do_row);
-    if (want_cols) fold_and_write<VEC, MAXG, 2>(p, slot, teams, team, tt, Gr, H, G, partials);
+    if (want_cols) write_partials<VEC, MAXG, 2>(p, tt, Gr, H, G, partials);
 }
 
 // ---- RMSNorm, vector path ----------------------------------------------------
@@ -152,12 +148,8 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
                 int w_bf16, int rows, int H, T *__restrict__ dx,
                 float *__restrict__ partials, int want_cols)
 {
-    extern __shared__ float lds[];
-    float *red = lds;
-    float *slot = lds + kRedFloats;
-    const int teams = blockDim.x / kTeam;
-    const int team = threadIdx.x / kTeam;
-    const int tt = threadIdx.x - team * kTeam;
+    __shared__ float red[kRedFloats];
+    const int tt = threadIdx.x;
     const int wave = tt / kWave;
     const int lane = tt & (kWave - 1);
     const int G = gridDim.x;
@@ -174,8 +166,8 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
         for (int e = 0; e < VEC; ++e) p[0][k][e] = 0.f;
     }
 
-    const int iters = (int)ceil_div(rows, (int64_t)G * teams);
-    auto row_of = [&](int it) { return (it * G + (int)blockIdx.x) * teams + team; };
+    const int iters = (int)ceil_div(rows, (int64_t)G);
+    auto row_of = [&](int it) { return it * G + (int)blockIdx.x; };
 
     // One row in flight (see the LayerNorm kernel: branch-free buffer loads).
     struct RowBuf {
@@ -216,7 +208,7 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
                 }
             }
         }
-        team_sum2(red + (it & 1) * (kRedFloats / 2), team, wave, lane, sgx, q);
+        team_sum2(red + (it & 1) * (kRedFloats / 2), wave, lane, sgx, q);
         if (active) {
             const float rinv = rms != nullptr ? 1.0f / b.rms : 1.0f / sqrtf(fmaf(q, invH, eps));
             const float c = rinv * rinv * rinv * sgx * invH;
@@ -240,7 +232,7 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
     };
 
     pipeline_rows<D, RowBuf>(iters, load_row, do_row);
-    if (want_cols) fold_and_write<VEC, MAXG, 1>(p, slot, teams, team, tt, Gr, H, G, partials);
+    if (want_cols) write_partials<VEC, MAXG, 1>(p, tt, Gr, H, G, partials);
 }
 
 // ---- generic path: scalar accesses, any width, any alignment -------------------
@@ -287,7 +279,7 @@ rows_generic_kernel(int kind, const TDY *__restrict__ dy, const TX *__restrict__
                 b = fmaf(xv, xv, b);
             }
         }
-        team_sum2(red + (it & 1) * (kRedFloats / 2), 0, wave, lane, a, b);
+        team_sum2(red + (it & 1) * (kRedFloats / 2), wave, lane, a, b);
         float rinv = 0.f, c = 0.f;
         if (kind == 1) {
             rinv = rms != nullptr ? 1.0f / rms[r] : 1.0f / sqrtf(fmaf(b, invH, eps));
@@ -358,20 +350,12 @@ rows_colsum_kernel(const float *__restrict__ partials, int G, int H, TOUT *__res
 }
 
 // ---- host dispatch ---------------------------------------------------------------
-int rows_lds_bytes(const RowsCall &a)
-{
-    const int Q = rows_q(a.kind);
-    return (kRedFloats + (a.teams > 1 ? Q * a.cols : 0)) * (int)sizeof(float);
-}
-
-
 // With a.occupancy_out set, report how many 256-thread blocks of `kernel`
 // fit on a CU (registers, LDS) instead of launching it.
 template <typename K>
 static hipError_t occupancy(const RowsCall &a, K kernel)
 {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kernel, kTeam,
-                                                        (size_t)rows_lds_bytes(a));
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kernel, kTeam, 0);
 }
 
 template <typename TX, typename TDY, typename TDX, int VEC, int MAXG, int D>
@@ -380,7 +364,7 @@ static hipError_t ln_vec_d(const RowsCall &a, hipStream_t s)
     constexpr int MT = kTeam;
     auto kern = ln_rows_kernel<TX, TDY, TDX, VEC, MAXG, MT, D>;
     if (a.occupancy_out) return occupancy(a, kern);
-    return launch(NH_K_LN_ROWS, kern, dim3(a.blocks), dim3(a.teams * kTeam), (uint32_t)rows_lds_bytes(a), s,
+    return launch(NH_K_LN_ROWS, kern, dim3(a.blocks), dim3(kTeam), 0u, s,
                   static_cast<const TDY *>(a.dy), static_cast<const TX *>(a.x), a.mean, a.rstd,
                   a.w, a.w_t, a.rows, a.cols, static_cast<TDX *>(a.dx), a.partials,
                   (int)(a.dweight != nullptr || a.dbias != nullptr));
@@ -404,7 +388,7 @@ static hipError_t rms_vec_d(const RowsCall &a, hipStream_t s)
     constexpr int MT = kTeam;
     auto kern = rms_rows_kernel<T, VEC, MAXG, MT, D>;
     if (a.occupancy_out) return occupancy(a, kern);
-    return launch(NH_K_RMS_ROWS, kern, dim3(a.blocks), dim3(a.teams * kTeam), (uint32_t)rows_lds_bytes(a), s,
+    return launch(NH_K_RMS_ROWS, kern, dim3(a.blocks), dim3(kTeam), 0u, s,
                   static_cast<const T *>(a.dy), static_cast<const T *>(a.x), a.rms, a.eps, a.w,
                   a.w_t, a.rows, a.cols, static_cast<T *>(a.dx), a.partials,
                   (int)(a.dweight != nullptr));
