@@ -554,7 +554,7 @@ PROFILE_CMD_TRACE = ("rocprofv3 --kernel-trace --stats -f csv --kernel-include-r
                      "--no-cpu-baseline")
 PROFILE_CMD_PMC = ("rocprofv3 --pmc {counter} -f csv --kernel-include-regex \"nh::\" -d <dir> "
                    "-o bench_quick -- python3 bench.py --quick --steps 5 --warmup 2 --no-cpu-baseline")
-BN_SOURCES = ["bn_kernels.hip", "nh_device.hpp", "nh_internal.hpp"]
+BN_SOURCES = ["bn_kernels.hip", "nh_device.hpp", "nh_internal.hpp", "nh_bn.hpp"]
 PROFILE_CMD_ALL_TRACE = ("rocprofv3 --kernel-trace --stats -f csv -d <dir> -o bench_all -- "
                          "python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline")
 PROFILE_CMD_ALL_PMC = ("rocprofv3 --pmc {counter} -f csv --kernel-include-regex \"nh::\" -d <dir> "

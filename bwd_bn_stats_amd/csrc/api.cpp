@@ -13,7 +13,9 @@
 #include <string>
 #include <vector>
 
+#include "nh_bn.hpp"
 #include "nh_internal.hpp"
+#include "nh_rows.hpp"
 #include "normhip.h"
 
 using namespace nh;

@@ -47,7 +47,7 @@
 // No atomics anywhere: each reduction block writes its own partial slot, the
 // finalize kernels combine slots in index order, so results are
 // bit-identical run to run and the workspace needs no zeroing.
-#include "nh_internal.hpp"
+#include "nh_bn.hpp"
 
 namespace nh {
 

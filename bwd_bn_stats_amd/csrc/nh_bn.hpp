@@ -1,0 +1,86 @@
+// Host/device interface of the BatchNorm kernels (bn_kernels.hip): launch
+// geometry, the unit-to-address map shared with the host self test, and the
+// call record api.cpp fills.
+#pragma once
+
+#include "nh_internal.hpp"
+
+namespace nh {
+
+// ---- BatchNorm -------------------------------------------------------------
+constexpr int kBnThreads = 256;
+constexpr int kBnUnroll = 4;     // vector units in flight per thread
+
+// Blocks per channel for a channel of `units` vector units: enough blocks
+// that all C*grid_y blocks fill the device's resident slots once, but no
+// block gets less than one full unrolled sweep of its threads.
+inline int64_t bn_auto_grid_y(int64_t units, int64_t C, int64_t slots)
+{
+    int64_t per_channel = slots / (C > 0 ? C : 1);
+    if (per_channel < 1) per_channel = 1;
+    int64_t want = ceil_div(units, (int64_t)kBnThreads * kBnUnroll);
+    if (want < 1) want = 1;
+    return want < per_channel ? want : per_channel;
+}
+
+// Geometry of a BatchNorm launch: channel c's M elements in units of V
+// consecutive elements inside one plane, block (c, yb) owning units
+// [yb*upb, min((yb+1)*upb, units)).
+struct BnGeom {
+    int C;
+    int HW;
+    int HWv;        // units per plane
+    FastDiv div_hwv;
+    int units;      // units per channel (N * HWv)
+    int upb;        // units per block
+    int grid_y;
+};
+
+// Element offset of unit u of channel c.  Unsigned arithmetic: callers may
+// form the offset of a unit past the end (never dereferenced), which must
+// not be signed overflow.
+template <int V>
+__host__ __device__ __forceinline__ int bn_unit_offset(const BnGeom &g, int c, uint32_t u)
+{
+    const uint32_t n = g.div_hwv.div(u);
+    const uint32_t j = u - n * (uint32_t)g.HWv;
+    return (int)((n * (uint32_t)g.C + (uint32_t)c) * (uint32_t)g.HW + j * (uint32_t)V);
+}
+
+inline BnGeom make_bn_geom(int N, int C, int HW, int vec, int grid_y)
+{
+    BnGeom g;
+    g.C = C;
+    g.HW = HW;
+    g.HWv = HW / vec;
+    g.div_hwv = make_fastdiv((uint32_t)g.HWv);
+    g.units = N * g.HWv;
+    g.grid_y = grid_y;
+    g.upb = (int)ceil_div(g.units, grid_y);
+    return g;
+}
+
+struct BnCall {
+    int io;              // 0 fp32, 1 bf16
+    int N, C, HW;
+    int vec;             // vector width in elements (1, 4 or 8)
+    int grid_y;          // blocks per channel of the reduction and elementwise passes
+    int separate_finalize;  // 1: finalize as its own kernel; 0: in the elementwise prologue
+    int inference;       // forward only: apply with the running statistics, no reduction
+    int act;             // 0 none, 1 ReLU, 2 LeakyReLU
+    float slope;         // LeakyReLU negative slope
+    const void *x;
+    const void *dy;      // backward only
+    void *out;           // y (forward) or dx (backward; may be NULL)
+    const float *gamma, *beta;         // beta is also read by the backward with an activation
+    float *running_mean, *running_var;
+    float momentum, eps;
+    float *stats;        // [4, C]
+    float *grads;        // [4, C] (backward)
+    float *partials;     // [2, grid_y, C]
+};
+
+hipError_t bn_forward_launch(const BnCall &a, hipStream_t s);
+hipError_t bn_backward_launch(const BnCall &a, hipStream_t s);
+
+} // namespace nh

@@ -1,0 +1,87 @@
+// Host interface of the LayerNorm / RMSNorm row kernels (rows_kernels.hip,
+// rows_bda_kernels.hip, rows_fwd_kernels.hip): call records and planning
+// constants.
+#pragma once
+
+#include "nh_internal.hpp"
+
+namespace nh {
+
+// ---- LayerNorm / RMSNorm rows -------------------------------------------------
+struct RowsCall {
+    int kind;            // 0 LayerNorm, 1 RMSNorm, 2 bias + dropout + add + LayerNorm
+    int x_t, dy_t, w_t, dx_t;
+    int rows, cols;
+    int blocks;          // G: column-partial rows
+    int maxg;            // 16-byte groups per thread per row (vector path); 0 = generic path
+    int vec;             // elements per group
+    const void *x, *dy, *w;
+    const float *mean, *rstd;  // LayerNorm
+    const float *rms;          // RMSNorm (NULL: recompute)
+    float eps;
+    void *dx, *dweight, *dbias;  // kind 2: dx is da (dtype dy_t)
+    const float *dresidual;      // kind 2: fp32 [rows, cols] or NULL
+    const uint8_t *mask;         // kind 2: 0/1 bytes [rows, cols] or NULL
+    float scale;                 // kind 2: dropout scale
+    float *dh;                   // kind 2: fp32 [rows, cols] out or NULL
+    void *dbias_in;              // kind 2: [cols] of w_t out or NULL
+    float *partials;     // [Q, G, cols]
+    int depth;           // row-pipeline depth of the vector path (0 = the kernel's default)
+    int colsum_cols;     // columns per column-finalize block (0 = default)
+    int *occupancy_out;  // non-NULL: report resident 256-thread blocks per CU
+                         // of the selected row kernel instead of launching
+};
+
+hipError_t rows_backward_launch(const RowsCall &a, hipStream_t s);
+hipError_t bda_backward_launch(const RowsCall &a, hipStream_t s);
+// Column finalize of the Q = rows_q(kind) partial rows into dweight, dbias, dbias_in.
+hipError_t rows_colsum_launch(const RowsCall &a, int kid, hipStream_t s);
+// Column sums per kind: LayerNorm dweight, dbias; RMSNorm dweight;
+// bias + dropout + add + LayerNorm dweight, dbias, dbias_in.
+constexpr int rows_q(int kind) { return kind == 0 ? 2 : (kind == 1 ? 1 : 3); }
+
+// Block-size bound of a vector forward row-kernel variant: 1024 threads
+// (128 VGPRs per thread) when a thread holds at most 8 elements of a row,
+// else 512 (256 VGPRs).  The forward fills the device with blocks, so it
+// keeps registers low.
+constexpr int rows_max_threads(int maxg, int vec) { return maxg * vec <= 8 ? 1024 : 512; }
+// The backward row kernels run one 256-thread team per block at no more
+// than kRowsMaxBlocksPerCu blocks per CU, i.e. 2 waves per SIMD: each wave
+// may use up to 256 VGPRs for its pipelined rows, weights and column sums.
+constexpr int kRowsBwdWavesPerSimd = 2;
+// Row-kernel blocks per CU, at most: more blocks shorten the row kernel a
+// little but every block adds a partial row that the column finalize reads
+// back (measured on MI355X: 2 per CU is the best total for 1600..8192 wide
+// rows).
+constexpr int kRowsMaxBlocksPerCu = 2;
+// Per kind: RMSNorm's wide rows (8192) keep enough rows in flight with one
+// block per CU, and halving the partial rows saves more than the second
+// block gains (27.9 -> 26.1 us bf16, 44.4 -> 41.0 us fp32 at 2048 x 8192);
+// LayerNorm and the bias+dropout+add backward at 1600 columns need two.
+constexpr int rows_blocks_per_cu(int kind) { return kind == 1 ? 1 : kRowsMaxBlocksPerCu; }
+constexpr int kRowsMaxBlocks = 2048;
+// Row elements a thread holds in the vector row kernels: 32 for LayerNorm and
+// RMSNorm; 16 for the bias + dropout + add + LayerNorm backward, whose row
+// also carries the incoming gradient and the mask (32 would spill).
+constexpr int kRowsMaxRowElems = 32;
+constexpr int kBdaMaxRowElems = 16;
+
+// ---- LayerNorm / RMSNorm forward ---------------------------------------------------
+struct FwdCall {
+    int kind;            // 0 LayerNorm, 1 RMSNorm
+    int x_t, y_t, w_t;
+    int rows, cols;
+    int blocks;
+    int maxg;            // 16-byte groups per thread per row (vector path); 0 = generic path
+    int vec;
+    const void *x, *w, *b;
+    float eps;
+    void *y;
+    float *stat0, *stat1;  // LayerNorm: mean, rstd; RMSNorm: rms
+    int depth;             // row-pipeline depth of the vector path (0 = the kernel's default)
+    int *occupancy_out;    // non-NULL: report blocks per CU instead of launching
+};
+
+hipError_t rows_forward_launch(const FwdCall &a, hipStream_t s);
+
+} // namespace nh

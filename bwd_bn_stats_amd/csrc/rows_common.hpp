@@ -3,7 +3,7 @@
 // and its fixed-order row sums.
 #pragma once
 
-#include "nh_internal.hpp"
+#include "nh_rows.hpp"
 
 namespace nh {
 
