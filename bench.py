@@ -517,6 +517,25 @@ def bench_copy(nh, torch, nbytes, K, W):
     return {"bytes": 2 * nbytes, "avg_us": avg, "gbs": 2 * nbytes / (avg * 1e3)}
 
 
+def bench_read(nh, torch, n_floats, K, W):
+    """Calibration floor of a read-only reduction shaped like the stats pass
+    (nh_calib_read over n fp32, cold rotating buffers)."""
+    device = torch.device("cuda:0")
+    R = _nsets(4 * n_floats, True)
+    sets = [torch.ones(n_floats, device=device) for _ in range(R)]
+    sums = torch.empty(4096, device=device)
+    torch.cuda.synchronize()
+
+    def step(i):
+        nh.calib_read(sets[i % R], sums)
+
+    ms, per = Timed(nh, torch).run(step, K, W, ["calib"])
+    avg = per["calib"]["avg_us"]
+    del sets
+    torch.cuda.empty_cache()
+    return {"bytes": 4 * n_floats, "avg_us": avg, "gbs": 4 * n_floats / (avg * 1e3)}
+
+
 # ---- CPU baseline: the oracle on this host ----------------------------------------------
 def cpu_baseline(case, budget_s=12.0):
     import numpy as np
@@ -763,6 +782,13 @@ def main():
     warm = bench_bn(nh, torch, main_case, K, W, cold=False)
     log("[bench] calibration floor (two reads, one write, bn_dx-sized)")
     calib = bench_calib(nh, torch, main_case.N * main_case.C * main_case.hw, K, W)
+    log("[bench] read-only floors (stats-sized and grad_sums-sized)")
+    E = main_case.N * main_case.C * main_case.hw
+    read1, read2 = bench_read(nh, torch, E, K, W), bench_read(nh, torch, 2 * E, K, W)
+    for k, rd in (("bn_stats", read1), ("bn_grad_sums", read2)):
+        if k in cold["kernels"]:
+            cold["kernels"][k]["read_floor_gbs"] = round(rd["gbs"], 1)
+            cold["kernels"][k]["frac_of_read_floor"] = round(cold["kernels"][k]["gbs"] / rd["gbs"], 4)
 
     others = {}
     if not args.quick:

@@ -798,6 +798,22 @@ nh_status nh_calib_copy(const void *src, void *dst, size_t bytes, void *stream)
     return ok();
 }
 
+nh_status nh_calib_read(const float *a, int64_t n, float *block_sums, int64_t max_blocks, void *stream)
+{
+    if (n < 0 || max_blocks < 0) return fail(NH_ERR_SHAPE, "negative size");
+    if (n == 0) return ok();
+    if (!a || !block_sums) return fail(NH_ERR_NULL, "a and block_sums are required");
+    if (n % 4 != 0 || !aligned(a, 16)) return fail(NH_ERR_SHAPE, "n must be a multiple of 4, a 16-byte aligned");
+    if (max_blocks < 1) return fail(NH_ERR_SHAPE, "max_blocks must be >= 1");
+    DeviceInfo d;
+    nh_status st = device_info(&d);
+    if (st != NH_OK) return st;
+    hipError_t e = calib_read_launch(a, n, block_sums, max_blocks, (int)bn_slots(d),
+                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "nh_calib_read launch");
+    return ok();
+}
+
 nh_status nh_calib_add(const float *a, const float *b, float *out, int64_t n, void *stream)
 {
     if (n < 0) return fail(NH_ERR_SHAPE, "negative n");

@@ -75,6 +75,40 @@ calib_add1_kernel(const float *__restrict__ a, const float *__restrict__ b, floa
         o[i] = a[i] + b[i];
 }
 
+// A read-only reduction stream shaped like the BatchNorm stats pass: one
+// contiguous chunk per block, kCalibUnroll cacheable 16-byte loads in flight
+// per thread, a block sum at the end, one float written per block.
+__global__ void __launch_bounds__(kCalibThreads)
+calib_read4_kernel(const float4 *__restrict__ a, int64_t n4, int64_t chunk, float *__restrict__ sums)
+{
+    __shared__ float red[kCalibThreads / kWave];
+    const int64_t b0 = (int64_t)blockIdx.x * chunk;
+    const int64_t b1 = b0 + chunk < n4 ? b0 + chunk : n4;
+    float acc = 0.f;
+    for (int64_t base = b0 + threadIdx.x; base < b1; base += kCalibThreads * kCalibUnroll) {
+        float4 v[kCalibUnroll];
+#pragma unroll
+        for (int k = 0; k < kCalibUnroll; ++k) {
+            const int64_t i = base + k * kCalibThreads;
+            if (i < b1) v[k] = a[i];
+        }
+#pragma unroll
+        for (int k = 0; k < kCalibUnroll; ++k) {
+            const int64_t i = base + k * kCalibThreads;
+            if (i < b1) acc += (v[k].x + v[k].y) + (v[k].z + v[k].w);
+        }
+    }
+    acc = wave_sum(acc);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = red[0];
+#pragma unroll
+        for (int w = 1; w < kCalibThreads / kWave; ++w) t += red[w];
+        sums[blockIdx.x] = t;
+    }
+}
+
 static unsigned calib_grid(int64_t items, int slots)
 {
     int64_t g = ceil_div(items, (int64_t)kCalibThreads * kCalibUnroll);
@@ -108,6 +142,15 @@ hipError_t calib_add_launch(const float *a, const float *b, float *o, int64_t n,
     }
     return launch(NH_K_CALIB, calib_add1_kernel, dim3(calib_grid(n, slots)), dim3(kCalibThreads),
                   0u, s, a, b, o, n);
+}
+
+hipError_t calib_read_launch(const float *a, int64_t n, float *sums, int64_t max_blocks, int slots,
+                             hipStream_t s)
+{
+    int64_t cap = max_blocks < slots ? max_blocks : slots;
+    const unsigned grid = calib_grid(n / 4, (int)cap);
+    return launch(NH_K_CALIB, calib_read4_kernel, dim3(grid), dim3(kCalibThreads), 0u, s,
+                  (const float4 *)a, n / 4, ceil_div(n / 4, grid), sums);
 }
 
 } // namespace nh

@@ -34,5 +34,7 @@ __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + 
 // ---- calibration --------------------------------------------------------------
 hipError_t calib_copy_launch(const void *src, void *dst, size_t bytes, int slots, hipStream_t s);
 hipError_t calib_add_launch(const float *a, const float *b, float *o, int64_t n, int slots, hipStream_t s);
+hipError_t calib_read_launch(const float *a, int64_t n, float *sums, int64_t max_blocks, int slots,
+                             hipStream_t s);
 
 } // namespace nh

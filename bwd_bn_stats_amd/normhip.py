@@ -34,7 +34,8 @@ EXPORTS = [
     "layernorm_backward_workspace", "layernorm_backward",
     "bda_layernorm_backward_workspace", "bda_layernorm_backward",
     "rmsnorm_backward_workspace", "rmsnorm_backward", "layernorm_forward", "rmsnorm_forward",
-    "nh_timing_enable", "nh_timing_reserve", "nh_timing_read", "nh_calib_copy", "nh_calib_add",
+    "nh_timing_enable", "nh_timing_reserve", "nh_timing_read",
+    "nh_calib_copy", "nh_calib_add", "nh_calib_read",
     "nh_bn_plan", "nh_rows_plan", "nh_plan_override", "nh_selftest_host",
 ]
 
@@ -79,6 +80,7 @@ def _load():
         "nh_timing_read": (i32, [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
         "nh_calib_copy": (i32, [p, p, sz, p]),
         "nh_calib_add": (i32, [p, p, p, i64, p]),
+        "nh_calib_read": (i32, [p, i64, p, i64, p]),
         "nh_bn_plan": (i32, [i64, i64, i64, i32, ctypes.POINTER(ctypes.c_int)]),
         "nh_rows_plan": (i32, [i64, i64, ctypes.POINTER(ctypes.c_int)]),
         "nh_plan_override": (i32, [ctypes.c_char_p, i64]),
@@ -418,6 +420,11 @@ def timing_read(kernel) -> tuple[float, int]:
 def calib_copy(src, dst):
     _check(lib.nh_calib_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(),
                              _stream(src.device)), "nh_calib_copy")
+
+
+def calib_read(a, block_sums):
+    _check(lib.nh_calib_read(_ptr(a), a.numel(), _ptr(block_sums), block_sums.numel(),
+                             _stream(a.device)), "nh_calib_read")
 
 
 def calib_add(a, b, out):

@@ -377,12 +377,18 @@ nh_status nh_timing_read(int kernel, double *total_ms, int64_t *launches);
  * backward elementwise pass against a plain add with the same traffic):
  *   nh_calib_copy: dst[i] = src[i] for `bytes` bytes (16-byte multiples take
  *                  the vector path);
+ *   nh_calib_read: reads n fp32 elements (n a multiple of 4, a 16-byte
+ *                  aligned) with the BatchNorm stats pass's shape: one
+ *                  contiguous chunk per block, cacheable 16-byte loads, one
+ *                  block sum written to block_sums[b] per block b; at most
+ *                  max_blocks blocks (block_sums holds max_blocks floats);
  *   nh_calib_add:  out[i] = a[i] + b[i] over n fp32 elements (two reads, one
  *                  write).
  * Both are timed under NH_K_CALIB.
  */
 nh_status nh_calib_copy(const void *src, void *dst, size_t bytes, void *stream);
 nh_status nh_calib_add(const float *a, const float *b, float *out, int64_t n, void *stream);
+nh_status nh_calib_read(const float *a, int64_t n, float *block_sums, int64_t max_blocks, void *stream);
 
 /*
  * Launch plan of the BatchNorm reductions on the current device: the number
