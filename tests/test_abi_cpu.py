@@ -200,6 +200,11 @@ def test_measurement_validation():
     assert nh.lib.nh_calib_add(FAKE, FAKE, FAKE, -1, NULL) == NH_ERR_SHAPE
     assert nh.lib.nh_calib_add(NULL, NULL, NULL, 0, NULL) == NH_OK
     assert nh.lib.nh_calib_copy(NULL, FAKE, 16, NULL) == NH_ERR_NULL
+    assert nh.lib.nh_calib_read(FAKE, -4, FAKE, 8, NULL) == NH_ERR_SHAPE
+    assert nh.lib.nh_calib_read(NULL, 0, NULL, 0, NULL) == NH_OK
+    assert nh.lib.nh_calib_read(NULL, 8, FAKE, 8, NULL) == NH_ERR_NULL
+    assert nh.lib.nh_calib_read(FAKE, 6, FAKE, 8, NULL) == NH_ERR_SHAPE
+    assert nh.lib.nh_calib_read(FAKE, 8, FAKE, 0, NULL) == NH_ERR_SHAPE
     out = ctypes.c_size_t(123)
     assert nh.lib.bn_forward_train_workspace(0, 3, 4, ctypes.byref(out)) == NH_OK and out.value == 0
     assert nh.lib.bn_forward_train_workspace(-1, 3, 4, ctypes.byref(out)) == NH_ERR_SHAPE
