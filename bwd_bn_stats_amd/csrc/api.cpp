@@ -88,6 +88,7 @@ nh_status device_info(DeviceInfo *out)
 
 // ---- plan overrides ------------------------------------------------------------
 std::atomic<int64_t> g_override_bn_grid_y{0};
+std::atomic<int64_t> g_override_bn_ew_grid_y{0};
 std::atomic<int64_t> g_override_rows_blocks{0};
 std::atomic<int64_t> g_override_bn_finalize_kernels{0};
 std::atomic<int64_t> g_override_rows_depth{0};
@@ -103,11 +104,22 @@ int64_t bn_slots(const DeviceInfo &d)
     return (int64_t)d.cus * per_cu;
 }
 
+// Blocks per channel of the reduction passes (stats, grad_sums); the
+// workspace holds this many partial slots.
 int64_t bn_grid_y_for(int64_t units, int64_t C, const DeviceInfo &d)
 {
     const int64_t ov = g_override_bn_grid_y.load();
     if (ov > 0) return ov < units ? ov : units;
     return bn_auto_grid_y(units, C, bn_slots(d));
+}
+
+// Blocks per channel of the elementwise passes (apply, dx, inference): the
+// reductions' split unless a tuning override sets its own.
+int64_t bn_ew_grid_y_for(int64_t units, int64_t C, const DeviceInfo &d)
+{
+    const int64_t ov = g_override_bn_ew_grid_y.load();
+    if (ov > 0) return ov < units ? ov : units;
+    return bn_grid_y_for(units, C, d);
 }
 
 // Largest grid_y any dtype/alignment can take for this shape (scalar units).
@@ -313,6 +325,7 @@ nh_status bn_act_forward_train(const void *x, void *y, nh_dtype io, int64_t N, i
     a.HW = (int)HW;
     a.vec = bn_vec(io, HW, x, y, nullptr);
     a.grid_y = (int)bn_grid_y_for(N * (HW / a.vec), C, d);
+    a.ew_grid_y = (int)bn_ew_grid_y_for(N * (HW / a.vec), C, d);
     a.x = x;
     a.out = y;
     a.gamma = gamma;
@@ -364,6 +377,7 @@ nh_status bn_act_backward(const void *dy, const void *x, nh_dtype io, int64_t N,
     a.HW = (int)HW;
     a.vec = bn_vec(io, HW, x, dy, dx);
     a.grid_y = (int)bn_grid_y_for(N * (HW / a.vec), C, d);
+    a.ew_grid_y = (int)bn_ew_grid_y_for(N * (HW / a.vec), C, d);
     a.x = x;
     a.dy = dy;
     a.out = dx;
@@ -409,6 +423,7 @@ nh_status bn_forward_infer(const void *x, void *y, nh_dtype io, int64_t N, int64
     a.HW = (int)HW;
     a.vec = bn_vec(io, HW, x, y, nullptr);
     a.grid_y = (int)bn_grid_y_for(N * (HW / a.vec), C, d);
+    a.ew_grid_y = (int)bn_ew_grid_y_for(N * (HW / a.vec), C, d);
     a.inference = 1;
     a.x = x;
     a.out = y;
@@ -858,6 +873,7 @@ nh_status nh_plan_override(const char *key, int64_t value)
     if (!key) return fail(NH_ERR_NULL, "key is NULL");
     if (value < 0) return fail(NH_ERR_ARG, "value must be >= 0");
     if (strcmp(key, "bn_grid_y") == 0) g_override_bn_grid_y.store(value);
+    else if (strcmp(key, "bn_ew_grid_y") == 0) g_override_bn_ew_grid_y.store(value);
     else if (strcmp(key, "rows_blocks") == 0) g_override_rows_blocks.store(value);
     else if (strcmp(key, "rows_depth") == 0) {
         if (value < 0 || value > 4) return fail(NH_ERR_ARG, "rows_depth must be 0..4");
@@ -903,7 +919,7 @@ nh_status nh_selftest_host(void)
             const int64_t cap = slots / C > 1 ? slots / C : 1;
             if (g < 1 || g > cap || g > u) return fail(NH_ERR_ARG, "bn grid %lld for C=%lld u=%lld",
                                                       (long long)g, (long long)C, (long long)u);
-            if (u >= cap * kBnThreads * kBnUnroll && g != cap)
+            if (u >= cap * kBnMinUnits && g != cap)
                 return fail(NH_ERR_ARG, "bn grid underfills: %lld", (long long)g);
         }
     // BatchNorm unit walk at the largest shapes the ABI accepts: for every
@@ -923,23 +939,26 @@ nh_status nh_selftest_host(void)
         const int64_t total = (int64_t)m.N * m.C * m.HW;
         if (total >= kMaxElems) return fail(NH_ERR_ARG, "max shape exceeds the element limit");
         const int64_t units = (int64_t)m.N * (m.HW / m.vec);
-        const int grid_y = (int)bn_auto_grid_y(units, m.C, slots);
-        const BnGeom g = make_bn_geom(m.N, m.C, m.HW, m.vec, grid_y);
-        const uint64_t stride = (uint64_t)kBnThreads * kBnUnroll;
-        for (int c = 0; c < m.C; c += (m.C > 1 ? m.C - 1 : 1)) {
-            for (int yb = 0; yb < g.grid_y; ++yb) {
-                const uint64_t u0 = (uint64_t)yb * (uint64_t)g.upb;
-                const uint64_t u1 = std::min<uint64_t>(u0 + (uint64_t)g.upb, (uint64_t)g.units);
-                if (u0 + (uint64_t)g.upb >= (1ull << 32) || u1 + stride >= (1ull << 32))
-                    return fail(NH_ERR_ARG, "bn unit index wraps (C=%d yb=%d)", c, yb);
-                if (u0 >= u1) continue;
-                const uint32_t probe[] = {(uint32_t)u0, (uint32_t)(u1 - 1)};
-                for (uint32_t u : probe) {
-                    const int64_t off = m.vec == 1 ? bn_unit_offset<1>(g, c, u)
-                                        : (m.vec == 4 ? bn_unit_offset<4>(g, c, u) : bn_unit_offset<8>(g, c, u));
-                    const int64_t n = u / (uint32_t)g.HWv, j = u % (uint32_t)g.HWv;
-                    if (off != (n * m.C + c) * m.HW + j * m.vec || off < 0 || off + m.vec > total)
-                        return fail(NH_ERR_ARG, "bn unit offset out of range (u=%u)", u);
+        // one block per channel, the planned split, and 2048 blocks per channel
+        for (int64_t grid_y : {(int64_t)1, bn_auto_grid_y(units, m.C, slots),
+                               std::min<int64_t>(units, 2048)}) {
+            const BnGeom g = make_bn_geom(m.N, m.C, m.HW, m.vec, (int)grid_y);
+            const uint64_t stride = (uint64_t)kBnThreads * kBnUnroll;
+            for (int c = 0; c < m.C; c += (m.C > 1 ? m.C - 1 : 1)) {
+                for (int yb = 0; yb < g.grid_y; ++yb) {
+                    const uint64_t u0 = (uint64_t)yb * (uint64_t)g.upb;
+                    const uint64_t u1 = std::min<uint64_t>(u0 + (uint64_t)g.upb, (uint64_t)g.units);
+                    if (u0 + (uint64_t)g.upb >= (1ull << 32) || u1 + stride >= (1ull << 32))
+                        return fail(NH_ERR_ARG, "bn unit index wraps (C=%d yb=%d)", c, yb);
+                    if (u0 >= u1) continue;
+                    const uint32_t probe[] = {(uint32_t)u0, (uint32_t)(u1 - 1)};
+                    for (uint32_t u : probe) {
+                        const int64_t off = m.vec == 1 ? bn_unit_offset<1>(g, c, u)
+                                            : (m.vec == 4 ? bn_unit_offset<4>(g, c, u) : bn_unit_offset<8>(g, c, u));
+                        const int64_t n = u / (uint32_t)g.HWv, j = u % (uint32_t)g.HWv;
+                        if (off != (n * m.C + c) * m.HW + j * m.vec || off < 0 || off + m.vec > total)
+                            return fail(NH_ERR_ARG, "bn unit offset out of range (u=%u)", u);
+                    }
                 }
             }
         }

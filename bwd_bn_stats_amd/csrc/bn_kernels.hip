@@ -319,6 +319,7 @@ bn_bwd_finalize(const float *__restrict__ partials, int grid_y, int C, int64_t M
 // chain at the cost of every block re-reading its channel's grid_y partials.
 struct FwdFinalizeArgs {
     const float *partials;
+    int red_grid_y;  // blocks per channel of the reduction that wrote the partials
     const float *gamma;
     float *running_mean, *running_var;
     float momentum, eps;
@@ -360,9 +361,9 @@ bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ 
         __shared__ float sh[2];
         if (threadIdx.x < kWave) {
             double S1, S2;
-            sum_partials(f.partials, g.grid_y, g.C, c, S1, S2);
+            sum_partials(f.partials, f.red_grid_y, g.C, c, S1, S2);
             if (threadIdx.x == 0) {
-                fwd_finalize_channel(S1, S2, f.partials[2 * g.grid_y * g.C + c], g.C, c, f.M, f.gamma,
+                fwd_finalize_channel(S1, S2, f.partials[2 * f.red_grid_y * g.C + c], g.C, c, f.M, f.gamma,
                                      f.running_mean, f.running_var, f.momentum, f.eps, yb == 0,
                                      stats, sh[0], sh[1]);
             }
@@ -407,8 +408,8 @@ template <typename T, int V, bool FUSED, int NT, int ACT>
 __global__ void __launch_bounds__(kBnThreads)
 bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ dx,
              const float *__restrict__ stats, float *__restrict__ grads, BnGeom g,
-             const float *__restrict__ partials, int64_t M, const float *__restrict__ beta,
-             float slope)
+             const float *__restrict__ partials, int red_grid_y, int64_t M,
+             const float *__restrict__ beta, float slope)
 {
     const int c = blockIdx.x / g.grid_y;
     const int yb = blockIdx.x - c * g.grid_y;
@@ -438,7 +439,7 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
         __shared__ float sh[2];
         if (threadIdx.x < kWave) {
             double Sdy, Sdyxc;
-            sum_partials(partials, g.grid_y, g.C, c, Sdy, Sdyxc);
+            sum_partials(partials, red_grid_y, g.C, c, Sdy, Sdyxc);
             if (threadIdx.x == 0)
                 bwd_finalize_channel(Sdy, Sdyxc, g.C, c, M, stats, yb == 0, grads, sh[0], sh[1]);
         }
@@ -480,20 +481,23 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
 }
 
 // ---- host launchers -----------------------------------------------------------
-static BnGeom make_geom(const BnCall &a) { return make_bn_geom(a.N, a.C, a.HW, a.vec, a.grid_y); }
-
+// The reductions run on a.grid_y blocks per channel, the elementwise passes on
+// a.ew_grid_y: the elementwise prologue reads the reduction's partial slots,
+// whatever its own split.
 template <typename T, int V, int ACT>
 static hipError_t bn_forward_t(const BnCall &a, hipStream_t s)
 {
-    const BnGeom g = make_geom(a);
+    const BnGeom gr = make_bn_geom(a.N, a.C, a.HW, a.vec, a.grid_y);
+    const BnGeom ge = make_bn_geom(a.N, a.C, a.HW, a.vec, a.ew_grid_y);
     const T *x = static_cast<const T *>(a.x);
-    const dim3 grid((unsigned)(a.C * a.grid_y)), block(kBnThreads);
+    const dim3 rgrid((unsigned)(a.C * a.grid_y)), egrid((unsigned)(a.C * a.ew_grid_y)), block(kBnThreads);
     const int64_t M = (int64_t)a.N * a.HW;
-    FwdFinalizeArgs f{a.partials, a.gamma, a.running_mean, a.running_var, a.momentum, a.eps, M};
+    FwdFinalizeArgs f{a.partials, a.grid_y, a.gamma, a.running_mean, a.running_var, a.momentum, a.eps, M};
     if (a.inference)
-        return launch(NH_K_BN_INFER, bn_apply_kernel<T, V, kApplyRunning, kBnNtPolicy, ACT>, grid, block,
-                      0, s, x, static_cast<T *>(a.out), a.stats, a.beta, g, f, a.slope);
-    hipError_t e = launch(NH_K_BN_STATS, bn_stats_kernel<T, V, kBnNtPolicy>, grid, block, 0, s, x, g, a.partials);
+        return launch(NH_K_BN_INFER, bn_apply_kernel<T, V, kApplyRunning, kBnNtPolicy, ACT>, egrid, block,
+                      0, s, x, static_cast<T *>(a.out), a.stats, a.beta, ge, f, a.slope);
+    hipError_t e = launch(NH_K_BN_STATS, bn_stats_kernel<T, V, kBnNtPolicy>, rgrid, block, 0, s, x, gr,
+                          a.partials);
     if (e != hipSuccess) return e;
     if (a.separate_finalize) {
         const dim3 fgrid((unsigned)ceil_div(a.C, kBnThreads / kWave));
@@ -501,22 +505,23 @@ static hipError_t bn_forward_t(const BnCall &a, hipStream_t s)
                    a.grid_y, a.C, M, a.gamma, a.running_mean, a.running_var, a.momentum,
                    a.eps, a.stats);
         if (e != hipSuccess) return e;
-        return launch(NH_K_BN_APPLY, bn_apply_kernel<T, V, kApplyStats, kBnNtPolicy, ACT>, grid, block, 0,
-                      s, x, static_cast<T *>(a.out), a.stats, a.beta, g, f, a.slope);
+        return launch(NH_K_BN_APPLY, bn_apply_kernel<T, V, kApplyStats, kBnNtPolicy, ACT>, egrid, block, 0,
+                      s, x, static_cast<T *>(a.out), a.stats, a.beta, ge, f, a.slope);
     }
-    return launch(NH_K_BN_APPLY, bn_apply_kernel<T, V, kApplyFinalize, kBnNtPolicy, ACT>, grid, block, 0,
-                  s, x, static_cast<T *>(a.out), a.stats, a.beta, g, f, a.slope);
+    return launch(NH_K_BN_APPLY, bn_apply_kernel<T, V, kApplyFinalize, kBnNtPolicy, ACT>, egrid, block, 0,
+                  s, x, static_cast<T *>(a.out), a.stats, a.beta, ge, f, a.slope);
 }
 
 template <typename T, int V, int ACT>
 static hipError_t bn_backward_t(const BnCall &a, hipStream_t s)
 {
-    const BnGeom g = make_geom(a);
+    const BnGeom gr = make_bn_geom(a.N, a.C, a.HW, a.vec, a.grid_y);
+    const BnGeom ge = make_bn_geom(a.N, a.C, a.HW, a.vec, a.ew_grid_y);
     const T *x = static_cast<const T *>(a.x);
     const T *dy = static_cast<const T *>(a.dy);
-    const dim3 grid((unsigned)(a.C * a.grid_y)), block(kBnThreads);
-    hipError_t e = launch(NH_K_BN_GRAD_SUMS, bn_grad_sums_kernel<T, V, kBnNtPolicy, ACT>, grid, block, 0,
-                          s, dy, x, a.stats, a.beta, a.slope, g, a.partials);
+    const dim3 rgrid((unsigned)(a.C * a.grid_y)), egrid((unsigned)(a.C * a.ew_grid_y)), block(kBnThreads);
+    hipError_t e = launch(NH_K_BN_GRAD_SUMS, bn_grad_sums_kernel<T, V, kBnNtPolicy, ACT>, rgrid, block, 0,
+                          s, dy, x, a.stats, a.beta, a.slope, gr, a.partials);
     if (e != hipSuccess) return e;
     const int64_t M = (int64_t)a.N * a.HW;
     if (a.separate_finalize || a.out == nullptr) {
@@ -524,11 +529,12 @@ static hipError_t bn_backward_t(const BnCall &a, hipStream_t s)
         e = launch(NH_K_BN_BWD_FINALIZE, bn_bwd_finalize, fgrid, block, 0, s, a.partials, a.grid_y,
                    a.C, M, a.stats, a.grads);
         if (e != hipSuccess || a.out == nullptr) return e;
-        return launch(NH_K_BN_DX, bn_dx_kernel<T, V, false, kBnNtPolicy, ACT>, grid, block, 0, s, dy, x,
-                      static_cast<T *>(a.out), a.stats, a.grads, g, a.partials, M, a.beta, a.slope);
+        return launch(NH_K_BN_DX, bn_dx_kernel<T, V, false, kBnNtPolicy, ACT>, egrid, block, 0, s, dy, x,
+                      static_cast<T *>(a.out), a.stats, a.grads, ge, a.partials, a.grid_y, M, a.beta,
+                      a.slope);
     }
-    return launch(NH_K_BN_DX, bn_dx_kernel<T, V, true, kBnNtPolicy, ACT>, grid, block, 0, s, dy, x,
-                  static_cast<T *>(a.out), a.stats, a.grads, g, a.partials, M, a.beta, a.slope);
+    return launch(NH_K_BN_DX, bn_dx_kernel<T, V, true, kBnNtPolicy, ACT>, egrid, block, 0, s, dy, x,
+                  static_cast<T *>(a.out), a.stats, a.grads, ge, a.partials, a.grid_y, M, a.beta, a.slope);
 }
 
 template <int ACT>

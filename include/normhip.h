@@ -392,8 +392,8 @@ nh_status nh_calib_read(const float *a, int64_t n, float *block_sums, int64_t ma
 
 /*
  * Launch plan of the BatchNorm reductions on the current device: the number
- * of blocks per channel (grid_y) that bn_forward_train / bn_backward use for
- * this shape and dtype.  Tests use it to cover single- and multi-block
+ * of blocks per channel (grid_y) that the stats and grad_sums passes of
+ * bn_forward_train / bn_backward use for this shape and dtype.  Tests use it to cover single- and multi-block
  * channels.
  */
 nh_status nh_bn_plan(int64_t N, int64_t C, int64_t HW, nh_dtype io, int *grid_y);
@@ -405,7 +405,8 @@ nh_status nh_rows_plan(int64_t rows, int64_t cols, int *blocks);
 
 /*
  * Plan overrides for tests and tuning sweeps: key "bn_grid_y" forces the
- * BatchNorm blocks per channel, key "rows_blocks" forces the row-kernel
+ * BatchNorm blocks per channel (reductions, and the elementwise passes unless
+ * "bn_ew_grid_y" forces those separately), key "rows_blocks" forces the row-kernel
  * block count (at most 2048 and at most one per row; both keys also size
  * the workspace queried afterwards), key
  * "bn_finalize_kernels" = 1 runs the BatchNorm finalize steps as separate

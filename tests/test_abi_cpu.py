@@ -193,6 +193,7 @@ def test_measurement_validation():
     assert nh.lib.nh_plan_override(b"nope", 3) == NH_ERR_ARG
     assert nh.lib.nh_plan_override(b"bn_grid_y", -1) == NH_ERR_ARG
     assert nh.lib.nh_plan_override(b"bn_grid_y", 0) == NH_OK
+    assert nh.lib.nh_plan_override(b"bn_ew_grid_y", 0) == NH_OK
     assert nh.lib.nh_plan_override(b"rows_depth", 5) == NH_ERR_ARG
     assert nh.lib.nh_plan_override(b"rows_depth", 0) == NH_OK
     assert nh.lib.nh_plan_override(b"colsum_cols", 12) == NH_ERR_ARG

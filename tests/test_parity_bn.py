@@ -129,6 +129,28 @@ def test_bn_forced_grid(nh, oracle_mod, grid_y):
     _compare(c, got, want)
 
 
+@pytest.mark.parametrize("red,ew,io", [(64, 3, wl.F32), (1, 100, wl.F32), (7, 7, wl.BF16),
+                                       (1000, 1, wl.BF16), (2, 257, wl.F32)])
+def test_bn_forced_split_grids(nh, oracle_mod, red, ew, io):
+    """Reductions and elementwise passes on different block splits: the
+    elementwise prologue finalizes from the reduction's partial slots."""
+    c = wl.bn_case(8, 4, 32, 33 if io == wl.F32 else 32, io, seed=44, x_mean=-1.0, x_std=0.7)
+    print(f"[bn parity] forced grid_y={red} ew_grid_y={ew} io={io}", flush=True)
+    want = _oracle_bn(oracle_mod, c)
+    nh.plan_override("bn_grid_y", red)
+    nh.plan_override("bn_ew_grid_y", ew)
+    try:
+        got = _gpu_bn(nh, c)
+        nh.plan_override("bn_finalize_kernels", 1)
+        got_sep = _gpu_bn(nh, c)
+    finally:
+        nh.plan_override("bn_grid_y", 0)
+        nh.plan_override("bn_ew_grid_y", 0)
+        nh.plan_override("bn_finalize_kernels", 0)
+    _compare(c, got, want)
+    _compare(c, got_sep, want)
+
+
 def test_bn_misaligned_pointers(nh, oracle_mod):
     """Tensors starting one element past a 16-byte boundary take the scalar path."""
     c = wl.bn_case(3, 4, 8, 8, wl.F32, seed=44)
