@@ -153,6 +153,7 @@ int bn_vec(int io, int64_t HW, const void *a, const void *b, const void *c)
 struct RowsPlan {
     int maxg = 0;   // 0 = generic path
     int vec = 1;
+    int team = kTeam;
     int blocks = 0;
 };
 
@@ -180,11 +181,17 @@ RowsPlan rows_variant(int64_t cols, int vec, bool vec_ok, int max_elems = kRowsM
     p.vec = vec;
     const int64_t groups = vec_ok && cols % vec == 0 ? cols / vec : -1;
     if (groups > 0) {
-        const int64_t per_thread = ceil_div(groups, 256);
+        const int64_t per_thread = ceil_div(groups, kTeam);
         int mg = 1;
         while (mg < per_thread) mg <<= 1;
         // A thread holds at most max_elems row elements in registers.
-        if (mg <= 8 && mg * vec <= max_elems) p.maxg = mg;
+        if (mg <= 8 && mg * vec <= max_elems) {
+            p.maxg = mg;
+        } else if (ceil_div(groups, kWideTeam) * vec <= max_elems) {
+            // Up to twice as wide: a 512-thread team at max_elems per thread.
+            p.team = kWideTeam;
+            p.maxg = max_elems / vec;
+        }
     }
     if (p.maxg == 0) p.vec = 1;
     return p;
@@ -512,14 +519,15 @@ static nh_status rows_run(RowsCall &a, int Q, void *ws, size_t ws_bytes, void *s
     RowsPlan p = rows_variant(a.cols, a.vec, vec_ok, a.kind == 2 ? kBdaMaxRowElems : kRowsMaxRowElems);
     a.maxg = p.maxg;
     a.vec = p.vec;
+    a.team = p.team;
     a.depth = (int)g_override_rows_depth.load();
     a.colsum_cols = (int)g_override_colsum_cols.load();
     // Occupancy of the chosen variant, cached per device and variant.
     int dev = 0;
     (void)hipGetDevice(&dev);
     const int dxt = a.dx != nullptr ? a.dx_t : a.dy_t;
-    const int64_t key = (((((((int64_t)dev * 4 + a.kind) * 2 + a.x_t) * 2 + a.dy_t) * 2 + dxt) * 16 +
-                          a.maxg) * 16 + a.vec) * 8 + a.depth;
+    const int64_t key = ((((((((int64_t)dev * 4 + a.kind) * 2 + a.x_t) * 2 + a.dy_t) * 2 + dxt) * 16 +
+                           a.maxg) * 16 + a.vec) * 8 + a.depth) * 2 + (a.team == kWideTeam);
     int occ = 0;
     {
         std::lock_guard<std::mutex> lk(g_dev_mu);
@@ -673,11 +681,12 @@ static nh_status rows_forward_run(FwdCall &a, void *stream)
     RowsPlan p = rows_variant(a.cols, a.vec, vec_ok);
     a.maxg = p.maxg;
     a.vec = p.vec;
+    a.team = p.team;
     a.depth = (int)g_override_rows_depth.load();
     int dev = 0;
     (void)hipGetDevice(&dev);
-    const int64_t key = -1 - ((((((((int64_t)dev * 2 + a.kind) * 2 + a.x_t) * 2 + a.y_t) * 16 + a.maxg) * 16) +
-                               a.vec) * 8 + a.depth);
+    const int64_t key = -1 - (((((((((int64_t)dev * 2 + a.kind) * 2 + a.x_t) * 2 + a.y_t) * 16 + a.maxg) * 16) +
+                                a.vec) * 8 + a.depth) * 2 + (a.team == kWideTeam));
     int occ = 0;
     {
         std::lock_guard<std::mutex> lk(g_dev_mu);

@@ -26,6 +26,7 @@ struct RowsCall {
     float *dh;                   // kind 2: fp32 [rows, cols] out or NULL
     void *dbias_in;              // kind 2: [cols] of w_t out or NULL
     float *partials;     // [Q, G, cols]
+    int team;            // threads per row team / block of the vector path (256 or 512)
     int depth;           // row-pipeline depth of the vector path (0 = the kernel's default)
     int colsum_cols;     // columns per column-finalize block (0 = default)
     int *occupancy_out;  // non-NULL: report resident 256-thread blocks per CU
@@ -65,6 +66,10 @@ constexpr int kRowsMaxBlocks = 2048;
 // also carries the incoming gradient and the mask (32 would spill).
 constexpr int kRowsMaxRowElems = 32;
 constexpr int kBdaMaxRowElems = 16;
+// Threads of a row team (one block): 256, or kWideTeam for rows too wide for
+// 256 threads at the element limit above (up to twice as wide).
+constexpr int kTeam = 256;
+constexpr int kWideTeam = 512;
 
 // ---- LayerNorm / RMSNorm forward ---------------------------------------------------
 struct FwdCall {
@@ -78,6 +83,7 @@ struct FwdCall {
     float eps;
     void *y;
     float *stat0, *stat1;  // LayerNorm: mean, rstd; RMSNorm: rms
+    int team;              // threads per row team / block of the vector path (256 or 512)
     int depth;             // row-pipeline depth of the vector path (0 = the kernel's default)
     int *occupancy_out;    // non-NULL: report blocks per CU instead of launching
 };

@@ -39,8 +39,8 @@ struct MaskGroup {
     }
 };
 
-template <typename TX, typename TDY, int VEC, int MAXG, int MAXT, int D>
-__global__ void __launch_bounds__(MAXT, kRowsBwdWavesPerSimd)
+template <typename TX, typename TDY, int VEC, int MAXG, int TEAM, int D>
+__global__ void __launch_bounds__(TEAM, kRowsBwdWavesPerSimd)
 bda_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
                 const float *__restrict__ mean, const float *__restrict__ rstd,
                 const void *__restrict__ w, int w_bf16, const float *__restrict__ dres,
@@ -48,7 +48,7 @@ bda_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
                 float *__restrict__ dh, TDY *__restrict__ da, float *__restrict__ partials,
                 int want_cols)
 {
-    __shared__ float red[kRedFloats];
+    __shared__ float red[red_floats(TEAM)];
     const int tt = threadIdx.x;
     const int wave = tt / kWave;
     const int lane = tt & (kWave - 1);
@@ -61,7 +61,7 @@ bda_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
     float p[3][MAXG][VEC];
 #pragma unroll
     for (int k = 0; k < MAXG; ++k) {
-        const int grp = tt + k * kTeam;
+        const int grp = tt + k * TEAM;
         if (grp < Gr) wv[k].load(w, w_bf16, grp * VEC);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) { p[0][k][e] = 0.f; p[1][k][e] = 0.f; p[2][k][e] = 0.f; }
@@ -89,7 +89,7 @@ bda_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
         const auto rm = make_rsrc(mask ? mask + rowoff : nullptr, live && mask ? (uint32_t)H : 0u);
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
-            const int grp = tt + k * kTeam;
+            const int grp = tt + k * TEAM;
             b.x[k].load_buf(rx, grp * VEC * (int)sizeof(TX));
             b.d[k].load_buf(rd, grp * VEC * (int)sizeof(TDY));
             b.r[k].load_buf(rr, grp * VEC * (int)sizeof(float));
@@ -106,7 +106,7 @@ bda_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
         float sa = 0.f, sb = 0.f;
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
-            const int grp = tt + k * kTeam;
+            const int grp = tt + k * TEAM;
             if (active && grp < Gr) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
@@ -120,13 +120,13 @@ bda_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
                 }
             }
         }
-        team_sum2(red + (it & 1) * (kRedFloats / 2), wave, lane, sa, sb);
+        team_sum2<TEAM / kWave>(red + (it & 1) * (red_floats(TEAM) / 2), wave, lane, sa, sb);
         if (!active) return;
         const float ca = sa * invH, cb = sb * invH;
         const size_t rowoff = (size_t)r * H;
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
-            const int grp = tt + k * kTeam;
+            const int grp = tt + k * TEAM;
             if (grp < Gr) {
                 float hv[VEC], av[VEC];
 #pragma unroll
@@ -144,7 +144,7 @@ bda_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
     };
 
     pipeline_rows<D, RowBuf>(iters, load_row, do_row);
-    if (want_cols) write_partials<VEC, MAXG, 3>(p, tt, Gr, H, G, partials);
+    if (want_cols) write_partials<VEC, MAXG, 3, TEAM>(p, tt, Gr, H, G, partials);
 }
 
 // Any width, any alignment: scalar accesses, two reads of each row (the
@@ -206,29 +206,32 @@ bda_generic_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
 }
 
 // ---- host dispatch ---------------------------------------------------------------
-template <typename TX, typename TDY, int VEC, int MAXG, int D>
+template <typename TX, typename TDY, int VEC, int MAXG, int TEAM, int D>
 static hipError_t bda_vec_d(const RowsCall &a, hipStream_t s)
 {
-    constexpr int MT = kTeam;
-    auto kern = bda_rows_kernel<TX, TDY, VEC, MAXG, MT, D>;
+    auto kern = bda_rows_kernel<TX, TDY, VEC, MAXG, TEAM, D>;
     if (a.occupancy_out)
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kern, kTeam, 0);
-    return launch(NH_K_BDA_ROWS, kern, dim3(a.blocks), dim3(kTeam), 0u, s, static_cast<const TDY *>(a.dy),
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kern, TEAM, 0);
+    return launch(NH_K_BDA_ROWS, kern, dim3(a.blocks), dim3(TEAM), 0u, s, static_cast<const TDY *>(a.dy),
                   static_cast<const TX *>(a.x), a.mean, a.rstd, a.w, a.w_t, a.dresidual, a.mask,
                   a.scale, a.rows, a.cols, a.dh, static_cast<TDY *>(a.dx), a.partials,
                   (int)(a.dweight != nullptr || a.dbias != nullptr || a.dbias_in != nullptr));
 }
 
-template <typename TX, typename TDY, int VEC, int MAXG>
+template <typename TX, typename TDY, int VEC, int MAXG, int TEAM = kTeam>
 static hipError_t bda_vec(const RowsCall &a, hipStream_t s)
 {
     // Row buffer: x, dy, the fp32 incoming gradient and the mask byte.
-    constexpr int DEF = rows_depth(MAXG * VEC * (int)(sizeof(TX) + sizeof(TDY) + 5));
-    switch (a.depth > 0 ? a.depth : DEF) {
-    case 1: return bda_vec_d<TX, TDY, VEC, MAXG, 1>(a, s);
-    case 2: return bda_vec_d<TX, TDY, VEC, MAXG, 2>(a, s);
-    case 3: return bda_vec_d<TX, TDY, VEC, MAXG, 3>(a, s);
-    default: return bda_vec_d<TX, TDY, VEC, MAXG, 4>(a, s);
+    constexpr int BYTES = MAXG * VEC * (int)(sizeof(TX) + sizeof(TDY) + 5);
+    if constexpr (TEAM != kTeam) {
+        return bda_vec_d<TX, TDY, VEC, MAXG, TEAM, rows_depth_wide(BYTES)>(a, s);
+    } else {
+        switch (a.depth > 0 ? a.depth : rows_depth(BYTES)) {
+        case 1: return bda_vec_d<TX, TDY, VEC, MAXG, TEAM, 1>(a, s);
+        case 2: return bda_vec_d<TX, TDY, VEC, MAXG, TEAM, 2>(a, s);
+        case 3: return bda_vec_d<TX, TDY, VEC, MAXG, TEAM, 3>(a, s);
+        default: return bda_vec_d<TX, TDY, VEC, MAXG, TEAM, 4>(a, s);
+        }
     }
 }
 
@@ -249,8 +252,13 @@ template <typename TX, typename TDY>
 static hipError_t bda_types(const RowsCall &a, hipStream_t s)
 {
     if (a.maxg == 0) return bda_generic<TX, TDY>(a, s);
-    // At most kBdaMaxRowElems row elements per thread (the planner sends
-    // wider rows to the generic path).
+    // At most kBdaMaxRowElems row elements per thread: a 256-thread team, or
+    // a 512-thread team for rows up to twice as wide; the planner sends wider
+    // rows to the generic path.
+    if (a.team == kWideTeam) {
+        if (a.vec == 4) return bda_vec<TX, TDY, 4, kBdaMaxRowElems / 4, kWideTeam>(a, s);
+        return bda_vec<TX, TDY, 8, kBdaMaxRowElems / 8, kWideTeam>(a, s);
+    }
     if (a.vec == 4) {
         switch (a.maxg) {
         case 1: return bda_vec<TX, TDY, 4, 1>(a, s);

@@ -7,9 +7,8 @@
 
 namespace nh {
 
-constexpr int kTeam = 256;
 constexpr int kTeamWaves = kTeam / kWave;
-constexpr int kRedFloats = 2 * kTeamWaves * 2;  // double-buffered row sums of two quantities
+constexpr int kRedFloats = 2 * kTeamWaves * 2;  // double-buffered row sums, 256-thread team
 
 __device__ __forceinline__ float load_param(const void *w, int w_bf16, int col)
 {
@@ -34,7 +33,11 @@ struct WeightGroup {
     __device__ __forceinline__ float get(int e) const { return v[e]; }
 };
 
-// Fixed-order sum of the 4 wave results of a team for two quantities.
+// LDS floats of a team's double-buffered row sums (two quantities per wave).
+constexpr int red_floats(int team) { return 2 * (team / kWave) * 2; }
+
+// Fixed-order sum of the WAVES wave results of a team for two quantities.
+template <int WAVES = kTeamWaves>
 __device__ __forceinline__ void team_sum2(float *red, int wave, int lane, float &a, float &b)
 {
     a = wave_sum(a);
@@ -47,7 +50,7 @@ __device__ __forceinline__ void team_sum2(float *red, int wave, int lane, float 
     float sa = red[0];
     float sb = red[1];
 #pragma unroll
-    for (int w = 1; w < kTeamWaves; ++w) {
+    for (int w = 1; w < WAVES; ++w) {
         sa += red[w * 2 + 0];
         sb += red[w * 2 + 1];
     }
@@ -85,18 +88,22 @@ constexpr int rows_depth(int row_bytes_per_thread)
 {
     return row_bytes_per_thread <= 32 ? 4 : (row_bytes_per_thread <= 64 ? 3 : (row_bytes_per_thread <= 256 ? 2 : 1));
 }
+// The 512-thread wide-row teams hold 32 elements per thread (16 for the
+// bias+dropout+add backward) at 2 waves per SIMD: depth 2 fits in 256 VGPRs
+// up to 192 bytes of row buffer per thread, beyond that depth 1.
+constexpr int rows_depth_wide(int row_bytes_per_thread) { return row_bytes_per_thread <= 192 ? 2 : 1; }
 // The forward kernels run up to 8 blocks per CU, so many rows are in flight
 // per CU already: depth 2 measured best (LayerNorm 1600, RMSNorm 8192).
 constexpr int kFwdDepth = 2;
 
 // Writes a block's column sums (Q quantities) as its row of partials[Q, G, H].
-template <int VEC, int MAXG, int Q>
+template <int VEC, int MAXG, int Q, int TEAM>
 __device__ __forceinline__ void write_partials(const float (&p)[Q][MAXG][VEC], int tt, int Gr, int H,
                                                int G, float *__restrict__ partials)
 {
 #pragma unroll
     for (int k = 0; k < MAXG; ++k) {
-        const int grp = tt + k * kTeam;
+        const int grp = tt + k * TEAM;
         if (grp < Gr)
 #pragma unroll
             for (int q = 0; q < Q; ++q)

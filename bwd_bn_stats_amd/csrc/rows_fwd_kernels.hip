@@ -36,13 +36,13 @@ struct ParamGroup {
 };
 
 // KIND 0: LayerNorm (stat0 = mean, stat1 = rstd); KIND 1: RMSNorm (stat0 = rms).
-template <int KIND, typename TX, typename TY, int VEC, int MAXG, int MT, int D>
+template <int KIND, typename TX, typename TY, int VEC, int MAXG, int MT, int D, int TEAM>
 __global__ void __launch_bounds__(MT)
 norm_fwd_rows_kernel(const TX *__restrict__ x, const void *__restrict__ w,
                      const void *__restrict__ b, int w_bf16, int rows, int H, float eps,
                      TY *__restrict__ y, float *__restrict__ stat0, float *__restrict__ stat1)
 {
-    __shared__ float red[kRedFloats];
+    __shared__ float red[red_floats(TEAM)];
     const int tt = threadIdx.x;
     const int wave = tt / kWave;
     const int lane = tt & (kWave - 1);
@@ -54,7 +54,7 @@ norm_fwd_rows_kernel(const TX *__restrict__ x, const void *__restrict__ w,
     ParamGroup<VEC> bv[KIND == 0 ? MAXG : 1];
 #pragma unroll
     for (int k = 0; k < MAXG; ++k) {
-        const int grp = tt + k * kTeam;
+        const int grp = tt + k * TEAM;
         if (grp < Gr) {
             wv[k].load(w, w_bf16, grp * VEC, 1.f);
             if constexpr (KIND == 0) bv[k].load(b, w_bf16, grp * VEC, 0.f);
@@ -73,7 +73,7 @@ norm_fwd_rows_kernel(const TX *__restrict__ x, const void *__restrict__ w,
         const size_t rowoff = (size_t)rc * H;
         const auto rx = make_rsrc(x + rowoff, live ? (uint32_t)(H * sizeof(TX)) : 0u);
 #pragma unroll
-        for (int k = 0; k < MAXG; ++k) rb.x[k].load_buf(rx, (tt + k * kTeam) * VEC * (int)sizeof(TX));
+        for (int k = 0; k < MAXG; ++k) rb.x[k].load_buf(rx, (tt + k * TEAM) * VEC * (int)sizeof(TX));
         rb.K = KIND == 0 ? to_f32(x[rowoff]) : 0.f;
     };
     auto do_row = [&](const RowBuf &rb, int it) {
@@ -82,7 +82,7 @@ norm_fwd_rows_kernel(const TX *__restrict__ x, const void *__restrict__ w,
         float s1 = 0.f, s2 = 0.f;
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
-            const int grp = tt + k * kTeam;
+            const int grp = tt + k * TEAM;
             if (active && grp < Gr) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
@@ -97,7 +97,7 @@ norm_fwd_rows_kernel(const TX *__restrict__ x, const void *__restrict__ w,
                 }
             }
         }
-        team_sum2(red + (it & 1) * (kRedFloats / 2), wave, lane, s1, s2);
+        team_sum2<TEAM / kWave>(red + (it & 1) * (red_floats(TEAM) / 2), wave, lane, s1, s2);
         if (!active) return;
         float a, c;  // y = fmaf(x - c, a*w, b) (LN) or y = (x*a)*w (RMS)
         if constexpr (KIND == 0) {
@@ -118,7 +118,7 @@ norm_fwd_rows_kernel(const TX *__restrict__ x, const void *__restrict__ w,
         const size_t rowoff = (size_t)r * H;
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
-            const int grp = tt + k * kTeam;
+            const int grp = tt + k * TEAM;
             if (grp < Gr) {
                 float o[VEC];
 #pragma unroll
@@ -198,26 +198,30 @@ norm_fwd_generic_kernel(const TX *__restrict__ x, const void *__restrict__ w,
 }
 
 // ---- host dispatch ------------------------------------------------------------------
-template <int KIND, typename TX, typename TY, int VEC, int MAXG, int D>
+template <int KIND, typename TX, typename TY, int VEC, int MAXG, int D, int TEAM>
 static hipError_t fwd_vec_d(const FwdCall &a, hipStream_t s)
 {
-    constexpr int MT = rows_max_threads(MAXG, VEC);
-    auto kern = norm_fwd_rows_kernel<KIND, TX, TY, VEC, MAXG, MT, D>;
+    constexpr int MT = rows_max_threads(MAXG, VEC) > TEAM ? rows_max_threads(MAXG, VEC) : TEAM;
+    auto kern = norm_fwd_rows_kernel<KIND, TX, TY, VEC, MAXG, MT, D, TEAM>;
     if (a.occupancy_out)
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kern, kTeam, 0);
-    return launch(KIND == 0 ? NH_K_LN_FWD : NH_K_RMS_FWD, kern, dim3(a.blocks), dim3(kTeam), 0u, s,
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kern, TEAM, 0);
+    return launch(KIND == 0 ? NH_K_LN_FWD : NH_K_RMS_FWD, kern, dim3(a.blocks), dim3(TEAM), 0u, s,
                   static_cast<const TX *>(a.x), a.w, a.b, a.w_t, a.rows, a.cols, a.eps,
                   static_cast<TY *>(a.y), a.stat0, a.stat1);
 }
 
-template <int KIND, typename TX, typename TY, int VEC, int MAXG>
+template <int KIND, typename TX, typename TY, int VEC, int MAXG, int TEAM = kTeam>
 static hipError_t fwd_vec(const FwdCall &a, hipStream_t s)
 {
-    switch (a.depth > 0 ? a.depth : kFwdDepth) {
-    case 1: return fwd_vec_d<KIND, TX, TY, VEC, MAXG, 1>(a, s);
-    case 2: return fwd_vec_d<KIND, TX, TY, VEC, MAXG, 2>(a, s);
-    case 3: return fwd_vec_d<KIND, TX, TY, VEC, MAXG, 3>(a, s);
-    default: return fwd_vec_d<KIND, TX, TY, VEC, MAXG, 4>(a, s);
+    if constexpr (TEAM != kTeam) {
+        return fwd_vec_d<KIND, TX, TY, VEC, MAXG, kFwdDepth, TEAM>(a, s);
+    } else {
+        switch (a.depth > 0 ? a.depth : kFwdDepth) {
+        case 1: return fwd_vec_d<KIND, TX, TY, VEC, MAXG, 1, TEAM>(a, s);
+        case 2: return fwd_vec_d<KIND, TX, TY, VEC, MAXG, 2, TEAM>(a, s);
+        case 3: return fwd_vec_d<KIND, TX, TY, VEC, MAXG, 3, TEAM>(a, s);
+        default: return fwd_vec_d<KIND, TX, TY, VEC, MAXG, 4, TEAM>(a, s);
+        }
     }
 }
 
@@ -235,6 +239,7 @@ static hipError_t fwd_generic(const FwdCall &a, hipStream_t s)
 template <int KIND, typename TX, typename TY, int VEC>
 static hipError_t fwd_maxg(const FwdCall &a, hipStream_t s)
 {
+    if (a.team == kWideTeam) return fwd_vec<KIND, TX, TY, VEC, kRowsMaxRowElems / VEC, kWideTeam>(a, s);
     switch (a.maxg) {
     case 1: return fwd_vec<KIND, TX, TY, VEC, 1>(a, s);
     case 2: return fwd_vec<KIND, TX, TY, VEC, 2>(a, s);

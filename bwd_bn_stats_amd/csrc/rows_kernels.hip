@@ -39,14 +39,14 @@ namespace nh {
 // loads of its rows i+1 .. i+D-1 are already in flight (D register sets,
 // used in rotation), so each team keeps D rows of HBM traffic outstanding
 // across the block barrier of the row sum.
-template <typename TX, typename TDY, typename TDX, int VEC, int MAXG, int MAXT, int D>
-__global__ void __launch_bounds__(MAXT, kRowsBwdWavesPerSimd)
+template <typename TX, typename TDY, typename TDX, int VEC, int MAXG, int TEAM, int D>
+__global__ void __launch_bounds__(TEAM, kRowsBwdWavesPerSimd)
 ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
                const float *__restrict__ mean, const float *__restrict__ rstd,
                const void *__restrict__ w, int w_bf16, int rows, int H,
                TDX *__restrict__ dx, float *__restrict__ partials, int want_cols)
 {
-    __shared__ float red[kRedFloats];
+    __shared__ float red[red_floats(TEAM)];
     const int tt = threadIdx.x;
     const int wave = tt / kWave;
     const int lane = tt & (kWave - 1);
@@ -58,7 +58,7 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
     float p[2][MAXG][VEC];
 #pragma unroll
     for (int k = 0; k < MAXG; ++k) {
-        const int grp = tt + k * kTeam;
+        const int grp = tt + k * TEAM;
         if (grp < Gr) wv[k].load(w, w_bf16, grp * VEC);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) { p[0][k][e] = 0.f; p[1][k][e] = 0.f; }
@@ -86,7 +86,7 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
         const auto rd = make_rsrc(dy + rowoff, live ? (uint32_t)(H * sizeof(TDY)) : 0u);
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
-            const int grp = tt + k * kTeam;
+            const int grp = tt + k * TEAM;
             b.x[k].load_buf(rx, grp * VEC * (int)sizeof(TX));
             b.d[k].load_buf(rd, grp * VEC * (int)sizeof(TDY));
         }
@@ -101,7 +101,7 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
         float a = 0.f, bb = 0.f;
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
-            const int grp = tt + k * kTeam;
+            const int grp = tt + k * TEAM;
             if (active && grp < Gr) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
@@ -115,13 +115,13 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
                 }
             }
         }
-        team_sum2(red + (it & 1) * (kRedFloats / 2), wave, lane, a, bb);
+        team_sum2<TEAM / kWave>(red + (it & 1) * (red_floats(TEAM) / 2), wave, lane, a, bb);
         if (active && dx != nullptr) {
             const float ca = a * invH, cb = bb * invH;
             const size_t rowoff = (size_t)r * H;
 #pragma unroll
             for (int k = 0; k < MAXG; ++k) {
-                const int grp = tt + k * kTeam;
+                const int grp = tt + k * TEAM;
                 if (grp < Gr) {
                     float o[VEC];
 #pragma unroll
@@ -137,18 +137,18 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
     };
 
     pipeline_rows<D, RowBuf>(iters, load_row, do_row);
-    if (want_cols) write_partials<VEC, MAXG, 2>(p, tt, Gr, H, G, partials);
+    if (want_cols) write_partials<VEC, MAXG, 2, TEAM>(p, tt, Gr, H, G, partials);
 }
 
 // ---- RMSNorm, vector path ----------------------------------------------------
-template <typename T, int VEC, int MAXG, int MAXT, int D>
-__global__ void __launch_bounds__(MAXT, kRowsBwdWavesPerSimd)
+template <typename T, int VEC, int MAXG, int TEAM, int D>
+__global__ void __launch_bounds__(TEAM, kRowsBwdWavesPerSimd)
 rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
                 const float *__restrict__ rms, float eps, const void *__restrict__ w,
                 int w_bf16, int rows, int H, T *__restrict__ dx,
                 float *__restrict__ partials, int want_cols)
 {
-    __shared__ float red[kRedFloats];
+    __shared__ float red[red_floats(TEAM)];
     const int tt = threadIdx.x;
     const int wave = tt / kWave;
     const int lane = tt & (kWave - 1);
@@ -160,7 +160,7 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
     float p[1][MAXG][VEC];
 #pragma unroll
     for (int k = 0; k < MAXG; ++k) {
-        const int grp = tt + k * kTeam;
+        const int grp = tt + k * TEAM;
         if (grp < Gr) wv[k].load(w, w_bf16, grp * VEC);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) p[0][k][e] = 0.f;
@@ -185,7 +185,7 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
         const auto rd = make_rsrc(dy + rowoff, nbytes);
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
-            const int grp = tt + k * kTeam;
+            const int grp = tt + k * TEAM;
             b.x[k].load_buf(rx, grp * VEC * (int)sizeof(T));
             b.d[k].load_buf(rd, grp * VEC * (int)sizeof(T));
         }
@@ -198,7 +198,7 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
         float sgx = 0.f, q = 0.f;  // sum g*x, sum x^2
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
-            const int grp = tt + k * kTeam;
+            const int grp = tt + k * TEAM;
             if (active && grp < Gr) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
@@ -208,14 +208,14 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
                 }
             }
         }
-        team_sum2(red + (it & 1) * (kRedFloats / 2), wave, lane, sgx, q);
+        team_sum2<TEAM / kWave>(red + (it & 1) * (red_floats(TEAM) / 2), wave, lane, sgx, q);
         if (active) {
             const float rinv = rms != nullptr ? 1.0f / b.rms : 1.0f / sqrtf(fmaf(q, invH, eps));
             const float c = rinv * rinv * rinv * sgx * invH;
             const size_t rowoff = (size_t)r * H;
 #pragma unroll
             for (int k = 0; k < MAXG; ++k) {
-                const int grp = tt + k * kTeam;
+                const int grp = tt + k * TEAM;
                 if (grp < Gr) {
                     float o[VEC];
 #pragma unroll
@@ -232,7 +232,7 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
     };
 
     pipeline_rows<D, RowBuf>(iters, load_row, do_row);
-    if (want_cols) write_partials<VEC, MAXG, 1>(p, tt, Gr, H, G, partials);
+    if (want_cols) write_partials<VEC, MAXG, 1, TEAM>(p, tt, Gr, H, G, partials);
 }
 
 // ---- generic path: scalar accesses, any width, any alignment -------------------
@@ -350,67 +350,78 @@ rows_colsum_kernel(const float *__restrict__ partials, int G, int H, TOUT *__res
 }
 
 // ---- host dispatch ---------------------------------------------------------------
-// With a.occupancy_out set, report how many 256-thread blocks of `kernel`
-// fit on a CU (registers, LDS) instead of launching it.
+// With a.occupancy_out set, report how many blocks of `kernel` (of `team`
+// threads) fit on a CU (registers, LDS) instead of launching it.
 template <typename K>
-static hipError_t occupancy(const RowsCall &a, K kernel)
+static hipError_t occupancy(const RowsCall &a, K kernel, int team = kTeam)
 {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kernel, kTeam, 0);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kernel, team, 0);
 }
 
-template <typename TX, typename TDY, typename TDX, int VEC, int MAXG, int D>
+template <typename TX, typename TDY, typename TDX, int VEC, int MAXG, int TEAM, int D>
 static hipError_t ln_vec_d(const RowsCall &a, hipStream_t s)
 {
-    constexpr int MT = kTeam;
-    auto kern = ln_rows_kernel<TX, TDY, TDX, VEC, MAXG, MT, D>;
-    if (a.occupancy_out) return occupancy(a, kern);
-    return launch(NH_K_LN_ROWS, kern, dim3(a.blocks), dim3(kTeam), 0u, s,
+    auto kern = ln_rows_kernel<TX, TDY, TDX, VEC, MAXG, TEAM, D>;
+    if (a.occupancy_out) return occupancy(a, kern, TEAM);
+    return launch(NH_K_LN_ROWS, kern, dim3(a.blocks), dim3(TEAM), 0u, s,
                   static_cast<const TDY *>(a.dy), static_cast<const TX *>(a.x), a.mean, a.rstd,
                   a.w, a.w_t, a.rows, a.cols, static_cast<TDX *>(a.dx), a.partials,
                   (int)(a.dweight != nullptr || a.dbias != nullptr));
 }
 
-template <typename TX, typename TDY, typename TDX, int VEC, int MAXG>
+// Pipeline depth: the kernel's default, or the rows_depth override (256-thread
+// teams; the 512-thread wide-row teams always run their default).
+template <typename TX, typename TDY, typename TDX, int VEC, int MAXG, int TEAM = kTeam>
 static hipError_t ln_vec(const RowsCall &a, hipStream_t s)
 {
-    constexpr int DEF = rows_depth(MAXG * VEC * (int)(sizeof(TX) + sizeof(TDY)));
-    switch (a.depth > 0 ? a.depth : DEF) {
-    case 1: return ln_vec_d<TX, TDY, TDX, VEC, MAXG, 1>(a, s);
-    case 2: return ln_vec_d<TX, TDY, TDX, VEC, MAXG, 2>(a, s);
-    case 3: return ln_vec_d<TX, TDY, TDX, VEC, MAXG, 3>(a, s);
-    default: return ln_vec_d<TX, TDY, TDX, VEC, MAXG, 4>(a, s);
+    constexpr int BYTES = MAXG * VEC * (int)(sizeof(TX) + sizeof(TDY));
+    if constexpr (TEAM != kTeam) {
+        return ln_vec_d<TX, TDY, TDX, VEC, MAXG, TEAM, rows_depth_wide(BYTES)>(a, s);
+    } else {
+        switch (a.depth > 0 ? a.depth : rows_depth(BYTES)) {
+        case 1: return ln_vec_d<TX, TDY, TDX, VEC, MAXG, TEAM, 1>(a, s);
+        case 2: return ln_vec_d<TX, TDY, TDX, VEC, MAXG, TEAM, 2>(a, s);
+        case 3: return ln_vec_d<TX, TDY, TDX, VEC, MAXG, TEAM, 3>(a, s);
+        default: return ln_vec_d<TX, TDY, TDX, VEC, MAXG, TEAM, 4>(a, s);
+        }
     }
 }
 
-template <typename T, int VEC, int MAXG, int D>
+template <typename T, int VEC, int MAXG, int TEAM, int D>
 static hipError_t rms_vec_d(const RowsCall &a, hipStream_t s)
 {
-    constexpr int MT = kTeam;
-    auto kern = rms_rows_kernel<T, VEC, MAXG, MT, D>;
-    if (a.occupancy_out) return occupancy(a, kern);
-    return launch(NH_K_RMS_ROWS, kern, dim3(a.blocks), dim3(kTeam), 0u, s,
+    auto kern = rms_rows_kernel<T, VEC, MAXG, TEAM, D>;
+    if (a.occupancy_out) return occupancy(a, kern, TEAM);
+    return launch(NH_K_RMS_ROWS, kern, dim3(a.blocks), dim3(TEAM), 0u, s,
                   static_cast<const T *>(a.dy), static_cast<const T *>(a.x), a.rms, a.eps, a.w,
                   a.w_t, a.rows, a.cols, static_cast<T *>(a.dx), a.partials,
                   (int)(a.dweight != nullptr));
 }
 
-template <typename T, int VEC, int MAXG>
+template <typename T, int VEC, int MAXG, int TEAM = kTeam>
 static hipError_t rms_vec(const RowsCall &a, hipStream_t s)
 {
-    constexpr int DEF = rows_depth(MAXG * VEC * 2 * (int)sizeof(T));
-    switch (a.depth > 0 ? a.depth : DEF) {
-    case 1: return rms_vec_d<T, VEC, MAXG, 1>(a, s);
-    case 2: return rms_vec_d<T, VEC, MAXG, 2>(a, s);
-    case 3: return rms_vec_d<T, VEC, MAXG, 3>(a, s);
-    default: return rms_vec_d<T, VEC, MAXG, 4>(a, s);
+    constexpr int BYTES = MAXG * VEC * 2 * (int)sizeof(T);
+    if constexpr (TEAM != kTeam) {
+        return rms_vec_d<T, VEC, MAXG, TEAM, rows_depth_wide(BYTES)>(a, s);
+    } else {
+        switch (a.depth > 0 ? a.depth : rows_depth(BYTES)) {
+        case 1: return rms_vec_d<T, VEC, MAXG, TEAM, 1>(a, s);
+        case 2: return rms_vec_d<T, VEC, MAXG, TEAM, 2>(a, s);
+        case 3: return rms_vec_d<T, VEC, MAXG, TEAM, 3>(a, s);
+        default: return rms_vec_d<T, VEC, MAXG, TEAM, 4>(a, s);
+        }
     }
 }
 
-// The widest vector variant holds 32 row elements per thread (MAXG = 8 only
-// with 4-element groups); the planner sends wider rows to the generic path.
+// A 256-thread team holds at most 32 row elements per thread (MAXG = 8 only
+// with 4-element groups); rows up to twice as wide take a 512-thread team at
+// 32 elements per thread (a.team == kWideTeam); wider rows take the generic
+// path.
 template <typename TX, typename TDY, typename TDX, int VEC>
 static hipError_t ln_maxg(const RowsCall &a, hipStream_t s)
 {
+    if (a.team == kWideTeam) return ln_vec<TX, TDY, TDX, VEC, kRowsMaxRowElems / VEC, kWideTeam>(a, s);
     switch (a.maxg) {
     case 1: return ln_vec<TX, TDY, TDX, VEC, 1>(a, s);
     case 2: return ln_vec<TX, TDY, TDX, VEC, 2>(a, s);
@@ -421,11 +432,10 @@ static hipError_t ln_maxg(const RowsCall &a, hipStream_t s)
     }
 }
 
-// A thread holds at most 32 row elements in the vector path (64 would not
-// fit the registers); the planner sends wider rows to the generic path.
 template <typename T, int VEC>
 static hipError_t rms_maxg(const RowsCall &a, hipStream_t s)
 {
+    if (a.team == kWideTeam) return rms_vec<T, VEC, kRowsMaxRowElems / VEC, kWideTeam>(a, s);
     switch (a.maxg) {
     case 1: return rms_vec<T, VEC, 1>(a, s);
     case 2: return rms_vec<T, VEC, 2>(a, s);

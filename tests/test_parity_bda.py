@@ -170,3 +170,10 @@ def test_bda_pipeline_depths(nh, oracle_mod, depth):
         _bda_case(nh, oracle_mod, wl.bda_case(1037, 1600, seed=87), override_blocks=100)
     finally:
         nh.plan_override("rows_depth", 0)
+
+
+@pytest.mark.parametrize("rows,cols,xt", [(64, 8192, wl.BF16), (50, 6144, wl.F32), (33, 8192, wl.F32)])
+def test_bda_wide_rows(nh, oracle_mod, rows, cols, xt):
+    """Rows too wide for 16 elements per thread in a 256-thread team take a
+    512-thread team."""
+    _bda_case(nh, oracle_mod, wl.bda_case(rows, cols, x_t=xt, dy_t=xt, w_t=wl.BF16, seed=rows + cols))

@@ -168,3 +168,11 @@ def test_forward_pipeline_depths(nh, oracle_mod, depth):
                                                     seed=76))
     finally:
         nh.plan_override("rows_depth", 0)
+
+
+@pytest.mark.parametrize("rows,cols,dt", [(64, 16384, wl.F32), (80, 12288, wl.BF16), (9, 32768, wl.BF16)])
+def test_forward_wide_rows(nh, oracle_mod, rows, cols, dt):
+    c = wl.rows_case(rows, cols, x_t=dt, dy_t=dt, w_t=wl.BF16, seed=rows + 7 * cols, with_bias=True)
+    _ln_fwd_case(nh, oracle_mod, c, dt)
+    r = wl.rows_case(rows, cols, x_t=dt, dy_t=dt, w_t=dt, seed=rows + 9 * cols)
+    _rms_fwd_case(nh, oracle_mod, r)

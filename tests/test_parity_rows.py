@@ -231,3 +231,16 @@ def test_rows_colsum_widths(nh, oracle_mod, cx):
         _ln_case(nh, oracle_mod, c, wl.F32, override_blocks=300)
     finally:
         nh.plan_override("colsum_cols", 0)
+
+
+@pytest.mark.parametrize("rows,cols,xt,dyt", [(64, 16384, wl.F32, wl.BF16), (96, 12288, wl.BF16, wl.BF16),
+                                              (40, 16384, wl.F32, wl.F32), (70, 10240, wl.BF16, wl.F32),
+                                              (9, 32768, wl.BF16, wl.BF16)])
+def test_wide_rows(nh, oracle_mod, rows, cols, xt, dyt):
+    """Rows too wide for a 256-thread team: 512-thread teams up to 16384
+    columns, the generic kernel beyond (32768)."""
+    c = wl.rows_case(rows, cols, x_t=xt, dy_t=dyt, w_t=wl.BF16, seed=rows + cols)
+    _ln_case(nh, oracle_mod, c, wl.F32)
+    r = wl.rows_case(rows, cols, x_t=xt, dy_t=xt, w_t=xt, seed=rows * 3 + cols)
+    _rms_case(nh, oracle_mod, r, saved=True)
+    _rms_case(nh, oracle_mod, r, saved=False)
