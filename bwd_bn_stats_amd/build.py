@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libnormhip.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "bn_kernels.hip", "rows_kernels.hip", "rows_fwd_kernels.hip", "rows_bda_kernels.hip",
-           "calib_kernels.hip"]
+           "rows_generic_kernels.hip", "calib_kernels.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-x", "hip",

@@ -168,9 +168,18 @@ int64_t rows_blocks_max(int64_t rows, const DeviceInfo &d)
     return g;
 }
 
-size_t rows_ws_bytes(int Q, int64_t rows, int64_t cols, const DeviceInfo &d)
+// Workspace of a row backward: the partial rows [Q, G, cols] (G at most
+// rows_blocks_max), then, for rows wider than kGenNarrowGroups that take the
+// generic strip kernels, two fp32 coefficients per row.
+size_t rows_partials_bytes(int Q, int64_t rows, int64_t cols, const DeviceInfo &d)
 {
     return round_up((size_t)(Q * rows_blocks_max(rows, d) * cols) * sizeof(float), 256);
+}
+
+size_t rows_ws_bytes(int Q, int64_t rows, int64_t cols, const DeviceInfo &d)
+{
+    const size_t coef = cols > kGenNarrowGroups ? round_up((size_t)rows * 2 * sizeof(float), 256) : 0;
+    return rows_partials_bytes(Q, rows, cols, d) + coef;
 }
 
 // Kernel variant for a row width: vector groups per thread (maxg, 0 = the
@@ -195,6 +204,49 @@ RowsPlan rows_variant(int64_t cols, int vec, bool vec_ok, int max_elems = kRowsM
     }
     if (p.maxg == 0) p.vec = 1;
     return p;
+}
+
+// Generic path (no vector variant fits): rows of at most kGenNarrowGroups
+// columns take the narrow kernel with scalar accesses and a subgroup of ct
+// lanes per row (ct = the power of two covering the row), each block's
+// 256/ct row slots taking at least 4 rows; wider rows take the coefficient
+// and strip kernels with vec-element groups when the tensors allow it, in
+// chunks of rows sized for about kGenTargetBlocks strip blocks, chunks of
+// at least kGenMinChunkRows rows.  The block count (partial rows) never
+// exceeds rows_blocks_max, which the workspace holds; the "rows_blocks"
+// override forces it.
+void rows_generic_plan(RowsCall &a, bool vec_ok, const DeviceInfo &d)
+{
+    const int64_t gmax = rows_blocks_max(a.rows, d);
+    const bool forced = g_override_rows_blocks.load() > 0;
+    a.maxg = 0;
+    a.team = kTeam;
+    if (a.cols <= kGenNarrowGroups) {
+        int ct = 1;
+        while (ct < a.cols) ct <<= 1;
+        const int64_t slots = kTeam / ct;
+        int64_t g = forced ? gmax : ceil_div(a.rows, slots * 4);
+        if (g > gmax) g = gmax;
+        if (g < 1) g = 1;
+        a.vec = 1;
+        a.gen_ct = ct;
+        a.gen_rpc = 0;
+        a.gen_coef_waves = 0;
+        a.blocks = (int)g;
+        return;
+    }
+    const int gvec = vec_ok && a.cols % a.vec == 0 ? a.vec : 1;
+    const int64_t groups = a.cols / gvec;
+    const int64_t strips = ceil_div(groups, kGenStripGroups);
+    int64_t rb = forced ? gmax : std::min(ceil_div(kGenTargetBlocks, strips), ceil_div(a.rows, kGenMinChunkRows));
+    if (rb > gmax) rb = gmax;
+    if (rb < 1) rb = 1;
+    const int64_t rpc = ceil_div(a.rows, rb);
+    a.vec = gvec;
+    a.gen_ct = 0;
+    a.gen_rpc = (int)rpc;
+    a.gen_coef_waves = groups >= kGenTeamCoefGroups ? kGenCoefTeamWaves : 1;
+    a.blocks = (int)ceil_div(a.rows, rpc);
 }
 
 // Blocks: as many as fit on the device at once (occupancy of the chosen
@@ -273,7 +325,7 @@ const char *nh_kernel_name(int k)
     static const char *names[NH_K_COUNT] = {
         "bn_stats", "bn_fwd_finalize", "bn_apply", "bn_grad_sums", "bn_bwd_finalize", "bn_dx",
         "ln_rows", "ln_colsum", "rms_rows", "rms_colsum", "calib", "ln_fwd", "rms_fwd", "bn_infer",
-        "bda_rows", "bda_colsum"};
+        "bda_rows", "bda_colsum", "rows_coef"};
     return (k >= 0 && k < NH_K_COUNT) ? names[k] : "";
 }
 
@@ -517,11 +569,21 @@ static nh_status rows_run(RowsCall &a, int Q, void *ws, size_t ws_bytes, void *s
         if (a.mask && !aligned(a.mask, (size_t)a.vec)) vec_ok = false;
     }
     RowsPlan p = rows_variant(a.cols, a.vec, vec_ok, a.kind == 2 ? kBdaMaxRowElems : kRowsMaxRowElems);
+    a.depth = (int)g_override_rows_depth.load();
+    a.colsum_cols = (int)g_override_colsum_cols.load();
+    hipError_t e = hipSuccess;
+    if (p.maxg == 0) {
+        rows_generic_plan(a, vec_ok, d);
+        a.coef = a.gen_ct == 0
+            ? reinterpret_cast<float *>(static_cast<char *>(ws) + rows_partials_bytes(Q, a.rows, a.cols, d))
+            : nullptr;
+        e = rows_backward_launch(a, s);
+        if (e != hipSuccess) return hip_fail(e, "rows backward launch");
+        return ok();
+    }
     a.maxg = p.maxg;
     a.vec = p.vec;
     a.team = p.team;
-    a.depth = (int)g_override_rows_depth.load();
-    a.colsum_cols = (int)g_override_colsum_cols.load();
     // Occupancy of the chosen variant, cached per device and variant.
     int dev = 0;
     (void)hipGetDevice(&dev);
@@ -534,7 +596,6 @@ static nh_status rows_run(RowsCall &a, int Q, void *ws, size_t ws_bytes, void *s
         auto it = g_rows_occupancy.find(key);
         if (it != g_rows_occupancy.end()) occ = it->second;
     }
-    hipError_t e = hipSuccess;
     if (occ == 0) {
         a.occupancy_out = &occ;
         e = rows_backward_launch(a, s);
@@ -972,6 +1033,51 @@ nh_status nh_selftest_host(void)
             }
         }
     }
+    // Generic row plan, on a 256-CU device: the blocks fit the workspace's
+    // partial rows, the chunks cover the rows exactly once, the strips cover
+    // the columns, the grid is launchable and the coefficient region exists.
+    DeviceInfo dv;
+    dv.valid = true;
+    dv.cus = 256;
+    const int64_t Rs[] = {1, 2, 31, 33, 97, 1000, 4097, 65537, (1 << 18) - 1, 33554431};
+    const int64_t Hs[] = {1, 2, 3, 31, 63, 64, 65, 257, 1000, 1601, 4096, 16385, 32768, 65536, 1 << 20};
+    for (int64_t rows : Rs)
+        for (int64_t cols : Hs) {
+            if (rows * cols >= kMaxElems) continue;
+            for (int vec : {4, 8})
+                for (bool vec_ok : {false, true}) {
+                    RowsCall a{};
+                    a.rows = (int)rows;
+                    a.cols = (int)cols;
+                    a.vec = vec;
+                    rows_generic_plan(a, vec_ok, dv);
+                    const int64_t gmax = rows_blocks_max(rows, dv);
+                    if (a.blocks < 1 || a.blocks > gmax)
+                        return fail(NH_ERR_ARG, "generic blocks %d (rows=%lld cols=%lld)", a.blocks,
+                                    (long long)rows, (long long)cols);
+                    if (a.gen_ct > 0) {
+                        if (cols > kGenNarrowGroups || a.gen_ct < cols || a.gen_ct > kGenNarrowGroups ||
+                            (a.gen_ct & (a.gen_ct - 1)) != 0 || a.vec != 1)
+                            return fail(NH_ERR_ARG, "narrow plan ct=%d cols=%lld", a.gen_ct, (long long)cols);
+                        continue;
+                    }
+                    const int64_t rpc = a.gen_rpc;
+                    const int64_t strips = ceil_div(cols / a.vec, kGenStripGroups);
+                    if (cols <= kGenNarrowGroups || rpc < 1 || (int64_t)(a.blocks - 1) * rpc >= rows ||
+                        (int64_t)a.blocks * rpc < rows || cols % a.vec != 0 ||
+                        (a.vec != 1 && (!vec_ok || a.vec != vec)) ||
+                        strips * kGenStripGroups * a.vec < cols || strips >= (1ll << 31) || a.blocks > 65535 ||
+                        (a.gen_coef_waves != 1 && a.gen_coef_waves != kGenCoefTeamWaves))
+                        return fail(NH_ERR_ARG, "strip plan rpc=%lld blocks=%d (rows=%lld cols=%lld)",
+                                    (long long)rpc, a.blocks, (long long)rows, (long long)cols);
+                    for (int Q = 1; Q <= 3; ++Q)
+                        if (rows_ws_bytes(Q, rows, cols, dv) <
+                            rows_partials_bytes(Q, rows, cols, dv) + (size_t)rows * 2 * sizeof(float) ||
+                            rows_partials_bytes(Q, rows, cols, dv) < (size_t)Q * a.blocks * cols * sizeof(float))
+                            return fail(NH_ERR_ARG, "generic workspace too small (rows=%lld cols=%lld)",
+                                        (long long)rows, (long long)cols);
+                }
+        }
     return ok();
 }
 

@@ -31,10 +31,17 @@ struct RowsCall {
     int colsum_cols;     // columns per column-finalize block (0 = default)
     int *occupancy_out;  // non-NULL: report resident 256-thread blocks per CU
                          // of the selected row kernel instead of launching
+    // Generic path (maxg == 0; vec is then 1 or the vector width):
+    int gen_ct;          // lanes per row of rows_narrow_kernel; 0 = coefficient + strip kernels
+    int gen_rpc;         // rows_strip_kernel: rows per chunk (blocks = number of chunks)
+    int gen_coef_waves;  // rows_coef_kernel: waves per row (1 or kTeamWaves)
+    float *coef;         // [rows, 2] per-row gradient coefficients (strip path)
 };
 
 hipError_t rows_backward_launch(const RowsCall &a, hipStream_t s);
 hipError_t bda_backward_launch(const RowsCall &a, hipStream_t s);
+// Row kernels of the generic path (any kind), without the column finalize.
+hipError_t rows_generic_launch(const RowsCall &a, hipStream_t s);
 // Column finalize of the Q = rows_q(kind) partial rows into dweight, dbias, dbias_in.
 hipError_t rows_colsum_launch(const RowsCall &a, int kid, hipStream_t s);
 // Column sums per kind: LayerNorm dweight, dbias; RMSNorm dweight;
@@ -70,6 +77,22 @@ constexpr int kBdaMaxRowElems = 16;
 // 256 threads at the element limit above (up to twice as wide).
 constexpr int kTeam = 256;
 constexpr int kWideTeam = 512;
+
+// Generic path (widths the vector kernels do not take, misaligned tensors).
+// Rows of at most kGenNarrowGroups groups take rows_narrow_kernel (a
+// subgroup of lanes per row); wider rows take rows_coef_kernel and
+// rows_strip_kernel, whose blocks cover kGenStripGroups column groups (one
+// wave) by 4 row lanes.  The strip grid aims at kGenTargetBlocks blocks (8
+// per CU) with chunks of at least kGenMinChunkRows rows, so that a chunk's
+// partial row costs little next to the rows it sums.  Row coefficients are
+// reduced by one wave per row, or by a 256-thread team for rows of at least
+// kGenTeamCoefGroups groups.
+constexpr int kGenNarrowGroups = 64;
+constexpr int kGenStripGroups = 64;
+constexpr int64_t kGenTargetBlocks = 2048;
+constexpr int64_t kGenMinChunkRows = 32;
+constexpr int kGenTeamCoefGroups = 1024;
+constexpr int kGenCoefTeamWaves = kTeam / 64;
 
 // ---- LayerNorm / RMSNorm forward ---------------------------------------------------
 struct FwdCall {

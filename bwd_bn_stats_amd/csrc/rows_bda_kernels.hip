@@ -147,64 +147,6 @@ bda_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
     if (want_cols) write_partials<VEC, MAXG, 3, TEAM>(p, tt, Gr, H, G, partials);
 }
 
-// Any width, any alignment: scalar accesses, two reads of each row (the
-// second mostly from cache), the column sums in the block's own partial rows.
-template <typename TX, typename TDY>
-__global__ void __launch_bounds__(kTeam)
-bda_generic_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
-                   const float *__restrict__ mean, const float *__restrict__ rstd,
-                   const void *__restrict__ w, int w_bf16, const float *__restrict__ dres,
-                   const uint8_t *__restrict__ mask, float scale, int rows, int H,
-                   float *__restrict__ dh, TDY *__restrict__ da, float *__restrict__ partials,
-                   int want_cols)
-{
-    __shared__ float red[kRedFloats];
-    const int tt = threadIdx.x;
-    const int wave = tt / kWave;
-    const int lane = tt & (kWave - 1);
-    const int G = gridDim.x;
-    const float invH = 1.0f / (float)H;
-    float *prow0 = partials + (size_t)blockIdx.x * H;
-    float *prow1 = partials + ((size_t)G + blockIdx.x) * H;
-    float *prow2 = partials + ((size_t)2 * G + blockIdx.x) * H;
-    if (want_cols)
-        for (int j = tt; j < H; j += kTeam) {
-            prow0[j] = 0.f;
-            prow1[j] = 0.f;
-            prow2[j] = 0.f;
-        }
-    int it = 0;
-    // 64-bit row index: rows may reach 2^31 - 1 (one column), r + G must not wrap.
-    for (int64_t r = blockIdx.x; r < rows; r += G, ++it) {
-        const size_t rowoff = (size_t)r * H;
-        const float mu = mean[r], rs = rstd[r];
-        float sa = 0.f, sb = 0.f;
-        for (int j = tt; j < H; j += kTeam) {
-            const float wj = w ? load_param(w, w_bf16, j) : 1.f;
-            const float g = to_f32(dy[rowoff + j]) * wj;
-            sa += g;
-            sb = fmaf(g, (to_f32(x[rowoff + j]) - mu) * rs, sb);
-        }
-        team_sum2(red + (it & 1) * (kRedFloats / 2), wave, lane, sa, sb);
-        const float ca = sa * invH, cb = sb * invH;
-        for (int j = tt; j < H; j += kTeam) {
-            const size_t i = rowoff + j;
-            const float wj = w ? load_param(w, w_bf16, j) : 1.f;
-            const float d = to_f32(dy[i]);
-            const float xh = (to_f32(x[i]) - mu) * rs;
-            const float h = rs * fmaf(-xh, cb, d * wj - ca) + (dres ? dres[i] : 0.f);
-            const float a = h * scale * (mask ? (mask[i] != 0 ? 1.f : 0.f) : 1.f);
-            if (want_cols) {
-                prow0[j] = fmaf(d, xh, prow0[j]);
-                prow1[j] += d;
-                prow2[j] += a;
-            }
-            if (dh != nullptr) dh[i] = h;
-            if (da != nullptr) da[i] = from_f32<TDY>(a);
-        }
-    }
-}
-
 // ---- host dispatch ---------------------------------------------------------------
 template <typename TX, typename TDY, int VEC, int MAXG, int TEAM, int D>
 static hipError_t bda_vec_d(const RowsCall &a, hipStream_t s)
@@ -236,22 +178,8 @@ static hipError_t bda_vec(const RowsCall &a, hipStream_t s)
 }
 
 template <typename TX, typename TDY>
-static hipError_t bda_generic(const RowsCall &a, hipStream_t s)
-{
-    auto kern = bda_generic_kernel<TX, TDY>;
-    if (a.occupancy_out)
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kern, kTeam, 0);
-    return launch(NH_K_BDA_ROWS, kern, dim3(a.blocks), dim3(kTeam), 0u, s,
-                  static_cast<const TDY *>(a.dy), static_cast<const TX *>(a.x), a.mean, a.rstd, a.w,
-                  a.w_t, a.dresidual, a.mask, a.scale, a.rows, a.cols, a.dh,
-                  static_cast<TDY *>(a.dx), a.partials,
-                  (int)(a.dweight != nullptr || a.dbias != nullptr || a.dbias_in != nullptr));
-}
-
-template <typename TX, typename TDY>
 static hipError_t bda_types(const RowsCall &a, hipStream_t s)
 {
-    if (a.maxg == 0) return bda_generic<TX, TDY>(a, s);
     // At most kBdaMaxRowElems row elements per thread: a 256-thread team, or
     // a 512-thread team for rows up to twice as wide; the planner sends wider
     // rows to the generic path.
@@ -277,7 +205,9 @@ static hipError_t bda_types(const RowsCall &a, hipStream_t s)
 hipError_t bda_backward_launch(const RowsCall &a, hipStream_t s)
 {
     hipError_t e = hipSuccess;
-    if (a.rows > 0) {
+    if (a.rows > 0 && a.maxg == 0) {
+        e = rows_generic_launch(a, s);
+    } else if (a.rows > 0) {
         switch (a.x_t * 2 + a.dy_t) {
         case 0: e = bda_types<float, float>(a, s); break;
         case 1: e = bda_types<float, uint16_t>(a, s); break;

@@ -27,9 +27,8 @@
 // No atomics: every output has one writer and a fixed summation order.
 //
 // Rows whose width is not a multiple of the group, misaligned pointers, or
-// rows wider than the vector path's register budget take rows_generic_kernel: the same
-// arithmetic with scalar accesses, two reads of each row (the second mostly
-// from cache) and the column sums kept in the block's own partial row.
+// rows wider than the vector path's register budget take the generic kernels
+// (rows_generic_kernels.hip).
 #include "rows_common.hpp"
 
 namespace nh {
@@ -235,78 +234,6 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
     if (want_cols) write_partials<VEC, MAXG, 1, TEAM>(p, tt, Gr, H, G, partials);
 }
 
-// ---- generic path: scalar accesses, any width, any alignment -------------------
-// Block = one team of 256 threads; the block's column sums live in its own
-// partial row (written only by the thread owning the column).
-template <typename TX, typename TDY, typename TDX>
-__global__ void __launch_bounds__(kTeam)
-rows_generic_kernel(int kind, const TDY *__restrict__ dy, const TX *__restrict__ x,
-                    const float *__restrict__ mean, const float *__restrict__ rstd,
-                    const float *__restrict__ rms, float eps,
-                    const void *__restrict__ w, int w_bf16, int rows, int H,
-                    TDX *__restrict__ dx, float *__restrict__ partials, int want_cols)
-{
-    __shared__ float red[kRedFloats];
-    const int tt = threadIdx.x;
-    const int wave = tt / kWave;
-    const int lane = tt & (kWave - 1);
-    const int G = gridDim.x;
-    const int Q = kind == 0 ? 2 : 1;
-    const float invH = 1.0f / (float)H;
-    float *prow0 = partials + (size_t)blockIdx.x * H;
-    float *prow1 = partials + ((size_t)G + blockIdx.x) * H;
-    if (want_cols)
-        for (int j = tt; j < H; j += kTeam) {
-            prow0[j] = 0.f;
-            if (Q == 2) prow1[j] = 0.f;
-        }
-    int it = 0;
-    // 64-bit row index: rows may reach 2^31 - 1 (one column), r + G must not wrap.
-    for (int64_t r = blockIdx.x; r < rows; r += G, ++it) {
-        const size_t rowoff = (size_t)r * H;
-        float a = 0.f, b = 0.f;
-        float mu = 0.f, rs = 0.f;
-        if (kind == 0) { mu = mean[r]; rs = rstd[r]; }
-        for (int j = tt; j < H; j += kTeam) {
-            const float wj = w ? load_param(w, w_bf16, j) : 1.f;
-            const float xv = to_f32(x[rowoff + j]);
-            const float g = to_f32(dy[rowoff + j]) * wj;
-            if (kind == 0) {
-                a += g;
-                b = fmaf(g, (xv - mu) * rs, b);
-            } else {
-                a = fmaf(g, xv, a);
-                b = fmaf(xv, xv, b);
-            }
-        }
-        team_sum2(red + (it & 1) * (kRedFloats / 2), wave, lane, a, b);
-        float rinv = 0.f, c = 0.f;
-        if (kind == 1) {
-            rinv = rms != nullptr ? 1.0f / rms[r] : 1.0f / sqrtf(fmaf(b, invH, eps));
-            c = rinv * rinv * rinv * a * invH;
-        }
-        for (int j = tt; j < H; j += kTeam) {
-            const float wj = w ? load_param(w, w_bf16, j) : 1.f;
-            const float xv = to_f32(x[rowoff + j]);
-            const float d = to_f32(dy[rowoff + j]);
-            const float g = d * wj;
-            float o;
-            if (kind == 0) {
-                const float xh = (xv - mu) * rs;
-                o = rs * fmaf(-xh, b * invH, g - a * invH);
-                if (want_cols) {
-                    prow0[j] = fmaf(d, xh, prow0[j]);
-                    prow1[j] += d;
-                }
-            } else {
-                o = fmaf(-xv, c, rinv * g);
-                if (want_cols) prow0[j] = fmaf(d * xv, rinv, prow0[j]);
-            }
-            if (dx != nullptr) dx[rowoff + j] = from_f32<TDX>(o);
-        }
-    }
-}
-
 // ---- column finalize: fp64 fixed-order sum of the G partial rows -------------
 // Block = CX columns x (1024/CX) slices; slice ty sums partial rows
 // ty, ty + CY, ... in order, then the slices are combined in slice order
@@ -452,17 +379,6 @@ static hipError_t ln_dispatch_vec(const RowsCall &a, hipStream_t s)
     return a.vec == 4 ? ln_maxg<TX, TDY, TDX, 4>(a, s) : ln_maxg<TX, TDY, TDX, 8>(a, s);
 }
 
-template <typename TX, typename TDY, typename TDX>
-static hipError_t generic_launch(const RowsCall &a, hipStream_t s)
-{
-    const int want = a.kind == 0 ? (a.dweight != nullptr || a.dbias != nullptr) : (a.dweight != nullptr);
-    if (a.occupancy_out) return occupancy(a, rows_generic_kernel<TX, TDY, TDX>);
-    return launch(a.kind == 0 ? NH_K_LN_ROWS : NH_K_RMS_ROWS, rows_generic_kernel<TX, TDY, TDX>,
-                  dim3(a.blocks), dim3(kTeam), 0u, s, a.kind, static_cast<const TDY *>(a.dy),
-                  static_cast<const TX *>(a.x), a.mean, a.rstd, a.rms, a.eps, a.w, a.w_t, a.rows,
-                  a.cols, static_cast<TDX *>(a.dx), a.partials, want);
-}
-
 // dtype code 0 = float, 1 = bf16 (uint16_t)
 template <template <typename, typename, typename> class F>
 static hipError_t by_types(int tx, int tdy, int tdx, const RowsCall &a, hipStream_t s)
@@ -482,9 +398,6 @@ static hipError_t by_types(int tx, int tdy, int tdx, const RowsCall &a, hipStrea
 
 template <typename TX, typename TDY, typename TDX> struct LnVecF {
     static hipError_t run(const RowsCall &a, hipStream_t s) { return ln_dispatch_vec<TX, TDY, TDX>(a, s); }
-};
-template <typename TX, typename TDY, typename TDX> struct GenericF {
-    static hipError_t run(const RowsCall &a, hipStream_t s) { return generic_launch<TX, TDY, TDX>(a, s); }
 };
 
 template <typename TOUT, int CX>
@@ -526,7 +439,7 @@ hipError_t rows_backward_launch(const RowsCall &a, hipStream_t s)
     if (a.rows == 0) {
         // nothing to launch for the rows; the finalize writes zero sums
     } else if (a.maxg == 0) {
-        e = by_types<GenericF>(a.x_t, a.dy_t, dxt, a, s);
+        e = rows_generic_launch(a, s);
     } else if (a.kind == 0) {
         e = by_types<LnVecF>(a.x_t, a.dy_t, dxt, a, s);
     } else {

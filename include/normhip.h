@@ -211,7 +211,10 @@ nh_status bn_forward_infer(const void *x, void *y, nh_dtype io,
 /* ------------------------------------------------------------------------
  * LayerNorm / RMSNorm backward over the last dimension of [rows, cols].
  * dweight/dbias are split over rows into per-block partials in the
- * workspace and summed by a finalize kernel in a fixed order.
+ * workspace and summed by a finalize kernel in a fixed order.  Rows wider
+ * than 64 columns that the register-resident kernels do not take (wider
+ * than they hold, odd widths, misaligned tensors) also keep two fp32
+ * coefficients per row in the workspace.
  * ---------------------------------------------------------------------- */
 
 nh_status layernorm_backward_workspace(int64_t rows, int64_t cols, size_t *ws_bytes);
@@ -350,7 +353,8 @@ typedef enum {
     NH_K_BN_INFER = 13,       /* BatchNorm inference apply */
     NH_K_BDA_ROWS = 14,       /* bias+dropout+add+LayerNorm backward row pass */
     NH_K_BDA_COLSUM = 15,     /* its dweight/dbias/dbias_in finalize */
-    NH_K_COUNT = 16
+    NH_K_ROWS_COEF = 16,      /* per-row gradient coefficients (wide or misaligned rows) */
+    NH_K_COUNT = 17
 } nh_kernel;
 
 /* Static name of a kernel id; "" for an unknown id. */

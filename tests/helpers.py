@@ -104,3 +104,19 @@ def clear_of_kink(oracle_mod, t, gamma, beta, eps, delta, max_iter=8):
         c32 = np.where(stuck, _next_toward(x32, up, t.dtype), c32)
         x32 = np.where(near, c32, x32)
     raise AssertionError("could not move x clear of the activation kink")
+
+
+def place(t: wl.Tensor, offset: int):
+    """Device copy of t starting `offset` elements into a larger buffer, so
+    that an offset of 1-3 leaves the tensor misaligned for 16-byte access."""
+    import torch
+    if t.dtype == wl.F32:
+        flat = torch.from_numpy(np.ascontiguousarray(t.store).reshape(-1))
+        buf = torch.zeros(flat.numel() + offset, dtype=torch.float32, device="cuda")
+        buf[offset:] = flat.cuda()
+    else:
+        flat = torch.from_numpy(np.ascontiguousarray(t.store).reshape(-1).view(np.int16))
+        buf = torch.zeros(flat.numel() + offset, dtype=torch.int16, device="cuda")
+        buf[offset:] = flat.cuda()
+        buf = buf.view(torch.bfloat16)
+    return buf[offset:].view(t.shape)

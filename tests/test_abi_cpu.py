@@ -43,8 +43,8 @@ def test_status_and_kernel_names():
         "NH_OK", "NH_ERR_NULL", "NH_ERR_SHAPE", "NH_ERR_DTYPE", "NH_ERR_WORKSPACE",
         "NH_ERR_HIP", "NH_ERR_ARG"]
     assert nh.status_string(99) == "NH_ERR_UNKNOWN"
-    assert [nh.lib.nh_kernel_name(i).decode() for i in range(16)] == nh.KERNELS
-    assert nh.lib.nh_kernel_name(16).decode() == ""
+    assert [nh.lib.nh_kernel_name(i).decode() for i in range(17)] == nh.KERNELS
+    assert nh.lib.nh_kernel_name(17).decode() == ""
 
 
 def bn_fwd(x=FAKE, y=FAKE, io=0, N=2, C=3, HW=4, rm=NULL, rv=NULL, eps=1e-5, mom=0.1,

@@ -1,0 +1,140 @@
+"""GPU parity of the generic backward row kernels against the CPU oracle.
+
+Shapes the register-resident row kernels do not take -- rows of up to 64
+columns with an odd width or a misaligned tensor (the narrow kernel, a lane
+subgroup per row), and wider rows that are odd, misaligned or wider than a
+512-thread team holds (the per-row coefficient kernel followed by the
+column-strip kernel) -- through LayerNorm, RMSNorm and the bias + dropout +
+add + LayerNorm backward.  Every output is compared with the oracle at the
+parity tolerances; the per-kernel timing records show which path ran."""
+import numpy as np
+import pytest
+
+from bwd_bn_stats_amd import workloads as wl
+
+from helpers import check, host, place
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+F32, BF16 = wl.F32, wl.BF16
+
+
+@pytest.fixture(scope="module")
+def nh():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from bwd_bn_stats_amd import normhip
+    return normhip
+
+
+def _tdt(t):
+    return torch.float32 if t == F32 else torch.bfloat16
+
+
+# rows, cols, x, dy, weight dtypes, element offset of the row tensors, path
+CASES = [
+    (3001, 1, F32, F32, F32, 1, "narrow"),
+    (2500, 5, BF16, BF16, BF16, 0, "narrow"),       # odd width, aligned
+    (4099, 33, F32, BF16, BF16, 2, "narrow"),
+    (1000, 64, BF16, F32, F32, 1, "narrow"),        # widest narrow row, misaligned
+    (777, 63, F32, F32, BF16, 0, "narrow"),
+    (300, 65, F32, BF16, F32, 1, "strip"),          # narrowest strip row
+    (513, 1601, BF16, BF16, BF16, 0, "strip"),      # odd width: scalar groups
+    (100, 5000, F32, F32, BF16, 1, "strip"),        # a 256-thread team per coefficient row
+    (37, 20000, BF16, F32, F32, 3, "strip"),
+    (200, 20000, BF16, BF16, BF16, 0, "strip"),     # aligned, too wide: 8-element groups
+    (70, 40960, F32, F32, F32, 0, "strip"),         # aligned fp32: 4-element groups
+    (40, 24576, F32, BF16, BF16, 0, "strip"),
+]
+
+
+def _path_ran(nh, path):
+    _, n = nh.timing_read("rows_coef")
+    assert (n > 0) == (path == "strip"), f"expected the {path} path, rows_coef launches: {n}"
+
+
+def _run_case(nh, oracle_mod, case, blocks=0):
+    rows, cols, xt, dyt, wt, offset, path = case
+    print(f"[generic] rows={rows} cols={cols} x={xt} dy={dyt} w={wt} offset={offset} path={path} "
+          f"blocks={blocks or 'auto'}", flush=True)
+    c = wl.bda_case(rows, cols, x_t=xt, dy_t=dyt, w_t=wt, seed=rows * 7 + cols, p_drop=0.25)
+    ln = c.ln
+    x, dy, w = place(ln.x, offset), place(ln.dy, offset), place(ln.w, offset)
+    mean, rstd = oracle_mod.layernorm_stats(ln.x.value, eps=ln.eps)
+    m32, r32 = mean.astype(np.float32), rstd.astype(np.float32)
+    dm, dr = torch.from_numpy(m32).cuda(), torch.from_numpy(r32).cuda()
+    if blocks:
+        nh.plan_override("rows_blocks", blocks)
+    nh.timing_enable(True)
+    try:
+        # LayerNorm backward, dx in x's dtype
+        wdx, wdw, wdb = oracle_mod.layernorm_backward(ln.x.value, ln.dy.value, m32, r32, ln.w.value)
+        dx, dw, db = nh.layernorm_backward(dy, x, dm, dr, w, dx_dtype=_tdt(xt))
+        torch.cuda.synchronize()
+        check("ln dx", host(dx), wdx, xt)
+        check("ln dweight", host(dw), wdw, wt)
+        check("ln dbias", host(db), wdb, wt)
+        _path_ran(nh, path)
+        # bias + dropout + add + LayerNorm backward on the same rows
+        mask = torch.from_numpy(c.mask).cuda()
+        dres = torch.from_numpy(c.dresidual).cuda()
+        want = oracle_mod.bda_layernorm_backward(ln.x.value, ln.dy.value, m32, r32, ln.w.value,
+                                                 c.dresidual, c.mask, c.scale)
+        got = nh.bda_layernorm_backward(dy, x, dm, dr, w, dres, mask, c.scale)
+        torch.cuda.synchronize()
+        for name, g, wv, dt in zip(("dh", "da", "dweight", "dbias", "dbias_in"), got, want,
+                                   (F32, dyt, wt, wt, wt)):
+            check(f"bda {name}", host(g), wv, dt)
+        # RMSNorm backward, one dtype (x's) for x, dy, weight; rms saved and recomputed
+        r = wl.rows_case(rows, cols, x_t=xt, dy_t=xt, w_t=xt, seed=rows * 11 + cols)
+        rx, rdy, rw = place(r.x, offset), place(r.dy, offset), place(r.w, offset)
+        _, wrms = oracle_mod.rmsnorm_forward(r.x.value, r.w.value, eps=r.eps)
+        rms32 = wrms.astype(np.float32)
+        for saved in (True, False):
+            wdx, wdw = oracle_mod.rmsnorm_backward(r.x.value, r.dy.value, r.w.value,
+                                                   rms32 if saved else None, eps=r.eps)
+            dx, dw = nh.rmsnorm_backward(rdy, rx, torch.from_numpy(rms32).cuda() if saved else None,
+                                         rw, r.eps)
+            torch.cuda.synchronize()
+            check(f"rms dx (saved={saved})", host(dx), wdx, xt)
+            check(f"rms dweight (saved={saved})", host(dw), wdw, xt)
+    finally:
+        nh.timing_enable(False)
+        if blocks:
+            nh.plan_override("rows_blocks", 0)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}x{c[1]}-{c[6]}-off{c[5]}")
+def test_generic_rows(nh, oracle_mod, case):
+    _run_case(nh, oracle_mod, case)
+
+
+@pytest.mark.parametrize("case,blocks", [
+    ((513, 1601, BF16, BF16, BF16, 0, "strip"), 1),     # one chunk of all rows
+    ((513, 1601, BF16, BF16, BF16, 0, "strip"), 7),     # ragged last chunk
+    ((513, 1601, F32, F32, F32, 1, "strip"), 513),      # a chunk per row
+    ((3001, 5, F32, BF16, F32, 1, "narrow"), 1),        # one block walks every row
+    ((3001, 5, F32, BF16, F32, 1, "narrow"), 1000),     # fewer rows than row slots
+])
+def test_generic_forced_blocks(nh, oracle_mod, case, blocks):
+    _run_case(nh, oracle_mod, case, blocks=blocks)
+
+
+@pytest.mark.parametrize("rows,cols,offset", [(2000, 17, 1), (300, 3000, 1), (64, 20000, 0)])
+def test_generic_bit_identical_runs(nh, rows, cols, offset):
+    """Two calls on the same inputs give the same bits (no atomics, fixed
+    summation order on the generic path too)."""
+    c = wl.rows_case(rows, cols, x_t=BF16, dy_t=BF16, w_t=BF16, seed=rows + cols)
+    x, dy, w = place(c.x, offset), place(c.dy, offset), place(c.w, offset)
+    m = torch.zeros(rows, device="cuda")
+    r = torch.ones(rows, device="cuda")
+    a = nh.layernorm_backward(dy, x, m, r, w, dx_dtype=torch.float32)
+    b = nh.layernorm_backward(dy, x, m, r, w, dx_dtype=torch.float32)
+    ra = nh.rmsnorm_backward(dy, x, None, w, 1e-5)
+    rb = nh.rmsnorm_backward(dy, x, None, w, 1e-5)
+    torch.cuda.synchronize()
+    for u, v in zip(list(a) + list(ra), list(b) + list(rb)):
+        bits = (lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32))
+        assert torch.equal(bits(u), bits(v))

@@ -10,7 +10,7 @@ import pytest
 
 from bwd_bn_stats_amd import workloads as wl
 
-from helpers import check, host
+from helpers import check, host, place as _place
 
 pytestmark = pytest.mark.gpu
 
@@ -23,20 +23,6 @@ def nh():
         pytest.skip("no GPU")
     from bwd_bn_stats_amd import normhip
     return normhip
-
-
-def _place(t: wl.Tensor, offset: int):
-    """Device copy of t starting `offset` elements into a larger buffer."""
-    if t.dtype == wl.F32:
-        flat = torch.from_numpy(np.ascontiguousarray(t.store).reshape(-1))
-        buf = torch.zeros(flat.numel() + offset, dtype=torch.float32, device="cuda")
-        buf[offset:] = flat.cuda()
-    else:
-        flat = torch.from_numpy(np.ascontiguousarray(t.store).reshape(-1).view(np.int16))
-        buf = torch.zeros(flat.numel() + offset, dtype=torch.int16, device="cuda")
-        buf[offset:] = flat.cuda()
-        buf = buf.view(torch.bfloat16)
-    return buf[offset:].view(t.shape)
 
 
 def _bn_cases():
