@@ -168,17 +168,33 @@ int64_t rows_blocks_max(int64_t rows, const DeviceInfo &d)
     return g;
 }
 
+// Partial rows the workspace holds: rows_blocks_max, or, for rows of at most
+// kGenNarrowGroups columns (short partial rows), up to kRowsMaxBlocks for the
+// narrow generic kernel, which needs many blocks to keep enough short rows
+// in flight.
+int64_t rows_partial_rows(int64_t rows, int64_t cols, const DeviceInfo &d)
+{
+    if (cols > kGenNarrowGroups) return rows_blocks_max(rows, d);
+    const int64_t ov = g_override_rows_blocks.load();
+    int64_t g = ov > 0 ? ov : kRowsMaxBlocks;
+    if (g > kRowsMaxBlocks) g = kRowsMaxBlocks;
+    if (g > rows) g = rows;
+    return g;
+}
+
 // Workspace of a row backward: the partial rows [Q, G, cols] (G at most
-// rows_blocks_max), then, for rows wider than kGenNarrowGroups that take the
-// generic strip kernels, two fp32 coefficients per row.
+// rows_partial_rows), then, for rows wider than kGenNarrowGroups that take
+// the generic strip kernels, two fp32 sums per row segment
+// (gen_coef_slots(rows) segments per row at most).
 size_t rows_partials_bytes(int Q, int64_t rows, int64_t cols, const DeviceInfo &d)
 {
-    return round_up((size_t)(Q * rows_blocks_max(rows, d) * cols) * sizeof(float), 256);
+    return round_up((size_t)(Q * rows_partial_rows(rows, cols, d) * cols) * sizeof(float), 256);
 }
 
 size_t rows_ws_bytes(int Q, int64_t rows, int64_t cols, const DeviceInfo &d)
 {
-    const size_t coef = cols > kGenNarrowGroups ? round_up((size_t)rows * 2 * sizeof(float), 256) : 0;
+    const size_t coef =
+        cols > kGenNarrowGroups ? round_up((size_t)(rows * gen_coef_slots(rows)) * 2 * sizeof(float), 256) : 0;
     return rows_partials_bytes(Q, rows, cols, d) + coef;
 }
 
@@ -209,15 +225,16 @@ RowsPlan rows_variant(int64_t cols, int vec, bool vec_ok, int max_elems = kRowsM
 // Generic path (no vector variant fits): rows of at most kGenNarrowGroups
 // columns take the narrow kernel with scalar accesses and a subgroup of ct
 // lanes per row (ct = the power of two covering the row), each block's
-// 256/ct row slots taking at least 4 rows; wider rows take the coefficient
+// 256/ct row slots taking at least kGenNarrowRowsInFlight rows, up to
+// rows_partial_rows blocks; wider rows take the coefficient
 // and strip kernels with vec-element groups when the tensors allow it, in
 // chunks of rows sized for about kGenTargetBlocks strip blocks, chunks of
 // at least kGenMinChunkRows rows.  The block count (partial rows) never
-// exceeds rows_blocks_max, which the workspace holds; the "rows_blocks"
+// exceeds rows_partial_rows, which the workspace holds; the "rows_blocks"
 // override forces it.
 void rows_generic_plan(RowsCall &a, bool vec_ok, const DeviceInfo &d)
 {
-    const int64_t gmax = rows_blocks_max(a.rows, d);
+    const int64_t gmax = rows_partial_rows(a.rows, a.cols, d);
     const bool forced = g_override_rows_blocks.load() > 0;
     a.maxg = 0;
     a.team = kTeam;
@@ -225,7 +242,7 @@ void rows_generic_plan(RowsCall &a, bool vec_ok, const DeviceInfo &d)
         int ct = 1;
         while (ct < a.cols) ct <<= 1;
         const int64_t slots = kTeam / ct;
-        int64_t g = forced ? gmax : ceil_div(a.rows, slots * 4);
+        int64_t g = forced ? gmax : ceil_div(a.rows, slots * kGenNarrowRowsInFlight);
         if (g > gmax) g = gmax;
         if (g < 1) g = 1;
         a.vec = 1;
@@ -246,6 +263,12 @@ void rows_generic_plan(RowsCall &a, bool vec_ok, const DeviceInfo &d)
     a.gen_ct = 0;
     a.gen_rpc = (int)rpc;
     a.gen_coef_waves = groups >= kGenTeamCoefGroups ? kGenCoefTeamWaves : 1;
+    int64_t segs = 1;
+    if (a.gen_coef_waves > 1) {
+        segs = std::min<int64_t>(gen_coef_slots(a.rows), groups / kGenCoefMinSegGroups);
+        if (segs < 1) segs = 1;
+    }
+    a.gen_coef_segs = (int)segs;
     a.blocks = (int)ceil_div(a.rows, rpc);
 }
 
@@ -934,7 +957,7 @@ nh_status nh_rows_plan(int64_t rows, int64_t cols, int *blocks)
     if (rows * cols == 0) { *blocks = 0; return ok(); }
     DeviceInfo d;
     if ((st = device_info(&d)) != NH_OK) return st;
-    *blocks = (int)rows_blocks_max(rows, d);
+    *blocks = (int)rows_partial_rows(rows, cols, d);
     return ok();
 }
 
@@ -1051,7 +1074,7 @@ nh_status nh_selftest_host(void)
                     a.cols = (int)cols;
                     a.vec = vec;
                     rows_generic_plan(a, vec_ok, dv);
-                    const int64_t gmax = rows_blocks_max(rows, dv);
+                    const int64_t gmax = rows_partial_rows(rows, cols, dv);
                     if (a.blocks < 1 || a.blocks > gmax)
                         return fail(NH_ERR_ARG, "generic blocks %d (rows=%lld cols=%lld)", a.blocks,
                                     (long long)rows, (long long)cols);
@@ -1067,12 +1090,16 @@ nh_status nh_selftest_host(void)
                         (int64_t)a.blocks * rpc < rows || cols % a.vec != 0 ||
                         (a.vec != 1 && (!vec_ok || a.vec != vec)) ||
                         strips * kGenStripGroups * a.vec < cols || strips >= (1ll << 31) || a.blocks > 65535 ||
-                        (a.gen_coef_waves != 1 && a.gen_coef_waves != kGenCoefTeamWaves))
+                        (a.gen_coef_waves != 1 && a.gen_coef_waves != kGenCoefTeamWaves) ||
+                        a.gen_coef_segs < 1 || a.gen_coef_segs > gen_coef_slots(rows) ||
+                        (a.gen_coef_waves == 1 && a.gen_coef_segs != 1) ||
+                        (a.gen_coef_segs > 1 && (cols / a.vec) / a.gen_coef_segs < kGenCoefMinSegGroups) ||
+                        rows * a.gen_coef_segs >= (1ll << 31))
                         return fail(NH_ERR_ARG, "strip plan rpc=%lld blocks=%d (rows=%lld cols=%lld)",
                                     (long long)rpc, a.blocks, (long long)rows, (long long)cols);
                     for (int Q = 1; Q <= 3; ++Q)
                         if (rows_ws_bytes(Q, rows, cols, dv) <
-                            rows_partials_bytes(Q, rows, cols, dv) + (size_t)rows * 2 * sizeof(float) ||
+                            rows_partials_bytes(Q, rows, cols, dv) + (size_t)rows * a.gen_coef_segs * 2 * sizeof(float) ||
                             rows_partials_bytes(Q, rows, cols, dv) < (size_t)Q * a.blocks * cols * sizeof(float))
                             return fail(NH_ERR_ARG, "generic workspace too small (rows=%lld cols=%lld)",
                                         (long long)rows, (long long)cols);

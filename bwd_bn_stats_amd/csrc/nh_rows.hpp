@@ -34,8 +34,9 @@ struct RowsCall {
     // Generic path (maxg == 0; vec is then 1 or the vector width):
     int gen_ct;          // lanes per row of rows_narrow_kernel; 0 = coefficient + strip kernels
     int gen_rpc;         // rows_strip_kernel: rows per chunk (blocks = number of chunks)
-    int gen_coef_waves;  // rows_coef_kernel: waves per row (1 or kTeamWaves)
-    float *coef;         // [rows, 2] per-row gradient coefficients (strip path)
+    int gen_coef_waves;  // rows_coef_kernel: waves per row segment (1 or kGenCoefTeamWaves)
+    int gen_coef_segs;   // rows_coef_kernel: column segments per row (1 with one wave per row)
+    float *coef;         // [rows, gen_coef_segs, 2] row-segment sums (strip path)
 };
 
 hipError_t rows_backward_launch(const RowsCall &a, hipStream_t s);
@@ -84,15 +85,28 @@ constexpr int kWideTeam = 512;
 // rows_strip_kernel, whose blocks cover kGenStripGroups column groups (one
 // wave) by 4 row lanes.  The strip grid aims at kGenTargetBlocks blocks (8
 // per CU) with chunks of at least kGenMinChunkRows rows, so that a chunk's
-// partial row costs little next to the rows it sums.  Row coefficients are
-// reduced by one wave per row, or by a 256-thread team for rows of at least
-// kGenTeamCoefGroups groups.
+// partial row costs little next to the rows it sums.  Row sums are reduced
+// by one wave per row, or by a 256-thread team for rows of at least
+// kGenTeamCoefGroups groups; with fewer than kGenCoefTargetBlocks such rows,
+// each row is cut into up to kGenCoefMaxSegs segments of at least
+// kGenCoefMinSegGroups groups, one team each, so that enough teams run.
 constexpr int kGenNarrowGroups = 64;
+constexpr int kGenNarrowRowsInFlight = 8;  // rows a narrow row slot loads at once
 constexpr int kGenStripGroups = 64;
 constexpr int64_t kGenTargetBlocks = 2048;
 constexpr int64_t kGenMinChunkRows = 32;
 constexpr int kGenTeamCoefGroups = 1024;
 constexpr int kGenCoefTeamWaves = kTeam / 64;
+constexpr int64_t kGenCoefTargetBlocks = 1024;
+constexpr int kGenCoefMaxSegs = 8;
+constexpr int kGenCoefMinSegGroups = 512;
+// Row-segment sum slots per row that the workspace holds for `rows` rows.
+constexpr int64_t gen_coef_slots(int64_t rows)
+{
+    return rows >= kGenCoefTargetBlocks ? 1
+         : ((kGenCoefTargetBlocks + rows - 1) / rows < kGenCoefMaxSegs ? (kGenCoefTargetBlocks + rows - 1) / rows
+                                                                      : kGenCoefMaxSegs);
+}
 
 // ---- LayerNorm / RMSNorm forward ---------------------------------------------------
 struct FwdCall {

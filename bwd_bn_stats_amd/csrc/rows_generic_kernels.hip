@@ -20,8 +20,9 @@
 // theirs through LDS, in slot order, once at the end.
 //
 // Wider rows: rows_coef_kernel, then rows_strip_kernel.  The first reduces
-// each row (one wave, or a 256-thread team for long rows) to the two
-// coefficients of its gradient, 8 bytes per row.  The second cuts [rows, H]
+// each row (one wave, or a 256-thread team for long rows, or several teams
+// for few long rows) to the two sums its gradient needs, 8 bytes per row
+// segment.  The second cuts [rows, H]
 // into strips of 64 column groups by chunks of rows.  A 256-thread block
 // takes one strip of one chunk as 64 column lanes by 4 row lanes, walks the
 // chunk's rows writing the outputs, keeps its columns' sums in registers and
@@ -46,13 +47,14 @@ struct GenArgs {
     float *dh;                  // bias+dropout+add: fp32 output, or NULL
     void *dx;                   // dx (LayerNorm, RMSNorm) or da (bias+dropout+add), or NULL
     float *partials;            // [Q, G, H]
-    float *coef;                // [rows, 2] (strip path)
+    float *coef;                // [rows, nseg, 2] row-segment sums (strip path)
     float eps, scale;
     int rows, cols;
     int w_bf16;
     int want_cols;
     int ct;                     // narrow: lanes per row
     int rpc;                    // strip: rows per chunk
+    int nseg;                   // strip: column segments per row in the row-sum pass
 };
 
 // One group of VEC consecutive elements of a row, widened to fp32: x, dy and,
@@ -194,7 +196,7 @@ __global__ void __launch_bounds__(kTeam)
 rows_narrow_kernel(GenArgs a)
 {
     constexpr int Q = rows_q(KIND);
-    constexpr int U = 4;  // rows of a slot in flight
+    constexpr int U = kGenNarrowRowsInFlight;
     __shared__ float red[Q * kTeam];
     const int tt = threadIdx.x;
     const int ct = a.ct;
@@ -250,31 +252,39 @@ rows_narrow_kernel(GenArgs a)
     }
 }
 
-// ---- wide rows, pass 1: per-row coefficients -------------------------------------
-// W waves per row: 1 (four rows per block) or the whole block.  Cacheable
-// loads, so that the strip pass finds the rows in the caches.
+// ---- wide rows, pass 1: per-row sums ----------------------------------------------
+// A unit is one of the a.nseg equal column segments of a row (a.nseg > 1
+// only for few, long rows, so that enough blocks run); it gets W waves: 1
+// (four units per block) or the whole block.  The unit's two sums go to
+// coef[unit] = coef[row*nseg + segment]; the strip pass adds a row's
+// segments in order.  Cacheable loads, so that the strip pass finds the rows
+// in the caches.
 template <int KIND, typename TX, typename TDY, int VEC, int W>
 __global__ void __launch_bounds__(kTeam)
 rows_coef_kernel(GenArgs a)
 {
     constexpr int RPB = kTeamWaves / W;
     constexpr int LANES = W * kWave;
-    constexpr int U = VEC == 1 ? 8 : 4;  // groups of a lane in flight
+    constexpr int U = VEC == 8 ? 4 : 8;  // groups of a lane in flight
     __shared__ float red[2 * kTeamWaves];
     const int tt = threadIdx.x;
     const int wave = tt / kWave;
     const int slot = wave / W;
     const int li = tt - slot * LANES;
-    const int64_t r = (int64_t)blockIdx.x * RPB + slot;
+    const int64_t unit = (int64_t)blockIdx.x * RPB + slot;
+    const int64_t r = unit / a.nseg;
+    const int seg = (int)(unit - r * a.nseg);
     const bool live = r < a.rows;
     const int groups = a.cols / VEC;
+    const int per_seg = (int)ceil_div(groups, a.nseg);
+    const int g1 = (seg + 1) * per_seg < groups ? (seg + 1) * per_seg : groups;
     float s0 = 0.f, s1 = 0.f;
     if (live) {
         const size_t rowoff = (size_t)r * a.cols;
         const float mu = KIND != 1 ? a.mean[r] : 0.f;
         const float rs = KIND != 1 ? a.rstd[r] : 0.f;
-        int gi = li;
-        for (; gi + (U - 1) * LANES < groups; gi += U * LANES) {
+        int gi = seg * per_seg + li;
+        for (; gi + (U - 1) * LANES < g1; gi += U * LANES) {
             GroupIn<VEC> g[U];
             WeightGroup<VEC> w[U];
 #pragma unroll
@@ -286,7 +296,7 @@ rows_coef_kernel(GenArgs a)
 #pragma unroll
             for (int k = 0; k < U; ++k) add_row_sums<KIND, VEC>(g[k], w[k].v, mu, rs, s0, s1);
         }
-        for (; gi < groups; gi += LANES) {
+        for (; gi < g1; gi += LANES) {
             GroupIn<VEC> g;
             WeightGroup<VEC> w;
             load_group<false, false, TX, TDY, VEC>(a, rowoff + (size_t)gi * VEC, g);
@@ -311,7 +321,20 @@ rows_coef_kernel(GenArgs a)
             s1 += red[(w0 + k) * 2 + 1];
         }
     }
-    if (live && li == 0) reinterpret_cast<float2 *>(a.coef)[r] = row_coefs<KIND>(a, r, s0, s1);
+    if (live && li == 0) reinterpret_cast<float2 *>(a.coef)[unit] = make_float2(s0, s1);
+}
+
+// The coefficients of row r from its segments' sums, added in segment order.
+template <int KIND>
+__device__ __forceinline__ float2 strip_coefs(const GenArgs &a, int64_t r)
+{
+    const float2 *c = reinterpret_cast<const float2 *>(a.coef) + r * a.nseg;
+    float s0 = c[0].x, s1 = c[0].y;
+    for (int k = 1; k < a.nseg; ++k) {
+        s0 += c[k].x;
+        s1 += c[k].y;
+    }
+    return row_coefs<KIND>(a, r, s0, s1);
 }
 
 // ---- wide rows, pass 2: column strips by row chunks --------------------------------
@@ -342,7 +365,6 @@ rows_strip_kernel(GenArgs a)
     if (col_ok) {
         WeightGroup<VEC> w;
         w.load(a.w, a.w_bf16, col);
-        const float2 *coef = reinterpret_cast<const float2 *>(a.coef);
         int64_t r = r0 + rl;
         for (; r + (U - 1) * RT < r1; r += U * RT) {
             GroupIn<VEC> g[U];
@@ -352,7 +374,7 @@ rows_strip_kernel(GenArgs a)
             for (int k = 0; k < U; ++k) {
                 const int64_t rk = r + k * RT;
                 load_group<KIND == 2, true, TX, TDY, VEC>(a, (size_t)rk * a.cols + col, g[k]);
-                c[k] = coef[rk];
+                c[k] = strip_coefs<KIND == 2 ? 0 : KIND>(a, rk);
                 mu[k] = KIND != 1 ? a.mean[rk] : 0.f;
                 rs[k] = KIND != 1 ? a.rstd[rk] : 0.f;
             }
@@ -366,7 +388,8 @@ rows_strip_kernel(GenArgs a)
             load_group<KIND == 2, true, TX, TDY, VEC>(a, (size_t)r * a.cols + col, g);
             const float mu = KIND != 1 ? a.mean[r] : 0.f;
             const float rs = KIND != 1 ? a.rstd[r] : 0.f;
-            group_out<KIND, TDX, VEC, Q>(a, (size_t)r * a.cols + col, g, w.v, mu, rs, coef[r], p);
+            group_out<KIND, TDX, VEC, Q>(a, (size_t)r * a.cols + col, g, w.v, mu, rs,
+                                         strip_coefs<KIND == 2 ? 0 : KIND>(a, r), p);
         }
     }
     if (!a.want_cols) return;
@@ -397,11 +420,12 @@ static hipError_t strip_launch(const RowsCall &a, const GenArgs &g, int kid, hip
 {
     constexpr int CK = KIND == 2 ? 0 : KIND;  // the bias+dropout+add rows reduce as LayerNorm's
     hipError_t e;
+    const int64_t units = (int64_t)a.rows * a.gen_coef_segs;
     if (a.gen_coef_waves == 1)
         e = launch(NH_K_ROWS_COEF, rows_coef_kernel<CK, TX, TDY, VEC, 1>,
-                   dim3((unsigned)ceil_div(a.rows, kTeamWaves)), dim3(kTeam), 0u, s, g);
+                   dim3((unsigned)ceil_div(units, kTeamWaves)), dim3(kTeam), 0u, s, g);
     else
-        e = launch(NH_K_ROWS_COEF, rows_coef_kernel<CK, TX, TDY, VEC, kTeamWaves>, dim3((unsigned)a.rows),
+        e = launch(NH_K_ROWS_COEF, rows_coef_kernel<CK, TX, TDY, VEC, kTeamWaves>, dim3((unsigned)units),
                    dim3(kTeam), 0u, s, g);
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)ceil_div(a.cols / VEC, kGenStripGroups), (unsigned)a.blocks);
@@ -479,7 +503,10 @@ hipError_t rows_generic_launch(const RowsCall &a, hipStream_t s)
                                  (a.kind == 2 && a.dbias_in != nullptr));
     g.ct = a.gen_ct;
     g.rpc = a.gen_rpc;
-    if (a.gen_ct <= 0 && (a.coef == nullptr || a.gen_rpc <= 0)) return hipErrorInvalidValue;
+    g.nseg = a.gen_coef_segs;
+    if (a.gen_ct <= 0 && (a.coef == nullptr || a.gen_rpc <= 0 || a.gen_coef_segs < 1 ||
+                          (a.gen_coef_segs > 1 && a.gen_coef_waves == 1)))
+        return hipErrorInvalidValue;
     switch (a.kind) {
     case 0: return generic_kind<0>(a, g, s);
     case 1: return generic_kind<1>(a, g, s);

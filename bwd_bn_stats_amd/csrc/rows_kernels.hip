@@ -417,7 +417,13 @@ static hipError_t colsum_cx(const RowsCall &a, int kid, hipStream_t s)
 template <typename TOUT>
 static hipError_t colsum(const RowsCall &a, int kid, hipStream_t s)
 {
-    switch (a.colsum_cols > 0 ? a.colsum_cols : 32) {
+    // Columns per block, measured on MI355X: 64 when there are at most 16
+    // partial rows (fewer, fuller blocks: 4.2 vs 6.5 us at 32768 columns),
+    // 16 for rows of at most 64 columns (more threads per column: 4.5 vs 14 us
+    // over 2048 partial rows), else 32.
+    const int cx = a.colsum_cols > 0 ? a.colsum_cols
+                 : (a.blocks <= 16 ? 64 : (a.cols <= kGenNarrowGroups ? 16 : 32));
+    switch (cx) {
     case 8: return colsum_cx<TOUT, 8>(a, kid, s);
     case 16: return colsum_cx<TOUT, 16>(a, kid, s);
     case 64: return colsum_cx<TOUT, 64>(a, kid, s);

@@ -404,7 +404,8 @@ nh_status nh_bn_plan(int64_t N, int64_t C, int64_t HW, nh_dtype io, int *grid_y)
 
 /* Row-kernel plan: the largest number of blocks G (column-partial rows) a
  * [rows, cols] LayerNorm or RMSNorm backward uses on the current device
- * (the workspace is sized for it; the dtypes decide the actual G). */
+ * (the workspace is sized for it; the dtypes and alignment decide the
+ * actual G). */
 nh_status nh_rows_plan(int64_t rows, int64_t cols, int *blocks);
 
 /*

@@ -42,7 +42,9 @@ CASES = [
     (777, 63, F32, F32, BF16, 0, "narrow"),
     (300, 65, F32, BF16, F32, 1, "strip"),          # narrowest strip row
     (513, 1601, BF16, BF16, BF16, 0, "strip"),      # odd width: scalar groups
-    (100, 5000, F32, F32, BF16, 1, "strip"),        # a 256-thread team per coefficient row
+    (100, 5000, F32, F32, BF16, 1, "strip"),        # few long rows: 8 team segments per row
+    (1100, 1100, F32, BF16, F32, 1, "strip"),       # one team per row
+    (2000, 700, BF16, F32, BF16, 1, "strip"),       # one wave per row
     (37, 20000, BF16, F32, F32, 3, "strip"),
     (200, 20000, BF16, BF16, BF16, 0, "strip"),     # aligned, too wide: 8-element groups
     (70, 40960, F32, F32, F32, 0, "strip"),         # aligned fp32: 4-element groups
