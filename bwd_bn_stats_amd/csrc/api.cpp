@@ -272,6 +272,39 @@ void rows_generic_plan(RowsCall &a, bool vec_ok, const DeviceInfo &d)
     a.blocks = (int)ceil_div(a.rows, rpc);
 }
 
+// Forward generic path (no vector variant fits): rows of at most
+// kGenNarrowGroups columns take the narrow kernel (a subgroup of ct lanes per
+// row, each row slot loading kGenNarrowRowsInFlight rows at once, at most 8
+// blocks per CU); wider rows a team per row with vec-element groups when the
+// tensors allow it, 1024 threads when 256-thread teams would leave the device
+// part empty and every thread still gets kGenFwdMinGroupsPerThread groups,
+// one block per row up to a full device.
+void rows_forward_generic_plan(FwdCall &a, bool vec_ok, const DeviceInfo &d)
+{
+    const int64_t full = (int64_t)d.cus * 8;  // resident 256-thread blocks
+    a.maxg = 0;
+    if (a.cols <= kGenNarrowGroups) {
+        int ct = 1;
+        while (ct < a.cols) ct <<= 1;
+        int64_t g = ceil_div(a.rows, (int64_t)(kTeam / ct) * kGenNarrowRowsInFlight);
+        if (g > full) g = full;
+        if (g < 1) g = 1;
+        a.vec = 1;
+        a.team = kTeam;
+        a.gen_ct = ct;
+        a.blocks = (int)g;
+        return;
+    }
+    const int gvec = vec_ok && a.cols % a.vec == 0 ? a.vec : 1;
+    const int64_t groups = a.cols / gvec;
+    const bool big = a.rows < full && groups >= (int64_t)kGenFwdBigTeam * kGenFwdMinGroupsPerThread;
+    a.vec = gvec;
+    a.gen_ct = 0;
+    a.team = big ? kGenFwdBigTeam : kTeam;
+    const int64_t cap = full * kTeam / a.team;
+    a.blocks = (int)(a.rows < cap ? a.rows : cap);
+}
+
 // Blocks: as many as fit on the device at once (occupancy of the chosen
 // variant, at most rows_blocks_per_cu(kind) per CU), at most one per row.
 // Measured on MI355X: single-team blocks beat fewer, wider blocks that
@@ -763,10 +796,17 @@ static nh_status rows_forward_run(FwdCall &a, void *stream)
     need_align(a.w, a.w_t);
     need_align(a.b, a.w_t);
     RowsPlan p = rows_variant(a.cols, a.vec, vec_ok);
+    a.depth = (int)g_override_rows_depth.load();
+    hipError_t e = hipSuccess;
+    if (p.maxg == 0) {
+        rows_forward_generic_plan(a, vec_ok, d);
+        e = rows_forward_launch(a, s);
+        if (e != hipSuccess) return hip_fail(e, "forward row kernel launch");
+        return ok();
+    }
     a.maxg = p.maxg;
     a.vec = p.vec;
     a.team = p.team;
-    a.depth = (int)g_override_rows_depth.load();
     int dev = 0;
     (void)hipGetDevice(&dev);
     const int64_t key = -1 - (((((((((int64_t)dev * 2 + a.kind) * 2 + a.x_t) * 2 + a.y_t) * 16 + a.maxg) * 16) +
@@ -777,7 +817,6 @@ static nh_status rows_forward_run(FwdCall &a, void *stream)
         auto it = g_rows_occupancy.find(key);
         if (it != g_rows_occupancy.end()) occ = it->second;
     }
-    hipError_t e = hipSuccess;
     if (occ == 0) {
         a.occupancy_out = &occ;
         e = rows_forward_launch(a, s);

@@ -120,10 +120,19 @@ struct FwdCall {
     float eps;
     void *y;
     float *stat0, *stat1;  // LayerNorm: mean, rstd; RMSNorm: rms
-    int team;              // threads per row team / block of the vector path (256 or 512)
+    int team;              // threads per row team / block: vector path 256 or 512, generic path 256 or 1024
     int depth;             // row-pipeline depth of the vector path (0 = the kernel's default)
     int *occupancy_out;    // non-NULL: report blocks per CU instead of launching
+    int gen_ct;            // generic path: lanes per row of the narrow kernel (0 = a team per row)
 };
+
+// Forward generic path: rows of at most kGenNarrowGroups columns take a
+// lane subgroup per row; wider rows a team per row that reads the row twice
+// (the second time from the caches), kGenFwdBigTeam threads wide when there
+// are too few rows to fill the device with 256-thread teams and each thread
+// still gets at least kGenFwdMinGroupsPerThread groups.
+constexpr int kGenFwdBigTeam = 1024;
+constexpr int kGenFwdMinGroupsPerThread = 2;
 
 hipError_t rows_forward_launch(const FwdCall &a, hipStream_t s);
 

@@ -58,6 +58,15 @@ __device__ __forceinline__ void team_sum2(float *red, int wave, int lane, float 
     b = sb;
 }
 
+// Sum over the ct lanes of a subgroup (ct a power of two, subgroups aligned
+// to ct inside the wave): a butterfly over xor distances ct/2 .. 1, so every
+// lane of the subgroup ends with the same bits, in a fixed order.
+__device__ __forceinline__ float sub_sum(float v, int ct)
+{
+    for (int o = ct >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
 // Software-pipelined walk over a team's rows with D row buffers in
 // registers: while row i is reduced and written, the loads of rows i+1 ..
 // i+D-1 are in flight.  Buffers rotate by unrolling, so each stays in fixed

@@ -136,63 +136,156 @@ norm_fwd_rows_kernel(const TX *__restrict__ x, const void *__restrict__ w,
     pipeline_rows<D, RowBuf>(iters, load_row, do_row);
 }
 
-// Any width, any alignment: scalar accesses, two reads of the row (the second
-// from cache).
+// ---- generic path ------------------------------------------------------------------
+// The row's statistics and output from its two sums (LayerNorm: shifted sum
+// and sum of squares; RMSNorm: sum of squares): y = fmaf(x - c, a*w, b)
+// (LayerNorm) or y = (x*a)*w (RMSNorm).  Writes the statistics if `writer`.
+template <int KIND>
+__device__ __forceinline__ void fwd_row_stats(float s1, float s2, float K, float invH, float eps, int64_t r,
+                                              bool writer, float *stat0, float *stat1, float &a, float &c)
+{
+    if constexpr (KIND == 0) {
+        const float md = s1 * invH;
+        const float var = fmaxf(s2 * invH - md * md, 0.f);
+        c = K + md;
+        a = 1.0f / sqrtf(var + eps);
+        if (writer) {
+            stat0[r] = c;
+            if (stat1 != nullptr) stat1[r] = a;
+        }
+    } else {
+        const float rms = sqrtf(fmaf(s2, invH, eps));
+        a = 1.0f / rms;
+        c = 0.f;
+        if (writer && stat0 != nullptr) stat0[r] = rms;
+    }
+}
+
+// Rows of at most 64 columns, any alignment: a subgroup of ct lanes (the
+// power of two covering the row) per row, U rows of a slot loaded at once,
+// the row sums reduced by lane exchanges inside the subgroup.
 template <int KIND, typename TX, typename TY>
 __global__ void __launch_bounds__(kTeam)
-norm_fwd_generic_kernel(const TX *__restrict__ x, const void *__restrict__ w,
-                        const void *__restrict__ b, int w_bf16, int rows, int H, float eps,
-                        TY *__restrict__ y, float *__restrict__ stat0, float *__restrict__ stat1)
+norm_fwd_narrow_kernel(const TX *__restrict__ x, const void *__restrict__ w,
+                       const void *__restrict__ b, int w_bf16, int rows, int H, float eps,
+                       TY *__restrict__ y, float *__restrict__ stat0, float *__restrict__ stat1, int ct)
 {
-    __shared__ float red[kRedFloats];
+    constexpr int U = kGenNarrowRowsInFlight;
+    const int tt = threadIdx.x;
+    const int lane = tt & (ct - 1);
+    const int slot = tt >> __builtin_ctz((unsigned)ct);
+    const int slots = kTeam / ct;
+    const bool col_ok = lane < H;
+    const int col = col_ok ? lane : 0;  // dead lanes read column 0 and drop it
+    const float invH = 1.0f / (float)H;
+    const float wj = w != nullptr ? load_param(w, w_bf16, col) : 1.f;
+    const float bj = KIND == 0 && b != nullptr ? load_param(b, w_bf16, col) : 0.f;
+    const int64_t stride = (int64_t)gridDim.x * slots;
+    for (int64_t r0 = (int64_t)blockIdx.x * slots + slot; r0 < rows; r0 += U * stride) {
+        float v[U], K[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t rk = r0 + k * stride;
+            const size_t rowoff = (size_t)(rk < rows ? rk : rows - 1) * H;
+            v[k] = to_f32(__builtin_nontemporal_load(x + rowoff + col));
+            K[k] = KIND == 0 ? to_f32(x[rowoff]) : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            float s1 = 0.f, s2 = 0.f;
+            if (col_ok) {
+                const float d = v[k] - K[k];
+                s1 = KIND == 0 ? d : 0.f;
+                s2 = d * d;
+            }
+            s1 = sub_sum(s1, ct);
+            s2 = sub_sum(s2, ct);
+            const int64_t rk = r0 + k * stride;
+            if (rk < rows) {
+                float a, c;
+                fwd_row_stats<KIND>(s1, s2, K[k], invH, eps, rk, lane == 0, stat0, stat1, a, c);
+                const float o = KIND == 0 ? fmaf((v[k] - c) * a, wj, bj) : wj * (v[k] * a);
+                if (col_ok) __builtin_nontemporal_store(from_f32<TY>(o), y + (size_t)rk * H + col);
+            }
+        }
+    }
+}
+
+// Wider rows, any alignment (VEC = 1) or too wide for the register-resident
+// kernel (VEC = the vector width): a TEAM-thread block per row, two reads of
+// the row -- the first (cacheable) for the sums, U groups of a thread in
+// flight, the second from the caches for the output.
+template <int KIND, typename TX, typename TY, int VEC, int TEAM>
+__global__ void __launch_bounds__(TEAM)
+norm_fwd_team_kernel(const TX *__restrict__ x, const void *__restrict__ w,
+                     const void *__restrict__ b, int w_bf16, int rows, int H, float eps,
+                     TY *__restrict__ y, float *__restrict__ stat0, float *__restrict__ stat1)
+{
+    constexpr int WAVES = TEAM / kWave;
+    constexpr int U = VEC == 8 ? 4 : 8;
+    __shared__ float red[red_floats(TEAM)];
     const int tt = threadIdx.x;
     const int wave = tt / kWave;
     const int lane = tt & (kWave - 1);
+    const int groups = H / VEC;
     const float invH = 1.0f / (float)H;
     int it = 0;
-    // 64-bit row index: rows may reach 2^31 - 1 (one column), r + G must not wrap.
+    // 64-bit row index: r + gridDim.x must not wrap.
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x, ++it) {
-        const size_t rowoff = (size_t)r * H;
-        const float K = KIND == 0 ? to_f32(x[rowoff]) : 0.f;
+        const TX *xr = x + (size_t)r * H;
+        const float K = KIND == 0 ? to_f32(xr[0]) : 0.f;
         float s1 = 0.f, s2 = 0.f;
-        for (int j = tt; j < H; j += kTeam) {
-            const float v = to_f32(x[rowoff + j]);
-            if (KIND == 0) {
-                const float d = v - K;
-                s1 += d;
+        auto add = [&](const float (&v)[VEC]) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const float d = v[e] - K;
+                if constexpr (KIND == 0) s1 += d;
                 s2 = fmaf(d, d, s2);
-            } else {
-                s2 = fmaf(v, v, s2);
             }
+        };
+        int gi = tt;
+        for (; gi + (U - 1) * TEAM < groups; gi += U * TEAM) {
+            float v[U][VEC];
+#pragma unroll
+            for (int k = 0; k < U; ++k) ld<false, TX, VEC>(xr + (size_t)(gi + k * TEAM) * VEC, v[k]);
+#pragma unroll
+            for (int k = 0; k < U; ++k) add(v[k]);
         }
-        team_sum2(red + (it & 1) * (kRedFloats / 2), wave, lane, s1, s2);
+        for (; gi < groups; gi += TEAM) {
+            float v[VEC];
+            ld<false, TX, VEC>(xr + (size_t)gi * VEC, v);
+            add(v);
+        }
+        team_sum2<WAVES>(red + (it & 1) * (red_floats(TEAM) / 2), wave, lane, s1, s2);
         float a, c;
-        if (KIND == 0) {
-            const float md = s1 * invH;
-            const float var = fmaxf(s2 * invH - md * md, 0.f);
-            c = K + md;
-            a = 1.0f / sqrtf(var + eps);
-            if (tt == 0) {
-                stat0[r] = c;
-                if (stat1 != nullptr) stat1[r] = a;
+        fwd_row_stats<KIND>(s1, s2, K, invH, eps, r, tt == 0, stat0, stat1, a, c);
+        TY *yr = y + (size_t)r * H;
+        auto out = [&](int grp, const float (&v)[VEC]) {
+            ParamGroup<VEC> wv, bv;
+            wv.load(w, w_bf16, grp * VEC, 1.f);
+            if constexpr (KIND == 0) bv.load(b, w_bf16, grp * VEC, 0.f);
+            float o[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                if constexpr (KIND == 0)
+                    o[e] = fmaf((v[e] - c) * a, wv.v[e], bv.v[e]);
+                else
+                    o[e] = wv.v[e] * (v[e] * a);
             }
-        } else {
-            const float rms = sqrtf(fmaf(s2, invH, eps));
-            a = 1.0f / rms;
-            c = 0.f;
-            if (tt == 0 && stat0 != nullptr) stat0[r] = rms;
+            st<true, TY, VEC>(yr + (size_t)grp * VEC, o);
+        };
+        gi = tt;
+        for (; gi + (U - 1) * TEAM < groups; gi += U * TEAM) {
+            float v[U][VEC];
+#pragma unroll
+            for (int k = 0; k < U; ++k) ld<true, TX, VEC>(xr + (size_t)(gi + k * TEAM) * VEC, v[k]);
+#pragma unroll
+            for (int k = 0; k < U; ++k) out(gi + k * TEAM, v[k]);
         }
-        for (int j = tt; j < H; j += kTeam) {
-            const float v = to_f32(x[rowoff + j]);
-            const float wj = w ? load_param(w, w_bf16, j) : 1.f;
-            float o;
-            if (KIND == 0) {
-                const float bj = b ? load_param(b, w_bf16, j) : 0.f;
-                o = fmaf((v - c) * a, wj, bj);
-            } else {
-                o = wj * (v * a);
-            }
-            y[rowoff + j] = from_f32<TY>(o);
+        for (; gi < groups; gi += TEAM) {
+            float v[VEC];
+            ld<true, TX, VEC>(xr + (size_t)gi * VEC, v);
+            out(gi, v);
         }
     }
 }
@@ -225,15 +318,33 @@ static hipError_t fwd_vec(const FwdCall &a, hipStream_t s)
     }
 }
 
+template <int KIND, typename TX, typename TY, int VEC>
+static hipError_t fwd_team(const FwdCall &a, hipStream_t s)
+{
+    const int kid = KIND == 0 ? NH_K_LN_FWD : NH_K_RMS_FWD;
+    if (a.team == kGenFwdBigTeam)
+        return launch(kid, norm_fwd_team_kernel<KIND, TX, TY, VEC, kGenFwdBigTeam>, dim3(a.blocks),
+                      dim3(kGenFwdBigTeam), 0u, s, static_cast<const TX *>(a.x), a.w, a.b, a.w_t, a.rows,
+                      a.cols, a.eps, static_cast<TY *>(a.y), a.stat0, a.stat1);
+    return launch(kid, norm_fwd_team_kernel<KIND, TX, TY, VEC, kTeam>, dim3(a.blocks), dim3(kTeam), 0u, s,
+                  static_cast<const TX *>(a.x), a.w, a.b, a.w_t, a.rows, a.cols, a.eps,
+                  static_cast<TY *>(a.y), a.stat0, a.stat1);
+}
+
+// Generic path: the plan (gen_ct, team, vec, blocks) comes from the host.
 template <int KIND, typename TX, typename TY>
 static hipError_t fwd_generic(const FwdCall &a, hipStream_t s)
 {
-    auto kern = norm_fwd_generic_kernel<KIND, TX, TY>;
-    if (a.occupancy_out)
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kern, kTeam, 0);
-    return launch(KIND == 0 ? NH_K_LN_FWD : NH_K_RMS_FWD, kern, dim3(a.blocks), dim3(kTeam), 0u, s,
-                  static_cast<const TX *>(a.x), a.w, a.b, a.w_t, a.rows, a.cols, a.eps,
-                  static_cast<TY *>(a.y), a.stat0, a.stat1);
+    if (a.occupancy_out) { *a.occupancy_out = 1; return hipSuccess; }  // not used by the generic plan
+    if (a.gen_ct > 0)
+        return launch(KIND == 0 ? NH_K_LN_FWD : NH_K_RMS_FWD, norm_fwd_narrow_kernel<KIND, TX, TY>,
+                      dim3(a.blocks), dim3(kTeam), 0u, s, static_cast<const TX *>(a.x), a.w, a.b, a.w_t,
+                      a.rows, a.cols, a.eps, static_cast<TY *>(a.y), a.stat0, a.stat1, a.gen_ct);
+    if (a.vec == 1) return fwd_team<KIND, TX, TY, 1>(a, s);
+    // The vector width of a type mix: 8 when x and y are both bf16, else 4.
+    constexpr int V = sizeof(TX) == 2 && sizeof(TY) == 2 ? 8 : 4;
+    if (a.vec != V) return hipErrorInvalidValue;
+    return fwd_team<KIND, TX, TY, V>(a, s);
 }
 
 template <int KIND, typename TX, typename TY, int VEC>

@@ -181,15 +181,6 @@ __device__ __forceinline__ void group_out(const GenArgs &a, size_t off, const Gr
     if (a.dx != nullptr) st<true, TDX, VEC>(static_cast<TDX *>(a.dx) + off, o);
 }
 
-// Sum over the ct lanes of a subgroup (ct a power of two, subgroups aligned
-// to ct inside the wave): a butterfly over xor distances ct/2 .. 1, so every
-// lane of the subgroup ends with the same bits, in a fixed order.
-__device__ __forceinline__ float sub_sum(float v, int ct)
-{
-    for (int o = ct >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
-}
-
 // ---- narrow rows: a subgroup of lanes per row ----------------------------------
 template <int KIND, typename TX, typename TDY, typename TDX>
 __global__ void __launch_bounds__(kTeam)

@@ -140,3 +140,28 @@ def test_generic_bit_identical_runs(nh, rows, cols, offset):
     for u, v in zip(list(a) + list(ra), list(b) + list(rb)):
         bits = (lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32))
         assert torch.equal(bits(u), bits(v))
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}x{c[1]}-{c[6]}-off{c[5]}")
+def test_generic_forward(nh, oracle_mod, case):
+    """LayerNorm forward (y in x's dtype, and fp32 y from bf16 x) and RMSNorm
+    forward on the same shapes and layouts: the narrow kernel for rows of at
+    most 64 columns, a team per row (256 or 1024 threads) beyond."""
+    rows, cols, xt, _, wt, offset, _ = case
+    print(f"[generic fwd] rows={rows} cols={cols} x={xt} w={wt} offset={offset}", flush=True)
+    c = wl.rows_case(rows, cols, x_t=xt, dy_t=xt, w_t=wt, seed=rows * 5 + cols, with_bias=True)
+    x, w, b = place(c.x, offset), place(c.w, offset), place(c.b, offset)
+    wy, wm, wr = oracle_mod.layernorm_forward(c.x.value, c.w.value, c.b.value, eps=c.eps)
+    for yt in sorted({xt, F32}):
+        y, m, r = nh.layernorm_forward(x, w, b, c.eps, y_dtype=_tdt(yt))
+        torch.cuda.synchronize()
+        check(f"ln y ({yt})", host(y), wy, yt)
+        check("ln mean", host(m), wm, F32)
+        check("ln rstd", host(r), wr, F32)
+    rc = wl.rows_case(rows, cols, x_t=xt, dy_t=xt, w_t=xt, seed=rows * 13 + cols)
+    rx, rw = place(rc.x, offset), place(rc.w, offset)
+    wy, wrms = oracle_mod.rmsnorm_forward(rc.x.value, rc.w.value, eps=rc.eps)
+    y, rms = nh.rmsnorm_forward(rx, rw, rc.eps)
+    torch.cuda.synchronize()
+    check("rms y", host(y), wy, xt)
+    check("rms rms", host(rms), wrms, F32)
