@@ -93,6 +93,7 @@ std::atomic<int64_t> g_override_rows_blocks{0};
 std::atomic<int64_t> g_override_bn_finalize_kernels{0};
 std::atomic<int64_t> g_override_rows_depth{0};
 std::atomic<int64_t> g_override_colsum_cols{0};
+std::atomic<int64_t> g_override_rows_teams{0};
 
 // ---- BatchNorm planning ----------------------------------------------------------
 // Resident 256-thread block slots of the device: CUs * (threads per CU / 256),
@@ -627,6 +628,7 @@ static nh_status rows_run(RowsCall &a, int Q, void *ws, size_t ws_bytes, void *s
     RowsPlan p = rows_variant(a.cols, a.vec, vec_ok, a.kind == 2 ? kBdaMaxRowElems : kRowsMaxRowElems);
     a.depth = (int)g_override_rows_depth.load();
     a.colsum_cols = (int)g_override_colsum_cols.load();
+    a.teams = (int)g_override_rows_teams.load();
     hipError_t e = hipSuccess;
     if (p.maxg == 0) {
         rows_generic_plan(a, vec_ok, d);
@@ -644,8 +646,8 @@ static nh_status rows_run(RowsCall &a, int Q, void *ws, size_t ws_bytes, void *s
     int dev = 0;
     (void)hipGetDevice(&dev);
     const int dxt = a.dx != nullptr ? a.dx_t : a.dy_t;
-    const int64_t key = ((((((((int64_t)dev * 4 + a.kind) * 2 + a.x_t) * 2 + a.dy_t) * 2 + dxt) * 16 +
-                           a.maxg) * 16 + a.vec) * 8 + a.depth) * 2 + (a.team == kWideTeam);
+    const int64_t key = (((((((((int64_t)dev * 4 + a.kind) * 2 + a.x_t) * 2 + a.dy_t) * 2 + dxt) * 16 +
+                           a.maxg) * 16 + a.vec) * 8 + a.depth) * 2 + (a.team == kWideTeam)) * 2 + (a.teams == 2);
     int occ = 0;
     {
         std::lock_guard<std::mutex> lk(g_dev_mu);
@@ -1015,6 +1017,10 @@ nh_status nh_plan_override(const char *key, int64_t value)
         if (value != 0 && value != 8 && value != 16 && value != 32 && value != 64)
             return fail(NH_ERR_ARG, "colsum_cols must be 0, 8, 16, 32 or 64");
         g_override_colsum_cols.store(value);
+    }
+    else if (strcmp(key, "rows_teams") == 0) {
+        if (value > 2) return fail(NH_ERR_ARG, "rows_teams must be 0, 1 or 2");
+        g_override_rows_teams.store(value);
     }
     else if (strcmp(key, "bn_finalize_kernels") == 0) g_override_bn_finalize_kernels.store(value);
     else return fail(NH_ERR_ARG, "unknown override key '%s'", key);

@@ -29,6 +29,7 @@ struct RowsCall {
     int team;            // threads per row team / block of the vector path (256 or 512)
     int depth;           // row-pipeline depth of the vector path (0 = the kernel's default)
     int colsum_cols;     // columns per column-finalize block (0 = default)
+    int teams;           // RMSNorm vector path: row teams per block (1 or 2; 0 = by row size)
     int *occupancy_out;  // non-NULL: report resident 256-thread blocks per CU
                          // of the selected row kernel instead of launching
     // Generic path (maxg == 0; vec is then 1 or the vector width):

@@ -140,15 +140,22 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
 }
 
 // ---- RMSNorm, vector path ----------------------------------------------------
-template <typename T, int VEC, int MAXG, int TEAM, int D>
-__global__ void __launch_bounds__(TEAM, kRowsBwdWavesPerSimd)
+// TEAMS teams per block (1 or 2): with 2, the teams take interleaved rows,
+// keep their own column sums, and add them through LDS into the block's one
+// partial row at the end -- twice the rows in flight per block at the same
+// number of partial rows.  Both teams pass every row-sum barrier (the block
+// barrier) the same number of times: they share the iteration count.
+template <typename T, int VEC, int MAXG, int TEAM, int D, int TEAMS = 1>
+__global__ void __launch_bounds__(TEAM * TEAMS, kRowsBwdWavesPerSimd)
 rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
                 const float *__restrict__ rms, float eps, const void *__restrict__ w,
                 int w_bf16, int rows, int H, T *__restrict__ dx,
                 float *__restrict__ partials, int want_cols)
 {
-    __shared__ float red[red_floats(TEAM)];
-    const int tt = threadIdx.x;
+    __shared__ float red_all[TEAMS * red_floats(TEAM)];
+    const int team = TEAMS > 1 ? (int)threadIdx.x / TEAM : 0;
+    const int tt = (int)threadIdx.x - team * TEAM;
+    float *red = red_all + team * red_floats(TEAM);
     const int wave = tt / kWave;
     const int lane = tt & (kWave - 1);
     const int G = gridDim.x;
@@ -165,8 +172,8 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
         for (int e = 0; e < VEC; ++e) p[0][k][e] = 0.f;
     }
 
-    const int iters = (int)ceil_div(rows, (int64_t)G);
-    auto row_of = [&](int it) { return it * G + (int)blockIdx.x; };
+    const int iters = (int)ceil_div(rows, (int64_t)G * TEAMS);
+    auto row_of = [&](int it) { return (it * G + (int)blockIdx.x) * TEAMS + team; };
 
     // One row in flight (see the LayerNorm kernel: branch-free buffer loads).
     struct RowBuf {
@@ -231,7 +238,24 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
     };
 
     pipeline_rows<D, RowBuf>(iters, load_row, do_row);
-    if (want_cols) write_partials<VEC, MAXG, 1, TEAM>(p, tt, Gr, H, G, partials);
+    if (!want_cols) return;
+    if constexpr (TEAMS > 1) {
+        // team 1's column sums into LDS (reusing nothing: a buffer of its own),
+        // then team 0 adds them and writes the block's partial row
+        __shared__ float comb[MAXG * VEC * TEAM];
+        if (team == 1)
+#pragma unroll
+            for (int k = 0; k < MAXG; ++k)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) comb[(k * VEC + e) * TEAM + tt] = p[0][k][e];
+        __syncthreads();
+        if (team != 0) return;
+#pragma unroll
+        for (int k = 0; k < MAXG; ++k)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) p[0][k][e] += comb[(k * VEC + e) * TEAM + tt];
+    }
+    write_partials<VEC, MAXG, 1, TEAM>(p, tt, Gr, H, G, partials);
 }
 
 // ---- column finalize: fp64 fixed-order sum of the G partial rows -------------
@@ -314,15 +338,32 @@ static hipError_t ln_vec(const RowsCall &a, hipStream_t s)
     }
 }
 
-template <typename T, int VEC, int MAXG, int TEAM, int D>
-static hipError_t rms_vec_d(const RowsCall &a, hipStream_t s)
+template <typename T, int VEC, int MAXG, int TEAM, int D, int TEAMS>
+static hipError_t rms_vec_dt(const RowsCall &a, hipStream_t s)
 {
-    auto kern = rms_rows_kernel<T, VEC, MAXG, TEAM, D>;
-    if (a.occupancy_out) return occupancy(a, kern, TEAM);
-    return launch(NH_K_RMS_ROWS, kern, dim3(a.blocks), dim3(TEAM), 0u, s,
+    auto kern = rms_rows_kernel<T, VEC, MAXG, TEAM, D, TEAMS>;
+    if (a.occupancy_out) return occupancy(a, kern, TEAM * TEAMS);
+    return launch(NH_K_RMS_ROWS, kern, dim3(a.blocks), dim3(TEAM * TEAMS), 0u, s,
                   static_cast<const T *>(a.dy), static_cast<const T *>(a.x), a.rms, a.eps, a.w,
                   a.w_t, a.rows, a.cols, static_cast<T *>(a.dx), a.partials,
                   (int)(a.dweight != nullptr));
+}
+
+// Row teams per block: 2 when a thread's row buffer is at most 64 bytes
+// (rows of up to 4096 bf16 / 2048 fp32 columns), else 1.  Measured on
+// MI355X with one block per CU: short rows leave one team per CU latency
+// bound (8192x1600 bf16: 31.6 -> 23.0 us with two teams; 4096x4096 bf16:
+// 26.3 -> 24.4 us), while at 8192 columns the second team only costs
+// registers (2048x8192 fp32: 40.6 -> 44.2 us).
+template <typename T, int VEC, int MAXG, int TEAM, int D>
+static hipError_t rms_vec_d(const RowsCall &a, hipStream_t s)
+{
+    constexpr int BYTES = MAXG * VEC * 2 * (int)sizeof(T);
+    if constexpr (TEAM == kTeam) {
+        const int teams = a.teams > 0 ? a.teams : (BYTES <= 64 ? 2 : 1);
+        if (teams == 2) return rms_vec_dt<T, VEC, MAXG, TEAM, D, 2>(a, s);
+    }
+    return rms_vec_dt<T, VEC, MAXG, TEAM, D, 1>(a, s);
 }
 
 template <typename T, int VEC, int MAXG, int TEAM = kTeam>

@@ -244,3 +244,20 @@ def test_wide_rows(nh, oracle_mod, rows, cols, xt, dyt):
     r = wl.rows_case(rows, cols, x_t=xt, dy_t=xt, w_t=xt, seed=rows * 3 + cols)
     _rms_case(nh, oracle_mod, r, saved=True)
     _rms_case(nh, oracle_mod, r, saved=False)
+
+
+@pytest.mark.parametrize("rows,cols,dt,blocks", [(2048, 8192, wl.BF16, 0), (1001, 8192, wl.F32, 0),
+                                                 (777, 1000, wl.BF16, 0), (37, 4096, wl.F32, 5),
+                                                 (3, 2048, wl.BF16, 0)])
+def test_rms_two_team_blocks(nh, oracle_mod, rows, cols, dt, blocks):
+    """RMSNorm with two row teams per block (rows_teams = 2): interleaved rows,
+    the teams' column sums added through LDS; odd row counts leave one team
+    a row short on the last iteration."""
+    c = wl.rows_case(rows, cols, x_t=dt, dy_t=dt, w_t=dt, seed=rows + 5 * cols)
+    nh.plan_override("rows_teams", 2)
+    try:
+        for saved in (True, False):
+            _rms_case(nh, oracle_mod, c, saved=saved, override_blocks=blocks)
+        _rms_case(nh, oracle_mod, c, need=(False, True))
+    finally:
+        nh.plan_override("rows_teams", 0)
