@@ -307,13 +307,14 @@ void rows_forward_generic_plan(FwdCall &a, bool vec_ok, const DeviceInfo &d)
 }
 
 // Blocks: as many as fit on the device at once (occupancy of the chosen
-// variant, at most rows_blocks_per_cu(kind) per CU), at most one per row.
-// Measured on MI355X: single-team blocks beat fewer, wider blocks that
-// synchronize more waves per row.
-void rows_grid(RowsPlan &p, int kind, int64_t rows, int occ, const DeviceInfo &d)
+// variant, at most rows_blocks_per_cu per CU), at most one per row.
+// Measured on MI355X: a 256-thread team per row beats wider teams that
+// synchronize more waves per row (512-thread teams only for rows a
+// 256-thread team cannot hold).
+void rows_grid(RowsPlan &p, int kind, int row_bytes, int64_t rows, int occ, const DeviceInfo &d)
 {
     if (occ < 1) occ = 1;
-    if (occ > rows_blocks_per_cu(kind)) occ = rows_blocks_per_cu(kind);
+    if (occ > rows_blocks_per_cu(kind, row_bytes)) occ = rows_blocks_per_cu(kind, row_bytes);
     int64_t g = (int64_t)d.cus * occ;
     const int64_t ov = g_override_rows_blocks.load();
     if (ov > 0) g = ov;
@@ -647,7 +648,7 @@ static nh_status rows_run(RowsCall &a, int Q, void *ws, size_t ws_bytes, void *s
     (void)hipGetDevice(&dev);
     const int dxt = a.dx != nullptr ? a.dx_t : a.dy_t;
     const int64_t key = (((((((((int64_t)dev * 4 + a.kind) * 2 + a.x_t) * 2 + a.dy_t) * 2 + dxt) * 16 +
-                           a.maxg) * 16 + a.vec) * 8 + a.depth) * 2 + (a.team == kWideTeam)) * 2 + (a.teams == 2);
+                           a.maxg) * 16 + a.vec) * 8 + a.depth) * 2 + (a.team == kWideTeam)) * 3 + a.teams;
     int occ = 0;
     {
         std::lock_guard<std::mutex> lk(g_dev_mu);
@@ -662,7 +663,7 @@ static nh_status rows_run(RowsCall &a, int Q, void *ws, size_t ws_bytes, void *s
         std::lock_guard<std::mutex> lk(g_dev_mu);
         g_rows_occupancy[key] = occ;
     }
-    rows_grid(p, a.kind, a.rows, occ, d);
+    rows_grid(p, a.kind, p.maxg * p.vec * (dtype_bytes(a.x_t) + dtype_bytes(a.dy_t)), a.rows, occ, d);
     a.blocks = p.blocks;
     e = rows_backward_launch(a, s);
     if (e != hipSuccess) return hip_fail(e, "rows backward launch");

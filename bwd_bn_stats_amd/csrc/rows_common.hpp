@@ -105,6 +105,37 @@ constexpr int rows_depth_wide(int row_bytes_per_thread) { return row_bytes_per_t
 // per CU already: depth 2 measured best (LayerNorm 1600, RMSNorm 8192).
 constexpr int kFwdDepth = 2;
 
+// Two row teams per block: adds team 1's column sums into team 0's through
+// LDS, one quantity at a time, in a fixed order.  Returns true for the
+// threads that then hold the block's sums (team 0; every thread with one
+// team).  Every thread of the block must call it.
+template <int Q, int MAXG, int VEC, int TEAM, int TEAMS>
+__device__ __forceinline__ bool combine_teams(float (&p)[Q][MAXG][VEC], int team, int tt)
+{
+    static_assert(TEAMS == 1 || TEAMS == 2, "one or two row teams per block");
+    if constexpr (TEAMS == 1) {
+        return true;
+    } else {
+        __shared__ float comb[MAXG * VEC * TEAM];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            if (q > 0) __syncthreads();  // team 0 has read the previous quantity
+            if (team == 1)
+#pragma unroll
+                for (int k = 0; k < MAXG; ++k)
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) comb[(k * VEC + e) * TEAM + tt] = p[q][k][e];
+            __syncthreads();
+            if (team == 0)
+#pragma unroll
+                for (int k = 0; k < MAXG; ++k)
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) p[q][k][e] += comb[(k * VEC + e) * TEAM + tt];
+        }
+        return team == 0;
+    }
+}
+
 // Writes a block's column sums (Q quantities) as its row of partials[Q, G, H].
 template <int VEC, int MAXG, int Q, int TEAM>
 __device__ __forceinline__ void write_partials(const float (&p)[Q][MAXG][VEC], int tt, int Gr, int H,

@@ -38,15 +38,23 @@ namespace nh {
 // loads of its rows i+1 .. i+D-1 are already in flight (D register sets,
 // used in rotation), so each team keeps D rows of HBM traffic outstanding
 // across the block barrier of the row sum.
-template <typename TX, typename TDY, typename TDX, int VEC, int MAXG, int TEAM, int D>
-__global__ void __launch_bounds__(TEAM, kRowsBwdWavesPerSimd)
+//
+// TEAMS row teams per block (1 or 2).  With 2, the teams take interleaved
+// rows and keep their own column sums, which meet in LDS at the end: twice
+// the rows in flight per block for the same number of partial rows.  Both
+// teams pass every row-sum barrier (a block barrier) the same number of
+// times, since they share the iteration count.
+template <typename TX, typename TDY, typename TDX, int VEC, int MAXG, int TEAM, int D, int TEAMS = 1>
+__global__ void __launch_bounds__(TEAM * TEAMS, kRowsBwdWavesPerSimd)
 ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
                const float *__restrict__ mean, const float *__restrict__ rstd,
                const void *__restrict__ w, int w_bf16, int rows, int H,
                TDX *__restrict__ dx, float *__restrict__ partials, int want_cols)
 {
-    __shared__ float red[red_floats(TEAM)];
-    const int tt = threadIdx.x;
+    __shared__ float red_all[TEAMS * red_floats(TEAM)];
+    const int team = TEAMS > 1 ? (int)threadIdx.x / TEAM : 0;
+    const int tt = (int)threadIdx.x - team * TEAM;
+    float *red = red_all + team * red_floats(TEAM);
     const int wave = tt / kWave;
     const int lane = tt & (kWave - 1);
     const int G = gridDim.x;
@@ -63,8 +71,8 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
         for (int e = 0; e < VEC; ++e) { p[0][k][e] = 0.f; p[1][k][e] = 0.f; }
     }
 
-    const int iters = (int)ceil_div(rows, (int64_t)G);
-    auto row_of = [&](int it) { return it * G + (int)blockIdx.x; };
+    const int iters = (int)ceil_div(rows, (int64_t)G * TEAMS);
+    auto row_of = [&](int it) { return (it * G + (int)blockIdx.x) * TEAMS + team; };
 
     // One row in flight: its x/dy groups and its saved statistics.  The row
     // is read through buffer resources sized to the row (empty past the last
@@ -136,15 +144,12 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
     };
 
     pipeline_rows<D, RowBuf>(iters, load_row, do_row);
-    if (want_cols) write_partials<VEC, MAXG, 2, TEAM>(p, tt, Gr, H, G, partials);
+    if (want_cols && combine_teams<2, MAXG, VEC, TEAM, TEAMS>(p, team, tt))
+        write_partials<VEC, MAXG, 2, TEAM>(p, tt, Gr, H, G, partials);
 }
 
 // ---- RMSNorm, vector path ----------------------------------------------------
-// TEAMS teams per block (1 or 2): with 2, the teams take interleaved rows,
-// keep their own column sums, and add them through LDS into the block's one
-// partial row at the end -- twice the rows in flight per block at the same
-// number of partial rows.  Both teams pass every row-sum barrier (the block
-// barrier) the same number of times: they share the iteration count.
+// TEAMS row teams per block (1 or 2), as in the LayerNorm kernel.
 template <typename T, int VEC, int MAXG, int TEAM, int D, int TEAMS = 1>
 __global__ void __launch_bounds__(TEAM * TEAMS, kRowsBwdWavesPerSimd)
 rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
@@ -238,24 +243,8 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
     };
 
     pipeline_rows<D, RowBuf>(iters, load_row, do_row);
-    if (!want_cols) return;
-    if constexpr (TEAMS > 1) {
-        // team 1's column sums into LDS (reusing nothing: a buffer of its own),
-        // then team 0 adds them and writes the block's partial row
-        __shared__ float comb[MAXG * VEC * TEAM];
-        if (team == 1)
-#pragma unroll
-            for (int k = 0; k < MAXG; ++k)
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) comb[(k * VEC + e) * TEAM + tt] = p[0][k][e];
-        __syncthreads();
-        if (team != 0) return;
-#pragma unroll
-        for (int k = 0; k < MAXG; ++k)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) p[0][k][e] += comb[(k * VEC + e) * TEAM + tt];
-    }
-    write_partials<VEC, MAXG, 1, TEAM>(p, tt, Gr, H, G, partials);
+    if (want_cols && combine_teams<1, MAXG, VEC, TEAM, TEAMS>(p, team, tt))
+        write_partials<VEC, MAXG, 1, TEAM>(p, tt, Gr, H, G, partials);
 }
 
 // ---- column finalize: fp64 fixed-order sum of the G partial rows -------------
@@ -309,15 +298,31 @@ static hipError_t occupancy(const RowsCall &a, K kernel, int team = kTeam)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(a.occupancy_out, kernel, team, 0);
 }
 
-template <typename TX, typename TDY, typename TDX, int VEC, int MAXG, int TEAM, int D>
-static hipError_t ln_vec_d(const RowsCall &a, hipStream_t s)
+template <typename TX, typename TDY, typename TDX, int VEC, int MAXG, int TEAM, int D, int TEAMS>
+static hipError_t ln_vec_dt(const RowsCall &a, hipStream_t s)
 {
-    auto kern = ln_rows_kernel<TX, TDY, TDX, VEC, MAXG, TEAM, D>;
-    if (a.occupancy_out) return occupancy(a, kern, TEAM);
-    return launch(NH_K_LN_ROWS, kern, dim3(a.blocks), dim3(TEAM), 0u, s,
+    auto kern = ln_rows_kernel<TX, TDY, TDX, VEC, MAXG, TEAM, D, TEAMS>;
+    if (a.occupancy_out) return occupancy(a, kern, TEAM * TEAMS);
+    return launch(NH_K_LN_ROWS, kern, dim3(a.blocks), dim3(TEAM * TEAMS), 0u, s,
                   static_cast<const TDY *>(a.dy), static_cast<const TX *>(a.x), a.mean, a.rstd,
                   a.w, a.w_t, a.rows, a.cols, static_cast<TDX *>(a.dx), a.partials,
                   (int)(a.dweight != nullptr || a.dbias != nullptr));
+}
+
+// Row teams per block: 2 when a thread's row buffer is at most 32 bytes
+// (1 bf16 group of x and dy), else 1.  Measured on MI355X: 8192x1600 bf16
+// 23.3 -> 22.1 us, 16384x1024 bf16 33.7 -> 27.5 us with two teams; at 48 B
+// (8192x1600, x fp32, dy bf16) and 64 B (4096x4096 bf16) one team per block,
+// two blocks per CU, is faster (28.9 vs 29.4 us, 27.6 vs 28.8 us).
+template <typename TX, typename TDY, typename TDX, int VEC, int MAXG, int TEAM, int D>
+static hipError_t ln_vec_d(const RowsCall &a, hipStream_t s)
+{
+    constexpr int BYTES = MAXG * VEC * (int)(sizeof(TX) + sizeof(TDY));
+    if constexpr (TEAM == kTeam) {
+        const int teams = a.teams > 0 ? a.teams : (BYTES <= 32 ? 2 : 1);
+        if (teams == 2) return ln_vec_dt<TX, TDY, TDX, VEC, MAXG, TEAM, D, 2>(a, s);
+    }
+    return ln_vec_dt<TX, TDY, TDX, VEC, MAXG, TEAM, D, 1>(a, s);
 }
 
 // Pipeline depth: the kernel's default, or the rows_depth override (256-thread

@@ -420,8 +420,8 @@ nh_status nh_rows_plan(int64_t rows, int64_t cols, int *blocks);
  * flight (its software-pipeline depth; same results), key "colsum_cols" =
  * 8, 16, 32 or 64 sets the columns per block of the column finalize (same
  * results), key "rows_teams" = 1 or 2 forces the row teams per block of the
- * RMSNorm backward's vector kernel (same results up to the order of the
- * column sums).  value 0 restores the automatic plan.  Process-wide; not for concurrent use with
+ * LayerNorm and RMSNorm backwards' vector kernels (same results up to the
+ * order of the column sums).  value 0 restores the automatic plan.  Process-wide; not for concurrent use with
  * other calls.
  */
 nh_status nh_plan_override(const char *key, int64_t value);

@@ -261,3 +261,18 @@ def test_rms_two_team_blocks(nh, oracle_mod, rows, cols, dt, blocks):
         _rms_case(nh, oracle_mod, c, need=(False, True))
     finally:
         nh.plan_override("rows_teams", 0)
+
+
+@pytest.mark.parametrize("rows,cols,xt,dyt,teams", [(8192, 1600, wl.BF16, wl.BF16, 0), (1001, 1024, wl.F32, wl.BF16, 2),
+                                                    (777, 1600, wl.F32, wl.F32, 2), (3, 512, wl.BF16, wl.BF16, 2),
+                                                    (2048, 8192, wl.BF16, wl.BF16, 0), (300, 1600, wl.F32, wl.BF16, 1)])
+def test_ln_team_plans(nh, oracle_mod, rows, cols, xt, dyt, teams):
+    """LayerNorm with one or two row teams per block (automatic or forced by
+    rows_teams), one or two blocks per CU: the oracle's results either way."""
+    c = wl.rows_case(rows, cols, x_t=xt, dy_t=dyt, w_t=wl.BF16, seed=rows + 3 * cols)
+    nh.plan_override("rows_teams", teams)
+    try:
+        _ln_case(nh, oracle_mod, c, xt)
+        _ln_case(nh, oracle_mod, c, wl.F32, need=(False, True, True))
+    finally:
+        nh.plan_override("rows_teams", 0)
