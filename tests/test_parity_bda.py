@@ -87,9 +87,9 @@ def test_bda_dtype_mix(nh, oracle_mod, xt, dyt, wt):
     (1, 1600, wl.F32),        # one row
     (7, 4, wl.F32),           # one group per row
     (513, 2048, wl.BF16),     # bf16 x and dy: 8-element groups
-    (100, 8192, wl.F32),      # wider than the vector path: generic kernel
-    (77, 8196, wl.F32),       # generic kernel
-    (64, 1001, wl.F32),       # odd width: generic kernel
+    (100, 8192, wl.F32),      # wider than a 256-thread team: 512-thread team
+    (77, 8196, wl.F32),       # wider than the vector path: generic strip kernels
+    (64, 1001, wl.F32),       # odd width: generic strip kernels, scalar groups
     (2000, 64, wl.BF16),      # narrow rows, many per block
 ])
 def test_bda_shapes(nh, oracle_mod, rows, cols, xt):
@@ -108,7 +108,7 @@ def test_bda_options(nh, oracle_mod):
 
 
 def test_bda_misaligned_mask(nh, oracle_mod):
-    """A mask at an odd address takes the generic kernel; same results."""
+    """A mask at an odd address takes the generic path; same results."""
     c = wl.bda_case(64, 1600, seed=84)
     buf = torch.zeros(c.mask.size + 1, dtype=torch.uint8, device="cuda")
     buf[1:] = torch.from_numpy(c.mask.reshape(-1)).cuda()

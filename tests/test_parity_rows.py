@@ -78,7 +78,7 @@ def test_ln_dtype_mix(nh, oracle_mod, xt, dyt, wt, dxt):
     (7, 4, wl.F32),           # one group per row
     (513, 4096, wl.F32),      # 4 groups per thread, teams of 4
     (100, 8192, wl.F32),      # 8 groups per thread, teams of 2
-    (77, 8196, wl.F32),       # wider than the vector path: generic kernel
+    (77, 8196, wl.F32),       # wider than a 256-thread team: 512-thread team
     (64, 1001, wl.F32),       # width not a multiple of the group: generic
     (50, 2050, wl.BF16),      # bf16 rows, ragged groups per thread
     (33, 16384, wl.BF16),     # all-bf16 row too wide for LayerNorm's vector path
@@ -238,7 +238,7 @@ def test_rows_colsum_widths(nh, oracle_mod, cx):
                                               (9, 32768, wl.BF16, wl.BF16)])
 def test_wide_rows(nh, oracle_mod, rows, cols, xt, dyt):
     """Rows too wide for a 256-thread team: 512-thread teams up to 16384
-    columns, the generic kernel beyond (32768)."""
+    columns, the generic coefficient + strip kernels beyond (32768)."""
     c = wl.rows_case(rows, cols, x_t=xt, dy_t=dyt, w_t=wl.BF16, seed=rows + cols)
     _ln_case(nh, oracle_mod, c, wl.F32)
     r = wl.rows_case(rows, cols, x_t=xt, dy_t=xt, w_t=xt, seed=rows * 3 + cols)
