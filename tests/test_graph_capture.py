@@ -72,3 +72,53 @@ def test_graph_replays_match_eager(nh):
             assert torch.equal(_bits(outs[k]), _bits(v)), f"replay {rep}: {k} differs from eager"
         del scratch
     print("[graph] 3 replays bit-identical to eager", flush=True)
+
+
+def test_graph_generic_rows(nh):
+    """The generic row kernels under capture: misaligned rows (coefficient
+    and strip kernels), short odd rows (narrow kernels) and rows wider than
+    the vector path, forward and backward, replayed against eager bits."""
+    from helpers import place
+    wide = wl.rows_case(64, 20000, x_t=wl.BF16, dy_t=wl.BF16, w_t=wl.BF16, seed=31, with_bias=True)
+    odd = wl.rows_case(3000, 1601, x_t=wl.F32, dy_t=wl.F32, w_t=wl.F32, seed=32, with_bias=True)
+    short = wl.rows_case(5000, 7, x_t=wl.F32, dy_t=wl.F32, w_t=wl.F32, seed=33, with_bias=True)
+    sets = []
+    for c, off in ((wide, 0), (odd, 1), (short, 1)):
+        sets.append(dict(x=place(c.x, off), dy=place(c.dy, off), w=place(c.w, off), b=place(c.b, off),
+                         ws=torch.empty(nh.layernorm_backward_workspace(c.rows, c.cols), dtype=torch.uint8,
+                                        device="cuda"),
+                         wsr=torch.empty(nh.rmsnorm_backward_workspace(c.rows, c.cols), dtype=torch.uint8,
+                                         device="cuda")))
+
+    def work():
+        out = {}
+        for i, t in enumerate(sets):
+            y, mean, rstd = nh.layernorm_forward(t["x"], t["w"], t["b"], 1e-5)
+            dx, dw, db = nh.layernorm_backward(t["dy"], t["x"], mean, rstd, t["w"], dx_dtype=torch.float32,
+                                               workspace=t["ws"])
+            ry, rms = nh.rmsnorm_forward(t["x"], t["w"], 1e-5)
+            rdx, rdw = nh.rmsnorm_backward(t["dy"], t["x"], None, t["w"], 1e-5, workspace=t["wsr"])
+            out.update({f"{k}{i}": v for k, v in dict(y=y, mean=mean, rstd=rstd, dx=dx, dw=dw, db=db, ry=ry,
+                                                      rms=rms, rdx=rdx, rdw=rdw).items()})
+        return out
+
+    eager = {k: v.clone() for k, v in work().items()}
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = work()
+    for rep in range(3):
+        scratch = torch.randn(1 << 20, device="cuda") * rep
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in eager.items():
+            assert torch.equal(_bits(outs[k]), _bits(v)), f"replay {rep}: {k} differs from eager"
+        del scratch
+    print("[graph] generic row kernels: 3 replays bit-identical to eager", flush=True)
