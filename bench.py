@@ -125,7 +125,8 @@ class Timed:
 
 
 # ---- BatchNorm --------------------------------------------------------------------
-BN_KERNELS = ["bn_stats", "bn_fwd_finalize", "bn_apply", "bn_grad_sums", "bn_bwd_finalize", "bn_dx"]
+BN_KERNELS = ["bn_stats", "bn_fwd_finalize", "bn_apply", "bn_grad_sums", "bn_bwd_finalize", "bn_dx",
+              "bn_fwd_channel", "bn_bwd_channel"]
 ACT_IDS = {"none": 0, "relu": 1, "leaky_relu": 2}
 
 
@@ -133,8 +134,14 @@ def bn_bytes(case):
     """Algorithmic bytes per launch: inputs read once, outputs written once."""
     s = 4 if case.io == "f32" else 2
     E = case.N * case.C * case.hw
+    # The one-block-per-channel kernels do both passes of a direction: the
+    # reduction's reads and the elementwise pass's reads and writes.
     return {"bn_stats": E * s, "bn_apply": 2 * E * s, "bn_grad_sums": 2 * E * s, "bn_dx": 3 * E * s,
-            "bn_fwd_finalize": None, "bn_bwd_finalize": None}
+            "bn_fwd_finalize": None, "bn_bwd_finalize": None,
+            "bn_fwd_channel": 3 * E * s, "bn_bwd_channel": 5 * E * s}
+
+
+BN_STEP_KERNELS = ("bn_stats", "bn_apply", "bn_grad_sums", "bn_dx")
 
 
 def bench_bn(nh, torch, case, K, W, cold=True, act="none", slope=0.01):
@@ -202,7 +209,7 @@ def bench_bn(nh, torch, case, K, W, cold=True, act="none", slope=0.01):
             v["bytes"] = byt[k]
             v["gbs"] = byt[k] / (v["avg_us"] * 1e3)
             v["frac_of_peak"] = v["gbs"] / HBM_PEAK_GBS
-    step_bytes = sum(v for v in byt.values() if v)
+    step_bytes = sum(byt[k] for k in BN_STEP_KERNELS)  # the same on either path
     del sets, calls
     torch.cuda.empty_cache()
     # one-touch minimum: forward x + y, backward x + dy + dx
@@ -551,7 +558,7 @@ def cpu_baseline(case, budget_s=12.0):
         oracle.bn_backward(x, dy, g, eps=case.eps)
         t_total += time.perf_counter() - t0
         reps += 1
-    step_bytes = sum(v for v in bn_bytes(case).values() if v)
+    step_bytes = sum(bn_bytes(case)[k] for k in BN_STEP_KERNELS)
     model = ""
     try:
         for line in open("/proc/cpuinfo"):

@@ -94,6 +94,7 @@ std::atomic<int64_t> g_override_bn_finalize_kernels{0};
 std::atomic<int64_t> g_override_rows_depth{0};
 std::atomic<int64_t> g_override_colsum_cols{0};
 std::atomic<int64_t> g_override_rows_teams{0};
+std::atomic<int64_t> g_override_bn_channel{0};
 
 // ---- BatchNorm planning ----------------------------------------------------------
 // Resident 256-thread block slots of the device: CUs * (threads per CU / 256),
@@ -121,6 +122,29 @@ int64_t bn_ew_grid_y_for(int64_t units, int64_t C, const DeviceInfo &d)
     const int64_t ov = g_override_bn_ew_grid_y.load();
     if (ov > 0) return ov < units ? ov : units;
     return bn_grid_y_for(units, C, d);
+}
+
+// One block per channel (the fused kernels) for channels of at most
+// kBnChannelMaxUnits units, or of at most twice that when the channels alone
+// fill a quarter of the resident block slots; unless a grid or finalize
+// override asks for the split path.  The "bn_channel" override forces it off
+// (1) or on (2).  Measured on MI355X, fwd+bwd per step:
+//   (3,37,41,40) fp32, 1230 units:   15.2 -> 10.9 us
+//   (16,128,16,16) bf16, 512 units:  15.6 -> 9.7 us
+//   (64,512,7,7) fp32, 3136 units:   22.8 -> 18.1 us
+//   (64,2048,7,7) bf16, 3136 units:  52.6 -> 47.8 us
+//   (256,64,8,8) fp32, 4096 units, 64 channels: 16.2 -> 17.9 us (split kept)
+//   (64,256,28,28) bf16, 6272 units: 42.5 -> 53.5 us (split kept)
+int bn_channel_fused(int64_t units, int64_t C, int64_t slots)
+{
+    const int64_t ov = g_override_bn_channel.load();
+    if (ov == 1) return 0;
+    if (ov == 2) return 1;
+    if (g_override_bn_grid_y.load() > 0 || g_override_bn_ew_grid_y.load() > 0 ||
+        g_override_bn_finalize_kernels.load() != 0)
+        return 0;
+    if (units <= kBnChannelMaxUnits) return 1;
+    return units <= 2 * kBnChannelMaxUnits && 4 * C >= slots ? 1 : 0;
 }
 
 // Largest grid_y any dtype/alignment can take for this shape (scalar units).
@@ -383,7 +407,7 @@ const char *nh_kernel_name(int k)
     static const char *names[NH_K_COUNT] = {
         "bn_stats", "bn_fwd_finalize", "bn_apply", "bn_grad_sums", "bn_bwd_finalize", "bn_dx",
         "ln_rows", "ln_colsum", "rms_rows", "rms_colsum", "calib", "ln_fwd", "rms_fwd", "bn_infer",
-        "bda_rows", "bda_colsum", "rows_coef"};
+        "bda_rows", "bda_colsum", "rows_coef", "bn_fwd_channel", "bn_bwd_channel"};
     return (k >= 0 && k < NH_K_COUNT) ? names[k] : "";
 }
 
@@ -456,6 +480,7 @@ nh_status bn_act_forward_train(const void *x, void *y, nh_dtype io, int64_t N, i
     a.stats = stats;
     a.partials = static_cast<float *>(ws);
     a.separate_finalize = g_override_bn_finalize_kernels.load() != 0;
+    a.channel_fused = bn_channel_fused(N * (HW / a.vec), C, bn_slots(d));
     hipError_t e = bn_forward_launch(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "bn_forward_train launch");
     return ok();
@@ -505,6 +530,7 @@ nh_status bn_act_backward(const void *dy, const void *x, nh_dtype io, int64_t N,
     a.grads = grads;
     a.partials = static_cast<float *>(ws);
     a.separate_finalize = g_override_bn_finalize_kernels.load() != 0;
+    a.channel_fused = bn_channel_fused(N * (HW / a.vec), C, bn_slots(d));
     hipError_t e = bn_backward_launch(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "bn_backward launch");
     return ok();
@@ -1018,6 +1044,10 @@ nh_status nh_plan_override(const char *key, int64_t value)
         if (value != 0 && value != 8 && value != 16 && value != 32 && value != 64)
             return fail(NH_ERR_ARG, "colsum_cols must be 0, 8, 16, 32 or 64");
         g_override_colsum_cols.store(value);
+    }
+    else if (strcmp(key, "bn_channel") == 0) {
+        if (value > 2) return fail(NH_ERR_ARG, "bn_channel must be 0, 1 or 2");
+        g_override_bn_channel.store(value);
     }
     else if (strcmp(key, "rows_teams") == 0) {
         if (value > 2) return fail(NH_ERR_ARG, "rows_teams must be 0, 1 or 2");

@@ -44,6 +44,10 @@
 // place of the batch statistics (mean = running_mean, scale =
 // gamma/sqrt(running_var + eps)): one elementwise pass, no workspace.
 //
+// Small channels (few units each) take one fused kernel per direction
+// instead: a block per channel reduces, finalizes and writes the elementwise
+// pass (bn_fwd_channel_kernel, bn_bwd_channel_kernel).
+//
 // No atomics anywhere: each reduction block writes its own partial slot, the
 // finalize kernels combine slots in index order, so results are
 // bit-identical run to run and the workspace needs no zeroing.
@@ -480,6 +484,158 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
     }
 }
 
+// ---- small channels: one block per channel ------------------------------------
+// When every channel has few units, one block takes a whole channel and the
+// step needs no other block's partial sums: the block reduces (the same
+// per-thread unrolled sums and block sum as bn_stats_kernel /
+// bn_grad_sums_kernel with one block per channel), finalizes in its first
+// thread (the same fp64 arithmetic), and runs the elementwise pass over the
+// channel again, now from the caches.  One launch per direction instead of
+// two; the results equal, bit for bit, those of the two-kernel path with one
+// block per channel.  In place (y == x, dx == dy) is safe: the block reads
+// the whole channel before it writes any of it, and each thread reads an
+// element just before writing it.
+template <typename T, int V, int NT, int ACT>
+__global__ void __launch_bounds__(kBnThreads)
+bn_fwd_channel_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ stats,
+                      const float *__restrict__ beta, BnGeom g, FwdFinalizeArgs f, float slope)
+{
+    const int c = blockIdx.x;
+    const uint32_t u1 = (uint32_t)g.units;
+    const float K = to_f32(x[c * g.HW]);
+    float s1[kBnUnroll], s2[kBnUnroll];
+#pragma unroll
+    for (int k = 0; k < kBnUnroll; ++k) { s1[k] = 0.f; s2[k] = 0.f; }
+    for (uint32_t base = threadIdx.x; base < u1; base += kBnThreads * kBnUnroll) {
+        float v[kBnUnroll][V];
+#pragma unroll
+        for (int k = 0; k < kBnUnroll; ++k) {
+            const uint32_t u = base + k * kBnThreads;
+            if (u < u1) ld<(NT & kNtReduceLoads) != 0, T, V>(x + bn_unit_offset<V>(g, c, u), v[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < kBnUnroll; ++k) {
+            const uint32_t u = base + k * kBnThreads;
+            if (u < u1) {
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float d = v[k][e] - K;
+                    s1[k] += d;
+                    s2[k] = fmaf(d, d, s2[k]);
+                }
+            }
+        }
+    }
+    float a = s1[0], b = s2[0];
+#pragma unroll
+    for (int k = 1; k < kBnUnroll; ++k) { a += s1[k]; b += s2[k]; }
+    block_sum2(a, b);
+    __shared__ float sh[2];
+    if (threadIdx.x == 0)
+        fwd_finalize_channel((double)a, (double)b, K, g.C, c, f.M, f.gamma, f.running_mean, f.running_var,
+                             f.momentum, f.eps, true, stats, sh[0], sh[1]);
+    __syncthreads();
+    const float mean = sh[0], scale = sh[1];
+    const float bc = beta ? beta[c] : 0.f;
+    for (uint32_t base = threadIdx.x; base < u1; base += kBnThreads * kBnUnroll) {
+        float v[kBnUnroll][V];
+        int off[kBnUnroll];
+#pragma unroll
+        for (int k = 0; k < kBnUnroll; ++k) {
+            const uint32_t u = base + k * kBnThreads;
+            off[k] = bn_unit_offset<V>(g, c, u);
+            if (u < u1) ld<(NT & kNtEwLoads) != 0, T, V>(x + off[k], v[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < kBnUnroll; ++k) {
+            const uint32_t u = base + k * kBnThreads;
+            if (u < u1) {
+                float o[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) o[e] = act_fwd<ACT>(fmaf(v[k][e] - mean, scale, bc), slope);
+                st<(NT & kNtStores) != 0, T, V>(y + off[k], o);
+            }
+        }
+    }
+}
+
+template <typename T, int V, int NT, int ACT>
+__global__ void __launch_bounds__(kBnThreads)
+bn_bwd_channel_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ dx,
+                      const float *__restrict__ stats, float *__restrict__ grads,
+                      const float *__restrict__ beta, float slope, BnGeom g, int64_t M)
+{
+    const int c = blockIdx.x;
+    const uint32_t u1 = (uint32_t)g.units;
+    const float mean = stats[c];
+    const float scale = stats[3 * g.C + c];
+    const float bz = (ACT != 0 && beta) ? beta[c] : 0.f;
+    float s1[kBnUnroll], s2[kBnUnroll];
+#pragma unroll
+    for (int k = 0; k < kBnUnroll; ++k) { s1[k] = 0.f; s2[k] = 0.f; }
+    for (uint32_t base = threadIdx.x; base < u1; base += kBnThreads * kBnUnroll) {
+        float vx[kBnUnroll][V], vd[kBnUnroll][V];
+#pragma unroll
+        for (int k = 0; k < kBnUnroll; ++k) {
+            const uint32_t u = base + k * kBnThreads;
+            if (u < u1) {
+                const int off = bn_unit_offset<V>(g, c, u);
+                ld<(NT & kNtReduceLoads) != 0, T, V>(x + off, vx[k]);
+                ld<(NT & kNtReduceLoads) != 0, T, V>(dy + off, vd[k]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kBnUnroll; ++k) {
+            const uint32_t u = base + k * kBnThreads;
+            if (u < u1) {
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float xc = vx[k][e] - mean;
+                    const float dz = act_bwd<ACT>(vd[k][e], fmaf(xc, ACT != 0 ? scale : 0.f, bz), slope);
+                    s1[k] += dz;
+                    s2[k] = fmaf(dz, xc, s2[k]);
+                }
+            }
+        }
+    }
+    float a = s1[0], b = s2[0];
+#pragma unroll
+    for (int k = 1; k < kBnUnroll; ++k) { a += s1[k]; b += s2[k]; }
+    block_sum2(a, b);
+    __shared__ float sh[2];
+    if (threadIdx.x == 0) bwd_finalize_channel((double)a, (double)b, g.C, c, M, stats, true, grads, sh[0], sh[1]);
+    __syncthreads();
+    if (dx == nullptr) return;  // uniform: the caller skipped dx
+    const float k1 = sh[0], k2 = sh[1];
+    for (uint32_t base = threadIdx.x; base < u1; base += kBnThreads * kBnUnroll) {
+        float vx[kBnUnroll][V], vd[kBnUnroll][V];
+        int off[kBnUnroll];
+#pragma unroll
+        for (int k = 0; k < kBnUnroll; ++k) {
+            const uint32_t u = base + k * kBnThreads;
+            off[k] = bn_unit_offset<V>(g, c, u);
+            if (u < u1) {
+                ld<(NT & kNtEwLoads) != 0, T, V>(x + off[k], vx[k]);
+                ld<(NT & kNtEwLoads) != 0, T, V>(dy + off[k], vd[k]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kBnUnroll; ++k) {
+            const uint32_t u = base + k * kBnThreads;
+            if (u < u1) {
+                float o[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float xc = vx[k][e] - mean;
+                    const float dz = act_bwd<ACT>(vd[k][e], fmaf(xc, scale, bz), slope);
+                    o[e] = fmaf(dz, scale, fmaf(xc, k1, k2));
+                }
+                st<(NT & kNtStores) != 0, T, V>(dx + off[k], o);
+            }
+        }
+    }
+}
+
 // ---- host launchers -----------------------------------------------------------
 // The reductions run on a.grid_y blocks per channel, the elementwise passes on
 // a.ew_grid_y: the elementwise prologue reads the reduction's partial slots,
@@ -496,6 +652,11 @@ static hipError_t bn_forward_t(const BnCall &a, hipStream_t s)
     if (a.inference)
         return launch(NH_K_BN_INFER, bn_apply_kernel<T, V, kApplyRunning, kBnNtPolicy, ACT>, egrid, block,
                       0, s, x, static_cast<T *>(a.out), a.stats, a.beta, ge, f, a.slope);
+    if (a.channel_fused) {
+        const BnGeom g1 = make_bn_geom(a.N, a.C, a.HW, a.vec, 1);
+        return launch(NH_K_BN_FWD_CHANNEL, bn_fwd_channel_kernel<T, V, kBnNtPolicy, ACT>, dim3((unsigned)a.C),
+                      block, 0, s, x, static_cast<T *>(a.out), a.stats, a.beta, g1, f, a.slope);
+    }
     hipError_t e = launch(NH_K_BN_STATS, bn_stats_kernel<T, V, kBnNtPolicy>, rgrid, block, 0, s, x, gr,
                           a.partials);
     if (e != hipSuccess) return e;
@@ -520,10 +681,15 @@ static hipError_t bn_backward_t(const BnCall &a, hipStream_t s)
     const T *x = static_cast<const T *>(a.x);
     const T *dy = static_cast<const T *>(a.dy);
     const dim3 rgrid((unsigned)(a.C * a.grid_y)), egrid((unsigned)(a.C * a.ew_grid_y)), block(kBnThreads);
+    const int64_t M = (int64_t)a.N * a.HW;
+    if (a.channel_fused) {
+        const BnGeom g1 = make_bn_geom(a.N, a.C, a.HW, a.vec, 1);
+        return launch(NH_K_BN_BWD_CHANNEL, bn_bwd_channel_kernel<T, V, kBnNtPolicy, ACT>, dim3((unsigned)a.C),
+                      block, 0, s, dy, x, static_cast<T *>(a.out), a.stats, a.grads, a.beta, a.slope, g1, M);
+    }
     hipError_t e = launch(NH_K_BN_GRAD_SUMS, bn_grad_sums_kernel<T, V, kBnNtPolicy, ACT>, rgrid, block, 0,
                           s, dy, x, a.stats, a.beta, a.slope, gr, a.partials);
     if (e != hipSuccess) return e;
-    const int64_t M = (int64_t)a.N * a.HW;
     if (a.separate_finalize || a.out == nullptr) {
         const dim3 fgrid((unsigned)ceil_div(a.C, kBnThreads / kWave));
         e = launch(NH_K_BN_BWD_FINALIZE, bn_bwd_finalize, fgrid, block, 0, s, a.partials, a.grid_y,

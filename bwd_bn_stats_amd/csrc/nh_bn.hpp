@@ -21,6 +21,15 @@ constexpr int kBnUnroll = 4;     // vector units in flight per thread
 // example 64 reduction blocks per channel, 32 elementwise) makes apply and dx
 // 25-40% slower, although no L2 line survives from one kernel to the next.
 constexpr int64_t kBnMinUnits = (int64_t)kBnThreads * kBnUnroll;
+
+// Channels of at most kBnChannelMaxUnits units (twice that with enough
+// channels to fill the device) take the one-block-per-channel fused kernels:
+// a block covers the channel in a few unrolled sweeps per pass, so the
+// launches it saves outweigh the lost split, and each fp32 per-thread sum
+// takes at most four units (the split path's fp64 combine of block sums keeps
+// large channels accurate; one block over a channel of a few hundred
+// thousand elements would not).
+constexpr int64_t kBnChannelMaxUnits = 2 * kBnMinUnits;
 inline int64_t bn_auto_grid_y(int64_t units, int64_t C, int64_t slots)
 {
     int64_t per_channel = slots / (C > 0 ? C : 1);
@@ -75,6 +84,7 @@ struct BnCall {
     int ew_grid_y;       // blocks per channel of the elementwise passes (apply, dx)
     int separate_finalize;  // 1: finalize as its own kernel; 0: in the elementwise prologue
     int inference;       // forward only: apply with the running statistics, no reduction
+    int channel_fused;   // 1: one block per channel, reduction + finalize + elementwise in one kernel
     int act;             // 0 none, 1 ReLU, 2 LeakyReLU
     float slope;         // LeakyReLU negative slope
     const void *x;

@@ -23,7 +23,7 @@ _DT = {torch.float32: F32, torch.bfloat16: BF16}
 
 KERNELS = ["bn_stats", "bn_fwd_finalize", "bn_apply", "bn_grad_sums", "bn_bwd_finalize", "bn_dx",
            "ln_rows", "ln_colsum", "rms_rows", "rms_colsum", "calib", "ln_fwd", "rms_fwd", "bn_infer",
-           "bda_rows", "bda_colsum", "rows_coef"]
+           "bda_rows", "bda_colsum", "rows_coef", "bn_fwd_channel", "bn_bwd_channel"]
 
 ACTS = {"none": 0, "relu": 1, "leaky_relu": 2}
 

@@ -354,7 +354,9 @@ typedef enum {
     NH_K_BDA_ROWS = 14,       /* bias+dropout+add+LayerNorm backward row pass */
     NH_K_BDA_COLSUM = 15,     /* its dweight/dbias/dbias_in finalize */
     NH_K_ROWS_COEF = 16,      /* per-row gradient coefficients (wide or misaligned rows) */
-    NH_K_COUNT = 17
+    NH_K_BN_FWD_CHANNEL = 17, /* BatchNorm forward, one block per small channel */
+    NH_K_BN_BWD_CHANNEL = 18, /* BatchNorm backward, one block per small channel */
+    NH_K_COUNT = 19
 } nh_kernel;
 
 /* Static name of a kernel id; "" for an unknown id. */
@@ -419,7 +421,9 @@ nh_status nh_rows_plan(int64_t rows, int64_t cols, int *blocks);
  * "rows_depth" = 1..4 forces the number of rows a row-kernel team keeps in
  * flight (its software-pipeline depth; same results), key "colsum_cols" =
  * 8, 16, 32 or 64 sets the columns per block of the column finalize (same
- * results), key "rows_teams" = 1 or 2 forces the row teams per block of the
+ * results), key "bn_channel" = 1 or 2 turns the one-block-per-channel
+ * fused BatchNorm kernels (used automatically for small channels) off or
+ * on, key "rows_teams" = 1 or 2 forces the row teams per block of the
  * LayerNorm and RMSNorm backwards' vector kernels (same results up to the
  * order of the column sums).  value 0 restores the automatic plan.  Process-wide; not for concurrent use with
  * other calls.

@@ -43,8 +43,8 @@ def test_status_and_kernel_names():
         "NH_OK", "NH_ERR_NULL", "NH_ERR_SHAPE", "NH_ERR_DTYPE", "NH_ERR_WORKSPACE",
         "NH_ERR_HIP", "NH_ERR_ARG"]
     assert nh.status_string(99) == "NH_ERR_UNKNOWN"
-    assert [nh.lib.nh_kernel_name(i).decode() for i in range(17)] == nh.KERNELS
-    assert nh.lib.nh_kernel_name(17).decode() == ""
+    assert [nh.lib.nh_kernel_name(i).decode() for i in range(19)] == nh.KERNELS
+    assert nh.lib.nh_kernel_name(19).decode() == ""
 
 
 def bn_fwd(x=FAKE, y=FAKE, io=0, N=2, C=3, HW=4, rm=NULL, rv=NULL, eps=1e-5, mom=0.1,
@@ -200,6 +200,8 @@ def test_measurement_validation():
     assert nh.lib.nh_plan_override(b"colsum_cols", 0) == NH_OK
     assert nh.lib.nh_plan_override(b"rows_teams", 3) == NH_ERR_ARG
     assert nh.lib.nh_plan_override(b"rows_teams", 0) == NH_OK
+    assert nh.lib.nh_plan_override(b"bn_channel", 3) == NH_ERR_ARG
+    assert nh.lib.nh_plan_override(b"bn_channel", 0) == NH_OK
     assert nh.lib.nh_calib_add(FAKE, FAKE, FAKE, -1, NULL) == NH_ERR_SHAPE
     assert nh.lib.nh_calib_add(NULL, NULL, NULL, 0, NULL) == NH_OK
     assert nh.lib.nh_calib_copy(NULL, FAKE, 16, NULL) == NH_ERR_NULL

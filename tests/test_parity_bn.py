@@ -284,15 +284,18 @@ def test_bn_bit_identical_runs(nh, name):
                                   "one_channel_64x1x128x128_f32"])
 def test_bn_separate_finalize_kernels_match_fused(nh, oracle_mod, name):
     """The finalize step as its own kernels (the three-launch structure) gives
-    the same bits as the finalize folded into the elementwise kernels."""
+    the same bits as the finalize folded into the elementwise kernels (both on
+    the split path: the one-block-per-channel kernels are off)."""
     c = CASES[name]()
     print(f"[bn parity] separate finalize kernels {name}", flush=True)
-    fused = _gpu_bn(nh, c)
-    nh.plan_override("bn_finalize_kernels", 1)
+    nh.plan_override("bn_channel", 1)
     try:
+        fused = _gpu_bn(nh, c)
+        nh.plan_override("bn_finalize_kernels", 1)
         separate = _gpu_bn(nh, c)
     finally:
         nh.plan_override("bn_finalize_kernels", 0)
+        nh.plan_override("bn_channel", 0)
     _compare(c, separate, _oracle_bn(oracle_mod, c))
     for k in fused:
         assert np.array_equal(fused[k].view(np.uint64), separate[k].view(np.uint64)), k

@@ -153,17 +153,21 @@ def test_bn_act_mask_matches_forward(nh, io, act, slope):
 
 
 def test_bn_act_separate_finalize_bit_identical(nh):
+    """Finalize folded into the elementwise kernels vs its own kernels, both on
+    the split path (the one-block-per-channel kernels off): same bits."""
     c = wl.bn_case(16, 12, 20, 20, wl.F32, seed=146, beta_std=1.0)
     x, dy, g, b = dev(c.x), dev(c.dy), dev(c.gamma), dev(c.beta)
     outs = []
     for sep in (0, 1):
         nh.plan_override("bn_finalize_kernels", sep)
+        nh.plan_override("bn_channel", 1)
         try:
             y, stats = nh.bn_forward_train(x, g, b, None, None, c.momentum, c.eps, act="leaky_relu",
                                            slope=0.1)
             dx, grads = nh.bn_backward(dy, x, stats, beta=b, act="leaky_relu", slope=0.1)
         finally:
             nh.plan_override("bn_finalize_kernels", 0)
+            nh.plan_override("bn_channel", 0)
         outs.append((y, stats, dx, grads))
     torch.cuda.synchronize()
     for u, v in zip(*outs):

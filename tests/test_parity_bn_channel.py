@@ -1,0 +1,135 @@
+"""The one-block-per-channel BatchNorm kernels (bn_fwd_channel_kernel,
+bn_bwd_channel_kernel): taken automatically for channels of few units, they
+must match the oracle and give the same bits as the split two-kernel path
+run with one block per channel, which does the same sums in the same order."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from bwd_bn_stats_amd import workloads as wl
+
+from helpers import check, clear_of_kink, dev, host, place
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def nh():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from bwd_bn_stats_amd import normhip
+    return normhip
+
+
+def _run(nh, c, act, slope, offset=0, in_place=False, need_dx=True):
+    x, dy = place(c.x, offset), place(c.dy, offset)
+    g, b = dev(c.gamma), dev(c.beta)
+    rm, rv = dev(c.running_mean), dev(c.running_var)
+    nh.timing_enable(True)
+    try:
+        if in_place:
+            xi = x.clone()
+            y, stats = nh.bn_forward_train(xi, g, b, rm, rv, c.momentum, c.eps, act=act, slope=slope, y=xi)
+            dyi = dy.clone()
+            dx, grads = nh.bn_backward(dyi, x, stats, beta=b, act=act, slope=slope, dx=dyi)
+        else:
+            y, stats = nh.bn_forward_train(x, g, b, rm, rv, c.momentum, c.eps, act=act, slope=slope)
+            dx, grads = nh.bn_backward(dy, x, stats, beta=b, act=act, slope=slope, need_dx=need_dx)
+        torch.cuda.synchronize()
+        launches = {k: nh.timing_read(k)[1] for k in ("bn_fwd_channel", "bn_bwd_channel", "bn_stats")}
+    finally:
+        nh.timing_enable(False)
+    out = dict(y=host(y), stats=host(stats), grads=host(grads), rm=host(rm), rv=host(rv))
+    if need_dx:
+        out["dx"] = host(dx)
+    return out, launches
+
+
+def _bits(a):
+    return np.asarray(a, np.float64).view(np.uint64)
+
+
+SHAPES = [((3, 37, 41, 40), wl.F32, "none"),        # the ragged config
+          ((8, 64, 7, 7), wl.BF16, "relu"),
+          ((2, 5, 7, 3), wl.F32, "leaky_relu"),      # odd planes: scalar units
+          ((32, 512, 7, 7), wl.F32, "none"),         # many small channels
+          ((64, 512, 7, 7), wl.BF16, "relu"),        # 3136 units: fused because 512 channels fill the device
+          ((1, 3, 2, 3), wl.F32, "relu"),            # six elements per channel
+          ((16, 24, 16, 16), wl.BF16, "leaky_relu")]
+
+
+@pytest.mark.parametrize("shape,io,act", SHAPES, ids=lambda v: str(v))
+def test_channel_kernels_match_split_path(nh, oracle_mod, shape, io, act):
+    N, C, H, W = shape
+    c = wl.bn_case(N, C, H, W, io, seed=N * C + H * W, x_mean=2.0, x_std=0.8, beta_std=0.5)
+    print(f"[bn channel] {shape} {io} act={act}", flush=True)
+    fused, l1 = _run(nh, c, act, 0.1)
+    assert l1["bn_fwd_channel"] == 1 and l1["bn_bwd_channel"] == 1 and l1["bn_stats"] == 0, l1
+    nh.plan_override("bn_channel", 1)
+    nh.plan_override("bn_grid_y", 1)
+    try:
+        split, l2 = _run(nh, c, act, 0.1)
+    finally:
+        nh.plan_override("bn_grid_y", 0)
+        nh.plan_override("bn_channel", 0)
+    assert l2["bn_fwd_channel"] == 0 and l2["bn_stats"] == 1, l2
+    for k in fused:
+        assert np.array_equal(_bits(fused[k]), _bits(split[k])), f"{k} differs from the split path"
+    # and the oracle, on inputs moved clear of the activation's kink
+    if act != "none":
+        c = dataclasses.replace(c, x=clear_of_kink(oracle_mod, c.x, c.gamma, c.beta, c.eps,
+                                                   1e-3 if io == wl.F32 else 1e-2))
+    got, _ = _run(nh, c, act, 0.1)
+    wy, wstats, wrm, wrv = oracle_mod.bn_act_forward_train(
+        c.x.value, c.gamma, c.beta, act, 0.1, eps=c.eps, momentum=c.momentum,
+        running_mean=c.running_mean, running_var=c.running_var)
+    wdx, wgrads = oracle_mod.bn_act_backward(c.x.value, c.dy.value, c.gamma, c.beta, act, 0.1, eps=c.eps)
+    check("y", got["y"], wy, io)
+    check("dx", got["dx"], wdx, io)
+    for k in range(4):
+        check(f"stats[{k}]", got["stats"][k], wstats[k], wl.F32)
+        check(f"grads[{k}]", got["grads"][k], wgrads[k], wl.F32)
+    check("running_mean", got["rm"], wrm, wl.F32)
+    check("running_var", got["rv"], wrv, wl.F32)
+
+
+def test_channel_kernels_in_place_misaligned_and_grads_only(nh):
+    c = wl.bn_case(4, 37, 9, 13, wl.F32, seed=77, x_mean=3.0)
+    ref, _ = _run(nh, c, "relu", 0.0)
+    inp, l1 = _run(nh, c, "relu", 0.0, in_place=True)
+    assert l1["bn_fwd_channel"] == 1
+    mis, _ = _run(nh, c, "relu", 0.0, offset=1)
+    go, _ = _run(nh, c, "relu", 0.0, need_dx=False)
+    for k in ref:
+        assert np.array_equal(_bits(ref[k]), _bits(inp[k])), f"in place: {k}"
+    for k in ("stats", "grads", "rm", "rv"):
+        assert np.array_equal(_bits(ref[k]), _bits(go[k])), f"grads only: {k}"
+    # misaligned tensors take scalar units: same sums in another order
+    for k in ref:
+        check(f"misaligned {k}", mis[k], ref[k], wl.F32)
+
+
+def test_channel_kernels_forced_on_larger_channels(nh, oracle_mod):
+    """Forced on for channels of 32768 elements (8 sweeps per block, beyond
+    the automatic limit): still the oracle's results.  (Much larger channels
+    put hundreds of values into each fp32 partial sum of one block and lose
+    the accuracy that the split path's fp64 combine keeps.)"""
+    c = wl.bn_case(32, 8, 32, 32, wl.F32, seed=91, x_mean=1.0)
+    nh.plan_override("bn_channel", 2)
+    try:
+        got, l1 = _run(nh, c, "none", 0.0)
+    finally:
+        nh.plan_override("bn_channel", 0)
+    assert l1["bn_fwd_channel"] == 1
+    y, stats, rm, rv = oracle_mod.bn_forward_train(c.x.value, c.gamma, c.beta, eps=c.eps,
+                                                   momentum=c.momentum, running_mean=c.running_mean,
+                                                   running_var=c.running_var)
+    dx, grads = oracle_mod.bn_backward(c.x.value, c.dy.value, c.gamma, eps=c.eps)
+    check("y", got["y"], y, wl.F32)
+    check("dx", got["dx"], dx, wl.F32)
+    for k in range(4):
+        check(f"stats[{k}]", got["stats"][k], stats[k], wl.F32)
+        check(f"grads[{k}]", got["grads"][k], grads[k], wl.F32)
