@@ -95,6 +95,7 @@ std::atomic<int64_t> g_override_rows_depth{0};
 std::atomic<int64_t> g_override_colsum_cols{0};
 std::atomic<int64_t> g_override_rows_teams{0};
 std::atomic<int64_t> g_override_bn_channel{0};
+std::atomic<int64_t> g_override_bn_channel_threads{0};
 
 // ---- BatchNorm planning ----------------------------------------------------------
 // Resident 256-thread block slots of the device: CUs * (threads per CU / 256),
@@ -145,6 +146,23 @@ int bn_channel_fused(int64_t units, int64_t C, int64_t slots)
         return 0;
     if (units <= kBnChannelMaxUnits) return 1;
     return units <= 2 * kBnChannelMaxUnits && 4 * C >= slots ? 1 : 0;
+}
+
+// Threads per block of the fused kernels: kBnChannelBigBlock (one sweep of
+// a 4096-unit channel) when every such block stays resident and a 256-thread
+// block would sweep more than once -- channels at most an eighth of the
+// 256-thread slots with more than kBnMinUnits units, or at most a quarter
+// with more than 2*kBnMinUnits -- else kBnThreads.  Measured on MI355X
+// (fwd+bwd per step, 256 -> 1024 threads): (3,37,41,40) fp32 10.6 -> 9.7 us,
+// (8,64,32,32) fp32 11.8 -> 10.7 us, (64,512,7,7) fp32 18.0 -> 15.5 us;
+// (32,512,7,7) fp32 12.5 -> 13.1 us and (64,2048,7,7) bf16 48 -> 56 us keep
+// 256.  The "bn_channel_threads" override forces either.
+int bn_channel_threads(int64_t units, int64_t C, int64_t slots)
+{
+    const int64_t ov = g_override_bn_channel_threads.load();
+    if (ov == kBnThreads || ov == kBnChannelBigBlock) return (int)ov;
+    const bool big = (8 * C <= slots && units > kBnMinUnits) || (4 * C <= slots && units > 2 * kBnMinUnits);
+    return big ? kBnChannelBigBlock : kBnThreads;
 }
 
 // Largest grid_y any dtype/alignment can take for this shape (scalar units).
@@ -481,6 +499,7 @@ nh_status bn_act_forward_train(const void *x, void *y, nh_dtype io, int64_t N, i
     a.partials = static_cast<float *>(ws);
     a.separate_finalize = g_override_bn_finalize_kernels.load() != 0;
     a.channel_fused = bn_channel_fused(N * (HW / a.vec), C, bn_slots(d));
+    a.channel_threads = bn_channel_threads(N * (HW / a.vec), C, bn_slots(d));
     hipError_t e = bn_forward_launch(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "bn_forward_train launch");
     return ok();
@@ -531,6 +550,7 @@ nh_status bn_act_backward(const void *dy, const void *x, nh_dtype io, int64_t N,
     a.partials = static_cast<float *>(ws);
     a.separate_finalize = g_override_bn_finalize_kernels.load() != 0;
     a.channel_fused = bn_channel_fused(N * (HW / a.vec), C, bn_slots(d));
+    a.channel_threads = bn_channel_threads(N * (HW / a.vec), C, bn_slots(d));
     hipError_t e = bn_backward_launch(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "bn_backward launch");
     return ok();
@@ -1048,6 +1068,11 @@ nh_status nh_plan_override(const char *key, int64_t value)
     else if (strcmp(key, "bn_channel") == 0) {
         if (value > 2) return fail(NH_ERR_ARG, "bn_channel must be 0, 1 or 2");
         g_override_bn_channel.store(value);
+    }
+    else if (strcmp(key, "bn_channel_threads") == 0) {
+        if (value != 0 && value != kBnThreads && value != kBnChannelBigBlock)
+            return fail(NH_ERR_ARG, "bn_channel_threads must be 0, %d or %d", kBnThreads, kBnChannelBigBlock);
+        g_override_bn_channel_threads.store(value);
     }
     else if (strcmp(key, "rows_teams") == 0) {
         if (value > 2) return fail(NH_ERR_ARG, "rows_teams must be 0, 1 or 2");

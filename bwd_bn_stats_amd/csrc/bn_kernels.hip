@@ -109,6 +109,36 @@ __device__ __forceinline__ void block_sum2(float &a, float &b)
     }
 }
 
+// Sums of (a, b) over a TB-thread block, in the order of block_sum2 (wave
+// sums, then the waves in index order); the result is valid in thread 0.
+template <int TB>
+__device__ __forceinline__ void block_sum2_tb(float &a, float &b)
+{
+    if constexpr (TB == kBnThreads) {
+        block_sum2(a, b);
+    } else {
+        __shared__ float red[TB / kWave][2];
+        a = wave_sum(a);
+        b = wave_sum(b);
+        const int wave = threadIdx.x / kWave;
+        if ((threadIdx.x & (kWave - 1)) == 0) {
+            red[wave][0] = a;
+            red[wave][1] = b;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float sa = red[0][0], sb = red[0][1];
+#pragma unroll
+            for (int w = 1; w < TB / kWave; ++w) {
+                sa += red[w][0];
+                sb += red[w][1];
+            }
+            a = sa;
+            b = sb;
+        }
+    }
+}
+
 // ---- forward reduction: shifted one-pass sums ------------------------------
 template <typename T, int V, int NT>
 __global__ void __launch_bounds__(kBnThreads)
@@ -495,8 +525,8 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
 // block per channel.  In place (y == x, dx == dy) is safe: the block reads
 // the whole channel before it writes any of it, and each thread reads an
 // element just before writing it.
-template <typename T, int V, int NT, int ACT>
-__global__ void __launch_bounds__(kBnThreads)
+template <typename T, int V, int NT, int ACT, int TB>
+__global__ void __launch_bounds__(TB)
 bn_fwd_channel_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ stats,
                       const float *__restrict__ beta, BnGeom g, FwdFinalizeArgs f, float slope)
 {
@@ -506,16 +536,16 @@ bn_fwd_channel_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restr
     float s1[kBnUnroll], s2[kBnUnroll];
 #pragma unroll
     for (int k = 0; k < kBnUnroll; ++k) { s1[k] = 0.f; s2[k] = 0.f; }
-    for (uint32_t base = threadIdx.x; base < u1; base += kBnThreads * kBnUnroll) {
+    for (uint32_t base = threadIdx.x; base < u1; base += TB * kBnUnroll) {
         float v[kBnUnroll][V];
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
-            const uint32_t u = base + k * kBnThreads;
+            const uint32_t u = base + k * TB;
             if (u < u1) ld<(NT & kNtReduceLoads) != 0, T, V>(x + bn_unit_offset<V>(g, c, u), v[k]);
         }
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
-            const uint32_t u = base + k * kBnThreads;
+            const uint32_t u = base + k * TB;
             if (u < u1) {
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
@@ -529,7 +559,7 @@ bn_fwd_channel_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restr
     float a = s1[0], b = s2[0];
 #pragma unroll
     for (int k = 1; k < kBnUnroll; ++k) { a += s1[k]; b += s2[k]; }
-    block_sum2(a, b);
+    block_sum2_tb<TB>(a, b);
     __shared__ float sh[2];
     if (threadIdx.x == 0)
         fwd_finalize_channel((double)a, (double)b, K, g.C, c, f.M, f.gamma, f.running_mean, f.running_var,
@@ -537,18 +567,18 @@ bn_fwd_channel_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restr
     __syncthreads();
     const float mean = sh[0], scale = sh[1];
     const float bc = beta ? beta[c] : 0.f;
-    for (uint32_t base = threadIdx.x; base < u1; base += kBnThreads * kBnUnroll) {
+    for (uint32_t base = threadIdx.x; base < u1; base += TB * kBnUnroll) {
         float v[kBnUnroll][V];
         int off[kBnUnroll];
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
-            const uint32_t u = base + k * kBnThreads;
+            const uint32_t u = base + k * TB;
             off[k] = bn_unit_offset<V>(g, c, u);
             if (u < u1) ld<(NT & kNtEwLoads) != 0, T, V>(x + off[k], v[k]);
         }
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
-            const uint32_t u = base + k * kBnThreads;
+            const uint32_t u = base + k * TB;
             if (u < u1) {
                 float o[V];
 #pragma unroll
@@ -559,8 +589,8 @@ bn_fwd_channel_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restr
     }
 }
 
-template <typename T, int V, int NT, int ACT>
-__global__ void __launch_bounds__(kBnThreads)
+template <typename T, int V, int NT, int ACT, int TB>
+__global__ void __launch_bounds__(TB)
 bn_bwd_channel_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ dx,
                       const float *__restrict__ stats, float *__restrict__ grads,
                       const float *__restrict__ beta, float slope, BnGeom g, int64_t M)
@@ -573,11 +603,11 @@ bn_bwd_channel_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__re
     float s1[kBnUnroll], s2[kBnUnroll];
 #pragma unroll
     for (int k = 0; k < kBnUnroll; ++k) { s1[k] = 0.f; s2[k] = 0.f; }
-    for (uint32_t base = threadIdx.x; base < u1; base += kBnThreads * kBnUnroll) {
+    for (uint32_t base = threadIdx.x; base < u1; base += TB * kBnUnroll) {
         float vx[kBnUnroll][V], vd[kBnUnroll][V];
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
-            const uint32_t u = base + k * kBnThreads;
+            const uint32_t u = base + k * TB;
             if (u < u1) {
                 const int off = bn_unit_offset<V>(g, c, u);
                 ld<(NT & kNtReduceLoads) != 0, T, V>(x + off, vx[k]);
@@ -586,7 +616,7 @@ bn_bwd_channel_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__re
         }
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
-            const uint32_t u = base + k * kBnThreads;
+            const uint32_t u = base + k * TB;
             if (u < u1) {
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
@@ -601,18 +631,18 @@ bn_bwd_channel_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__re
     float a = s1[0], b = s2[0];
 #pragma unroll
     for (int k = 1; k < kBnUnroll; ++k) { a += s1[k]; b += s2[k]; }
-    block_sum2(a, b);
+    block_sum2_tb<TB>(a, b);
     __shared__ float sh[2];
     if (threadIdx.x == 0) bwd_finalize_channel((double)a, (double)b, g.C, c, M, stats, true, grads, sh[0], sh[1]);
     __syncthreads();
     if (dx == nullptr) return;  // uniform: the caller skipped dx
     const float k1 = sh[0], k2 = sh[1];
-    for (uint32_t base = threadIdx.x; base < u1; base += kBnThreads * kBnUnroll) {
+    for (uint32_t base = threadIdx.x; base < u1; base += TB * kBnUnroll) {
         float vx[kBnUnroll][V], vd[kBnUnroll][V];
         int off[kBnUnroll];
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
-            const uint32_t u = base + k * kBnThreads;
+            const uint32_t u = base + k * TB;
             off[k] = bn_unit_offset<V>(g, c, u);
             if (u < u1) {
                 ld<(NT & kNtEwLoads) != 0, T, V>(x + off[k], vx[k]);
@@ -621,7 +651,7 @@ bn_bwd_channel_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__re
         }
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
-            const uint32_t u = base + k * kBnThreads;
+            const uint32_t u = base + k * TB;
             if (u < u1) {
                 float o[V];
 #pragma unroll
@@ -654,8 +684,13 @@ static hipError_t bn_forward_t(const BnCall &a, hipStream_t s)
                       0, s, x, static_cast<T *>(a.out), a.stats, a.beta, ge, f, a.slope);
     if (a.channel_fused) {
         const BnGeom g1 = make_bn_geom(a.N, a.C, a.HW, a.vec, 1);
-        return launch(NH_K_BN_FWD_CHANNEL, bn_fwd_channel_kernel<T, V, kBnNtPolicy, ACT>, dim3((unsigned)a.C),
-                      block, 0, s, x, static_cast<T *>(a.out), a.stats, a.beta, g1, f, a.slope);
+        if (a.channel_threads == kBnChannelBigBlock)
+            return launch(NH_K_BN_FWD_CHANNEL, bn_fwd_channel_kernel<T, V, kBnNtPolicy, ACT, kBnChannelBigBlock>,
+                          dim3((unsigned)a.C), dim3(kBnChannelBigBlock), 0, s, x, static_cast<T *>(a.out),
+                          a.stats, a.beta, g1, f, a.slope);
+        return launch(NH_K_BN_FWD_CHANNEL, bn_fwd_channel_kernel<T, V, kBnNtPolicy, ACT, kBnThreads>,
+                      dim3((unsigned)a.C), block, 0, s, x, static_cast<T *>(a.out), a.stats, a.beta, g1, f,
+                      a.slope);
     }
     hipError_t e = launch(NH_K_BN_STATS, bn_stats_kernel<T, V, kBnNtPolicy>, rgrid, block, 0, s, x, gr,
                           a.partials);
@@ -684,8 +719,13 @@ static hipError_t bn_backward_t(const BnCall &a, hipStream_t s)
     const int64_t M = (int64_t)a.N * a.HW;
     if (a.channel_fused) {
         const BnGeom g1 = make_bn_geom(a.N, a.C, a.HW, a.vec, 1);
-        return launch(NH_K_BN_BWD_CHANNEL, bn_bwd_channel_kernel<T, V, kBnNtPolicy, ACT>, dim3((unsigned)a.C),
-                      block, 0, s, dy, x, static_cast<T *>(a.out), a.stats, a.grads, a.beta, a.slope, g1, M);
+        if (a.channel_threads == kBnChannelBigBlock)
+            return launch(NH_K_BN_BWD_CHANNEL, bn_bwd_channel_kernel<T, V, kBnNtPolicy, ACT, kBnChannelBigBlock>,
+                          dim3((unsigned)a.C), dim3(kBnChannelBigBlock), 0, s, dy, x, static_cast<T *>(a.out),
+                          a.stats, a.grads, a.beta, a.slope, g1, M);
+        return launch(NH_K_BN_BWD_CHANNEL, bn_bwd_channel_kernel<T, V, kBnNtPolicy, ACT, kBnThreads>,
+                      dim3((unsigned)a.C), block, 0, s, dy, x, static_cast<T *>(a.out), a.stats, a.grads, a.beta,
+                      a.slope, g1, M);
     }
     hipError_t e = launch(NH_K_BN_GRAD_SUMS, bn_grad_sums_kernel<T, V, kBnNtPolicy, ACT>, rgrid, block, 0,
                           s, dy, x, a.stats, a.beta, a.slope, gr, a.partials);

@@ -30,6 +30,7 @@ constexpr int64_t kBnMinUnits = (int64_t)kBnThreads * kBnUnroll;
 // large channels accurate; one block over a channel of a few hundred
 // thousand elements would not).
 constexpr int64_t kBnChannelMaxUnits = 2 * kBnMinUnits;
+constexpr int kBnChannelBigBlock = 1024;  // threads of the larger fused-kernel block
 inline int64_t bn_auto_grid_y(int64_t units, int64_t C, int64_t slots)
 {
     int64_t per_channel = slots / (C > 0 ? C : 1);
@@ -85,6 +86,7 @@ struct BnCall {
     int separate_finalize;  // 1: finalize as its own kernel; 0: in the elementwise prologue
     int inference;       // forward only: apply with the running statistics, no reduction
     int channel_fused;   // 1: one block per channel, reduction + finalize + elementwise in one kernel
+    int channel_threads; // threads of that block: kBnThreads or kBnChannelBigBlock
     int act;             // 0 none, 1 ReLU, 2 LeakyReLU
     float slope;         // LeakyReLU negative slope
     const void *x;

@@ -63,10 +63,17 @@ SHAPES = [((3, 37, 41, 40), wl.F32, "none"),        # the ragged config
 
 @pytest.mark.parametrize("shape,io,act", SHAPES, ids=lambda v: str(v))
 def test_channel_kernels_match_split_path(nh, oracle_mod, shape, io, act):
+    """256-thread fused blocks do the split path's sums in its order: same
+    bits as the split path with one block per channel.  Both block sizes (and
+    the automatic choice) match the oracle."""
     N, C, H, W = shape
     c = wl.bn_case(N, C, H, W, io, seed=N * C + H * W, x_mean=2.0, x_std=0.8, beta_std=0.5)
     print(f"[bn channel] {shape} {io} act={act}", flush=True)
-    fused, l1 = _run(nh, c, act, 0.1)
+    nh.plan_override("bn_channel_threads", 256)
+    try:
+        fused, l1 = _run(nh, c, act, 0.1)
+    finally:
+        nh.plan_override("bn_channel_threads", 0)
     assert l1["bn_fwd_channel"] == 1 and l1["bn_bwd_channel"] == 1 and l1["bn_stats"] == 0, l1
     nh.plan_override("bn_channel", 1)
     nh.plan_override("bn_grid_y", 1)
@@ -82,21 +89,36 @@ def test_channel_kernels_match_split_path(nh, oracle_mod, shape, io, act):
     if act != "none":
         c = dataclasses.replace(c, x=clear_of_kink(oracle_mod, c.x, c.gamma, c.beta, c.eps,
                                                    1e-3 if io == wl.F32 else 1e-2))
-    got, _ = _run(nh, c, act, 0.1)
     wy, wstats, wrm, wrv = oracle_mod.bn_act_forward_train(
         c.x.value, c.gamma, c.beta, act, 0.1, eps=c.eps, momentum=c.momentum,
         running_mean=c.running_mean, running_var=c.running_var)
     wdx, wgrads = oracle_mod.bn_act_backward(c.x.value, c.dy.value, c.gamma, c.beta, act, 0.1, eps=c.eps)
-    check("y", got["y"], wy, io)
-    check("dx", got["dx"], wdx, io)
-    for k in range(4):
-        check(f"stats[{k}]", got["stats"][k], wstats[k], wl.F32)
-        check(f"grads[{k}]", got["grads"][k], wgrads[k], wl.F32)
-    check("running_mean", got["rm"], wrm, wl.F32)
-    check("running_var", got["rv"], wrv, wl.F32)
+    for threads in (0, 256, 1024):
+        nh.plan_override("bn_channel_threads", threads)
+        try:
+            got, _ = _run(nh, c, act, 0.1)
+        finally:
+            nh.plan_override("bn_channel_threads", 0)
+        print(f"  threads={threads or 'auto'}", flush=True)
+        check("y", got["y"], wy, io)
+        check("dx", got["dx"], wdx, io)
+        for k in range(4):
+            check(f"stats[{k}]", got["stats"][k], wstats[k], wl.F32)
+            check(f"grads[{k}]", got["grads"][k], wgrads[k], wl.F32)
+        check("running_mean", got["rm"], wrm, wl.F32)
+        check("running_var", got["rv"], wrv, wl.F32)
 
 
-def test_channel_kernels_in_place_misaligned_and_grads_only(nh):
+@pytest.mark.parametrize("threads", [256, 1024])
+def test_channel_kernels_in_place_misaligned_and_grads_only(nh, threads):
+    nh.plan_override("bn_channel_threads", threads)
+    try:
+        _in_place_misaligned_grads_only(nh)
+    finally:
+        nh.plan_override("bn_channel_threads", 0)
+
+
+def _in_place_misaligned_grads_only(nh):
     c = wl.bn_case(4, 37, 9, 13, wl.F32, seed=77, x_mean=3.0)
     ref, _ = _run(nh, c, "relu", 0.0)
     inp, l1 = _run(nh, c, "relu", 0.0, in_place=True)
