@@ -96,6 +96,7 @@ std::atomic<int64_t> g_override_colsum_cols{0};
 std::atomic<int64_t> g_override_rows_teams{0};
 std::atomic<int64_t> g_override_bn_channel{0};
 std::atomic<int64_t> g_override_bn_channel_threads{0};
+std::atomic<int64_t> g_override_rows_narrow{0};
 
 // ---- BatchNorm planning ----------------------------------------------------------
 // Resident 256-thread block slots of the device: CUs * (threads per CU / 256),
@@ -265,6 +266,19 @@ RowsPlan rows_variant(int64_t cols, int vec, bool vec_ok, int max_elems = kRowsM
     return p;
 }
 
+// Rows short enough for the narrow kernels (a lane subgroup per row): at
+// most kGenNarrowGroups groups of `vec` elements.  With vector groups this
+// also takes aligned rows the 256-thread team kernels would run with most of
+// their threads idle and a block barrier per row -- measured on MI355X,
+// RMSNorm backward 131072x128 bf16 203 us and 1048576x16 bf16 1604 us on
+// the team kernel.  The "rows_narrow" override = 1 keeps aligned rows on the
+// team kernels.
+bool rows_narrow(int64_t cols, int vec)
+{
+    if (vec == 1) return cols <= kGenNarrowGroups;
+    return g_override_rows_narrow.load() != 1 && cols / vec <= kGenNarrowGroups;
+}
+
 // Generic path (no vector variant fits): rows of at most kGenNarrowGroups
 // columns take the narrow kernel with scalar accesses and a subgroup of ct
 // lanes per row (ct = the power of two covering the row), each block's
@@ -281,22 +295,22 @@ void rows_generic_plan(RowsCall &a, bool vec_ok, const DeviceInfo &d)
     const bool forced = g_override_rows_blocks.load() > 0;
     a.maxg = 0;
     a.team = kTeam;
-    if (a.cols <= kGenNarrowGroups) {
+    const int gvec = vec_ok && a.cols % a.vec == 0 ? a.vec : 1;
+    const int64_t groups = a.cols / gvec;
+    if (rows_narrow(a.cols, gvec)) {
         int ct = 1;
-        while (ct < a.cols) ct <<= 1;
+        while (ct < groups) ct <<= 1;
         const int64_t slots = kTeam / ct;
         int64_t g = forced ? gmax : ceil_div(a.rows, slots * kGenNarrowRowsInFlight);
         if (g > gmax) g = gmax;
         if (g < 1) g = 1;
-        a.vec = 1;
+        a.vec = gvec;
         a.gen_ct = ct;
         a.gen_rpc = 0;
         a.gen_coef_waves = 0;
         a.blocks = (int)g;
         return;
     }
-    const int gvec = vec_ok && a.cols % a.vec == 0 ? a.vec : 1;
-    const int64_t groups = a.cols / gvec;
     const int64_t strips = ceil_div(groups, kGenStripGroups);
     int64_t rb = forced ? gmax : std::min(ceil_div(kGenTargetBlocks, strips), ceil_div(a.rows, kGenMinChunkRows));
     if (rb > gmax) rb = gmax;
@@ -315,10 +329,11 @@ void rows_generic_plan(RowsCall &a, bool vec_ok, const DeviceInfo &d)
     a.blocks = (int)ceil_div(a.rows, rpc);
 }
 
-// Forward generic path (no vector variant fits): rows of at most
-// kGenNarrowGroups columns take the narrow kernel (a subgroup of ct lanes per
-// row, each row slot loading kGenNarrowRowsInFlight rows at once, at most 8
-// blocks per CU); wider rows a team per row with vec-element groups when the
+// Forward generic path (no vector variant fits, or rows short enough for
+// the narrow kernel, see rows_narrow): short rows take the narrow kernel (a
+// subgroup of ct lanes per row, each row slot loading up to
+// kGenNarrowRowsInFlight rows at once, at most 8 blocks per CU); wider rows
+// a team per row with vec-element groups when the
 // tensors allow it, 1024 threads when 256-thread teams would leave the device
 // part empty and every thread still gets kGenFwdMinGroupsPerThread groups,
 // one block per row up to a full device.
@@ -326,20 +341,20 @@ void rows_forward_generic_plan(FwdCall &a, bool vec_ok, const DeviceInfo &d)
 {
     const int64_t full = (int64_t)d.cus * 8;  // resident 256-thread blocks
     a.maxg = 0;
-    if (a.cols <= kGenNarrowGroups) {
+    const int gvec = vec_ok && a.cols % a.vec == 0 ? a.vec : 1;
+    const int64_t groups = a.cols / gvec;
+    if (rows_narrow(a.cols, gvec)) {
         int ct = 1;
-        while (ct < a.cols) ct <<= 1;
+        while (ct < groups) ct <<= 1;
         int64_t g = ceil_div(a.rows, (int64_t)(kTeam / ct) * kGenNarrowRowsInFlight);
         if (g > full) g = full;
         if (g < 1) g = 1;
-        a.vec = 1;
+        a.vec = gvec;
         a.team = kTeam;
         a.gen_ct = ct;
         a.blocks = (int)g;
         return;
     }
-    const int gvec = vec_ok && a.cols % a.vec == 0 ? a.vec : 1;
-    const int64_t groups = a.cols / gvec;
     const bool big = a.rows < full && groups >= (int64_t)kGenFwdBigTeam * kGenFwdMinGroupsPerThread;
     a.vec = gvec;
     a.gen_ct = 0;
@@ -677,7 +692,8 @@ static nh_status rows_run(RowsCall &a, int Q, void *ws, size_t ws_bytes, void *s
     a.colsum_cols = (int)g_override_colsum_cols.load();
     a.teams = (int)g_override_rows_teams.load();
     hipError_t e = hipSuccess;
-    if (p.maxg == 0) {
+    const bool vec_groups = vec_ok && a.cols % a.vec == 0;
+    if (p.maxg == 0 || rows_narrow(a.cols, vec_groups ? a.vec : 1)) {
         rows_generic_plan(a, vec_ok, d);
         a.coef = a.gen_ct == 0
             ? reinterpret_cast<float *>(static_cast<char *>(ws) + rows_partials_bytes(Q, a.rows, a.cols, d))
@@ -847,7 +863,8 @@ static nh_status rows_forward_run(FwdCall &a, void *stream)
     RowsPlan p = rows_variant(a.cols, a.vec, vec_ok);
     a.depth = (int)g_override_rows_depth.load();
     hipError_t e = hipSuccess;
-    if (p.maxg == 0) {
+    const bool vec_groups = vec_ok && a.cols % a.vec == 0;
+    if (p.maxg == 0 || rows_narrow(a.cols, vec_groups ? a.vec : 1)) {
         rows_forward_generic_plan(a, vec_ok, d);
         e = rows_forward_launch(a, s);
         if (e != hipSuccess) return hip_fail(e, "forward row kernel launch");
@@ -1074,6 +1091,10 @@ nh_status nh_plan_override(const char *key, int64_t value)
             return fail(NH_ERR_ARG, "bn_channel_threads must be 0, %d or %d", kBnThreads, kBnChannelBigBlock);
         g_override_bn_channel_threads.store(value);
     }
+    else if (strcmp(key, "rows_narrow") == 0) {
+        if (value > 1) return fail(NH_ERR_ARG, "rows_narrow must be 0 or 1");
+        g_override_rows_narrow.store(value);
+    }
     else if (strcmp(key, "rows_teams") == 0) {
         if (value > 2) return fail(NH_ERR_ARG, "rows_teams must be 0, 1 or 2");
         g_override_rows_teams.store(value);
@@ -1164,7 +1185,8 @@ nh_status nh_selftest_host(void)
     dv.valid = true;
     dv.cus = 256;
     const int64_t Rs[] = {1, 2, 31, 33, 97, 1000, 4097, 65537, (1 << 18) - 1, 33554431};
-    const int64_t Hs[] = {1, 2, 3, 31, 63, 64, 65, 257, 1000, 1601, 4096, 16385, 32768, 65536, 1 << 20};
+    const int64_t Hs[] = {1, 2, 3, 8, 31, 63, 64, 65, 128, 256, 257, 512, 1000, 1601, 4096, 16385, 32768,
+                          65536, 1 << 20};
     for (int64_t rows : Rs)
         for (int64_t cols : Hs) {
             if (rows * cols >= kMaxElems) continue;
@@ -1180,9 +1202,13 @@ nh_status nh_selftest_host(void)
                         return fail(NH_ERR_ARG, "generic blocks %d (rows=%lld cols=%lld)", a.blocks,
                                     (long long)rows, (long long)cols);
                     if (a.gen_ct > 0) {
-                        if (cols > kGenNarrowGroups || a.gen_ct < cols || a.gen_ct > kGenNarrowGroups ||
-                            (a.gen_ct & (a.gen_ct - 1)) != 0 || a.vec != 1)
-                            return fail(NH_ERR_ARG, "narrow plan ct=%d cols=%lld", a.gen_ct, (long long)cols);
+                        const bool vec_fits = vec_ok && cols % vec == 0;
+                        if ((a.vec != 1 && (a.vec != vec || !vec_fits)) || cols % a.vec != 0 ||
+                            cols / a.vec > kGenNarrowGroups || a.gen_ct < cols / a.vec ||
+                            a.gen_ct > kGenNarrowGroups || (a.gen_ct & (a.gen_ct - 1)) != 0 ||
+                            (vec_fits && a.vec == 1))
+                            return fail(NH_ERR_ARG, "narrow plan ct=%d vec=%d cols=%lld", a.gen_ct, a.vec,
+                                        (long long)cols);
                         continue;
                     }
                     const int64_t rpc = a.gen_rpc;

@@ -161,42 +161,47 @@ __device__ __forceinline__ void fwd_row_stats(float s1, float s2, float K, float
     }
 }
 
-// Rows of at most 64 columns, any alignment: a subgroup of ct lanes (the
-// power of two covering the row) per row, U rows of a slot loaded at once,
-// the row sums reduced by lane exchanges inside the subgroup.
-template <int KIND, typename TX, typename TY>
+// Rows of at most 64 groups of VEC elements (VEC = 1 for any alignment, or
+// the vector width for aligned rows): a subgroup of ct lanes (the power of
+// two covering the groups) per row, U rows of a slot loaded at once, the row
+// sums reduced by lane exchanges inside the subgroup.
+template <int KIND, typename TX, typename TY, int VEC>
 __global__ void __launch_bounds__(kTeam)
 norm_fwd_narrow_kernel(const TX *__restrict__ x, const void *__restrict__ w,
                        const void *__restrict__ b, int w_bf16, int rows, int H, float eps,
                        TY *__restrict__ y, float *__restrict__ stat0, float *__restrict__ stat1, int ct)
 {
-    constexpr int U = kGenNarrowRowsInFlight;
+    constexpr int U = VEC == 1 ? kGenNarrowRowsInFlight : 4;
     const int tt = threadIdx.x;
     const int lane = tt & (ct - 1);
     const int slot = tt >> __builtin_ctz((unsigned)ct);
     const int slots = kTeam / ct;
-    const bool col_ok = lane < H;
-    const int col = col_ok ? lane : 0;  // dead lanes read column 0 and drop it
+    const bool col_ok = lane < H / VEC;
+    const int col = (col_ok ? lane : 0) * VEC;  // dead lanes read group 0 and drop it
     const float invH = 1.0f / (float)H;
-    const float wj = w != nullptr ? load_param(w, w_bf16, col) : 1.f;
-    const float bj = KIND == 0 && b != nullptr ? load_param(b, w_bf16, col) : 0.f;
+    ParamGroup<VEC> wv, bv;
+    wv.load(w, w_bf16, col, 1.f);
+    bv.load(KIND == 0 ? b : nullptr, w_bf16, col, 0.f);
     const int64_t stride = (int64_t)gridDim.x * slots;
     for (int64_t r0 = (int64_t)blockIdx.x * slots + slot; r0 < rows; r0 += U * stride) {
-        float v[U], K[U];
+        float v[U][VEC], K[U];
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             const int64_t rk = r0 + k * stride;
             const size_t rowoff = (size_t)(rk < rows ? rk : rows - 1) * H;
-            v[k] = to_f32(__builtin_nontemporal_load(x + rowoff + col));
+            ld<true, TX, VEC>(x + rowoff + col, v[k]);
             K[k] = KIND == 0 ? to_f32(x[rowoff]) : 0.f;
         }
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             float s1 = 0.f, s2 = 0.f;
             if (col_ok) {
-                const float d = v[k] - K[k];
-                s1 = KIND == 0 ? d : 0.f;
-                s2 = d * d;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const float d = v[k][e] - K[k];
+                    if constexpr (KIND == 0) s1 += d;
+                    s2 = fmaf(d, d, s2);
+                }
             }
             s1 = sub_sum(s1, ct);
             s2 = sub_sum(s2, ct);
@@ -204,8 +209,13 @@ norm_fwd_narrow_kernel(const TX *__restrict__ x, const void *__restrict__ w,
             if (rk < rows) {
                 float a, c;
                 fwd_row_stats<KIND>(s1, s2, K[k], invH, eps, rk, lane == 0, stat0, stat1, a, c);
-                const float o = KIND == 0 ? fmaf((v[k] - c) * a, wj, bj) : wj * (v[k] * a);
-                if (col_ok) __builtin_nontemporal_store(from_f32<TY>(o), y + (size_t)rk * H + col);
+                if (col_ok) {
+                    float o[VEC];
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        o[e] = KIND == 0 ? fmaf((v[k][e] - c) * a, wv.v[e], bv.v[e]) : wv.v[e] * (v[k][e] * a);
+                    st<true, TY, VEC>(y + (size_t)rk * H + col, o);
+                }
             }
         }
     }
@@ -336,14 +346,20 @@ template <int KIND, typename TX, typename TY>
 static hipError_t fwd_generic(const FwdCall &a, hipStream_t s)
 {
     if (a.occupancy_out) { *a.occupancy_out = 1; return hipSuccess; }  // not used by the generic plan
-    if (a.gen_ct > 0)
-        return launch(KIND == 0 ? NH_K_LN_FWD : NH_K_RMS_FWD, norm_fwd_narrow_kernel<KIND, TX, TY>,
-                      dim3(a.blocks), dim3(kTeam), 0u, s, static_cast<const TX *>(a.x), a.w, a.b, a.w_t,
-                      a.rows, a.cols, a.eps, static_cast<TY *>(a.y), a.stat0, a.stat1, a.gen_ct);
-    if (a.vec == 1) return fwd_team<KIND, TX, TY, 1>(a, s);
     // The vector width of a type mix: 8 when x and y are both bf16, else 4.
     constexpr int V = sizeof(TX) == 2 && sizeof(TY) == 2 ? 8 : 4;
-    if (a.vec != V) return hipErrorInvalidValue;
+    if (a.vec != 1 && a.vec != V) return hipErrorInvalidValue;
+    const int kid = KIND == 0 ? NH_K_LN_FWD : NH_K_RMS_FWD;
+    if (a.gen_ct > 0) {
+        if (a.vec == 1)
+            return launch(kid, norm_fwd_narrow_kernel<KIND, TX, TY, 1>, dim3(a.blocks), dim3(kTeam), 0u, s,
+                          static_cast<const TX *>(a.x), a.w, a.b, a.w_t, a.rows, a.cols, a.eps,
+                          static_cast<TY *>(a.y), a.stat0, a.stat1, a.gen_ct);
+        return launch(kid, norm_fwd_narrow_kernel<KIND, TX, TY, V>, dim3(a.blocks), dim3(kTeam), 0u, s,
+                      static_cast<const TX *>(a.x), a.w, a.b, a.w_t, a.rows, a.cols, a.eps,
+                      static_cast<TY *>(a.y), a.stat0, a.stat1, a.gen_ct);
+    }
+    if (a.vec == 1) return fwd_team<KIND, TX, TY, 1>(a, s);
     return fwd_team<KIND, TX, TY, V>(a, s);
 }
 

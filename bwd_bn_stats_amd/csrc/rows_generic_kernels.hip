@@ -12,9 +12,11 @@
 // partials[Q, G, H] and reduced by rows_colsum_kernel as for the vector path.
 // Only the mapping of rows and columns to threads differs.
 //
-// Narrow rows (H <= 64, scalar accesses): rows_narrow_kernel.  A subgroup of
-// ct lanes of a wave (ct = the power of two covering H) owns one row at a
-// time, so a 256-thread block works on 256/ct rows at once.  The row sums
+// Narrow rows (at most 64 groups of VEC elements: H <= 64 with scalar
+// accesses, or up to 64 vector groups when the tensors are aligned):
+// rows_narrow_kernel.  A subgroup of ct lanes of a wave (ct = the power of
+// two covering the groups) owns one row at a time, so a 256-thread block
+// works on 256/ct rows at once.  The row sums
 // are lane exchanges inside the subgroup, with no barrier; every lane keeps
 // its column's sums in registers across rows, and the block's row slots add
 // theirs through LDS, in slot order, once at the end.
@@ -182,63 +184,75 @@ __device__ __forceinline__ void group_out(const GenArgs &a, size_t off, const Gr
 }
 
 // ---- narrow rows: a subgroup of lanes per row ----------------------------------
-template <int KIND, typename TX, typename TDY, typename TDX>
+// VEC elements per lane (1, or the vector width when the tensors allow it);
+// a row holds at most kGenNarrowGroups groups.
+template <int KIND, typename TX, typename TDY, typename TDX, int VEC>
 __global__ void __launch_bounds__(kTeam)
 rows_narrow_kernel(GenArgs a)
 {
     constexpr int Q = rows_q(KIND);
-    constexpr int U = kGenNarrowRowsInFlight;
-    __shared__ float red[Q * kTeam];
+    // rows of a slot in flight: fewer for wide groups, to stay within registers
+    constexpr int U = VEC == 1 ? kGenNarrowRowsInFlight : (KIND == 2 && VEC == 8 ? 2 : 4);
+    __shared__ float red[Q * VEC * kTeam];
     const int tt = threadIdx.x;
     const int ct = a.ct;
-    const int lane = tt & (ct - 1);        // the lane's column
+    const int lane = tt & (ct - 1);        // the lane's column group
     const int slot = tt >> __builtin_ctz((unsigned)ct);
     const int slots = kTeam / ct;
     const int H = a.cols;
-    const bool col_ok = lane < H;
-    const int col = col_ok ? lane : 0;     // dead lanes read column 0 and drop it
+    const bool col_ok = lane < H / VEC;
+    const int col = (col_ok ? lane : 0) * VEC;  // dead lanes read group 0 and drop it
     const int64_t rows = a.rows;
-    float w[1];
-    w[0] = a.w != nullptr ? load_param(a.w, a.w_bf16, col) : 1.f;
-    float p[Q][1];
+    WeightGroup<VEC> w;
+    w.load(a.w, a.w_bf16, col);
+    float p[Q][VEC];
 #pragma unroll
-    for (int q = 0; q < Q; ++q) p[q][0] = 0.f;
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) p[q][e] = 0.f;
 
     const int64_t stride = (int64_t)gridDim.x * slots;
     for (int64_t r0 = (int64_t)blockIdx.x * slots + slot; r0 < rows; r0 += U * stride) {
-        GroupIn<1> g[U];
+        GroupIn<VEC> g[U];
         float mu[U], rs[U];
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             const int64_t rk = r0 + k * stride;
             const int64_t rc = rk < rows ? rk : rows - 1;  // in bounds; results dropped below
-            load_group<KIND == 2, true, TX, TDY, 1>(a, (size_t)rc * H + col, g[k]);
+            load_group<KIND == 2, true, TX, TDY, VEC>(a, (size_t)rc * H + col, g[k]);
             mu[k] = KIND != 1 ? a.mean[rc] : 0.f;
             rs[k] = KIND != 1 ? a.rstd[rc] : 0.f;
         }
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             float s0 = 0.f, s1 = 0.f;
-            if (col_ok) add_row_sums<KIND, 1>(g[k], w, mu[k], rs[k], s0, s1);
+            if (col_ok) add_row_sums<KIND, VEC>(g[k], w.v, mu[k], rs[k], s0, s1);
             s0 = sub_sum(s0, ct);
             s1 = sub_sum(s1, ct);
             const int64_t rk = r0 + k * stride;
             if (rk < rows && col_ok) {
                 const float2 c = row_coefs<KIND>(a, rk, s0, s1);
-                group_out<KIND, TDX, 1, Q>(a, (size_t)rk * H + col, g[k], w, mu[k], rs[k], c, p);
+                group_out<KIND, TDX, VEC, Q>(a, (size_t)rk * H + col, g[k], w.v, mu[k], rs[k], c, p);
             }
         }
     }
     if (!a.want_cols) return;
 #pragma unroll
-    for (int q = 0; q < Q; ++q) red[q * kTeam + tt] = p[q][0];
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) red[(q * VEC + e) * kTeam + tt] = p[q][e];
     __syncthreads();
     if (tt < ct && col_ok) {
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
-            float s = 0.f;
-            for (int k = 0; k < slots; ++k) s += red[q * kTeam + k * ct + tt];
-            a.partials[((size_t)q * gridDim.x + blockIdx.x) * H + col] = s;
+            float sv[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                float acc = 0.f;
+                for (int k = 0; k < slots; ++k) acc += red[(q * VEC + e) * kTeam + k * ct + tt];
+                sv[e] = acc;
+            }
+            store_vec<float, VEC>(a.partials + ((size_t)q * gridDim.x + blockIdx.x) * H + col, sv);
         }
     }
 }
@@ -427,13 +441,17 @@ template <int KIND, typename TX, typename TDY, typename TDX>
 static hipError_t generic_types(const RowsCall &a, const GenArgs &g, hipStream_t s)
 {
     const int kid = KIND == 0 ? NH_K_LN_ROWS : (KIND == 1 ? NH_K_RMS_ROWS : NH_K_BDA_ROWS);
-    if (a.gen_ct > 0)
-        return launch(kid, rows_narrow_kernel<KIND, TX, TDY, TDX>, dim3((unsigned)a.blocks), dim3(kTeam),
-                      0u, s, g);
-    if (a.vec == 1) return strip_launch<KIND, TX, TDY, TDX, 1>(a, g, kid, s);
     // The vector width of a type mix: 8 when every row tensor is bf16, else 4.
     constexpr int V = sizeof(TX) == 2 && sizeof(TDY) == 2 && sizeof(TDX) == 2 ? 8 : 4;
-    if (a.vec != V) return hipErrorInvalidValue;
+    if (a.vec != 1 && a.vec != V) return hipErrorInvalidValue;
+    if (a.gen_ct > 0) {
+        if (a.vec == 1)
+            return launch(kid, rows_narrow_kernel<KIND, TX, TDY, TDX, 1>, dim3((unsigned)a.blocks),
+                          dim3(kTeam), 0u, s, g);
+        return launch(kid, rows_narrow_kernel<KIND, TX, TDY, TDX, V>, dim3((unsigned)a.blocks), dim3(kTeam),
+                      0u, s, g);
+    }
+    if (a.vec == 1) return strip_launch<KIND, TX, TDY, TDX, 1>(a, g, kid, s);
     return strip_launch<KIND, TX, TDY, TDX, V>(a, g, kid, s);
 }
 

@@ -423,7 +423,9 @@ nh_status nh_rows_plan(int64_t rows, int64_t cols, int *blocks);
  * 8, 16, 32 or 64 sets the columns per block of the column finalize (same
  * results), key "bn_channel" = 1 or 2 turns the one-block-per-channel
  * fused BatchNorm kernels (used automatically for small channels) off or
- * on, key "bn_channel_threads" = 256 or 1024 sets their block size, key "rows_teams" = 1 or 2 forces the row teams per block of the
+ * on, key "bn_channel_threads" = 256 or 1024 sets their block size, key "rows_narrow" = 1 keeps aligned rows of at most 64 vector groups
+ * on the 256-thread team kernels instead of the lane-subgroup kernels, key
+ * "rows_teams" = 1 or 2 forces the row teams per block of the
  * LayerNorm and RMSNorm backwards' vector kernels (same results up to the
  * order of the column sums).  value 0 restores the automatic plan.  Process-wide; not for concurrent use with
  * other calls.

@@ -40,6 +40,10 @@ CASES = [
     (4099, 33, F32, BF16, BF16, 2, "narrow"),
     (1000, 64, BF16, F32, F32, 1, "narrow"),        # widest narrow row, misaligned
     (777, 63, F32, F32, BF16, 0, "narrow"),
+    (2000, 128, BF16, BF16, BF16, 0, "narrow"),     # aligned short rows: vector groups, 16 lanes per row
+    (777, 256, F32, BF16, BF16, 0, "narrow"),       # 64 groups of 4: the widest fp32 narrow row
+    (1000, 512, BF16, BF16, BF16, 0, "narrow"),     # 64 groups of 8
+    (5003, 16, BF16, BF16, BF16, 0, "narrow"),      # two lanes per row
     (300, 65, F32, BF16, F32, 1, "strip"),          # narrowest strip row
     (513, 1601, BF16, BF16, BF16, 0, "strip"),      # odd width: scalar groups
     (100, 5000, F32, F32, BF16, 1, "strip"),        # few long rows: 8 team segments per row
@@ -165,3 +169,30 @@ def test_generic_forward(nh, oracle_mod, case):
     torch.cuda.synchronize()
     check("rms y", host(y), wy, xt)
     check("rms rms", host(rms), wrms, F32)
+
+
+@pytest.mark.parametrize("rows,cols,dt", [(2000, 128, BF16), (1001, 64, F32), (300, 512, BF16)])
+def test_short_aligned_rows_on_team_kernels(nh, oracle_mod, rows, cols, dt):
+    """With the "rows_narrow" override the aligned short rows stay on the
+    256-thread team kernels: still the oracle's results."""
+    nh.plan_override("rows_narrow", 1)
+    try:
+        c = wl.bda_case(rows, cols, x_t=dt, dy_t=dt, w_t=dt, seed=rows + cols, p_drop=0.2)
+        ln = c.ln
+        mean, rstd = oracle_mod.layernorm_stats(ln.x.value, eps=ln.eps)
+        m32, r32 = mean.astype(np.float32), rstd.astype(np.float32)
+        from helpers import dev
+        x, dy, w = dev(ln.x), dev(ln.dy), dev(ln.w)
+        wdx, wdw, wdb = oracle_mod.layernorm_backward(ln.x.value, ln.dy.value, m32, r32, ln.w.value)
+        dx, dw, db = nh.layernorm_backward(dy, x, torch.from_numpy(m32).cuda(), torch.from_numpy(r32).cuda(), w,
+                                           dx_dtype=_tdt(dt))
+        y, fm, fr = nh.layernorm_forward(x, w, None, ln.eps)
+        torch.cuda.synchronize()
+        check("ln dx", host(dx), wdx, dt)
+        check("ln dweight", host(dw), wdw, dt)
+        check("ln dbias", host(db), wdb, dt)
+        wy, wm, wr = oracle_mod.layernorm_forward(ln.x.value, ln.w.value, eps=ln.eps)
+        check("ln y", host(y), wy, dt)
+        check("ln mean", host(fm), wm, F32)
+    finally:
+        nh.plan_override("rows_narrow", 0)
