@@ -1,6 +1,8 @@
-// Backward row kernels for the shapes that the register-resident kernels do
-// not take: rows wider than a 512-thread team holds, widths that are not a
-// multiple of the 16-byte group, and tensors at misaligned addresses.  The
+// Backward row kernels for the shapes that the register-resident team
+// kernels do not take -- rows wider than a 512-thread team holds, widths that
+// are not a multiple of the 16-byte group, tensors at misaligned addresses --
+// and for short rows (at most 64 groups), which a 256-thread team per row
+// would run with most of its threads idle.  The
 // arithmetic is that of the vector kernels -- LayerNorm and RMSNorm backward
 // (NVIDIA/Fuser issues #1473 and #3629) and the bias + dropout + add +
 // LayerNorm backward (issue #1473, first example):
