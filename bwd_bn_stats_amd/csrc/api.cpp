@@ -368,10 +368,12 @@ void rows_forward_generic_plan(FwdCall &a, bool vec_ok, const DeviceInfo &d)
 // Measured on MI355X: a 256-thread team per row beats wider teams that
 // synchronize more waves per row (512-thread teams only for rows a
 // 256-thread team cannot hold).
-void rows_grid(RowsPlan &p, int kind, int row_bytes, int64_t rows, int occ, const DeviceInfo &d)
+void rows_grid(RowsPlan &p, int kind, int row_bytes, int64_t groups, int64_t rows, int occ,
+               const DeviceInfo &d)
 {
+    const int per_cu = rows_blocks_per_cu(kind, row_bytes, groups);
     if (occ < 1) occ = 1;
-    if (occ > rows_blocks_per_cu(kind, row_bytes)) occ = rows_blocks_per_cu(kind, row_bytes);
+    if (occ > per_cu) occ = per_cu;
     int64_t g = (int64_t)d.cus * occ;
     const int64_t ov = g_override_rows_blocks.load();
     if (ov > 0) g = ov;
@@ -725,7 +727,8 @@ static nh_status rows_run(RowsCall &a, int Q, void *ws, size_t ws_bytes, void *s
         std::lock_guard<std::mutex> lk(g_dev_mu);
         g_rows_occupancy[key] = occ;
     }
-    rows_grid(p, a.kind, p.maxg * p.vec * (dtype_bytes(a.x_t) + dtype_bytes(a.dy_t)), a.rows, occ, d);
+    rows_grid(p, a.kind, p.maxg * p.vec * (dtype_bytes(a.x_t) + dtype_bytes(a.dy_t)), a.cols / p.vec, a.rows,
+              occ, d);
     a.blocks = p.blocks;
     e = rows_backward_launch(a, s);
     if (e != hipSuccess) return hip_fail(e, "rows backward launch");

@@ -64,17 +64,20 @@ constexpr int kRowsBwdWavesPerSimd = 2;
 // back (measured on MI355X: 2 per CU is the best total for 1600..8192 wide
 // rows).
 constexpr int kRowsMaxBlocksPerCu = 2;
-// Per kind and row size (row_bytes: bytes of x and dy a thread holds per
-// row).  Rows of at least 128 B per thread (8192 columns) keep enough rows
-// in flight with one block per CU, and halving the partial rows saves more
-// than the second block gains -- RMSNorm at 2048 x 8192: 27.9 -> 26.1 us
-// bf16, 44.4 -> 41.0 us fp32; LayerNorm: 33.8 -> 29.7 us bf16, 51.2 -> 49.1
-// us fp32.  RMSNorm keeps one block per CU for short rows too, where its
-// blocks hold two row teams; LayerNorm below 128 B and the
-// bias+dropout+add backward use two.
-constexpr int rows_blocks_per_cu(int kind, int row_bytes)
+// Per kind, row size (row_bytes: bytes of x and dy a thread holds per row)
+// and row groups.  Rows of at least 128 B per thread (8192 columns) keep
+// enough rows in flight with one block per CU, and halving the partial rows
+// saves more than the second block gains -- RMSNorm at 2048 x 8192: 27.9 ->
+// 26.1 us bf16, 44.4 -> 41.0 us fp32; LayerNorm: 33.8 -> 29.7 us bf16, 51.2
+// -> 49.1 us fp32.  RMSNorm keeps one block per CU (of two row teams) for
+// rows of 256 groups too (16384 x 1024 fp32: 38.5 vs 41.8 us), but rows of
+// at most 128 groups leave half of each team idle and want two blocks
+// (32768 x 512 fp32: 53.2 -> 41.0 us, 16384 x 1024 bf16: 34.7 -> 28.8 us).
+// LayerNorm below 128 B and the bias+dropout+add backward use two.
+constexpr int rows_blocks_per_cu(int kind, int row_bytes, int64_t groups)
 {
-    return kind == 1 || (kind == 0 && row_bytes >= 128) ? 1 : kRowsMaxBlocksPerCu;
+    if (kind == 1) return groups <= 128 ? kRowsMaxBlocksPerCu : 1;
+    return kind == 0 && row_bytes >= 128 ? 1 : kRowsMaxBlocksPerCu;
 }
 constexpr int kRowsMaxBlocks = 2048;
 // Row elements a thread holds in the vector row kernels: 32 for LayerNorm and
