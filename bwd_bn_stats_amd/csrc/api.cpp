@@ -185,12 +185,16 @@ nh_status bn_check_shape(int64_t N, int64_t C, int64_t HW)
     return NH_OK;
 }
 
+// Elements per BatchNorm unit: 16 bytes (4 fp32 / 8 bf16) when the plane
+// length and the pointers allow it; for bf16, 8-byte units (4 elements) when
+// only those fit (planes of 4k elements, e.g. 14x14); else single elements.
 int bn_vec(int io, int64_t HW, const void *a, const void *b, const void *c)
 {
-    const int v = io == NH_F32 ? 4 : 8;
-    if (HW % v != 0) return 1;
-    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16)) return 1;
-    return v;
+    auto all_aligned = [&](size_t al) { return aligned(a, al) && aligned(b, al) && aligned(c, al); };
+    if (io == NH_F32) return HW % 4 == 0 && all_aligned(16) ? 4 : 1;
+    if (HW % 8 == 0 && all_aligned(16)) return 8;
+    if (HW % 4 == 0 && all_aligned(8)) return 4;
+    return 1;
 }
 
 // ---- rows planning ---------------------------------------------------------------

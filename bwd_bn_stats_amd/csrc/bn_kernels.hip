@@ -26,7 +26,8 @@
 // Work split: channel c owns N planes of HW contiguous elements (one per
 // image n, stride C*HW).  Its M = N*HW elements are cut into `units` of `V`
 // consecutive elements inside one plane (V = 16 bytes of data when the
-// plane length and pointers allow it, else 1), numbered plane-major.  The
+// plane length and pointers allow it; 8 bytes for bf16 planes of 4k
+// elements; else 1), numbered plane-major.  The
 // launch has C*grid_y blocks; block (c, yb) takes the contiguous unit range
 // [yb*upb, (yb+1)*upb) of channel c, so every block touches one channel
 // only and reads its per-channel constants once into scalar registers.  The
@@ -743,18 +744,24 @@ static hipError_t bn_backward_t(const BnCall &a, hipStream_t s)
                   static_cast<T *>(a.out), a.stats, a.grads, ge, a.partials, a.grid_y, M, a.beta, a.slope);
 }
 
+// Unit widths: fp32 4 or 1 elements; bf16 8, 4 (8-byte units for planes of
+// 4k elements) or 1.
 template <int ACT>
 static hipError_t bn_forward_act(const BnCall &a, hipStream_t s)
 {
     if (a.io == 0) return a.vec == 4 ? bn_forward_t<float, 4, ACT>(a, s) : bn_forward_t<float, 1, ACT>(a, s);
-    return a.vec == 8 ? bn_forward_t<uint16_t, 8, ACT>(a, s) : bn_forward_t<uint16_t, 1, ACT>(a, s);
+    if (a.vec == 8) return bn_forward_t<uint16_t, 8, ACT>(a, s);
+    if (a.vec == 4) return bn_forward_t<uint16_t, 4, ACT>(a, s);
+    return bn_forward_t<uint16_t, 1, ACT>(a, s);
 }
 
 template <int ACT>
 static hipError_t bn_backward_act(const BnCall &a, hipStream_t s)
 {
     if (a.io == 0) return a.vec == 4 ? bn_backward_t<float, 4, ACT>(a, s) : bn_backward_t<float, 1, ACT>(a, s);
-    return a.vec == 8 ? bn_backward_t<uint16_t, 8, ACT>(a, s) : bn_backward_t<uint16_t, 1, ACT>(a, s);
+    if (a.vec == 8) return bn_backward_t<uint16_t, 8, ACT>(a, s);
+    if (a.vec == 4) return bn_backward_t<uint16_t, 4, ACT>(a, s);
+    return bn_backward_t<uint16_t, 1, ACT>(a, s);
 }
 
 hipError_t bn_forward_launch(const BnCall &a, hipStream_t s)

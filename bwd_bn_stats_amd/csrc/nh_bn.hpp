@@ -80,7 +80,7 @@ inline BnGeom make_bn_geom(int N, int C, int HW, int vec, int grid_y)
 struct BnCall {
     int io;              // 0 fp32, 1 bf16
     int N, C, HW;
-    int vec;             // vector width in elements (1, 4 or 8)
+    int vec;             // unit width in elements: fp32 4 or 1; bf16 8, 4 or 1
     int grid_y;          // blocks per channel of the reduction passes (stats, grad_sums)
     int ew_grid_y;       // blocks per channel of the elementwise passes (apply, dx)
     int separate_finalize;  // 1: finalize as its own kernel; 0: in the elementwise prologue

@@ -75,6 +75,9 @@ CASES = {
     # scalar path: H*W not a multiple of the vector width
     "odd_plane_2x5x7x3_f32": lambda: wl.bn_case(2, 5, 7, 3, wl.F32, seed=31, x_mean=1.0, x_std=2.0),
     "odd_plane_3x6x5x5_bf16": lambda: wl.bn_case(3, 6, 5, 5, wl.BF16, seed=32, x_mean=-2.0, x_std=0.7),
+    # bf16 planes of 4k elements (14x14): 8-byte units, split and fused paths
+    "plane_4k_64x96x14x14_bf16": lambda: wl.bn_case(64, 96, 14, 14, wl.BF16, seed=36, x_mean=3.0),
+    "plane_4k_4x40x10x10_bf16": lambda: wl.bn_case(4, 40, 10, 10, wl.BF16, seed=37, x_mean=-1.0, x_std=0.5),
     # more channels than resident block slots: one block per channel
     "many_channels_2x3000x2x2_f32": lambda: wl.bn_case(2, 3000, 2, 2, wl.F32, seed=33),
     # one channel, a million elements: every slot on one channel
@@ -299,3 +302,21 @@ def test_bn_separate_finalize_kernels_match_fused(nh, oracle_mod, name):
     _compare(c, separate, _oracle_bn(oracle_mod, c))
     for k in fused:
         assert np.array_equal(fused[k].view(np.uint64), separate[k].view(np.uint64)), k
+
+
+@pytest.mark.parametrize("offset", [0, 2, 4])
+def test_bn_bf16_unit_widths_by_alignment(nh, oracle_mod, offset):
+    """bf16 planes of 4k elements at element offsets 0, 2, 4: 8-byte units
+    when the pointers are 8-byte aligned (offsets 0 and 4), single elements
+    otherwise; the oracle's results either way."""
+    from helpers import place
+    c = wl.bn_case(16, 48, 14, 14, wl.BF16, seed=38, x_mean=2.0)
+    print(f"[bn parity] bf16 14x14 planes at offset {offset}", flush=True)
+    x, dy = place(c.x, offset), place(c.dy, offset)
+    g, b = dev(c.gamma), dev(c.beta)
+    rm, rv = dev(c.running_mean), dev(c.running_var)
+    y, stats = nh.bn_forward_train(x, g, b, rm, rv, c.momentum, c.eps)
+    dx, grads = nh.bn_backward(dy, x, stats)
+    torch.cuda.synchronize()
+    got = dict(y=host(y), stats=host(stats), dx=host(dx), grads=host(grads), rm=host(rm), rv=host(rv))
+    _compare(c, got, _oracle_bn(oracle_mod, c))
