@@ -1141,7 +1141,7 @@ nh_status nh_selftest_host(void)
             const int64_t cap = slots / C > 1 ? slots / C : 1;
             if (g < 1 || g > cap || g > u) return fail(NH_ERR_ARG, "bn grid %lld for C=%lld u=%lld",
                                                       (long long)g, (long long)C, (long long)u);
-            if (u >= cap * kBnMinUnits && g != cap)
+            if (u >= cap * kBnGridMinUnits && g != cap)
                 return fail(NH_ERR_ARG, "bn grid underfills: %lld", (long long)g);
         }
     // BatchNorm unit walk at the largest shapes the ABI accepts: for every

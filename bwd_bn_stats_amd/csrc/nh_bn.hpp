@@ -11,16 +11,31 @@ namespace nh {
 constexpr int kBnThreads = 256;
 constexpr int kBnUnroll = 4;     // vector units in flight per thread
 
+constexpr int64_t kBnMinUnits = (int64_t)kBnThreads * kBnUnroll;  // one full unrolled sweep
+
 // Blocks per channel for a channel of `units` vector units: enough blocks
 // that all C*grid_y blocks fill the device's resident slots once, but no
-// block gets less than one full unrolled sweep of its threads.
+// block gets less than kBnGridMinUnits units (two per thread).  Measured on
+// MI355X against a minimum of one full unrolled sweep (1024 units) per
+// block, fwd+bwd step: (32,64,32,32) bf16 19.7 -> 17.2 us, (64,256,28,28)
+// bf16 42.4 -> 39.7 us, but (16,32,32,32) fp32 15.0 -> 15.8 us and
+// (128,64,16,16) fp32 18.6 -> 19.3 us; the configs' grids (bound by the
+// slots) do not change.
 //
 // The reductions and the elementwise passes use the same split: an
 // elementwise block then reads exactly the units that the reduction block of
 // the same index read.  Measured on MI355X, splitting them differently (for
 // example 64 reduction blocks per channel, 32 elementwise) makes apply and dx
 // 25-40% slower, although no L2 line survives from one kernel to the next.
-constexpr int64_t kBnMinUnits = (int64_t)kBnThreads * kBnUnroll;
+constexpr int64_t kBnGridMinUnits = (int64_t)kBnThreads * 2;
+inline int64_t bn_auto_grid_y(int64_t units, int64_t C, int64_t slots)
+{
+    int64_t per_channel = slots / (C > 0 ? C : 1);
+    if (per_channel < 1) per_channel = 1;
+    int64_t want = ceil_div(units, kBnGridMinUnits);
+    if (want < 1) want = 1;
+    return want < per_channel ? want : per_channel;
+}
 
 // Channels of at most kBnChannelMaxUnits units (twice that with enough
 // channels to fill the device) take the one-block-per-channel fused kernels:
@@ -31,14 +46,6 @@ constexpr int64_t kBnMinUnits = (int64_t)kBnThreads * kBnUnroll;
 // thousand elements would not).
 constexpr int64_t kBnChannelMaxUnits = 2 * kBnMinUnits;
 constexpr int kBnChannelBigBlock = 1024;  // threads of the larger fused-kernel block
-inline int64_t bn_auto_grid_y(int64_t units, int64_t C, int64_t slots)
-{
-    int64_t per_channel = slots / (C > 0 ? C : 1);
-    if (per_channel < 1) per_channel = 1;
-    int64_t want = ceil_div(units, kBnMinUnits);
-    if (want < 1) want = 1;
-    return want < per_channel ? want : per_channel;
-}
 
 // Geometry of a BatchNorm launch: channel c's M elements in units of V
 // consecutive elements inside one plane, block (c, yb) owning units
