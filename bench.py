@@ -347,7 +347,7 @@ def bench_rows(nh, torch, case, kind, K, W, cold=True, saved=True):
                                         p["ws"], nb, stream)
             if st:
                 raise RuntimeError(nh.last_error())
-        kernels = ["ln_rows", "ln_colsum"]
+        kernels = ["ln_rows", "ln_colsum", "rows_coef"]
     else:
         rms_p = pa if saved else None
 
@@ -357,7 +357,7 @@ def bench_rows(nh, torch, case, kind, K, W, cold=True, saved=True):
                                       p["dx"], p["dw"], p["ws"], nb, stream)
             if st:
                 raise RuntimeError(nh.last_error())
-        kernels = ["rms_rows", "rms_colsum"]
+        kernels = ["rms_rows", "rms_colsum", "rows_coef"]
 
     tm = Timed(nh, torch)
     ms, per = tm.run(step, K, W, kernels)
@@ -831,6 +831,23 @@ def main():
         for dt in (wl.BF16, wl.F32):
             log(f"[bench] rms_fwd_2048x8192_{dt}")
             others[f"rms_fwd_2048x8192_{dt}"] = bench_rows_fwd(nh, torch, wl.rms_bwd(dt), "rms", kk, W)
+        # shapes beyond the configs, one per planner path: late ResNet BatchNorm
+        # layers (one fused block per channel; 8-byte bf16 units), RMSNorm over a
+        # 128-wide head dimension (lane-subgroup rows) and 32768-wide rows
+        # (row-sum + column-strip kernels)
+        for name, fn in (("bn_late_64x2048x7x7_bf16",
+                          lambda: wl.bn_case(64, 2048, 7, 7, wl.BF16, seed=1011, x_mean=3.0)),
+                         ("bn_64x1024x14x14_bf16",
+                          lambda: wl.bn_case(64, 1024, 14, 14, wl.BF16, seed=1012, x_mean=3.0))):
+            log(f"[bench] {name}")
+            others[name] = bench_bn(nh, torch, fn(), kk, W, cold=True)
+        log("[bench] rms_bwd_131072x128_bf16 (head-dimension rows)")
+        others["rms_bwd_131072x128_bf16"] = bench_rows(
+            nh, torch, wl.rows_case(131072, 128, x_t=wl.BF16, dy_t=wl.BF16, w_t=wl.BF16, seed=1013), "rms", kk, W)
+        log("[bench] ln_bwd_512x32768_bf16 (rows wider than a 512-thread team)")
+        others["ln_bwd_512x32768_bf16"] = bench_rows(
+            nh, torch, wl.rows_case(512, 32768, x_t=wl.BF16, dy_t=wl.BF16, w_t=wl.BF16, seed=1014, with_bias=True),
+            "ln", kk, W)
 
     if not args.quick:
         # one-read/one-write kernels against a plain copy of the same bytes
