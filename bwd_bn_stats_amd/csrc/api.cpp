@@ -216,13 +216,13 @@ int64_t rows_blocks_max(int64_t rows, const DeviceInfo &d)
     return g;
 }
 
-// Partial rows the workspace holds: rows_blocks_max, or, for rows of at most
-// kGenNarrowGroups columns (short partial rows), up to kRowsMaxBlocks for the
-// narrow generic kernel, which needs many blocks to keep enough short rows
-// in flight.
+// Partial rows the workspace holds: rows_blocks_max, or, for rows short
+// enough for the lane-subgroup kernels (at most kGenNarrowMaxCols columns:
+// short partial rows), up to kRowsMaxBlocks, since those kernels need many
+// blocks to keep enough short rows in flight.
 int64_t rows_partial_rows(int64_t rows, int64_t cols, const DeviceInfo &d)
 {
-    if (cols > kGenNarrowGroups) return rows_blocks_max(rows, d);
+    if (cols > kGenNarrowMaxCols) return rows_blocks_max(rows, d);
     const int64_t ov = g_override_rows_blocks.load();
     int64_t g = ov > 0 ? ov : kRowsMaxBlocks;
     if (g > kRowsMaxBlocks) g = kRowsMaxBlocks;

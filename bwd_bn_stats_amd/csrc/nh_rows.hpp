@@ -102,6 +102,7 @@ constexpr int kWideTeam = 512;
 // each row is cut into up to kGenCoefMaxSegs segments of at least
 // kGenCoefMinSegGroups groups, one team each, so that enough teams run.
 constexpr int kGenNarrowGroups = 64;
+constexpr int kGenNarrowMaxCols = 8 * kGenNarrowGroups;  // widest narrow row: 64 groups of 8
 constexpr int kGenNarrowRowsInFlight = 8;  // rows a narrow row slot loads at once
 constexpr int kGenStripGroups = 64;
 constexpr int64_t kGenTargetBlocks = 2048;
