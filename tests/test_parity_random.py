@@ -3,8 +3,12 @@
 A fixed, seeded list of small cases per operation: random N, C, H, W (or
 rows, cols), dtypes, activation, affine on/off, and tensors placed at an
 element offset inside a larger buffer (so pointers are misaligned and the
-scalar paths run).  Every output is compared with the oracle at the parity
-tolerances.  The cases are the same on every run."""
+scalar paths run).  Odd-numbered BatchNorm cases force the split path
+(reduction, then elementwise kernel) where the small random shapes would
+otherwise take the one-block-per-channel kernels; a second set of row cases
+covers short aligned rows (the lane-subgroup kernels with vector groups).
+Every output is compared with the oracle at the parity tolerances.  The cases
+are the same on every run."""
 import numpy as np
 import pytest
 
@@ -52,8 +56,9 @@ def test_bn_random(nh, oracle_mod, case):
     beta = c.beta if affine else np.zeros(C)
     x_t = clear_of_kink(oracle_mod, c.x, gamma, beta, c.eps, 1e-3 if io == wl.F32 else 1e-2) \
         if act != "none" else c.x
+    split = i % 2 == 1  # odd cases: the split path even where one block per channel would be taken
     print(f"[bn random {i}] N={N} C={C} H={H} W={W} io={io} act={act} offset={offset} "
-          f"affine={affine}", flush=True)
+          f"affine={affine} split={split}", flush=True)
     wy, wstats, wrm, wrv = oracle_mod.bn_act_forward_train(
         x_t.value, gamma, beta, act, 0.1, eps=c.eps, momentum=c.momentum,
         running_mean=c.running_mean, running_var=c.running_var)
@@ -62,9 +67,14 @@ def test_bn_random(nh, oracle_mod, case):
     g = torch.from_numpy(c.gamma).cuda() if affine else None
     b = torch.from_numpy(c.beta).cuda() if affine else None
     rm, rv = torch.from_numpy(c.running_mean).cuda(), torch.from_numpy(c.running_var).cuda()
-    y, stats = nh.bn_forward_train(x, g, b, rm, rv, c.momentum, c.eps, act=act, slope=0.1)
-    dx, grads = nh.bn_backward(dy, x, stats, beta=b, act=act, slope=0.1)
-    torch.cuda.synchronize()
+    if split:
+        nh.plan_override("bn_channel", 1)
+    try:
+        y, stats = nh.bn_forward_train(x, g, b, rm, rv, c.momentum, c.eps, act=act, slope=0.1)
+        dx, grads = nh.bn_backward(dy, x, stats, beta=b, act=act, slope=0.1)
+        torch.cuda.synchronize()
+    finally:
+        nh.plan_override("bn_channel", 0)
     check("y", host(y), wy, io)
     check("dx", host(dx), wdx, io)
     for k in range(4):
@@ -84,6 +94,16 @@ def _rows_cases():
         dyt = wl.F32 if rng.random() < 0.5 else wl.BF16
         wt = wl.F32 if rng.random() < 0.5 else wl.BF16
         offset = int(rng.integers(0, 3))
+        cases.append((i, rows, cols, xt, dyt, wt, offset))
+    # short aligned rows (lane-subgroup kernels with vector groups), more rows
+    rng = np.random.Generator(np.random.PCG64(4344))
+    for i in range(24, 36):
+        rows = int(rng.integers(100, 3000))
+        cols = int(rng.choice([8, 16, 24, 32, 96, 128, 200, 256, 384, 512]))
+        xt = wl.F32 if rng.random() < 0.5 else wl.BF16
+        dyt = wl.F32 if rng.random() < 0.5 else wl.BF16
+        wt = wl.F32 if rng.random() < 0.5 else wl.BF16
+        offset = 0
         cases.append((i, rows, cols, xt, dyt, wt, offset))
     return cases
 
