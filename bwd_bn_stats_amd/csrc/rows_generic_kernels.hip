@@ -2,10 +2,10 @@
 // kernels do not take -- rows wider than a 512-thread team holds, widths that
 // are not a multiple of the 16-byte group, tensors at misaligned addresses --
 // and for short rows (at most 64 groups), which a 256-thread team per row
-// would run with most of its threads idle.  The
-// arithmetic is that of the vector kernels -- LayerNorm and RMSNorm backward
-// (NVIDIA/Fuser issues #1473 and #3629) and the bias + dropout + add +
-// LayerNorm backward (issue #1473, first example):
+// would run with most of its threads idle.  The arithmetic is that of the
+// vector kernels -- LayerNorm and RMSNorm backward (NVIDIA/Fuser issues
+// #1473 and #3629) and the bias + dropout + add + LayerNorm backward (issue
+// #1473, first example):
 //   LayerNorm: xhat = (x - mean)*rstd, g = dy*w,
 //              dx = rstd*(g - sum g/H - xhat*sum(g*xhat)/H)
 //   RMSNorm:   rinv = 1/rms, g = dy*w, dx = rinv*g - x*rinv^3*sum(g*x)/H
@@ -14,26 +14,26 @@
 // partials[Q, G, H] and reduced by rows_colsum_kernel as for the vector path.
 // Only the mapping of rows and columns to threads differs.
 //
-// Narrow rows (at most 64 groups of VEC elements: H <= 64 with scalar
+// Short rows (at most 64 groups of VEC elements: H <= 64 with scalar
 // accesses, or up to 64 vector groups when the tensors are aligned):
 // rows_narrow_kernel.  A subgroup of ct lanes of a wave (ct = the power of
 // two covering the groups) owns one row at a time, so a 256-thread block
-// works on 256/ct rows at once.  The row sums
-// are lane exchanges inside the subgroup, with no barrier; every lane keeps
-// its column's sums in registers across rows, and the block's row slots add
-// theirs through LDS, in slot order, once at the end.
+// works on 256/ct rows at once.  The row sums are lane exchanges inside the
+// subgroup, with no barrier; every lane keeps its columns' sums in registers
+// across rows, and the block's row slots add theirs through LDS, in slot
+// order, once at the end.
 //
 // Wider rows: rows_coef_kernel, then rows_strip_kernel.  The first reduces
-// each row (one wave, or a 256-thread team for long rows, or several teams
-// for few long rows) to the two sums its gradient needs, 8 bytes per row
-// segment.  The second cuts [rows, H]
-// into strips of 64 column groups by chunks of rows.  A 256-thread block
-// takes one strip of one chunk as 64 column lanes by 4 row lanes, walks the
-// chunk's rows writing the outputs, keeps its columns' sums in registers and
-// writes them once as the chunk's partial row (the 4 row lanes meet in LDS).
-// x and dy are read twice; the second read comes from the Infinity Cache
-// when the tensors fit it.  No partial row is read back while rows are
-// walked, and every output element has one writer.
+// each row (one wave, a 256-thread team for long rows, or several teams for
+// few long rows) to the two sums its gradient needs, 8 bytes per row
+// segment.  The second cuts [rows, H] into strips of 64 column groups by
+// chunks of rows.  A 256-thread block takes one strip of one chunk as 64
+// column lanes by 4 row lanes, walks the chunk's rows writing the outputs,
+// keeps its columns' sums in registers and writes them once as the chunk's
+// partial row (the 4 row lanes meet in LDS).  x and dy are read twice; the
+// second read comes from the Infinity Cache when the tensors fit it.  No
+// partial row is read back while rows are walked, and every output element
+// has one writer.
 #include "rows_common.hpp"
 
 namespace nh {
