@@ -169,10 +169,64 @@ int bn_channel_threads(int64_t units, int64_t C, int64_t slots)
 // Largest grid_y any dtype/alignment can take for this shape (scalar units).
 int64_t bn_grid_y_max(int64_t M, int64_t C, const DeviceInfo &d) { return bn_grid_y_for(M, C, d); }
 
-size_t bn_ws_bytes(int64_t M, int64_t C, const DeviceInfo &d)
+// Small planes take the row layout (bn_col_* kernels): planes of at most
+// kBnColMaxPlaneBytes bytes, where the channel layout reads short runs
+// scattered C*HW elements apart -- unless the channel layout would run one
+// fused kernel per direction on vector units, which its two launches (against
+// the row layout's three per direction) make faster.  Measured on MI355X,
+// fwd+bwd per step, channel layout -> row layout:
+//   (16384,2048,1,1) bf16  5774 -> 139 us     (4096,1024,1,1) fp32  521 -> 40.5 us
+//   (65536,256,1,1) bf16   1428 -> 107 us     (64,2048,7,7) bf16    48.1 -> 34.3 us
+//   but (256,512,4,4) fp32 17.3 -> 26.1 us and (128,256,8,8) bf16 14.3 -> 29.0 us
+//   (fused, vector units: kept on the channel layout).
+// `chan_vec` and `fused` are the channel layout's unit width and fused-kernel
+// choice (fused = 0 for inference).  The "bn_layout" override forces the
+// channel layout (1) or the row layout (2).
+constexpr int64_t kBnColMaxPlaneBytes = 128;
+std::atomic<int64_t> g_override_bn_layout{0};
+
+bool bn_col_possible(int io, int64_t HW) { return HW * (io == NH_F32 ? 4 : 2) <= kBnColMaxPlaneBytes; }
+
+bool bn_col_layout(int io, int64_t HW, int chan_vec, int fused)
 {
+    const int64_t ov = g_override_bn_layout.load();
+    if (ov == 1) return false;
+    if (ov == 2) return true;
+    // overrides that shape the channel layout's plan ask for that layout
+    if (g_override_bn_grid_y.load() > 0 || g_override_bn_ew_grid_y.load() > 0 ||
+        g_override_bn_finalize_kernels.load() != 0 || g_override_bn_channel.load() == 2)
+        return false;
+    return bn_col_possible(io, HW) && (chan_vec == 1 || !fused);
+}
+
+// Workspace of the row layout for either dtype (the workspace query takes no
+// dtype): partials[2, rb, C*HW].
+size_t bn_col_ws_bytes(int64_t N, int64_t C, int64_t HW)
+{
+    const int64_t ov = g_override_bn_layout.load();
+    if (ov == 1 || (ov != 2 && !bn_col_possible(NH_F32, HW) && !bn_col_possible(NH_BF16, HW))) return 0;
+    return round_up((size_t)(2 * bn_col_chunks_max(N) * C * HW) * sizeof(float), 256);
+}
+
+int bn_vec(int io, int64_t HW, const void *a, const void *b, const void *c);
+
+// Row-layout plan: the unit width along the rows (bn_vec over the row length),
+// the geometry; the one-block-per-channel kernels do not apply.
+void bn_col_plan(BnCall &a, const void *p0, const void *p1, const void *p2)
+{
+    a.col = 1;
+    a.channel_fused = 0;
+    a.vec = bn_vec(a.io, (int64_t)a.C * a.HW, p0, p1, p2);
+    a.colg = make_bn_col_geom(a.N, a.C, a.HW, a.vec);
+}
+
+size_t bn_ws_bytes(int64_t N, int64_t C, int64_t HW, const DeviceInfo &d)
+{
+    const int64_t M = N * HW;
+    const size_t col = bn_col_ws_bytes(N, C, HW);
     // partials[2, grid_y, C] + shifts K[C]
-    return round_up((size_t)((2 * bn_grid_y_max(M, C, d) + 1) * C) * sizeof(float), 256);
+    const size_t chan = round_up((size_t)((2 * bn_grid_y_max(M, C, d) + 1) * C) * sizeof(float), 256);
+    return chan > col ? chan : col;
 }
 
 nh_status bn_check_shape(int64_t N, int64_t C, int64_t HW)
@@ -459,7 +513,7 @@ nh_status bn_forward_train_workspace(int64_t N, int64_t C, int64_t HW, size_t *w
     if (N * C * HW == 0) { *ws_bytes = 0; return ok(); }
     DeviceInfo d;
     if ((st = device_info(&d)) != NH_OK) return st;
-    *ws_bytes = bn_ws_bytes(N * HW, C, d);
+    *ws_bytes = bn_ws_bytes(N, C, HW, d);
     return ok();
 }
 
@@ -494,7 +548,7 @@ nh_status bn_act_forward_train(const void *x, void *y, nh_dtype io, int64_t N, i
     if ((st = check_act(act, slope)) != NH_OK) return st;
     DeviceInfo d;
     if ((st = device_info(&d)) != NH_OK) return st;
-    const size_t need = bn_ws_bytes(M, C, d);
+    const size_t need = bn_ws_bytes(N, C, HW, d);
     if (!ws || ws_bytes < need || !aligned(ws, 16))
         return fail(NH_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu)", need, ws_bytes);
 
@@ -521,6 +575,7 @@ nh_status bn_act_forward_train(const void *x, void *y, nh_dtype io, int64_t N, i
     a.separate_finalize = g_override_bn_finalize_kernels.load() != 0;
     a.channel_fused = bn_channel_fused(N * (HW / a.vec), C, bn_slots(d));
     a.channel_threads = bn_channel_threads(N * (HW / a.vec), C, bn_slots(d));
+    if (bn_col_layout(io, HW, a.vec, a.channel_fused)) bn_col_plan(a, x, y, nullptr);
     hipError_t e = bn_forward_launch(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "bn_forward_train launch");
     return ok();
@@ -547,8 +602,7 @@ nh_status bn_act_backward(const void *dy, const void *x, nh_dtype io, int64_t N,
     if ((st = check_act(act, slope)) != NH_OK) return st;
     DeviceInfo d;
     if ((st = device_info(&d)) != NH_OK) return st;
-    const int64_t M = N * HW;
-    const size_t need = bn_ws_bytes(M, C, d);
+    const size_t need = bn_ws_bytes(N, C, HW, d);
     if (!ws || ws_bytes < need || !aligned(ws, 16))
         return fail(NH_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu)", need, ws_bytes);
 
@@ -572,6 +626,7 @@ nh_status bn_act_backward(const void *dy, const void *x, nh_dtype io, int64_t N,
     a.separate_finalize = g_override_bn_finalize_kernels.load() != 0;
     a.channel_fused = bn_channel_fused(N * (HW / a.vec), C, bn_slots(d));
     a.channel_threads = bn_channel_threads(N * (HW / a.vec), C, bn_slots(d));
+    if (bn_col_layout(io, HW, a.vec, a.channel_fused)) bn_col_plan(a, x, dy, dx);
     hipError_t e = bn_backward_launch(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "bn_backward launch");
     return ok();
@@ -618,6 +673,7 @@ nh_status bn_forward_infer(const void *x, void *y, nh_dtype io, int64_t N, int64
     a.eps = eps;
     a.act = act;
     a.slope = slope;
+    if (bn_col_layout(io, HW, a.vec, 0)) bn_col_plan(a, x, y, nullptr);
     hipError_t e = bn_forward_launch(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "bn_forward_infer launch");
     return ok();
@@ -1089,6 +1145,10 @@ nh_status nh_plan_override(const char *key, int64_t value)
             return fail(NH_ERR_ARG, "colsum_cols must be 0, 8, 16, 32 or 64");
         g_override_colsum_cols.store(value);
     }
+    else if (strcmp(key, "bn_layout") == 0) {
+        if (value > 2) return fail(NH_ERR_ARG, "bn_layout must be 0, 1 or 2");
+        g_override_bn_layout.store(value);
+    }
     else if (strcmp(key, "bn_channel") == 0) {
         if (value > 2) return fail(NH_ERR_ARG, "bn_channel must be 0, 1 or 2");
         g_override_bn_channel.store(value);
@@ -1184,6 +1244,24 @@ nh_status nh_selftest_host(void)
                 }
             }
         }
+    }
+    // BatchNorm row layout: the chunks cover the rows exactly once, within the
+    // workspace's chunks, the strips cover the row length.
+    {
+        const int64_t Ns[] = {1, 2, 15, 16, 17, 1000, 4097, 65536, 1 << 20};
+        const int64_t Ls[][2] = {{1, 1}, {3, 1}, {64, 1}, {1000, 1}, {4096, 1}, {37, 4}, {256, 16}, {2048, 49}};
+        for (int64_t n : Ns)
+            for (const auto &cl : Ls)
+                for (int vec : {1, 4, 8}) {
+                    const int64_t C = cl[0], HW = cl[1];
+                    if ((C * HW) % vec != 0 || n * C * HW >= kMaxElems) continue;
+                    const BnColGeom g = make_bn_col_geom((int)n, (int)C, (int)HW, vec);
+                    if (g.rb < 1 || g.rpc < 1 || (int64_t)g.rb * g.rpc < n || (int64_t)(g.rb - 1) * g.rpc >= n ||
+                        g.rb > bn_col_chunks_max(n) || (int64_t)g.strips * kBnColLanes * vec < C * HW ||
+                        (int64_t)(g.strips - 1) * kBnColLanes * vec >= C * HW || g.L != C * HW)
+                        return fail(NH_ERR_ARG, "bn row-layout plan (N=%lld C=%lld HW=%lld vec=%d)", (long long)n,
+                                    (long long)C, (long long)HW, vec);
+                }
     }
     // Generic row plan, on a 256-CU device: the blocks fit the workspace's
     // partial rows, the chunks cover the rows exactly once, the strips cover

@@ -47,7 +47,10 @@
 //
 // Small channels (few units each) take one fused kernel per direction
 // instead: a block per channel reduces, finalizes and writes the elementwise
-// pass (bn_fwd_channel_kernel, bn_bwd_channel_kernel).
+// pass (bn_fwd_channel_kernel, bn_bwd_channel_kernel).  Small planes (a few
+// elements per image and channel) take the row layout: the tensor as
+// [N, C*HW] rows, column sums over row chunks (bn_col_* kernels below).
+// Which path runs is the host plan's choice (api.cpp).
 //
 // No atomics anywhere: each reduction block writes its own partial slot, the
 // finalize kernels combine slots in index order, so results are
@@ -667,6 +670,357 @@ bn_bwd_channel_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__re
     }
 }
 
+// ---- small planes: the tensor as rows of L = C*HW columns ------------------------
+// With small planes a channel's elements lie in short runs C*HW apart, and a
+// block per channel reads scattered sectors.  Viewed as [N, L] (column j in
+// channel j/HW) the per-channel sums are column sums over the rows, and
+// every pass reads whole rows.  A block is kBnColLanes column lanes (each a
+// group of V consecutive columns, one wave) by kBnColRowLanes row lanes over
+// one chunk of rows: the reduction passes keep their columns' sums in
+// registers and write partials[2, rb, L]; a wave per channel then adds a
+// channel's rb*HW partials in fp64 in a fixed order (chunk-major) and
+// finalizes with the arithmetic of the channel path; the elementwise passes
+// load their columns' per-channel constants once and stream the rows.  The
+// shift is K_c = x[0, c, 0, 0], as in bn_stats_kernel.
+constexpr int kBnColRowLanes = kBnThreads / kBnColLanes;
+
+// Rows of a column lane in flight.
+template <int V>
+constexpr int bn_col_unroll() { return V == 8 ? 2 : 4; }
+
+// Column sums of the chunk for one column group: the row lanes' sums meet in
+// LDS, added in row-lane order by row lane 0, which writes both partial rows.
+template <int V>
+__device__ __forceinline__ void bn_col_write_partials(float (&s1)[V], float (&s2)[V], int rl, int lane, bool ok,
+                                                      int j0, const BnColGeom &g, float *__restrict__ partials)
+{
+    __shared__ float red[(kBnColRowLanes - 1) * 2 * V * kBnColLanes];
+    if (rl > 0)
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            red[(((rl - 1) * 2 + 0) * V + e) * kBnColLanes + lane] = s1[e];
+            red[(((rl - 1) * 2 + 1) * V + e) * kBnColLanes + lane] = s2[e];
+        }
+    __syncthreads();
+    if (rl != 0 || !ok) return;
+#pragma unroll
+    for (int e = 0; e < V; ++e)
+#pragma unroll
+        for (int k = 1; k < kBnColRowLanes; ++k) {
+            s1[e] += red[(((k - 1) * 2 + 0) * V + e) * kBnColLanes + lane];
+            s2[e] += red[(((k - 1) * 2 + 1) * V + e) * kBnColLanes + lane];
+        }
+    store_vec<float, V>(partials + (size_t)blockIdx.y * g.L + j0, s1);
+    store_vec<float, V>(partials + ((size_t)g.rb + blockIdx.y) * g.L + j0, s2);
+}
+
+template <typename T, int V, int NT>
+__global__ void __launch_bounds__(kBnThreads)
+bn_col_stats_kernel(const T *__restrict__ x, BnColGeom g, float *__restrict__ partials)
+{
+    constexpr int U = bn_col_unroll<V>();
+    const int lane = threadIdx.x & (kBnColLanes - 1);
+    const int rl = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kBnColLanes);
+    const int grp = (int)blockIdx.x * kBnColLanes + lane;
+    const bool ok = grp < g.L / V;
+    const int j0 = ok ? grp * V : 0;
+    const int64_t r0 = (int64_t)blockIdx.y * g.rpc;
+    const int64_t r1 = r0 + g.rpc < g.N ? r0 + g.rpc : g.N;
+    float K[V], s1[V], s2[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        K[e] = to_f32(x[g.div_hw.div((uint32_t)(j0 + e)) * (uint32_t)g.HW]);
+        s1[e] = 0.f;
+        s2[e] = 0.f;
+    }
+    if (ok) {
+        int64_t r = r0 + rl;
+        for (; r + (U - 1) * kBnColRowLanes < r1; r += U * kBnColRowLanes) {
+            float v[U][V];
+#pragma unroll
+            for (int k = 0; k < U; ++k)
+                ld<(NT & kNtReduceLoads) != 0, T, V>(x + (size_t)(r + k * kBnColRowLanes) * g.L + j0, v[k]);
+#pragma unroll
+            for (int k = 0; k < U; ++k)
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float d = v[k][e] - K[e];
+                    s1[e] += d;
+                    s2[e] = fmaf(d, d, s2[e]);
+                }
+        }
+        for (; r < r1; r += kBnColRowLanes) {
+            float v[V];
+            ld<(NT & kNtReduceLoads) != 0, T, V>(x + (size_t)r * g.L + j0, v);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float d = v[e] - K[e];
+                s1[e] += d;
+                s2[e] = fmaf(d, d, s2[e]);
+            }
+        }
+    }
+    bn_col_write_partials<V>(s1, s2, rl, lane, ok, j0, g, partials);
+}
+
+// A channel's rb*HW partial pairs in fp64: lane l takes flat indices l,
+// l+64, ... (chunk-major), the butterfly combines the lanes.
+__device__ __forceinline__ void bn_col_sum_partials(const float *__restrict__ partials, const BnColGeom &g, int c,
+                                                    double &s1, double &s2)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int n = g.rb * g.HW;
+    double a = 0.0, b = 0.0;
+    for (int i = lane; i < n; i += kWave) {
+        const int rbi = (int)g.div_hw.div((uint32_t)i);
+        const int col = c * g.HW + (i - rbi * g.HW);
+        a += (double)partials[(size_t)rbi * g.L + col];
+        b += (double)partials[((size_t)g.rb + rbi) * g.L + col];
+    }
+    s1 = wave_sum(a);
+    s2 = wave_sum(b);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kBnThreads)
+bn_col_fwd_finalize(const float *__restrict__ partials, const T *__restrict__ x, BnColGeom g,
+                    const float *__restrict__ gamma, float *__restrict__ running_mean,
+                    float *__restrict__ running_var, float momentum, float eps, float *__restrict__ stats)
+{
+    const int c = blockIdx.x * (kBnThreads / kWave) + (int)threadIdx.x / kWave;
+    if (c >= g.C) return;  // whole wave exits together
+    double S1, S2;
+    bn_col_sum_partials(partials, g, c, S1, S2);
+    if ((threadIdx.x & (kWave - 1)) != 0) return;
+    float mean, scale;
+    fwd_finalize_channel(S1, S2, to_f32(x[(size_t)c * g.HW]), g.C, c, (int64_t)g.N * g.HW, gamma,
+                         running_mean, running_var, momentum, eps, true, stats, mean, scale);
+}
+
+// Per-column constants of the elementwise passes.
+template <int V>
+__device__ __forceinline__ void bn_col_channels(const BnColGeom &g, int j0, int (&ch)[V])
+{
+#pragma unroll
+    for (int e = 0; e < V; ++e) ch[e] = (int)g.div_hw.div((uint32_t)(j0 + e));
+}
+
+template <typename T, int V, int SRC, int NT, int ACT>
+__global__ void __launch_bounds__(kBnThreads)
+bn_col_apply_kernel(const T *__restrict__ x, T *__restrict__ y, const float *__restrict__ stats,
+                    const float *__restrict__ beta, BnColGeom g, FwdFinalizeArgs f, float slope)
+{
+    constexpr int U = bn_col_unroll<V>();
+    const int lane = threadIdx.x & (kBnColLanes - 1);
+    const int rl = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kBnColLanes);
+    const int grp = (int)blockIdx.x * kBnColLanes + lane;
+    if (grp >= g.L / V) return;
+    const int j0 = grp * V;
+    int ch[V];
+    bn_col_channels<V>(g, j0, ch);
+    float mean[V], scale[V], b[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        const int c = ch[e];
+        if constexpr (SRC == kApplyRunning) {
+            // as bn_apply_kernel: inv_std in fp64, scale rounded once to fp32
+            mean[e] = f.running_mean[c];
+            const double inv_std = 1.0 / sqrt((double)f.running_var[c] + (double)f.eps);
+            scale[e] = (float)((f.gamma ? (double)f.gamma[c] : 1.0) * inv_std);
+        } else {
+            mean[e] = stats[c];
+            scale[e] = stats[3 * g.C + c];
+        }
+        b[e] = beta ? beta[c] : 0.f;
+    }
+    const int64_t r0 = (int64_t)blockIdx.y * g.rpc;
+    const int64_t r1 = r0 + g.rpc < g.N ? r0 + g.rpc : g.N;
+    auto out = [&](int64_t r, const float (&v)[V]) {
+        float o[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) o[e] = act_fwd<ACT>(fmaf(v[e] - mean[e], scale[e], b[e]), slope);
+        st<(NT & kNtStores) != 0, T, V>(y + (size_t)r * g.L + j0, o);
+    };
+    int64_t r = r0 + rl;
+    for (; r + (U - 1) * kBnColRowLanes < r1; r += U * kBnColRowLanes) {
+        float v[U][V];
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            ld<(NT & kNtEwLoads) != 0, T, V>(x + (size_t)(r + k * kBnColRowLanes) * g.L + j0, v[k]);
+#pragma unroll
+        for (int k = 0; k < U; ++k) out(r + k * kBnColRowLanes, v[k]);
+    }
+    for (; r < r1; r += kBnColRowLanes) {
+        float v[V];
+        ld<(NT & kNtEwLoads) != 0, T, V>(x + (size_t)r * g.L + j0, v);
+        out(r, v);
+    }
+}
+
+template <typename T, int V, int NT, int ACT>
+__global__ void __launch_bounds__(kBnThreads)
+bn_col_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x, const float *__restrict__ stats,
+                        const float *__restrict__ beta, float slope, BnColGeom g, float *__restrict__ partials)
+{
+    constexpr int U = bn_col_unroll<V>();
+    const int lane = threadIdx.x & (kBnColLanes - 1);
+    const int rl = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kBnColLanes);
+    const int grp = (int)blockIdx.x * kBnColLanes + lane;
+    const bool ok = grp < g.L / V;
+    const int j0 = ok ? grp * V : 0;
+    int ch[V];
+    bn_col_channels<V>(g, j0, ch);
+    float mean[V], scale[V], bz[V], s1[V], s2[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        mean[e] = stats[ch[e]];
+        scale[e] = ACT != 0 ? stats[3 * g.C + ch[e]] : 0.f;
+        bz[e] = (ACT != 0 && beta) ? beta[ch[e]] : 0.f;
+        s1[e] = 0.f;
+        s2[e] = 0.f;
+    }
+    const int64_t r0 = (int64_t)blockIdx.y * g.rpc;
+    const int64_t r1 = r0 + g.rpc < g.N ? r0 + g.rpc : g.N;
+    auto add = [&](const float (&vx)[V], const float (&vd)[V]) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const float xc = vx[e] - mean[e];
+            const float dz = act_bwd<ACT>(vd[e], fmaf(xc, scale[e], bz[e]), slope);
+            s1[e] += dz;
+            s2[e] = fmaf(dz, xc, s2[e]);
+        }
+    };
+    if (ok) {
+        int64_t r = r0 + rl;
+        for (; r + (U - 1) * kBnColRowLanes < r1; r += U * kBnColRowLanes) {
+            float vx[U][V], vd[U][V];
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+                const size_t off = (size_t)(r + k * kBnColRowLanes) * g.L + j0;
+                ld<(NT & kNtReduceLoads) != 0, T, V>(x + off, vx[k]);
+                ld<(NT & kNtReduceLoads) != 0, T, V>(dy + off, vd[k]);
+            }
+#pragma unroll
+            for (int k = 0; k < U; ++k) add(vx[k], vd[k]);
+        }
+        for (; r < r1; r += kBnColRowLanes) {
+            float vx[V], vd[V];
+            ld<(NT & kNtReduceLoads) != 0, T, V>(x + (size_t)r * g.L + j0, vx);
+            ld<(NT & kNtReduceLoads) != 0, T, V>(dy + (size_t)r * g.L + j0, vd);
+            add(vx, vd);
+        }
+    }
+    bn_col_write_partials<V>(s1, s2, rl, lane, ok, j0, g, partials);
+}
+
+__global__ void __launch_bounds__(kBnThreads)
+bn_col_bwd_finalize(const float *__restrict__ partials, BnColGeom g, const float *__restrict__ stats,
+                    float *__restrict__ grads)
+{
+    const int c = blockIdx.x * (kBnThreads / kWave) + (int)threadIdx.x / kWave;
+    if (c >= g.C) return;
+    double Sdy, Sdyxc;
+    bn_col_sum_partials(partials, g, c, Sdy, Sdyxc);
+    if ((threadIdx.x & (kWave - 1)) != 0) return;
+    float k1, k2;
+    bwd_finalize_channel(Sdy, Sdyxc, g.C, c, (int64_t)g.N * g.HW, stats, true, grads, k1, k2);
+}
+
+template <typename T, int V, int NT, int ACT>
+__global__ void __launch_bounds__(kBnThreads)
+bn_col_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ dx,
+                 const float *__restrict__ stats, const float *__restrict__ grads,
+                 const float *__restrict__ beta, float slope, BnColGeom g)
+{
+    constexpr int U = bn_col_unroll<V>();
+    const int lane = threadIdx.x & (kBnColLanes - 1);
+    const int rl = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kBnColLanes);
+    const int grp = (int)blockIdx.x * kBnColLanes + lane;
+    if (grp >= g.L / V) return;
+    const int j0 = grp * V;
+    int ch[V];
+    bn_col_channels<V>(g, j0, ch);
+    float mean[V], scale[V], b[V], k1[V], k2[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        const int c = ch[e];
+        mean[e] = stats[c];
+        scale[e] = stats[3 * g.C + c];
+        b[e] = (ACT != 0 && beta) ? beta[c] : 0.f;
+        k1[e] = grads[2 * g.C + c];
+        k2[e] = grads[3 * g.C + c];
+    }
+    const int64_t r0 = (int64_t)blockIdx.y * g.rpc;
+    const int64_t r1 = r0 + g.rpc < g.N ? r0 + g.rpc : g.N;
+    auto out = [&](int64_t r, const float (&vx)[V], const float (&vd)[V]) {
+        float o[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const float xc = vx[e] - mean[e];
+            const float dz = act_bwd<ACT>(vd[e], fmaf(xc, scale[e], b[e]), slope);
+            o[e] = fmaf(dz, scale[e], fmaf(xc, k1[e], k2[e]));
+        }
+        st<(NT & kNtStores) != 0, T, V>(dx + (size_t)r * g.L + j0, o);
+    };
+    int64_t r = r0 + rl;
+    for (; r + (U - 1) * kBnColRowLanes < r1; r += U * kBnColRowLanes) {
+        float vx[U][V], vd[U][V];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const size_t off = (size_t)(r + k * kBnColRowLanes) * g.L + j0;
+            ld<(NT & kNtEwLoads) != 0, T, V>(x + off, vx[k]);
+            ld<(NT & kNtEwLoads) != 0, T, V>(dy + off, vd[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) out(r + k * kBnColRowLanes, vx[k], vd[k]);
+    }
+    for (; r < r1; r += kBnColRowLanes) {
+        float vx[V], vd[V];
+        ld<(NT & kNtEwLoads) != 0, T, V>(x + (size_t)r * g.L + j0, vx);
+        ld<(NT & kNtEwLoads) != 0, T, V>(dy + (size_t)r * g.L + j0, vd);
+        out(r, vx, vd);
+    }
+}
+
+template <typename T, int V, int ACT>
+static hipError_t bn_col_forward_t(const BnCall &a, hipStream_t s)
+{
+    const BnColGeom &g = a.colg;
+    const T *x = static_cast<const T *>(a.x);
+    const dim3 grid((unsigned)g.strips, (unsigned)g.rb), block(kBnThreads);
+    FwdFinalizeArgs f{a.partials, 1, a.gamma, a.running_mean, a.running_var, a.momentum, a.eps,
+                      (int64_t)a.N * a.HW};
+    if (a.inference)
+        return launch(NH_K_BN_INFER, bn_col_apply_kernel<T, V, kApplyRunning, kBnNtPolicy, ACT>, grid, block, 0,
+                      s, x, static_cast<T *>(a.out), a.stats, a.beta, g, f, a.slope);
+    hipError_t e = launch(NH_K_BN_STATS, bn_col_stats_kernel<T, V, kBnNtPolicy>, grid, block, 0, s, x, g,
+                          a.partials);
+    if (e != hipSuccess) return e;
+    e = launch(NH_K_BN_FWD_FINALIZE, bn_col_fwd_finalize<T>, dim3((unsigned)ceil_div(a.C, kBnThreads / kWave)),
+               block, 0, s, (const float *)a.partials, x, g, a.gamma, a.running_mean, a.running_var,
+               a.momentum, a.eps, a.stats);
+    if (e != hipSuccess) return e;
+    return launch(NH_K_BN_APPLY, bn_col_apply_kernel<T, V, kApplyStats, kBnNtPolicy, ACT>, grid, block, 0, s, x,
+                  static_cast<T *>(a.out), a.stats, a.beta, g, f, a.slope);
+}
+
+template <typename T, int V, int ACT>
+static hipError_t bn_col_backward_t(const BnCall &a, hipStream_t s)
+{
+    const BnColGeom &g = a.colg;
+    const T *x = static_cast<const T *>(a.x);
+    const T *dy = static_cast<const T *>(a.dy);
+    const dim3 grid((unsigned)g.strips, (unsigned)g.rb), block(kBnThreads);
+    hipError_t e = launch(NH_K_BN_GRAD_SUMS, bn_col_grad_sums_kernel<T, V, kBnNtPolicy, ACT>, grid, block, 0, s,
+                          dy, x, a.stats, a.beta, a.slope, g, a.partials);
+    if (e != hipSuccess) return e;
+    e = launch(NH_K_BN_BWD_FINALIZE, bn_col_bwd_finalize, dim3((unsigned)ceil_div(a.C, kBnThreads / kWave)),
+               block, 0, s, (const float *)a.partials, g, a.stats, a.grads);
+    if (e != hipSuccess || a.out == nullptr) return e;
+    return launch(NH_K_BN_DX, bn_col_dx_kernel<T, V, kBnNtPolicy, ACT>, grid, block, 0, s, dy, x,
+                  static_cast<T *>(a.out), a.stats, a.grads, a.beta, a.slope, g);
+}
+
 // ---- host launchers -----------------------------------------------------------
 // The reductions run on a.grid_y blocks per channel, the elementwise passes on
 // a.ew_grid_y: the elementwise prologue reads the reduction's partial slots,
@@ -749,6 +1103,12 @@ static hipError_t bn_backward_t(const BnCall &a, hipStream_t s)
 template <int ACT>
 static hipError_t bn_forward_act(const BnCall &a, hipStream_t s)
 {
+    if (a.col) {
+        if (a.io == 0) return a.vec == 4 ? bn_col_forward_t<float, 4, ACT>(a, s) : bn_col_forward_t<float, 1, ACT>(a, s);
+        if (a.vec == 8) return bn_col_forward_t<uint16_t, 8, ACT>(a, s);
+        if (a.vec == 4) return bn_col_forward_t<uint16_t, 4, ACT>(a, s);
+        return bn_col_forward_t<uint16_t, 1, ACT>(a, s);
+    }
     if (a.io == 0) return a.vec == 4 ? bn_forward_t<float, 4, ACT>(a, s) : bn_forward_t<float, 1, ACT>(a, s);
     if (a.vec == 8) return bn_forward_t<uint16_t, 8, ACT>(a, s);
     if (a.vec == 4) return bn_forward_t<uint16_t, 4, ACT>(a, s);
@@ -758,6 +1118,12 @@ static hipError_t bn_forward_act(const BnCall &a, hipStream_t s)
 template <int ACT>
 static hipError_t bn_backward_act(const BnCall &a, hipStream_t s)
 {
+    if (a.col) {
+        if (a.io == 0) return a.vec == 4 ? bn_col_backward_t<float, 4, ACT>(a, s) : bn_col_backward_t<float, 1, ACT>(a, s);
+        if (a.vec == 8) return bn_col_backward_t<uint16_t, 8, ACT>(a, s);
+        if (a.vec == 4) return bn_col_backward_t<uint16_t, 4, ACT>(a, s);
+        return bn_col_backward_t<uint16_t, 1, ACT>(a, s);
+    }
     if (a.io == 0) return a.vec == 4 ? bn_backward_t<float, 4, ACT>(a, s) : bn_backward_t<float, 1, ACT>(a, s);
     if (a.vec == 8) return bn_backward_t<uint16_t, 8, ACT>(a, s);
     if (a.vec == 4) return bn_backward_t<uint16_t, 4, ACT>(a, s);

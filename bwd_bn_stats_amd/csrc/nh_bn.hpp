@@ -84,6 +84,45 @@ inline BnGeom make_bn_geom(int N, int C, int HW, int vec, int grid_y)
     return g;
 }
 
+// Small planes: the tensor viewed as [N, L] rows, L = C*HW, column j in
+// channel j/HW.  A launch covers `strips` column strips of kBnColLanes groups
+// of `vec` elements by `rb` chunks of `rpc` rows; the reduction passes write
+// partials[2, rb, L].
+constexpr int kBnColLanes = 64;              // column lanes per block: one wave
+constexpr int64_t kBnColMaxChunks = 256;     // row chunks, at most (the workspace holds them)
+constexpr int64_t kBnColMinChunkRows = 16;   // rows per chunk, at least
+constexpr int64_t kBnColTargetBlocks = 2048; // blocks aimed at: the resident 256-thread slots
+struct BnColGeom {
+    int N, C, HW, L;
+    int strips, rb, rpc;
+    FastDiv div_hw;  // column -> channel
+};
+
+// Row chunks the workspace holds for N rows.
+inline int64_t bn_col_chunks_max(int64_t N)
+{
+    const int64_t c = ceil_div(N, kBnColMinChunkRows);
+    return c < kBnColMaxChunks ? (c < 1 ? 1 : c) : kBnColMaxChunks;
+}
+
+inline BnColGeom make_bn_col_geom(int N, int C, int HW, int vec)
+{
+    BnColGeom g;
+    g.N = N;
+    g.C = C;
+    g.HW = HW;
+    g.L = C * HW;
+    g.div_hw = make_fastdiv((uint32_t)HW);
+    const int64_t groups = g.L / vec;
+    g.strips = (int)ceil_div(groups, kBnColLanes);
+    int64_t rb = ceil_div(kBnColTargetBlocks, g.strips);
+    if (rb > bn_col_chunks_max(N)) rb = bn_col_chunks_max(N);
+    if (rb < 1) rb = 1;
+    g.rpc = (int)ceil_div(N, rb);
+    g.rb = (int)ceil_div(N, g.rpc);
+    return g;
+}
+
 struct BnCall {
     int io;              // 0 fp32, 1 bf16
     int N, C, HW;
@@ -94,6 +133,8 @@ struct BnCall {
     int inference;       // forward only: apply with the running statistics, no reduction
     int channel_fused;   // 1: one block per channel, reduction + finalize + elementwise in one kernel
     int channel_threads; // threads of that block: kBnThreads or kBnChannelBigBlock
+    int col;             // 1: small planes, the [N, C*HW] row layout (colg; vec along the rows)
+    BnColGeom colg;
     int act;             // 0 none, 1 ReLU, 2 LeakyReLU
     float slope;         // LeakyReLU negative slope
     const void *x;

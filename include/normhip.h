@@ -421,7 +421,9 @@ nh_status nh_rows_plan(int64_t rows, int64_t cols, int *blocks);
  * "rows_depth" = 1..4 forces the number of rows a row-kernel team keeps in
  * flight (its software-pipeline depth; same results), key "colsum_cols" =
  * 8, 16, 32 or 64 sets the columns per block of the column finalize (same
- * results), key "bn_channel" = 1 or 2 turns the one-block-per-channel
+ * results), key "bn_layout" = 1 or 2 forces the BatchNorm channel layout or
+ * the row layout (the tensor as [N, C*HW] rows, used automatically for planes
+ * of at most 128 bytes), key "bn_channel" = 1 or 2 turns the one-block-per-channel
  * fused BatchNorm kernels (used automatically for small channels) off or
  * on, key "bn_channel_threads" = 256 or 1024 sets their block size, key "rows_narrow" = 1 keeps aligned rows of at most 64 vector groups
  * on the 256-thread team kernels instead of the lane-subgroup kernels, key

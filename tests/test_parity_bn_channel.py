@@ -24,6 +24,15 @@ def nh():
     return normhip
 
 
+@pytest.fixture(autouse=True)
+def channel_layout(nh):
+    """These tests are about the channel layout's kernels: small planes would
+    otherwise take the row layout."""
+    nh.plan_override("bn_layout", 1)
+    yield
+    nh.plan_override("bn_layout", 0)
+
+
 def _run(nh, c, act, slope, offset=0, in_place=False, need_dx=True):
     x, dy = place(c.x, offset), place(c.dy, offset)
     g, b = dev(c.gamma), dev(c.beta)
