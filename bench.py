@@ -832,15 +832,18 @@ def main():
             log(f"[bench] rms_fwd_2048x8192_{dt}")
             others[f"rms_fwd_2048x8192_{dt}"] = bench_rows_fwd(nh, torch, wl.rms_bwd(dt), "rms", kk, W)
         # shapes beyond the configs, one per planner path: late ResNet BatchNorm
-        # layers (one fused block per channel; 8-byte bf16 units), RMSNorm over a
-        # 128-wide head dimension (lane-subgroup rows) and 32768-wide rows
-        # (row-sum + column-strip kernels)
+        # layers (one fused block per channel; 8-byte bf16 units), BatchNorm over
+        # [N, C] (the row layout), RMSNorm over a 128-wide head dimension
+        # (lane-subgroup rows) and 32768-wide rows (row-sum + column-strip kernels)
         for name, fn in (("bn_late_64x2048x7x7_bf16",
                           lambda: wl.bn_case(64, 2048, 7, 7, wl.BF16, seed=1011, x_mean=3.0)),
                          ("bn_64x1024x14x14_bf16",
                           lambda: wl.bn_case(64, 1024, 14, 14, wl.BF16, seed=1012, x_mean=3.0))):
             log(f"[bench] {name}")
             others[name] = bench_bn(nh, torch, fn(), kk, W, cold=True)
+        log("[bench] bn_16384x2048x1x1_bf16 (BatchNorm over [N, C]: the row layout)")
+        others["bn_16384x2048x1x1_bf16"] = bench_bn(
+            nh, torch, wl.bn_case(16384, 2048, 1, 1, wl.BF16, seed=1015), kk, W, cold=True)
         log("[bench] rms_bwd_131072x128_bf16 (head-dimension rows)")
         others["rms_bwd_131072x128_bf16"] = bench_rows(
             nh, torch, wl.rows_case(131072, 128, x_t=wl.BF16, dy_t=wl.BF16, w_t=wl.BF16, seed=1013), "rms", kk, W)
