@@ -73,11 +73,16 @@ constexpr int kRowsMaxBlocksPerCu = 2;
 // rows of 256 groups too (16384 x 1024 fp32: 38.5 vs 41.8 us), but rows of
 // at most 128 groups leave half of each team idle and want two blocks
 // (32768 x 512 fp32: 53.2 -> 41.0 us, 16384 x 1024 bf16: 34.7 -> 28.8 us).
-// LayerNorm below 128 B and the bias+dropout+add backward use two.
+// LayerNorm at 33..64 B runs one block of two row teams per CU: as many
+// rows in flight as two one-team blocks, half the partial rows (8192 x 1600
+// x fp32 / dy bf16: 29.4 -> 28.5 us; 4096 x 4096 bf16: 30.2 -> 27.1 us;
+// 4096 x 2048 fp32: 25.5 -> 23.7 us).  LayerNorm at <= 32 B (two teams per
+// block, two blocks) and at 96 B, and the bias+dropout+add backward, use two.
 constexpr int rows_blocks_per_cu(int kind, int row_bytes, int64_t groups)
 {
     if (kind == 1) return groups <= 128 ? kRowsMaxBlocksPerCu : 1;
-    return kind == 0 && row_bytes >= 128 ? 1 : kRowsMaxBlocksPerCu;
+    if (kind == 0 && (row_bytes >= 128 || (row_bytes > 32 && row_bytes <= 64))) return 1;
+    return kRowsMaxBlocksPerCu;
 }
 constexpr int kRowsMaxBlocks = 2048;
 // Row elements a thread holds in the vector row kernels: 32 for LayerNorm and

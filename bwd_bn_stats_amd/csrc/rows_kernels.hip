@@ -309,17 +309,19 @@ static hipError_t ln_vec_dt(const RowsCall &a, hipStream_t s)
                   (int)(a.dweight != nullptr || a.dbias != nullptr));
 }
 
-// Row teams per block: 2 when a thread's row buffer is at most 32 bytes
-// (1 bf16 group of x and dy), else 1.  Measured on MI355X: 8192x1600 bf16
-// 23.3 -> 22.1 us, 16384x1024 bf16 33.7 -> 27.5 us with two teams; at 48 B
-// (8192x1600, x fp32, dy bf16) and 64 B (4096x4096 bf16) one team per block,
-// two blocks per CU, is faster (28.9 vs 29.4 us, 27.6 vs 28.8 us).
+// Row teams per block: 2 when a thread's row buffer is at most 64 bytes
+// (rows of up to 4096 bf16 / 2048 fp32 columns), else 1.  Measured on
+// MI355X: at <= 32 B (two such blocks per CU) 8192x1600 bf16 23.3 -> 22.1 us,
+// 16384x1024 bf16 33.7 -> 27.5 us; at 48 and 64 B one two-team block per CU
+// beats two one-team blocks (8192x1600 x fp32 / dy bf16 29.4 -> 28.5 us,
+// 4096x4096 bf16 30.2 -> 27.1 us), while two two-team blocks per CU are
+// slower than either (30.2, 31.1 us).
 template <typename TX, typename TDY, typename TDX, int VEC, int MAXG, int TEAM, int D>
 static hipError_t ln_vec_d(const RowsCall &a, hipStream_t s)
 {
     constexpr int BYTES = MAXG * VEC * (int)(sizeof(TX) + sizeof(TDY));
     if constexpr (TEAM == kTeam) {
-        const int teams = a.teams > 0 ? a.teams : (BYTES <= 32 ? 2 : 1);
+        const int teams = a.teams > 0 ? a.teams : (BYTES <= 64 ? 2 : 1);
         if (teams == 2) return ln_vec_dt<TX, TDY, TDX, VEC, MAXG, TEAM, D, 2>(a, s);
     }
     return ln_vec_dt<TX, TDY, TDX, VEC, MAXG, TEAM, D, 1>(a, s);

@@ -133,17 +133,19 @@ def test_bda_zero_rows(nh):
 def test_bda_without_extras_is_layernorm_backward(nh, oracle_mod):
     """No incoming gradient, no mask, scale 1: dh and da equal
     layernorm_backward's dx and the shared column gradients agree bit for bit
-    (same block count)."""
+    (same block count, one row team per block in both)."""
     c = wl.bda_case(1000, 1600, x_t=wl.F32, dy_t=wl.F32, w_t=wl.F32, seed=86)
     mean32, rstd32 = _stats(oracle_mod, c)
     args = (dev(c.ln.dy), dev(c.ln.x), dev(mean32), dev(rstd32), dev(c.ln.w))
     nh.plan_override("rows_blocks", 256)
+    nh.plan_override("rows_teams", 1)
     try:
         dh, da, dw, db, dbi = nh.bda_layernorm_backward(*args, None, None, 1.0)
         dx, dw0, db0 = nh.layernorm_backward(*args, dx_dtype=torch.float32)
         torch.cuda.synchronize()
     finally:
         nh.plan_override("rows_blocks", 0)
+        nh.plan_override("rows_teams", 0)
     assert torch.equal(dh, dx) and torch.equal(da, dx)
     assert torch.equal(dw.view(torch.int32), dw0.view(torch.int32))
     assert torch.equal(db.view(torch.int32), db0.view(torch.int32))

@@ -265,7 +265,9 @@ def test_rms_two_team_blocks(nh, oracle_mod, rows, cols, dt, blocks):
 
 @pytest.mark.parametrize("rows,cols,xt,dyt,teams", [(8192, 1600, wl.BF16, wl.BF16, 0), (1001, 1024, wl.F32, wl.BF16, 2),
                                                     (777, 1600, wl.F32, wl.F32, 2), (3, 512, wl.BF16, wl.BF16, 2),
-                                                    (2048, 8192, wl.BF16, wl.BF16, 0), (300, 1600, wl.F32, wl.BF16, 1)])
+                                                    (2048, 8192, wl.BF16, wl.BF16, 0), (300, 1600, wl.F32, wl.BF16, 1),
+                                                    (1000, 4096, wl.BF16, wl.BF16, 0), (600, 2048, wl.F32, wl.F32, 0),
+                                                    (777, 1600, wl.F32, wl.BF16, 0)])
 def test_ln_team_plans(nh, oracle_mod, rows, cols, xt, dyt, teams):
     """LayerNorm with one or two row teams per block (automatic or forced by
     rows_teams), one or two blocks per CU: the oracle's results either way."""
