@@ -199,13 +199,13 @@ bool bn_col_layout(int io, int64_t HW, int chan_vec, int fused)
     return bn_col_possible(io, HW) && (chan_vec == 1 || !fused);
 }
 
-// Workspace of the row layout for either dtype (the workspace query takes no
-// dtype): partials[2, rb, C*HW].
+// Workspace of the row layout for either dtype and unit width (the workspace
+// query takes no dtype): partials[2, rb, C*HW].
 size_t bn_col_ws_bytes(int64_t N, int64_t C, int64_t HW)
 {
     const int64_t ov = g_override_bn_layout.load();
     if (ov == 1 || (ov != 2 && !bn_col_possible(NH_F32, HW) && !bn_col_possible(NH_BF16, HW))) return 0;
-    return round_up((size_t)(2 * bn_col_chunks_max(N) * C * HW) * sizeof(float), 256);
+    return round_up((size_t)(2 * bn_col_chunks_max(N, C * HW) * C * HW) * sizeof(float), 256);
 }
 
 int bn_vec(int io, int64_t HW, const void *a, const void *b, const void *c);
@@ -1246,19 +1246,37 @@ nh_status nh_selftest_host(void)
         }
     }
     // BatchNorm row layout: the chunks cover the rows exactly once, within the
-    // workspace's chunks, the strips cover the row length.
+    // workspace's chunks; the column lanes are a power of two of at most
+    // kBnColLanes that, with the row lanes, make one block; the strips cover
+    // the row length; block ids map one to one onto (strip, chunk).
     {
-        const int64_t Ns[] = {1, 2, 15, 16, 17, 1000, 4097, 65536, 1 << 20};
-        const int64_t Ls[][2] = {{1, 1}, {3, 1}, {64, 1}, {1000, 1}, {4096, 1}, {37, 4}, {256, 16}, {2048, 49}};
+        const int64_t Ns[] = {1, 2, 15, 16, 17, 255, 1000, 4097, 65536, 200704, 1 << 20};
+        const int64_t Ls[][2] = {{1, 1},   {3, 1},    {8, 1},     {64, 1},  {256, 1}, {1000, 1},
+                                 {4096, 1}, {37, 4}, {256, 16}, {2048, 49}, {5, 3}};
+        std::vector<int> seen;
         for (int64_t n : Ns)
             for (const auto &cl : Ls)
                 for (int vec : {1, 4, 8}) {
                     const int64_t C = cl[0], HW = cl[1];
                     if ((C * HW) % vec != 0 || n * C * HW >= kMaxElems) continue;
                     const BnColGeom g = make_bn_col_geom((int)n, (int)C, (int)HW, vec);
-                    if (g.rb < 1 || g.rpc < 1 || (int64_t)g.rb * g.rpc < n || (int64_t)(g.rb - 1) * g.rpc >= n ||
-                        g.rb > bn_col_chunks_max(n) || (int64_t)g.strips * kBnColLanes * vec < C * HW ||
-                        (int64_t)(g.strips - 1) * kBnColLanes * vec >= C * HW || g.L != C * HW)
+                    const int64_t lanes = (int64_t)1 << g.cl_log2;
+                    bool bad = g.rb < 1 || g.rpc < 1 || (int64_t)g.rb * g.rpc < n ||
+                               (int64_t)(g.rb - 1) * g.rpc >= n || g.rb > bn_col_chunks_max(n, C * HW) ||
+                               lanes > kBnColLanes || lanes * g.rl != kBnThreads ||
+                               g.strips * lanes * vec < C * HW || (int64_t)(g.strips - 1) * lanes * vec >= C * HW ||
+                               g.L != C * HW;
+                    if (!bad) {
+                        const int total = g.strips * g.rb;
+                        seen.assign((size_t)total, 0);
+                        for (int id = 0; id < total && !bad; ++id) {
+                            const BnColWork w = bn_col_work(g, id);
+                            const int64_t k = (int64_t)w.chunk * g.strips + w.strip;
+                            bad = w.strip < 0 || w.strip >= g.strips || w.chunk < 0 || w.chunk >= g.rb ||
+                                  seen[(size_t)k]++ != 0;
+                        }
+                    }
+                    if (bad)
                         return fail(NH_ERR_ARG, "bn row-layout plan (N=%lld C=%lld HW=%lld vec=%d)", (long long)n,
                                     (long long)C, (long long)HW, vec);
                 }

@@ -674,44 +674,70 @@ bn_bwd_channel_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__re
 // With small planes a channel's elements lie in short runs C*HW apart, and a
 // block per channel reads scattered sectors.  Viewed as [N, L] (column j in
 // channel j/HW) the per-channel sums are column sums over the rows, and
-// every pass reads whole rows.  A block is kBnColLanes column lanes (each a
-// group of V consecutive columns, one wave) by kBnColRowLanes row lanes over
-// one chunk of rows: the reduction passes keep their columns' sums in
-// registers and write partials[2, rb, L]; a wave per channel then adds a
-// channel's rb*HW partials in fp64 in a fixed order (chunk-major) and
-// finalizes with the arithmetic of the channel path; the elementwise passes
-// load their columns' per-channel constants once and stream the rows.  The
-// shift is K_c = x[0, c, 0, 0], as in bn_stats_kernel.
-constexpr int kBnColRowLanes = kBnThreads / kBnColLanes;
+// every pass reads whole rows.  A block is 2^cl_log2 column lanes (each a
+// group of V consecutive columns) by rl row lanes over one chunk of rows (the
+// geometry and the block -> strip/chunk mapping: make_bn_col_geom,
+// bn_col_work).  The reduction passes keep their columns' sums in registers
+// and write partials[2, rb, L]; the finalize adds each column's rb chunk sums
+// and then a channel's HW column sums, in fp64 in a fixed order, and
+// finalizes with the arithmetic of the channel path; the elementwise passes load their columns'
+// per-channel constants once and stream the rows.  The shift is
+// K_c = x[0, c, 0, 0], as in bn_stats_kernel.
 
 // Rows of a column lane in flight.
 template <int V>
 constexpr int bn_col_unroll() { return V == 8 ? 2 : 4; }
 
-// Column sums of the chunk for one column group: the row lanes' sums meet in
-// LDS, added in row-lane order by row lane 0, which writes both partial rows.
+// A thread's place in the row layout: its column lane and row lane, its
+// column group, and the rows [r0, r1) of its block's chunk.  Row lanes are
+// not wave-uniform when a block has fewer than 64 column lanes.
+struct BnColLane {
+    int lane, rl, grp, chunk;
+    int64_t r0, r1;
+};
+__device__ __forceinline__ BnColLane bn_col_lane(const BnColGeom &g)
+{
+    const BnColWork w = bn_col_work(g, (int)blockIdx.x);
+    BnColLane c;
+    c.lane = (int)threadIdx.x & ((1 << g.cl_log2) - 1);
+    c.rl = (int)threadIdx.x >> g.cl_log2;
+    c.grp = (w.strip << g.cl_log2) + c.lane;
+    c.chunk = w.chunk;
+    c.r0 = (int64_t)w.chunk * g.rpc;
+    c.r1 = c.r0 + g.rpc < g.N ? c.r0 + g.rpc : g.N;
+    return c;
+}
+
+// Column sums of the chunk for one column group: the row lanes' sums are
+// added pairwise through LDS (for h = rl/2, ..., 1 row lane r < h adds row
+// lane r + h), and row lane 0 writes the chunk's two partial rows.  (Adding
+// the row lanes in order instead, behind one barrier, measured slower on
+// MI355X: (65536, 256) bf16 fwd+bwd 65 -> 80 us.)
 template <int V>
-__device__ __forceinline__ void bn_col_write_partials(float (&s1)[V], float (&s2)[V], int rl, int lane, bool ok,
+__device__ __forceinline__ void bn_col_write_partials(float (&s1)[V], float (&s2)[V], const BnColLane &c, bool ok,
                                                       int j0, const BnColGeom &g, float *__restrict__ partials)
 {
-    __shared__ float red[(kBnColRowLanes - 1) * 2 * V * kBnColLanes];
-    if (rl > 0)
+    __shared__ float red[2 * V * kBnThreads];
+    const int cl = 1 << g.cl_log2;
+    auto slot = [&](int r, int q, int e) { return ((r * 2 + q) * V + e) * cl + c.lane; };
+    for (int h = g.rl >> 1; h >= 1; h >>= 1) {
+        if (c.rl >= h && c.rl < 2 * h)
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-            red[(((rl - 1) * 2 + 0) * V + e) * kBnColLanes + lane] = s1[e];
-            red[(((rl - 1) * 2 + 1) * V + e) * kBnColLanes + lane] = s2[e];
-        }
-    __syncthreads();
-    if (rl != 0 || !ok) return;
+            for (int e = 0; e < V; ++e) {
+                red[slot(c.rl, 0, e)] = s1[e];
+                red[slot(c.rl, 1, e)] = s2[e];
+            }
+        __syncthreads();
+        if (c.rl < h)
 #pragma unroll
-    for (int e = 0; e < V; ++e)
-#pragma unroll
-        for (int k = 1; k < kBnColRowLanes; ++k) {
-            s1[e] += red[(((k - 1) * 2 + 0) * V + e) * kBnColLanes + lane];
-            s2[e] += red[(((k - 1) * 2 + 1) * V + e) * kBnColLanes + lane];
-        }
-    store_vec<float, V>(partials + (size_t)blockIdx.y * g.L + j0, s1);
-    store_vec<float, V>(partials + ((size_t)g.rb + blockIdx.y) * g.L + j0, s2);
+            for (int e = 0; e < V; ++e) {
+                s1[e] += red[slot(c.rl + h, 0, e)];
+                s2[e] += red[slot(c.rl + h, 1, e)];
+            }
+    }
+    if (c.rl != 0 || !ok) return;
+    store_vec<float, V>(partials + (size_t)c.chunk * g.L + j0, s1);
+    store_vec<float, V>(partials + ((size_t)g.rb + c.chunk) * g.L + j0, s2);
 }
 
 template <typename T, int V, int NT>
@@ -719,13 +745,10 @@ __global__ void __launch_bounds__(kBnThreads)
 bn_col_stats_kernel(const T *__restrict__ x, BnColGeom g, float *__restrict__ partials)
 {
     constexpr int U = bn_col_unroll<V>();
-    const int lane = threadIdx.x & (kBnColLanes - 1);
-    const int rl = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kBnColLanes);
-    const int grp = (int)blockIdx.x * kBnColLanes + lane;
-    const bool ok = grp < g.L / V;
-    const int j0 = ok ? grp * V : 0;
-    const int64_t r0 = (int64_t)blockIdx.y * g.rpc;
-    const int64_t r1 = r0 + g.rpc < g.N ? r0 + g.rpc : g.N;
+    const BnColLane c = bn_col_lane(g);
+    const int RL = g.rl;
+    const bool ok = c.grp < g.L / V;
+    const int j0 = ok ? c.grp * V : 0;
     float K[V], s1[V], s2[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) {
@@ -734,12 +757,12 @@ bn_col_stats_kernel(const T *__restrict__ x, BnColGeom g, float *__restrict__ pa
         s2[e] = 0.f;
     }
     if (ok) {
-        int64_t r = r0 + rl;
-        for (; r + (U - 1) * kBnColRowLanes < r1; r += U * kBnColRowLanes) {
+        int64_t r = c.r0 + c.rl;
+        for (; r + (U - 1) * RL < c.r1; r += U * RL) {
             float v[U][V];
 #pragma unroll
             for (int k = 0; k < U; ++k)
-                ld<(NT & kNtReduceLoads) != 0, T, V>(x + (size_t)(r + k * kBnColRowLanes) * g.L + j0, v[k]);
+                ld<(NT & kNtReduceLoads) != 0, T, V>(x + (size_t)(r + k * RL) * g.L + j0, v[k]);
 #pragma unroll
             for (int k = 0; k < U; ++k)
 #pragma unroll
@@ -749,7 +772,7 @@ bn_col_stats_kernel(const T *__restrict__ x, BnColGeom g, float *__restrict__ pa
                     s2[e] = fmaf(d, d, s2[e]);
                 }
         }
-        for (; r < r1; r += kBnColRowLanes) {
+        for (; r < c.r1; r += RL) {
             float v[V];
             ld<(NT & kNtReduceLoads) != 0, T, V>(x + (size_t)r * g.L + j0, v);
 #pragma unroll
@@ -760,38 +783,129 @@ bn_col_stats_kernel(const T *__restrict__ x, BnColGeom g, float *__restrict__ pa
             }
         }
     }
-    bn_col_write_partials<V>(s1, s2, rl, lane, ok, j0, g, partials);
+    bn_col_write_partials<V>(s1, s2, c, ok, j0, g, partials);
 }
 
-// A channel's rb*HW partial pairs in fp64: lane l takes flat indices l,
-// l+64, ... (chunk-major), the butterfly combines the lanes.
-__device__ __forceinline__ void bn_col_sum_partials(const float *__restrict__ partials, const BnColGeom &g, int c,
-                                                    double &s1, double &s2)
+// Finalize of the row layout.  A block of kBnColLanes x RF threads takes k =
+// max(1, kBnColLanes / HW) whole channels, i.e. their k*HW consecutive
+// columns, kBnColLanes columns at a time (one pass unless a forced row
+// layout has planes of more than kBnColLanes elements), by RF row lanes: row
+// lane r adds the chunk sums r, r + RF, ... of its column in fp64, reading
+// rows of partials[2, rb, L] coalesced across the lanes.  The row lanes' sums
+// meet in LDS in row-lane order, and thread t < k adds the column sums of
+// channel c0 + t in column order.  RF = 16 for at least kBnColFinManyChunks
+// chunks, else 4.
+constexpr int kBnColFinManyChunks = 64;
+__host__ __device__ inline int bn_col_fin_channels(const BnColGeom &g)
 {
-    const int lane = threadIdx.x & (kWave - 1);
+    return g.HW >= kBnColLanes ? 1 : kBnColLanes / g.HW;
+}
+
+// Planes of at least kBnColWaveFinalizeHW elements: a wave per channel (four
+// channels per block) adds the channel's rb*HW chunk sums chunk-major, lane l
+// taking l, l + 64, ... (runs of HW consecutive columns, read coalesced), and
+// the butterfly combines the lanes.  RF = 0 selects this team.
+constexpr int kBnColWaveFinalizeHW = 16;
+__device__ __forceinline__ bool bn_col_wave_sums(const float *__restrict__ partials, const BnColGeom &g, int &c,
+                                                 double &s1, double &s2)
+{
+    c = (int)blockIdx.x * (kBnThreads / kWave) + (int)threadIdx.x / kWave;
+    if (c >= g.C) return false;  // a whole wave together; no barrier follows
+    const int lane = (int)threadIdx.x & (kWave - 1);
     const int n = g.rb * g.HW;
     double a = 0.0, b = 0.0;
     for (int i = lane; i < n; i += kWave) {
         const int rbi = (int)g.div_hw.div((uint32_t)i);
-        const int col = c * g.HW + (i - rbi * g.HW);
+        const size_t col = (size_t)c * g.HW + (i - rbi * g.HW);
         a += (double)partials[(size_t)rbi * g.L + col];
         b += (double)partials[((size_t)g.rb + rbi) * g.L + col];
     }
     s1 = wave_sum(a);
     s2 = wave_sum(b);
+    return lane == 0;
 }
 
-template <typename T>
-__global__ void __launch_bounds__(kBnThreads)
+// Returns false for the threads that hold no channel; the others get their
+// channel c and its two sums.  Every thread passes every barrier.
+template <int RF>
+__device__ __forceinline__ bool bn_col_channel_sums(const float *__restrict__ partials, const BnColGeom &g, int &c,
+                                                    double &s1, double &s2)
+{
+    constexpr int kBnColFinRows = RF;
+    __shared__ double red[2][kBnColFinRows][kBnColLanes];
+    const int k = bn_col_fin_channels(g);
+    const int c0 = (int)blockIdx.x * k;
+    const int kc = g.C - c0 < k ? g.C - c0 : k;
+    const int ncol = kc * g.HW;
+    const int lane = (int)threadIdx.x & (kBnColLanes - 1);
+    const int rf = (int)threadIdx.x / kBnColLanes;
+    const int t = (int)threadIdx.x;
+    s1 = 0.0;
+    s2 = 0.0;
+    for (int cb = 0; cb < ncol; cb += kBnColLanes) {
+        const int col = cb + lane;
+        double a = 0.0, b = 0.0;
+        if (col < ncol) {
+            const float *p1 = partials + (size_t)c0 * g.HW + col;
+            const float *p2 = p1 + (size_t)g.rb * g.L;
+            int r = rf;
+            for (; r + 3 * kBnColFinRows < g.rb; r += 4 * kBnColFinRows) {
+                float u[4], v[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    u[i] = p1[(size_t)(r + i * kBnColFinRows) * g.L];
+                    v[i] = p2[(size_t)(r + i * kBnColFinRows) * g.L];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    a += (double)u[i];
+                    b += (double)v[i];
+                }
+            }
+            for (; r < g.rb; r += kBnColFinRows) {
+                a += (double)p1[(size_t)r * g.L];
+                b += (double)p2[(size_t)r * g.L];
+            }
+        }
+        red[0][rf][lane] = a;
+        red[1][rf][lane] = b;
+        __syncthreads();
+        if (rf == 0 && col < ncol) {
+            for (int r = 1; r < kBnColFinRows; ++r) {
+                a += red[0][r][lane];
+                b += red[1][r][lane];
+            }
+            red[0][0][lane] = a;
+            red[1][0][lane] = b;
+        }
+        __syncthreads();
+        if (t < kc) {
+            const int h0 = t * g.HW > cb ? t * g.HW : cb;
+            const int h1 = (t + 1) * g.HW < cb + kBnColLanes ? (t + 1) * g.HW : cb + kBnColLanes;
+            for (int h = h0; h < h1; ++h) {
+                s1 += red[0][0][h - cb];
+                s2 += red[1][0][h - cb];
+            }
+        }
+        __syncthreads();
+    }
+    c = c0 + t;
+    return t < kc;
+}
+
+template <typename T, int RF>
+__global__ void __launch_bounds__(RF == 0 ? kBnThreads : kBnColLanes * RF)
 bn_col_fwd_finalize(const float *__restrict__ partials, const T *__restrict__ x, BnColGeom g,
                     const float *__restrict__ gamma, float *__restrict__ running_mean,
                     float *__restrict__ running_var, float momentum, float eps, float *__restrict__ stats)
 {
-    const int c = blockIdx.x * (kBnThreads / kWave) + (int)threadIdx.x / kWave;
-    if (c >= g.C) return;  // whole wave exits together
+    int c;
     double S1, S2;
-    bn_col_sum_partials(partials, g, c, S1, S2);
-    if ((threadIdx.x & (kWave - 1)) != 0) return;
+    if constexpr (RF == 0) {
+        if (!bn_col_wave_sums(partials, g, c, S1, S2)) return;
+    } else {
+        if (!bn_col_channel_sums<RF>(partials, g, c, S1, S2)) return;
+    }
     float mean, scale;
     fwd_finalize_channel(S1, S2, to_f32(x[(size_t)c * g.HW]), g.C, c, (int64_t)g.N * g.HW, gamma,
                          running_mean, running_var, momentum, eps, true, stats, mean, scale);
@@ -811,46 +925,43 @@ bn_col_apply_kernel(const T *__restrict__ x, T *__restrict__ y, const float *__r
                     const float *__restrict__ beta, BnColGeom g, FwdFinalizeArgs f, float slope)
 {
     constexpr int U = bn_col_unroll<V>();
-    const int lane = threadIdx.x & (kBnColLanes - 1);
-    const int rl = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kBnColLanes);
-    const int grp = (int)blockIdx.x * kBnColLanes + lane;
-    if (grp >= g.L / V) return;
-    const int j0 = grp * V;
+    const BnColLane c = bn_col_lane(g);
+    const int RL = g.rl;
+    if (c.grp >= g.L / V) return;
+    const int j0 = c.grp * V;
     int ch[V];
     bn_col_channels<V>(g, j0, ch);
     float mean[V], scale[V], b[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-        const int c = ch[e];
+        const int cc = ch[e];
         if constexpr (SRC == kApplyRunning) {
             // as bn_apply_kernel: inv_std in fp64, scale rounded once to fp32
-            mean[e] = f.running_mean[c];
-            const double inv_std = 1.0 / sqrt((double)f.running_var[c] + (double)f.eps);
-            scale[e] = (float)((f.gamma ? (double)f.gamma[c] : 1.0) * inv_std);
+            mean[e] = f.running_mean[cc];
+            const double inv_std = 1.0 / sqrt((double)f.running_var[cc] + (double)f.eps);
+            scale[e] = (float)((f.gamma ? (double)f.gamma[cc] : 1.0) * inv_std);
         } else {
-            mean[e] = stats[c];
-            scale[e] = stats[3 * g.C + c];
+            mean[e] = stats[cc];
+            scale[e] = stats[3 * g.C + cc];
         }
-        b[e] = beta ? beta[c] : 0.f;
+        b[e] = beta ? beta[cc] : 0.f;
     }
-    const int64_t r0 = (int64_t)blockIdx.y * g.rpc;
-    const int64_t r1 = r0 + g.rpc < g.N ? r0 + g.rpc : g.N;
     auto out = [&](int64_t r, const float (&v)[V]) {
         float o[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) o[e] = act_fwd<ACT>(fmaf(v[e] - mean[e], scale[e], b[e]), slope);
         st<(NT & kNtStores) != 0, T, V>(y + (size_t)r * g.L + j0, o);
     };
-    int64_t r = r0 + rl;
-    for (; r + (U - 1) * kBnColRowLanes < r1; r += U * kBnColRowLanes) {
+    int64_t r = c.r0 + c.rl;
+    for (; r + (U - 1) * RL < c.r1; r += U * RL) {
         float v[U][V];
 #pragma unroll
         for (int k = 0; k < U; ++k)
-            ld<(NT & kNtEwLoads) != 0, T, V>(x + (size_t)(r + k * kBnColRowLanes) * g.L + j0, v[k]);
+            ld<(NT & kNtEwLoads) != 0, T, V>(x + (size_t)(r + k * RL) * g.L + j0, v[k]);
 #pragma unroll
-        for (int k = 0; k < U; ++k) out(r + k * kBnColRowLanes, v[k]);
+        for (int k = 0; k < U; ++k) out(r + k * RL, v[k]);
     }
-    for (; r < r1; r += kBnColRowLanes) {
+    for (; r < c.r1; r += RL) {
         float v[V];
         ld<(NT & kNtEwLoads) != 0, T, V>(x + (size_t)r * g.L + j0, v);
         out(r, v);
@@ -863,11 +974,10 @@ bn_col_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x, const
                         const float *__restrict__ beta, float slope, BnColGeom g, float *__restrict__ partials)
 {
     constexpr int U = bn_col_unroll<V>();
-    const int lane = threadIdx.x & (kBnColLanes - 1);
-    const int rl = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kBnColLanes);
-    const int grp = (int)blockIdx.x * kBnColLanes + lane;
-    const bool ok = grp < g.L / V;
-    const int j0 = ok ? grp * V : 0;
+    const BnColLane c = bn_col_lane(g);
+    const int RL = g.rl;
+    const bool ok = c.grp < g.L / V;
+    const int j0 = ok ? c.grp * V : 0;
     int ch[V];
     bn_col_channels<V>(g, j0, ch);
     float mean[V], scale[V], bz[V], s1[V], s2[V];
@@ -879,8 +989,6 @@ bn_col_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x, const
         s1[e] = 0.f;
         s2[e] = 0.f;
     }
-    const int64_t r0 = (int64_t)blockIdx.y * g.rpc;
-    const int64_t r1 = r0 + g.rpc < g.N ? r0 + g.rpc : g.N;
     auto add = [&](const float (&vx)[V], const float (&vd)[V]) {
 #pragma unroll
         for (int e = 0; e < V; ++e) {
@@ -891,37 +999,40 @@ bn_col_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x, const
         }
     };
     if (ok) {
-        int64_t r = r0 + rl;
-        for (; r + (U - 1) * kBnColRowLanes < r1; r += U * kBnColRowLanes) {
+        int64_t r = c.r0 + c.rl;
+        for (; r + (U - 1) * RL < c.r1; r += U * RL) {
             float vx[U][V], vd[U][V];
 #pragma unroll
             for (int k = 0; k < U; ++k) {
-                const size_t off = (size_t)(r + k * kBnColRowLanes) * g.L + j0;
+                const size_t off = (size_t)(r + k * RL) * g.L + j0;
                 ld<(NT & kNtReduceLoads) != 0, T, V>(x + off, vx[k]);
                 ld<(NT & kNtReduceLoads) != 0, T, V>(dy + off, vd[k]);
             }
 #pragma unroll
             for (int k = 0; k < U; ++k) add(vx[k], vd[k]);
         }
-        for (; r < r1; r += kBnColRowLanes) {
+        for (; r < c.r1; r += RL) {
             float vx[V], vd[V];
             ld<(NT & kNtReduceLoads) != 0, T, V>(x + (size_t)r * g.L + j0, vx);
             ld<(NT & kNtReduceLoads) != 0, T, V>(dy + (size_t)r * g.L + j0, vd);
             add(vx, vd);
         }
     }
-    bn_col_write_partials<V>(s1, s2, rl, lane, ok, j0, g, partials);
+    bn_col_write_partials<V>(s1, s2, c, ok, j0, g, partials);
 }
 
-__global__ void __launch_bounds__(kBnThreads)
+template <int RF>
+__global__ void __launch_bounds__(RF == 0 ? kBnThreads : kBnColLanes * RF)
 bn_col_bwd_finalize(const float *__restrict__ partials, BnColGeom g, const float *__restrict__ stats,
                     float *__restrict__ grads)
 {
-    const int c = blockIdx.x * (kBnThreads / kWave) + (int)threadIdx.x / kWave;
-    if (c >= g.C) return;
+    int c;
     double Sdy, Sdyxc;
-    bn_col_sum_partials(partials, g, c, Sdy, Sdyxc);
-    if ((threadIdx.x & (kWave - 1)) != 0) return;
+    if constexpr (RF == 0) {
+        if (!bn_col_wave_sums(partials, g, c, Sdy, Sdyxc)) return;
+    } else {
+        if (!bn_col_channel_sums<RF>(partials, g, c, Sdy, Sdyxc)) return;
+    }
     float k1, k2;
     bwd_finalize_channel(Sdy, Sdyxc, g.C, c, (int64_t)g.N * g.HW, stats, true, grads, k1, k2);
 }
@@ -933,25 +1044,22 @@ bn_col_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restric
                  const float *__restrict__ beta, float slope, BnColGeom g)
 {
     constexpr int U = bn_col_unroll<V>();
-    const int lane = threadIdx.x & (kBnColLanes - 1);
-    const int rl = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kBnColLanes);
-    const int grp = (int)blockIdx.x * kBnColLanes + lane;
-    if (grp >= g.L / V) return;
-    const int j0 = grp * V;
+    const BnColLane c = bn_col_lane(g);
+    const int RL = g.rl;
+    if (c.grp >= g.L / V) return;
+    const int j0 = c.grp * V;
     int ch[V];
     bn_col_channels<V>(g, j0, ch);
     float mean[V], scale[V], b[V], k1[V], k2[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-        const int c = ch[e];
-        mean[e] = stats[c];
-        scale[e] = stats[3 * g.C + c];
-        b[e] = (ACT != 0 && beta) ? beta[c] : 0.f;
-        k1[e] = grads[2 * g.C + c];
-        k2[e] = grads[3 * g.C + c];
+        const int cc = ch[e];
+        mean[e] = stats[cc];
+        scale[e] = stats[3 * g.C + cc];
+        b[e] = (ACT != 0 && beta) ? beta[cc] : 0.f;
+        k1[e] = grads[2 * g.C + cc];
+        k2[e] = grads[3 * g.C + cc];
     }
-    const int64_t r0 = (int64_t)blockIdx.y * g.rpc;
-    const int64_t r1 = r0 + g.rpc < g.N ? r0 + g.rpc : g.N;
     auto out = [&](int64_t r, const float (&vx)[V], const float (&vd)[V]) {
         float o[V];
 #pragma unroll
@@ -962,19 +1070,19 @@ bn_col_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restric
         }
         st<(NT & kNtStores) != 0, T, V>(dx + (size_t)r * g.L + j0, o);
     };
-    int64_t r = r0 + rl;
-    for (; r + (U - 1) * kBnColRowLanes < r1; r += U * kBnColRowLanes) {
+    int64_t r = c.r0 + c.rl;
+    for (; r + (U - 1) * RL < c.r1; r += U * RL) {
         float vx[U][V], vd[U][V];
 #pragma unroll
         for (int k = 0; k < U; ++k) {
-            const size_t off = (size_t)(r + k * kBnColRowLanes) * g.L + j0;
+            const size_t off = (size_t)(r + k * RL) * g.L + j0;
             ld<(NT & kNtEwLoads) != 0, T, V>(x + off, vx[k]);
             ld<(NT & kNtEwLoads) != 0, T, V>(dy + off, vd[k]);
         }
 #pragma unroll
-        for (int k = 0; k < U; ++k) out(r + k * kBnColRowLanes, vx[k], vd[k]);
+        for (int k = 0; k < U; ++k) out(r + k * RL, vx[k], vd[k]);
     }
-    for (; r < r1; r += kBnColRowLanes) {
+    for (; r < c.r1; r += RL) {
         float vx[V], vd[V];
         ld<(NT & kNtEwLoads) != 0, T, V>(x + (size_t)r * g.L + j0, vx);
         ld<(NT & kNtEwLoads) != 0, T, V>(dy + (size_t)r * g.L + j0, vd);
@@ -987,7 +1095,7 @@ static hipError_t bn_col_forward_t(const BnCall &a, hipStream_t s)
 {
     const BnColGeom &g = a.colg;
     const T *x = static_cast<const T *>(a.x);
-    const dim3 grid((unsigned)g.strips, (unsigned)g.rb), block(kBnThreads);
+    const dim3 grid((unsigned)(g.strips * g.rb)), block(kBnThreads);
     FwdFinalizeArgs f{a.partials, 1, a.gamma, a.running_mean, a.running_var, a.momentum, a.eps,
                       (int64_t)a.N * a.HW};
     if (a.inference)
@@ -996,9 +1104,19 @@ static hipError_t bn_col_forward_t(const BnCall &a, hipStream_t s)
     hipError_t e = launch(NH_K_BN_STATS, bn_col_stats_kernel<T, V, kBnNtPolicy>, grid, block, 0, s, x, g,
                           a.partials);
     if (e != hipSuccess) return e;
-    e = launch(NH_K_BN_FWD_FINALIZE, bn_col_fwd_finalize<T>, dim3((unsigned)ceil_div(a.C, kBnThreads / kWave)),
-               block, 0, s, (const float *)a.partials, x, g, a.gamma, a.running_mean, a.running_var,
-               a.momentum, a.eps, a.stats);
+    const dim3 fgrid((unsigned)ceil_div(a.C, bn_col_fin_channels(g)));
+    if (g.HW >= kBnColWaveFinalizeHW)
+        e = launch(NH_K_BN_FWD_FINALIZE, bn_col_fwd_finalize<T, 0>, dim3((unsigned)ceil_div(a.C, kBnThreads / kWave)),
+                   block, 0, s, (const float *)a.partials, x, g, a.gamma, a.running_mean, a.running_var, a.momentum,
+                   a.eps, a.stats);
+    else if (g.rb >= kBnColFinManyChunks)
+        e = launch(NH_K_BN_FWD_FINALIZE, bn_col_fwd_finalize<T, 16>, fgrid, dim3(kBnColLanes * 16), 0, s,
+                   (const float *)a.partials, x, g, a.gamma, a.running_mean, a.running_var, a.momentum, a.eps,
+                   a.stats);
+    else
+        e = launch(NH_K_BN_FWD_FINALIZE, bn_col_fwd_finalize<T, 4>, fgrid, dim3(kBnColLanes * 4), 0, s,
+                   (const float *)a.partials, x, g, a.gamma, a.running_mean, a.running_var, a.momentum, a.eps,
+                   a.stats);
     if (e != hipSuccess) return e;
     return launch(NH_K_BN_APPLY, bn_col_apply_kernel<T, V, kApplyStats, kBnNtPolicy, ACT>, grid, block, 0, s, x,
                   static_cast<T *>(a.out), a.stats, a.beta, g, f, a.slope);
@@ -1010,12 +1128,20 @@ static hipError_t bn_col_backward_t(const BnCall &a, hipStream_t s)
     const BnColGeom &g = a.colg;
     const T *x = static_cast<const T *>(a.x);
     const T *dy = static_cast<const T *>(a.dy);
-    const dim3 grid((unsigned)g.strips, (unsigned)g.rb), block(kBnThreads);
+    const dim3 grid((unsigned)(g.strips * g.rb)), block(kBnThreads);
     hipError_t e = launch(NH_K_BN_GRAD_SUMS, bn_col_grad_sums_kernel<T, V, kBnNtPolicy, ACT>, grid, block, 0, s,
                           dy, x, a.stats, a.beta, a.slope, g, a.partials);
     if (e != hipSuccess) return e;
-    e = launch(NH_K_BN_BWD_FINALIZE, bn_col_bwd_finalize, dim3((unsigned)ceil_div(a.C, kBnThreads / kWave)),
-               block, 0, s, (const float *)a.partials, g, a.stats, a.grads);
+    const dim3 fgrid((unsigned)ceil_div(a.C, bn_col_fin_channels(g)));
+    if (g.HW >= kBnColWaveFinalizeHW)
+        e = launch(NH_K_BN_BWD_FINALIZE, bn_col_bwd_finalize<0>, dim3((unsigned)ceil_div(a.C, kBnThreads / kWave)),
+                   block, 0, s, (const float *)a.partials, g, a.stats, a.grads);
+    else if (g.rb >= kBnColFinManyChunks)
+        e = launch(NH_K_BN_BWD_FINALIZE, bn_col_bwd_finalize<16>, fgrid, dim3(kBnColLanes * 16), 0, s,
+                   (const float *)a.partials, g, a.stats, a.grads);
+    else
+        e = launch(NH_K_BN_BWD_FINALIZE, bn_col_bwd_finalize<4>, fgrid, dim3(kBnColLanes * 4), 0, s,
+                   (const float *)a.partials, g, a.stats, a.grads);
     if (e != hipSuccess || a.out == nullptr) return e;
     return launch(NH_K_BN_DX, bn_col_dx_kernel<T, V, kBnNtPolicy, ACT>, grid, block, 0, s, dy, x,
                   static_cast<T *>(a.out), a.stats, a.grads, a.beta, a.slope, g);

@@ -85,24 +85,38 @@ inline BnGeom make_bn_geom(int N, int C, int HW, int vec, int grid_y)
 }
 
 // Small planes: the tensor viewed as [N, L] rows, L = C*HW, column j in
-// channel j/HW.  A launch covers `strips` column strips of kBnColLanes groups
-// of `vec` elements by `rb` chunks of `rpc` rows; the reduction passes write
-// partials[2, rb, L].
-constexpr int kBnColLanes = 64;              // column lanes per block: one wave
-constexpr int64_t kBnColMaxChunks = 256;     // row chunks, at most (the workspace holds them)
-constexpr int64_t kBnColMinChunkRows = 16;   // rows per chunk, at least
+// channel j/HW.  A block is 2^cl_log2 column lanes (the power of two covering
+// the row's groups of `vec` elements, at most kBnColLanes) by rl =
+// kBnThreads / 2^cl_log2 row lanes over one chunk of rpc rows, so every lane
+// has columns even when the row holds fewer than kBnColLanes groups.  A launch
+// is a 1-D grid of strips x rb blocks (bn_col_work maps a block to its strip
+// and chunk).  The reduction passes write partials[2, rb, L].
+constexpr int kBnColLanes = 64;              // column lanes per block, at most: one wave
+constexpr int64_t kBnColMaxChunks = 256;     // row chunks, at most
+constexpr int64_t kBnColMinChunkRows = 16;   // rows per chunk, at least (and at least the row lanes)
 constexpr int64_t kBnColTargetBlocks = 2048; // blocks aimed at: the resident 256-thread slots
+constexpr int kBnColMaxVec = 8;              // widest unit (bf16, 16 bytes)
+constexpr int kXcds = 8;                     // XCDs of the device; blocks are dealt to them by id
 struct BnColGeom {
     int N, C, HW, L;
     int strips, rb, rpc;
-    FastDiv div_hw;  // column -> channel
+    int cl_log2, rl;  // column lanes per block = 1 << cl_log2; row lanes = kBnThreads >> cl_log2
+    FastDiv div_hw;   // column -> channel
 };
 
-// Row chunks the workspace holds for N rows.
-inline int64_t bn_col_chunks_max(int64_t N)
+// Row chunks the workspace holds for N rows of L columns, for every unit
+// width: at most one per kBnColMinChunkRows rows, at most kBnColMaxChunks,
+// and at most kBnColTargetBlocks over the fewest strips any unit width gives
+// (kBnColLanes groups of kBnColMaxVec elements to a strip).
+inline int64_t bn_col_chunks_max(int64_t N, int64_t L)
 {
-    const int64_t c = ceil_div(N, kBnColMinChunkRows);
-    return c < kBnColMaxChunks ? (c < 1 ? 1 : c) : kBnColMaxChunks;
+    int64_t c = ceil_div(N, kBnColMinChunkRows);
+    int64_t s = ceil_div(L, (int64_t)kBnColMaxVec * kBnColLanes);
+    if (s < 1) s = 1;
+    const int64_t t = ceil_div(kBnColTargetBlocks, s);
+    if (c > t) c = t;
+    if (c > kBnColMaxChunks) c = kBnColMaxChunks;
+    return c < 1 ? 1 : c;
 }
 
 inline BnColGeom make_bn_col_geom(int N, int C, int HW, int vec)
@@ -114,13 +128,42 @@ inline BnColGeom make_bn_col_geom(int N, int C, int HW, int vec)
     g.L = C * HW;
     g.div_hw = make_fastdiv((uint32_t)HW);
     const int64_t groups = g.L / vec;
-    g.strips = (int)ceil_div(groups, kBnColLanes);
+    int lg = 0;
+    while ((1 << lg) < groups && (1 << lg) < kBnColLanes) ++lg;
+    g.cl_log2 = lg;
+    g.rl = kBnThreads >> lg;
+    g.strips = (int)ceil_div(groups, (int64_t)1 << lg);
     int64_t rb = ceil_div(kBnColTargetBlocks, g.strips);
-    if (rb > bn_col_chunks_max(N)) rb = bn_col_chunks_max(N);
+    const int64_t by_rows = ceil_div(N, g.rl > kBnColMinChunkRows ? (int64_t)g.rl : kBnColMinChunkRows);
+    if (rb > by_rows) rb = by_rows;
+    if (rb > bn_col_chunks_max(N, g.L)) rb = bn_col_chunks_max(N, g.L);
     if (rb < 1) rb = 1;
     g.rpc = (int)ceil_div(N, rb);
     g.rb = (int)ceil_div(N, g.rpc);
     return g;
+}
+
+// Block id -> (strip, chunk) of the row layout's 1-D grid.  Work items are
+// numbered strip-fastest.  With at least kBnColXcdMinChunks chunks, the
+// blocks that land on one XCD (ids k, k + 8, ...) take consecutive work items,
+// so each XCD streams one contiguous part of the tensor (measured on MI355X:
+// (16384, 2048) bf16 fwd+bwd 123 -> 106 us); with fewer, block id = work
+// item, which is faster there ((64, 2048, 7, 7) bf16).  Every row-layout pass
+// uses this mapping, so an elementwise block re-reads the rows that the
+// reduction block of its id read, on the same XCD.  A bijection on
+// [0, strips * rb).
+constexpr int kBnColXcdMinChunks = 64;
+struct BnColWork {
+    int strip, chunk;
+};
+__host__ __device__ inline BnColWork bn_col_work(const BnColGeom &g, int id)
+{
+    if (g.rb < kBnColXcdMinChunks) return {id % g.strips, id / g.strips};
+    const int total = g.strips * g.rb;
+    const int k = id % kXcds, s = id / kXcds;
+    const int q = total / kXcds, rem = total % kXcds;
+    const int w = k * q + (k < rem ? k : rem) + s;
+    return {w % g.strips, w / g.strips};
 }
 
 struct BnCall {

@@ -88,7 +88,9 @@ const char *nh_last_error(void);
 
 /* ------------------------------------------------------------------------
  * BatchNorm2d, NCHW, statistics per channel over (N, H, W); HW = H*W,
- * M = N*HW elements per channel.
+ * M = N*HW elements per channel.  A channels-last (NHWC) tensor, and
+ * BatchNorm over [N, C], is the case HW = 1 with N*H*W (or N) rows of C
+ * channels: pass it as N' = N*H*W, C, HW = 1.
  * ---------------------------------------------------------------------- */
 
 /* Workspace bytes needed by bn_forward_train / bn_backward for this shape on

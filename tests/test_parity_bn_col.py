@@ -66,7 +66,12 @@ SHAPES = [((4096, 1024, 1, 1), F32, "none"),      # BatchNorm over [N, C]
           ((333, 64, 3, 3), BF16, "none"),         # 3x3 planes
           ((64, 100, 7, 7), BF16, "relu"),         # 7x7 bf16 planes (98 bytes)
           ((17, 5, 1, 1), F32, "none"),            # one partial chunk, one strip
-          ((5000, 3, 1, 1), BF16, "leaky_relu")]   # rows shorter than a group
+          ((5000, 3, 1, 1), BF16, "leaky_relu"),   # rows shorter than a group
+          ((40000, 64, 1, 1), F32, "none"),        # 16 column lanes, 2000 chunks, a block per channel finalizes
+          ((30000, 256, 1, 1), BF16, "relu"),      # 32 column lanes, 1875 chunks
+          ((3000, 8, 1, 1), BF16, "none"),         # one column lane, 256 row lanes
+          ((2000, 2, 3, 1), F32, "none"),          # scalar units, 8 column lanes
+          ((20000, 4, 2, 2), F32, "leaky_relu")]   # 2x2 planes, a block finalizes HW * rb sums
 
 
 @pytest.mark.parametrize("shape,io,act", SHAPES, ids=lambda v: str(v))
