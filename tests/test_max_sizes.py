@@ -116,6 +116,69 @@ def test_bn_max_size(nh, shape, io):
     assert dx_err <= 2e-5 * dx_scale
 
 
+@pytest.mark.parametrize("N,C,dtype", [((1 << 31) // 256 - 1, 256, torch.bfloat16),  # 32 column lanes
+                                        ((1 << 31) // 64 - 1, 64, torch.float32)])    # 16 column lanes
+def test_bn_rows_layout_max_size(nh, N, C, dtype):
+    """BatchNorm over [N, C] (the row layout, HW = 1) just below 2^31
+    elements.  Channel c alternates a_c + b_c, a_c - b_c along the N rows
+    (N odd: the mean moves by b_c/N), and dy = d_c everywhere."""
+    tol = 8e-3 if dtype == torch.bfloat16 else 2e-5
+    print(f"[max size] BatchNorm row layout N={N} C={C} ({N * C} elements) {dtype}", flush=True)
+    cyc = torch.arange(C) % 4
+    a = torch.tensor([0.5, -1.0, 2.0, 3.0], dtype=torch.float64)[cyc]
+    b = torch.tensor([0.25, 0.5, 1.0, 2.0], dtype=torch.float64)[cyc]
+    d = torch.tensor([1.0, -0.5, 2.0, 0.25], dtype=torch.float64)[cyc]
+    gamma = torch.tensor([1.25, 0.75, 1.0, 0.5], dtype=torch.float32)[cyc]
+    beta = torch.tensor([0.1, -0.2, 0.3, 0.0], dtype=torch.float32)[cyc]
+    x = torch.empty((N, C, 1, 1), dtype=dtype, device="cuda")
+    a_d, b_d = a.float().cuda(), b.float().cuda()
+    step = 1 << 20
+    for r0 in range(0, N, step):
+        r1 = min(N, r0 + step)
+        sgn = 1.0 - 2.0 * (torch.arange(r0, r1, device="cuda") % 2).float()
+        x[r0:r1, :, 0, 0] = (a_d[None, :] + b_d[None, :] * sgn[:, None]).to(dtype)
+    M = N
+    mean = a + b * (N % 2) / M
+    ex2 = (a + b) ** 2 * ((N + 1) // 2) / M + (a - b) ** 2 * (N // 2) / M
+    var = ex2 - mean ** 2
+    inv = 1.0 / torch.sqrt(var + EPS)
+    g64, b64 = gamma.double(), beta.double()
+    rm, rv = torch.zeros(C, device="cuda"), torch.ones(C, device="cuda")
+    y, stats = nh.bn_forward_train(x, gamma.cuda(), beta.cuda(), rm, rv, 0.1, EPS)
+    torch.cuda.synchronize()
+    st = stats.cpu().double()
+    for i, (name, want) in enumerate((("mean", mean), ("var", var), ("inv_std", inv),
+                                      ("scale", g64 * inv))):
+        err = float((st[i] - want).abs().max() / want.abs().max())
+        print(f"  stats.{name}: {err:.2e}", flush=True)
+        assert err <= 2e-5
+    want_rm, want_rv = 0.1 * mean, 0.9 + 0.1 * var * M / (M - 1)
+    assert float((rm.cpu().double() - want_rm).abs().max() / want_rm.abs().max()) <= 2e-5
+    assert float((rv.cpu().double() - want_rv).abs().max() / want_rv.abs().max()) <= 2e-5
+    vp = (g64 * (a + b - mean) * inv + b64).float().cuda()
+    vn = (g64 * (a - b - mean) * inv + b64).float().cuda()
+    y2 = y.view(N, C)
+    scale = float(torch.maximum(vp.abs(), vn.abs()).max())
+    err = max(float((y2[0::2].float() - vp[None, :]).abs().max()),
+              float((y2[1::2].float() - vn[None, :]).abs().max()))
+    print(f"  y: normwise error {err / scale:.2e} (tol {tol:.0e})", flush=True)
+    assert err <= tol * scale
+    del y, y2
+    dy = torch.empty_like(x)
+    dy.view(N, C)[:] = d.to(dtype).cuda()[None, :]
+    dx, grads = nh.bn_backward(dy, x, stats)
+    torch.cuda.synchronize()
+    gr = grads.cpu().double()
+    want_db = M * d
+    assert float((gr[1] - want_db).abs().max() / want_db.abs().max()) <= 2e-5
+    dg_scale = (inv * d.abs() * b).max() * M
+    assert float(gr[0].abs().max()) <= 2e-5 * float(dg_scale)
+    dx_scale = float((d.abs() * g64 * inv).max())
+    dx_err = float(dx.float().abs().max())
+    print(f"  dx: max |dx| {dx_err:.2e} vs |dy*scale| {dx_scale:.2e}", flush=True)
+    assert dx_err <= 2e-5 * dx_scale
+
+
 def _rows_input(rows, cols, a_of_row, b, dtype):
     """x[r, j] = a_r + b*(+1, -1, ...)_j on the device."""
     s = _alt(cols, torch.float32)
