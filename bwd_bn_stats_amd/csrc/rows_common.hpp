@@ -58,12 +58,37 @@ __device__ __forceinline__ void team_sum2(float *red, int wave, int lane, float 
     b = sb;
 }
 
+// DPP lane selections inside a row of 16 lanes (gfx9 encodings): quad_perm
+// [1,0,3,2] (lane i <-> i^1) and [2,3,0,1] (i <-> i^2), row_half_mirror
+// (i <-> 7-i in each half row) and row_mirror (i <-> 15-i).
+constexpr int kDppQuadXor1 = 0xB1;
+constexpr int kDppQuadXor2 = 0x4E;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+// v plus the v of the partner lane that CTRL selects.  The partners pair up,
+// so both sides add the same two values.
+template <int CTRL>
+__device__ __forceinline__ float dpp_pair_add(float v)
+{
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 // Sum over the ct lanes of a subgroup (ct a power of two, subgroups aligned
-// to ct inside the wave): a butterfly over xor distances ct/2 .. 1, so every
-// lane of the subgroup ends with the same bits, in a fixed order.
+// to ct inside the wave).  Each step adds a partner lane, so every lane of
+// the subgroup ends with the same bits, in a fixed order: xor 32 and xor 16
+// across rows of 16 lanes (lane permutes through the LDS crossbar), then
+// row_mirror, row_half_mirror, xor 2 and xor 1 inside a row as DPP operand
+// selections, which cost no LDS round trip.  The steps a subgroup needs are
+// uniform branches on ct.
 __device__ __forceinline__ float sub_sum(float v, int ct)
 {
-    for (int o = ct >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    if (ct > 32) v += __shfl_xor(v, 32, kWave);
+    if (ct > 16) v += __shfl_xor(v, 16, kWave);
+    if (ct > 8) v = dpp_pair_add<kDppRowMirror>(v);
+    if (ct > 4) v = dpp_pair_add<kDppRowHalfMirror>(v);
+    if (ct > 2) v = dpp_pair_add<kDppQuadXor2>(v);
+    if (ct > 1) v = dpp_pair_add<kDppQuadXor1>(v);
     return v;
 }
 
