@@ -36,28 +36,6 @@ struct WeightGroup {
 // LDS floats of a team's double-buffered row sums (two quantities per wave).
 constexpr int red_floats(int team) { return 2 * (team / kWave) * 2; }
 
-// Fixed-order sum of the WAVES wave results of a team for two quantities.
-template <int WAVES = kTeamWaves>
-__device__ __forceinline__ void team_sum2(float *red, int wave, int lane, float &a, float &b)
-{
-    a = wave_sum(a);
-    b = wave_sum(b);
-    if (lane == 0) {
-        red[wave * 2 + 0] = a;
-        red[wave * 2 + 1] = b;
-    }
-    lds_barrier();
-    float sa = red[0];
-    float sb = red[1];
-#pragma unroll
-    for (int w = 1; w < WAVES; ++w) {
-        sa += red[w * 2 + 0];
-        sb += red[w * 2 + 1];
-    }
-    a = sa;
-    b = sb;
-}
-
 // DPP lane selections inside a row of 16 lanes (gfx9 encodings): quad_perm
 // [1,0,3,2] (lane i <-> i^1) and [2,3,0,1] (i <-> i^2), row_half_mirror
 // (i <-> 7-i in each half row) and row_mirror (i <-> 15-i).
@@ -72,6 +50,46 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_pair_add(float v)
 {
     return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wave, the same in every lane: DPP steps give
+// every lane its 16-lane row's sum, then the four row sums (lanes 0, 16, 32,
+// 48) are added pairwise, (r0 + r1) + (r2 + r3).  All lanes must be active.
+__device__ __forceinline__ float wave_total(float v)
+{
+    v = dpp_pair_add<kDppRowMirror>(v);
+    v = dpp_pair_add<kDppRowHalfMirror>(v);
+    v = dpp_pair_add<kDppQuadXor2>(v);
+    v = dpp_pair_add<kDppQuadXor1>(v);
+    const int u = __float_as_int(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(u, 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(u, 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(u, 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(u, 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// Fixed-order sum of the WAVES wave results of a team for two quantities.
+// Called by every thread of the block.
+template <int WAVES = kTeamWaves>
+__device__ __forceinline__ void team_sum2(float *red, int wave, int lane, float &a, float &b)
+{
+    a = wave_total(a);
+    b = wave_total(b);
+    if (lane == 0) {
+        red[wave * 2 + 0] = a;
+        red[wave * 2 + 1] = b;
+    }
+    lds_barrier();
+    float sa = red[0];
+    float sb = red[1];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) {
+        sa += red[w * 2 + 0];
+        sb += red[w * 2 + 1];
+    }
+    a = sa;
+    b = sb;
 }
 
 // Sum over the ct lanes of a subgroup (ct a power of two, subgroups aligned
