@@ -149,7 +149,8 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
 }
 
 // ---- RMSNorm, vector path ----------------------------------------------------
-constexpr int kRmsKeepGMinGroups = 4;  // groups per thread (see do_row)
+constexpr int kRmsKeepGMinGroups = 4;      // groups per thread (see do_row)
+constexpr int kRmsKeepGMaxRowBytes = 128;  // x and dy bytes per thread and row
 // TEAMS row teams per block (1 or 2), as in the LayerNorm kernel.
 template <typename T, int VEC, int MAXG, int TEAM, int D, int TEAMS = 1>
 __global__ void __launch_bounds__(TEAM * TEAMS, kRowsBwdWavesPerSimd)
@@ -204,13 +205,16 @@ rms_rows_kernel(const T *__restrict__ dy, const T *__restrict__ x,
         b.rms = rms != nullptr ? rms[rc] : 0.f;
     };
 
-    // Rows of at least kRmsKeepGMinGroups groups per thread keep g = dy*w from
-    // the row sums for dx and skip sum x^2 when rms is given (a uniform branch:
-    // two copies of the loop); shorter rows recompute g, as the extra registers
-    // and copies cost more than they save there (measured on MI355X, same
-    // results bit for bit: 2048x8192 bf16 26.2 -> 25.3 us, but 8192x1600 bf16
-    // 20.4 -> 21.2 us).
-    constexpr bool KEEP_G = MAXG >= kRmsKeepGMinGroups;
+    // Rows of at least kRmsKeepGMinGroups groups per thread, whose x and dy
+    // take at most kRmsKeepGMaxRowBytes bytes of registers per thread, keep
+    // g = dy*w from the row sums for dx and skip sum x^2 when rms is given (a
+    // uniform branch: two copies of the loop).  Other rows recompute g: short
+    // rows gain nothing from it, and larger row buffers spill.  Measured on
+    // MI355X, same results bit for bit: 2048x8192 bf16 26.2 -> 25.3 us and
+    // 4096x4096 fp32 37.0 -> 36.4 us, but 8192x1600 bf16 20.4 -> 21.2 us and
+    // 2048x8192 fp32 40.0 -> 58.5 us.
+    constexpr bool KEEP_G =
+        MAXG >= kRmsKeepGMinGroups && MAXG * VEC * 2 * (int)sizeof(T) <= kRmsKeepGMaxRowBytes;
     auto do_row = [&](const RowBuf &b, int it) {
         const int r = row_of(it);
         const bool active = r < rows;
