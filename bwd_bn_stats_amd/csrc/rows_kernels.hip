@@ -34,6 +34,7 @@
 namespace nh {
 
 // ---- LayerNorm, vector path ----------------------------------------------------
+constexpr int kLnKeepMaxElems = 16;  // row elements per thread (see do_row)
 // D: software-pipeline depth.  While a team reduces and writes row i, the
 // loads of its rows i+1 .. i+D-1 are already in flight (D register sets,
 // used in rotation), so each team keeps D rows of HBM traffic outstanding
@@ -101,11 +102,16 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
         b.rs = rstd[rc];
     };
 
+    // Rows of at most kLnKeepMaxElems elements per thread keep xhat and
+    // g = dy*w from the row sums for dx instead of recomputing them (same
+    // values, so the same results bit for bit).
+    constexpr bool KEEP = MAXG * VEC <= kLnKeepMaxElems;
     auto do_row = [&](const RowBuf &b, int it) {
         const int r = row_of(it);
         const bool active = r < rows;
         const float mu = b.mu, rs = b.rs;
         float a = 0.f, bb = 0.f;
+        float kx[KEEP ? MAXG : 1][VEC], kg[KEEP ? MAXG : 1][VEC];
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
             const int grp = tt + k * TEAM;
@@ -115,10 +121,20 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
                     const float d = b.d[k].get(e);
                     const float xh = (b.x[k].get(e) - mu) * rs;
                     const float g = d * wv[k].get(e);
+                    if constexpr (KEEP) {
+                        kx[k][e] = xh;
+                        kg[k][e] = g;
+                    }
                     a += g;
                     bb = fmaf(g, xh, bb);
                     p[0][k][e] = fmaf(d, xh, p[0][k][e]);
                     p[1][k][e] += d;
+                }
+            } else if constexpr (KEEP) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    kx[k][e] = 0.f;
+                    kg[k][e] = 0.f;
                 }
             }
         }
@@ -133,8 +149,14 @@ ln_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
                     float o[VEC];
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) {
-                        const float xh = (b.x[k].get(e) - mu) * rs;
-                        const float g = b.d[k].get(e) * wv[k].get(e);
+                        float xh, g;
+                        if constexpr (KEEP) {
+                            xh = kx[k][e];
+                            g = kg[k][e];
+                        } else {
+                            xh = (b.x[k].get(e) - mu) * rs;
+                            g = b.d[k].get(e) * wv[k].get(e);
+                        }
                         o[e] = rs * fmaf(-xh, cb, g - ca);
                     }
                     st<true, TDX, VEC>(dx + rowoff + grp * VEC, o);
