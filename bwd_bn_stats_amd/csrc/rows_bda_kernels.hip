@@ -99,11 +99,16 @@ bda_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
         b.rs = rstd[rc];
     };
 
+    // As in the LayerNorm kernel: rows of at most kLnKeepMaxElems elements per
+    // thread keep xhat and g = dy*w from the row sums, so dh rounds exactly as
+    // layernorm_backward's dx does.
+    constexpr bool KEEP = MAXG * VEC <= kLnKeepMaxElems;
     auto do_row = [&](const RowBuf &b, int it) {
         const int r = row_of(it);
         const bool active = r < rows;
         const float mu = b.mu, rs = b.rs;
         float sa = 0.f, sb = 0.f;
+        float kx[KEEP ? MAXG : 1][VEC], kg[KEEP ? MAXG : 1][VEC];
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
             const int grp = tt + k * TEAM;
@@ -113,10 +118,20 @@ bda_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
                     const float d = b.d[k].get(e);
                     const float xh = (b.x[k].get(e) - mu) * rs;
                     const float g = d * wv[k].get(e);
+                    if constexpr (KEEP) {
+                        kx[k][e] = xh;
+                        kg[k][e] = g;
+                    }
                     sa += g;
                     sb = fmaf(g, xh, sb);
                     p[0][k][e] = fmaf(d, xh, p[0][k][e]);
                     p[1][k][e] += d;
+                }
+            } else if constexpr (KEEP) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    kx[k][e] = 0.f;
+                    kg[k][e] = 0.f;
                 }
             }
         }
@@ -131,8 +146,14 @@ bda_rows_kernel(const TDY *__restrict__ dy, const TX *__restrict__ x,
                 float hv[VEC], av[VEC];
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    const float xh = (b.x[k].get(e) - mu) * rs;
-                    const float g = b.d[k].get(e) * wv[k].get(e);
+                    float xh, g;
+                    if constexpr (KEEP) {
+                        xh = kx[k][e];
+                        g = kg[k][e];
+                    } else {
+                        xh = (b.x[k].get(e) - mu) * rs;
+                        g = b.d[k].get(e) * wv[k].get(e);
+                    }
                     hv[e] = rs * fmaf(-xh, cb, g - ca) + b.r[k].get(e);
                     av[e] = hv[e] * scale * (has_mask ? b.m[k].get(e) : 1.f);
                     p[2][k][e] += av[e];

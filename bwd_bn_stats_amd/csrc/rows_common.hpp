@@ -33,6 +33,10 @@ struct WeightGroup {
     __device__ __forceinline__ float get(int e) const { return v[e]; }
 };
 
+// LayerNorm-type row kernels keep xhat and g = dy*w from the row sums for
+// rows of at most this many elements per thread.
+constexpr int kLnKeepMaxElems = 16;
+
 // LDS floats of a team's double-buffered row sums (two quantities per wave).
 constexpr int red_floats(int team) { return 2 * (team / kWave) * 2; }
 

@@ -34,7 +34,6 @@
 namespace nh {
 
 // ---- LayerNorm, vector path ----------------------------------------------------
-constexpr int kLnKeepMaxElems = 16;  // row elements per thread (see do_row)
 // D: software-pipeline depth.  While a team reduces and writes row i, the
 // loads of its rows i+1 .. i+D-1 are already in flight (D register sets,
 // used in rotation), so each team keeps D rows of HBM traffic outstanding
