@@ -865,6 +865,18 @@ def main():
             cp = bench_copy(nh, torch, o["kernels"][kern]["bytes"] // 32 * 16, max(10, K // 2), W)
             o["copy_floor"] = {"gbs": round(cp["gbs"], 1), "avg_us": round(cp["avg_us"], 3)}
             o["kernels"][kern]["frac_of_copy_floor"] = round(o["kernels"][kern]["gbs"] / cp["gbs"], 4)
+        # the row backwards (two reads, one write per element) against the
+        # calibration add (two fp32 reads, one write) of the same total bytes
+        for name, kern in (("ln_bwd_16x512x1600", "ln_rows"), ("rms_bwd_2048x8192_bf16_saved_rms", "rms_rows"),
+                           ("rms_bwd_2048x8192_f32_saved_rms", "rms_rows")):
+            o = others.get(name)
+            if not o or kern not in o["kernels"] or not o["kernels"][kern].get("bytes"):
+                continue
+            log(f"[bench] add floor for {name}")
+            ad = bench_calib(nh, torch, o["kernels"][kern]["bytes"] // 12 // 1024 * 1024, max(10, K // 2), W)
+            o["add_floor"] = {"gbs": round(ad["gbs"], 1), "avg_us": round(ad["avg_us"], 3)}
+            o["kernels"][kern]["frac_of_add_floor"] = round(o["kernels"][kern]["gbs"] / ad["gbs"], 4)
+            o["call_frac_of_add_floor"] = round(o["gbs"] / ad["gbs"], 4)
 
     # dominant kernel of the step: the largest share of the step's kernel time
     per = cold["kernels"]
