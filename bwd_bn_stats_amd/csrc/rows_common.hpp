@@ -3,6 +3,8 @@
 // and its fixed-order row sums.
 #pragma once
 
+#include <type_traits>
+
 #include "nh_rows.hpp"
 
 namespace nh {
