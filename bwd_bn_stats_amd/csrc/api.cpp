@@ -530,10 +530,11 @@ static nh_status check_act(nh_act act, float slope)
     return NH_OK;
 }
 
-nh_status bn_act_forward_train(const void *x, void *y, nh_dtype io, int64_t N, int64_t C, int64_t HW,
-                               const float *gamma, const float *beta, float *running_mean,
-                               float *running_var, float momentum, float eps, nh_act act, float slope,
-                               float *stats, void *ws, size_t ws_bytes, void *stream)
+// The BatchNorm training forward, whole (stage 0) or one of its two stages.
+static nh_status bn_forward_impl(int stage, const void *x, void *y, nh_dtype io, int64_t N, int64_t C,
+                                 int64_t HW, const float *gamma, const float *beta, float *running_mean,
+                                 float *running_var, float momentum, float eps, nh_act act, float slope,
+                                 float *stats, void *ws, size_t ws_bytes, void *stream)
 {
     if (!valid_dtype(io)) return fail(NH_ERR_DTYPE, "io dtype %d", (int)io);
     nh_status st = bn_check_shape(N, C, HW);
@@ -572,6 +573,7 @@ nh_status bn_act_forward_train(const void *x, void *y, nh_dtype io, int64_t N, i
     a.slope = slope;
     a.stats = stats;
     a.partials = static_cast<float *>(ws);
+    a.stage = stage;
     a.separate_finalize = g_override_bn_finalize_kernels.load() != 0;
     a.channel_fused = bn_channel_fused(N * (HW / a.vec), C, bn_slots(d));
     a.channel_threads = bn_channel_threads(N * (HW / a.vec), C, bn_slots(d));
@@ -579,6 +581,25 @@ nh_status bn_act_forward_train(const void *x, void *y, nh_dtype io, int64_t N, i
     hipError_t e = bn_forward_launch(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "bn_forward_train launch");
     return ok();
+}
+
+nh_status bn_act_forward_train(const void *x, void *y, nh_dtype io, int64_t N, int64_t C, int64_t HW,
+                               const float *gamma, const float *beta, float *running_mean,
+                               float *running_var, float momentum, float eps, nh_act act, float slope,
+                               float *stats, void *ws, size_t ws_bytes, void *stream)
+{
+    return bn_forward_impl(0, x, y, io, N, C, HW, gamma, beta, running_mean, running_var, momentum, eps, act,
+                           slope, stats, ws, ws_bytes, stream);
+}
+
+nh_status bn_forward_train_stage(int stage, const void *x, void *y, nh_dtype io, int64_t N, int64_t C,
+                                 int64_t HW, const float *gamma, const float *beta, float *running_mean,
+                                 float *running_var, float momentum, float eps, float *stats, void *ws,
+                                 size_t ws_bytes, void *stream)
+{
+    if (stage != 1 && stage != 2) return fail(NH_ERR_ARG, "stage must be 1 or 2 (got %d)", stage);
+    return bn_forward_impl(stage, x, y, io, N, C, HW, gamma, beta, running_mean, running_var, momentum, eps,
+                           NH_ACT_NONE, 0.f, stats, ws, ws_bytes, stream);
 }
 
 nh_status bn_forward_train(const void *x, void *y, nh_dtype io, int64_t N, int64_t C, int64_t HW,
@@ -590,9 +611,10 @@ nh_status bn_forward_train(const void *x, void *y, nh_dtype io, int64_t N, int64
                                 eps, NH_ACT_NONE, 0.f, stats, ws, ws_bytes, stream);
 }
 
-nh_status bn_act_backward(const void *dy, const void *x, nh_dtype io, int64_t N, int64_t C, int64_t HW,
-                          const float *stats, const float *beta, nh_act act, float slope, void *dx,
-                          float *grads, void *ws, size_t ws_bytes, void *stream)
+// The BatchNorm training backward, whole (stage 0) or one of its two stages.
+static nh_status bn_backward_impl(int stage, const void *dy, const void *x, nh_dtype io, int64_t N, int64_t C,
+                                  int64_t HW, const float *stats, const float *beta, nh_act act, float slope,
+                                  void *dx, float *grads, void *ws, size_t ws_bytes, void *stream)
 {
     if (!valid_dtype(io)) return fail(NH_ERR_DTYPE, "io dtype %d", (int)io);
     nh_status st = bn_check_shape(N, C, HW);
@@ -623,6 +645,7 @@ nh_status bn_act_backward(const void *dy, const void *x, nh_dtype io, int64_t N,
     a.stats = const_cast<float *>(stats);
     a.grads = grads;
     a.partials = static_cast<float *>(ws);
+    a.stage = stage;
     a.separate_finalize = g_override_bn_finalize_kernels.load() != 0;
     a.channel_fused = bn_channel_fused(N * (HW / a.vec), C, bn_slots(d));
     a.channel_threads = bn_channel_threads(N * (HW / a.vec), C, bn_slots(d));
@@ -630,6 +653,22 @@ nh_status bn_act_backward(const void *dy, const void *x, nh_dtype io, int64_t N,
     hipError_t e = bn_backward_launch(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "bn_backward launch");
     return ok();
+}
+
+nh_status bn_act_backward(const void *dy, const void *x, nh_dtype io, int64_t N, int64_t C, int64_t HW,
+                          const float *stats, const float *beta, nh_act act, float slope, void *dx,
+                          float *grads, void *ws, size_t ws_bytes, void *stream)
+{
+    return bn_backward_impl(0, dy, x, io, N, C, HW, stats, beta, act, slope, dx, grads, ws, ws_bytes, stream);
+}
+
+nh_status bn_backward_stage(int stage, const void *dy, const void *x, nh_dtype io, int64_t N, int64_t C,
+                            int64_t HW, const float *stats, void *dx, float *grads, void *ws, size_t ws_bytes,
+                            void *stream)
+{
+    if (stage != 1 && stage != 2) return fail(NH_ERR_ARG, "stage must be 1 or 2 (got %d)", stage);
+    return bn_backward_impl(stage, dy, x, io, N, C, HW, stats, nullptr, NH_ACT_NONE, 0.f, dx, grads, ws,
+                            ws_bytes, stream);
 }
 
 nh_status bn_backward(const void *dy, const void *x, nh_dtype io, int64_t N, int64_t C, int64_t HW,

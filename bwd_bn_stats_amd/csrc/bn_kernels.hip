@@ -71,6 +71,18 @@ enum : int { kNtReduceLoads = 1, kNtEwLoads = 2, kNtStores = 4 };
 #endif
 constexpr int kBnNtPolicy = NH_BN_NT_POLICY;
 
+// Loads a unit into its storage form (bf16 stays packed, two per register):
+// the widening to fp32 happens where the values are used, so a conditional
+// load's block holds the load alone and the unit's loads of a sweep all stay
+// in flight together, instead of each waiting for its data before the next
+// one issues.
+template <bool NT, typename T, int V>
+__device__ __forceinline__ void ldr(Raw<T, V> &r, const T *p)
+{
+    if constexpr (NT) r.load_nt(p);
+    else r.load(p);
+}
+
 // Activations: 0 none, 1 ReLU, 2 LeakyReLU.
 template <int ACT>
 __device__ __forceinline__ float act_fwd(float z, float slope)
@@ -143,6 +155,24 @@ __device__ __forceinline__ void block_sum2_tb(float &a, float &b)
     }
 }
 
+// The shift x[0, c, 0, 0] of the forward reductions, read with a vector
+// memory load: as a scalar load it would be waited for, together with the
+// kernel arguments loaded after it, before the block's first loads of x were
+// issued, putting one more memory round trip in every block's path.
+__device__ __forceinline__ float load_shift(const float *p)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p, 4u), 0, 0, 0));
+}
+__device__ __forceinline__ float load_shift(const uint16_t *p)
+{
+    // the bf16 bits straight into the high half of a zeroed register: the
+    // fp32 value with no instruction between the load and its first use
+    typedef short short2_t __attribute__((ext_vector_type(2)));
+    short2_t t = {0, 0};
+    t.y = (short)__builtin_amdgcn_raw_buffer_load_b16(make_rsrc(p, 2u), 0, 0, 0);
+    return __builtin_bit_cast(float, t);
+}
+
 // ---- forward reduction: shifted one-pass sums ------------------------------
 template <typename T, int V, int NT>
 __global__ void __launch_bounds__(kBnThreads)
@@ -154,31 +184,43 @@ bn_stats_kernel(const T *__restrict__ x, BnGeom g, float *__restrict__ partials)
     // and the loop index runs up to a stride past the last one.
     const uint32_t u0 = (uint32_t)yb * (uint32_t)g.upb;
     const uint32_t u1 = min(u0 + (uint32_t)g.upb, (uint32_t)g.units);
-    // The shift: the channel's first element, x[0, c, 0, 0].
-    const float K = to_f32(x[c * g.HW]);
 
     float s1[kBnUnroll], s2[kBnUnroll];
 #pragma unroll
     for (int k = 0; k < kBnUnroll; ++k) { s1[k] = 0.f; s2[k] = 0.f; }
 
-    for (uint32_t base = u0 + threadIdx.x; base < u1; base += kBnThreads * kBnUnroll) {
-        float v[kBnUnroll][V];
+    // The first sweep's loads go out before the shift's, so that no load of
+    // x waits for the shift (loads complete in issue order).
+    // The first sweep's loads go out before the shift's, so that no load of
+    // x waits for the shift (loads complete in issue order).
+    uint32_t base = u0 + threadIdx.x;
+    Raw<T, V> v[kBnUnroll];
 #pragma unroll
-        for (int k = 0; k < kBnUnroll; ++k) {
-            const uint32_t u = base + k * kBnThreads;
-            if (u < u1) ld<(NT & kNtReduceLoads) != 0, T, V>(x + bn_unit_offset<V>(g, c, u), v[k]);
-        }
+    for (int k = 0; k < kBnUnroll; ++k) {
+        const uint32_t u = base + k * kBnThreads;
+        if (u < u1) ldr<(NT & kNtReduceLoads) != 0>(v[k], x + bn_unit_offset<V>(g, c, u));
+    }
+    // The shift: the channel's first element, x[0, c, 0, 0].
+    const float K = load_shift(x + c * g.HW);
+    while (base < u1) {
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
             const uint32_t u = base + k * kBnThreads;
             if (u < u1) {
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
-                    const float d = v[k][e] - K;
+                    const float d = v[k].get(e) - K;
                     s1[k] += d;
                     s2[k] = fmaf(d, d, s2[k]);
                 }
             }
+        }
+        base += kBnThreads * kBnUnroll;
+        if (base >= u1) break;
+#pragma unroll
+        for (int k = 0; k < kBnUnroll; ++k) {
+            const uint32_t u = base + k * kBnThreads;
+            if (u < u1) ldr<(NT & kNtReduceLoads) != 0>(v[k], x + bn_unit_offset<V>(g, c, u));
         }
     }
     float a = s1[0], b = s2[0];
@@ -217,14 +259,14 @@ bn_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x,
     for (int k = 0; k < kBnUnroll; ++k) { s1[k] = 0.f; s2[k] = 0.f; }
 
     for (uint32_t base = u0 + threadIdx.x; base < u1; base += kBnThreads * kBnUnroll) {
-        float vx[kBnUnroll][V], vd[kBnUnroll][V];
+        Raw<T, V> vx[kBnUnroll], vd[kBnUnroll];
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
             const uint32_t u = base + k * kBnThreads;
             if (u < u1) {
                 const int off = bn_unit_offset<V>(g, c, u);
-                ld<(NT & kNtReduceLoads) != 0, T, V>(x + off, vx[k]);
-                ld<(NT & kNtReduceLoads) != 0, T, V>(dy + off, vd[k]);
+                ldr<(NT & kNtReduceLoads) != 0>(vx[k], x + off);
+                ldr<(NT & kNtReduceLoads) != 0>(vd[k], dy + off);
             }
         }
 #pragma unroll
@@ -233,8 +275,8 @@ bn_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x,
             if (u < u1) {
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
-                    const float xc = vx[k][e] - mean;
-                    const float dz = act_bwd<ACT>(vd[k][e], fmaf(xc, scale, bz), slope);
+                    const float xc = vx[k].get(e) - mean;
+                    const float dz = act_bwd<ACT>(vd[k].get(e), fmaf(xc, scale, bz), slope);
                     s1[k] += dz;
                     s2[k] = fmaf(dz, xc, s2[k]);
                 }
@@ -385,13 +427,13 @@ bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ 
     const float b = beta ? beta[c] : 0.f;
 
     uint32_t base = u0 + threadIdx.x;
-    float v[kBnUnroll][V];
+    Raw<T, V> v[kBnUnroll];
     int off[kBnUnroll];
 #pragma unroll
     for (int k = 0; k < kBnUnroll; ++k) {
         const uint32_t u = base + k * kBnThreads;
         off[k] = bn_unit_offset<V>(g, c, u);
-        if (u < u1) ld<(NT & kNtEwLoads) != 0, T, V>(x + off[k], v[k]);
+        if (u < u1) ldr<(NT & kNtEwLoads) != 0>(v[k], x + off[k]);
     }
 
     float mean, scale;
@@ -427,7 +469,7 @@ bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ 
             if (u < u1) {
                 float o[V];
 #pragma unroll
-                for (int e = 0; e < V; ++e) o[e] = act_fwd<ACT>(fmaf(v[k][e] - mean, scale, b), slope);
+                for (int e = 0; e < V; ++e) o[e] = act_fwd<ACT>(fmaf(v[k].get(e) - mean, scale, b), slope);
                 st<(NT & kNtStores) != 0, T, V>(y + off[k], o);
             }
         }
@@ -437,7 +479,7 @@ bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ 
         for (int k = 0; k < kBnUnroll; ++k) {
             const uint32_t u = base + k * kBnThreads;
             off[k] = bn_unit_offset<V>(g, c, u);
-            if (u < u1) ld<(NT & kNtEwLoads) != 0, T, V>(x + off[k], v[k]);
+            if (u < u1) ldr<(NT & kNtEwLoads) != 0>(v[k], x + off[k]);
         }
     }
 }
@@ -460,15 +502,15 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
     const float b = (ACT != 0 && beta) ? beta[c] : 0.f;
 
     uint32_t base = u0 + threadIdx.x;
-    float vx[kBnUnroll][V], vd[kBnUnroll][V];
+    Raw<T, V> vx[kBnUnroll], vd[kBnUnroll];
     int off[kBnUnroll];
 #pragma unroll
     for (int k = 0; k < kBnUnroll; ++k) {
         const uint32_t u = base + k * kBnThreads;
         off[k] = bn_unit_offset<V>(g, c, u);
         if (u < u1) {
-            ld<(NT & kNtEwLoads) != 0, T, V>(x + off[k], vx[k]);
-            ld<(NT & kNtEwLoads) != 0, T, V>(dy + off[k], vd[k]);
+            ldr<(NT & kNtEwLoads) != 0>(vx[k], x + off[k]);
+            ldr<(NT & kNtEwLoads) != 0>(vd[k], dy + off[k]);
         }
     }
 
@@ -497,8 +539,8 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
                 float o[V];
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
-                    const float xc = vx[k][e] - mean;
-                    const float dz = act_bwd<ACT>(vd[k][e], fmaf(xc, scale, b), slope);
+                    const float xc = vx[k].get(e) - mean;
+                    const float dz = act_bwd<ACT>(vd[k].get(e), fmaf(xc, scale, b), slope);
                     o[e] = fmaf(dz, scale, fmaf(xc, k1, k2));
                 }
                 st<(NT & kNtStores) != 0, T, V>(dx + off[k], o);
@@ -511,8 +553,8 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
             const uint32_t u = base + k * kBnThreads;
             off[k] = bn_unit_offset<V>(g, c, u);
             if (u < u1) {
-                ld<(NT & kNtEwLoads) != 0, T, V>(x + off[k], vx[k]);
-                ld<(NT & kNtEwLoads) != 0, T, V>(dy + off[k], vd[k]);
+                ldr<(NT & kNtEwLoads) != 0>(vx[k], x + off[k]);
+                ldr<(NT & kNtEwLoads) != 0>(vd[k], dy + off[k]);
             }
         }
     }
@@ -1101,9 +1143,11 @@ static hipError_t bn_col_forward_t(const BnCall &a, hipStream_t s)
     if (a.inference)
         return launch(NH_K_BN_INFER, bn_col_apply_kernel<T, V, kApplyRunning, kBnNtPolicy, ACT>, grid, block, 0,
                       s, x, static_cast<T *>(a.out), a.stats, a.beta, g, f, a.slope);
-    hipError_t e = launch(NH_K_BN_STATS, bn_col_stats_kernel<T, V, kBnNtPolicy>, grid, block, 0, s, x, g,
-                          a.partials);
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (a.stage != 2) {
+        e = launch(NH_K_BN_STATS, bn_col_stats_kernel<T, V, kBnNtPolicy>, grid, block, 0, s, x, g, a.partials);
+        if (e != hipSuccess || a.stage == 1) return e;
+    }
     const dim3 fgrid((unsigned)ceil_div(a.C, bn_col_fin_channels(g)));
     if (g.HW >= kBnColWaveFinalizeHW)
         e = launch(NH_K_BN_FWD_FINALIZE, bn_col_fwd_finalize<T, 0>, dim3((unsigned)ceil_div(a.C, kBnThreads / kWave)),
@@ -1129,9 +1173,12 @@ static hipError_t bn_col_backward_t(const BnCall &a, hipStream_t s)
     const T *x = static_cast<const T *>(a.x);
     const T *dy = static_cast<const T *>(a.dy);
     const dim3 grid((unsigned)(g.strips * g.rb)), block(kBnThreads);
-    hipError_t e = launch(NH_K_BN_GRAD_SUMS, bn_col_grad_sums_kernel<T, V, kBnNtPolicy, ACT>, grid, block, 0, s,
-                          dy, x, a.stats, a.beta, a.slope, g, a.partials);
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (a.stage != 2) {
+        e = launch(NH_K_BN_GRAD_SUMS, bn_col_grad_sums_kernel<T, V, kBnNtPolicy, ACT>, grid, block, 0, s, dy, x,
+                   a.stats, a.beta, a.slope, g, a.partials);
+        if (e != hipSuccess || a.stage == 1) return e;
+    }
     const dim3 fgrid((unsigned)ceil_div(a.C, bn_col_fin_channels(g)));
     if (g.HW >= kBnColWaveFinalizeHW)
         e = launch(NH_K_BN_BWD_FINALIZE, bn_col_bwd_finalize<0>, dim3((unsigned)ceil_div(a.C, kBnThreads / kWave)),
@@ -1164,6 +1211,8 @@ static hipError_t bn_forward_t(const BnCall &a, hipStream_t s)
         return launch(NH_K_BN_INFER, bn_apply_kernel<T, V, kApplyRunning, kBnNtPolicy, ACT>, egrid, block,
                       0, s, x, static_cast<T *>(a.out), a.stats, a.beta, ge, f, a.slope);
     if (a.channel_fused) {
+        // one kernel per direction: it runs as the second stage
+        if (a.stage == 1) return hipSuccess;
         const BnGeom g1 = make_bn_geom(a.N, a.C, a.HW, a.vec, 1);
         if (a.channel_threads == kBnChannelBigBlock)
             return launch(NH_K_BN_FWD_CHANNEL, bn_fwd_channel_kernel<T, V, kBnNtPolicy, ACT, kBnChannelBigBlock>,
@@ -1173,9 +1222,11 @@ static hipError_t bn_forward_t(const BnCall &a, hipStream_t s)
                       dim3((unsigned)a.C), block, 0, s, x, static_cast<T *>(a.out), a.stats, a.beta, g1, f,
                       a.slope);
     }
-    hipError_t e = launch(NH_K_BN_STATS, bn_stats_kernel<T, V, kBnNtPolicy>, rgrid, block, 0, s, x, gr,
-                          a.partials);
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (a.stage != 2) {
+        e = launch(NH_K_BN_STATS, bn_stats_kernel<T, V, kBnNtPolicy>, rgrid, block, 0, s, x, gr, a.partials);
+        if (e != hipSuccess || a.stage == 1) return e;
+    }
     if (a.separate_finalize) {
         const dim3 fgrid((unsigned)ceil_div(a.C, kBnThreads / kWave));
         e = launch(NH_K_BN_FWD_FINALIZE, bn_fwd_finalize, fgrid, block, 0, s, a.partials,
@@ -1199,6 +1250,7 @@ static hipError_t bn_backward_t(const BnCall &a, hipStream_t s)
     const dim3 rgrid((unsigned)(a.C * a.grid_y)), egrid((unsigned)(a.C * a.ew_grid_y)), block(kBnThreads);
     const int64_t M = (int64_t)a.N * a.HW;
     if (a.channel_fused) {
+        if (a.stage == 1) return hipSuccess;
         const BnGeom g1 = make_bn_geom(a.N, a.C, a.HW, a.vec, 1);
         if (a.channel_threads == kBnChannelBigBlock)
             return launch(NH_K_BN_BWD_CHANNEL, bn_bwd_channel_kernel<T, V, kBnNtPolicy, ACT, kBnChannelBigBlock>,
@@ -1208,9 +1260,12 @@ static hipError_t bn_backward_t(const BnCall &a, hipStream_t s)
                       dim3((unsigned)a.C), block, 0, s, dy, x, static_cast<T *>(a.out), a.stats, a.grads, a.beta,
                       a.slope, g1, M);
     }
-    hipError_t e = launch(NH_K_BN_GRAD_SUMS, bn_grad_sums_kernel<T, V, kBnNtPolicy, ACT>, rgrid, block, 0,
-                          s, dy, x, a.stats, a.beta, a.slope, gr, a.partials);
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (a.stage != 2) {
+        e = launch(NH_K_BN_GRAD_SUMS, bn_grad_sums_kernel<T, V, kBnNtPolicy, ACT>, rgrid, block, 0, s, dy, x,
+                   a.stats, a.beta, a.slope, gr, a.partials);
+        if (e != hipSuccess || a.stage == 1) return e;
+    }
     if (a.separate_finalize || a.out == nullptr) {
         const dim3 fgrid((unsigned)ceil_div(a.C, kBnThreads / kWave));
         e = launch(NH_K_BN_BWD_FINALIZE, bn_bwd_finalize, fgrid, block, 0, s, a.partials, a.grid_y,

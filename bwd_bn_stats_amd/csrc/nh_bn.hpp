@@ -178,6 +178,8 @@ struct BnCall {
     int channel_threads; // threads of that block: kBnThreads or kBnChannelBigBlock
     int col;             // 1: small planes, the [N, C*HW] row layout (colg; vec along the rows)
     BnColGeom colg;
+    int stage;           // 0 the whole operation; 1 its reduction pass only (partials into the
+                         // workspace); 2 the rest (finalize + elementwise pass, from those partials)
     int act;             // 0 none, 1 ReLU, 2 LeakyReLU
     float slope;         // LeakyReLU negative slope
     const void *x;

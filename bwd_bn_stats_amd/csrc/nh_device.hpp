@@ -212,6 +212,14 @@ template <int V> struct Raw<float, V> {
     __device__ __forceinline__ float get(int e) const { return v[e]; }
 };
 
+// A single bf16 element, kept as its bit pattern until widened.
+template <> struct Raw<uint16_t, 1> {
+    uint32_t u;
+    __device__ __forceinline__ void load(const uint16_t *p) { u = *p; }
+    __device__ __forceinline__ void load_nt(const uint16_t *p) { u = (uint16_t)__builtin_nontemporal_load(p); }
+    __device__ __forceinline__ float get(int) const { return __uint_as_float(u << 16); }
+};
+
 template <int V> struct Raw<uint16_t, V> {
     static_assert(V == 4 || V == 8, "bf16 groups hold 4 or 8 elements");
     uint32_t u[V / 2];

@@ -30,6 +30,7 @@ ACTS = {"none": 0, "relu": 1, "leaky_relu": 2}
 EXPORTS = [
     "nh_status_string", "nh_last_error", "nh_kernel_name",
     "bn_forward_train_workspace", "bn_backward_workspace", "bn_forward_train", "bn_backward",
+    "bn_forward_train_stage", "bn_backward_stage",
     "bn_act_forward_train", "bn_act_backward", "bn_forward_infer",
     "layernorm_backward_workspace", "layernorm_backward",
     "bda_layernorm_backward_workspace", "bda_layernorm_backward",
@@ -62,6 +63,8 @@ def _load():
         "bn_backward_workspace": (i32, [i64, i64, i64, psz]),
         "bn_forward_train": (i32, [p, p, i32, i64, i64, i64, p, p, p, p, f32, f32, p, p, sz, p]),
         "bn_backward": (i32, [p, p, i32, i64, i64, i64, p, p, p, p, sz, p]),
+        "bn_forward_train_stage": (i32, [i32, p, p, i32, i64, i64, i64, p, p, p, p, f32, f32, p, p, sz, p]),
+        "bn_backward_stage": (i32, [i32, p, p, i32, i64, i64, i64, p, p, p, p, sz, p]),
         "bn_act_forward_train": (i32, [p, p, i32, i64, i64, i64, p, p, p, p, f32, f32, i32, f32, p, p,
                                        sz, p]),
         "bn_act_backward": (i32, [p, p, i32, i64, i64, i64, p, p, i32, f32, p, p, p, sz, p]),
@@ -246,6 +249,42 @@ def bn_backward(dy, x, stats, *, beta=None, act="none", slope: float = 0.01, dx=
                                    _act(act), slope, _ptr(dx), _ptr(grads), _ptr(ws), nb,
                                    _stream(x.device)), "bn_act_backward")
     return dx, grads
+
+
+def bn_forward_train_stage(stage: int, x, y, stats, workspace, gamma=None, beta=None, running_mean=None,
+                           running_var=None, momentum: float = 0.1, eps: float = 1e-5):
+    """One stage of the BatchNorm2d training forward (bn_forward_train_stage):
+    1 = the statistics pass into `workspace`, 2 = finalize + apply from it.
+    Both stages take the same tensors; stage 1 then stage 2 equals
+    bn_forward_train."""
+    _dev_tensor(x, "x")
+    N, C, HW = _nchw(x)
+    f32 = torch.float32
+    for t, n in ((gamma, "gamma"), (beta, "beta"), (running_mean, "running_mean"),
+                 (running_var, "running_var")):
+        _dev_tensor(t, n, f32, C)
+    _dev_tensor(y, "y", x.dtype, x.numel())
+    _dev_tensor(stats, "stats", f32, 4 * C)
+    nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.bn_forward_train_stage(int(stage), _ptr(x), _ptr(y), _dt(x), N, C, HW, _ptr(gamma), _ptr(beta),
+                                      _ptr(running_mean), _ptr(running_var), momentum, eps, _ptr(stats),
+                                      _ptr(workspace), nb, _stream(x.device)), "bn_forward_train_stage")
+
+
+def bn_backward_stage(stage: int, dy, x, stats, dx, grads, workspace):
+    """One stage of the BatchNorm2d training backward (bn_backward_stage): 1 =
+    the grad_sums pass into `workspace`, 2 = finalize + dx from it (dx may be
+    None).  Both stages take the same tensors."""
+    _dev_tensor(x, "x")
+    _dev_tensor(dy, "dy", x.dtype, x.numel())
+    N, C, HW = _nchw(x)
+    f32 = torch.float32
+    _dev_tensor(stats, "stats", f32, 4 * C)
+    _dev_tensor(dx, "dx", x.dtype, x.numel())
+    _dev_tensor(grads, "grads", f32, 4 * C)
+    nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.bn_backward_stage(int(stage), _ptr(dy), _ptr(x), _dt(x), N, C, HW, _ptr(stats), _ptr(dx),
+                                 _ptr(grads), _ptr(workspace), nb, _stream(x.device)), "bn_backward_stage")
 
 
 def bn_forward_infer(x, running_mean, running_var, gamma=None, beta=None, eps: float = 1e-5, *,

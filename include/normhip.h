@@ -141,6 +141,40 @@ nh_status bn_backward(const void *dy, const void *x, nh_dtype io,
                       const float *stats, void *dx, float *grads,
                       void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * The two stages of each BatchNorm call, as the Aether-ML PR #18 kernels split
+ * it: the forward's statistics pass (stats kernel: shifted sums into
+ * per-block partials) and then its finalize + apply; the backward's grad_sums
+ * pass and then its finalize + dx.  The stage-1 results stay in the
+ * workspace, so a host can start the reduction early and the rest later, or
+ * run the reduction alone (a data-parallel BatchNorm exchanges the per-block
+ * sums between the two stages).
+ *
+ *   stage         1: the reduction pass only -- writes the workspace, nothing
+ *                    else (stats, grads, y, dx and the running statistics are
+ *                    untouched);
+ *                 2: everything after it, from the workspace stage 1 wrote.
+ *                 Any other value: NH_ERR_ARG.
+ *   other arguments   exactly those of bn_forward_train / bn_backward, and the
+ *                 SAME values for both stages (the launch plan depends on the
+ *                 shape and on the pointers' alignment, y's and dx's included).
+ * Stage 1 then stage 2 on the same stream, with the same arguments and no
+ * other use of the workspace in between, gives bit for bit the results of the
+ * one-call form.  Shapes whose whole direction runs as one kernel (channels
+ * of a few thousand elements) launch nothing in stage 1 and that kernel in
+ * stage 2.
+ */
+nh_status bn_forward_train_stage(int stage, const void *x, void *y, nh_dtype io,
+                                 int64_t N, int64_t C, int64_t HW,
+                                 const float *gamma, const float *beta,
+                                 float *running_mean, float *running_var,
+                                 float momentum, float eps,
+                                 float *stats, void *ws, size_t ws_bytes, void *stream);
+nh_status bn_backward_stage(int stage, const void *dy, const void *x, nh_dtype io,
+                            int64_t N, int64_t C, int64_t HW,
+                            const float *stats, void *dx, float *grads,
+                            void *ws, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------------------
  * BatchNorm2d + activation, and BatchNorm2d inference.
  *

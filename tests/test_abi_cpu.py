@@ -85,6 +85,23 @@ def test_bn_backward_validation():
     assert f(NULL, NULL, 0, 0, 3, 4, NULL, NULL, NULL, NULL, 0, NULL) == NH_OK
 
 
+def test_bn_stage_validation():
+    fs = nh.lib.bn_forward_train_stage
+    bs = nh.lib.bn_backward_stage
+    for st in (0, 3, -1):
+        assert fs(st, FAKE, FAKE, 0, 2, 3, 4, NULL, NULL, NULL, NULL, 0.1, 1e-5, FAKE, FAKE, 1 << 20,
+                  NULL) == NH_ERR_ARG
+        assert "stage" in nh.last_error()
+        assert bs(st, FAKE, FAKE, 0, 2, 3, 4, FAKE, FAKE, FAKE, FAKE, 1 << 20, NULL) == NH_ERR_ARG
+    # a valid stage runs the one-call form's validation
+    assert fs(1, FAKE, FAKE, 2, 2, 3, 4, NULL, NULL, NULL, NULL, 0.1, 1e-5, FAKE, FAKE, 1 << 20,
+              NULL) == NH_ERR_DTYPE
+    assert fs(2, NULL, FAKE, 0, 2, 3, 4, NULL, NULL, NULL, NULL, 0.1, 1e-5, FAKE, FAKE, 1 << 20,
+              NULL) == NH_ERR_NULL
+    assert bs(1, FAKE, FAKE, 0, 2, 3, 4, NULL, FAKE, FAKE, FAKE, 1 << 20, NULL) == NH_ERR_NULL
+    assert bs(2, NULL, NULL, 0, 0, 3, 4, NULL, NULL, NULL, NULL, 0, NULL) == NH_OK
+
+
 def test_bn_act_and_infer_validation():
     fa = nh.lib.bn_act_forward_train
     # x, y, io, N, C, HW, gamma, beta, rm, rv, momentum, eps, act, slope, stats, ws, ws_bytes, stream
