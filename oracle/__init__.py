@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-Wall", "-Wextra",
              "-shared", "-fPIC"]
 
 
@@ -53,11 +53,12 @@ def _load():
                                                        p, p]
         lib.oracle_rmsnorm_rms.argtypes = [i64, i64, p, dbl, p]
         lib.oracle_rmsnorm_backward.argtypes = [i64, i64, p, p, p, p, dbl, p, p]
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
         for f in ("oracle_bn_forward_train", "oracle_bn_backward", "oracle_bn_act_forward_train",
                   "oracle_bn_act_backward", "oracle_bn_infer", "oracle_layernorm_stats",
                   "oracle_layernorm_forward", "oracle_layernorm_backward",
                   "oracle_bda_layernorm_backward", "oracle_rmsnorm_rms",
-                  "oracle_rmsnorm_forward", "oracle_rmsnorm_backward"):
+                  "oracle_rmsnorm_forward", "oracle_rmsnorm_backward", "oracle_set_threads"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -77,10 +78,17 @@ def _check(rc, name):
         raise ValueError(f"{name}: bad arguments (rc={rc})")
 
 
+def _threads(n):
+    """Threads for the next call's independent loops (channels, rows, column
+    blocks); the results do not depend on it."""
+    _check(_load().oracle_set_threads(int(n)), "oracle_set_threads")
+
+
 def bn_forward_train(x, gamma, beta, *, eps=1e-5, momentum=0.1,
-                     running_mean=None, running_var=None):
+                     running_mean=None, running_var=None, threads=1):
     """x: [N,C,H,W] (or [N,C,HW]).  Returns (y, stats[4,C], rm', rv').
     rm'/rv' are None when the running statistics are not given."""
+    _threads(threads)
     x = _d(x)
     N, C = x.shape[0], x.shape[1]
     HW = int(np.prod(x.shape[2:])) if x.ndim > 2 else 1
@@ -96,8 +104,9 @@ def bn_forward_train(x, gamma, beta, *, eps=1e-5, momentum=0.1,
     return y, stats, rm, rv
 
 
-def bn_backward(x, dy, gamma, *, eps=1e-5):
+def bn_backward(x, dy, gamma, *, eps=1e-5, threads=1):
     """Returns (dx, grads[4,C] = (dgamma, dbeta, k1, k2))."""
+    _threads(threads)
     x, dy = _d(x), _d(dy)
     N, C = x.shape[0], x.shape[1]
     HW = int(np.prod(x.shape[2:])) if x.ndim > 2 else 1
@@ -160,8 +169,9 @@ def bn_infer(x, gamma, beta, running_mean, running_var, act="none", slope=0.01, 
     return y
 
 
-def layernorm_stats(x, *, eps=1e-5):
+def layernorm_stats(x, *, eps=1e-5, threads=1):
     """x: [rows, cols].  Returns (mean[rows], rstd[rows])."""
+    _threads(threads)
     x = _d(x)
     rows, cols = x.shape
     mean = np.empty(rows, np.float64)
@@ -185,8 +195,9 @@ def layernorm_forward(x, w=None, b=None, *, eps=1e-5):
     return y, mean, rstd
 
 
-def layernorm_backward(x, dy, mean, rstd, w=None):
+def layernorm_backward(x, dy, mean, rstd, w=None, *, threads=1):
     """Returns (dx, dweight, dbias)."""
+    _threads(threads)
     x, dy, mean, rstd = _d(x), _d(dy), _d(mean), _d(rstd)
     w = None if w is None else _d(w)
     rows, cols = x.shape
@@ -219,7 +230,8 @@ def bda_layernorm_backward(x, dy, mean, rstd, w=None, dresidual=None, mask=None,
     return dh, da, dw, db, dbi
 
 
-def rmsnorm_rms(x, *, eps=1e-5):
+def rmsnorm_rms(x, *, eps=1e-5, threads=1):
+    _threads(threads)
     x = _d(x)
     rows, cols = x.shape
     rms = np.empty(rows, np.float64)
@@ -239,9 +251,12 @@ def rmsnorm_forward(x, w=None, *, eps=1e-5):
     return y, rms
 
 
-def rmsnorm_backward(x, dy, w, rms=None, *, eps=1e-5):
-    """Returns (dx, dweight).  rms=None recomputes rms from x with eps."""
-    x, dy, w = _d(x), _d(dy), _d(w)
+def rmsnorm_backward(x, dy, w, rms=None, *, eps=1e-5, threads=1):
+    """Returns (dx, dweight).  rms=None recomputes rms from x with eps;
+    w=None means weight 1."""
+    _threads(threads)
+    x, dy = _d(x), _d(dy)
+    w = None if w is None else _d(w)
     rms = None if rms is None else _d(rms)
     rows, cols = x.shape
     dx = np.empty_like(x)

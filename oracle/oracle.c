@@ -9,7 +9,12 @@
  * Every quantity is computed in double precision, straight from its
  * definition: means and variances by two passes over the data, sums with
  * Neumaier-compensated accumulation, no one-pass shifted sums, no partials,
- * no coefficient-form shortcuts.  Loops are sequential and single-threaded.
+ * no coefficient-form shortcuts.  Loops run sequentially by default;
+ * oracle_set_threads(n) spreads independent channels (BatchNorm) or rows
+ * (LayerNorm/RMSNorm) over n OpenMP threads, and column sums over disjoint
+ * blocks of columns.  Every sum still adds its terms in the same order, so
+ * the results are bit-identical at any thread count.  (This is for timing
+ * the oracle on a host's cores; the arithmetic is the sequential one.)
  *
  * Layouts: BatchNorm tensors are NCHW, contiguous, element (n,c,j) at
  * (n*C + c)*HW + j with HW = H*W.  LayerNorm/RMSNorm tensors are
@@ -41,6 +46,20 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
+
+/* ---- threads for the independent loops (1 = sequential) ------------------ */
+static int g_threads = 1;
+
+int oracle_set_threads(int n)
+{
+    if (n < 1) return -1;
+    g_threads = n;
+    return 0;
+}
+
+/* Columns per block of the threaded column sums: each block's columns are
+ * summed by one thread in row order. */
+#define COL_BLOCK 64
 
 /* ---- compensated summation (Neumaier's improvement of Kahan's method) ---- */
 typedef struct {
@@ -120,6 +139,7 @@ int oracle_bn_forward_train(int64_t N, int64_t C, int64_t HW,
     const int64_t M = N * HW;
     if (M == 0) return -1;
     if ((running_mean || running_var) && M < 2) return -1;
+#pragma omp parallel for num_threads(g_threads) schedule(dynamic, 1) if (g_threads > 1)
     for (int64_t c = 0; c < C; ++c) {
         double mean, var;
         bn_channel_moments(x, N, C, HW, c, &mean, &var);
@@ -170,6 +190,7 @@ int oracle_bn_backward(int64_t N, int64_t C, int64_t HW,
     const int64_t Mi = N * HW;
     if (Mi == 0) return -1;
     const double M = (double)Mi;
+#pragma omp parallel for num_threads(g_threads) schedule(dynamic, 1) if (g_threads > 1)
     for (int64_t c = 0; c < C; ++c) {
         double mean, var;
         bn_channel_moments(x, N, C, HW, c, &mean, &var);
@@ -294,6 +315,7 @@ int oracle_layernorm_stats(int64_t rows, int64_t cols, const double *x, double e
                            double *mean, double *rstd)
 {
     if (rows < 0 || cols <= 0) return -1;
+#pragma omp parallel for num_threads(g_threads) schedule(static) if (g_threads > 1)
     for (int64_t r = 0; r < rows; ++r) {
         const double *xr = x + (size_t)r * (size_t)cols;
         ksum_t s;
@@ -358,6 +380,7 @@ int oracle_layernorm_backward(int64_t rows, int64_t cols,
 {
     if (rows < 0 || cols <= 0) return -1;
     const double H = (double)cols;
+#pragma omp parallel for num_threads(g_threads) schedule(static) if (g_threads > 1)
     for (int64_t r = 0; r < rows; ++r) {
         const double *xr = x + (size_t)r * (size_t)cols;
         const double *dyr = dy + (size_t)r * (size_t)cols;
@@ -383,12 +406,16 @@ int oracle_layernorm_backward(int64_t rows, int64_t cols,
     ksum_t *sb = (ksum_t *)malloc((size_t)cols * sizeof(ksum_t));
     if (!sw || !sb) { free(sw); free(sb); return -1; }
     for (int64_t j = 0; j < cols; ++j) { ks_init(&sw[j]); ks_init(&sb[j]); }
-    for (int64_t r = 0; r < rows; ++r)
-        for (int64_t j = 0; j < cols; ++j) {
-            size_t i = (size_t)r * (size_t)cols + (size_t)j;
-            ks_add(&sw[j], dy[i] * (x[i] - mean[r]) * rstd[r]);
-            ks_add(&sb[j], dy[i]);
-        }
+#pragma omp parallel for num_threads(g_threads) schedule(static) if (g_threads > 1)
+    for (int64_t jb = 0; jb < cols; jb += COL_BLOCK) {
+        const int64_t je = jb + COL_BLOCK < cols ? jb + COL_BLOCK : cols;
+        for (int64_t r = 0; r < rows; ++r)
+            for (int64_t j = jb; j < je; ++j) {
+                size_t i = (size_t)r * (size_t)cols + (size_t)j;
+                ks_add(&sw[j], dy[i] * (x[i] - mean[r]) * rstd[r]);
+                ks_add(&sb[j], dy[i]);
+            }
+    }
     for (int64_t j = 0; j < cols; ++j) {
         if (dweight) dweight[j] = ks_value(&sw[j]);
         if (dbias) dbias[j] = ks_value(&sb[j]);
@@ -454,6 +481,7 @@ int oracle_rmsnorm_rms(int64_t rows, int64_t cols, const double *x, double eps,
                        double *rms)
 {
     if (rows < 0 || cols <= 0) return -1;
+#pragma omp parallel for num_threads(g_threads) schedule(static) if (g_threads > 1)
     for (int64_t r = 0; r < rows; ++r) {
         const double *xr = x + (size_t)r * (size_t)cols;
         ksum_t s;
@@ -494,7 +522,7 @@ int oracle_rmsnorm_forward(int64_t rows, int64_t cols, const double *x, const do
  *   dweight_j = sum_rows dy * x * rinv            [T16, T23, T25]
  * which is dx = g/rms - x*sum(g*x)/(H*rms^3).
  * rms may be NULL: it is then recomputed from x with eps (oracle_rmsnorm_rms).
- * dweight may be NULL.
+ * w may be NULL (weight = 1).  dweight may be NULL.
  */
 int oracle_rmsnorm_backward(int64_t rows, int64_t cols,
                             const double *x, const double *dy, const double *w,
@@ -512,6 +540,7 @@ int oracle_rmsnorm_backward(int64_t rows, int64_t cols,
         oracle_rmsnorm_rms(rows, cols, x, eps, rms);
     }
     for (int64_t j = 0; j < cols; ++j) ks_init(&sw[j]);
+#pragma omp parallel for num_threads(g_threads) schedule(static) if (g_threads > 1)
     for (int64_t r = 0; r < rows; ++r) {
         const double *xr = x + (size_t)r * (size_t)cols;
         const double *dyr = dy + (size_t)r * (size_t)cols;
@@ -520,14 +549,24 @@ int oracle_rmsnorm_backward(int64_t rows, int64_t cols,
         ksum_t s;
         ks_init(&s);
         for (int64_t j = 0; j < cols; ++j) {
-            double g = dyr[j] * w[j];
+            double g = dyr[j] * (w ? w[j] : 1.0);
             ks_add(&s, -g * xr[j] / (rms[r] * rms[r]));
         }
         double t = ks_value(&s) / (2.0 * rms[r]) / H;
         for (int64_t j = 0; j < cols; ++j) {
-            double g = dyr[j] * w[j];
+            double g = dyr[j] * (w ? w[j] : 1.0);
             dxr[j] = g * rinv + 2.0 * t * xr[j];
-            ks_add(&sw[j], dyr[j] * xr[j] * rinv);
+        }
+    }
+    /* dweight: each column summed over the rows in row order. */
+#pragma omp parallel for num_threads(g_threads) schedule(static) if (g_threads > 1)
+    for (int64_t jb = 0; jb < cols; jb += COL_BLOCK) {
+        const int64_t je = jb + COL_BLOCK < cols ? jb + COL_BLOCK : cols;
+        for (int64_t r = 0; r < rows; ++r) {
+            const double *xr = x + (size_t)r * (size_t)cols;
+            const double *dyr = dy + (size_t)r * (size_t)cols;
+            const double rinv = 1.0 / rms[r];
+            for (int64_t j = jb; j < je; ++j) ks_add(&sw[j], dyr[j] * xr[j] * rinv);
         }
     }
     if (dweight)
