@@ -592,6 +592,58 @@ nh_status bn_act_forward_train(const void *x, void *y, nh_dtype io, int64_t N, i
                            slope, stats, ws, ws_bytes, stream);
 }
 
+// ---- the allocation-free training forward -----------------------------------
+// bn_forward_train_noalloc keeps its workspace (the stats pass's partials and
+// shifts) in this file-scope device array instead of a caller's buffer: one
+// copy per GPU, held until the process ends.  Host code must not pass the
+// array's name to a kernel (in host code it is a host-side stand-in, not a
+// device address): it uses the address hipGetSymbolAddress returns for the
+// current device, resolved once per device on the first call there.
+constexpr size_t kNoallocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[64];
+
+static nh_status scratch_ptr(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(NH_ERR_HIP, "device id %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(NH_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return NH_OK;
+}
+
+nh_status bn_forward_train_noalloc(const void *x, void *y, nh_dtype io, int64_t N, int64_t C, int64_t HW,
+                                   const float *gamma, const float *beta, float *running_mean,
+                                   float *running_var, float momentum, float eps, float *stats, void *stream)
+{
+    if (!valid_dtype(io)) return fail(NH_ERR_DTYPE, "io dtype %d", (int)io);
+    nh_status st = bn_check_shape(N, C, HW);
+    if (st != NH_OK) return st;
+    if (N * C * HW == 0) return ok();
+    DeviceInfo d;
+    if ((st = device_info(&d)) != NH_OK) return st;
+    const size_t need = bn_ws_bytes(N, C, HW, d);
+    if (need > kNoallocScratchBytes)
+        return fail(NH_ERR_WORKSPACE,
+                    "this shape needs %zu bytes of workspace; the allocation-free forward holds %zu bytes "
+                    "(use bn_forward_train with a workspace)", need, kNoallocScratchBytes);
+    void *ws = nullptr;
+    if ((st = scratch_ptr(&ws)) != NH_OK) return st;
+    return bn_forward_impl(0, x, y, io, N, C, HW, gamma, beta, running_mean, running_var, momentum, eps,
+                           NH_ACT_NONE, 0.f, stats, ws, kNoallocScratchBytes, stream);
+}
+
 nh_status bn_forward_train_stage(int stage, const void *x, void *y, nh_dtype io, int64_t N, int64_t C,
                                  int64_t HW, const float *gamma, const float *beta, float *running_mean,
                                  float *running_var, float momentum, float eps, float *stats, void *ws,

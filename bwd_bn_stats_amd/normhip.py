@@ -30,7 +30,7 @@ ACTS = {"none": 0, "relu": 1, "leaky_relu": 2}
 EXPORTS = [
     "nh_status_string", "nh_last_error", "nh_kernel_name",
     "bn_forward_train_workspace", "bn_backward_workspace", "bn_forward_train", "bn_backward",
-    "bn_forward_train_stage", "bn_backward_stage",
+    "bn_forward_train_stage", "bn_backward_stage", "bn_forward_train_noalloc",
     "bn_act_forward_train", "bn_act_backward", "bn_forward_infer",
     "layernorm_backward_workspace", "layernorm_backward",
     "bda_layernorm_backward_workspace", "bda_layernorm_backward",
@@ -64,6 +64,7 @@ def _load():
         "bn_forward_train": (i32, [p, p, i32, i64, i64, i64, p, p, p, p, f32, f32, p, p, sz, p]),
         "bn_backward": (i32, [p, p, i32, i64, i64, i64, p, p, p, p, sz, p]),
         "bn_forward_train_stage": (i32, [i32, p, p, i32, i64, i64, i64, p, p, p, p, f32, f32, p, p, sz, p]),
+        "bn_forward_train_noalloc": (i32, [p, p, i32, i64, i64, i64, p, p, p, p, f32, f32, p, p]),
         "bn_backward_stage": (i32, [i32, p, p, i32, i64, i64, i64, p, p, p, p, sz, p]),
         "bn_act_forward_train": (i32, [p, p, i32, i64, i64, i64, p, p, p, p, f32, f32, i32, f32, p, p,
                                        sz, p]),

@@ -142,6 +142,28 @@ nh_status bn_backward(const void *dy, const void *x, nh_dtype io,
                       void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Allocation-free training forward, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): bn_forward_train without the workspace arguments.  Its
+ * workspace is a library-owned device array of 16 MiB (16777216 bytes) per GPU,
+ * held until the process ends; its address on each device is looked up once,
+ * on the first call on that device.  The call allocates nothing.
+ *   arguments     as bn_forward_train, minus ws and ws_bytes
+ *   errors        as bn_forward_train; NH_ERR_WORKSPACE (nothing launched)
+ *                 when the shape's workspace, bn_forward_train_workspace,
+ *                 exceeds 16 MiB
+ * Every call on one GPU uses that GPU's one array (nothing in it carries over
+ * from call to call): calls that overlap on one GPU -- on two streams, or from
+ * two threads -- race and give undefined results.  Results equal
+ * bn_forward_train's bit for bit.
+ */
+nh_status bn_forward_train_noalloc(const void *x, void *y, nh_dtype io,
+                                   int64_t N, int64_t C, int64_t HW,
+                                   const float *gamma, const float *beta,
+                                   float *running_mean, float *running_var,
+                                   float momentum, float eps, float *stats, void *stream);
+
+/*
  * The two stages of each BatchNorm call, as the Aether-ML PR #18 kernels split
  * it: the forward's statistics pass (stats kernel: shifted sums into
  * per-block partials) and then its finalize + apply; the backward's grad_sums

@@ -102,6 +102,15 @@ def test_bn_stage_validation():
     assert bs(2, NULL, NULL, 0, 0, 3, 4, NULL, NULL, NULL, NULL, 0, NULL) == NH_OK
 
 
+def test_bn_noalloc_validation():
+    f = nh.lib.bn_forward_train_noalloc
+    # x, y, io, N, C, HW, gamma, beta, rm, rv, momentum, eps, stats, stream
+    assert f(FAKE, FAKE, 2, 2, 3, 4, NULL, NULL, NULL, NULL, 0.1, 1e-5, FAKE, NULL) == NH_ERR_DTYPE
+    assert f(FAKE, FAKE, 0, 2, -3, 4, NULL, NULL, NULL, NULL, 0.1, 1e-5, FAKE, NULL) == NH_ERR_SHAPE
+    assert f(FAKE, FAKE, 0, 1 << 16, 1 << 8, 1 << 8, NULL, NULL, NULL, NULL, 0.1, 1e-5, FAKE, NULL) == NH_ERR_SHAPE
+    assert f(NULL, NULL, 0, 0, 3, 4, NULL, NULL, NULL, NULL, 0.1, 1e-5, NULL, NULL) == NH_OK
+
+
 def test_bn_act_and_infer_validation():
     fa = nh.lib.bn_act_forward_train
     # x, y, io, N, C, HW, gamma, beta, rm, rv, momentum, eps, act, slope, stats, ws, ws_bytes, stream
