@@ -583,11 +583,11 @@ bn_fwd_channel_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restr
 #pragma unroll
     for (int k = 0; k < kBnUnroll; ++k) { s1[k] = 0.f; s2[k] = 0.f; }
     for (uint32_t base = threadIdx.x; base < u1; base += TB * kBnUnroll) {
-        float v[kBnUnroll][V];
+        Raw<T, V> v[kBnUnroll];
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
             const uint32_t u = base + k * TB;
-            if (u < u1) ld<(NT & kNtReduceLoads) != 0, T, V>(x + bn_unit_offset<V>(g, c, u), v[k]);
+            if (u < u1) ldr<(NT & kNtReduceLoads) != 0>(v[k], x + bn_unit_offset<V>(g, c, u));
         }
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
@@ -595,7 +595,7 @@ bn_fwd_channel_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restr
             if (u < u1) {
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
-                    const float d = v[k][e] - K;
+                    const float d = v[k].get(e) - K;
                     s1[k] += d;
                     s2[k] = fmaf(d, d, s2[k]);
                 }
@@ -614,13 +614,13 @@ bn_fwd_channel_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restr
     const float mean = sh[0], scale = sh[1];
     const float bc = beta ? beta[c] : 0.f;
     for (uint32_t base = threadIdx.x; base < u1; base += TB * kBnUnroll) {
-        float v[kBnUnroll][V];
+        Raw<T, V> v[kBnUnroll];
         int off[kBnUnroll];
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
             const uint32_t u = base + k * TB;
             off[k] = bn_unit_offset<V>(g, c, u);
-            if (u < u1) ld<(NT & kNtEwLoads) != 0, T, V>(x + off[k], v[k]);
+            if (u < u1) ldr<(NT & kNtEwLoads) != 0>(v[k], x + off[k]);
         }
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
@@ -628,7 +628,7 @@ bn_fwd_channel_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restr
             if (u < u1) {
                 float o[V];
 #pragma unroll
-                for (int e = 0; e < V; ++e) o[e] = act_fwd<ACT>(fmaf(v[k][e] - mean, scale, bc), slope);
+                for (int e = 0; e < V; ++e) o[e] = act_fwd<ACT>(fmaf(v[k].get(e) - mean, scale, bc), slope);
                 st<(NT & kNtStores) != 0, T, V>(y + off[k], o);
             }
         }
@@ -650,14 +650,14 @@ bn_bwd_channel_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__re
 #pragma unroll
     for (int k = 0; k < kBnUnroll; ++k) { s1[k] = 0.f; s2[k] = 0.f; }
     for (uint32_t base = threadIdx.x; base < u1; base += TB * kBnUnroll) {
-        float vx[kBnUnroll][V], vd[kBnUnroll][V];
+        Raw<T, V> vx[kBnUnroll], vd[kBnUnroll];
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
             const uint32_t u = base + k * TB;
             if (u < u1) {
                 const int off = bn_unit_offset<V>(g, c, u);
-                ld<(NT & kNtReduceLoads) != 0, T, V>(x + off, vx[k]);
-                ld<(NT & kNtReduceLoads) != 0, T, V>(dy + off, vd[k]);
+                ldr<(NT & kNtReduceLoads) != 0>(vx[k], x + off);
+                ldr<(NT & kNtReduceLoads) != 0>(vd[k], dy + off);
             }
         }
 #pragma unroll
@@ -666,8 +666,8 @@ bn_bwd_channel_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__re
             if (u < u1) {
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
-                    const float xc = vx[k][e] - mean;
-                    const float dz = act_bwd<ACT>(vd[k][e], fmaf(xc, ACT != 0 ? scale : 0.f, bz), slope);
+                    const float xc = vx[k].get(e) - mean;
+                    const float dz = act_bwd<ACT>(vd[k].get(e), fmaf(xc, ACT != 0 ? scale : 0.f, bz), slope);
                     s1[k] += dz;
                     s2[k] = fmaf(dz, xc, s2[k]);
                 }
@@ -684,15 +684,15 @@ bn_bwd_channel_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__re
     if (dx == nullptr) return;  // uniform: the caller skipped dx
     const float k1 = sh[0], k2 = sh[1];
     for (uint32_t base = threadIdx.x; base < u1; base += TB * kBnUnroll) {
-        float vx[kBnUnroll][V], vd[kBnUnroll][V];
+        Raw<T, V> vx[kBnUnroll], vd[kBnUnroll];
         int off[kBnUnroll];
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
             const uint32_t u = base + k * TB;
             off[k] = bn_unit_offset<V>(g, c, u);
             if (u < u1) {
-                ld<(NT & kNtEwLoads) != 0, T, V>(x + off[k], vx[k]);
-                ld<(NT & kNtEwLoads) != 0, T, V>(dy + off[k], vd[k]);
+                ldr<(NT & kNtEwLoads) != 0>(vx[k], x + off[k]);
+                ldr<(NT & kNtEwLoads) != 0>(vd[k], dy + off[k]);
             }
         }
 #pragma unroll
@@ -702,8 +702,8 @@ bn_bwd_channel_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__re
                 float o[V];
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
-                    const float xc = vx[k][e] - mean;
-                    const float dz = act_bwd<ACT>(vd[k][e], fmaf(xc, scale, bz), slope);
+                    const float xc = vx[k].get(e) - mean;
+                    const float dz = act_bwd<ACT>(vd[k].get(e), fmaf(xc, scale, bz), slope);
                     o[e] = fmaf(dz, scale, fmaf(xc, k1, k2));
                 }
                 st<(NT & kNtStores) != 0, T, V>(dx + off[k], o);
