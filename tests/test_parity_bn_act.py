@@ -96,8 +96,11 @@ def test_bn_act_parity(nh, oracle_mod, name, act, slope):
     _run_case(nh, oracle_mod, CASES[name](), act, slope)
 
 
-def test_bn_act_resnet_bf16(nh, oracle_mod):
-    _run_case(nh, oracle_mod, wl.bn_resnet(), "relu", 0.0)
+@pytest.mark.parametrize("act,slope", [("relu", 0.0), ("leaky_relu", 0.01)])
+def test_bn_act_parity_resnet_64x256x56x56_bf16(nh, oracle_mod, act, slope):
+    """The BatchNorm + activation workload the benchmark times
+    (bn2d_relu_train_fwd_bwd_nchw_64x256x56x56_bf16), at its full size."""
+    _run_case(nh, oracle_mod, wl.bn_resnet(), act, slope)
 
 
 def test_bn_act_options(nh, oracle_mod):
