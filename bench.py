@@ -770,7 +770,7 @@ KERNEL_SOURCES = ["bn_kernels.hip", "nh_device.hpp", "nh_internal.hpp", "nh_bn.h
 PROFILE_TRACE = ("rocprofv3 --kernel-trace --stats -f csv -d <dir> -o {w} -- python3 bench.py --workloads {w} "
                  "--steps 20 --warmup 3 --reps 3 --no-cpu-baseline --no-floors")
 PROFILE_PMC = ("rocprofv3 --pmc {counter} -f csv -d <dir> -o {w} -- python3 bench.py --workloads {w} --steps 4 "
-               "--warmup 1 --reps 1 --no-cpu-baseline --no-floors --no-calib")
+               "--warmup 1 --reps 1 --no-cpu-baseline --no-floors --no-calib --eager")
 PROFILE_CALIB = ("rocprofv3 --pmc {counter} -f csv -d <dir> -o calib -- python3 bench.py --calib-only")
 
 
@@ -803,8 +803,10 @@ def calib_run(nh, torch):
 
 def summarize_workload(workload, trace_csv, fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, out_path):
     """One workload's kernels: calls and mean duration (kernel trace), and
-    HBM-side bytes per dispatch (FETCH_SIZE / WRITE_SIZE, each scaled by the
-    same counter on the calibration add of known size)."""
+    data-fabric bytes per dispatch (FETCH_SIZE / WRITE_SIZE, each scaled by
+    the same counter on the calibration add of known size).  The counters
+    see the L2's traffic to the fabric, so reads the Infinity Cache serves
+    count as well as HBM reads; no counter separates the two."""
     import collections
     import csv
 
@@ -816,15 +818,7 @@ def summarize_workload(workload, trace_csv, fetch_csv, write_csv, calib_fetch_cs
         return d
 
     dur = per_kernel(trace_csv, lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    # each dispatch's duration by the kernel dispatched just before it (the
-    # same kernel in a reduction-only region, the other passes in a step)
-    ctx = collections.OrderedDict()
-    prev = None
-    for r in sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Dispatch_Id"])):
-        name = _short_kernel(r["Kernel_Name"])
-        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        ctx.setdefault(name, collections.OrderedDict()).setdefault(prev, []).append(d)
-        prev = name
+    ctx = _context_split(trace_csv)
     fet = per_kernel(fetch_csv, lambda r: float(r["Counter_Value"])) if fetch_csv else {}
     wri = per_kernel(write_csv, lambda r: float(r["Counter_Value"])) if write_csv else {}
     cf = per_kernel(calib_fetch_csv, lambda r: float(r["Counter_Value"])) if calib_fetch_csv else {}
@@ -833,7 +827,7 @@ def summarize_workload(workload, trace_csv, fetch_csv, write_csv, calib_fetch_cs
     ck = next((k for k in cf if "calib_add" in k), None)
     fscale = (2 * n * 4) / (np.mean(cf[ck]) * 1024) if ck else None
     wscale = (n * 4) / (np.mean(cw[ck]) * 1024) if ck and ck in cw else None
-    lines = [f"# {workload}: MI355X kernel durations (rocprofv3 kernel trace) and HBM-side bytes per dispatch",
+    lines = [f"# {workload}: MI355X kernel durations (rocprofv3 kernel trace) and data-fabric bytes per dispatch",
              f"command_trace: {PROFILE_TRACE.format(w=workload)}",
              f"command_fetch: {PROFILE_PMC.format(counter='FETCH_SIZE', w=workload)}",
              f"command_write: {PROFILE_PMC.format(counter='WRITE_SIZE', w=workload)}",
@@ -843,43 +837,68 @@ def summarize_workload(workload, trace_csv, fetch_csv, write_csv, calib_fetch_cs
              "protocol: every call cold (inputs last touched > 1 GiB earlier); no warm steps",
              f"fetch_scale: {fscale:.5f}" if fscale else "fetch_scale: none",
              f"write_scale: {wscale:.5f}" if wscale else "write_scale: none",
-             "note: FETCH_SIZE counts the L2's fetches from the data fabric: reads served by the Infinity Cache "
-             "count as well as HBM reads",
+             "note: read_MB / write_MB are the L2's traffic to the data fabric (FETCH_SIZE / WRITE_SIZE): reads "
+             "the Infinity Cache serves count as well as HBM reads; the PMC passes run eagerly (no graph replay)",
              f"sources: {','.join(KERNEL_SOURCES)}",
              f"source_sha256_16: {sources_digest()}",
              "",
              f"{'kernel':70s} {'calls':>6s} {'avg_us':>8s} {'min_us':>8s} {'max_us':>8s} {'read_MB':>9s} {'write_MB':>9s}"]
-    def short(n):
-        return (n or "(first)").replace("nh::", "")
-
     for k, ds in dur.items():
         if not k.startswith("nh::"):
             continue
         rd = f"{np.mean(fet[k]) * 1024 * fscale / 1e6:9.2f}" if fscale and k in fet else f"{'-':>9s}"
         wr = f"{np.mean(wri[k]) * 1024 * wscale / 1e6:9.2f}" if wscale and k in wri else f"{'-':>9s}"
         lines.append(f"{k[:70]:70s} {len(ds):6d} {np.mean(ds):8.3f} {np.min(ds):8.3f} {np.max(ds):8.3f} {rd} {wr}")
-        for p, v in ctx.get(k, {}).items():
-            if len(v) >= 5:
-                lines.append(f"    after {short(p)[:57]:57s} {len(v):6d} {np.mean(v):8.3f}")
+        lines += _context_lines(ctx.get(k, {}), 57)
     open(out_path, "w").write("\n".join(lines) + "\n")
 
 
-def summarize_stats(stats_csv, out_path, command):
-    """rocprofv3 --stats kernel table of one command -> short text."""
+def _context_split(trace_csv):
+    """Each dispatch's duration grouped by kernel, then by the kernel
+    dispatched just before it (the same kernel in a reduction-only region,
+    the other passes in a step)."""
+    import collections
+    import csv
+    ctx = collections.OrderedDict()
+    prev = None
+    for r in sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Dispatch_Id"])):
+        name = _short_kernel(r["Kernel_Name"])
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        ctx.setdefault(name, collections.OrderedDict()).setdefault(prev, []).append(d)
+        prev = name
+    return ctx
+
+
+def _context_lines(by_prev, width):
+    out = []
+    for p, v in by_prev.items():
+        if len(v) >= 5:
+            out.append(f"    after {(p or '(first)').replace('nh::', '')[:width]:{width}s} {len(v):6d} {np.mean(v):8.3f}")
+    return out
+
+
+def summarize_stats(stats_csv, trace_csv, out_path, command):
+    """rocprofv3 --stats kernel table of one command -> short text, with each
+    library kernel's durations split by the kernel dispatched before it when
+    the kernel trace is given."""
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
+    ctx = _context_split(trace_csv) if trace_csv else {}
     lines = ["# rocprofv3 kernel-trace statistics (MI355X)", f"command: {command}",
              f"source_sha256_16: {sources_digest()}", "",
              f"{'kernel':80s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
     for r in rows:
-        lines.append(f"{_short_kernel(r['Name'])[:80]:80s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.3f} "
+        name = _short_kernel(r['Name'])
+        lines.append(f"{name[:80]:80s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.3f} "
                      f"{float(r['MinNs']) / 1e3:9.3f} {float(r['MaxNs']) / 1e3:9.3f}")
+        if name.startswith("nh::"):
+            lines += _context_lines(ctx.get(name, {}), 67)
     open(out_path, "w").write("\n".join(lines) + "\n")
 
 
 def _traffic_for(kernel_key, workload):
-    """HBM-side bytes per launch (read + write) of a kernel from the committed
-    counter summary of `workload`, if it was taken on the current kernel
+    """Data-fabric bytes per launch (read + write) of a kernel from the
+    committed counter summary of `workload`, if it was taken on the current kernel
     sources (else None)."""
     path = os.path.join(ROOT, "profiles", f"{workload}.txt")
     if not os.path.exists(path):
@@ -922,8 +941,8 @@ def main():
     ap.add_argument("--summarize", nargs=6, metavar=("WORKLOAD", "TRACE", "FETCH", "WRITE", "CALIB_FETCH",
                                                      "CALIB_WRITE"),
                     help="write profiles/<WORKLOAD>.txt from rocprofv3 csv files and exit")
-    ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "OUT"),
-                    help="write a profiles/ summary of a rocprofv3 --stats table and exit")
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "TRACE_CSV", "OUT"),
+                    help="write a profiles/ summary of a rocprofv3 --stats table (TRACE_CSV may be -) and exit")
     args = ap.parse_args()
     if args.summarize:
         w = args.summarize[0]
@@ -932,7 +951,8 @@ def main():
         return
     if args.summarize_stats:
         cmd = "rocprofv3 --kernel-trace --stats -f csv -d <dir> -o bench -- python3 bench.py"
-        summarize_stats(args.summarize_stats[0], args.summarize_stats[1], cmd)
+        tr = args.summarize_stats[1]
+        summarize_stats(args.summarize_stats[0], tr if tr != "-" else None, args.summarize_stats[2], cmd)
         return
     from bwd_bn_stats_amd import workloads as wl
     if args.list:
