@@ -16,7 +16,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libnormhip.so")
+# NORMHIP_LIBRARY names another build of the same library (the host-sanitizer
+# build of the test suite); by default the in-tree one.
+LIB_PATH = os.environ.get("NORMHIP_LIBRARY") or os.path.join(_HERE, "libnormhip.so")
 
 F32, BF16 = 0, 1
 _DT = {torch.float32: F32, torch.bfloat16: BF16}

@@ -64,9 +64,16 @@
 extern "C" {
 #endif
 
+/* The enums a caller passes in carry two range markers that are not valid
+ * values: they make every int value representable in the enum type, so an
+ * out-of-range value reaches the library's validation as a well-defined
+ * value and is rejected there (C++ gives an enum without them only the
+ * range of its enumerators' bits). */
 typedef enum {
     NH_F32 = 0,  /* IEEE binary32 */
-    NH_BF16 = 1  /* bfloat16, stored as uint16 bit patterns */
+    NH_BF16 = 1, /* bfloat16, stored as uint16 bit patterns */
+    NH_DTYPE_RANGE_MIN_ = -0x7fffffff - 1, /* range markers, not dtypes */
+    NH_DTYPE_RANGE_MAX_ = 0x7fffffff
 } nh_dtype;
 
 typedef enum {
@@ -217,7 +224,9 @@ nh_status bn_backward_stage(int stage, const void *dy, const void *x, nh_dtype i
 typedef enum {
     NH_ACT_NONE = 0,
     NH_ACT_RELU = 1,
-    NH_ACT_LEAKY_RELU = 2
+    NH_ACT_LEAKY_RELU = 2,
+    NH_ACT_RANGE_MIN_ = -0x7fffffff - 1, /* range markers, not activations */
+    NH_ACT_RANGE_MAX_ = 0x7fffffff
 } nh_act;
 
 /*
@@ -414,7 +423,9 @@ typedef enum {
     NH_K_ROWS_COEF = 16,      /* per-row gradient coefficients (wide or misaligned rows) */
     NH_K_BN_FWD_CHANNEL = 17, /* BatchNorm forward, one block per small channel */
     NH_K_BN_BWD_CHANNEL = 18, /* BatchNorm backward, one block per small channel */
-    NH_K_COUNT = 19
+    NH_K_COUNT = 19,
+    NH_K_RANGE_MIN_ = -0x7fffffff - 1, /* range markers, not kernel ids */
+    NH_K_RANGE_MAX_ = 0x7fffffff
 } nh_kernel;
 
 /* Static name of a kernel id; "" for an unknown id. */

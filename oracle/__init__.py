@@ -14,19 +14,23 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIBRARY names another build of oracle.c (the host-sanitizer build of
+# the test suite); by default the in-tree one.
+_LIB = os.environ.get("ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
 
 GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-Wall", "-Wextra",
              "-shared", "-fPIC"]
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c with gcc (plain C, no GPU code)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        subprocess.run(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"], check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+def build(force: bool = True, cc: str = "gcc", extra_flags=(), out: str | None = None) -> str:
+    """Compile oracle.c (plain C, no GPU code); by default with gcc into the
+    in-tree liboracle.so."""
+    out = out or _LIB
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        subprocess.run([cc, *GCC_FLAGS, *extra_flags, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, out)
+    return out
 
 
 _lib = None

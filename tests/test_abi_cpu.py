@@ -252,6 +252,7 @@ def test_measurement_validation():
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     """The binding has no fallback: a missing library is an ImportError."""
     import importlib.util
+    monkeypatch.delenv("NORMHIP_LIBRARY", raising=False)
     src = os.path.join(ROOT, "bwd_bn_stats_amd", "normhip.py")
     pkg = tmp_path / "pkg"
     pkg.mkdir()
