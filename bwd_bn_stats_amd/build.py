@@ -32,12 +32,42 @@ FLAGS = [
 ]
 
 
+# hipcc's per-kernel resource remarks.  Scratch (private memory) in these
+# streaming kernels means a spill or a stack object, which turns uniform
+# values into per-lane loads and serializes the memory pipeline.  Sources in
+# SCRATCH_FREE fail the build if any of their kernels uses scratch.  The row
+# backward kernels (LayerNorm, RMSNorm, bias+dropout+add) also instantiate
+# deep software pipelines for the "rows_depth" tuning override, some of which
+# spill by design; their scratch users are listed (SCRATCH_REPORT) but do not
+# fail the build.
+RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
+SCRATCH_FREE = {"bn_kernels.hip", "rows_fwd_kernels.hip", "rows_generic_kernels.hip", "calib_kernels.hip",
+                "api.cpp"}
+SCRATCH_REPORT = {}
+
+
+def _scratch_kernels(stderr: str):
+    bad, name = [], None
+    for line in stderr.splitlines():
+        if "remark: Function Name:" in line:
+            name = line.split("Function Name:", 1)[1].split("[")[0].strip()
+        elif "ScratchSize [bytes/lane]:" in line or "VGPRs Spill:" in line or "SGPRs Spill:" in line:
+            key, val = line.split("remark:", 1)[1].split("[-Rpass")[0].rsplit(":", 1)
+            if int(val.strip() or 0) > 0:
+                bad.append(f"{name}: {key.strip()} {val.strip()}")
+    return bad
+
+
 def _compile(src: str, build_dir: str, extra_flags) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, RESOURCE_REMARKS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    bad = _scratch_kernels(r.stderr)
+    if bad and src in SCRATCH_FREE:
+        raise RuntimeError(f"kernels in {src} use scratch memory:\n" + "\n".join(bad))
+    SCRATCH_REPORT[src] = bad
     return obj
 
 
@@ -55,6 +85,9 @@ def build(verbose: bool = False, extra_flags=(), link_flags=(), lib: str = LIB, 
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, lib)
     if verbose:
+        spill = sorted({b.split(":")[0] for bad in SCRATCH_REPORT.values() for b in bad})
+        if spill:
+            print(f"{len(spill)} row-kernel variants use scratch (tuning-override pipeline depths)")
         print(f"built {lib}")
     return lib
 

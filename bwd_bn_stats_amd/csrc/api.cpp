@@ -97,6 +97,7 @@ std::atomic<int64_t> g_override_rows_teams{0};
 std::atomic<int64_t> g_override_bn_channel{0};
 std::atomic<int64_t> g_override_bn_channel_threads{0};
 std::atomic<int64_t> g_override_rows_narrow{0};
+std::atomic<int64_t> g_override_bn_block_order{0};
 
 // ---- BatchNorm planning ----------------------------------------------------------
 // Resident 256-thread block slots of the device: CUs * (threads per CU / 256),
@@ -164,6 +165,24 @@ int bn_channel_threads(int64_t units, int64_t C, int64_t slots)
     if (ov == kBnThreads || ov == kBnChannelBigBlock) return (int)ov;
     const bool big = (8 * C <= slots && units > kBnMinUnits) || (4 * C <= slots && units > 2 * kBnMinUnits);
     return big ? kBnChannelBigBlock : kBnThreads;
+}
+
+// Block numbering of the split BatchNorm passes (bn_block): channel-fastest
+// unless the "bn_block_order" override asks for channel-major (1) or
+// channel-fastest (2).  Measured on MI355X, cold per call, the same box,
+// channel-major -> channel-fastest: (256,32,32,32) fp32 fwd+bwd 42.2 ->
+// 40.5 us (all four passes faster), inference + ReLU at that shape 13.9 ->
+// 13.0 us and at (64,256,56,56) bf16 39.1 -> 37.5 us; (64,256,56,56) bf16
+// and (256,32,32,32) bf16 fwd+bwd within 0.5% either way.  A probe of the
+// bare access pattern showed the same: reading the fp32 tensor by channel
+// runs took 8.2 us in channel-major order, 7.4 us channel-fastest and 7.2 us
+// as contiguous chunks.
+int bn_chan_fast()
+{
+    const int64_t ov = g_override_bn_block_order.load();
+    if (ov == 1) return 0;
+    if (ov == 2) return 1;
+    return 1;
 }
 
 // Largest grid_y any dtype/alignment can take for this shape (scalar units).
@@ -561,6 +580,7 @@ static nh_status bn_forward_impl(int stage, const void *x, void *y, nh_dtype io,
     a.vec = bn_vec(io, HW, x, y, nullptr);
     a.grid_y = (int)bn_grid_y_for(N * (HW / a.vec), C, d);
     a.ew_grid_y = (int)bn_ew_grid_y_for(N * (HW / a.vec), C, d);
+    a.chan_fast = bn_chan_fast();
     a.x = x;
     a.out = y;
     a.gamma = gamma;
@@ -688,6 +708,7 @@ static nh_status bn_backward_impl(int stage, const void *dy, const void *x, nh_d
     a.vec = bn_vec(io, HW, x, dy, dx);
     a.grid_y = (int)bn_grid_y_for(N * (HW / a.vec), C, d);
     a.ew_grid_y = (int)bn_ew_grid_y_for(N * (HW / a.vec), C, d);
+    a.chan_fast = bn_chan_fast();
     a.x = x;
     a.dy = dy;
     a.out = dx;
@@ -754,6 +775,7 @@ nh_status bn_forward_infer(const void *x, void *y, nh_dtype io, int64_t N, int64
     a.vec = bn_vec(io, HW, x, y, nullptr);
     a.grid_y = (int)bn_grid_y_for(N * (HW / a.vec), C, d);
     a.ew_grid_y = (int)bn_ew_grid_y_for(N * (HW / a.vec), C, d);
+    a.chan_fast = bn_chan_fast();
     a.inference = 1;
     a.x = x;
     a.out = y;
@@ -1258,6 +1280,10 @@ nh_status nh_plan_override(const char *key, int64_t value)
         g_override_rows_teams.store(value);
     }
     else if (strcmp(key, "bn_finalize_kernels") == 0) g_override_bn_finalize_kernels.store(value);
+    else if (strcmp(key, "bn_block_order") == 0) {
+        if (value > 2) return fail(NH_ERR_ARG, "bn_block_order must be 0, 1 or 2");
+        g_override_bn_block_order.store(value);
+    }
     else return fail(NH_ERR_ARG, "unknown override key '%s'", key);
     return ok();
 }
@@ -1315,7 +1341,7 @@ nh_status nh_selftest_host(void)
         // one block per channel, the planned split, and 2048 blocks per channel
         for (int64_t grid_y : {(int64_t)1, bn_auto_grid_y(units, m.C, slots),
                                std::min<int64_t>(units, 2048)}) {
-            const BnGeom g = make_bn_geom(m.N, m.C, m.HW, m.vec, (int)grid_y);
+            const BnGeom g = make_bn_geom(m.N, m.C, m.HW, m.vec, (int)grid_y, 0);
             const uint64_t stride = (uint64_t)kBnThreads * kBnUnroll;
             for (int c = 0; c < m.C; c += (m.C > 1 ? m.C - 1 : 1)) {
                 for (int yb = 0; yb < g.grid_y; ++yb) {

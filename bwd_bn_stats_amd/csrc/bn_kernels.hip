@@ -178,8 +178,8 @@ template <typename T, int V, int NT>
 __global__ void __launch_bounds__(kBnThreads)
 bn_stats_kernel(const T *__restrict__ x, BnGeom g, float *__restrict__ partials)
 {
-    const int c = blockIdx.x / g.grid_y;
-    const int yb = blockIdx.x - c * g.grid_y;
+    const BnBlock blk = bn_block(g);
+    const int c = blk.c, yb = blk.yb;
     // Unit indices are unsigned: a channel may hold up to 2^31 - 1 units,
     // and the loop index runs up to a stride past the last one.
     const uint32_t u0 = (uint32_t)yb * (uint32_t)g.upb;
@@ -244,8 +244,8 @@ bn_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x,
                     const float *__restrict__ stats, const float *__restrict__ beta, float slope,
                     BnGeom g, float *__restrict__ partials)
 {
-    const int c = blockIdx.x / g.grid_y;
-    const int yb = blockIdx.x - c * g.grid_y;
+    const BnBlock blk = bn_block(g);
+    const int c = blk.c, yb = blk.yb;
     // Unit indices are unsigned: a channel may hold up to 2^31 - 1 units,
     // and the loop index runs up to a stride past the last one.
     const uint32_t u0 = (uint32_t)yb * (uint32_t)g.upb;
@@ -418,8 +418,8 @@ __global__ void __launch_bounds__(kBnThreads)
 bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ stats,
                 const float *__restrict__ beta, BnGeom g, FwdFinalizeArgs f, float slope)
 {
-    const int c = blockIdx.x / g.grid_y;
-    const int yb = blockIdx.x - c * g.grid_y;
+    const BnBlock blk = bn_block(g);
+    const int c = blk.c, yb = blk.yb;
     // Unit indices are unsigned: a channel may hold up to 2^31 - 1 units,
     // and the loop index runs up to a stride past the last one.
     const uint32_t u0 = (uint32_t)yb * (uint32_t)g.upb;
@@ -491,8 +491,8 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
              const float *__restrict__ partials, int red_grid_y, int64_t M,
              const float *__restrict__ beta, float slope)
 {
-    const int c = blockIdx.x / g.grid_y;
-    const int yb = blockIdx.x - c * g.grid_y;
+    const BnBlock blk = bn_block(g);
+    const int c = blk.c, yb = blk.yb;
     // Unit indices are unsigned: a channel may hold up to 2^31 - 1 units,
     // and the loop index runs up to a stride past the last one.
     const uint32_t u0 = (uint32_t)yb * (uint32_t)g.upb;
@@ -1201,8 +1201,8 @@ static hipError_t bn_col_backward_t(const BnCall &a, hipStream_t s)
 template <typename T, int V, int ACT>
 static hipError_t bn_forward_t(const BnCall &a, hipStream_t s)
 {
-    const BnGeom gr = make_bn_geom(a.N, a.C, a.HW, a.vec, a.grid_y);
-    const BnGeom ge = make_bn_geom(a.N, a.C, a.HW, a.vec, a.ew_grid_y);
+    const BnGeom gr = make_bn_geom(a.N, a.C, a.HW, a.vec, a.grid_y, a.chan_fast);
+    const BnGeom ge = make_bn_geom(a.N, a.C, a.HW, a.vec, a.ew_grid_y, a.chan_fast);
     const T *x = static_cast<const T *>(a.x);
     const dim3 rgrid((unsigned)(a.C * a.grid_y)), egrid((unsigned)(a.C * a.ew_grid_y)), block(kBnThreads);
     const int64_t M = (int64_t)a.N * a.HW;
@@ -1213,7 +1213,7 @@ static hipError_t bn_forward_t(const BnCall &a, hipStream_t s)
     if (a.channel_fused) {
         // one kernel per direction: it runs as the second stage
         if (a.stage == 1) return hipSuccess;
-        const BnGeom g1 = make_bn_geom(a.N, a.C, a.HW, a.vec, 1);
+        const BnGeom g1 = make_bn_geom(a.N, a.C, a.HW, a.vec, 1, 0);
         if (a.channel_threads == kBnChannelBigBlock)
             return launch(NH_K_BN_FWD_CHANNEL, bn_fwd_channel_kernel<T, V, kBnNtPolicy, ACT, kBnChannelBigBlock>,
                           dim3((unsigned)a.C), dim3(kBnChannelBigBlock), 0, s, x, static_cast<T *>(a.out),
@@ -1243,15 +1243,15 @@ static hipError_t bn_forward_t(const BnCall &a, hipStream_t s)
 template <typename T, int V, int ACT>
 static hipError_t bn_backward_t(const BnCall &a, hipStream_t s)
 {
-    const BnGeom gr = make_bn_geom(a.N, a.C, a.HW, a.vec, a.grid_y);
-    const BnGeom ge = make_bn_geom(a.N, a.C, a.HW, a.vec, a.ew_grid_y);
+    const BnGeom gr = make_bn_geom(a.N, a.C, a.HW, a.vec, a.grid_y, a.chan_fast);
+    const BnGeom ge = make_bn_geom(a.N, a.C, a.HW, a.vec, a.ew_grid_y, a.chan_fast);
     const T *x = static_cast<const T *>(a.x);
     const T *dy = static_cast<const T *>(a.dy);
     const dim3 rgrid((unsigned)(a.C * a.grid_y)), egrid((unsigned)(a.C * a.ew_grid_y)), block(kBnThreads);
     const int64_t M = (int64_t)a.N * a.HW;
     if (a.channel_fused) {
         if (a.stage == 1) return hipSuccess;
-        const BnGeom g1 = make_bn_geom(a.N, a.C, a.HW, a.vec, 1);
+        const BnGeom g1 = make_bn_geom(a.N, a.C, a.HW, a.vec, 1, 0);
         if (a.channel_threads == kBnChannelBigBlock)
             return launch(NH_K_BN_BWD_CHANNEL, bn_bwd_channel_kernel<T, V, kBnNtPolicy, ACT, kBnChannelBigBlock>,
                           dim3((unsigned)a.C), dim3(kBnChannelBigBlock), 0, s, dy, x, static_cast<T *>(a.out),

@@ -58,7 +58,32 @@ struct BnGeom {
     int units;      // units per channel (N * HWv)
     int upb;        // units per block
     int grid_y;
+    int chan_fast;  // block numbering: 0 channel-major, 1 channel-fastest (bn_block)
 };
+
+// Block id -> (channel c, block yb of that channel).  Channel-major: the
+// grid_y blocks of a channel have consecutive ids.  Channel-fastest:
+// consecutive ids take consecutive channels at the same yb, so the blocks
+// dispatched first cover the first planes of every channel, one contiguous
+// stretch of the tensor, and the launch walks memory in address order.
+// Every pass of one call uses the same numbering, so an elementwise block
+// still re-reads the units that the reduction block of its id read.
+//
+// One division and two value selects: assigning c and yb in the two arms of
+// a branch let the compiler merge the arms into stores through a selected
+// address, which put both in scratch memory and made every address that
+// depends on them a per-lane value.
+struct BnBlock {
+    int c, yb;
+};
+__device__ __forceinline__ BnBlock bn_block(const BnGeom &g)
+{
+    const int b = (int)blockIdx.x;
+    const int d = g.chan_fast ? g.C : g.grid_y;
+    const int q = b / d;
+    const int r = b - q * d;
+    return {g.chan_fast ? r : q, g.chan_fast ? q : r};
+}
 
 // Element offset of unit u of channel c.  Unsigned arithmetic: callers may
 // form the offset of a unit past the end (never dereferenced), which must
@@ -71,9 +96,10 @@ __host__ __device__ __forceinline__ int bn_unit_offset(const BnGeom &g, int c, u
     return (int)((n * (uint32_t)g.C + (uint32_t)c) * (uint32_t)g.HW + j * (uint32_t)V);
 }
 
-inline BnGeom make_bn_geom(int N, int C, int HW, int vec, int grid_y)
+inline BnGeom make_bn_geom(int N, int C, int HW, int vec, int grid_y, int chan_fast)
 {
     BnGeom g;
+    g.chan_fast = chan_fast;
     g.C = C;
     g.HW = HW;
     g.HWv = HW / vec;
@@ -172,6 +198,7 @@ struct BnCall {
     int vec;             // unit width in elements: fp32 4 or 1; bf16 8, 4 or 1
     int grid_y;          // blocks per channel of the reduction passes (stats, grad_sums)
     int ew_grid_y;       // blocks per channel of the elementwise passes (apply, dx)
+    int chan_fast;       // block numbering of the split passes (BnGeom::chan_fast)
     int separate_finalize;  // 1: finalize as its own kernel; 0: in the elementwise prologue
     int inference;       // forward only: apply with the running statistics, no reduction
     int channel_fused;   // 1: one block per channel, reduction + finalize + elementwise in one kernel

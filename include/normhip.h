@@ -498,7 +498,9 @@ nh_status nh_rows_plan(int64_t rows, int64_t cols, int *blocks);
  * on the 256-thread team kernels instead of the lane-subgroup kernels, key
  * "rows_teams" = 1 or 2 forces the row teams per block of the
  * LayerNorm and RMSNorm backwards' vector kernels (same results up to the
- * order of the column sums).  value 0 restores the automatic plan.  Process-wide; not for concurrent use with
+ * order of the column sums), key "bn_block_order" = 1 or 2 numbers the split
+ * BatchNorm passes' blocks channel-major or channel-fastest (same results).
+ * value 0 restores the automatic plan.  Process-wide; not for concurrent use with
  * other calls.
  */
 nh_status nh_plan_override(const char *key, int64_t value);

@@ -304,6 +304,28 @@ def test_bn_separate_finalize_kernels_match_fused(nh, oracle_mod, name):
         assert np.array_equal(fused[k].view(np.uint64), separate[k].view(np.uint64)), k
 
 
+@pytest.mark.parametrize("name", ["cifar_256x32x32x32_f32", "resnet_64x256x56x56_bf16",
+                                  "odd_plane_3x6x5x5_bf16", "one_channel_64x1x128x128_f32"])
+def test_bn_block_orders_match(nh, oracle_mod, name):
+    """Channel-major and channel-fastest block numbering of the split passes
+    give the same bits (each block's units and the partial slots it writes do
+    not depend on the numbering), and the oracle's results."""
+    c = CASES[name]()
+    print(f"[bn parity] block orders {name}", flush=True)
+    nh.plan_override("bn_channel", 1)
+    try:
+        nh.plan_override("bn_block_order", 1)
+        major = _gpu_bn(nh, c)
+        nh.plan_override("bn_block_order", 2)
+        fastest = _gpu_bn(nh, c)
+    finally:
+        nh.plan_override("bn_block_order", 0)
+        nh.plan_override("bn_channel", 0)
+    _compare(c, fastest, _oracle_bn(oracle_mod, c))
+    for k in major:
+        assert np.array_equal(major[k].view(np.uint64), fastest[k].view(np.uint64)), k
+
+
 @pytest.mark.parametrize("offset", [0, 2, 4])
 def test_bn_bf16_unit_widths_by_alignment(nh, oracle_mod, offset):
     """bf16 planes of 4k elements at element offsets 0, 2, 4: 8-byte units
