@@ -767,6 +767,16 @@ def _roofline(res, traffic_tag):
 KERNEL_SOURCES = ["bn_kernels.hip", "nh_device.hpp", "nh_internal.hpp", "nh_bn.hpp", "rows_kernels.hip",
                   "rows_common.hpp", "nh_rows.hpp", "rows_fwd_kernels.hip", "rows_bda_kernels.hip",
                   "rows_generic_kernels.hip", "calib_kernels.hip"]
+_COMMON_SOURCES = ["nh_device.hpp", "nh_internal.hpp"]
+_BN_SOURCES = ["bn_kernels.hip", "nh_bn.hpp"] + _COMMON_SOURCES
+_ROWS_SOURCES = ["rows_kernels.hip", "rows_common.hpp", "nh_rows.hpp", "rows_fwd_kernels.hip",
+                 "rows_bda_kernels.hip", "rows_generic_kernels.hip"] + _COMMON_SOURCES
+
+
+def workload_sources(workload):
+    """The kernel sources a workload's kernels are compiled from: a counter
+    summary stays valid until one of these changes."""
+    return _BN_SOURCES if workload.startswith("bn") else _ROWS_SOURCES
 PROFILE_TRACE = ("rocprofv3 --kernel-trace --stats -f csv -d <dir> -o {w} -- python3 bench.py --workloads {w} "
                  "--steps 20 --warmup 3 --reps 3 --no-cpu-baseline --no-floors")
 PROFILE_PMC = ("rocprofv3 --pmc {counter} -f csv -d <dir> -o {w} -- python3 bench.py --workloads {w} --steps 4 "
@@ -839,8 +849,8 @@ def summarize_workload(workload, trace_csv, fetch_csv, write_csv, calib_fetch_cs
              f"write_scale: {wscale:.5f}" if wscale else "write_scale: none",
              "note: read_MB / write_MB are the L2's traffic to the data fabric (FETCH_SIZE / WRITE_SIZE): reads "
              "the Infinity Cache serves count as well as HBM reads; the PMC passes run eagerly (no graph replay)",
-             f"sources: {','.join(KERNEL_SOURCES)}",
-             f"source_sha256_16: {sources_digest()}",
+             f"sources: {','.join(workload_sources(workload))}",
+             f"source_sha256_16: {sources_digest(workload_sources(workload))}",
              "",
              f"{'kernel':70s} {'calls':>6s} {'avg_us':>8s} {'min_us':>8s} {'max_us':>8s} {'read_MB':>9s} {'write_MB':>9s}"]
     for k, ds in dur.items():
@@ -909,7 +919,7 @@ def _traffic_for(kernel_key, workload):
             digest = line.split(":", 1)[1].strip()
         elif line.startswith("nh::"):
             rows.append((line[:70].strip(), line[70:].split()))
-    if digest != sources_digest():
+    if digest != sources_digest(workload_sources(workload)):
         return None
     want = "nh::" + {"bn_stats": "bn_stats_kernel", "bn_grad_sums": "bn_grad_sums_kernel",
                      "bn_apply": "bn_apply_kernel", "bn_dx": "bn_dx_kernel"}.get(kernel_key, kernel_key)
