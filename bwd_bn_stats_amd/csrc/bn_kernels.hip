@@ -102,11 +102,12 @@ __device__ __forceinline__ float act_bwd(float dy, float z, float slope)
 }
 
 // Sums of (a, b) over a 256-thread block; the result is valid in thread 0.
+// The wave sums are DPP steps (wave_total), then the waves in index order.
 __device__ __forceinline__ void block_sum2(float &a, float &b)
 {
     __shared__ float red[kBnThreads / kWave][2];
-    a = wave_sum(a);
-    b = wave_sum(b);
+    a = wave_total(a);
+    b = wave_total(b);
     const int wave = threadIdx.x / kWave;
     if ((threadIdx.x & (kWave - 1)) == 0) {
         red[wave][0] = a;
@@ -134,8 +135,8 @@ __device__ __forceinline__ void block_sum2_tb(float &a, float &b)
         block_sum2(a, b);
     } else {
         __shared__ float red[TB / kWave][2];
-        a = wave_sum(a);
-        b = wave_sum(b);
+        a = wave_total(a);
+        b = wave_total(b);
         const int wave = threadIdx.x / kWave;
         if ((threadIdx.x & (kWave - 1)) == 0) {
             red[wave][0] = a;
@@ -163,6 +164,23 @@ __device__ __forceinline__ float load_shift(const float *p)
 {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p, 4u), 0, 0, 0));
 }
+
+// A per-channel fp32 value (stats, gamma, beta, a shift, running
+// statistics) read with a vector memory load, for the same reason: issued
+// right after a pass's first loads of x, it arrives with them, where a
+// scalar load would add a memory round trip before the elementwise work.
+__device__ __forceinline__ float ldv(const float *p) { return load_shift(p); }
+
+// p[i] by a vector memory load, or 0 when `on` is false or p is NULL: the
+// buffer range is then empty and the load touches no memory.  No branch
+// surrounds the load, so the compiler keeps it in flight with the caller's
+// other loads (a load under a branch is waited for where the branches meet).
+__device__ __forceinline__ float ldv_if(const float *p, int i, bool on)
+{
+    const bool live = on && p != nullptr;
+    return __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(live ? p + i : p, live ? 4u : 0u), 0, 0, 0));
+}
 __device__ __forceinline__ float load_shift(const uint16_t *p)
 {
     // the bf16 bits straight into the high half of a zeroed register: the
@@ -175,7 +193,7 @@ __device__ __forceinline__ float load_shift(const uint16_t *p)
 
 // ---- forward reduction: shifted one-pass sums ------------------------------
 template <typename T, int V, int NT>
-__global__ void __launch_bounds__(kBnThreads)
+__global__ void __launch_bounds__(kBnThreads, kBnWavesPerSimd)
 bn_stats_kernel(const T *__restrict__ x, BnGeom g, float *__restrict__ partials)
 {
     const BnBlock blk = bn_block(g);
@@ -239,7 +257,7 @@ bn_stats_kernel(const T *__restrict__ x, BnGeom g, float *__restrict__ partials)
 // ---- backward reduction: sum dy, sum dy*(x - mean) ----------------------------
 // With an activation, dy is first replaced by dz = dy * act'(z).
 template <typename T, int V, int NT, int ACT>
-__global__ void __launch_bounds__(kBnThreads)
+__global__ void __launch_bounds__(kBnThreads, kBnWavesPerSimd)
 bn_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x,
                     const float *__restrict__ stats, const float *__restrict__ beta, float slope,
                     BnGeom g, float *__restrict__ partials)
@@ -294,30 +312,89 @@ bn_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x,
 }
 
 // ---- finalize: one wave per channel, fp64 fixed-order combine -----------------
-// Lane l sums slots l, l+64, ... in order; the butterfly then combines lanes.
-__device__ __forceinline__ void sum_partials(const float *__restrict__ partials, int grid_y,
-                                             int C, int c, double &s1, double &s2)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    double a = 0.0, b = 0.0;
-    for (int yb = lane; yb < grid_y; yb += kWave) {
-        a += (double)partials[(0 * grid_y + yb) * C + c];
-        b += (double)partials[(1 * grid_y + yb) * C + c];
+// Lane l sums slots l, l+64, ... in order; the DPP wave total then combines
+// the lanes.  The loads (load) are separate from the sums (sum) so that an
+// elementwise pass issues them together with its first loads of x: they
+// arrive with that data instead of a memory round trip after it.  Lanes hold
+// up to S slots in registers (grid_y <= 64*S); the rest are read in the sum.
+// The elementwise prologues hold 2 (every channel count of at least 16 at
+// 2048 resident blocks), which keeps the fused dx pass within the 64 VGPRs of
+// 8 waves per SIMD; the finalize kernels hold 4.
+constexpr int kFinSlotsEw = 2;
+constexpr int kFinSlotsKernel = 4;
+template <int S>
+struct PartialSlots {
+    float a[S], b[S];
+
+    // BUF: through buffer resources over the channel's two columns of slots,
+    // so that a slot past grid_y reads 0 without a branch or a memory access
+    // and the loads stay in flight with the caller's (byte offsets yb*C*4:
+    // the host plan keeps grid_y*C*4 below 2^31 for this form).  Else plain
+    // loads.
+    template <bool BUF>
+    __device__ __forceinline__ void load(const float *__restrict__ partials, int grid_y, int C, int c)
+    {
+        const int lane = threadIdx.x & (kWave - 1);
+        if constexpr (BUF) {
+            const uint32_t span = (uint32_t)(grid_y - 1) * (uint32_t)C * 4u + 4u;
+            const auto r0 = make_rsrc(partials + c, span);
+            const auto r1 = make_rsrc(partials + (size_t)grid_y * C + c, span);
+#pragma unroll
+            for (int k = 0; k < S; ++k) {
+                const int yb = lane + k * kWave;
+                const uint32_t off = yb < grid_y ? (uint32_t)yb * (uint32_t)C * 4u : span;
+                a[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r0, off, 0, 0));
+                b[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, off, 0, 0));
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < S; ++k) {
+                const int yb = lane + k * kWave;
+                a[k] = yb < grid_y ? partials[(0 * grid_y + yb) * C + c] : 0.f;
+                b[k] = yb < grid_y ? partials[(1 * grid_y + yb) * C + c] : 0.f;
+            }
+        }
     }
-    s1 = wave_sum(a);
-    s2 = wave_sum(b);
+    // Called by all 64 lanes of a wave (the wave total needs every lane).
+    __device__ __forceinline__ void sum(const float *__restrict__ partials, int grid_y, int C, int c, double &s1,
+                                        double &s2) const
+    {
+        const int lane = threadIdx.x & (kWave - 1);
+        double x = 0.0, y = 0.0;
+#pragma unroll
+        for (int k = 0; k < S; ++k) {
+            if (lane + k * kWave < grid_y) {
+                x += (double)a[k];
+                y += (double)b[k];
+            }
+        }
+        for (int yb = lane + S * kWave; yb < grid_y; yb += kWave) {
+            x += (double)partials[(0 * grid_y + yb) * C + c];
+            y += (double)partials[(1 * grid_y + yb) * C + c];
+        }
+        s1 = wave_total(x);
+        s2 = wave_total(y);
+    }
+};
+
+__device__ __forceinline__ void sum_partials(const float *__restrict__ partials, int grid_y, int C, int c,
+                                             double &s1, double &s2)
+{
+    PartialSlots<kFinSlotsKernel> ps;
+    ps.load<false>(partials, grid_y, C, c);
+    ps.sum(partials, grid_y, C, c, s1, s2);
 }
 
-// Forward finalize of channel c from its shifted sums (called by one lane):
-// stats[4, C] = (mean, var, inv_std, scale) and the running statistics.
-// Returns mean and scale for the caller's apply.
-__device__ __forceinline__ void fwd_finalize_channel(double S1, double S2, float K, int C, int c,
-                                                     int64_t M, const float *__restrict__ gamma,
-                                                     float *__restrict__ running_mean,
-                                                     float *__restrict__ running_var,
-                                                     float momentum, float eps, bool write,
-                                                     float *__restrict__ stats, float &mean_out,
-                                                     float &scale_out)
+// Forward finalize of channel c from its shifted sums, every input given:
+// gm = gamma[c] (or 1), rm / rv = the running statistics before the update
+// (used only when write).  stats[4, C] = (mean, var, inv_std, scale) and the
+// running statistics are written when `write` (one lane of the grid per
+// channel).  Returns mean and scale for the caller's apply.
+__device__ __forceinline__ void fwd_finalize_core(double S1, double S2, float K, int C, int c, int64_t M,
+                                                  double gm, float rm, float rv, float *__restrict__ running_mean,
+                                                  float *__restrict__ running_var, float momentum, float eps,
+                                                  bool write, float *__restrict__ stats, float &mean_out,
+                                                  float &scale_out)
 {
     const double Md = (double)M;
     const double md = S1 / Md;                    // mean of the shifted values
@@ -325,7 +402,6 @@ __device__ __forceinline__ void fwd_finalize_channel(double S1, double S2, float
     if (var < 0.0) var = 0.0;
     const double mean = (double)K + md;
     const double inv_std = 1.0 / sqrt(var + (double)eps);
-    const double gm = gamma ? (double)gamma[c] : 1.0;
     const float meanf = (float)mean, scalef = (float)(gm * inv_std);
     mean_out = meanf;
     scale_out = scalef;
@@ -335,22 +411,35 @@ __device__ __forceinline__ void fwd_finalize_channel(double S1, double S2, float
     stats[2 * C + c] = (float)inv_std;
     stats[3 * C + c] = scalef;
     const double m = (double)momentum;
-    if (running_mean)
-        running_mean[c] = (float)((1.0 - m) * (double)running_mean[c] + m * mean);
-    if (running_var)
-        running_var[c] = (float)((1.0 - m) * (double)running_var[c] + m * var * Md / (Md - 1.0));
+    if (running_mean) running_mean[c] = (float)((1.0 - m) * (double)rm + m * mean);
+    if (running_var) running_var[c] = (float)((1.0 - m) * (double)rv + m * var * Md / (Md - 1.0));
 }
 
-// Backward finalize of channel c (called by one lane): grads[4, C] =
-// (dgamma, dbeta, k1, k2) with k1 = -scale*inv_std^2*S/M, k2 = -scale*dbeta/M.
-__device__ __forceinline__ void bwd_finalize_channel(double Sdy, double Sdyxc, int C, int c, int64_t M,
-                                                     const float *__restrict__ stats, bool write,
-                                                     float *__restrict__ grads, float &k1_out,
-                                                     float &k2_out)
+// The same, reading gamma and the running statistics itself (called by one
+// lane).
+__device__ __forceinline__ void fwd_finalize_channel(double S1, double S2, float K, int C, int c,
+                                                     int64_t M, const float *__restrict__ gamma,
+                                                     float *__restrict__ running_mean,
+                                                     float *__restrict__ running_var,
+                                                     float momentum, float eps, bool write,
+                                                     float *__restrict__ stats, float &mean_out,
+                                                     float &scale_out)
+{
+    const double gm = gamma ? (double)gamma[c] : 1.0;
+    const float rm = (write && running_mean) ? running_mean[c] : 0.f;
+    const float rv = (write && running_var) ? running_var[c] : 0.f;
+    fwd_finalize_core(S1, S2, K, C, c, M, gm, rm, rv, running_mean, running_var, momentum, eps, write, stats,
+                      mean_out, scale_out);
+}
+
+// Backward finalize of channel c: grads[4, C] = (dgamma, dbeta, k1, k2)
+// with k1 = -scale*inv_std^2*S/M, k2 = -scale*dbeta/M, from inv_std and
+// scale (stats rows 2 and 3); grads written when `write`.
+__device__ __forceinline__ void bwd_finalize_core(double Sdy, double Sdyxc, int C, int c, int64_t M,
+                                                  double inv_std, double scale, bool write,
+                                                  float *__restrict__ grads, float &k1_out, float &k2_out)
 {
     const double Md = (double)M;
-    const double inv_std = (double)stats[2 * C + c];
-    const double scale = (double)stats[3 * C + c];
     const float k1 = (float)(-scale * inv_std * inv_std * Sdyxc / Md);
     const float k2 = (float)(-scale * Sdy / Md);
     k1_out = k1;
@@ -360,6 +449,16 @@ __device__ __forceinline__ void bwd_finalize_channel(double Sdy, double Sdyxc, i
     grads[1 * C + c] = (float)Sdy;                // dbeta
     grads[2 * C + c] = k1;
     grads[3 * C + c] = k2;
+}
+
+// The same, reading inv_std and scale from stats (called by one lane).
+__device__ __forceinline__ void bwd_finalize_channel(double Sdy, double Sdyxc, int C, int c, int64_t M,
+                                                     const float *__restrict__ stats, bool write,
+                                                     float *__restrict__ grads, float &k1_out,
+                                                     float &k2_out)
+{
+    bwd_finalize_core(Sdy, Sdyxc, C, c, M, (double)stats[2 * C + c], (double)stats[3 * C + c], write, grads,
+                      k1_out, k2_out);
 }
 
 __global__ void __launch_bounds__(kBnThreads)
@@ -392,11 +491,21 @@ bn_bwd_finalize(const float *__restrict__ partials, int grid_y, int C, int64_t M
 }
 
 // ---- elementwise passes ------------------------------------------------------
-// FUSED: the block first finalizes its own channel from the partials (wave 0,
-// fixed order, the same arithmetic as the finalize kernels; block yb == 0
-// writes stats/grads and the running statistics), with its first loads of x
-// already in flight.  This removes the finalize launch from the dependency
-// chain at the cost of every block re-reading its channel's grid_y partials.
+// FUSED: wave 0 of every block finalizes the block's channel from the
+// partials (fixed order, the same arithmetic as the finalize kernels; lane 0
+// of block yb == 0 writes stats/grads and the running statistics) and passes
+// the two per-channel constants to the other waves through LDS.  All of the
+// pass's per-channel inputs -- partial slots, shift, gamma, beta, stats,
+// running statistics -- are vector loads issued right after the first loads
+// of x, before any is used, so they arrive together with that data: the
+// elementwise work starts one memory round trip after the launch, plus the
+// fp64 arithmetic.  (Read in a second round trip, as the scalar loads of an
+// earlier version were, they cost a round trip per pass.)  One wave per block
+// does the fp64 work: with every wave doing it, the eight waves of a SIMD
+// ran the same divisions and square roots one after the other, which
+// measured 15-28% slower at (256,32,32,32).  This removes the finalize
+// launch from the dependency chain at the cost of every block re-reading its
+// channel's grid_y partials (L2 hits).
 struct FwdFinalizeArgs {
     const float *partials;
     int red_grid_y;  // blocks per channel of the reduction that wrote the partials
@@ -414,7 +523,7 @@ enum : int {
 };
 
 template <typename T, int V, int SRC, int NT, int ACT>
-__global__ void __launch_bounds__(kBnThreads)
+__global__ void __launch_bounds__(kBnThreads, kBnWavesPerSimd)
 bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ stats,
                 const float *__restrict__ beta, BnGeom g, FwdFinalizeArgs f, float slope)
 {
@@ -424,7 +533,6 @@ bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ 
     // and the loop index runs up to a stride past the last one.
     const uint32_t u0 = (uint32_t)yb * (uint32_t)g.upb;
     const uint32_t u1 = min(u0 + (uint32_t)g.upb, (uint32_t)g.units);
-    const float b = beta ? beta[c] : 0.f;
 
     uint32_t base = u0 + threadIdx.x;
     Raw<T, V> v[kBnUnroll];
@@ -436,30 +544,50 @@ bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ 
         if (u < u1) ldr<(NT & kNtEwLoads) != 0>(v[k], x + off[k]);
     }
 
+    // The per-channel inputs, loaded together with the first units of x.
+    // Every load is issued before any result is used (the scheduling barrier):
+    // loads complete in issue order, so an early use of one would wait for the
+    // loads of x as well, and the later loads would start a round trip after.
+    const float b = ldv_if(beta, c, true);
     float mean, scale;
     if constexpr (SRC == kApplyFinalize) {
         __shared__ float sh[2];
-        if (threadIdx.x < kWave) {
+        if (threadIdx.x < kWave) {  // wave 0
+            PartialSlots<kFinSlotsEw> ps;
+            ps.load<true>(f.partials, f.red_grid_y, g.C, c);
+            const float K = ldv(f.partials + 2 * f.red_grid_y * g.C + c);
+            const float gv = ldv_if(f.gamma, c, true);
+            const float rm = ldv_if(f.running_mean, c, yb == 0);
+            const float rv = ldv_if(f.running_var, c, yb == 0);
+            __builtin_amdgcn_sched_barrier(0);
+            const double gm = f.gamma ? (double)gv : 1.0;
             double S1, S2;
-            sum_partials(f.partials, f.red_grid_y, g.C, c, S1, S2);
+            ps.sum(f.partials, f.red_grid_y, g.C, c, S1, S2);
+            float m, sc;
+            fwd_finalize_core(S1, S2, K, g.C, c, f.M, gm, rm, rv, f.running_mean, f.running_var, f.momentum,
+                              f.eps, yb == 0 && threadIdx.x == 0, stats, m, sc);
             if (threadIdx.x == 0) {
-                fwd_finalize_channel(S1, S2, f.partials[2 * f.red_grid_y * g.C + c], g.C, c, f.M, f.gamma,
-                                     f.running_mean, f.running_var, f.momentum, f.eps, yb == 0,
-                                     stats, sh[0], sh[1]);
+                sh[0] = m;
+                sh[1] = sc;
             }
         }
         __syncthreads();
         mean = sh[0];
         scale = sh[1];
     } else if constexpr (SRC == kApplyRunning) {
+        const float p0 = ldv(f.running_mean + c);
+        const float rv = ldv(f.running_var + c);
+        const float gv = ldv_if(f.gamma, c, true);
+        __builtin_amdgcn_sched_barrier(0);
         // Same rounding steps as the training finalize: inv_std in fp64,
         // scale rounded once to fp32.
-        mean = f.running_mean[c];
-        const double inv_std = 1.0 / sqrt((double)f.running_var[c] + (double)f.eps);
-        scale = (float)((f.gamma ? (double)f.gamma[c] : 1.0) * inv_std);
+        mean = p0;
+        const double gm = f.gamma ? (double)gv : 1.0;
+        const double inv_std = 1.0 / sqrt((double)rv + (double)f.eps);
+        scale = (float)(gm * inv_std);
     } else {
-        mean = stats[c];
-        scale = stats[3 * g.C + c];
+        mean = ldv(stats + c);
+        scale = ldv(stats + 3 * g.C + c);
     }
 
     for (;;) {
@@ -485,7 +613,7 @@ bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ 
 }
 
 template <typename T, int V, bool FUSED, int NT, int ACT>
-__global__ void __launch_bounds__(kBnThreads)
+__global__ void __launch_bounds__(kBnThreads, kBnWavesPerSimd)
 bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ dx,
              const float *__restrict__ stats, float *__restrict__ grads, BnGeom g,
              const float *__restrict__ partials, int red_grid_y, int64_t M,
@@ -497,38 +625,52 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
     // and the loop index runs up to a stride past the last one.
     const uint32_t u0 = (uint32_t)yb * (uint32_t)g.upb;
     const uint32_t u1 = min(u0 + (uint32_t)g.upb, (uint32_t)g.units);
-    const float mean = stats[c];
-    const float scale = stats[3 * g.C + c];
-    const float b = (ACT != 0 && beta) ? beta[c] : 0.f;
 
+    // The unit offsets are recomputed for the stores rather than kept: held
+    // from the loads to the stores they pushed the bf16 fused pass past the
+    // 64 VGPRs of 8 waves per SIMD.
     uint32_t base = u0 + threadIdx.x;
     Raw<T, V> vx[kBnUnroll], vd[kBnUnroll];
-    int off[kBnUnroll];
 #pragma unroll
     for (int k = 0; k < kBnUnroll; ++k) {
         const uint32_t u = base + k * kBnThreads;
-        off[k] = bn_unit_offset<V>(g, c, u);
         if (u < u1) {
-            ldr<(NT & kNtEwLoads) != 0>(vx[k], x + off[k]);
-            ldr<(NT & kNtEwLoads) != 0>(vd[k], dy + off[k]);
+            const int off = bn_unit_offset<V>(g, c, u);
+            ldr<(NT & kNtEwLoads) != 0>(vx[k], x + off);
+            ldr<(NT & kNtEwLoads) != 0>(vd[k], dy + off);
         }
     }
 
+    // The per-channel inputs, loaded together with the first units of x, dy,
+    // every one issued before any is used (as in bn_apply_kernel; wave 0
+    // finalizes).
+    const float mean = ldv(stats + c);
+    const float scale = ldv(stats + 3 * g.C + c);
+    const float b = ldv_if(beta, c, ACT != 0);
     float k1, k2;
     if constexpr (FUSED) {
         __shared__ float sh[2];
-        if (threadIdx.x < kWave) {
+        if (threadIdx.x < kWave) {  // wave 0
+            PartialSlots<kFinSlotsEw> ps;
+            ps.load<true>(partials, red_grid_y, g.C, c);
+            const float inv_std = ldv(stats + 2 * g.C + c);
+            __builtin_amdgcn_sched_barrier(0);
             double Sdy, Sdyxc;
-            sum_partials(partials, red_grid_y, g.C, c, Sdy, Sdyxc);
-            if (threadIdx.x == 0)
-                bwd_finalize_channel(Sdy, Sdyxc, g.C, c, M, stats, yb == 0, grads, sh[0], sh[1]);
+            ps.sum(partials, red_grid_y, g.C, c, Sdy, Sdyxc);
+            float a1, a2;
+            bwd_finalize_core(Sdy, Sdyxc, g.C, c, M, (double)inv_std, (double)scale, yb == 0 && threadIdx.x == 0,
+                              grads, a1, a2);
+            if (threadIdx.x == 0) {
+                sh[0] = a1;
+                sh[1] = a2;
+            }
         }
         __syncthreads();
         k1 = sh[0];
         k2 = sh[1];
     } else {
-        k1 = grads[2 * g.C + c];
-        k2 = grads[3 * g.C + c];
+        k1 = ldv(grads + 2 * g.C + c);
+        k2 = ldv(grads + 3 * g.C + c);
     }
 
     for (;;) {
@@ -543,7 +685,7 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
                     const float dz = act_bwd<ACT>(vd[k].get(e), fmaf(xc, scale, b), slope);
                     o[e] = fmaf(dz, scale, fmaf(xc, k1, k2));
                 }
-                st<(NT & kNtStores) != 0, T, V>(dx + off[k], o);
+                st<(NT & kNtStores) != 0, T, V>(dx + bn_unit_offset<V>(g, c, u), o);
             }
         }
         base += kBnThreads * kBnUnroll;
@@ -551,10 +693,10 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
             const uint32_t u = base + k * kBnThreads;
-            off[k] = bn_unit_offset<V>(g, c, u);
             if (u < u1) {
-                ldr<(NT & kNtEwLoads) != 0>(vx[k], x + off[k]);
-                ldr<(NT & kNtEwLoads) != 0>(vd[k], dy + off[k]);
+                const int off = bn_unit_offset<V>(g, c, u);
+                ldr<(NT & kNtEwLoads) != 0>(vx[k], x + off);
+                ldr<(NT & kNtEwLoads) != 0>(vd[k], dy + off);
             }
         }
     }

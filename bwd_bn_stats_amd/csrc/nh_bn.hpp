@@ -13,6 +13,13 @@ constexpr int kBnUnroll = 4;     // vector units in flight per thread
 
 constexpr int64_t kBnMinUnits = (int64_t)kBnThreads * kBnUnroll;  // one full unrolled sweep
 
+// Waves per SIMD the split passes are compiled for: 8 blocks of 256 threads
+// per CU, the resident slots the grid plan fills (at most 64 VGPRs each).
+// Measured on MI355X: the fused dx pass at 68 VGPRs ran 7 blocks per CU and
+// left an eighth of the grid for a second round ((64,256,56,56) bf16 dx
+// 42.3 -> 43.2 us).
+constexpr int kBnWavesPerSimd = 8;
+
 // Blocks per channel for a channel of `units` vector units: enough blocks
 // that all C*grid_y blocks fill the device's resident slots once, but no
 // block gets less than kBnGridMinUnits units (two per thread).  Measured on

@@ -255,6 +255,65 @@ __device__ __forceinline__ T wave_sum(T v)
     return v;
 }
 
+// ---- DPP wave sums -------------------------------------------------------------
+// DPP lane selections inside a row of 16 lanes (gfx9 encodings): quad_perm
+// [1,0,3,2] (lane i <-> i^1) and [2,3,0,1] (i <-> i^2), row_half_mirror
+// (i <-> 7-i in each half row) and row_mirror (i <-> 15-i).
+constexpr int kDppQuadXor1 = 0xB1;
+constexpr int kDppQuadXor2 = 0x4E;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+// v plus the v of the partner lane that CTRL selects.  The partners pair up,
+// so both sides add the same two values.
+template <int CTRL>
+__device__ __forceinline__ float dpp_pair_add(float v)
+{
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// The fp64 form moves the two 32-bit halves with one DPP selection each.
+template <int CTRL>
+__device__ __forceinline__ double dpp_pair_add(double v)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    return v + __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over the 64 lanes of a wave, the same in every lane: DPP steps give
+// every lane its 16-lane row's sum, then the four row sums (lanes 0, 16, 32,
+// 48) are added pairwise, (r0 + r1) + (r2 + r3).  All lanes must be active.
+// A DPP step is a register operand of the add, so the four in-row steps take
+// no LDS round trip (the __shfl_xor butterfly above takes six).
+__device__ __forceinline__ float wave_total(float v)
+{
+    v = dpp_pair_add<kDppRowMirror>(v);
+    v = dpp_pair_add<kDppRowHalfMirror>(v);
+    v = dpp_pair_add<kDppQuadXor2>(v);
+    v = dpp_pair_add<kDppQuadXor1>(v);
+    const int u = __float_as_int(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(u, 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(u, 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(u, 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(u, 48));
+    return (r0 + r1) + (r2 + r3);
+}
+__device__ __forceinline__ double wave_total(double v)
+{
+    v = dpp_pair_add<kDppRowMirror>(v);
+    v = dpp_pair_add<kDppRowHalfMirror>(v);
+    v = dpp_pair_add<kDppQuadXor2>(v);
+    v = dpp_pair_add<kDppQuadXor1>(v);
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    auto row = [&](int lane) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+        return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+    };
+    return (row(0) + row(16)) + (row(32) + row(48));
+}
+
 // ---- workgroup barrier for LDS traffic only ---------------------------------------
 // __syncthreads() orders every address space, so it also waits for all of the
 // wave's outstanding global loads (s_waitcnt vmcnt(0)) -- including loads

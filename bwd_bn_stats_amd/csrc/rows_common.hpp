@@ -42,38 +42,7 @@ constexpr int kLnKeepMaxElems = 16;
 // LDS floats of a team's double-buffered row sums (two quantities per wave).
 constexpr int red_floats(int team) { return 2 * (team / kWave) * 2; }
 
-// DPP lane selections inside a row of 16 lanes (gfx9 encodings): quad_perm
-// [1,0,3,2] (lane i <-> i^1) and [2,3,0,1] (i <-> i^2), row_half_mirror
-// (i <-> 7-i in each half row) and row_mirror (i <-> 15-i).
-constexpr int kDppQuadXor1 = 0xB1;
-constexpr int kDppQuadXor2 = 0x4E;
-constexpr int kDppRowHalfMirror = 0x141;
-constexpr int kDppRowMirror = 0x140;
-
-// v plus the v of the partner lane that CTRL selects.  The partners pair up,
-// so both sides add the same two values.
-template <int CTRL>
-__device__ __forceinline__ float dpp_pair_add(float v)
-{
-    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over the 64 lanes of a wave, the same in every lane: DPP steps give
-// every lane its 16-lane row's sum, then the four row sums (lanes 0, 16, 32,
-// 48) are added pairwise, (r0 + r1) + (r2 + r3).  All lanes must be active.
-__device__ __forceinline__ float wave_total(float v)
-{
-    v = dpp_pair_add<kDppRowMirror>(v);
-    v = dpp_pair_add<kDppRowHalfMirror>(v);
-    v = dpp_pair_add<kDppQuadXor2>(v);
-    v = dpp_pair_add<kDppQuadXor1>(v);
-    const int u = __float_as_int(v);
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(u, 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(u, 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(u, 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(u, 48));
-    return (r0 + r1) + (r2 + r3);
-}
+// The DPP wave sums (dpp_pair_add, wave_total) live in nh_device.hpp.
 
 // Fixed-order sum of the WAVES wave results of a team for two quantities.
 // Called by every thread of the block.
