@@ -98,6 +98,7 @@ std::atomic<int64_t> g_override_bn_channel{0};
 std::atomic<int64_t> g_override_bn_channel_threads{0};
 std::atomic<int64_t> g_override_rows_narrow{0};
 std::atomic<int64_t> g_override_bn_block_order{0};
+std::atomic<int64_t> g_override_bn_unit_order{0};
 
 // ---- BatchNorm planning ----------------------------------------------------------
 // Resident 256-thread block slots of the device: CUs * (threads per CU / 256),
@@ -109,13 +110,24 @@ int64_t bn_slots(const DeviceInfo &d)
     return (int64_t)d.cus * per_cu;
 }
 
+// Unit assignment of the split BatchNorm passes (bn_range): interleaved
+// sweeps unless the "bn_unit_order" override asks for contiguous ranges (1)
+// (2 is the automatic choice).  Interleaved only where every block of the
+// channel gets at least one whole sweep; with fewer units per channel some
+// blocks would sit idle.  bn_auto_grid_y sizes the grid for it.
+bool bn_interleave_wanted() { return g_override_bn_unit_order.load() != 1; }
+int bn_interleave(int64_t units, int64_t grid_y)
+{
+    return bn_interleave_wanted() && units >= grid_y * kBnMinUnits ? 1 : 0;
+}
+
 // Blocks per channel of the reduction passes (stats, grad_sums); the
 // workspace holds this many partial slots.
 int64_t bn_grid_y_for(int64_t units, int64_t C, const DeviceInfo &d)
 {
     const int64_t ov = g_override_bn_grid_y.load();
     if (ov > 0) return ov < units ? ov : units;
-    return bn_auto_grid_y(units, C, bn_slots(d));
+    return bn_auto_grid_y(units, C, bn_slots(d), bn_interleave_wanted());
 }
 
 // Blocks per channel of the elementwise passes (apply, dx, inference): the
@@ -587,6 +599,7 @@ static nh_status bn_forward_impl(int stage, const void *x, void *y, nh_dtype io,
     a.grid_y = (int)bn_grid_y_for(N * (HW / a.vec), C, d);
     a.ew_grid_y = (int)bn_ew_grid_y_for(N * (HW / a.vec), C, d);
     a.chan_fast = bn_chan_fast();
+    a.ilv = bn_interleave(N * (HW / a.vec), std::max(a.grid_y, a.ew_grid_y));
     a.x = x;
     a.out = y;
     a.gamma = gamma;
@@ -715,6 +728,7 @@ static nh_status bn_backward_impl(int stage, const void *dy, const void *x, nh_d
     a.grid_y = (int)bn_grid_y_for(N * (HW / a.vec), C, d);
     a.ew_grid_y = (int)bn_ew_grid_y_for(N * (HW / a.vec), C, d);
     a.chan_fast = bn_chan_fast();
+    a.ilv = bn_interleave(N * (HW / a.vec), std::max(a.grid_y, a.ew_grid_y));
     a.x = x;
     a.dy = dy;
     a.out = dx;
@@ -782,6 +796,7 @@ nh_status bn_forward_infer(const void *x, void *y, nh_dtype io, int64_t N, int64
     a.grid_y = (int)bn_grid_y_for(N * (HW / a.vec), C, d);
     a.ew_grid_y = (int)bn_ew_grid_y_for(N * (HW / a.vec), C, d);
     a.chan_fast = bn_chan_fast();
+    a.ilv = bn_interleave(N * (HW / a.vec), std::max(a.grid_y, a.ew_grid_y));
     a.inference = 1;
     a.x = x;
     a.out = y;
@@ -1290,6 +1305,10 @@ nh_status nh_plan_override(const char *key, int64_t value)
         if (value > 2) return fail(NH_ERR_ARG, "bn_block_order must be 0, 1 or 2");
         g_override_bn_block_order.store(value);
     }
+    else if (strcmp(key, "bn_unit_order") == 0) {
+        if (value > 2) return fail(NH_ERR_ARG, "bn_unit_order must be 0, 1 or 2");
+        g_override_bn_unit_order.store(value);
+    }
     else return fail(NH_ERR_ARG, "unknown override key '%s'", key);
     return ok();
 }
@@ -1313,19 +1332,32 @@ nh_status nh_selftest_host(void)
         const uint32_t n = (uint32_t)((s >> 32) & 0x7fffffffu);
         if (make_fastdiv(d).div(n) != n / d) return fail(NH_ERR_ARG, "fastdiv %u/%u", n, d);
     }
-    // BatchNorm grid: within [1, slots/C] (at least 1), and enough blocks to
-    // fill the slots whenever the channel has the work for them.
+    // BatchNorm grid.  Contiguous: within [1, slots/C] (at least 1), and
+    // enough blocks to fill the slots whenever the channel has the work for
+    // them.  Interleaved: the contiguous grid where a block would get less
+    // than a whole sweep; else within [that grid, 2*slots/C] with a whole
+    // sweep for every block.  Both never decrease with the unit count (the
+    // workspace query sizes the partials for the largest unit count a shape
+    // can take).
     const int64_t slots = 2048;
     const int64_t Cs[] = {1, 3, 32, 37, 256, 2048, 5000};
-    const int64_t Us[] = {1, 100, 1023, 1024, 65536, 1 << 20};
+    const int64_t Us[] = {1, 100, 1023, 1024, 65536, 1 << 20, 25088, 6272, 100352};
     for (int64_t C : Cs)
         for (int64_t u : Us) {
-            const int64_t g = bn_auto_grid_y(u, C, slots);
+            const int64_t g = bn_auto_grid_y(u, C, slots, false);
+            const int64_t gi = bn_auto_grid_y(u, C, slots, true);
             const int64_t cap = slots / C > 1 ? slots / C : 1;
             if (g < 1 || g > cap || g > u) return fail(NH_ERR_ARG, "bn grid %lld for C=%lld u=%lld",
                                                       (long long)g, (long long)C, (long long)u);
             if (u >= cap * kBnGridMinUnits && g != cap)
                 return fail(NH_ERR_ARG, "bn grid underfills: %lld", (long long)g);
+            if (u < g * kBnMinUnits ? gi != g
+                                    : (gi < g || gi > 2 * cap || gi * kBnMinUnits > u))
+                return fail(NH_ERR_ARG, "bn interleaved grid %lld for C=%lld u=%lld", (long long)gi,
+                            (long long)C, (long long)u);
+            for (bool il : {false, true})
+                if (bn_auto_grid_y(u + 1, C, slots, il) < bn_auto_grid_y(u, C, slots, il))
+                    return fail(NH_ERR_ARG, "bn grid decreases at C=%lld u=%lld", (long long)C, (long long)u);
         }
     // BatchNorm unit walk at the largest shapes the ABI accepts: for every
     // block, the unsigned loop index (up to a stride past the block's last
@@ -1345,15 +1377,20 @@ nh_status nh_selftest_host(void)
         if (total >= kMaxElems) return fail(NH_ERR_ARG, "max shape exceeds the element limit");
         const int64_t units = (int64_t)m.N * (m.HW / m.vec);
         // one block per channel, the planned split, and 2048 blocks per channel
-        for (int64_t grid_y : {(int64_t)1, bn_auto_grid_y(units, m.C, slots),
+        for (int64_t grid_y : {(int64_t)1, bn_auto_grid_y(units, m.C, slots, true),
                                std::min<int64_t>(units, 2048)}) {
-            const BnGeom g = make_bn_geom(m.N, m.C, m.HW, m.vec, (int)grid_y, 0);
-            const uint64_t stride = (uint64_t)kBnThreads * kBnUnroll;
+          for (int ilv = 0; ilv < 2; ++ilv) {
+            const BnGeom g = make_bn_geom(m.N, m.C, m.HW, m.vec, (int)grid_y, 0, ilv);
+            const uint64_t sweep = (uint64_t)kBnMinUnits;
             for (int c = 0; c < m.C; c += (m.C > 1 ? m.C - 1 : 1)) {
                 for (int yb = 0; yb < g.grid_y; ++yb) {
-                    const uint64_t u0 = (uint64_t)yb * (uint64_t)g.upb;
-                    const uint64_t u1 = std::min<uint64_t>(u0 + (uint64_t)g.upb, (uint64_t)g.units);
-                    if (u0 + (uint64_t)g.upb >= (1ull << 32) || u1 + stride >= (1ull << 32))
+                    // bn_range in 64-bit arithmetic: the 32-bit forms must not wrap
+                    // for any index the loops form (up to a step past u1).
+                    const uint64_t c0 = (uint64_t)yb * (uint64_t)g.upb;
+                    const uint64_t u0 = ilv ? (uint64_t)yb * sweep : c0;
+                    const uint64_t u1 = ilv ? (uint64_t)g.units : std::min<uint64_t>(c0 + (uint64_t)g.upb, (uint64_t)g.units);
+                    const uint64_t step = ilv ? (uint64_t)g.grid_y * sweep : sweep;
+                    if (c0 + (uint64_t)g.upb >= (1ull << 32) || u0 >= (1ull << 32) || u1 + step >= (1ull << 32))
                         return fail(NH_ERR_ARG, "bn unit index wraps (C=%d yb=%d)", c, yb);
                     if (u0 >= u1) continue;
                     const uint32_t probe[] = {(uint32_t)u0, (uint32_t)(u1 - 1)};
@@ -1366,6 +1403,7 @@ nh_status nh_selftest_host(void)
                     }
                 }
             }
+          }
         }
     }
     // BatchNorm row layout: the chunks cover the rows exactly once, within the

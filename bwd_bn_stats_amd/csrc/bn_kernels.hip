@@ -28,10 +28,11 @@
 // consecutive elements inside one plane (V = 16 bytes of data when the
 // plane length and pointers allow it; 8 bytes for bf16 planes of 4k
 // elements; else 1), numbered plane-major.  The
-// launch has C*grid_y blocks; block (c, yb) takes the contiguous unit range
-// [yb*upb, (yb+1)*upb) of channel c, so every block touches one channel
-// only and reads its per-channel constants once into scalar registers.  The
-// elementwise passes use the same split as the reductions.
+// launch has C*grid_y blocks; block (c, yb) takes units of channel c only
+// (the contiguous range [yb*upb, (yb+1)*upb), or every grid_y-th sweep of
+// the channel: bn_range), so it reads its per-channel constants once into
+// scalar registers.  The elementwise passes use the same split as the
+// reductions.
 //
 // Activation (the BatchNorm + ReLU/LeakyReLU fusion the PR lists as its
 // follow-up): with z = fmaf(x - mean, scale, beta) the forward stores act(z),
@@ -199,16 +200,14 @@ bn_stats_kernel(const T *__restrict__ x, BnGeom g, float *__restrict__ partials)
     const BnBlock blk = bn_block(g);
     const int c = blk.c, yb = blk.yb;
     // Unit indices are unsigned: a channel may hold up to 2^31 - 1 units,
-    // and the loop index runs up to a stride past the last one.
-    const uint32_t u0 = (uint32_t)yb * (uint32_t)g.upb;
-    const uint32_t u1 = min(u0 + (uint32_t)g.upb, (uint32_t)g.units);
+    // and the loop index runs up to a step past the last one.
+    const BnRange rg = bn_range(g, yb);
+    const uint32_t u0 = rg.u0, u1 = rg.u1, step = rg.step;
 
     float s1[kBnUnroll], s2[kBnUnroll];
 #pragma unroll
     for (int k = 0; k < kBnUnroll; ++k) { s1[k] = 0.f; s2[k] = 0.f; }
 
-    // The first sweep's loads go out before the shift's, so that no load of
-    // x waits for the shift (loads complete in issue order).
     // The first sweep's loads go out before the shift's, so that no load of
     // x waits for the shift (loads complete in issue order).
     uint32_t base = u0 + threadIdx.x;
@@ -233,7 +232,7 @@ bn_stats_kernel(const T *__restrict__ x, BnGeom g, float *__restrict__ partials)
                 }
             }
         }
-        base += kBnThreads * kBnUnroll;
+        base += step;
         if (base >= u1) break;
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
@@ -265,9 +264,9 @@ bn_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x,
     const BnBlock blk = bn_block(g);
     const int c = blk.c, yb = blk.yb;
     // Unit indices are unsigned: a channel may hold up to 2^31 - 1 units,
-    // and the loop index runs up to a stride past the last one.
-    const uint32_t u0 = (uint32_t)yb * (uint32_t)g.upb;
-    const uint32_t u1 = min(u0 + (uint32_t)g.upb, (uint32_t)g.units);
+    // and the loop index runs up to a step past the last one.
+    const BnRange rg = bn_range(g, yb);
+    const uint32_t u0 = rg.u0, u1 = rg.u1, step = rg.step;
     const float mean = stats[c];
     const float scale = ACT != 0 ? stats[3 * g.C + c] : 0.f;
     const float bz = (ACT != 0 && beta) ? beta[c] : 0.f;
@@ -276,7 +275,7 @@ bn_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x,
 #pragma unroll
     for (int k = 0; k < kBnUnroll; ++k) { s1[k] = 0.f; s2[k] = 0.f; }
 
-    for (uint32_t base = u0 + threadIdx.x; base < u1; base += kBnThreads * kBnUnroll) {
+    for (uint32_t base = u0 + threadIdx.x; base < u1; base += step) {
         Raw<T, V> vx[kBnUnroll], vd[kBnUnroll];
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
@@ -530,9 +529,9 @@ bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ 
     const BnBlock blk = bn_block(g);
     const int c = blk.c, yb = blk.yb;
     // Unit indices are unsigned: a channel may hold up to 2^31 - 1 units,
-    // and the loop index runs up to a stride past the last one.
-    const uint32_t u0 = (uint32_t)yb * (uint32_t)g.upb;
-    const uint32_t u1 = min(u0 + (uint32_t)g.upb, (uint32_t)g.units);
+    // and the loop index runs up to a step past the last one.
+    const BnRange rg = bn_range(g, yb);
+    const uint32_t u0 = rg.u0, u1 = rg.u1, step = rg.step;
 
     uint32_t base = u0 + threadIdx.x;
     Raw<T, V> v[kBnUnroll];
@@ -601,7 +600,7 @@ bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ 
                 st<(NT & kNtStores) != 0, T, V>(y + off[k], o);
             }
         }
-        base += kBnThreads * kBnUnroll;
+        base += step;
         if (base >= u1) break;
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
@@ -622,9 +621,9 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
     const BnBlock blk = bn_block(g);
     const int c = blk.c, yb = blk.yb;
     // Unit indices are unsigned: a channel may hold up to 2^31 - 1 units,
-    // and the loop index runs up to a stride past the last one.
-    const uint32_t u0 = (uint32_t)yb * (uint32_t)g.upb;
-    const uint32_t u1 = min(u0 + (uint32_t)g.upb, (uint32_t)g.units);
+    // and the loop index runs up to a step past the last one.
+    const BnRange rg = bn_range(g, yb);
+    const uint32_t u0 = rg.u0, u1 = rg.u1, step = rg.step;
 
     // The unit offsets are recomputed for the stores rather than kept: held
     // from the loads to the stores they pushed the bf16 fused pass past the
@@ -688,7 +687,7 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
                 st<(NT & kNtStores) != 0, T, V>(dx + bn_unit_offset<V>(g, c, u), o);
             }
         }
-        base += kBnThreads * kBnUnroll;
+        base += step;
         if (base >= u1) break;
 #pragma unroll
         for (int k = 0; k < kBnUnroll; ++k) {
@@ -1343,8 +1342,8 @@ static hipError_t bn_col_backward_t(const BnCall &a, hipStream_t s)
 template <typename T, int V, int ACT>
 static hipError_t bn_forward_t(const BnCall &a, hipStream_t s)
 {
-    const BnGeom gr = make_bn_geom(a.N, a.C, a.HW, a.vec, a.grid_y, a.chan_fast);
-    const BnGeom ge = make_bn_geom(a.N, a.C, a.HW, a.vec, a.ew_grid_y, a.chan_fast);
+    const BnGeom gr = make_bn_geom(a.N, a.C, a.HW, a.vec, a.grid_y, a.chan_fast, a.ilv);
+    const BnGeom ge = make_bn_geom(a.N, a.C, a.HW, a.vec, a.ew_grid_y, a.chan_fast, a.ilv);
     const T *x = static_cast<const T *>(a.x);
     const dim3 rgrid((unsigned)(a.C * a.grid_y)), egrid((unsigned)(a.C * a.ew_grid_y)), block(kBnThreads);
     const int64_t M = (int64_t)a.N * a.HW;
@@ -1355,7 +1354,7 @@ static hipError_t bn_forward_t(const BnCall &a, hipStream_t s)
     if (a.channel_fused) {
         // one kernel per direction: it runs as the second stage
         if (a.stage == 1) return hipSuccess;
-        const BnGeom g1 = make_bn_geom(a.N, a.C, a.HW, a.vec, 1, 0);
+        const BnGeom g1 = make_bn_geom(a.N, a.C, a.HW, a.vec, 1, 0, 0);
         if (a.channel_threads == kBnChannelBigBlock)
             return launch(NH_K_BN_FWD_CHANNEL, bn_fwd_channel_kernel<T, V, kBnNtPolicy, ACT, kBnChannelBigBlock>,
                           dim3((unsigned)a.C), dim3(kBnChannelBigBlock), 0, s, x, static_cast<T *>(a.out),
@@ -1385,15 +1384,15 @@ static hipError_t bn_forward_t(const BnCall &a, hipStream_t s)
 template <typename T, int V, int ACT>
 static hipError_t bn_backward_t(const BnCall &a, hipStream_t s)
 {
-    const BnGeom gr = make_bn_geom(a.N, a.C, a.HW, a.vec, a.grid_y, a.chan_fast);
-    const BnGeom ge = make_bn_geom(a.N, a.C, a.HW, a.vec, a.ew_grid_y, a.chan_fast);
+    const BnGeom gr = make_bn_geom(a.N, a.C, a.HW, a.vec, a.grid_y, a.chan_fast, a.ilv);
+    const BnGeom ge = make_bn_geom(a.N, a.C, a.HW, a.vec, a.ew_grid_y, a.chan_fast, a.ilv);
     const T *x = static_cast<const T *>(a.x);
     const T *dy = static_cast<const T *>(a.dy);
     const dim3 rgrid((unsigned)(a.C * a.grid_y)), egrid((unsigned)(a.C * a.ew_grid_y)), block(kBnThreads);
     const int64_t M = (int64_t)a.N * a.HW;
     if (a.channel_fused) {
         if (a.stage == 1) return hipSuccess;
-        const BnGeom g1 = make_bn_geom(a.N, a.C, a.HW, a.vec, 1, 0);
+        const BnGeom g1 = make_bn_geom(a.N, a.C, a.HW, a.vec, 1, 0, 0);
         if (a.channel_threads == kBnChannelBigBlock)
             return launch(NH_K_BN_BWD_CHANNEL, bn_bwd_channel_kernel<T, V, kBnNtPolicy, ACT, kBnChannelBigBlock>,
                           dim3((unsigned)a.C), dim3(kBnChannelBigBlock), 0, s, dy, x, static_cast<T *>(a.out),

@@ -34,14 +34,35 @@ constexpr int kBnWavesPerSimd = 8;
 // the same index read.  Measured on MI355X, splitting them differently (for
 // example 64 reduction blocks per channel, 32 elementwise) makes apply and dx
 // 25-40% slower, although no L2 line survives from one kernel to the next.
+//
+// Interleaved unit assignment (bn_range) where the channel holds at least
+// one whole sweep per block of that grid: then up to twice the resident
+// slots per channel, as many as give every block a whole sweep.  Measured on
+// MI355X, cold per call, fwd+bwd step, contiguous at the one-round grid ->
+// interleaved at the same grid -> interleaved at the larger grid:
+//   (64,256,56,56) bf16    124.6 -> 123.3 -> 121.8 us (16 blocks per channel)
+//   (64,64,112,112) bf16   125.5 -> 123.1 -> 120.8 us (64)
+//   (128,256,28,28) fp32   137.0 -> 135.4 -> 132.7 us (16)
+//   (32,128,56,56) fp32     61.0 ->  60.1 ->  59.6 us (24)
+//   (64,512,28,28) bf16     71.3 ->  71.2 ->  70.7 us (6)
+// and inference + ReLU at (64,64,112,112) bf16 38.5 -> 35.5 -> 34.5 us.
+// More blocks per channel lose again: (64,256,56,56) bf16 at 32 blocks per
+// channel 122.6 us.  The one-round grid is what the Aether-ML PR's
+// "Reduction grid" rule gives; the second round only pays with the
+// interleaved order.
 constexpr int64_t kBnGridMinUnits = (int64_t)kBnThreads * 2;
-inline int64_t bn_auto_grid_y(int64_t units, int64_t C, int64_t slots)
+inline int64_t bn_auto_grid_y(int64_t units, int64_t C, int64_t slots, bool interleave)
 {
     int64_t per_channel = slots / (C > 0 ? C : 1);
     if (per_channel < 1) per_channel = 1;
     int64_t want = ceil_div(units, kBnGridMinUnits);
     if (want < 1) want = 1;
-    return want < per_channel ? want : per_channel;
+    const int64_t one_round = want < per_channel ? want : per_channel;
+    if (interleave && units >= one_round * kBnMinUnits) {
+        const int64_t whole = units / kBnMinUnits;
+        return whole < 2 * per_channel ? whole : 2 * per_channel;
+    }
+    return one_round;
 }
 
 // Channels of at most kBnChannelMaxUnits units (twice that with enough
@@ -55,8 +76,9 @@ constexpr int64_t kBnChannelMaxUnits = 2 * kBnMinUnits;
 constexpr int kBnChannelBigBlock = 1024;  // threads of the larger fused-kernel block
 
 // Geometry of a BatchNorm launch: channel c's M elements in units of V
-// consecutive elements inside one plane, block (c, yb) owning units
-// [yb*upb, min((yb+1)*upb, units)).
+// consecutive elements inside one plane, block (c, yb) owning either the
+// units [yb*upb, min((yb+1)*upb, units)) or every grid_y-th sweep of the
+// channel (bn_range).
 struct BnGeom {
     int C;
     int HW;
@@ -66,6 +88,7 @@ struct BnGeom {
     int upb;        // units per block
     int grid_y;
     int chan_fast;  // block numbering: 0 channel-major, 1 channel-fastest (bn_block)
+    int ilv;        // unit assignment: 0 contiguous ranges, 1 interleaved sweeps (bn_range)
 };
 
 // Block id -> (channel c, block yb of that channel).  Channel-major: the
@@ -92,6 +115,26 @@ __device__ __forceinline__ BnBlock bn_block(const BnGeom &g)
     return {g.chan_fast ? r : q, g.chan_fast ? q : r};
 }
 
+// The units of block yb: sweeps of kBnMinUnits units (one unrolled pass of
+// the block's threads) starting at u0, u0 + step, ..., each cut at u1.
+// Contiguous: one range of upb units, step one sweep.  Interleaved: sweep s
+// of the channel goes to block s mod grid_y, so at any moment the blocks of
+// a channel read neighbouring sweeps and, with the channels side by side in
+// memory, the whole grid reads one compact stretch of the tensor.  Every
+// pass of one call uses the same assignment, so an elementwise block still
+// re-reads the units that the reduction block of its id read.  Value selects,
+// as in bn_block.
+struct BnRange {
+    uint32_t u0, u1, step;
+};
+__device__ __forceinline__ BnRange bn_range(const BnGeom &g, int yb)
+{
+    constexpr uint32_t S = (uint32_t)kBnMinUnits;
+    const uint32_t c0 = (uint32_t)yb * (uint32_t)g.upb;
+    const uint32_t c1 = min(c0 + (uint32_t)g.upb, (uint32_t)g.units);
+    return {g.ilv ? (uint32_t)yb * S : c0, g.ilv ? (uint32_t)g.units : c1, g.ilv ? (uint32_t)g.grid_y * S : S};
+}
+
 // Element offset of unit u of channel c.  Unsigned arithmetic: callers may
 // form the offset of a unit past the end (never dereferenced), which must
 // not be signed overflow.
@@ -103,10 +146,11 @@ __host__ __device__ __forceinline__ int bn_unit_offset(const BnGeom &g, int c, u
     return (int)((n * (uint32_t)g.C + (uint32_t)c) * (uint32_t)g.HW + j * (uint32_t)V);
 }
 
-inline BnGeom make_bn_geom(int N, int C, int HW, int vec, int grid_y, int chan_fast)
+inline BnGeom make_bn_geom(int N, int C, int HW, int vec, int grid_y, int chan_fast, int ilv)
 {
     BnGeom g;
     g.chan_fast = chan_fast;
+    g.ilv = ilv;
     g.C = C;
     g.HW = HW;
     g.HWv = HW / vec;
@@ -206,6 +250,7 @@ struct BnCall {
     int grid_y;          // blocks per channel of the reduction passes (stats, grad_sums)
     int ew_grid_y;       // blocks per channel of the elementwise passes (apply, dx)
     int chan_fast;       // block numbering of the split passes (BnGeom::chan_fast)
+    int ilv;             // unit assignment of the split passes (BnGeom::ilv)
     int separate_finalize;  // 1: finalize as its own kernel; 0: in the elementwise prologue
     int inference;       // forward only: apply with the running statistics, no reduction
     int channel_fused;   // 1: one block per channel, reduction + finalize + elementwise in one kernel

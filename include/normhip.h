@@ -499,7 +499,13 @@ nh_status nh_rows_plan(int64_t rows, int64_t cols, int *blocks);
  * "rows_teams" = 1 or 2 forces the row teams per block of the
  * LayerNorm and RMSNorm backwards' vector kernels (same results up to the
  * order of the column sums), key "bn_block_order" = 1 or 2 numbers the split
- * BatchNorm passes' blocks channel-major or channel-fastest (same results).
+ * BatchNorm passes' blocks channel-major or channel-fastest (same results),
+ * key "bn_unit_order" = 1 gives each block of a channel one contiguous range
+ * of its units, on a grid of at most one round of resident blocks, instead
+ * of the automatic plan (2 forces that plan): every grid_y-th sweep of 1024
+ * units to one block, where each block gets a whole sweep, on up to two
+ * rounds (results equal up to the rounding of the per-block sums; a
+ * workspace queried under 1 may be too small for the automatic plan).
  * value 0 restores the automatic plan.  Process-wide; not for concurrent use with
  * other calls.
  */

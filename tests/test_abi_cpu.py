@@ -236,6 +236,8 @@ def test_measurement_validation():
     assert nh.lib.nh_plan_override(b"bn_layout", 0) == NH_OK
     assert nh.lib.nh_plan_override(b"bn_block_order", 3) == NH_ERR_ARG
     assert nh.lib.nh_plan_override(b"bn_block_order", 0) == NH_OK
+    assert nh.lib.nh_plan_override(b"bn_unit_order", 3) == NH_ERR_ARG
+    assert nh.lib.nh_plan_override(b"bn_unit_order", 0) == NH_OK
     assert nh.lib.nh_calib_add(FAKE, FAKE, FAKE, -1, NULL) == NH_ERR_SHAPE
     assert nh.lib.nh_calib_add(NULL, NULL, NULL, 0, NULL) == NH_OK
     assert nh.lib.nh_calib_copy(NULL, FAKE, 16, NULL) == NH_ERR_NULL

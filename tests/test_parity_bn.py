@@ -326,6 +326,43 @@ def test_bn_block_orders_match(nh, oracle_mod, name):
         assert np.array_equal(major[k].view(np.uint64), fastest[k].view(np.uint64)), k
 
 
+@pytest.mark.parametrize("name,grid_y,ew_grid_y", [
+    ("cifar_256x32x32x32_f32", 0, 0),        # one sweep per block: the contiguous assignment
+    ("resnet_64x256x56x56_bf16", 0, 0),      # 24.5 sweeps per channel over 8 blocks
+    ("one_channel_64x1x128x128_f32", 64, 0),  # 4 sweeps per block
+    ("scalar_5x24x33x31_f32", 2, 0),         # scalar units, a short last sweep, 3 and 2 sweeps
+    ("scalar_5x24x33x31_f32", 2, 4),         # elementwise passes on their own split
+])
+def test_bn_unit_orders(nh, oracle_mod, name, grid_y, ew_grid_y):
+    """Interleaved unit assignment (block yb of a channel takes its sweeps
+    yb, yb + grid_y, ...) gives the oracle's results in the forward, the
+    backward and the separate-finalize path; where every block holds exactly
+    one sweep it is the contiguous assignment, bit for bit."""
+    c = (wl.bn_case(5, 24, 33, 31, wl.F32, seed=49, x_mean=0.5, x_std=1.5) if name.startswith("scalar")
+         else CASES[name]())
+    print(f"[bn parity] unit orders {name} grid_y={grid_y} ew_grid_y={ew_grid_y}", flush=True)
+    want = _oracle_bn(oracle_mod, c)
+    nh.plan_override("bn_grid_y", grid_y)
+    nh.plan_override("bn_ew_grid_y", ew_grid_y)
+    try:
+        nh.plan_override("bn_unit_order", 1)
+        contiguous = _gpu_bn(nh, c)
+        nh.plan_override("bn_unit_order", 2)
+        interleaved = _gpu_bn(nh, c)
+        nh.plan_override("bn_finalize_kernels", 1)
+        interleaved_sep = _gpu_bn(nh, c)
+    finally:
+        for key in ("bn_unit_order", "bn_finalize_kernels", "bn_grid_y", "bn_ew_grid_y"):
+            nh.plan_override(key, 0)
+    _compare(c, interleaved, want)
+    _compare(c, interleaved_sep, want)
+    for k in interleaved:
+        assert np.array_equal(interleaved[k].view(np.uint64), interleaved_sep[k].view(np.uint64)), k
+    if name.startswith("cifar"):
+        for k in interleaved:
+            assert np.array_equal(interleaved[k].view(np.uint64), contiguous[k].view(np.uint64)), k
+
+
 @pytest.mark.parametrize("offset", [0, 2, 4])
 def test_bn_bf16_unit_widths_by_alignment(nh, oracle_mod, offset):
     """bf16 planes of 4k elements at element offsets 0, 2, 4: 8-byte units
