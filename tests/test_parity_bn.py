@@ -342,6 +342,18 @@ def test_bn_unit_orders(nh, oracle_mod, name, grid_y, ew_grid_y):
          else CASES[name]())
     print(f"[bn parity] unit orders {name} grid_y={grid_y} ew_grid_y={ew_grid_y}", flush=True)
     want = _oracle_bn(oracle_mod, c)
+    if grid_y == 0:
+        # the automatic plan: the one-round grid for contiguous ranges; with
+        # interleaved sweeps up to twice that, a whole 1024-unit sweep per block
+        io = 0 if c.io == wl.F32 else 1
+        units = c.N * c.hw // (4 if io == 0 else 8)
+        nh.plan_override("bn_unit_order", 1)
+        try:
+            one_round = nh.bn_plan(c.N, c.C, c.hw, io)
+        finally:
+            nh.plan_override("bn_unit_order", 0)
+        auto = nh.bn_plan(c.N, c.C, c.hw, io)
+        assert auto == (min(2 * one_round, units // 1024) if units >= one_round * 1024 else one_round), (auto, one_round)
     nh.plan_override("bn_grid_y", grid_y)
     nh.plan_override("bn_ew_grid_y", ew_grid_y)
     try:
