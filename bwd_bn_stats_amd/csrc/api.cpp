@@ -1336,7 +1336,8 @@ nh_status nh_selftest_host(void)
     // enough blocks to fill the slots whenever the channel has the work for
     // them.  Interleaved: the contiguous grid where a block would get less
     // than a whole sweep; else within [that grid, 2*slots/C] with a whole
-    // sweep for every block.  Both never decrease with the unit count (the
+    // sweep for every block, and the contiguous grid itself where two rounds
+    // would exceed kBnTwoRoundMaxGrid blocks per channel.  Both never decrease with the unit count (the
     // workspace query sizes the partials for the largest unit count a shape
     // can take).
     const int64_t slots = 2048;
@@ -1352,7 +1353,8 @@ nh_status nh_selftest_host(void)
             if (u >= cap * kBnGridMinUnits && g != cap)
                 return fail(NH_ERR_ARG, "bn grid underfills: %lld", (long long)g);
             if (u < g * kBnMinUnits ? gi != g
-                                    : (gi < g || gi > 2 * cap || gi * kBnMinUnits > u))
+                                    : (gi < g || gi > 2 * cap || gi * kBnMinUnits > u ||
+                                       (2 * cap > kBnTwoRoundMaxGrid && gi != g)))
                 return fail(NH_ERR_ARG, "bn interleaved grid %lld for C=%lld u=%lld", (long long)gi,
                             (long long)C, (long long)u);
             for (bool il : {false, true})

@@ -321,7 +321,12 @@ bn_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x,
 // 8 waves per SIMD; the finalize kernels hold 4.
 constexpr int kFinSlotsEw = 2;
 constexpr int kFinSlotsKernel = 4;
-template <int S>
+// Slots per lane loaded together past the register-held ones
+// (PartialSlots::sum): 4 in the elementwise prologues (8 would push the
+// fused dx pass past 64 VGPRs), 8 in the finalize kernels.
+constexpr int kFinBatchEw = 4;
+constexpr int kFinBatchKernel = 8;
+template <int S, int B>
 struct PartialSlots {
     float a[S], b[S];
 
@@ -367,9 +372,25 @@ struct PartialSlots {
                 y += (double)b[k];
             }
         }
-        for (int yb = lane + S * kWave; yb < grid_y; yb += kWave) {
-            x += (double)partials[(0 * grid_y + yb) * C + c];
-            y += (double)partials[(1 * grid_y + yb) * C + c];
+        // The rest in batches of B slots per lane, every load of a
+        // batch in flight at once (one round trip per batch instead of per
+        // slot): a slot past grid_y loads slot grid_y - 1 and adds 0, so no
+        // branch separates the loads.  Each lane still adds its slots in
+        // index order.
+        for (int y0 = lane + S * kWave; y0 < grid_y; y0 += B * kWave) {
+            float ra[B], rb[B];
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                const int yb = min(y0 + j * kWave, grid_y - 1);
+                ra[j] = partials[(size_t)(0 * grid_y + yb) * C + c];
+                rb[j] = partials[(size_t)(1 * grid_y + yb) * C + c];
+            }
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                const bool live = y0 + j * kWave < grid_y;
+                x += live ? (double)ra[j] : 0.0;
+                y += live ? (double)rb[j] : 0.0;
+            }
         }
         s1 = wave_total(x);
         s2 = wave_total(y);
@@ -379,7 +400,7 @@ struct PartialSlots {
 __device__ __forceinline__ void sum_partials(const float *__restrict__ partials, int grid_y, int C, int c,
                                              double &s1, double &s2)
 {
-    PartialSlots<kFinSlotsKernel> ps;
+    PartialSlots<kFinSlotsKernel, kFinBatchKernel> ps;
     ps.load<false>(partials, grid_y, C, c);
     ps.sum(partials, grid_y, C, c, s1, s2);
 }
@@ -552,7 +573,7 @@ bn_apply_kernel(const T *__restrict__ x, T *__restrict__ y, float *__restrict__ 
     if constexpr (SRC == kApplyFinalize) {
         __shared__ float sh[2];
         if (threadIdx.x < kWave) {  // wave 0
-            PartialSlots<kFinSlotsEw> ps;
+            PartialSlots<kFinSlotsEw, kFinBatchEw> ps;
             ps.load<true>(f.partials, f.red_grid_y, g.C, c);
             const float K = ldv(f.partials + 2 * f.red_grid_y * g.C + c);
             const float gv = ldv_if(f.gamma, c, true);
@@ -650,7 +671,7 @@ bn_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ 
     if constexpr (FUSED) {
         __shared__ float sh[2];
         if (threadIdx.x < kWave) {  // wave 0
-            PartialSlots<kFinSlotsEw> ps;
+            PartialSlots<kFinSlotsEw, kFinBatchEw> ps;
             ps.load<true>(partials, red_grid_y, g.C, c);
             const float inv_std = ldv(stats + 2 * g.C + c);
             __builtin_amdgcn_sched_barrier(0);

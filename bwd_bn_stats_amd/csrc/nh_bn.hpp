@@ -49,8 +49,17 @@ constexpr int kBnWavesPerSimd = 8;
 // More blocks per channel lose again: (64,256,56,56) bf16 at 32 blocks per
 // channel 122.6 us.  The one-round grid is what the Aether-ML PR's
 // "Reduction grid" rule gives; the second round only pays with the
-// interleaved order.
+// interleaved order, and only while a channel has at most
+// kBnTwoRoundMaxGrid blocks: every elementwise block first sums its
+// channel's partial slots, and with two rounds that prologue's latency is
+// paid twice.  Fewer channels keep the one-round grid, interleaved.
+// Measured, contiguous / interleaved one round / interleaved two rounds:
+//   (256,4,128,128) fp32    78.7 / 78.5 / 84.9 us (512 -> 1024 blocks per channel)
+//   (64,3,224,224) fp32     52.3 / 47.8 / 48.7 us (682 -> 784)
+//   (32,16,224,224) fp32   123.0 / 121.8 / 121.1 us (128 -> 256)
+//   (128,32,112,112) bf16  124.8 / 122.5 / 121.2 us (64 -> 128)
 constexpr int64_t kBnGridMinUnits = (int64_t)kBnThreads * 2;
+constexpr int64_t kBnTwoRoundMaxGrid = 256;
 inline int64_t bn_auto_grid_y(int64_t units, int64_t C, int64_t slots, bool interleave)
 {
     int64_t per_channel = slots / (C > 0 ? C : 1);
@@ -60,7 +69,8 @@ inline int64_t bn_auto_grid_y(int64_t units, int64_t C, int64_t slots, bool inte
     const int64_t one_round = want < per_channel ? want : per_channel;
     if (interleave && units >= one_round * kBnMinUnits) {
         const int64_t whole = units / kBnMinUnits;
-        return whole < 2 * per_channel ? whole : 2 * per_channel;
+        const int64_t cap = 2 * per_channel <= kBnTwoRoundMaxGrid ? 2 * per_channel : one_round;
+        return whole < cap ? whole : cap;
     }
     return one_round;
 }
