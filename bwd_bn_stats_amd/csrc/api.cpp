@@ -198,10 +198,11 @@ int bn_chan_fast()
 }
 
 // The finalize in the elementwise prologue reads a channel's partial slots
-// through buffer resources with 32-bit byte offsets yb*C*4: it runs there only
-// while the slots span less than 2^31 bytes (always, short of a forced grid
-// on millions of channels); else the finalize runs as its own kernel.
-bool bn_fused_finalize_fits(int64_t grid_y, int64_t C) { return grid_y * C * 4 < ((int64_t)1 << 31); }
+// (a row of grid_y floats) through buffer resources with 32-bit byte offsets
+// yb*4: it runs there only while a row spans less than 2^31 bytes (always,
+// short of a forced grid beyond 2^29 blocks per channel); else the finalize
+// runs as its own kernel.
+bool bn_fused_finalize_fits(int64_t grid_y) { return grid_y * 4 < ((int64_t)1 << 31); }
 
 // Largest grid_y any dtype/alignment can take for this shape (scalar units).
 int64_t bn_grid_y_max(int64_t M, int64_t C, const DeviceInfo &d) { return bn_grid_y_for(M, C, d); }
@@ -261,7 +262,7 @@ size_t bn_ws_bytes(int64_t N, int64_t C, int64_t HW, const DeviceInfo &d)
 {
     const int64_t M = N * HW;
     const size_t col = bn_col_ws_bytes(N, C, HW);
-    // partials[2, grid_y, C] + shifts K[C]
+    // partials[C, 2, grid_y] + shifts K[C]
     const size_t chan = round_up((size_t)((2 * bn_grid_y_max(M, C, d) + 1) * C) * sizeof(float), 256);
     return chan > col ? chan : col;
 }
@@ -613,7 +614,7 @@ static nh_status bn_forward_impl(int stage, const void *x, void *y, nh_dtype io,
     a.stats = stats;
     a.partials = static_cast<float *>(ws);
     a.stage = stage;
-    a.separate_finalize = g_override_bn_finalize_kernels.load() != 0 || !bn_fused_finalize_fits(a.grid_y, C);
+    a.separate_finalize = g_override_bn_finalize_kernels.load() != 0 || !bn_fused_finalize_fits(a.grid_y);
     a.channel_fused = bn_channel_fused(N * (HW / a.vec), C, bn_slots(d));
     a.channel_threads = bn_channel_threads(N * (HW / a.vec), C, bn_slots(d));
     if (bn_col_layout(io, HW, a.vec, a.channel_fused)) bn_col_plan(a, x, y, nullptr);
@@ -739,7 +740,7 @@ static nh_status bn_backward_impl(int stage, const void *dy, const void *x, nh_d
     a.grads = grads;
     a.partials = static_cast<float *>(ws);
     a.stage = stage;
-    a.separate_finalize = g_override_bn_finalize_kernels.load() != 0 || !bn_fused_finalize_fits(a.grid_y, C);
+    a.separate_finalize = g_override_bn_finalize_kernels.load() != 0 || !bn_fused_finalize_fits(a.grid_y);
     a.channel_fused = bn_channel_fused(N * (HW / a.vec), C, bn_slots(d));
     a.channel_threads = bn_channel_threads(N * (HW / a.vec), C, bn_slots(d));
     if (bn_col_layout(io, HW, a.vec, a.channel_fused)) bn_col_plan(a, x, dy, dx);

@@ -404,7 +404,7 @@ nh_status rmsnorm_forward(const void *x, nh_dtype t, const void *weight,
 
 /* Kernel ids for per-kernel timing. */
 typedef enum {
-    NH_K_BN_STATS = 0,        /* shifted sums -> partials[2, grid_y, C] */
+    NH_K_BN_STATS = 0,        /* shifted sums -> partials[C, 2, grid_y] */
     NH_K_BN_FWD_FINALIZE = 1, /* partials -> stats[4, C], running stats */
     NH_K_BN_APPLY = 2,        /* y = (x - mean)*scale + beta */
     NH_K_BN_GRAD_SUMS = 3,    /* sum dy, sum dy*(x - mean) -> partials */
