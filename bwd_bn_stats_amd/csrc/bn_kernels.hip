@@ -74,7 +74,9 @@ namespace nh {
 // of the eight combinations keeps the reduction passes' loads cacheable (the
 // elementwise pass re-reads the same x and dy right after, and finds them in
 // the 256 MB Infinity Cache), streams the elementwise passes' loads (last
-// use) and streams every store.
+// use) and streams every store.  No setting of a load's cache-policy bits
+// (sc0, nt, sc1) both reads at the nontemporal rate and leaves the data in
+// the Infinity Cache: the nt bit decides both.
 enum : int { kNtReduceLoads = 1, kNtEwLoads = 2, kNtStores = 4 };
 #ifndef NH_BN_NT_POLICY
 #define NH_BN_NT_POLICY (kNtEwLoads | kNtStores)
@@ -325,9 +327,10 @@ bn_grad_sums_kernel(const T *__restrict__ dy, const T *__restrict__ x,
 // elementwise pass issues them together with its first loads of x: they
 // arrive with that data instead of a memory round trip after it.  Lanes hold
 // up to S slots in registers (grid_y <= 64*S); the rest are read in the sum.
-// The elementwise prologues hold 2 (every channel count of at least 16 at
-// 2048 resident blocks), which keeps the fused dx pass within the 64 VGPRs of
-// 8 waves per SIMD; the finalize kernels hold 4.
+// The elementwise prologues hold 2 (the one-round grid of every channel
+// count of at least 16 at 2048 resident blocks; two rounds and fewer
+// channels read the rest in batches), which keeps the fused dx pass within
+// the 64 VGPRs of 8 waves per SIMD; the finalize kernels hold 4.
 constexpr int kFinSlotsEw = 2;
 constexpr int kFinSlotsKernel = 4;
 // Slots per lane loaded together past the register-held ones
