@@ -584,6 +584,52 @@ def floor_read(nh, torch, n_floats, K, W, reps):
     return {"bytes": 4 * n_floats, "avg_us": round(us, 3), "gbs": round(4 * n_floats / (us * 1e3), 1)}
 
 
+def floor_warm(nh, torch, n_floats, kind, K, W, reps):
+    """hipMemcpyAsync (kind "copy") or torch.add (kind "add") whose sources a
+    plain read stream (nh_calib_read) read just before, so that they come from
+    the Infinity Cache while the output goes to HBM: the floor of the
+    elementwise passes, which re-read x (and dy) right after the reduction
+    pass read them.  Cold buffer sets; the op's time is a region of
+    (reads, op) calls less a region of the reads alone.  GB/s counts the
+    bytes read plus written."""
+    hip = _hip()
+    device = torch.device("cuda:0")
+    nsrc = 1 if kind == "copy" else 2
+    R = _nsets(4 * n_floats * (nsrc + 1))
+    sets = [[torch.ones(n_floats, device=device) for _ in range(nsrc)] + [torch.empty(n_floats, device=device)]
+            for _ in range(R)]
+    sums = torch.empty(4096, device=device)
+    ps = P(sums.data_ptr())
+    torch.cuda.synchronize()
+
+    def make(with_op):
+        def mk(stream):
+            def call(i):
+                t = sets[i % R]
+                for a in t[:nsrc]:
+                    nh.lib.nh_calib_read(P(a.data_ptr()), n_floats, ps, 4096, stream)
+                if not with_op:
+                    return
+                if kind == "copy":
+                    hip.hipMemcpyAsync(P(t[1].data_ptr()), P(t[0].data_ptr()), 4 * n_floats, 3, stream)
+                else:
+                    torch.add(t[0], t[1], out=t[2])
+            return call
+        return mk
+    for i in range(max(W, 1)):
+        make(True)(P(torch.cuda.current_stream().cuda_stream))(i)
+    torch.cuda.synchronize()
+    K = _round_up(K, R)
+    full = float(np.median(Regions(torch, reps).run(make(True), K)))
+    base = float(np.median(Regions(torch, reps).run(make(False), K)))
+    del sets
+    torch.cuda.empty_cache()
+    us = full - base
+    nb = 4 * n_floats * (nsrc + 1)
+    return {"bytes": nb, "avg_us": round(us, 3), "gbs": round(nb / (us * 1e3), 1),
+            "with_reads_us": round(full, 3), "reads_us": round(base, 3)}
+
+
 def floors_for(nh, torch, read_bytes, add_bytes, copy_bytes, K, W, reps):
     out = {}
     if read_bytes:
@@ -737,7 +783,8 @@ def run_workload(nh, torch, wl, name, K, W, reps):
 def _floors_for_bn(nh, torch, res, K, W, reps):
     """Independent streams of the BatchNorm kernels' sizes: the reduction
     passes' reads (x; x and dy), the dx pass's two reads and one write, and a
-    copy of x (the apply pass's read + write)."""
+    copy of x (the apply pass's read + write), the last two both cold and with
+    their sources just read (as the elementwise passes find x and dy)."""
     k = res.get("kernels", {})
     if "bn_stats" not in k:
         return None
@@ -746,6 +793,11 @@ def _floors_for_bn(nh, torch, res, K, W, reps):
           "grad_sums_read": floors_for(nh, torch, 2 * E_s, 0, 0, K, W, reps),
           "dx_add": floors_for(nh, torch, 0, 3 * E_s, 0, K, W, reps),
           "apply_copy": floors_for(nh, torch, 0, 0, 2 * E_s, K, W, reps)}
+    n = E_s // 4 // 4 * 4
+    fl["apply_copy"]["hip_memcpy_d2d_cached_src"] = floor_warm(nh, torch, n, "copy", K, W, reps)
+    fl["dx_add"]["torch_add_cached_srcs"] = floor_warm(nh, torch, n, "add", K, W, reps)
+    for v in (fl["apply_copy"]["hip_memcpy_d2d_cached_src"], fl["dx_add"]["torch_add_cached_srcs"]):
+        v["frac_of_peak"] = round(v["gbs"] / HBM_PEAK_GBS, 4)
     for kname, fkey, skey in (("bn_stats", "stats_read", "read_stream"), ("bn_grad_sums", "grad_sums_read",
                                                                            "read_stream")):
         k[kname]["frac_of_read_stream"] = round(k[kname]["gbs"] / fl[fkey][skey]["gbs"], 4)
