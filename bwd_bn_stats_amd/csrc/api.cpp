@@ -569,6 +569,32 @@ static nh_status check_act(nh_act act, float slope)
 }
 
 // The BatchNorm training forward, whole (stage 0) or one of its two stages.
+// The launch plan every BatchNorm call shares: blocks per channel for the
+// reduction and elementwise passes, block numbering, and the unit order.
+static void bn_plan_grid(BnCall &a, nh_dtype io, int64_t N, int64_t C, int64_t HW, int vec, const DeviceInfo &d)
+{
+    a.io = io;
+    a.N = (int)N;
+    a.C = (int)C;
+    a.HW = (int)HW;
+    a.vec = vec;
+    const int64_t units = N * (HW / vec);
+    a.grid_y = (int)bn_grid_y_for(units, C, d);
+    a.ew_grid_y = (int)bn_ew_grid_y_for(units, C, d);
+    a.chan_fast = bn_chan_fast();
+    a.ilv = bn_interleave(units, std::max(a.grid_y, a.ew_grid_y));
+}
+
+// The training calls' further choices: where the finalize runs, and whether
+// one block per channel does the whole pass.
+static void bn_plan_training(BnCall &a, const DeviceInfo &d)
+{
+    const int64_t units = (int64_t)a.N * (a.HW / a.vec);
+    a.separate_finalize = g_override_bn_finalize_kernels.load() != 0 || !bn_fused_finalize_fits(a.grid_y);
+    a.channel_fused = bn_channel_fused(units, a.C, bn_slots(d));
+    a.channel_threads = bn_channel_threads(units, a.C, bn_slots(d));
+}
+
 static nh_status bn_forward_impl(int stage, const void *x, void *y, nh_dtype io, int64_t N, int64_t C,
                                  int64_t HW, const float *gamma, const float *beta, float *running_mean,
                                  float *running_var, float momentum, float eps, nh_act act, float slope,
@@ -592,15 +618,7 @@ static nh_status bn_forward_impl(int stage, const void *x, void *y, nh_dtype io,
         return fail(NH_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu)", need, ws_bytes);
 
     BnCall a{};
-    a.io = io;
-    a.N = (int)N;
-    a.C = (int)C;
-    a.HW = (int)HW;
-    a.vec = bn_vec(io, HW, x, y, nullptr);
-    a.grid_y = (int)bn_grid_y_for(N * (HW / a.vec), C, d);
-    a.ew_grid_y = (int)bn_ew_grid_y_for(N * (HW / a.vec), C, d);
-    a.chan_fast = bn_chan_fast();
-    a.ilv = bn_interleave(N * (HW / a.vec), std::max(a.grid_y, a.ew_grid_y));
+    bn_plan_grid(a, io, N, C, HW, bn_vec(io, HW, x, y, nullptr), d);
     a.x = x;
     a.out = y;
     a.gamma = gamma;
@@ -614,9 +632,7 @@ static nh_status bn_forward_impl(int stage, const void *x, void *y, nh_dtype io,
     a.stats = stats;
     a.partials = static_cast<float *>(ws);
     a.stage = stage;
-    a.separate_finalize = g_override_bn_finalize_kernels.load() != 0 || !bn_fused_finalize_fits(a.grid_y);
-    a.channel_fused = bn_channel_fused(N * (HW / a.vec), C, bn_slots(d));
-    a.channel_threads = bn_channel_threads(N * (HW / a.vec), C, bn_slots(d));
+    bn_plan_training(a, d);
     if (bn_col_layout(io, HW, a.vec, a.channel_fused)) bn_col_plan(a, x, y, nullptr);
     hipError_t e = bn_forward_launch(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "bn_forward_train launch");
@@ -721,15 +737,7 @@ static nh_status bn_backward_impl(int stage, const void *dy, const void *x, nh_d
         return fail(NH_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu)", need, ws_bytes);
 
     BnCall a{};
-    a.io = io;
-    a.N = (int)N;
-    a.C = (int)C;
-    a.HW = (int)HW;
-    a.vec = bn_vec(io, HW, x, dy, dx);
-    a.grid_y = (int)bn_grid_y_for(N * (HW / a.vec), C, d);
-    a.ew_grid_y = (int)bn_ew_grid_y_for(N * (HW / a.vec), C, d);
-    a.chan_fast = bn_chan_fast();
-    a.ilv = bn_interleave(N * (HW / a.vec), std::max(a.grid_y, a.ew_grid_y));
+    bn_plan_grid(a, io, N, C, HW, bn_vec(io, HW, x, dy, dx), d);
     a.x = x;
     a.dy = dy;
     a.out = dx;
@@ -740,9 +748,7 @@ static nh_status bn_backward_impl(int stage, const void *dy, const void *x, nh_d
     a.grads = grads;
     a.partials = static_cast<float *>(ws);
     a.stage = stage;
-    a.separate_finalize = g_override_bn_finalize_kernels.load() != 0 || !bn_fused_finalize_fits(a.grid_y);
-    a.channel_fused = bn_channel_fused(N * (HW / a.vec), C, bn_slots(d));
-    a.channel_threads = bn_channel_threads(N * (HW / a.vec), C, bn_slots(d));
+    bn_plan_training(a, d);
     if (bn_col_layout(io, HW, a.vec, a.channel_fused)) bn_col_plan(a, x, dy, dx);
     hipError_t e = bn_backward_launch(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "bn_backward launch");
@@ -789,15 +795,7 @@ nh_status bn_forward_infer(const void *x, void *y, nh_dtype io, int64_t N, int64
     if ((st = device_info(&d)) != NH_OK) return st;
 
     BnCall a{};
-    a.io = io;
-    a.N = (int)N;
-    a.C = (int)C;
-    a.HW = (int)HW;
-    a.vec = bn_vec(io, HW, x, y, nullptr);
-    a.grid_y = (int)bn_grid_y_for(N * (HW / a.vec), C, d);
-    a.ew_grid_y = (int)bn_ew_grid_y_for(N * (HW / a.vec), C, d);
-    a.chan_fast = bn_chan_fast();
-    a.ilv = bn_interleave(N * (HW / a.vec), std::max(a.grid_y, a.ew_grid_y));
+    bn_plan_grid(a, io, N, C, HW, bn_vec(io, HW, x, y, nullptr), d);
     a.inference = 1;
     a.x = x;
     a.out = y;
