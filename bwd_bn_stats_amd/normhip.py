@@ -11,6 +11,7 @@ plus the workspace queries and measurement helpers.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch
@@ -144,11 +145,39 @@ def _dev_tensor(t, name, dtype=None, numel=None):
 
 
 def _workspace(nbytes: int, device, workspace):
-    """The caller's workspace tensor as given (the library checks its size),
-    or a new one of the queried size."""
+    """The caller's workspace tensor (device memory, contiguous; the library
+    checks its size and alignment), or a new one of the queried size."""
     if workspace is None and nbytes > 0:
         return torch.empty(nbytes, dtype=torch.uint8, device=device)
-    return workspace
+    return _dev_tensor(workspace, "workspace")
+
+
+def common_device(tensors):
+    """The one device of the device tensors among `tensors` (None when there
+    are none); ValueError when they span several.  The library runs on the
+    current HIP device and takes every pointer and the stream on it."""
+    devs = []
+    for t in tensors:
+        d = getattr(t, "device", None)
+        if getattr(t, "is_cuda", False) and d not in devs:
+            devs.append(d)
+    if len(devs) > 1:
+        raise ValueError(f"all tensors must be on one device, got {', '.join(str(d) for d in devs)}")
+    return devs[0] if devs else None
+
+
+def _on_tensor_device(f):
+    """Runs f with the device of its tensor arguments current (all on one
+    device), so that the library's current device, the stream and every
+    pointer agree."""
+    @functools.wraps(f)
+    def g(*args, **kw):
+        d = common_device([a for a in list(args) + list(kw.values()) if isinstance(a, torch.Tensor)])
+        if d is None:
+            return f(*args, **kw)
+        with torch.cuda.device(d):
+            return f(*args, **kw)
+    return g
 
 
 def _nchw(x: torch.Tensor):
@@ -198,6 +227,7 @@ def _act(act):
     return ACTS[act] if isinstance(act, str) else int(act)
 
 
+@_on_tensor_device
 def bn_forward_train(x, gamma=None, beta=None, running_mean=None, running_var=None,
                      momentum: float = 0.1, eps: float = 1e-5, *, act="none", slope: float = 0.01,
                      y=None, stats=None, workspace=None):
@@ -226,6 +256,7 @@ def bn_forward_train(x, gamma=None, beta=None, running_mean=None, running_var=No
     return y, stats
 
 
+@_on_tensor_device
 def bn_backward(dy, x, stats, *, beta=None, act="none", slope: float = 0.01, dx=None, grads=None,
                 need_dx=True, workspace=None):
     """BatchNorm2d training backward (bn_backward, or bn_act_backward when act
@@ -254,6 +285,7 @@ def bn_backward(dy, x, stats, *, beta=None, act="none", slope: float = 0.01, dx=
     return dx, grads
 
 
+@_on_tensor_device
 def bn_forward_train_stage(stage: int, x, y, stats, workspace, gamma=None, beta=None, running_mean=None,
                            running_var=None, momentum: float = 0.1, eps: float = 1e-5):
     """One stage of the BatchNorm2d training forward (bn_forward_train_stage):
@@ -268,12 +300,14 @@ def bn_forward_train_stage(stage: int, x, y, stats, workspace, gamma=None, beta=
         _dev_tensor(t, n, f32, C)
     _dev_tensor(y, "y", x.dtype, x.numel())
     _dev_tensor(stats, "stats", f32, 4 * C)
+    _dev_tensor(workspace, "workspace")
     nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.bn_forward_train_stage(int(stage), _ptr(x), _ptr(y), _dt(x), N, C, HW, _ptr(gamma), _ptr(beta),
                                       _ptr(running_mean), _ptr(running_var), momentum, eps, _ptr(stats),
                                       _ptr(workspace), nb, _stream(x.device)), "bn_forward_train_stage")
 
 
+@_on_tensor_device
 def bn_backward_stage(stage: int, dy, x, stats, dx, grads, workspace):
     """One stage of the BatchNorm2d training backward (bn_backward_stage): 1 =
     the grad_sums pass into `workspace`, 2 = finalize + dx from it (dx may be
@@ -285,11 +319,13 @@ def bn_backward_stage(stage: int, dy, x, stats, dx, grads, workspace):
     _dev_tensor(stats, "stats", f32, 4 * C)
     _dev_tensor(dx, "dx", x.dtype, x.numel())
     _dev_tensor(grads, "grads", f32, 4 * C)
+    _dev_tensor(workspace, "workspace")
     nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.bn_backward_stage(int(stage), _ptr(dy), _ptr(x), _dt(x), N, C, HW, _ptr(stats), _ptr(dx),
                                  _ptr(grads), _ptr(workspace), nb, _stream(x.device)), "bn_backward_stage")
 
 
+@_on_tensor_device
 def bn_forward_infer(x, running_mean, running_var, gamma=None, beta=None, eps: float = 1e-5, *,
                      act="none", slope: float = 0.01, y=None):
     """BatchNorm2d inference from the running statistics (+ activation).  Returns y."""
@@ -313,6 +349,7 @@ def _rows(x):
     return rows, cols
 
 
+@_on_tensor_device
 def layernorm_backward(dy, x, mean, rstd, weight=None, *, dx_dtype=None, w_dtype=None,
                        need_dx=True, need_dweight=True, need_dbias=True, dx=None,
                        dweight=None, dbias=None, workspace=None):
@@ -346,6 +383,7 @@ def layernorm_backward(dy, x, mean, rstd, weight=None, *, dx_dtype=None, w_dtype
     return dx, dweight, dbias
 
 
+@_on_tensor_device
 def bda_layernorm_backward(dy, x, mean, rstd, weight=None, dresidual=None, mask=None,
                            scale: float = 1.0, *, w_dtype=None, need_dh=True, need_da=True,
                            need_dweight=True, need_dbias=True, need_dbias_in=True, workspace=None):
@@ -379,6 +417,7 @@ def bda_layernorm_backward(dy, x, mean, rstd, weight=None, dresidual=None, mask=
     return (dh, da, *cols_out)
 
 
+@_on_tensor_device
 def rmsnorm_backward(dy, x, rms=None, weight=None, eps: float = 1e-5, *, need_dx=True,
                      need_dweight=True, dx=None, dweight=None, workspace=None):
     """RMSNorm backward over the last dim.  rms=None recomputes rms from x
@@ -402,6 +441,7 @@ def rmsnorm_backward(dy, x, rms=None, weight=None, eps: float = 1e-5, *, need_dx
     return dx, dweight
 
 
+@_on_tensor_device
 def layernorm_forward(x, weight=None, bias=None, eps: float = 1e-5, *, y_dtype=None, w_dtype=None,
                       y=None, mean=None, rstd=None, need_rstd=True):
     """LayerNorm training forward over the last dim.  Returns (y, mean, rstd)
@@ -425,6 +465,7 @@ def layernorm_forward(x, weight=None, bias=None, eps: float = 1e-5, *, y_dtype=N
     return y, mean, rstd
 
 
+@_on_tensor_device
 def rmsnorm_forward(x, weight=None, eps: float = 1e-5, *, y=None, rms=None, need_rms=True):
     """RMSNorm forward over the last dim.  Returns (y, rms or None)."""
     _dev_tensor(x, "x")
@@ -459,17 +500,29 @@ def timing_read(kernel) -> tuple[float, int]:
     return ms.value, n.value
 
 
+@_on_tensor_device
 def calib_copy(src, dst):
-    _check(lib.nh_calib_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(),
-                             _stream(src.device)), "nh_calib_copy")
+    _dev_tensor(src, "src")
+    _dev_tensor(dst, "dst")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError(f"dst holds fewer than the {nbytes} bytes of src")
+    _check(lib.nh_calib_copy(_ptr(src), _ptr(dst), nbytes, _stream(src.device)), "nh_calib_copy")
 
 
+@_on_tensor_device
 def calib_read(a, block_sums):
+    _dev_tensor(a, "a", torch.float32)
+    _dev_tensor(block_sums, "block_sums", torch.float32)
     _check(lib.nh_calib_read(_ptr(a), a.numel(), _ptr(block_sums), block_sums.numel(),
                              _stream(a.device)), "nh_calib_read")
 
 
+@_on_tensor_device
 def calib_add(a, b, out):
+    _dev_tensor(a, "a", torch.float32)
+    _dev_tensor(b, "b", torch.float32, a.numel())
+    _dev_tensor(out, "out", torch.float32, a.numel())
     _check(lib.nh_calib_add(_ptr(a), _ptr(b), _ptr(out), a.numel(), _stream(a.device)), "nh_calib_add")
 
 

@@ -265,3 +265,36 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     mod = importlib.util.module_from_spec(spec)
     with pytest.raises(ImportError, match="no CPU fallback"):
         spec.loader.exec_module(mod)
+
+
+def test_binding_requires_one_device():
+    """The binding runs each call with its tensors' device current and
+    refuses tensors spread over several devices (the library takes every
+    pointer and the stream on the current device)."""
+    from types import SimpleNamespace as NS
+    a, b = NS(is_cuda=True, device="cuda:0"), NS(is_cuda=True, device="cuda:1")
+    host = NS(is_cuda=False, device="cpu")
+    assert nh.common_device([a, host, NS(is_cuda=True, device="cuda:0")]) == "cuda:0"
+    assert nh.common_device([host]) is None and nh.common_device([]) is None
+    with pytest.raises(ValueError, match="one device"):
+        nh.common_device([a, host, b])
+
+
+def test_binding_refuses_host_tensors():
+    """Host tensors never reach a kernel: each binding call that takes
+    tensors raises before calling the library."""
+    import torch
+    x = torch.ones(2, 3, 4)
+    f = torch.ones(16)
+    with pytest.raises(ValueError, match="device tensor"):
+        nh.bn_forward_train(x)
+    with pytest.raises(ValueError, match="device tensor"):
+        nh.bn_forward_train_stage(1, x, x, torch.ones(4, 3), torch.ones(64, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="device tensor"):
+        nh.calib_copy(f, f)
+    with pytest.raises(ValueError, match="device tensor"):
+        nh.calib_read(f, f)
+    with pytest.raises(ValueError, match="device tensor"):
+        nh.calib_add(f, f, f)
+    with pytest.raises(ValueError, match="device tensor"):
+        nh.rmsnorm_forward(torch.ones(4, 8))

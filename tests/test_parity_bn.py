@@ -272,6 +272,37 @@ def test_bn_error_paths(nh):
     assert bool(torch.all(rm == 2.0)) and bool(torch.all(rv == 3.0))
 
 
+def test_binding_refuses_host_memory_beside_device_tensors(nh):
+    """A host tensor among device ones (a workspace, a per-channel vector, a
+    calibration buffer) or a too-small calibration output raises in the
+    binding before any launch; nothing is written."""
+    x = torch.randn(2, 3, 4, 4, device="cuda")
+    rm = torch.full((3,), 2.0, device="cuda")
+    rv = torch.full((3,), 3.0, device="cuda")
+    host_ws = torch.empty(1 << 16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="workspace must be a device tensor"):
+        nh.bn_forward_train(x, None, None, rm, rv, workspace=host_ws)
+    with pytest.raises(ValueError, match="gamma must be a device tensor"):
+        nh.bn_forward_train(x, torch.ones(3), None, rm, rv)
+    y, stats = torch.empty_like(x), torch.empty(4, 3, device="cuda")
+    with pytest.raises(ValueError, match="workspace must be a device tensor"):
+        nh.bn_forward_train_stage(1, x, y, stats, host_ws, None, None, rm, rv)
+    g = torch.empty(4, 3, device="cuda")
+    with pytest.raises(ValueError, match="workspace must be a device tensor"):
+        nh.bn_backward_stage(1, x, x, stats, y, g, host_ws)
+    with pytest.raises(ValueError, match="workspace must be a device tensor"):
+        nh.bn_backward(x, x, stats, workspace=host_ws)
+    r = torch.randn(8, 64, device="cuda")
+    with pytest.raises(ValueError, match="workspace must be a device tensor"):
+        nh.rmsnorm_backward(r, r, torch.ones(8, device="cuda"), torch.ones(64, device="cuda"), workspace=host_ws)
+    with pytest.raises(ValueError, match="fewer than"):
+        nh.calib_copy(torch.ones(64, device="cuda"), torch.empty(32, device="cuda"))
+    with pytest.raises(ValueError, match="must have 64 elements"):
+        nh.calib_add(torch.ones(64, device="cuda"), torch.ones(32, device="cuda"), torch.empty(64, device="cuda"))
+    torch.cuda.synchronize()
+    assert bool(torch.all(rm == 2.0)) and bool(torch.all(rv == 3.0))
+
+
 @pytest.mark.parametrize("name", ["cifar_256x32x32x32_f32", "resnet_64x256x56x56_bf16",
                                   "ragged_3x37x41x40_f32"])
 def test_bn_bit_identical_runs(nh, name):
