@@ -39,8 +39,10 @@ struct WeightGroup {
 // rows of at most this many elements per thread.
 constexpr int kLnKeepMaxElems = 16;
 
-// LDS floats of a team's double-buffered row sums (two quantities per wave).
+// LDS floats of a team's double-buffered row sums (two quantities per wave;
+// red3_floats: three).
 constexpr int red_floats(int team) { return 2 * (team / kWave) * 2; }
+constexpr int red3_floats(int team) { return 2 * (team / kWave) * 3; }
 
 // The DPP wave sums (dpp_pair_add, wave_total) live in nh_device.hpp.
 
@@ -65,6 +67,33 @@ __device__ __forceinline__ void team_sum2(float *red, int wave, int lane, float 
     }
     a = sa;
     b = sb;
+}
+
+// The same for three quantities.
+template <int WAVES = kTeamWaves>
+__device__ __forceinline__ void team_sum3(float *red, int wave, int lane, float &a, float &b, float &c)
+{
+    a = wave_total(a);
+    b = wave_total(b);
+    c = wave_total(c);
+    if (lane == 0) {
+        red[wave * 3 + 0] = a;
+        red[wave * 3 + 1] = b;
+        red[wave * 3 + 2] = c;
+    }
+    lds_barrier();
+    float sa = red[0];
+    float sb = red[1];
+    float sc = red[2];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) {
+        sa += red[w * 3 + 0];
+        sb += red[w * 3 + 1];
+        sc += red[w * 3 + 2];
+    }
+    a = sa;
+    b = sb;
+    c = sc;
 }
 
 // Sum over the ct lanes of a subgroup (ct a power of two, subgroups aligned

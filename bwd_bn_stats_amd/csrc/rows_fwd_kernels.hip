@@ -2,11 +2,17 @@
 // writing the statistics their backward passes consume.
 //
 //   LayerNorm: the statistics NVIDIA/Fuser issue #1473's layer_norm backward
-//     takes as inputs (mean and rstd per row), computed with the one-pass
-//     shifted sums of Aether-ML PR #18 ("One-pass statistics") applied per
-//     row: with K = the row's first element and d = x - K,
-//       mean = K + sum d / H,  var = sum d^2 / H - (sum d / H)^2 (clamped at 0),
-//       rstd = 1/sqrt(var + eps),  y = (x - mean)*rstd*w + b.
+//     takes as inputs (mean and rstd per row).  The variance comes from the
+//     one-pass shifted sums of Aether-ML PR #18 ("One-pass statistics")
+//     applied per row: with K = the row's first element, d = x - K and
+//     md = sum d / H,
+//       var = sum d^2 / H - md^2 (clamped at 0),  rstd = 1/sqrt(var + eps),
+//       y = ((x - K) - md)*rstd*w + b,
+//     and the stored mean from the plain sum, mean = sum x / H.  Both avoid
+//     forming K + md in fp32: that sum cancels K against md (a row's mean is
+//     often far smaller than its elements) and loses the cancelled digits,
+//     and x - (K + md) rounds the mean before a subtraction that rstd (up to
+//     1/sqrt(eps)) then amplifies on nearly constant rows.
 //   RMSNorm: NVIDIA/Fuser issue #3629's rmsnorm_prims,
 //       rms = sqrt(sum x^2 / H + eps),  y = w*(x/rms)
 //     (rms is what that issue's rmsnorm_bwd_fusion takes as its saved input).
@@ -35,6 +41,43 @@ struct ParamGroup {
     }
 };
 
+// A row's statistics from its sums (LayerNorm: plain sum s0, shifted sum s1
+// and sum of squares s2 of d = x - K; RMSNorm: sum of squares s2 of x), and
+// the two numbers its output takes: a = rstd (LayerNorm) or 1/rms (RMSNorm),
+// md = s1 / H (LayerNorm) or 0.  Writes the statistics if `writer`.
+template <int KIND>
+__device__ __forceinline__ void fwd_row_stats(float s0, float s1, float s2, float invH, float eps, int64_t r,
+                                              bool writer, float *stat0, float *stat1, float &a, float &md)
+{
+    if constexpr (KIND == 0) {
+        md = s1 * invH;
+        const float var = fmaxf(s2 * invH - md * md, 0.f);
+        a = 1.0f / sqrtf(var + eps);
+        if (writer) {
+            stat0[r] = s0 * invH;
+            if (stat1 != nullptr) stat1[r] = a;
+        }
+    } else {
+        const float rms = sqrtf(fmaf(s2, invH, eps));
+        a = 1.0f / rms;
+        md = 0.f;
+        if (writer && stat0 != nullptr) stat0[r] = rms;
+    }
+}
+
+// One output element: ((x - K) - md)*rstd*w + b (LayerNorm), w*(x/rms) (RMSNorm).
+template <int KIND>
+__device__ __forceinline__ float fwd_out(float v, float K, float md, float a, float w, float b)
+{
+    if constexpr (KIND == 0) return fmaf(((v - K) - md) * a, w, b);
+    else return w * (v * a);
+}
+
+// LDS floats of a team's double-buffered row sums: three for LayerNorm, two
+// for RMSNorm (only the second is used).
+template <int KIND>
+constexpr int fwd_red_floats(int team) { return KIND == 0 ? red3_floats(team) : red_floats(team); }
+
 // KIND 0: LayerNorm (stat0 = mean, stat1 = rstd); KIND 1: RMSNorm (stat0 = rms).
 template <int KIND, typename TX, typename TY, int VEC, int MAXG, int MT, int D, int TEAM>
 __global__ void __launch_bounds__(MT)
@@ -42,7 +85,8 @@ norm_fwd_rows_kernel(const TX *__restrict__ x, const void *__restrict__ w,
                      const void *__restrict__ b, int w_bf16, int rows, int H, float eps,
                      TY *__restrict__ y, float *__restrict__ stat0, float *__restrict__ stat1)
 {
-    __shared__ float red[red_floats(TEAM)];
+    constexpr int kRed = fwd_red_floats<KIND>(TEAM);
+    __shared__ float red[kRed];
     const int tt = threadIdx.x;
     const int wave = tt / kWave;
     const int lane = tt & (kWave - 1);
@@ -79,7 +123,7 @@ norm_fwd_rows_kernel(const TX *__restrict__ x, const void *__restrict__ w,
     auto do_row = [&](const RowBuf &rb, int it) {
         const int r = it * G + (int)blockIdx.x;
         const bool active = r < rows;
-        float s1 = 0.f, s2 = 0.f;
+        float s0 = 0.f, s1 = 0.f, s2 = 0.f;
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
             const int grp = tt + k * TEAM;
@@ -89,6 +133,7 @@ norm_fwd_rows_kernel(const TX *__restrict__ x, const void *__restrict__ w,
                     const float v = rb.x[k].get(e);
                     if constexpr (KIND == 0) {
                         const float d = v - rb.K;
+                        s0 += v;
                         s1 += d;
                         s2 = fmaf(d, d, s2);
                     } else {
@@ -97,24 +142,13 @@ norm_fwd_rows_kernel(const TX *__restrict__ x, const void *__restrict__ w,
                 }
             }
         }
-        team_sum2<TEAM / kWave>(red + (it & 1) * (red_floats(TEAM) / 2), wave, lane, s1, s2);
+        if constexpr (KIND == 0)
+            team_sum3<TEAM / kWave>(red + (it & 1) * (kRed / 2), wave, lane, s0, s1, s2);
+        else
+            team_sum2<TEAM / kWave>(red + (it & 1) * (kRed / 2), wave, lane, s1, s2);
         if (!active) return;
-        float a, c;  // y = fmaf(x - c, a*w, b) (LN) or y = (x*a)*w (RMS)
-        if constexpr (KIND == 0) {
-            const float md = s1 * invH;
-            const float var = fmaxf(s2 * invH - md * md, 0.f);
-            c = rb.K + md;
-            a = 1.0f / sqrtf(var + eps);
-            if (tt == 0) {
-                stat0[r] = c;
-                if (stat1 != nullptr) stat1[r] = a;
-            }
-        } else {
-            const float rms = sqrtf(fmaf(s2, invH, eps));
-            a = 1.0f / rms;
-            c = 0.f;
-            if (tt == 0 && stat0 != nullptr) stat0[r] = rms;
-        }
+        float a, md;
+        fwd_row_stats<KIND>(s0, s1, s2, invH, eps, r, tt == 0, stat0, stat1, a, md);
         const size_t rowoff = (size_t)r * H;
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
@@ -123,10 +157,9 @@ norm_fwd_rows_kernel(const TX *__restrict__ x, const void *__restrict__ w,
                 float o[VEC];
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    if constexpr (KIND == 0)
-                        o[e] = fmaf((rb.x[k].get(e) - c) * a, wv[k].v[e], bv[k].v[e]);
-                    else
-                        o[e] = wv[k].v[e] * (rb.x[k].get(e) * a);
+                    float bias = 0.f;
+                    if constexpr (KIND == 0) bias = bv[k].v[e];
+                    o[e] = fwd_out<KIND>(rb.x[k].get(e), rb.K, md, a, wv[k].v[e], bias);
                 }
                 st<true, TY, VEC>(y + rowoff + grp * VEC, o);
             }
@@ -137,30 +170,6 @@ norm_fwd_rows_kernel(const TX *__restrict__ x, const void *__restrict__ w,
 }
 
 // ---- generic path ------------------------------------------------------------------
-// The row's statistics and output from its two sums (LayerNorm: shifted sum
-// and sum of squares; RMSNorm: sum of squares): y = fmaf(x - c, a*w, b)
-// (LayerNorm) or y = (x*a)*w (RMSNorm).  Writes the statistics if `writer`.
-template <int KIND>
-__device__ __forceinline__ void fwd_row_stats(float s1, float s2, float K, float invH, float eps, int64_t r,
-                                              bool writer, float *stat0, float *stat1, float &a, float &c)
-{
-    if constexpr (KIND == 0) {
-        const float md = s1 * invH;
-        const float var = fmaxf(s2 * invH - md * md, 0.f);
-        c = K + md;
-        a = 1.0f / sqrtf(var + eps);
-        if (writer) {
-            stat0[r] = c;
-            if (stat1 != nullptr) stat1[r] = a;
-        }
-    } else {
-        const float rms = sqrtf(fmaf(s2, invH, eps));
-        a = 1.0f / rms;
-        c = 0.f;
-        if (writer && stat0 != nullptr) stat0[r] = rms;
-    }
-}
-
 // Rows of at most 64 groups of VEC elements (VEC = 1 for any alignment, or
 // the vector width for aligned rows): a subgroup of ct lanes (the power of
 // two covering the groups) per row, U rows of a slot loaded at once, the row
@@ -194,26 +203,31 @@ norm_fwd_narrow_kernel(const TX *__restrict__ x, const void *__restrict__ w,
         }
 #pragma unroll
         for (int k = 0; k < U; ++k) {
-            float s1 = 0.f, s2 = 0.f;
+            float s0 = 0.f, s1 = 0.f, s2 = 0.f;
             if (col_ok) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
                     const float d = v[k][e] - K[k];
-                    if constexpr (KIND == 0) s1 += d;
+                    if constexpr (KIND == 0) {
+                        s0 += v[k][e];
+                        s1 += d;
+                    }
                     s2 = fmaf(d, d, s2);
                 }
             }
-            s1 = sub_sum(s1, ct);
+            if constexpr (KIND == 0) {
+                s0 = sub_sum(s0, ct);
+                s1 = sub_sum(s1, ct);
+            }
             s2 = sub_sum(s2, ct);
             const int64_t rk = r0 + k * stride;
             if (rk < rows) {
-                float a, c;
-                fwd_row_stats<KIND>(s1, s2, K[k], invH, eps, rk, lane == 0, stat0, stat1, a, c);
+                float a, md;
+                fwd_row_stats<KIND>(s0, s1, s2, invH, eps, rk, lane == 0, stat0, stat1, a, md);
                 if (col_ok) {
                     float o[VEC];
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e)
-                        o[e] = KIND == 0 ? fmaf((v[k][e] - c) * a, wv.v[e], bv.v[e]) : wv.v[e] * (v[k][e] * a);
+                    for (int e = 0; e < VEC; ++e) o[e] = fwd_out<KIND>(v[k][e], K[k], md, a, wv.v[e], bv.v[e]);
                     st<true, TY, VEC>(y + (size_t)rk * H + col, o);
                 }
             }
@@ -224,16 +238,26 @@ norm_fwd_narrow_kernel(const TX *__restrict__ x, const void *__restrict__ w,
 // Wider rows, any alignment (VEC = 1) or too wide for the register-resident
 // kernel (VEC = the vector width): a TEAM-thread block per row, two reads of
 // the row -- the first (cacheable) for the sums, U groups of a thread in
-// flight, the second from the caches for the output.
+// flight, the second from the caches for the output.  The plan counts on two
+// 1024-thread blocks per CU (8 waves per SIMD); the one variant the compiler
+// otherwise gives more than 64 VGPRs (bf16 rows in 8-byte groups, fp32
+// output) is held to that explicitly -- bounding the others makes them spill.
 template <int KIND, typename TX, typename TY, int VEC, int TEAM>
-__global__ void __launch_bounds__(TEAM)
+constexpr int fwd_team_min_waves()
+{
+    return TEAM == kGenFwdBigTeam && sizeof(TX) == 2 && sizeof(TY) == 4 && VEC == 4 ? 8 : 1;
+}
+
+template <int KIND, typename TX, typename TY, int VEC, int TEAM>
+__global__ void __launch_bounds__(TEAM, (fwd_team_min_waves<KIND, TX, TY, VEC, TEAM>()))
 norm_fwd_team_kernel(const TX *__restrict__ x, const void *__restrict__ w,
                      const void *__restrict__ b, int w_bf16, int rows, int H, float eps,
                      TY *__restrict__ y, float *__restrict__ stat0, float *__restrict__ stat1)
 {
     constexpr int WAVES = TEAM / kWave;
     constexpr int U = VEC == 8 ? 4 : 8;
-    __shared__ float red[red_floats(TEAM)];
+    constexpr int kRed = fwd_red_floats<KIND>(TEAM);
+    __shared__ float red[kRed];
     const int tt = threadIdx.x;
     const int wave = tt / kWave;
     const int lane = tt & (kWave - 1);
@@ -244,12 +268,15 @@ norm_fwd_team_kernel(const TX *__restrict__ x, const void *__restrict__ w,
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x, ++it) {
         const TX *xr = x + (size_t)r * H;
         const float K = KIND == 0 ? to_f32(xr[0]) : 0.f;
-        float s1 = 0.f, s2 = 0.f;
+        float s0 = 0.f, s1 = 0.f, s2 = 0.f;
         auto add = [&](const float (&v)[VEC]) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
                 const float d = v[e] - K;
-                if constexpr (KIND == 0) s1 += d;
+                if constexpr (KIND == 0) {
+                    s0 += v[e];
+                    s1 += d;
+                }
                 s2 = fmaf(d, d, s2);
             }
         };
@@ -266,9 +293,12 @@ norm_fwd_team_kernel(const TX *__restrict__ x, const void *__restrict__ w,
             ld<false, TX, VEC>(xr + (size_t)gi * VEC, v);
             add(v);
         }
-        team_sum2<WAVES>(red + (it & 1) * (red_floats(TEAM) / 2), wave, lane, s1, s2);
-        float a, c;
-        fwd_row_stats<KIND>(s1, s2, K, invH, eps, r, tt == 0, stat0, stat1, a, c);
+        if constexpr (KIND == 0)
+            team_sum3<WAVES>(red + (it & 1) * (kRed / 2), wave, lane, s0, s1, s2);
+        else
+            team_sum2<WAVES>(red + (it & 1) * (kRed / 2), wave, lane, s1, s2);
+        float a, md;
+        fwd_row_stats<KIND>(s0, s1, s2, invH, eps, r, tt == 0, stat0, stat1, a, md);
         TY *yr = y + (size_t)r * H;
         auto out = [&](int grp, const float (&v)[VEC]) {
             ParamGroup<VEC> wv, bv;
@@ -276,12 +306,7 @@ norm_fwd_team_kernel(const TX *__restrict__ x, const void *__restrict__ w,
             if constexpr (KIND == 0) bv.load(b, w_bf16, grp * VEC, 0.f);
             float o[VEC];
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                if constexpr (KIND == 0)
-                    o[e] = fmaf((v[e] - c) * a, wv.v[e], bv.v[e]);
-                else
-                    o[e] = wv.v[e] * (v[e] * a);
-            }
+            for (int e = 0; e < VEC; ++e) o[e] = fwd_out<KIND>(v[e], K, md, a, wv.v[e], KIND == 0 ? bv.v[e] : 0.f);
             st<true, TY, VEC>(yr + (size_t)grp * VEC, o);
         };
         gi = tt;

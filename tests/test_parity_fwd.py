@@ -83,6 +83,42 @@ def test_ln_forward_large_offset(nh, oracle_mod):
     check("mean", host(gm), want_m, wl.F32)
 
 
+# Rows whose outputs are ill-conditioned in fp32, found by a seeded random
+# sweep: wide rows whose mean is far smaller than their elements (the stored
+# mean), and 2-column rows whose two values nearly coincide (rstd near
+# 1/sqrt(eps) amplifies any rounding of x - mean).  Summed as K + sum(x - K)
+# (K the first element) and applied as x - mean, they missed the fp32 bound
+# by up to 1.7x; the plain sum for the mean and (x - K) - sum(x - K)/H for the
+# output keep them within it.
+@pytest.mark.parametrize("rows,cols,xt,wt,yt,bias,in_place,seed", [
+    (195, 39921, wl.BF16, wl.F32, wl.F32, False, False, 20002),
+    (208, 32768, wl.BF16, wl.BF16, wl.BF16, True, True, 20016),
+    (86, 36335, wl.F32, wl.F32, wl.F32, True, False, 20026),
+    (65536, 2, wl.F32, wl.BF16, wl.F32, True, False, 20029)])
+def test_ln_forward_ill_conditioned_rows(nh, oracle_mod, rows, cols, xt, wt, yt, bias, in_place, seed):
+    c = wl.rows_case(rows, cols, x_t=xt, dy_t=xt, w_t=wt, seed=seed, with_bias=True)
+    _ln_fwd_case(nh, oracle_mod, c, yt, bias=bias, in_place=in_place)
+
+
+def test_ln_forward_nearly_constant_rows(nh, oracle_mod):
+    """Rows of 2-5 elements around 2.5 with a spread of 1e-3 (variance far
+    below eps): the output is (x - mean) * rstd with rstd near 1/sqrt(eps)."""
+    rng = np.random.Generator(np.random.PCG64(74))
+    for cols in (2, 3, 5):
+        x = (2.5 + 1e-3 * rng.normal(size=(8192, cols))).astype(np.float32)
+        w = (0.5 + rng.random(cols)).astype(np.float32)
+        b = (0.1 * rng.normal(size=cols)).astype(np.float32)
+        want_y, want_m, want_r = oracle_mod.layernorm_forward(x.astype(np.float64), w.astype(np.float64),
+                                                              b.astype(np.float64), eps=1e-5)
+        print(f"[ln fwd parity] nearly constant rows 8192x{cols}", flush=True)
+        gy, gm, gr = nh.layernorm_forward(torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda(),
+                                          torch.from_numpy(b).cuda(), 1e-5)
+        torch.cuda.synchronize()
+        check("y", host(gy), want_y, wl.F32)
+        check("mean", host(gm), want_m, wl.F32)
+        check("rstd", host(gr), want_r, wl.F32)
+
+
 def _rms_fwd_case(nh, oracle_mod, c, *, weight=True, need_rms=True, in_place=False):
     want_y, want_rms = oracle_mod.rmsnorm_forward(c.x.value, c.w.value if weight else None, eps=c.eps)
     print(f"[rms fwd parity] {c.rows}x{c.cols} t={c.x.dtype} weight={weight} in_place={in_place}",
