@@ -7,12 +7,14 @@
 //     applied per row: with K = the row's first element, d = x - K and
 //     md = sum d / H,
 //       var = sum d^2 / H - md^2 (clamped at 0),  rstd = 1/sqrt(var + eps),
-//       y = ((x - K) - md)*rstd*w + b,
-//     and the stored mean from the plain sum, mean = sum x / H.  Both avoid
-//     forming K + md in fp32: that sum cancels K against md (a row's mean is
-//     often far smaller than its elements) and loses the cancelled digits,
-//     and x - (K + md) rounds the mean before a subtraction that rstd (up to
-//     1/sqrt(eps)) then amplifies on nearly constant rows.
+//       y = ((x - K) - md)*rstd*w + b:
+//     x - (K + md) would round the mean before a subtraction that rstd (up
+//     to 1/sqrt(eps)) amplifies on nearly constant rows.  The stored mean is
+//     K + md or sum x / H, whichever sums the smaller terms: an fp32 sum errs
+//     in proportion to the magnitude of its terms, |x - K| for the one and
+//     |x| for the other, and |md| < |sum x / H| says the first are smaller
+//     (rows far from zero relative to their spread; rows around zero take
+//     the plain sum, which K + md would lose to cancellation).
 //   RMSNorm: NVIDIA/Fuser issue #3629's rmsnorm_prims,
 //       rms = sqrt(sum x^2 / H + eps),  y = w*(x/rms)
 //     (rms is what that issue's rmsnorm_bwd_fusion takes as its saved input).
@@ -46,15 +48,17 @@ struct ParamGroup {
 // the two numbers its output takes: a = rstd (LayerNorm) or 1/rms (RMSNorm),
 // md = s1 / H (LayerNorm) or 0.  Writes the statistics if `writer`.
 template <int KIND>
-__device__ __forceinline__ void fwd_row_stats(float s0, float s1, float s2, float invH, float eps, int64_t r,
-                                              bool writer, float *stat0, float *stat1, float &a, float &md)
+__device__ __forceinline__ void fwd_row_stats(float s0, float s1, float s2, float K, float invH, float eps,
+                                              int64_t r, bool writer, float *stat0, float *stat1, float &a,
+                                              float &md)
 {
     if constexpr (KIND == 0) {
         md = s1 * invH;
         const float var = fmaxf(s2 * invH - md * md, 0.f);
         a = 1.0f / sqrtf(var + eps);
         if (writer) {
-            stat0[r] = s0 * invH;
+            const float mp = s0 * invH;
+            stat0[r] = fabsf(md) < fabsf(mp) ? K + md : mp;
             if (stat1 != nullptr) stat1[r] = a;
         }
     } else {
@@ -148,7 +152,7 @@ norm_fwd_rows_kernel(const TX *__restrict__ x, const void *__restrict__ w,
             team_sum2<TEAM / kWave>(red + (it & 1) * (kRed / 2), wave, lane, s1, s2);
         if (!active) return;
         float a, md;
-        fwd_row_stats<KIND>(s0, s1, s2, invH, eps, r, tt == 0, stat0, stat1, a, md);
+        fwd_row_stats<KIND>(s0, s1, s2, rb.K, invH, eps, r, tt == 0, stat0, stat1, a, md);
         const size_t rowoff = (size_t)r * H;
 #pragma unroll
         for (int k = 0; k < MAXG; ++k) {
@@ -223,7 +227,7 @@ norm_fwd_narrow_kernel(const TX *__restrict__ x, const void *__restrict__ w,
             const int64_t rk = r0 + k * stride;
             if (rk < rows) {
                 float a, md;
-                fwd_row_stats<KIND>(s0, s1, s2, invH, eps, rk, lane == 0, stat0, stat1, a, md);
+                fwd_row_stats<KIND>(s0, s1, s2, K[k], invH, eps, rk, lane == 0, stat0, stat1, a, md);
                 if (col_ok) {
                     float o[VEC];
 #pragma unroll
@@ -298,7 +302,7 @@ norm_fwd_team_kernel(const TX *__restrict__ x, const void *__restrict__ w,
         else
             team_sum2<WAVES>(red + (it & 1) * (kRed / 2), wave, lane, s1, s2);
         float a, md;
-        fwd_row_stats<KIND>(s0, s1, s2, invH, eps, r, tt == 0, stat0, stat1, a, md);
+        fwd_row_stats<KIND>(s0, s1, s2, K, invH, eps, r, tt == 0, stat0, stat1, a, md);
         TY *yr = y + (size_t)r * H;
         auto out = [&](int grp, const float (&v)[VEC]) {
             ParamGroup<VEC> wv, bv;

@@ -72,8 +72,18 @@ def test_ln_forward_options(nh, oracle_mod):
     _ln_fwd_case(nh, oracle_mod, c, wl.F32, in_place=True)
 
 
+def _mean_ulps(got, want):
+    """Largest |got - want| per row in units of the fp32 spacing at want."""
+    u = np.spacing(np.abs(np.asarray(want)).astype(np.float32)).astype(np.float64)
+    return float(np.max(np.abs(np.asarray(got, np.float64) - want) / u))
+
+
 def test_ln_forward_large_offset(nh, oracle_mod):
-    """Rows with |mean| >> std: the shifted one-pass variance keeps rstd accurate."""
+    """Rows with |mean| >> std: the shifted one-pass variance keeps rstd
+    accurate, and the stored mean is the shifted K + md (the sum of the
+    smaller terms), within 0.6 ulp of the exact mean: one rounding of it
+    plus the shifted sum's error.  (The plain sum x / H errs by up to 0.9
+    ulp on these rows.)"""
     rng = np.random.Generator(np.random.PCG64(73))
     x = (1e4 + 0.01 * rng.normal(size=(64, 1600))).astype(np.float32)
     want_y, want_m, want_r = oracle_mod.layernorm_forward(x.astype(np.float64), eps=1e-5)
@@ -81,6 +91,7 @@ def test_ln_forward_large_offset(nh, oracle_mod):
     torch.cuda.synchronize()
     check("rstd", host(gr), want_r, wl.F32)
     check("mean", host(gm), want_m, wl.F32)
+    assert _mean_ulps(host(gm), want_m) <= 0.6
 
 
 # Rows whose outputs are ill-conditioned in fp32, found by a seeded random
@@ -102,7 +113,9 @@ def test_ln_forward_ill_conditioned_rows(nh, oracle_mod, rows, cols, xt, wt, yt,
 
 def test_ln_forward_nearly_constant_rows(nh, oracle_mod):
     """Rows of 2-5 elements around 2.5 with a spread of 1e-3 (variance far
-    below eps): the output is (x - mean) * rstd with rstd near 1/sqrt(eps)."""
+    below eps): the output is (x - mean) * rstd with rstd near 1/sqrt(eps),
+    and the stored mean stays within 0.6 ulp (the plain sum errs by up to
+    1.6 ulp on these rows)."""
     rng = np.random.Generator(np.random.PCG64(74))
     for cols in (2, 3, 5):
         x = (2.5 + 1e-3 * rng.normal(size=(8192, cols))).astype(np.float32)
@@ -117,6 +130,7 @@ def test_ln_forward_nearly_constant_rows(nh, oracle_mod):
         check("y", host(gy), want_y, wl.F32)
         check("mean", host(gm), want_m, wl.F32)
         check("rstd", host(gr), want_r, wl.F32)
+        assert _mean_ulps(host(gm), want_m) <= 0.6
 
 
 def _rms_fwd_case(nh, oracle_mod, c, *, weight=True, need_rms=True, in_place=False):
