@@ -7,6 +7,9 @@ scalar paths run).  Odd-numbered BatchNorm cases force the split path
 (reduction, then elementwise kernel) where the small random shapes would
 otherwise take the one-block-per-channel kernels; a second set of row cases
 covers short aligned rows (the lane-subgroup kernels with vector groups).
+A third set draws LayerNorm and RMSNorm forward rows (1 to 40000 columns,
+every dtype mix, in place), bias+dropout+add backward rows and BatchNorm
+inference shapes, the paths a wider seeded sweep covered.
 Every output is compared with the oracle at the parity tolerances.  The cases
 are the same on every run."""
 import numpy as np
@@ -156,3 +159,83 @@ def test_rows_random(nh, oracle_mod, case):
     torch.cuda.synchronize()
     check("rms dx", host(dx), wdx, xt)
     check("rms dweight", host(dw), wdw, xt)
+
+
+# ---- forward rows, bias+dropout+add backward, BatchNorm inference ---------------
+_FWD_COLS = [1, 2, 3, 5, 17, 31, 64, 100, 513, 1600, 3000, 4096, 8192, 12288, 20000, 32768, 39921]
+
+
+def _fwd_cases():
+    rng = np.random.Generator(np.random.PCG64(4343))
+    dts = (wl.F32, wl.BF16)
+    cases = []
+    for i in range(28):
+        cols = int(rng.choice(_FWD_COLS)) if rng.random() < 0.7 else int(rng.integers(1, 40000))
+        rows = int(max(1, min(65536, int(rng.integers(1, 2_000_000)) // cols)))
+        xt, wt, yt = (dts[int(rng.integers(2))] for _ in range(3))
+        cases.append((i, "ln" if i % 2 == 0 else "rms", rows, cols, xt, wt, yt, bool(rng.random() < 0.8),
+                      bool(rng.random() < 0.7), bool(rng.random() < 0.2)))
+    return cases
+
+
+@pytest.mark.parametrize("case", _fwd_cases(), ids=lambda c: f"fwd{c[0]}")
+def test_forward_random(nh, oracle_mod, case):
+    import test_parity_fwd as TF
+    i, kind, rows, cols, xt, wt, yt, weight, bias, in_place = case
+    if kind == "ln":
+        c = wl.rows_case(rows, cols, x_t=xt, dy_t=xt, w_t=wt, seed=6000 + i, with_bias=True)
+        TF._ln_fwd_case(nh, oracle_mod, c, yt, weight=weight, bias=bias, in_place=in_place and yt == xt)
+    else:
+        c = wl.rows_case(rows, cols, x_t=xt, dy_t=xt, w_t=xt, seed=6000 + i)
+        TF._rms_fwd_case(nh, oracle_mod, c, weight=weight, in_place=in_place)
+
+
+def _bda_cases():
+    rng = np.random.Generator(np.random.PCG64(4444))
+    dts = (wl.F32, wl.BF16)
+    cases = []
+    for i in range(10):
+        cols = int(rng.choice(_FWD_COLS[4:])) if rng.random() < 0.7 else int(rng.integers(1, 20000))
+        rows = int(max(1, min(65536, int(rng.integers(1, 1_000_000)) // cols)))
+        xt, dyt, wt = (dts[int(rng.integers(2))] for _ in range(3))
+        flags = tuple(bool(rng.random() < 0.8) for _ in range(3))
+        need = tuple(bool(rng.random() < 0.85) for _ in range(5))
+        cases.append((i, rows, cols, xt, dyt, wt, float(rng.uniform(0.0, 0.5)), flags, need))
+    return cases
+
+
+@pytest.mark.parametrize("case", _bda_cases(), ids=lambda c: f"bda{c[0]}")
+def test_bda_random(nh, oracle_mod, case):
+    import test_parity_bda as TB
+    i, rows, cols, xt, dyt, wt, p_drop, (weight, dres, mask), need = case
+    c = wl.bda_case(rows, cols, x_t=xt, dy_t=dyt, w_t=wt, seed=6100 + i, p_drop=p_drop)
+    TB._bda_case(nh, oracle_mod, c, weight=weight, dres=dres, mask=mask, need=need)
+
+
+def _infer_cases():
+    rng = np.random.Generator(np.random.PCG64(4545))
+    cases = []
+    for i in range(8):
+        C = int(rng.choice([1, 3, 16, 64, 256, 1024]))
+        HW = int(rng.choice([1, 2, 3, 7, 49, 196, 784, 1000, 3136]))
+        N = int(max(1, min(4096, int(rng.integers(1, 4_000_000)) // (C * HW))))
+        cases.append((i, N, C, HW, wl.F32 if rng.random() < 0.5 else wl.BF16,
+                      ["none", "relu", "leaky_relu"][int(rng.integers(0, 3))], bool(rng.random() < 0.8)))
+    return cases
+
+
+@pytest.mark.parametrize("case", _infer_cases(), ids=lambda c: f"infer{c[0]}")
+def test_bn_infer_random(nh, oracle_mod, case):
+    from helpers import dev
+    i, N, C, HW, io, act, affine = case
+    c = wl.bn_case(N, C, HW, 1, io, seed=6200 + i, x_mean=1.0, x_std=1.0, beta_std=0.5)
+    rng = np.random.Generator(np.random.PCG64(6300 + i))
+    rm = wl.round_f32(rng.normal(0.0, 1.0, size=C))
+    rv = wl.round_f32(rng.uniform(0.2, 4.0, size=C))
+    g, b = (c.gamma, c.beta) if affine else (None, None)
+    print(f"[bn infer random {i}] N={N} C={C} HW={HW} io={io} act={act} affine={affine}", flush=True)
+    want = oracle_mod.bn_infer(c.x.value, g, b, rm, rv, act, 0.1, eps=c.eps)
+    y = nh.bn_forward_infer(dev(c.x), dev(rm), dev(rv), dev(g) if affine else None, dev(b) if affine else None,
+                            c.eps, act=act, slope=0.1)
+    torch.cuda.synchronize()
+    check("y", host(y), want, io)
