@@ -372,11 +372,14 @@ nh_status bda_layernorm_backward(const void *dy, nh_dtype dy_t,
 
 /*
  * LayerNorm forward.  NVIDIA/Fuser issue #1473's layer_norm backward takes
- * the per-row mean and rstd of this forward as inputs; they are computed with
- * the one-pass shifted sums of Aether-ML PR #18 ("One-pass statistics")
- * applied per row (shift = the row's first element):
- *   mean = K + sum d / H, var = sum d^2 / H - (sum d / H)^2 (clamped at 0),
- *   rstd = 1/sqrt(var + eps), y = (x - mean)*rstd*weight + bias.
+ * the per-row mean and rstd of this forward as inputs.  The variance comes
+ * from the one-pass shifted sums of Aether-ML PR #18 ("One-pass statistics")
+ * applied per row, with K = the row's first element, d = x - K, md = sum d / H:
+ *   var = sum d^2 / H - md^2 (clamped at 0),  rstd = 1/sqrt(var + eps),
+ *   y = ((x - K) - md)*rstd*weight + bias,
+ * and the stored mean is K + md or sum x / H, whichever sums the smaller
+ * terms (|md| < |sum x / H| picks K + md): both equal the row mean up to
+ * rounding.
  *
  *   x             [rows, cols] of x_t;   y [rows, cols] of y_t (y may equal x)
  *   weight, bias  [cols] of w_t, each may be NULL (weight = 1, bias = 0)
