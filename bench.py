@@ -958,6 +958,41 @@ def summarize_stats(stats_csv, trace_csv, out_path, command):
     open(out_path, "w").write("\n".join(lines) + "\n")
 
 
+PROFILE_UTIL_COUNTERS = "VALUBusy MemUnitStalled SQ_INSTS_VALU SQ_INSTS_VMEM_RD SQ_WAVES"
+PROFILE_UTIL = ("rocprofv3 --pmc " + PROFILE_UTIL_COUNTERS + " -f csv -d <dir> -o {w} -- python3 bench.py "
+                "--workloads {w} --steps 4 --warmup 1 --reps 1 --no-cpu-baseline --no-floors --no-calib --eager")
+
+
+def summarize_util(workload, counter_csv, out_path):
+    """One workload's library kernels: the mean per dispatch of each counter of
+    one rocprofv3 --pmc pass (VALUBusy: % of GPU time the vector ALUs issue;
+    MemUnitStalled: % of GPU time the memory unit stalls; instruction and
+    wave counts per dispatch)."""
+    import collections
+    import csv
+    vals = collections.OrderedDict()
+    for r in csv.DictReader(open(counter_csv)):
+        name = _short_kernel(r["Kernel_Name"])
+        if name.startswith("nh::"):
+            vals.setdefault(name, collections.OrderedDict()).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    names = PROFILE_UTIL_COUNTERS.split()
+    lines = [f"# {workload}: MI355X per-kernel utilisation counters (one rocprofv3 --pmc pass, eager calls)",
+             f"command: {PROFILE_UTIL.format(w=workload)}",
+             f"summarized by: python bench.py --summarize-util {workload} <counter_collection.csv>",
+             "note: VALUBusy = % of GPU time the vector ALUs issue instructions; MemUnitStalled = % of GPU time "
+             "the memory unit is stalled; the other columns are per-dispatch totals",
+             f"sources: {','.join(workload_sources(workload))}",
+             f"source_sha256_16: {sources_digest(workload_sources(workload))}",
+             "",
+             f"{'kernel':70s} {'calls':>6s} " + " ".join(f"{n:>16s}" for n in names)]
+    for k, d in vals.items():
+        calls = max(len(v) for v in d.values())
+        cols = " ".join(f"{np.mean(d[n]):16.2f}" if n in d else f"{'-':>16s}" for n in names)
+        lines.append(f"{k[:70]:70s} {calls:6d} {cols}")
+    open(out_path, "w").write("\n".join(lines) + "\n")
+
+
 def _traffic_for(kernel_key, workload):
     """Data-fabric bytes per launch (read + write) of a kernel from the
     committed counter summary of `workload`, if it was taken on the current kernel
@@ -1003,6 +1038,8 @@ def main():
     ap.add_argument("--summarize", nargs=6, metavar=("WORKLOAD", "TRACE", "FETCH", "WRITE", "CALIB_FETCH",
                                                      "CALIB_WRITE"),
                     help="write profiles/<WORKLOAD>.txt from rocprofv3 csv files and exit")
+    ap.add_argument("--summarize-util", nargs=2, metavar=("WORKLOAD", "COUNTER_CSV"),
+                    help="write profiles/<WORKLOAD>_util.txt from a rocprofv3 --pmc csv and exit")
     ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "TRACE_CSV", "OUT"),
                     help="write a profiles/ summary of a rocprofv3 --stats table (TRACE_CSV may be -) and exit")
     args = ap.parse_args()
@@ -1010,6 +1047,10 @@ def main():
         w = args.summarize[0]
         files = [f if f != "-" else None for f in args.summarize[1:]]
         summarize_workload(w, *files, os.path.join(ROOT, "profiles", f"{w}.txt"))
+        return
+    if args.summarize_util:
+        w = args.summarize_util[0]
+        summarize_util(w, args.summarize_util[1], os.path.join(ROOT, "profiles", f"{w}_util.txt"))
         return
     if args.summarize_stats:
         cmd = "rocprofv3 --kernel-trace --stats -f csv -d <dir> -o bench -- python3 bench.py"

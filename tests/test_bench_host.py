@@ -164,3 +164,23 @@ def test_workload_sources_split():
     assert "bn_kernels.hip" not in bench.workload_sources("ln_bwd_16x512x1600_xf32_dybf16_wbf16")
     for f in ("nh_device.hpp", "nh_internal.hpp"):
         assert f in bench.workload_sources(MAIN) and f in bench.workload_sources("rms_fwd_2048x8192_bf16")
+
+
+def test_summarize_util_means_per_kernel(tmp_path):
+    """One --pmc pass's counters averaged per library kernel; other kernels
+    (torch's fills) left out."""
+    k1 = "void nh::bn_grad_sums_kernel<float, 4, 6, 0>(float const*)"
+    rows = []
+    for v in (10.0, 12.0):
+        rows += [[k1, "VALUBusy", v], [k1, "MemUnitStalled", v / 10], [k1, "SQ_WAVES", 8192]]
+    rows += [["at::native::fill_kernel(float*)", "VALUBusy", 99.0]]
+    _write_csv(tmp_path / "c.csv", ["Kernel_Name", "Counter_Name", "Counter_Value"], rows)
+    out = tmp_path / "u.txt"
+    bench.summarize_util(MAIN, str(tmp_path / "c.csv"), str(out))
+    text = out.read_text().splitlines()
+    assert text[1].startswith("command: rocprofv3 --pmc VALUBusy MemUnitStalled")
+    lines = [ln for ln in text if ln.startswith("nh::")]
+    assert len(lines) == 1
+    f = lines[0][70:].split()
+    assert int(f[0]) == 2 and float(f[1]) == pytest.approx(11.0) and float(f[2]) == pytest.approx(1.1)
+    assert f[3] == "-" and f[4] == "-" and float(f[5]) == 8192
