@@ -245,6 +245,21 @@ def test_bn_large_offset_variance(nh):
         assert abs(s[0, ch] - float(mu)) <= 1e-6 * abs(float(mu))
 
 
+@pytest.mark.parametrize("io", [wl.F32, wl.BF16])
+def test_bn_offset_100_spreads(nh, oracle_mod, io):
+    """Channels whose mean is 100 times their spread, every output against
+    the oracle.  The normalized output and the gradients use the mean as the
+    statistics carry it, rounded to fp32; the oracle uses the exact mean, so
+    the normwise error of y grows as about 2e-8 * |mean|/std and that of
+    dgamma as about 6e-8 * |mean|/std, inside the fp32 bound up to a few
+    hundred spreads."""
+    c = wl.bn_case(16, 8, 33, 35, io, seed=49, x_mean=20.0, x_std=0.2)
+    print(f"[bn parity] mean/std = 100, {io}", flush=True)
+    want = _oracle_bn(oracle_mod, c)
+    got = _gpu_bn(nh, c)
+    _compare(c, got, want)
+
+
 def test_bn_empty_is_a_no_op(nh):
     x = torch.empty((0, 4, 3, 3), device="cuda")
     stats = torch.full((4, 4), 7.0, device="cuda")
