@@ -233,9 +233,15 @@ def test_bn_large_offset_variance(nh):
     c = wl.bn_case(3, 4, 41, 40, wl.F32, seed=48, x_mean=1e4, x_std=0.01)
     print("[bn parity] large offset", flush=True)
     x = dev(c.x)
-    _, stats = nh.bn_forward_train(x, dev(c.gamma), dev(c.beta), None, None, c.momentum, c.eps)
+    y, stats = nh.bn_forward_train(x, dev(c.gamma), dev(c.beta), None, None, c.momentum, c.eps)
     torch.cuda.synchronize()
     s = host(stats)
+    # y is the output its own fp32 statistics imply: (x - mean) * scale + beta
+    # with the mean as stored; the exact mean is not representable this far
+    # from zero, and its rounding is the only deviation from the oracle's y.
+    xs = c.x.value.reshape(c.N, c.C, -1)
+    want_y = (xs - s[0][None, :, None]) * s[3][None, :, None] + np.asarray(c.beta)[None, :, None]
+    check("y from the stored statistics", host(y).reshape(c.N, c.C, -1), want_y, wl.F32)
     for ch in range(c.C):
         v = c.x.value[:, ch].ravel()
         fr = [Fraction(float(t)) for t in v]
